@@ -1,0 +1,193 @@
+"""ctypes wrapper around the CPU oracle (``oracle/liboracle.so``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``; never by the library's compute path.
+Everything here takes and returns numpy arrays on the host.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_sign_fbi.argtypes = [P, I64, I64, P]
+    lib.oracle_sign_bitnet.argtypes = [P, I64, I64, ctypes.c_float, P]
+    lib.oracle_fbi_alpha.argtypes = [P, I64, I64, P]
+    lib.oracle_bitnet_scalars.argtypes = [P, I64, I64, P, P]
+    lib.oracle_packed_words.argtypes = [I64, I64]
+    lib.oracle_packed_words.restype = I64
+    lib.oracle_pack.argtypes = [P, I64, I64, P]
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32.restype = ctypes.c_float
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.oracle_fbi_linear.argtypes = [P, ctypes.c_int, I64, I64, P, I64, P, P]
+    lib.oracle_ln_absmax_quant.argtypes = [P, I64, I64, ctypes.c_double, ctypes.c_int,
+                                           ctypes.c_float, P, P, P, P]
+    lib.oracle_bitlinear_acc.argtypes = [P, I64, I64, P, I64, ctypes.c_float, P]
+    lib.oracle_bitlinear_out.argtypes = [P, I64, I64, ctypes.c_float, ctypes.c_float,
+                                         ctypes.c_int, P]
+    for name in ("oracle_sign_fbi", "oracle_sign_bitnet", "oracle_fbi_alpha",
+                 "oracle_bitnet_scalars", "oracle_pack", "oracle_fbi_linear",
+                 "oracle_ln_absmax_quant", "oracle_bitlinear_acc", "oracle_bitlinear_out"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"{what} rejected its arguments (rc={rc})")
+
+
+def _f32(W):
+    return np.ascontiguousarray(W, dtype=np.float32)
+
+
+def sign_fbi(W: np.ndarray) -> np.ndarray:
+    W = _f32(W)
+    K, N = W.shape
+    S = np.empty((K, N), np.int8)
+    _check(_load().oracle_sign_fbi(_ptr(W), K, N, _ptr(S)), "sign_fbi")
+    return S
+
+
+def sign_bitnet(W: np.ndarray, c: float) -> np.ndarray:
+    W = _f32(W)
+    K, N = W.shape
+    S = np.empty((K, N), np.int8)
+    _check(_load().oracle_sign_bitnet(_ptr(W), K, N, ctypes.c_float(c), _ptr(S)), "sign_bitnet")
+    return S
+
+
+def fbi_alpha(W: np.ndarray) -> np.ndarray:
+    W = _f32(W)
+    K, N = W.shape
+    a = np.empty(N, np.float32)
+    _check(_load().oracle_fbi_alpha(_ptr(W), K, N, _ptr(a)), "fbi_alpha")
+    return a
+
+
+def bitnet_scalars(W: np.ndarray):
+    W = _f32(W)
+    K, N = W.shape
+    c = np.zeros(1, np.float32)
+    b = np.zeros(1, np.float32)
+    _check(_load().oracle_bitnet_scalars(_ptr(W), K, N, _ptr(c), _ptr(b)), "bitnet_scalars")
+    return np.float32(c[0]), np.float32(b[0])
+
+
+def packed_words(K: int, N: int) -> int:
+    n = _load().oracle_packed_words(K, N)
+    if n < 0:
+        raise ValueError("K must be a positive multiple of 32")
+    return int(n)
+
+
+def pack(S: np.ndarray) -> np.ndarray:
+    S = np.ascontiguousarray(S, dtype=np.int8)
+    K, N = S.shape
+    P = np.empty(packed_words(K, N), np.uint32)
+    _check(_load().oracle_pack(_ptr(S), K, N, _ptr(P)), "pack")
+    return P
+
+
+def f32_to_f16(a: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    out = np.fromiter((lib.oracle_f32_to_f16(float(v)) for v in flat), dtype=np.uint16, count=flat.size)
+    return out.reshape(np.shape(a))
+
+
+def f16_to_f32(h: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.ascontiguousarray(h, dtype=np.uint16).ravel()
+    out = np.fromiter((lib.oracle_f16_to_f32(int(v)) for v in flat), dtype=np.float32, count=flat.size)
+    return out.reshape(np.shape(h))
+
+
+def fbi_linear(x_bits: np.ndarray, W: np.ndarray, alpha: np.ndarray, x_kind: str = "bf16") -> np.ndarray:
+    """y (fp64) = alpha_j * sum_i sign(W_ij) x_mi for 16-bit activations given as bit patterns."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    W = _f32(W)
+    alpha = np.ascontiguousarray(alpha, dtype=np.float32)
+    M, K = x_bits.shape
+    K2, N = W.shape
+    if K2 != K or alpha.shape != (N,):
+        raise ValueError("shape mismatch")
+    y = np.empty((M, N), np.float64)
+    kind = {"bf16": 0, "f16": 1}[x_kind]
+    _check(_load().oracle_fbi_linear(_ptr(x_bits), kind, M, K, _ptr(W), N, _ptr(alpha), _ptr(y)),
+           "fbi_linear")
+    return y
+
+
+def ln_absmax_quant(x: np.ndarray, ln_eps: float = 1e-5, bits: int = 8, q_eps: float = 1e-3):
+    """Returns (q int8 [M][K], gamma float32, mu32 [M], rstd32 [M])."""
+    x = _f32(x)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    g = np.zeros(1, np.float32)
+    mu = np.empty(M, np.float32)
+    rs = np.empty(M, np.float32)
+    _check(_load().oracle_ln_absmax_quant(_ptr(x), M, K, ctypes.c_double(ln_eps), bits,
+                                          ctypes.c_float(q_eps), _ptr(q), _ptr(g), _ptr(mu), _ptr(rs)),
+           "ln_absmax_quant")
+    return q, np.float32(g[0]), mu, rs
+
+
+def bitlinear_acc(q: np.ndarray, W: np.ndarray, c: float) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    W = _f32(W)
+    M, K = q.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError("shape mismatch")
+    acc = np.empty((M, N), np.int64)
+    _check(_load().oracle_bitlinear_acc(_ptr(q), M, K, _ptr(W), N, ctypes.c_float(c), _ptr(acc)),
+           "bitlinear_acc")
+    return acc
+
+
+def bitlinear_out(acc: np.ndarray, beta: float, gamma: float, bits: int = 8) -> np.ndarray:
+    acc = np.ascontiguousarray(acc, dtype=np.int64)
+    M, N = acc.shape
+    y = np.empty((M, N), np.float64)
+    _check(_load().oracle_bitlinear_out(_ptr(acc), M, N, ctypes.c_float(beta), ctypes.c_float(gamma),
+                                        bits, _ptr(y)), "bitlinear_out")
+    return y

@@ -1,0 +1,72 @@
+/*
+ * CPU oracle for the binarized linear layers -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded reference written from the pages'
+ * definitions. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load it; the library's compute path never does.
+ * It shares no code, header or table with the device library.
+ *
+ * Sources (by page title and passage):
+ *   [FBI-news]  "FBI-LLM ... An AI Framework Utilizing Autoregressive Distillation
+ *               for 1-bit Weight Binarization of LLMs from Scratch", the paragraph
+ *               introducing FBI-linear (sign binarization, full-precision
+ *               per-column scale initialised from column averages) and the
+ *               experiments paragraph (W1A16).
+ *   [BitNet]    "BitNet b1.58: 1bit LLM时代" blog, section 一 (BitNet):
+ *               eq. (1)-(3) weight binarization, eq. (4)-(5) absmax quant,
+ *               eq. (7)-(8) BitLinear output, LayerNorm and beta.
+ *
+ * Layout conventions: W is float32 [K][N] row-major (row i = input feature,
+ * column j = output feature); activations are [M][K]; outputs [M][N].
+ * All functions return 0 on success and a negative value on bad arguments.
+ */
+#ifndef BGB_ORACLE_H
+#define BGB_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sign with ties to -1 ([BitNet] eq. (2)); FBI-linear takes the sign of W itself. */
+int oracle_sign_fbi(const float* W, int64_t K, int64_t N, int8_t* S);
+/* BitNet: sign of (W - c), again with ties to -1 ([BitNet] eq. (1)-(2)). */
+int oracle_sign_bitnet(const float* W, int64_t K, int64_t N, float c, int8_t* S);
+
+/* FBI per-output-column scale: alpha_j = mean_i |W_ij|, fp64 sum rounded once to fp32. */
+int oracle_fbi_alpha(const float* W, int64_t K, int64_t N, float* alpha);
+/* BitNet centre c = mean(W) ([BitNet] eq. (3)) and beta = ||W||_1/(KN) ([BitNet] eq. (8)). */
+int oracle_bitnet_scalars(const float* W, int64_t K, int64_t N, float* c, float* beta);
+
+/* Packed sign format: number of uint32 words, and the packing itself. */
+int64_t oracle_packed_words(int64_t K, int64_t N);
+int oracle_pack(const int8_t* S, int64_t K, int64_t N, uint32_t* P);
+
+/* IEEE binary16 conversions (round to nearest even) used for stored scales. */
+uint16_t oracle_f32_to_f16(float f);
+float oracle_f16_to_f32(uint16_t h);
+float oracle_bf16_to_f32(uint16_t b);
+
+/* FBI-linear W1A16: y[m][j] = alpha_j * sum_i sign(W_ij) * x[m][i], in fp64.
+ * x_kind: 0 = bf16 bits, 1 = f16 bits. alpha is the stored scale widened to float. */
+int oracle_fbi_linear(const uint16_t* x, int x_kind, int64_t M, int64_t K,
+                      const float* W, int64_t N, const float* alpha, double* y);
+
+/* BitLinear prologue: per-token LayerNorm (no affine), then absmax quantization to
+ * [-Q_b+eps, Q_b-eps] with Q_b = 2^(bits-1), gamma = max |LN(x)| over the tensor.
+ * Statistics in fp64; the quantization decision in fp32 (see oracle.c).
+ * Outputs: q [M][K], gamma, and per-row mu32/rstd32 (optional, may be NULL). */
+int oracle_ln_absmax_quant(const float* x, int64_t M, int64_t K, double ln_eps, int bits,
+                           float q_eps, int8_t* q, float* gamma, float* mu32, float* rstd32);
+
+/* BitLinear integer product acc[m][j] = sum_i sign(W_ij - c) * q[m][i] (exact). */
+int oracle_bitlinear_acc(const int8_t* q, int64_t M, int64_t K, const float* W, int64_t N,
+                         float c, int64_t* acc);
+/* BitLinear output y = acc * beta * gamma / Q_b in fp64 ([BitNet] eq. (7)). */
+int oracle_bitlinear_out(const int64_t* acc, int64_t M, int64_t N, float beta, float gamma,
+                         int bits, double* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
