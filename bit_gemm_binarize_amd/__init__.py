@@ -1,0 +1,201 @@
+"""Python binding of libbgb.so (binarized linear layers on gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/bgb.h``. torch supplies device
+memory and the current stream. If the shared library is missing this module
+raises; there is no fallback path.
+
+Entry points mirror the C names:
+    binarize_pack(W, mode)            -> packed signs + scales
+    fbi_linear_w1a16(x, P, alpha, N)  -> FBI-linear forward (W1A16)
+    bitlinear_w1a8(x, P, beta, N)     -> BitLinear forward (W1A8)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+__all__ = [
+    "load", "lib_path", "packed_bytes", "workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
+    "bitlinear_w1a8", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
+    "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbgb.so")
+
+BGB_F32, BGB_F16, BGB_BF16 = 0, 1, 2
+MODE_FBI, MODE_BITNET = 0, 1
+OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR = 0, 1, 2, 3
+GEMV_MAX_M = 16
+
+EXPORTS = ("bgb_packed_bytes", "bgb_workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
+           "bitlinear_w1a8", "bgb_status_string", "bgb_last_hip_error", "bgb_version")
+
+
+class BgbError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"bgb status {status}: {msg}")
+        self.status = status
+
+
+class _QP(ctypes.Structure):
+    _fields_ = [("ln_eps", ctypes.c_double), ("bits", ctypes.c_int), ("q_eps", ctypes.c_float)]
+
+
+@dataclass
+class QuantParams:
+    ln_eps: float = 1e-5
+    bits: int = 8
+    q_eps: float = 1e-3
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libbgb.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m bit_gemm_binarize_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.bgb_packed_bytes.argtypes = [I64, I64]
+    lib.bgb_packed_bytes.restype = SZ
+    lib.bgb_workspace_bytes.argtypes = [I, I64, I64, I64]
+    lib.bgb_workspace_bytes.restype = SZ
+    lib.binarize_pack.argtypes = [P, I64, I64, I, P, P, I, P, P, P, SZ, P]
+    lib.binarize_pack.restype = I
+    lib.fbi_linear_w1a16.argtypes = [P, I, I64, I64, I64, P, P, I, P, I, P, SZ, P]
+    lib.fbi_linear_w1a16.restype = I
+    lib.bitlinear_w1a8.argtypes = [P, I, I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, P, P, SZ, P]
+    lib.bitlinear_w1a8.restype = I
+    lib.bgb_status_string.argtypes = [I]
+    lib.bgb_status_string.restype = ctypes.c_char_p
+    lib.bgb_last_hip_error.argtypes = []
+    lib.bgb_last_hip_error.restype = I
+    lib.bgb_version.argtypes = []
+    lib.bgb_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load()
+        msg = lib.bgb_status_string(rc).decode()
+        if rc == -3:
+            msg += f" (hipError {lib.bgb_last_hip_error()})"
+        raise BgbError(rc, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    return {torch.float32: BGB_F32, torch.float16: BGB_F16, torch.bfloat16: BGB_BF16}[t.dtype if hasattr(t, "dtype") else t]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def packed_bytes(K: int, N: int) -> int:
+    return int(load().bgb_packed_bytes(K, N))
+
+
+def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
+    return int(load().bgb_workspace_bytes(op, M, K, N))
+
+
+def _workspace(op, M, K, N, ws, device):
+    need = workspace_bytes(op, M, K, N)
+    if ws is None:
+        torch = _torch()
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def binarize_pack(W, mode: int = MODE_FBI, alpha_dtype=None, *, P=None, alpha=None, beta=None, centre=None,
+                  ws=None, stream=None):
+    """W: float32 [K][N] on the GPU. Returns (P, alpha) for FBI or (P, beta, centre) for BitNet.
+    P is an int32 tensor holding the uint32 words of the packed format."""
+    torch = _torch()
+    K, N = W.shape
+    dev = W.device
+    if P is None:
+        P = torch.empty(max(packed_bytes(K, N) // 4, 4), dtype=torch.int32, device=dev)
+    op = OP_PACK_FBI if mode == MODE_FBI else OP_PACK_BITNET
+    ws = _workspace(op, 0, K, N, ws, dev)
+    if mode == MODE_FBI:
+        adt = torch.float32 if alpha_dtype is None else alpha_dtype
+        if alpha is None:
+            alpha = torch.empty(max(N, 8), dtype=adt, device=dev)[:N]
+        _check(load().binarize_pack(_ptr(W), K, N, mode, _ptr(P), _ptr(alpha), _dt(alpha), None, None,
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+        return P, alpha
+    if beta is None:
+        beta = torch.empty(4, dtype=torch.float32, device=dev)
+    if centre is None:
+        centre = torch.empty(4, dtype=torch.float32, device=dev)
+    _check(load().binarize_pack(_ptr(W), K, N, mode, _ptr(P), None, BGB_F32, _ptr(beta), _ptr(centre),
+                                _ptr(ws), ws.numel(), _stream(stream)))
+    return P, beta[:1], centre[:1]
+
+
+def fbi_linear_w1a16(x, P, alpha, N: int, y_dtype=None, *, y=None, ws=None, stream=None):
+    """x: bf16/f16 [M][K]; P: packed signs; alpha: [N] f32/f16. Returns y [M][N]."""
+    torch = _torch()
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32 if y_dtype is None else y_dtype, device=x.device)
+    ws = _workspace(OP_FBI_LINEAR, M, K, N, ws, x.device)
+    _check(load().fbi_linear_w1a16(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(alpha), _dt(alpha), _ptr(y), _dt(y),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=None, want_q=False,
+                   want_gamma=False, want_acc=False, ws=None, stream=None):
+    """x: f32/bf16 [M][K]; P: packed signs of W - c; beta: device scalar.
+    Returns y, or (y, extras) with the requested taps (q, gamma, acc)."""
+    torch = _torch()
+    M, K = x.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q = torch.empty((M, K), dtype=torch.int8, device=dev) if want_q else None
+    g = torch.empty(4, dtype=torch.float32, device=dev) if want_gamma else None
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
+    ws = _workspace(OP_BITLINEAR, M, K, N, ws, dev)
+    qp = qp or QuantParams()
+    cqp = _QP(float(qp.ln_eps), int(qp.bits), float(qp.q_eps))
+    _check(load().bitlinear_w1a8(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y),
+                                 _ptr(q), _ptr(g), _ptr(acc), _ptr(ws), ws.numel(), _stream(stream)))
+    if not (want_q or want_gamma or want_acc):
+        return y
+    extras = {}
+    if want_q:
+        extras["q"] = q
+    if want_gamma:
+        extras["gamma"] = g[:1]
+    if want_acc:
+        extras["acc"] = acc
+    return y, extras

@@ -1,0 +1,149 @@
+// C ABI of libbgb.so: argument validation, workspace carving, dispatch on M.
+// The declarations and the full contract are in include/bgb.h.
+#include "../../include/bgb.h"
+#include "bgb_internal.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+// Shared shape rules; M may be 0 (empty), N may be 0 (empty).
+int check_shape(int64_t M, int64_t K, int64_t N) {
+    if (K <= 0 || (K % 32) != 0 || K > bgb::kMaxK) return BGB_EINVAL;
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return BGB_EINVAL;
+    if (M * K > kMaxElems || K * N > kMaxElems || M * N > kMaxElems) return BGB_EINVAL;
+    return BGB_OK;
+}
+
+int finish(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = int(e);
+        return BGB_EHIP;
+    }
+    return BGB_OK;
+}
+
+char* carve(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+size_t bgb_packed_bytes(int64_t K, int64_t N) {
+    if (K <= 0 || (K % 32) != 0 || N < 0) return 0;
+    return size_t(bgb::tiles_per_col(K)) * size_t(N) * 16u;
+}
+
+size_t bgb_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
+    if (K <= 0 || (K % 32) != 0 || M < 0 || N < 0) return 0;
+    switch (op) {
+        case BGB_OP_PACK_FBI: return bgb::PackFbiWs::make(K, N).total;
+        case BGB_OP_PACK_BITNET: return bgb::PackBitnetWs::make().total;
+        case BGB_OP_FBI_LINEAR: return bgb::FbiLinearWs::make(M, K).total;
+        case BGB_OP_BITLINEAR: return bgb::BitlinearWs::make(M, K).total;
+        default: return 0;
+    }
+}
+
+int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P, void* alpha, int alpha_dtype,
+                  float* beta, float* centre, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(0, K, N);
+    if (rc) return rc;
+    if (mode != BGB_MODE_FBI && mode != BGB_MODE_BITNET) return BGB_EUNSUPPORTED;
+    if (!W || !P || !aligned16(W) || !aligned16(P)) return BGB_EINVAL;
+    if (mode == BGB_MODE_FBI) {
+        if (alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+        if (!alpha || !aligned16(alpha)) return BGB_EINVAL;
+    } else {
+        if (!beta || !centre || !aligned16(beta) || !aligned16(centre)) return BGB_EINVAL;
+    }
+    const int op = mode == BGB_MODE_FBI ? BGB_OP_PACK_FBI : BGB_OP_PACK_BITNET;
+    const size_t need = bgb_workspace_bytes(op, 0, K, N);
+    if (need && (!ws || ws_bytes < need || !aligned16(ws))) return BGB_EINVAL;
+    if (N == 0) return BGB_OK;
+    return finish(bgb::launch_pack(W, K, N, mode, P, alpha, alpha_dtype == BGB_F16, beta, centre, ws,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                     const void* alpha, int alpha_dtype, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int rc = check_shape(M, K, N);
+    if (rc) return rc;
+    if (x_dtype != BGB_BF16 && x_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (y_dtype != BGB_F32 && y_dtype != BGB_BF16 && y_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (!x || !P || !alpha || !y) return BGB_EINVAL;
+    if (!aligned16(x) || !aligned16(P) || !aligned16(alpha) || !aligned16(y)) return BGB_EINVAL;
+    const bgb::FbiLinearWs lay = bgb::FbiLinearWs::make(M, K);
+    if (lay.total && (!ws || ws_bytes < lay.total || !aligned16(ws))) return BGB_EINVAL;
+    if (M == 0 || N == 0) return BGB_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int x_f16 = x_dtype == BGB_F16;
+    const int a_f16 = alpha_dtype == BGB_F16;
+    const int ydt = y_dtype == BGB_F32 ? 0 : (y_dtype == BGB_F16 ? 1 : 2);
+    if (M <= bgb::kGemvMaxM) {
+        uint16_t* xp = reinterpret_cast<uint16_t*>(carve(ws, lay.xp));
+        float* xsum = reinterpret_cast<float*>(carve(ws, lay.xsum));
+        hipError_t e = bgb::launch_w1a16_prep(x, x_f16, M, K, xp, xsum, s);
+        if (e != hipSuccess) return finish(e);
+        return finish(bgb::launch_w1a16_gemv(xp, xsum, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
+    }
+    return finish(bgb::launch_w1a16_gemm(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
+}
+
+int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                   const float* beta, const bgb_quant_params* qp, float* y, int8_t* xq_opt, float* gamma_opt,
+                   int32_t* acc_opt, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(M, K, N);
+    if (rc) return rc;
+    if (x_dtype != BGB_F32 && x_dtype != BGB_BF16) return BGB_EUNSUPPORTED;
+    bgb_quant_params p = {1e-5, 8, 1e-3f};
+    if (qp) p = *qp;
+    if (p.bits < 2 || p.bits > 8) return BGB_EUNSUPPORTED;
+    const float qb = float(1 << (p.bits - 1));
+    if (!(p.ln_eps >= 0.0) || !(p.q_eps >= 0.0f) || !(p.q_eps < 1.0f)) return BGB_EINVAL;
+    if (!x || !P || !beta || !y) return BGB_EINVAL;
+    if (!aligned16(x) || !aligned16(P) || !aligned16(y)) return BGB_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(beta) & 3u) || (gamma_opt && (reinterpret_cast<uintptr_t>(gamma_opt) & 3u)))
+        return BGB_EINVAL;
+    if ((xq_opt && !aligned16(xq_opt)) || (acc_opt && !aligned16(acc_opt))) return BGB_EINVAL;
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
+    if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
+    if (M == 0 || N == 0) return BGB_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float lim = qb - p.q_eps;               // fl32(Q_b - eps), as the reference computes it
+    float* stats = reinterpret_cast<float*>(carve(ws, lay.stats));
+    float* gamma = reinterpret_cast<float*>(carve(ws, lay.gamma));
+    int32_t* rowsum = reinterpret_cast<int32_t*>(carve(ws, lay.rowsum));
+    int8_t* q = reinterpret_cast<int8_t*>(carve(ws, lay.q));
+    const bool decode = M <= bgb::kGemvMaxM;
+    hipError_t e = bgb::launch_ln_quant(x, x_dtype == BGB_BF16, M, K, p.ln_eps, qb, lim, decode ? 0 : 1, q, rowsum,
+                                        stats, gamma, xq_opt, gamma_opt, s);
+    if (e != hipSuccess) return finish(e);
+    if (decode) return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
+    return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
+}
+
+const char* bgb_status_string(int status) {
+    switch (status) {
+        case BGB_OK: return "ok";
+        case BGB_EINVAL: return "invalid argument (null pointer, shape, alignment or workspace size)";
+        case BGB_EUNSUPPORTED: return "unsupported dtype or mode";
+        case BGB_EHIP: return "HIP launch failed (see bgb_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int bgb_last_hip_error(void) { return g_last_hip_error; }
+
+const char* bgb_version(void) { return "bgb 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Device-side helpers shared by the kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#define BGB_DEV __device__ __forceinline__
+
+namespace bgb {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+enum { kDtF32 = 0, kDtF16 = 1, kDtBF16 = 2 };
+
+// 16-bit float formats <-> float (round to nearest even on the way down).
+BGB_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+BGB_DEV float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+BGB_DEV uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+BGB_DEV uint16_t f32_to_f16_rne(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+// Exact "a > b" for fp32 independent of the denormal mode: NaN compares
+// false, +0 == -0, subnormals keep their order.
+BGB_DEV uint32_t f32_order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) == 0) u = 0;                    // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+BGB_DEV bool f32_is_nan(float v) { return (__float_as_uint(v) & 0x7fffffffu) > 0x7f800000u; }
+BGB_DEV bool f32_gt_exact(float a, float b) {
+    if (f32_is_nan(a) || f32_is_nan(b)) return false;
+    return f32_order_key(a) > f32_order_key(b);
+}
+// a > 0 on the bit pattern: positive subnormals and +inf are > 0; zeros and NaN are not.
+BGB_DEV bool f32_gt_zero(float a) {
+    uint32_t u = __float_as_uint(a);
+    return int32_t(u) > 0 && u <= 0x7f800000u;
+}
+
+// ---- wave / block reductions (fixed trees -> deterministic) -----------------
+BGB_DEV double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+BGB_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+BGB_DEV int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Block-wide reductions; `scratch` must hold blockDim.x/64 entries. All
+// threads get the result. Contains __syncthreads().
+template <int NT>
+BGB_DEV double block_sum(double v, double* scratch) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[w] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += scratch[i];
+    return t;
+}
+template <int NT>
+BGB_DEV float block_max(float v, float* scratch) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[w] = v;
+    __syncthreads();
+    float t = scratch[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) t = fmaxf(t, scratch[i]);
+    return t;
+}
+template <int NT>
+BGB_DEV int block_sum_i(int v, int* scratch) {
+    v = wave_sum_i(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[w] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += scratch[i];
+    return t;
+}
+
+// Rank the tiles so that each of the 8 XCDs (block b runs on XCD b % 8)
+// works through one contiguous range of tiles. Launch 8 * ceil(n/8) blocks;
+// a block whose tile is >= n has nothing to do.
+BGB_DEV int xcd_tile(int b, int n) {
+    const int per = (n + 7) / 8;
+    return (b % 8) * per + b / 8;
+}
+inline int xcd_grid(int n) { return 8 * ((n + 7) / 8); }
+
+}  // namespace bgb

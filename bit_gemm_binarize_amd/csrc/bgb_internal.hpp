@@ -1,0 +1,98 @@
+// Internal declarations shared by the C-ABI layer and the kernel files.
+// Host-side only: launcher prototypes, workspace layout, size rules.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bgb {
+
+constexpr int kWords4 = 4;             // words per 16-byte column tile (128 rows)
+constexpr int kGemvMaxM = 16;          // M <= 16 -> decode kernels
+constexpr int kMaxK = 524288;
+
+inline int64_t words_per_col(int64_t K) { return K / 32; }                // T
+inline int64_t tiles_per_col(int64_t K) { return (K / 32 + 3) / 4; }      // TQ
+inline int64_t padded_k(int64_t K) { return tiles_per_col(K) * 128; }    // Kp
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// ---- workspace layouts (all offsets 256-byte aligned) -----------------------
+struct PackFbiWs {          // fp64 partial |W| sums per (tile, column)
+    size_t colsum, total;
+    static PackFbiWs make(int64_t K, int64_t N) {
+        PackFbiWs w{};
+        w.colsum = 0;
+        w.total = align256(size_t(tiles_per_col(K)) * size_t(N) * sizeof(double));
+        return w;
+    }
+};
+
+constexpr int kBitnetReduceBlocks = 1024;
+struct PackBitnetWs {       // fp64 (sum W, sum |W|) per reduction block
+    size_t partial, total;
+    static PackBitnetWs make() {
+        PackBitnetWs w{};
+        w.partial = 0;
+        w.total = align256(size_t(kBitnetReduceBlocks) * 2 * sizeof(double));
+        return w;
+    }
+};
+
+struct FbiLinearWs {        // decode only: permuted activations + per-type sums
+    size_t xp, xsum, total;
+    static FbiLinearWs make(int64_t M, int64_t K) {
+        FbiLinearWs w{};
+        if (M > kGemvMaxM) { w.xp = w.xsum = w.total = 0; return w; }
+        w.xp = 0;
+        w.xsum = align256(size_t(M) * size_t(padded_k(K)) * 2);
+        w.total = w.xsum + align256(size_t(M) * 4 * sizeof(float));
+        return w;
+    }
+};
+
+struct BitlinearWs {
+    size_t stats, gamma, rowsum, q, total;
+    static BitlinearWs make(int64_t M, int64_t K) {
+        BitlinearWs w{};
+        w.stats = 0;                                               // float [M][3] mu32, rstd32, rowmax
+        w.gamma = w.stats + align256(size_t(M) * 3 * sizeof(float));
+        w.rowsum = w.gamma + 256;                                  // int32 [M]
+        w.q = w.rowsum + align256(size_t(M) * sizeof(int32_t));    // int8 [M][Kp], layout per path
+        w.total = w.q + align256(size_t(M) * size_t(padded_k(K)));
+        return w;
+    }
+};
+
+// ---- launchers (each returns hipGetLastError() after its launches) -----------
+hipError_t launch_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
+                       void* alpha, int alpha_f16, float* beta, float* centre,
+                       void* ws, hipStream_t s);
+
+// q layout written by the prologue: 0 = decode kernel layout, 1 = GEMM layout
+hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, double ln_eps,
+                           float qb, float lim, int layout, int8_t* q, int32_t* rowsum,
+                           float* stats, float* gamma_ws, int8_t* xq_opt, float* gamma_opt,
+                           hipStream_t s);
+
+hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp,
+                             float* xsum, hipStream_t s);
+
+hipError_t launch_w1a16_gemv(const uint16_t* xp, const float* xsum, int x_f16, int64_t M,
+                             int64_t K, int64_t N, const uint32_t* P, const void* alpha,
+                             int alpha_f16, void* y, int y_dtype, hipStream_t s);
+
+hipError_t launch_w1a16_gemm(const void* x, int x_f16, int64_t M, int64_t K, int64_t N,
+                             const uint32_t* P, const void* alpha, int alpha_f16, void* y,
+                             int y_dtype, hipStream_t s);
+
+hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma,
+                            const float* beta, float qb, int64_t M, int64_t K, int64_t N,
+                            const uint32_t* P, float* y, int32_t* acc_opt, hipStream_t s);
+
+hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
+                            const float* beta, float qb, int64_t M, int64_t K, int64_t N,
+                            const uint32_t* P, float* y, int32_t* acc_opt, hipStream_t s);
+
+}  // namespace bgb

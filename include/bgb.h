@@ -1,0 +1,168 @@
+/*
+ * bgb.h -- C ABI of the binarized linear layer library (libbgb.so, gfx950).
+ *
+ * Two layers are provided, each as a one-time weight conversion plus a
+ * forward pass:
+ *
+ *   FBI-linear (W1A16), from "FBI-LLM ... An AI Framework Utilizing
+ *   Autoregressive Distillation for 1-bit Weight Binarization of LLMs from
+ *   Scratch" (news rewrite of the FBI-LLM paper), paragraph introducing
+ *   FBI-linear: weights binarized with the sign function, one full-precision
+ *   scale per column initialised from the column average, 16-bit activations
+ *   (the W1A16 setting of its experiments paragraph).
+ *
+ *   BitLinear (W1A8), from the "BitNet b1.58: 1bit LLM时代" blog, section 一
+ *   (BitNet): eq. (1)-(3) zero-centred sign binarization, eq. (4)-(5) absmax
+ *   activation quantization, eq. (7)-(8) output rescale, LayerNorm and beta.
+ *   "BitNet-Transformers: 1比特量化技术在大型语言模型中的应用与实现" presents
+ *   BitLinear as a drop-in replacement for a linear layer, which fixes the
+ *   shape of this interface: a conversion step plus a forward call.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Shapes: W is float32 [K][N] row-major (row i = input feature, column j =
+ *   output feature); activations x are [M][K]; outputs y are [M][N]; all
+ *   row-major and contiguous. y = x . W_b (scaled), i.e. the same product as
+ *   a linear layer with in_features = K and out_features = N.
+ * - K must be a positive multiple of 32. M == 0 or N == 0 is a valid empty
+ *   call that launches nothing. Limits: K <= 524288, M <= 2^24, N <= 2^24,
+ *   and M*K, K*N, M*N each < 2^31 elements.
+ * - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *   16-byte aligned, owned by the caller. The library allocates nothing and
+ *   keeps no state between calls except the last HIP error code.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream). Nothing is copied back to the host. Results are bit-identical
+ *   from run to run (fixed reduction orders, no floating-point atomics).
+ * - Scratch memory comes from the caller's workspace `ws` of `ws_bytes`
+ *   bytes (256-byte aligned); bgb_workspace_bytes() gives the size needed.
+ *   Calls that share a workspace must be ordered (same stream).
+ * - Errors: 0 on success, else a negative bgb_status. Arguments are
+ *   validated before any launch; a rejected call writes no output.
+ *
+ * Packed sign format P (the pages only say each weight takes one bit):
+ *   T = K/32 words per column, TQ = ceil(T/4); P holds TQ*N*4 uint32 words
+ *   (bgb_packed_bytes). The word covering rows 32t..32t+31 of column j sits
+ *   at index (t/4)*4N + 4j + (t%4), so each column's 128 consecutive rows
+ *   form one 16-byte tile and the tiles of one 128-row band are stored column
+ *   after column. Bit b (LSB = 0) of that word is 1 iff the sign of weight
+ *   (row 32t+b, column j) is +1, 0 iff it is -1. Words with t >= T are 0.
+ */
+#ifndef BGB_H
+#define BGB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BGB_OK = 0,
+    BGB_EINVAL = -1,        /* null pointer, bad shape, misalignment, small workspace */
+    BGB_EUNSUPPORTED = -2,  /* dtype or mode combination not implemented */
+    BGB_EHIP = -3           /* a HIP launch failed; see bgb_last_hip_error() */
+} bgb_status;
+
+typedef enum { BGB_F32 = 0, BGB_F16 = 1, BGB_BF16 = 2 } bgb_dtype;
+
+typedef enum { BGB_MODE_FBI = 0, BGB_MODE_BITNET = 1 } bgb_mode;
+
+typedef enum {
+    BGB_OP_PACK_FBI = 0,
+    BGB_OP_PACK_BITNET = 1,
+    BGB_OP_FBI_LINEAR = 2,
+    BGB_OP_BITLINEAR = 3
+} bgb_op;
+
+/* Activation quantization parameters of BitLinear ("BitNet b1.58: 1bit LLM时代",
+ * section 一, eq. (4), (5), (8)). */
+typedef struct {
+    double ln_eps;   /* LayerNorm epsilon added to the variance (1e-5) */
+    int bits;        /* b in Q_b = 2^(b-1); 2..8 (8 -> Q_b = 128, int8 codes) */
+    float q_eps;     /* clip margin: codes are clipped to [-Q_b+eps, Q_b-eps] (1e-3) */
+} bgb_quant_params;
+
+/* Size in bytes of the packed array P for a K x N weight (0 if K is invalid). */
+size_t bgb_packed_bytes(int64_t K, int64_t N);
+
+/* Workspace bytes that `op` needs for these sizes (M is ignored by the packs). */
+size_t bgb_workspace_bytes(int op, int64_t M, int64_t K, int64_t N);
+
+/*
+ * binarize_pack -- one-time weight conversion.
+ *
+ * mode BGB_MODE_FBI (FBI-linear paragraph of the FBI-LLM news rewrite; tie
+ * rule from the BitNet blog, eq. (2)): s_ij = +1 iff W_ij > 0, else -1
+ * (zeros and NaN give -1; positive subnormals give +1).
+ *   alpha_j = mean_i |W_ij| over the K inputs of output column j, summed in
+ *   fp64 and rounded once to fp32 (then to fp16 by round-to-nearest-even
+ *   when alpha_dtype == BGB_F16). alpha: [N] of alpha_dtype (F32 or F16).
+ *   beta and centre are ignored (may be NULL).
+ * mode BGB_MODE_BITNET (BitNet blog, eq. (1)-(3) and (8)):
+ *   centre c = mean(W), beta = ||W||_1/(K N), each an fp64 sum rounded once to
+ *   fp32 and written to device scalars `centre` and `beta`;
+ *   s_ij = +1 iff W_ij > c (compared exactly in fp32), else -1.
+ *   alpha/alpha_dtype are ignored (may be NULL).
+ * W: [K][N] float32 (input). P: bgb_packed_bytes(K, N) bytes (output).
+ * ws: bgb_workspace_bytes(BGB_OP_PACK_FBI or _BITNET, 0, K, N) bytes.
+ * Errors: BGB_EINVAL (null, K % 32 != 0, sizes, alignment, workspace),
+ *         BGB_EUNSUPPORTED (alpha dtype not F32/F16, unknown mode), BGB_EHIP.
+ */
+int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
+                  void* alpha, int alpha_dtype, float* beta, float* centre,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fbi_linear_w1a16 -- FBI-linear forward (W1A16).
+ *   y[m][j] = alpha_j * sum_i s_ij * x[m][i]
+ * x: [M][K] bf16 or f16 (x_dtype BGB_BF16 / BGB_F16). P: packed signs (above).
+ * alpha: [N] in alpha_dtype (F32 or F16), used as given (a trained scale is
+ * accepted). y: [M][N] in y_dtype (F32, BF16 or F16; 16-bit outputs are
+ * rounded to nearest even). Products of +-1 and x are exact; sums use fp32
+ * accumulation on the matrix cores; alpha is applied once to the fp32 sum.
+ * M <= 16 runs the memory-bound decode kernel, M > 16 the MFMA GEMM.
+ * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes.
+ * Activations with |x| >= 2^124 are outside the supported range.
+ * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP.
+ */
+int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
+                     const uint32_t* P, const void* alpha, int alpha_dtype,
+                     void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bitlinear_w1a8 -- BitLinear forward (BitNet blog, section 一, eq. (4)-(8)).
+ *   h = LN(x) per token (biased variance, no affine): E(x), Var(x) in fp64,
+ *       then h = fl32(fl32(x - fl32(E)) * fl32(1/sqrt(Var + ln_eps)))
+ *   gamma = max |h| over the whole M x K tensor
+ *   q = trunc(clip(fl32(h * Q_b / gamma), -(Q_b - q_eps), Q_b - q_eps))
+ *       (q = 0 when gamma == 0); |q| <= Q_b - 1
+ *   acc[m][j] = sum_i s_ij * q[m][i]           (exact int32)
+ *   y[m][j] = fl32(float(acc) * fl32(fl32(beta * gamma) / Q_b))
+ * x: [M][K] F32 or BF16. P: packed signs of W - c (binarize_pack BITNET).
+ * beta: device scalar from binarize_pack. qp: host pointer (NULL = defaults
+ * ln_eps 1e-5, bits 8, q_eps 1e-3). y: [M][N] float32.
+ * Optional outputs (NULL to skip): xq_opt int8 [M][K] codes, gamma_opt device
+ * float scalar, acc_opt int32 [M][N].
+ * ws: bgb_workspace_bytes(BGB_OP_BITLINEAR, M, K, N) bytes.
+ * M <= 16 runs the memory-bound decode kernel, M > 16 the int8 MFMA GEMM.
+ * Errors: BGB_EINVAL, BGB_EUNSUPPORTED, BGB_EHIP.
+ */
+int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
+                   const uint32_t* P, const float* beta, const bgb_quant_params* qp,
+                   float* y, int8_t* xq_opt, float* gamma_opt, int32_t* acc_opt,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Message for a status code (static string). */
+const char* bgb_status_string(int status);
+
+/* The hipError_t value behind the most recent BGB_EHIP (0 if none). */
+int bgb_last_hip_error(void);
+
+/* Library version string. */
+const char* bgb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BGB_H */

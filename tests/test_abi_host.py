@@ -1,0 +1,119 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+that include/bgb.h declares, and rejects bad arguments before touching the
+GPU. Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+import bit_gemm_binarize_amd as bgb
+
+HDR = os.path.join(ROOT, "include", "bgb.h")
+
+BAD = -1        # BGB_EINVAL
+UNSUP = -2      # BGB_EUNSUPPORTED
+A = 1 << 20     # a 16-byte aligned, never dereferenced fake device address
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bgb.lib_path()):
+        pytest.fail("libbgb.so is not built (python -m bit_gemm_binarize_amd.build)")
+    return bgb.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("binarize_pack", "fbi_linear_w1a16", "bitlinear_w1a8", "bgb_workspace_bytes",
+              "bgb_packed_bytes", "bgb_status_string", "bgb_last_hip_error", "bgb_version"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(bgb.lib_path())
+    for n in declared_functions():
+        assert hasattr(raw, n), f"{n} declared in bgb.h but not exported"
+    assert set(bgb.EXPORTS) <= set(declared_functions())
+
+
+def test_sizes(lib):
+    assert bgb.packed_bytes(32, 5) == 1 * 5 * 16
+    assert bgb.packed_bytes(128, 5) == 1 * 5 * 16
+    assert bgb.packed_bytes(160, 3) == 2 * 3 * 16
+    assert bgb.packed_bytes(4096, 11008) == 5636096
+    assert bgb.packed_bytes(31, 5) == 0
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 64, 4096, 4096) == 0        # GEMM path needs none
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 16, 4096, 4096) >= 16 * 4096 * 2
+    assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 1, 4096, 11008) >= 4096
+    assert bgb.workspace_bytes(99, 1, 32, 32) == 0
+    assert lib.bgb_version().decode().startswith("bgb")
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -7):
+        assert len(lib.bgb_status_string(code)) > 0
+
+
+def call_pack(lib, W=A, K=64, N=8, mode=0, P=A, alpha=A, adt=0, beta=A, centre=A, ws=A, wsb=1 << 30):
+    return lib.binarize_pack(W, K, N, mode, P, alpha, adt, beta, centre, ws, wsb, None)
+
+
+def test_pack_validation(lib):
+    assert call_pack(lib, K=48) == BAD                 # K % 32 != 0
+    assert call_pack(lib, K=0) == BAD
+    assert call_pack(lib, N=-1) == BAD
+    assert call_pack(lib, W=None) == BAD
+    assert call_pack(lib, P=A + 4) == BAD              # misaligned
+    assert call_pack(lib, mode=5) == UNSUP
+    assert call_pack(lib, adt=2) == UNSUP              # bf16 alpha
+    assert call_pack(lib, alpha=None) == BAD
+    assert call_pack(lib, mode=1, beta=None) == BAD
+    assert call_pack(lib, wsb=8) == BAD                # workspace too small
+    assert call_pack(lib, N=0) == 0                    # empty: nothing launched
+
+
+def call_fbi(lib, x=A, xdt=2, M=4, K=64, N=8, P=A, alpha=A, adt=0, y=A, ydt=0, ws=A, wsb=1 << 30):
+    return lib.fbi_linear_w1a16(x, xdt, M, K, N, P, alpha, adt, y, ydt, ws, wsb, None)
+
+
+def test_fbi_linear_validation(lib):
+    assert call_fbi(lib, K=40) == BAD
+    assert call_fbi(lib, M=-1) == BAD
+    assert call_fbi(lib, xdt=0) == UNSUP               # f32 activations are not W1A16
+    assert call_fbi(lib, adt=2) == UNSUP
+    assert call_fbi(lib, ydt=7) == UNSUP
+    assert call_fbi(lib, x=None) == BAD
+    assert call_fbi(lib, y=A + 2) == BAD
+    assert call_fbi(lib, wsb=0) == BAD                 # decode path needs a workspace
+    assert call_fbi(lib, M=1 << 25) == BAD
+    assert call_fbi(lib, M=0) == 0 and call_fbi(lib, N=0) == 0
+
+
+def call_bl(lib, x=A, xdt=0, M=1, K=64, N=8, P=A, beta=A, qp=None, y=A, xq=None, g=None, acc=None, ws=A,
+            wsb=1 << 30):
+    return lib.bitlinear_w1a8(x, xdt, M, K, N, P, beta, qp, y, xq, g, acc, ws, wsb, None)
+
+
+def test_bitlinear_validation(lib):
+    assert call_bl(lib, K=33) == BAD
+    assert call_bl(lib, xdt=1) == UNSUP                # f16 activations not offered here
+    assert call_bl(lib, beta=None) == BAD
+    assert call_bl(lib, ws=None) == BAD
+    assert call_bl(lib, wsb=16) == BAD
+    assert call_bl(lib, xq=A + 1) == BAD
+    bad_bits = bgb._QP(1e-5, 9, 1e-3)
+    assert call_bl(lib, qp=ctypes.pointer(bad_bits)) == UNSUP
+    bad_eps = bgb._QP(1e-5, 8, 2.0)
+    assert call_bl(lib, qp=ctypes.pointer(bad_eps)) == BAD
+    assert call_bl(lib, M=0) == 0

@@ -1,0 +1,98 @@
+"""GPU parity: bitlinear_w1a8 (LN + absmax prologue, W1A8 product, epilogue)
+against the oracle: gamma and codes bit-exact, int32 accumulators bit-exact,
+outputs within 1e-5 of the fp64 epilogue."""
+import numpy as np
+import pytest
+import torch
+
+import bgb_synth as syn
+from gpu_util import check_w1a8, dev_bits16, dev_f32, host_f32, say, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(bgb, orc, W, x_host, x_dev, qp=None, bits=8):
+    K, N = W.shape
+    P, beta, centre = bgb.binarize_pack(dev_f32(W), bgb.MODE_BITNET)
+    y, ex = bgb.bitlinear_w1a8(x_dev, P, beta, N, qp, want_q=True, want_gamma=True, want_acc=True)
+    torch.cuda.synchronize()
+    c_ref, b_ref = orc.bitnet_scalars(W)
+    q_ref, g_ref, _, _ = orc.ln_absmax_quant(x_host, bits=bits)
+    g = np.float32(host_f32(ex["gamma"])[0])
+    assert g.view(np.uint32) == g_ref.view(np.uint32), (g, g_ref)
+    q = ex["q"].cpu().numpy()
+    assert np.array_equal(q, q_ref), f"{int((q != q_ref).sum())} codes differ"
+    acc_ref = orc.bitlinear_acc(q_ref, W, c_ref)
+    acc = ex["acc"].cpu().numpy().astype(np.int64)
+    assert np.array_equal(acc, acc_ref)
+    y_ref = orc.bitlinear_out(acc_ref, b_ref, g_ref, bits=bits)
+    return to_bits(y), y_ref
+
+
+CASES = [(1, 4096, 11008), (1, 96, 65), (3, 160, 300), (16, 768, 260), (17, 96, 65), (40, 1024, 300),
+         (130, 256, 513), (5, 11008, 64)]
+
+
+@pytest.mark.parametrize("M,K,N", CASES)
+@pytest.mark.parametrize("x_kind", ["f32", "bf16"])
+def test_bitlinear_parity(bgb_gpu, orc, M, K, N, x_kind):
+    say(f"bitlinear M={M} K={K} N={N} x={x_kind}")
+    seed = 500 + M + K
+    W = syn.normal_f32(seed, 0, (K, N), mean=0.001, std=0.02)
+    xf = syn.normal_f32(seed, 1, (M, K))
+    if x_kind == "bf16":
+        xb = syn.f32_to_bf16_bits(xf)
+        x_host = syn.bf16_bits_to_f32(xb)
+        x_dev = dev_bits16(xb, torch.bfloat16)
+    else:
+        x_host, x_dev = xf, dev_f32(xf)
+    y, y_ref = _run(bgb_gpu, orc, W, x_host, x_dev)
+    check_w1a8(y, y_ref, f"M={M} K={K} N={N}")
+
+
+def test_bitlinear_quant_closed_forms(bgb_gpu, orc):
+    """Rows (-3,-1,1,3)... give codes (-127,-42,42,127); constant rows give 0."""
+    say("bitlinear closed forms")
+    K, N = 96, 40
+    x = np.tile(np.array([-3, -1, 1, 3], np.float32), (4, K // 4))
+    x[2] = 0.75
+    W = syn.normal_f32(3, 0, (K, N), mean=0.001, std=0.02)
+    y, y_ref = _run(bgb_gpu, orc, W, x, dev_f32(x))
+    check_w1a8(y, y_ref)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_bitlinear_bits_and_all_tie_weights(bgb_gpu, orc, bits):
+    """Constant W: every weight ties to -1, so acc = -sum(q) for every column."""
+    say(f"bitlinear constant weights bits={bits}")
+    from bit_gemm_binarize_amd import QuantParams
+    K, N = 256, 33
+    W = np.full((K, N), 0.37, np.float32)
+    for M in (2, 20):
+        xf = syn.normal_f32(4, 1, (M, K))
+        y, y_ref = _run(bgb_gpu, orc, W, xf, dev_f32(xf), qp=QuantParams(bits=bits), bits=bits)
+        check_w1a8(y, y_ref)
+
+
+def test_bitlinear_zero_input(bgb_gpu, orc):
+    say("bitlinear zero input")
+    K, N = 128, 20
+    W = syn.normal_f32(5, 0, (K, N), mean=0.001, std=0.02)
+    for M in (1, 18):
+        x = np.zeros((M, K), np.float32)
+        y, y_ref = _run(bgb_gpu, orc, W, x, dev_f32(x))
+        assert np.all(y == 0) and np.all(y_ref == 0)
+
+
+def test_bitlinear_empty_and_deterministic(bgb_gpu):
+    say("bitlinear empty + determinism")
+    K, N = 1024, 300
+    P, beta, _ = bgb_gpu.binarize_pack(dev_f32(syn.normal_f32(6, 0, (K, N), mean=0.001, std=0.02)),
+                                       bgb_gpu.MODE_BITNET)
+    assert bgb_gpu.bitlinear_w1a8(torch.zeros((0, K), device="cuda"), P, beta, N).shape == (0, N)
+    for M in (1, 70):
+        x = dev_f32(syn.normal_f32(6, 1, (M, K)))
+        ys = [bgb_gpu.bitlinear_w1a8(x, P, beta, N) for _ in range(5)]
+        torch.cuda.synchronize()
+        for t in ys[1:]:
+            assert torch.equal(ys[0], t)

@@ -1,0 +1,116 @@
+"""GPU parity: fbi_linear_w1a16 (decode kernel for M <= 16, MFMA GEMM above)
+against the fp64 oracle, plus exactness probes that pin the bit layout."""
+import numpy as np
+import pytest
+import torch
+
+import bgb_synth as syn
+from gpu_util import check_w1a16, dev_bits16, dev_f32, say, to_bits
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _x_bits(x_kind, seed, M, K, scale=1.0):
+    a = syn.normal_f32(seed, 1, (M, K)) * np.float32(scale)
+    return syn.f32_to_bf16_bits(a) if x_kind == "bf16" else syn.f32_to_f16_bits(a)
+
+
+def _run(bgb, orc, W, xb, x_kind, y_kind, adt="f32"):
+    K, N = W.shape
+    P, alpha = bgb.binarize_pack(dev_f32(W), bgb.MODE_FBI, TORCH_DT[adt])
+    x = dev_bits16(xb, TORCH_DT[x_kind])
+    y = bgb.fbi_linear_w1a16(x, P, alpha, N, TORCH_DT[y_kind])
+    torch.cuda.synchronize()
+    a_host = alpha.detach().float().cpu().numpy().astype(np.float32)
+    ref = orc.fbi_linear(xb, W, a_host, x_kind)
+    return to_bits(y), ref, a_host
+
+
+CASES = [
+    # (M, K, N): decode (M <= 16) and GEMM (M > 16) paths, ragged N and K tails
+    (1, 768, 768), (8, 768, 768), (3, 96, 65), (16, 160, 300), (5, 4096, 33), (1, 11008, 100),
+    (17, 96, 65), (40, 768, 260), (130, 256, 300), (64, 2048, 520), (200, 352, 513),
+]
+
+
+@pytest.mark.parametrize("M,K,N", CASES)
+@pytest.mark.parametrize("y_kind", ["f32", "bf16"])
+def test_fbi_linear_bf16_parity(bgb_gpu, orc, M, K, N, y_kind):
+    say(f"fbi_linear bf16 M={M} K={K} N={N} y={y_kind}")
+    W = syn.normal_f32(100 + M + K, 0, (K, N), std=0.02)
+    xb = _x_bits("bf16", 100 + M + K, M, K)
+    y, ref, _ = _run(bgb_gpu, orc, W, xb, "bf16", y_kind)
+    check_w1a16(y, ref, y_kind, f"M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 768, 768), (7, 160, 300), (16, 4096, 64), (40, 768, 260), (129, 96, 65)])
+@pytest.mark.parametrize("y_kind", ["f32", "f16"])
+def test_fbi_linear_f16_parity(bgb_gpu, orc, M, K, N, y_kind):
+    say(f"fbi_linear f16 M={M} K={K} N={N} y={y_kind}")
+    W = syn.normal_f32(200 + M, 0, (K, N), std=0.02)
+    xb = _x_bits("f16", 200 + M, M, K)
+    y, ref, _ = _run(bgb_gpu, orc, W, xb, "f16", y_kind, adt="f16")
+    check_w1a16(y, ref, y_kind, f"f16 M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 96, 65), (5, 1024, 300), (16, 4096, 70), (40, 1024, 300), (131, 96, 257)])
+@pytest.mark.parametrize("x_kind", ["bf16", "f16"])
+def test_fbi_linear_integer_activations_bit_exact(bgb_gpu, orc, M, K, N, x_kind):
+    """Integer-valued activations (|x| <= 16) make every partial sum exact in
+    fp32 whatever the order, so the fp32 output must equal fl32(alpha * S)."""
+    say(f"fbi_linear integer-exact {x_kind} M={M} K={K} N={N}")
+    rng = syn.rng_for(300 + M, 2)
+    xf = rng.integers(-16, 17, size=(M, K)).astype(np.float32)
+    xb = syn.f32_to_bf16_bits(xf) if x_kind == "bf16" else syn.f32_to_f16_bits(xf)
+    W = syn.normal_f32(300 + M, 0, (K, N), std=0.02)
+    y, ref, _ = _run(bgb_gpu, orc, W, xb, x_kind, "f32")
+    assert np.array_equal(y.astype(np.float32), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("K,N", [(96, 65), (768, 300), (4096, 20)])
+def test_unit_vector_probes_read_back_signs(bgb_gpu, orc, K, N):
+    """x = e_k gives y_j = alpha_j s_kj exactly: reads row k of the signs through
+    the kernel, pinning bit order and layout without trusting P."""
+    say(f"fbi_linear unit probes K={K} N={N}")
+    W = syn.normal_f32(400 + K, 0, (K, N), std=0.02)
+    ks = sorted(set([0, 1, 15, 16, 17, 31, 32, 63, 64, 100 % K, K - 33, K - 1]))
+    for M in (len(ks[:16]), 40):
+        rows = (ks * 4)[:M]
+        e = np.zeros((M, K), np.float32)
+        e[np.arange(M), rows] = 1.0
+        y, ref, a = _run(bgb_gpu, orc, W, syn.f32_to_bf16_bits(e), "bf16", "f32")
+        S = orc.sign_fbi(W)
+        assert np.array_equal(y.astype(np.float32), (a[None, :] * S[rows].astype(np.float32)))
+
+
+def test_fbi_linear_trained_alpha_and_closed_forms(bgb_gpu, orc):
+    """All-positive weights give y = alpha * sum(x); a caller-supplied alpha is used as is."""
+    say("fbi_linear closed forms")
+    K, N = 256, 48
+    for M in (3, 33):
+        xb = _x_bits("bf16", 7, M, K)
+        xf = syn.bf16_bits_to_f32(xb).astype(np.float64)
+        W = np.full((K, N), 0.5, np.float32)
+        P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI)
+        custom = np.linspace(-2, 3, N).astype(np.float32)
+        y = bgb_gpu.fbi_linear_w1a16(dev_bits16(xb, torch.bfloat16), P, dev_f32(custom), N)
+        torch.cuda.synchronize()
+        ref = xf.sum(1)[:, None] * custom[None, :].astype(np.float64)
+        check_w1a16(to_bits(y), ref, "f32", "closed form")
+
+
+def test_fbi_linear_empty_and_deterministic(bgb_gpu):
+    say("fbi_linear empty + determinism")
+    K, N = 1024, 300
+    W = dev_f32(syn.normal_f32(9, 0, (K, N), std=0.02))
+    P, alpha = bgb_gpu.binarize_pack(W, bgb_gpu.MODE_FBI)
+    x0 = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    assert bgb_gpu.fbi_linear_w1a16(x0, P, alpha, N).shape == (0, N)
+    for M in (4, 64):
+        x = dev_bits16(_x_bits("bf16", 9, M, K), torch.bfloat16)
+        ys = [bgb_gpu.fbi_linear_w1a16(x, P, alpha, N) for _ in range(5)]
+        torch.cuda.synchronize()
+        for t in ys[1:]:
+            assert torch.equal(ys[0], t)
