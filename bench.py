@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Benchmark of the binarized linear layers on one MI355X (gfx950).
+
+Headline (one JSON line on stdout): BitLinear W1A8 decode of one token through
+a 4096 x 11008 layer -- LayerNorm + absmax-quant prologue, then the packed
+1-bit GEMV with its epilogue -- as whole-step throughput in GB/s of algorithmic
+bytes, with the weights rotated over enough distinct copies (> 512 MB) that
+every step streams its packed signs from HBM rather than the 256 MB MALL.
+The timed region replays a HIP graph of exactly K captured steps.
+
+Extra objects on the same line:
+  roofline      the decode GEMV kernel: algorithmic bytes per launch over its
+                average launch duration (per-launch HIP event pairs on the
+                launch stream, queued behind a busy kernel so the GPU never
+                idles between them), against 8 TB/s.
+  cpu_baseline  the CPU oracle on the same workload (one thread, bounded sample).
+  legs          every other hot-path row at its workload: the two weight
+                conversions, W1A16 decode over a 7B-shaped layer (B = 1, 4, 16),
+                the W1A16 and W1A8 prefill GEMMs at 4096 x 4096 x 11008, and a
+                1.3B-shaped 24-layer stack (decode B = 64, prefill 2 x 1024).
+Progress lines go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+METRIC = "packed-W1 GEMV HBM GB/s (% of peak); W1 GEMM TFLOP/s/TOP/s (% MFMA peak)"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000, help="timed steps of the headline workload")
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--rotate-mb", type=float, default=640.0, help="packed weight bytes in the rotation")
+    ap.add_argument("--legs", default="all", help="comma list of extra legs, 'all' or 'none'")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- timing ----
+
+def graph_time(torch, body, steps, warmup):
+    """Capture `steps` calls of body(i) into one HIP graph; replay once untimed
+    (warm-up, also `warmup` eager calls before capture) and once timed.
+    Returns milliseconds for the timed replay."""
+    for i in range(warmup):
+        body(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            body(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del g
+    return ms
+
+
+def per_launch_ms(torch, launch, n, busy_mb=1024):
+    """Average device duration of launch(i) from event pairs around each call.
+    A long copy is queued first so all n calls are enqueued before the GPU
+    reaches them: each event pair then brackets only the kernel(s)."""
+    a = torch.empty(int(busy_mb * 2**20) // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for _ in range(max(16, n // 10)):          # ~0.4 ms each: longer than enqueueing n calls
+        b.copy_(a)
+    for i in range(n):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    d = sorted(s.elapsed_time(e) for s, e in ev)
+    del a, b
+    return sum(d) / n, d[len(d) // 2]
+
+
+# ---------------------------------------------------------- headline leg ----
+
+def headline(torch, bgb, syn, args):
+    cfg = syn.CONFIGS["bitlinear_decode_4096x11008"]
+    K, N, M, seed = cfg["K"], cfg["N"], cfg["M"], cfg["seed"]
+    W_host = syn.normal_f32(seed, 0, (K, N), mean=cfg["w_mean"], std=cfg["w_std"])
+    x_host = syn.normal_f32(seed, 1, (M, K))
+    P0, beta, centre = bgb.binarize_pack(torch.from_numpy(W_host).cuda(), bgb.MODE_BITNET)
+    pbytes = bgb.packed_bytes(K, N)
+    R = max(2, math.ceil(args.rotate_mb * 1e6 / pbytes))
+    Ps = [P0] + [P0.clone() for _ in range(R - 1)]
+    x = torch.from_numpy(x_host).cuda()
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(bgb.workspace_bytes(bgb.OP_BITLINEAR, M, K, N), 256), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        bgb.bitlinear_w1a8(x, Ps[i % R], beta, N, y=y, ws=ws)
+
+    log(f"headline: BitLinear W1A8 decode M={M} K={K} N={N}, {R} weight copies ({R * pbytes / 1e6:.0f} MB)")
+    ms = graph_time(torch, step, args.steps, args.warmup)
+    ms_step = ms / args.steps
+    step_bytes = pbytes + M * K * 4 + M * N * 4          # packed signs + x (f32) + y (f32)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"headline: {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s")
+
+    # roofline of the dominant kernel: the GEMV (bitlinear_matmul) alone
+    bgb.bitlinear_quantize(x, ws=ws)
+    n = min(400, 4 * R)
+
+    def mm(i):
+        bgb.bitlinear_matmul(M, K, Ps[i % R], beta, N, ws=ws, y=y)
+
+    for i in range(50):
+        mm(i)
+    avg_ms, med_ms = per_launch_ms(torch, mm, n)
+    kbytes = pbytes + M * bgb_padded_k(K) + M * N * 4    # signs + codes + y
+    achieved = kbytes / (avg_ms * 1e-3) / 1e9
+    roof = {"kernel": "gemv_w1a8_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None, "bytes_per_launch": kbytes, "avg_launch_us": round(avg_ms * 1e3, 3),
+            "median_launch_us": round(med_ms * 1e3, 3), "launches": n}
+    log(f"headline: GEMV kernel {avg_ms * 1e3:.2f} us avg ({med_ms * 1e3:.2f} median), {achieved:.1f} GB/s")
+
+    # correctness spot check of the timed configuration against the first copy
+    y_ref = bgb.bitlinear_w1a8(x, P0, beta, N)
+    bgb.bitlinear_w1a8(x, Ps[R - 1], beta, N, y=y, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref), "rotated copy disagrees"
+
+    state = dict(W=W_host, x=x_host, K=K, N=N, M=M, step_bytes=step_bytes)
+    del Ps
+    return ms_step, value, roof, R, state
+
+
+def bgb_padded_k(K):
+    return ((K // 32 + 3) // 4) * 128
+
+
+# ------------------------------------------------------------ cpu baseline ----
+
+def cpu_baseline(state, seconds):
+    import numpy as np
+    import oracle
+    W, x = state["W"], state["x"]
+    c, beta = oracle.bitnet_scalars(W)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        q, g, _, _ = oracle.ln_absmax_quant(x)
+        acc = oracle.bitlinear_acc(q, W, c)
+        oracle.bitlinear_out(acc, beta, g)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    value = state["step_bytes"] / dt / 1e9
+    log(f"cpu oracle: {dt * 1e3:.1f} ms/step over {n} steps")
+    return {"value": round(value, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full decode steps (M=1, K=4096, N=11008: LN+quant, integer product, output) "
+                      f"in {n * dt:.1f} s, plain single-thread C oracle", "ms_per_step": round(dt * 1e3, 2)}
+
+
+# ------------------------------------------------------------------ legs ----
+
+def leg_pack(torch, bgb, syn):
+    out = {}
+    K, N = 4096, 11008
+    W = syn.gpu_normal(3, 0, (K, N), mean=0.001, std=0.02)
+    pbytes = bgb.packed_bytes(K, N)
+    for name, mode in (("pack_fbi_4096x11008", bgb.MODE_FBI), ("pack_bitnet_4096x11008", bgb.MODE_BITNET)):
+        ws = torch.empty(max(bgb.workspace_bytes(mode, 0, K, N), 256), dtype=torch.uint8, device="cuda")
+        P = torch.empty(pbytes // 4, dtype=torch.int32, device="cuda")
+        alpha = torch.empty(N, dtype=torch.float32, device="cuda")
+        beta = torch.empty(4, dtype=torch.float32, device="cuda")
+        cen = torch.empty(4, dtype=torch.float32, device="cuda")
+
+        def body(i):
+            bgb.binarize_pack(W, mode, P=P, alpha=alpha, beta=beta, centre=cen, ws=ws)
+
+        steps = 20
+        ms = graph_time(torch, body, steps, 3) / steps
+        reads = K * N * 4 * (1 if mode == bgb.MODE_FBI else 2)
+        nbytes = reads + pbytes + (N * 4 if mode == bgb.MODE_FBI else 8)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                     "bytes": nbytes, "bound": "hbm"}
+        log(f"{name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    return out
+
+
+def build_layer(torch, bgb, syn, seed, shapes, layer, alpha_dtype):
+    Ps, alphas = [], []
+    for li, (_, K, N) in enumerate(shapes):
+        W = syn.gpu_normal(seed, 100 * layer + li, (K, N), std=0.02)
+        P, a = bgb.binarize_pack(W, bgb.MODE_FBI, alpha_dtype)
+        Ps.append(P)
+        alphas.append(a)
+        del W
+    return Ps, alphas
+
+
+def leg_decode_7b(torch, bgb, syn, steps):
+    cfg = syn.CONFIGS["w1a16_decode_7b_layer"]
+    shapes = cfg["shapes"]
+    L = 32                                              # distinct layer copies: 809 MB of signs
+    P1, A1 = build_layer(torch, bgb, syn, cfg["seed"], shapes, 0, torch.float16)
+    layers = [(P1, A1)] + [([p.clone() for p in P1], A1) for _ in range(L - 1)]
+    pbytes = sum(bgb.packed_bytes(K, N) for _, K, N in shapes)
+    abytes = sum(2 * N for _, K, N in shapes)
+    out = {}
+    for B in cfg["batches"]:
+        xs = {K: torch.randn((B, K), device="cuda").to(torch.bfloat16) for K in (4096, 11008)}
+        ys = {N: torch.empty((B, N), dtype=torch.bfloat16, device="cuda") for N in (4096, 11008)}
+        wsz = max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, B, K, N) for _, K, N in shapes)
+        ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
+
+        def body(i, B=B, xs=xs, ys=ys, ws=ws):
+            Ps, As = layers[i % L]
+            for li, (_, K, N) in enumerate(shapes):
+                bgb.fbi_linear_w1a16(xs[K], Ps[li], As[li], N, y=ys[N], ws=ws)
+
+        n = steps
+        ms = graph_time(torch, body, n, 4) / n
+        xb = sum(2 * B * K for _, K, N in shapes)
+        yb = sum(2 * B * N for _, K, N in shapes)
+        nbytes = pbytes + abytes + xb + yb
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"w1a16_decode_7b_layer_b{B}"] = {
+            "us_per_layer": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_layer": nbytes, "bound": "hbm", "layer_copies": L, "launches_per_layer": 14}
+        log(f"decode 7B layer B={B}: {ms * 1e3:.1f} us/layer, {gbs:.0f} GB/s")
+    del layers
+    return out
+
+
+def leg_prefill(torch, bgb, syn):
+    cfg = syn.CONFIGS["w1_prefill_4096x4096x11008"]
+    M, K, N, seed = cfg["M"], cfg["K"], cfg["N"], cfg["seed"]
+    W = syn.gpu_normal(seed, 0, (K, N), std=cfg["w_std"])
+    x = syn.gpu_normal(seed, 1, (M, K)).to(torch.bfloat16)
+    flops = 2 * M * K * N
+    out = {}
+    P, alpha = bgb.binarize_pack(W, bgb.MODE_FBI)
+    y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def f16(i):
+        bgb.fbi_linear_w1a16(x, P, alpha, N, y=y16)
+
+    ms = graph_time(torch, f16, 10, 3) / 10
+    tf = flops / (ms * 1e-3) / 1e12
+    out["w1a16_prefill_gemm_4096x4096x11008"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                                 "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
+                                                 "flops": flops, "bound": "mfma"}
+    log(f"W1A16 prefill GEMM: {ms * 1e3:.0f} us, {tf:.0f} TFLOP/s")
+    Pb, beta, _ = bgb.binarize_pack(W, bgb.MODE_BITNET)
+    y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bgb.workspace_bytes(bgb.OP_BITLINEAR, M, K, N), dtype=torch.uint8, device="cuda")
+
+    def f8(i):
+        bgb.bitlinear_w1a8(x, Pb, beta, N, y=y32, ws=ws)
+
+    ms = graph_time(torch, f8, 10, 3) / 10
+    bgb.bitlinear_quantize(x, ws=ws)
+
+    def m8(i):
+        bgb.bitlinear_matmul(M, K, Pb, beta, N, ws=ws, y=y32)
+
+    ms_mm = graph_time(torch, m8, 10, 3) / 10
+    t8 = flops / (ms_mm * 1e-3) / 1e12
+    out["w1a8_prefill_gemm_4096x4096x11008"] = {
+        "ms_gemm": round(ms_mm, 4), "TOP/s": round(t8, 1), "frac_mfma_int8": round(t8 / INT8_PEAK_TOPS, 4),
+        "ms_with_prologue": round(ms, 4), "ops": flops, "bound": "mfma"}
+    log(f"W1A8 prefill GEMM: {ms_mm * 1e3:.0f} us ({ms * 1e3:.0f} with prologue), {t8:.0f} TOP/s")
+    return out
+
+
+def leg_stack_1p3b(torch, bgb, syn):
+    cfg = syn.CONFIGS["w1a16_1p3b_stack"]
+    shapes, L = cfg["shapes"], cfg["layers"]
+    layers = [build_layer(torch, bgb, syn, cfg["seed"], shapes, l, torch.float16) for l in range(L)]
+    out = {}
+    for name, M in (("decode_b64", cfg["decode_batch"]), ("prefill_2x1024", cfg["prefill_tokens"])):
+        xs = {K: torch.randn((M, K), device="cuda").to(torch.bfloat16) for K in (2048, 5632)}
+        ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N in (2048, 5632)}
+        ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+        def body(i, xs=xs, ys=ys, ws=ws):
+            for Ps, As in layers:
+                for li, (_, K, N) in enumerate(shapes):
+                    bgb.fbi_linear_w1a16(xs[K], Ps[li], As[li], N, y=ys[N], ws=ws)
+
+        n = 10 if M <= 64 else 3
+        # cold: flush the MALL between steps is not possible inside one graph;
+        # this is the warm number (154 MB of signs stay resident across steps)
+        ms = graph_time(torch, body, n, 2) / n
+        flops = 2 * M * sum(K * N for _, K, N in shapes) * L
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"w1a16_1p3b_stack_{name}"] = {"ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                           "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops,
+                                           "linears": L * len(shapes), "bound": "mfma"}
+        log(f"1.3B stack {name}: {ms * 1e3:.0f} us/step, {tf:.0f} TFLOP/s")
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path; see DESIGN.md for how the layer would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bgb_synth as syn
+    import bit_gemm_binarize_amd as bgb
+    bgb.load()
+    torch.cuda.set_device(0)
+    torch.backends.cuda.matmul.allow_tf32 = False
+
+    ms_step, value, roof, R, state = headline(torch, bgb, syn, args)
+
+    legs = {}
+    want = set() if args.legs == "none" else (
+        {"pack", "decode7b", "prefill", "stack"} if args.legs == "all" else set(args.legs.split(",")))
+    if "pack" in want:
+        legs.update(leg_pack(torch, bgb, syn))
+        torch.cuda.empty_cache()
+    if "decode7b" in want:
+        legs.update(leg_decode_7b(torch, bgb, syn, 64))
+        torch.cuda.empty_cache()
+    if "prefill" in want:
+        legs.update(leg_prefill(torch, bgb, syn))
+        torch.cuda.empty_cache()
+    if "stack" in want:
+        legs.update(leg_stack_1p3b(torch, bgb, syn))
+        torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(state, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic: seeded N(0.001, 0.02) fp32 weights packed to 1 bit, N(0,1) fp32 activations",
+        "config": {"workload": "bitlinear_w1a8_decode_4096x11008", "M": state["M"], "K": state["K"],
+                   "N": state["N"], "x_dtype": "f32", "weight_copies": R,
+                   "step": "LN+absmax prologue kernel + packed GEMV kernel (one HIP graph of all steps)"},
+        "roofline": roof, "cpu_baseline": cpu, "legs": legs,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

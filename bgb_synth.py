@@ -90,3 +90,19 @@ CONFIGS = {
     "w1a16_1p3b_stack": dict(seed=4, layers=24, shapes=LINEAR_SHAPES_1P3B, decode_batch=64,
                              prefill_tokens=2048, w_std=0.02),
 }
+
+
+def gpu_normal(seed: int, tensor_id: int, shape, mean: float = 0.0, std: float = 1.0, device="cuda"):
+    """Seeded normal float32 tensor drawn directly on the GPU (torch's Philox
+    generator seeded with seed * 1000 + tensor_id). Used for the large
+    benchmark-only weight stacks, where host generation would dominate setup;
+    parity tests use the numpy draws above."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000 + int(tensor_id))
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    if mean != 0.0:
+        t.add_(mean)
+    return t

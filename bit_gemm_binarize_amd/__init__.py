@@ -19,7 +19,7 @@ from typing import Optional
 
 __all__ = [
     "load", "lib_path", "packed_bytes", "workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
-    "bitlinear_w1a8", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
+    "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
     "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M",
 ]
 
@@ -32,7 +32,8 @@ OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR = 0, 1, 2, 3
 GEMV_MAX_M = 16
 
 EXPORTS = ("bgb_packed_bytes", "bgb_workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
-           "bitlinear_w1a8", "bgb_status_string", "bgb_last_hip_error", "bgb_version")
+           "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bgb_status_string",
+           "bgb_last_hip_error", "bgb_version")
 
 
 class BgbError(RuntimeError):
@@ -78,6 +79,10 @@ def load():
     lib.fbi_linear_w1a16.restype = I
     lib.bitlinear_w1a8.argtypes = [P, I, I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, P, P, SZ, P]
     lib.bitlinear_w1a8.restype = I
+    lib.bitlinear_quantize.argtypes = [P, I, I64, I64, ctypes.POINTER(_QP), P, P, P, SZ, P]
+    lib.bitlinear_quantize.restype = I
+    lib.bitlinear_matmul.argtypes = [I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, SZ, P]
+    lib.bitlinear_matmul.restype = I
     lib.bgb_status_string.argtypes = [I]
     lib.bgb_status_string.restype = ctypes.c_char_p
     lib.bgb_last_hip_error.argtypes = []
@@ -199,3 +204,31 @@ def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=No
     if want_acc:
         extras["acc"] = acc
     return y, extras
+
+
+def bitlinear_quantize(x, qp: Optional[QuantParams] = None, *, ws, N_max: int = 0, want_q=False, want_gamma=False,
+                       stream=None):
+    """Prologue only: leaves the codes in `ws` for bitlinear_matmul. Returns the requested taps."""
+    torch = _torch()
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if want_q else None
+    g = torch.empty(4, dtype=torch.float32, device=x.device) if want_gamma else None
+    qp = qp or QuantParams()
+    cqp = _QP(float(qp.ln_eps), int(qp.bits), float(qp.q_eps))
+    _check(load().bitlinear_quantize(_ptr(x), _dt(x), M, K, ctypes.byref(cqp), _ptr(q), _ptr(g), _ptr(ws),
+                                     ws.numel(), _stream(stream)))
+    return {"q": q, "gamma": None if g is None else g[:1]}
+
+
+def bitlinear_matmul(M: int, K: int, P, beta, N: int, qp: Optional[QuantParams] = None, *, ws, y=None,
+                     want_acc=False, stream=None):
+    """Product + epilogue from the codes a previous bitlinear_quantize left in `ws`."""
+    torch = _torch()
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=ws.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=ws.device) if want_acc else None
+    qp = qp or QuantParams()
+    cqp = _QP(float(qp.ln_eps), int(qp.bits), float(qp.q_eps))
+    _check(load().bitlinear_matmul(M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y), _ptr(acc), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+    return (y, acc) if want_acc else y

@@ -57,9 +57,10 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P, v
     int rc = check_shape(0, K, N);
     if (rc) return rc;
     if (mode != BGB_MODE_FBI && mode != BGB_MODE_BITNET) return BGB_EUNSUPPORTED;
+    if (mode == BGB_MODE_FBI && alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (N == 0) return BGB_OK;                    // empty: nothing is read or written
     if (!W || !P || !aligned16(W) || !aligned16(P)) return BGB_EINVAL;
     if (mode == BGB_MODE_FBI) {
-        if (alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
         if (!alpha || !aligned16(alpha)) return BGB_EINVAL;
     } else {
         if (!beta || !centre || !aligned16(beta) || !aligned16(centre)) return BGB_EINVAL;
@@ -67,7 +68,6 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P, v
     const int op = mode == BGB_MODE_FBI ? BGB_OP_PACK_FBI : BGB_OP_PACK_BITNET;
     const size_t need = bgb_workspace_bytes(op, 0, K, N);
     if (need && (!ws || ws_bytes < need || !aligned16(ws))) return BGB_EINVAL;
-    if (N == 0) return BGB_OK;
     return finish(bgb::launch_pack(W, K, N, mode, P, alpha, alpha_dtype == BGB_F16, beta, centre, ws,
                                    static_cast<hipStream_t>(stream)));
 }
@@ -80,11 +80,11 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
     if (x_dtype != BGB_BF16 && x_dtype != BGB_F16) return BGB_EUNSUPPORTED;
     if (alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
     if (y_dtype != BGB_F32 && y_dtype != BGB_BF16 && y_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (M == 0 || N == 0) return BGB_OK;          // empty: nothing is read or written
     if (!x || !P || !alpha || !y) return BGB_EINVAL;
     if (!aligned16(x) || !aligned16(P) || !aligned16(alpha) || !aligned16(y)) return BGB_EINVAL;
     const bgb::FbiLinearWs lay = bgb::FbiLinearWs::make(M, K);
     if (lay.total && (!ws || ws_bytes < lay.total || !aligned16(ws))) return BGB_EINVAL;
-    if (M == 0 || N == 0) return BGB_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int x_f16 = x_dtype == BGB_F16;
     const int a_f16 = alpha_dtype == BGB_F16;
@@ -99,17 +99,72 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
     return finish(bgb::launch_w1a16_gemm(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
 }
 
+// Shared checks of the BitLinear entry points; fills qb/lim from qp.
+static int bitlinear_params(const bgb_quant_params* qp, bgb_quant_params* p, float* qb, float* lim) {
+    *p = bgb_quant_params{1e-5, 8, 1e-3f};
+    if (qp) *p = *qp;
+    if (p->bits < 2 || p->bits > 8) return BGB_EUNSUPPORTED;
+    if (!(p->ln_eps >= 0.0) || !(p->q_eps >= 0.0f) || !(p->q_eps < 1.0f)) return BGB_EINVAL;
+    *qb = float(1 << (p->bits - 1));
+    *lim = *qb - p->q_eps;                       // fl32(Q_b - eps), as the reference computes it
+    return BGB_OK;
+}
+
+int bitlinear_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const bgb_quant_params* qp,
+                       int8_t* xq_opt, float* gamma_opt, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(M, K, 0);
+    if (rc) return rc;
+    if (x_dtype != BGB_F32 && x_dtype != BGB_BF16) return BGB_EUNSUPPORTED;
+    bgb_quant_params p;
+    float qb, lim;
+    if ((rc = bitlinear_params(qp, &p, &qb, &lim))) return rc;
+    if (M == 0) return BGB_OK;                    // empty: nothing is read or written
+    if (!x || !aligned16(x)) return BGB_EINVAL;
+    if ((gamma_opt && (reinterpret_cast<uintptr_t>(gamma_opt) & 3u)) || (xq_opt && !aligned16(xq_opt)))
+        return BGB_EINVAL;
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
+    if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
+    const bool decode = M <= bgb::kGemvMaxM;
+    return finish(bgb::launch_ln_quant(x, x_dtype == BGB_BF16, M, K, p.ln_eps, qb, lim, decode ? 0 : 1,
+                                       reinterpret_cast<int8_t*>(carve(ws, lay.q)),
+                                       reinterpret_cast<int32_t*>(carve(ws, lay.rowsum)),
+                                       reinterpret_cast<float*>(carve(ws, lay.stats)),
+                                       reinterpret_cast<float*>(carve(ws, lay.gamma)), xq_opt, gamma_opt,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
+                     const bgb_quant_params* qp, float* y, int32_t* acc_opt, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int rc = check_shape(M, K, N);
+    if (rc) return rc;
+    bgb_quant_params p;
+    float qb, lim;
+    if ((rc = bitlinear_params(qp, &p, &qb, &lim))) return rc;
+    if (M == 0 || N == 0) return BGB_OK;          // empty: nothing is read or written
+    if (!P || !beta || !y || !aligned16(P) || !aligned16(y)) return BGB_EINVAL;
+    if (reinterpret_cast<uintptr_t>(beta) & 3u) return BGB_EINVAL;
+    if (acc_opt && !aligned16(acc_opt)) return BGB_EINVAL;
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
+    if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int8_t* q = reinterpret_cast<const int8_t*>(carve(ws, lay.q));
+    const int32_t* rowsum = reinterpret_cast<const int32_t*>(carve(ws, lay.rowsum));
+    const float* gamma = reinterpret_cast<const float*>(carve(ws, lay.gamma));
+    if (M <= bgb::kGemvMaxM) return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
+    return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
+}
+
 int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
                    const float* beta, const bgb_quant_params* qp, float* y, int8_t* xq_opt, float* gamma_opt,
                    int32_t* acc_opt, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_shape(M, K, N);
     if (rc) return rc;
     if (x_dtype != BGB_F32 && x_dtype != BGB_BF16) return BGB_EUNSUPPORTED;
-    bgb_quant_params p = {1e-5, 8, 1e-3f};
-    if (qp) p = *qp;
-    if (p.bits < 2 || p.bits > 8) return BGB_EUNSUPPORTED;
-    const float qb = float(1 << (p.bits - 1));
-    if (!(p.ln_eps >= 0.0) || !(p.q_eps >= 0.0f) || !(p.q_eps < 1.0f)) return BGB_EINVAL;
+    bgb_quant_params p;
+    float qb, lim;
+    if ((rc = bitlinear_params(qp, &p, &qb, &lim))) return rc;
+    if (M == 0 || N == 0) return BGB_OK;          // empty: nothing is read or written
     if (!x || !P || !beta || !y) return BGB_EINVAL;
     if (!aligned16(x) || !aligned16(P) || !aligned16(y)) return BGB_EINVAL;
     if ((reinterpret_cast<uintptr_t>(beta) & 3u) || (gamma_opt && (reinterpret_cast<uintptr_t>(gamma_opt) & 3u)))
@@ -117,19 +172,9 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, 
     if ((xq_opt && !aligned16(xq_opt)) || (acc_opt && !aligned16(acc_opt))) return BGB_EINVAL;
     const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
-    if (M == 0 || N == 0) return BGB_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const float lim = qb - p.q_eps;               // fl32(Q_b - eps), as the reference computes it
-    float* stats = reinterpret_cast<float*>(carve(ws, lay.stats));
-    float* gamma = reinterpret_cast<float*>(carve(ws, lay.gamma));
-    int32_t* rowsum = reinterpret_cast<int32_t*>(carve(ws, lay.rowsum));
-    int8_t* q = reinterpret_cast<int8_t*>(carve(ws, lay.q));
-    const bool decode = M <= bgb::kGemvMaxM;
-    hipError_t e = bgb::launch_ln_quant(x, x_dtype == BGB_BF16, M, K, p.ln_eps, qb, lim, decode ? 0 : 1, q, rowsum,
-                                        stats, gamma, xq_opt, gamma_opt, s);
-    if (e != hipSuccess) return finish(e);
-    if (decode) return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
-    return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
+    rc = bitlinear_quantize(x, x_dtype, M, K, qp, xq_opt, gamma_opt, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return bitlinear_matmul(M, K, N, P, beta, qp, y, acc_opt, ws, ws_bytes, stream);
 }
 
 const char* bgb_status_string(int status) {

@@ -25,7 +25,8 @@
  *   row-major and contiguous. y = x . W_b (scaled), i.e. the same product as
  *   a linear layer with in_features = K and out_features = N.
  * - K must be a positive multiple of 32. M == 0 or N == 0 is a valid empty
- *   call that launches nothing. Limits: K <= 524288, M <= 2^24, N <= 2^24,
+ *   call that launches nothing (its array pointers may then be NULL; shapes,
+ *   dtypes and parameters are still checked). Limits: K <= 524288, M <= 2^24, N <= 2^24,
  *   and M*K, K*N, M*N each < 2^31 elements.
  * - Every pointer argument is a DEVICE pointer on the current HIP device,
  *   16-byte aligned, owned by the caller. The library allocates nothing and
@@ -123,7 +124,6 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
  * accumulation on the matrix cores; alpha is applied once to the fp32 sum.
  * M <= 16 runs the memory-bound decode kernel, M > 16 the MFMA GEMM.
  * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes.
- * Activations with |x| >= 2^124 are outside the supported range.
  * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP.
  */
 int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
@@ -152,6 +152,26 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
                    const uint32_t* P, const float* beta, const bgb_quant_params* qp,
                    float* y, int8_t* xq_opt, float* gamma_opt, int32_t* acc_opt,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bitlinear_quantize + bitlinear_matmul -- the two stages of bitlinear_w1a8,
+ * for callers that apply several BitLinear weights to one input (the
+ * q/k/v or gate/up projections of a block share theirs).
+ * bitlinear_quantize runs the prologue (LN, gamma, codes) for x [M][K] and
+ * leaves the codes, their row sums and gamma in `ws` (sized by
+ * bgb_workspace_bytes(BGB_OP_BITLINEAR, M, K, N) for the largest N used);
+ * xq_opt / gamma_opt are optional copies as above.
+ * bitlinear_matmul then computes y (and optionally acc) for one packed weight
+ * from that workspace; M, K and qp->bits must match the quantize call, and
+ * the two calls must be ordered on one stream. bitlinear_w1a8 is exactly
+ * bitlinear_quantize followed by bitlinear_matmul.
+ */
+int bitlinear_quantize(const void* x, int x_dtype, int64_t M, int64_t K,
+                       const bgb_quant_params* qp, int8_t* xq_opt, float* gamma_opt,
+                       void* ws, size_t ws_bytes, void* stream);
+int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
+                     const bgb_quant_params* qp, float* y, int32_t* acc_opt,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* Message for a status code (static string). */
 const char* bgb_status_string(int status);

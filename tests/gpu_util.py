@@ -56,18 +56,26 @@ def normwise_row_err(y: np.ndarray, ref: np.ndarray) -> np.ndarray:
 
 
 def check_w1a16(y: np.ndarray, ref: np.ndarray, y_kind: str, tag: str = ""):
+    """fp32 outputs: normwise per row <= 2e-3. 16-bit outputs carry one more
+    rounding (unit roundoff 2^-8 for bf16, 2^-11 for f16), so each element
+    must lie within 2e-3 * rowmax + half an ulp of the fp64 value, and within
+    one ulp of it."""
     err = normwise_row_err(y, ref)
-    assert np.all(err <= W1A16_NORMWISE_TOL), f"{tag} normwise err {err.max():.3e}"
-    if y_kind in ("bf16", "f16"):
+    if y_kind == "f32":
+        assert np.all(err <= W1A16_NORMWISE_TOL), f"{tag} normwise err {err.max():.3e}"
+    else:
         mant = 7 if y_kind == "bf16" else 10
         a = np.abs(ref)
         e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
         if y_kind == "f16":
             e = np.maximum(e, -14)
         ulp = np.exp2(e - mant)
-        slack = 1e-5 * np.max(np.abs(ref), axis=1, keepdims=True)
-        bad = np.abs(y - ref) > ulp + slack
-        assert not np.any(bad), f"{tag} {int(bad.sum())} outputs beyond 1 ulp"
+        rowmax = np.max(np.abs(ref), axis=1, keepdims=True)
+        d = np.abs(y - ref)
+        bad = d > W1A16_NORMWISE_TOL * rowmax + 0.5 * ulp
+        assert not np.any(bad), f"{tag} {int(bad.sum())} outputs beyond 2e-3*rowmax + ulp/2"
+        bad1 = d > ulp + 1e-6 * rowmax
+        assert not np.any(bad1), f"{tag} {int(bad1.sum())} outputs beyond 1 ulp"
     return float(err.max()) if err.size else 0.0
 
 
