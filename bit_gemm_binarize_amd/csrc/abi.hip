@@ -89,6 +89,8 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
     const int x_f16 = x_dtype == BGB_F16;
     const int a_f16 = alpha_dtype == BGB_F16;
     const int ydt = y_dtype == BGB_F32 ? 0 : (y_dtype == BGB_F16 ? 1 : 2);
+    if (M == 1 && bgb::w1a16_decode1_supported(K))
+        return finish(bgb::launch_w1a16_decode1(x, x_f16, K, N, P, alpha, a_f16, y, ydt, s));
     if (M <= bgb::kGemvMaxM) {
         uint16_t* xp = reinterpret_cast<uint16_t*>(carve(ws, lay.xp));
         float* xsum = reinterpret_cast<float*>(carve(ws, lay.xsum));
@@ -172,6 +174,10 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, 
     if ((xq_opt && !aligned16(xq_opt)) || (acc_opt && !aligned16(acc_opt))) return BGB_EINVAL;
     const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
+    if (M == 1 && bgb::w1a8_decode1_supported(K)) {
+        return finish(bgb::launch_w1a8_decode1(x, x_dtype == BGB_BF16, K, N, p.ln_eps, qb, lim, P, beta, y, acc_opt,
+                                               xq_opt, gamma_opt, static_cast<hipStream_t>(stream)));
+    }
     rc = bitlinear_quantize(x, x_dtype, M, K, qp, xq_opt, gamma_opt, ws, ws_bytes, stream);
     if (rc) return rc;
     return bitlinear_matmul(M, K, N, P, beta, qp, y, acc_opt, ws, ws_bytes, stream);

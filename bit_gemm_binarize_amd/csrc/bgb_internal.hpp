@@ -9,7 +9,8 @@
 namespace bgb {
 
 constexpr int kWords4 = 4;             // words per 16-byte column tile (128 rows)
-constexpr int kGemvMaxM = 16;          // M <= 16 -> decode kernels
+constexpr int kGemvMaxM = 64;          // M <= 64 -> decode (streaming) kernels
+constexpr int kSmallPrologueM = 16;    // M <= 16 -> single-block LN + quant prologue
 constexpr int kMaxK = 524288;
 
 inline int64_t words_per_col(int64_t K) { return K / 32; }                // T
@@ -90,6 +91,15 @@ hipError_t launch_w1a16_gemm(const void* x, int x_f16, int64_t M, int64_t K, int
 hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             const float* beta, float qb, int64_t M, int64_t K, int64_t N,
                             const uint32_t* P, float* y, int32_t* acc_opt, hipStream_t s);
+
+// Single-token fused kernels (prologue / activation staging inside the GEMV).
+bool w1a8_decode1_supported(int64_t K);
+hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
+                               const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
+                               float* gamma_opt, hipStream_t s);
+bool w1a16_decode1_supported(int64_t K);
+hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             const float* beta, float qb, int64_t M, int64_t K, int64_t N,

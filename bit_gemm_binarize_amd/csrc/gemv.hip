@@ -1,74 +1,351 @@
-// Decode kernels (M <= 16): stream the packed signs once from HBM and run the
-// contraction on the matrix cores with the batch padded to 16 tokens.
+// Decode kernels (M <= 64): stream the packed signs once from HBM and run the
+// contraction on the matrix cores, tokens padded to 16-token fragments.
 //
 // FBI-linear W1A16 (FBI-LLM news rewrite, FBI-linear paragraph):
 //   y[m][j] = alpha_j * sum_k s_kj x[m][k]
-// BitLinear W1A8 ("BitNet b1.58: 1bit LLM时代", section 一, eq. (7)):
+// BitLinear W1A8 ("BitNet b1.58: 1bit LLM时代", section 一, eq. (4)-(8)):
 //   acc[m][j] = sum_k s_kj q[m][k];  y = acc * beta * gamma / Q_b
 //
-// Work split: a block of 4 waves owns 16 output columns. Each wave takes
-// every 4th "step" of 4 column tiles (512 rows); in a step lane group g
-// (lanes 16g..16g+15) loads the 16-byte tile (4 words, 128 rows) of column
-// j0 + (lane % 16) in tile 4*step + g, so one load instruction moves 1 KB.
-// The MFMA A operand is built from these words (rows of A = columns j), the
-// B operand is the activation slice of token (lane % 16); the 4 waves' partial
-// sums are added in a fixed order through LDS.
+// Work split: a block of 4 waves owns 16 output columns. The column's tiles
+// are taken 4 at a time ("steps" of 512 rows): in a step, lane group g (lanes
+// 16g..16g+15) loads the 16-byte tile (4 words, 128 rows) of column
+// j0 + (lane % 16) from tile 4*step + g, so one load instruction moves 1 KB.
+// Wave w takes steps w, w+4, w+8, ... and issues the loads of up to 8 of its
+// steps before it decodes any of them, so a whole layer's signs are in flight
+// at once. The MFMA A operand is decoded from these words in registers (rows
+// of A = output columns), the B operand holds 16 tokens' activations; the 4
+// waves' partial sums are added in a fixed order through LDS.
 //
-// Sign decoding, written so that the only per-weight work is one AND (W1A8)
-// or one AND-OR (W1A16) per pair/quad of weights:
+// Sign decoding keeps the per-weight work to one bitwise op per 2 or 4 weights:
 // * W1A8: with b = 1 for +1, sum_k s q = 2 sum_k b q - sum_k q. The int8 MFMA
-//   for shift s takes bytes (word & (0x01010101 << s)) -- the value 2^s b, or
-//   -128 b for s = 7 -- from the 4 words of the tile, so it accumulates
-//   2^s sum b q exactly; the 8 accumulators are shifted back and added.
-// * W1A16: a 16-bit float whose exponent field is set and one low field bit
-//   b is free encodes a + c b. MFMA u (0..15) takes bit u and bit u + 16 of
-//   each word, moved by a per-u constant shift into field bit p = P0 + u % 4
-//   (one shift per word for four MFMAs): p = P0..P0+2 are mantissa bits over a
-//   base of 1.0 (a = 1, c = 1/8, 1/4, 1/2), p = P0+3 is the exponent's lowest
-//   bit over a base of 0.5 (a = 1/2, c = 1/2). MFMAs of one type T = u % 4 share
-//   an accumulator acc_T = a_T X_T + c_T sum_{k in T} b x, with X_T the sum of x
-//   over the rows of type T (rows k with k % 4 == T), so
-//   sum_k b x = sum_T (acc_T - a_T X_T) / c_T, exact scalings by powers of two.
+//   for shift s takes bytes (word & (0x01010101 << s)) -- 2^s b, or -128 b for
+//   s = 7 -- from the 4 words of the tile, so it accumulates 2^s sum b q
+//   exactly; the 8 accumulators are shifted back and added.
+// * W1A16: a 16-bit float whose exponent field is set and one low field bit b
+//   free encodes a + c b. MFMA u (0..15) takes bit u and bit u + 16 of each
+//   word, moved by a per-u constant shift into field bit p = P0 + u % 4 (one
+//   shift per word serves four MFMAs): p = P0..P0+2 are mantissa bits over a
+//   base of 1.0 (a = 1; c = 1/8, 1/4, 1/2), p = P0+3 is the exponent's lowest
+//   bit over a base of 0.5 (a = 1/2, c = 1/2). MFMAs of one type T = u % 4
+//   share an accumulator acc_T = a_T X_T + c_T sum_{k in T} b x, with X_T the
+//   sum of x over the rows of type T (k % 4 == T), so
+//   sum_k b x = sum_T (acc_T - a_T X_T) / c_T, all scalings powers of two.
+//
+// Single-token calls (M == 1, the common decode case) fuse the activation
+// side into the same launch: every block first issues its weight loads, then
+// builds the activation operand in LDS (BitLinear: LayerNorm, absmax and the
+// int8 codes; FBI-linear: the permuted bf16/f16 row and the four X_T) while
+// the signs are in flight. Each block repeats that small prologue; its
+// results are identical in every block.
 #include "bgb_device.hpp"
 #include "bgb_internal.hpp"
 
 namespace bgb {
 
-// ---------------------------------------------------------------- W1A16 prep --
-// xp[m][128 tq + 8u + 2d + h] = x[m][32 (4 tq + d) + u + 16 h]  (0 beyond K),
-// xsum[m][T] = sum of x[m][k] over k % 4 == T (fp32, fixed order).
-__global__ void __launch_bounds__(256)
-w1a16_prep_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t Kp, int is_f16,
-                  uint16_t* __restrict__ xp, float* __restrict__ xsum) {
-    __shared__ double dscr[4];
-    const int64_t m = blockIdx.x;
-    const uint16_t* xr = x + m * K;
-    uint16_t* out = xp + m * Kp;
-    for (int64_t p = threadIdx.x; p < Kp; p += 256) {
-        const int64_t tq = p / 128;
-        const int r = int(p % 128);
-        const int u = r >> 3, d = (r >> 1) & 3, h = r & 1;
-        const int64_t k = 32 * (4 * tq + d) + u + 16 * h;
-        out[p] = k < K ? xr[k] : uint16_t(0);
-    }
-    for (int T = 0; T < 4; ++T) {
-        double s = 0.0;
-        for (int64_t k = 4 * int64_t(threadIdx.x) + T; k < K; k += 4 * 256)
-            s += double(is_f16 ? f16_to_f32(xr[k]) : bf16_to_f32(xr[k]));
-        s = block_sum<256>(s, dscr);
-        if (threadIdx.x == 0) xsum[4 * m + T] = float(s);
+constexpr int kMaxSteps = 8;   // steps preloaded per wave and pass (16384 rows per block pass)
+
+// ------------------------------------------------------------ shared bits ----
+
+// Position of activation row k in the W1A8 decode layout (int8, per 128-row
+// tile: [s = k%8][d = t%4][e = (k%32)/8] with t = k/32).
+BGB_DEV int q_pos(int64_t k) {
+    const int64_t t = k >> 5;
+    const int b = int(k & 31);
+    return int((t >> 2) * 128) + (b & 7) * 16 + int(t & 3) * 4 + (b >> 3);
+}
+// Position of activation row k in the W1A16 decode layout (16-bit elements,
+// per 128-row tile: [u = k%16][d = t%4][h = (k%32)/16]).
+BGB_DEV int x_pos(int64_t k) {
+    const int64_t t = k >> 5;
+    const int b = int(k & 31);
+    return int((t >> 2) * 128) + (b & 15) * 8 + int(t & 3) * 2 + (b >> 4);
+}
+
+BGB_DEV u32x4_t load_tile(const uint32_t* P, int64_t tq, int64_t N, int64_t j) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(P + (tq * N + j) * 4));
+}
+
+// Preload the tiles of up to kMaxSteps steps of this wave (zeros past the end).
+BGB_DEV void preload(u32x4_t* w, const uint32_t* P, int64_t base, int64_t steps, int64_t TQ, int64_t N,
+                     int64_t j, int g) {
+#pragma unroll
+    for (int i = 0; i < kMaxSteps; ++i) {
+        const int64_t st = base + 4 * i;
+        const int64_t tq = st * 4 + g;
+        w[i] = (st < steps && tq < TQ && j < N) ? load_tile(P, tq, N, j) : u32x4_t{0u, 0u, 0u, 0u};
     }
 }
 
-hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp, float* xsum,
-                                hipStream_t s) {
-    w1a16_prep_kernel<<<unsigned(M), 256, 0, s>>>(static_cast<const uint16_t*>(x), K, padded_k(K), is_f16, xp,
-                                                  xsum);
+BGB_DEV void store_y(void* y, int y_dtype, int64_t i, float v) {
+    if (y_dtype == kDtF32) static_cast<float*>(y)[i] = v;
+    else if (y_dtype == kDtBF16) static_cast<uint16_t*>(y)[i] = f32_to_bf16_rne(v);
+    else static_cast<uint16_t*>(y)[i] = f32_to_f16_rne(v);
+}
+
+BGB_DEV float load_alpha(const void* alpha, int alpha_f16, int64_t j) {
+    return alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[j]) : static_cast<const float*>(alpha)[j];
+}
+
+// ------------------------------------------------------------------ W1A8 -----
+
+template <int S>
+BGB_DEV i32x4_t w1a8_mfma(const u32x4_t& w, const i32x4_t& b, const i32x4_t& c) {
+    constexpr uint32_t mask = 0x01010101u << S;
+    const i32x4_t a = {int(w.x & mask), int(w.y & mask), int(w.z & mask), int(w.w & mask)};
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+BGB_DEV void w1a8_step(const u32x4_t& w, const i32x4_t* b, i32x4_t* acc) {
+    acc[0] = w1a8_mfma<0>(w, b[0], acc[0]);
+    acc[1] = w1a8_mfma<1>(w, b[1], acc[1]);
+    acc[2] = w1a8_mfma<2>(w, b[2], acc[2]);
+    acc[3] = w1a8_mfma<3>(w, b[3], acc[3]);
+    acc[4] = w1a8_mfma<4>(w, b[4], acc[4]);
+    acc[5] = w1a8_mfma<5>(w, b[5], acc[5]);
+    acc[6] = w1a8_mfma<6>(w, b[6], acc[6]);
+    acc[7] = w1a8_mfma<7>(w, b[7], acc[7]);
+}
+
+// sum_k b q from the 8 shift accumulators (each division by 2^s is exact).
+BGB_DEV i32x4_t w1a8_combine(const i32x4_t* acc) {
+    i32x4_t t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int v = 0;
+#pragma unroll
+        for (int s = 0; s < 7; ++s) v += acc[s][i] >> s;
+        t[i] = v - (acc[7][i] >> 7);
+    }
+    return t;
+}
+
+// General decode: codes from the prologue in the decode layout, M <= 16 * TF.
+template <int TF>
+__global__ void __launch_bounds__(256)
+gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsum, const float* __restrict__ gamma,
+                 const float* __restrict__ beta, float qb, int M, int64_t N, int64_t TQ,
+                 const uint32_t* __restrict__ P, float* __restrict__ y, int32_t* __restrict__ acc_opt) {
+    __shared__ i32x4_t red[4][TF][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
+    const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
+    i32x4_t acc[TF][8];
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc[tf][s] = i32x4_t{0, 0, 0, 0};
+    for (int64_t base = wave; base < steps; base += 4 * kMaxSteps) {
+        u32x4_t w[kMaxSteps];
+        preload(w, P, base, steps, TQ, N, j, g);
+#pragma unroll
+        for (int i = 0; i < kMaxSteps; ++i) {
+            const int64_t st = base + 4 * i;
+            if (st >= steps) break;
+            const int64_t tq = st * 4 + g;
+#pragma unroll
+            for (int tf = 0; tf < TF; ++tf) {
+                const int m = 16 * tf + r;
+                const bool bv = tq < TQ && m < M;
+                const i32x4_t* src = reinterpret_cast<const i32x4_t*>(q + int64_t(m) * Kp + tq * 128);
+                i32x4_t b[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) b[s] = bv ? src[s] : i32x4_t{0, 0, 0, 0};
+                w1a8_step(w[i], b, acc[tf]);
+            }
+        }
+    }
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf) red[wave][tf][lane] = w1a8_combine(acc[tf]);
+    __syncthreads();
+    if (wave != 0) return;
+    const float scale = (beta[0] * gamma[0]) / qb;
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf) {
+        const int mm = 16 * tf + r;
+        if (mm >= M) continue;
+        const i32x4_t sum = ((red[0][tf][lane] + red[1][tf][lane]) + red[2][tf][lane]) + red[3][tf][lane];
+        const int32_t rs = rowsum[mm];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t col = j0 + 4 * g + i;
+            if (col >= N) continue;
+            const int32_t a = 2 * sum[i] - rs;
+            y[int64_t(mm) * N + col] = float(a) * scale;
+            if (acc_opt) acc_opt[int64_t(mm) * N + col] = a;
+        }
+    }
+}
+
+// Single token, prologue fused: x [K] (float or bf16 bits), K <= 1024 * NV.
+template <typename XT> BGB_DEV void load4(const XT* x, int64_t e, float* v);
+template <> BGB_DEV void load4<float>(const float* x, int64_t e, float* v) {
+    const float4 t = *reinterpret_cast<const float4*>(x + e);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+template <> BGB_DEV void load4<uint16_t>(const uint16_t* x, int64_t e, float* v) {
+    const uint2 t = *reinterpret_cast<const uint2*>(x + e);
+    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+}
+
+constexpr int kFusedMaxKp = 16384;
+
+template <int NV, typename XT>
+__global__ void __launch_bounds__(256)
+bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
+                         const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
+                         int32_t* __restrict__ acc_opt, int8_t* __restrict__ xq_opt,
+                         float* __restrict__ gamma_opt) {
+    __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
+    __shared__ i32x4_t red[4][64];
+    __shared__ double dscr[4];
+    __shared__ float fscr[4];
+    __shared__ int iscr[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
+    const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
+
+    // 1. the signs: all of this wave's tiles in flight before anything else
+    u32x4_t w[kMaxSteps];
+    preload(w, P, wave, steps, TQ, N, j, g);
+
+    // 2. LayerNorm statistics and absmax of the token (identical in every block)
+    float v[NV][4];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t e = (int64_t(i) * 256 + tid) * 4;
+        if (e < K) load4(x, e, v[i]);
+        else v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0f;
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s += double(v[i][c]);
+    s = block_sum<256>(s, dscr);
+    const double mu = s / double(K);
+    double s2 = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if ((int64_t(i) * 256 + tid) * 4 >= K) continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const double d = double(v[i][c]) - mu;
+            s2 += d * d;
+        }
+    }
+    s2 = block_sum<256>(s2, dscr);
+    const float mu32 = float(mu);
+    const float rs32 = float(1.0 / sqrt(s2 / double(K) + eps));
+    float lm = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            v[i][c] = (v[i][c] - mu32) * rs32;          // h; padded slots give |h| ignored below
+            if ((int64_t(i) * 256 + tid) * 4 < K) lm = fmaxf(lm, fabsf(v[i][c]));
+        }
+    const float gamma = block_max<256>(lm, fscr);
+
+    // 3. codes into LDS in the decode layout; zero padding rows K..Kp-1
+    int sq = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t e = (int64_t(i) * 256 + tid) * 4;
+        if (e >= K) continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            int code = 0;
+            if (gamma != 0.0f) {
+                float t = (v[i][c] * qb) / gamma;
+                t = fminf(fmaxf(t, -lim), lim);
+                code = int(t);
+            }
+            qs[q_pos(e + c)] = int8_t(code);
+            sq += code;
+            if (xq_opt && blockIdx.x == 0) xq_opt[e + c] = int8_t(code);
+        }
+    }
+    for (int64_t k = K + tid; k < Kp; k += 256) qs[q_pos(k)] = 0;
+    const int rowsum = block_sum_i<256>(sq, iscr);     // ends with a barrier: qs is complete
+    if (gamma_opt && blockIdx.x == 0 && tid == 0) gamma_opt[0] = gamma;
+
+    // 4. the product: token 0 lives in lanes with r == 0, the rest are zero
+    i32x4_t acc[8];
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kMaxSteps; ++i) {
+        const int64_t st = wave + 4 * i;
+        if (st >= steps) break;
+        const int64_t tq = st * 4 + g;
+        const bool bv = tq < TQ && r == 0;
+        const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs + tq * 128);
+        i32x4_t b[8];
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) b[s8] = bv ? src[s8] : i32x4_t{0, 0, 0, 0};
+        w1a8_step(w[i], b, acc);
+    }
+    red[wave][lane] = w1a8_combine(acc);
+    __syncthreads();
+    if (wave != 0 || r != 0) return;
+    const i32x4_t sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    const float scale = (beta[0] * gamma) / qb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t col = j0 + 4 * g + i;
+        if (col >= N) continue;
+        const int32_t a = 2 * sum[i] - rowsum;
+        y[col] = float(a) * scale;
+        if (acc_opt) acc_opt[col] = a;
+    }
+}
+
+bool w1a8_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
+
+hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
+                               const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
+                               float* gamma_opt, hipStream_t s) {
+    const unsigned grid = unsigned((N + 15) / 16);
+    const int64_t TQ = tiles_per_col(K);
+    const int nv = int((K + 1023) / 1024);
+#define BGB_D1(NVV)                                                                                              \
+    if (x_bf16)                                                                                                  \
+        bitlinear_decode1_kernel<NVV, uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), K, N, TQ,   \
+                                                                     eps, qb, lim, P, beta, y, acc_opt, xq_opt,  \
+                                                                     gamma_opt);                                 \
+    else                                                                                                         \
+        bitlinear_decode1_kernel<NVV, float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), K, N, TQ, eps,    \
+                                                                  qb, lim, P, beta, y, acc_opt, xq_opt,          \
+                                                                  gamma_opt);
+    if (nv <= 1) { BGB_D1(1) }
+    else if (nv <= 2) { BGB_D1(2) }
+    else if (nv <= 4) { BGB_D1(4) }
+    else if (nv <= 8) { BGB_D1(8) }
+    else { BGB_D1(16) }
+#undef BGB_D1
     return hipGetLastError();
 }
 
-// Field-bit constants per 16-bit format: P0 = first field bit used, the
-// 1.0 and 0.5 bases (replicated in both halves of a dword).
+hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma, const float* beta, float qb,
+                            int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
+                            hipStream_t s) {
+    const unsigned grid = unsigned((N + 15) / 16);
+    const int64_t TQ = tiles_per_col(K);
+    const int tf = int((M + 15) / 16);
+    if (tf == 1) gemv_w1a8_kernel<1><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
+    else if (tf == 2) gemv_w1a8_kernel<2><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
+    else if (tf == 3) gemv_w1a8_kernel<3><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
+    else gemv_w1a8_kernel<4><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- W1A16 -----
+
+// Field-bit constants per 16-bit format: P0 = first field bit used; the 1.0
+// and 0.5 bases replicated in both halves of a dword.
 template <bool kF16> struct Fmt16;
 template <> struct Fmt16<false> {   // bf16: 7 mantissa bits, exponent LSB = bit 7
     static constexpr int P0 = 4;
@@ -95,9 +372,9 @@ BGB_DEV uint32_t shift_word(uint32_t w) {
     else return w >> (-kShift);
 }
 
-// One MFMA u of a step: A dwords from the four words' bit pair (u, u+16).
+// A operand of MFMA u: the four words' bit pair (u, u+16) moved to field bit p.
 template <bool kF16, int U>
-BGB_DEV void w1a16_mfma_u(const u32x4_t& w, const u32x4_t& b, f32x4_t* acc) {
+BGB_DEV u32x4_t w1a16_a(const u32x4_t& w) {
     using F = Fmt16<kF16>;
     constexpr int T = U % 4;
     constexpr int p = F::P0 + T;
@@ -109,72 +386,190 @@ BGB_DEV void w1a16_mfma_u(const u32x4_t& w, const u32x4_t& b, f32x4_t* acc) {
     a.y = (shift_word<sh>(w.y) & mask) | base;
     a.z = (shift_word<sh>(w.z) & mask) | base;
     a.w = (shift_word<sh>(w.w) & mask) | base;
-    acc[T] = mfma16<kF16>(a, b, acc[T]);
+    return a;
 }
 
-BGB_DEV void store_y(void* y, int y_dtype, int64_t i, float v) {
-    if (y_dtype == kDtF32) static_cast<float*>(y)[i] = v;
-    else if (y_dtype == kDtBF16) static_cast<uint16_t*>(y)[i] = f32_to_bf16_rne(v);
-    else static_cast<uint16_t*>(y)[i] = f32_to_f16_rne(v);
+// One step (16 MFMAs) for TF token fragments; b(u, tf) yields the B operand.
+template <bool kF16, int TF, int U, typename BF>
+BGB_DEV void w1a16_u(const u32x4_t& w, BF&& bsrc, f32x4_t (*acc)[4]) {
+    const u32x4_t a = w1a16_a<kF16, U>(w);
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf) acc[tf][U % 4] = mfma16<kF16>(a, bsrc(U, tf), acc[tf][U % 4]);
+}
+template <bool kF16, int TF, typename BF>
+BGB_DEV void w1a16_step(const u32x4_t& w, BF&& bsrc, f32x4_t (*acc)[4]) {
+    w1a16_u<kF16, TF, 0>(w, bsrc, acc);  w1a16_u<kF16, TF, 1>(w, bsrc, acc);
+    w1a16_u<kF16, TF, 2>(w, bsrc, acc);  w1a16_u<kF16, TF, 3>(w, bsrc, acc);
+    w1a16_u<kF16, TF, 4>(w, bsrc, acc);  w1a16_u<kF16, TF, 5>(w, bsrc, acc);
+    w1a16_u<kF16, TF, 6>(w, bsrc, acc);  w1a16_u<kF16, TF, 7>(w, bsrc, acc);
+    w1a16_u<kF16, TF, 8>(w, bsrc, acc);  w1a16_u<kF16, TF, 9>(w, bsrc, acc);
+    w1a16_u<kF16, TF, 10>(w, bsrc, acc); w1a16_u<kF16, TF, 11>(w, bsrc, acc);
+    w1a16_u<kF16, TF, 12>(w, bsrc, acc); w1a16_u<kF16, TF, 13>(w, bsrc, acc);
+    w1a16_u<kF16, TF, 14>(w, bsrc, acc); w1a16_u<kF16, TF, 15>(w, bsrc, acc);
 }
 
-BGB_DEV float load_alpha(const void* alpha, int alpha_f16, int64_t j) {
-    return alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[j]) : static_cast<const float*>(alpha)[j];
+// Output for one token: s = 2 sum_k b x - sum_k x from the type accumulators.
+BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2, float X3) {
+    const float sb = ((8.0f * (tot[0][i] - X0) + 4.0f * (tot[1][i] - X1)) + 2.0f * (tot[2][i] - X2)) +
+                     2.0f * (tot[3][i] - 0.5f * X3);
+    return 2.0f * sb - (((X0 + X1) + X2) + X3);
 }
 
-template <bool kF16>
+// xp[m][x_pos(k)] = x[m][k] (0 beyond K); xsum[m][T] = fl32(sum over k%4 == T, fp64).
+__global__ void __launch_bounds__(256)
+w1a16_prep_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t Kp, int is_f16, uint16_t* __restrict__ xp,
+                  float* __restrict__ xsum) {
+    __shared__ double dscr[4];
+    const int64_t m = blockIdx.x;
+    const uint16_t* xr = x + m * K;
+    uint16_t* out = xp + m * Kp;
+    for (int64_t k = threadIdx.x; k < Kp; k += 256) out[x_pos(k)] = k < K ? xr[k] : uint16_t(0);
+    for (int T = 0; T < 4; ++T) {
+        double s = 0.0;
+        for (int64_t k = 4 * int64_t(threadIdx.x) + T; k < K; k += 4 * 256)
+            s += double(is_f16 ? f16_to_f32(xr[k]) : bf16_to_f32(xr[k]));
+        s = block_sum<256>(s, dscr);
+        if (threadIdx.x == 0) xsum[4 * m + T] = float(s);
+    }
+}
+
+hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp, float* xsum,
+                             hipStream_t s) {
+    w1a16_prep_kernel<<<unsigned(M), 256, 0, s>>>(static_cast<const uint16_t*>(x), K, padded_k(K), is_f16, xp,
+                                                  xsum);
+    return hipGetLastError();
+}
+
+// General decode: permuted activations from the prep kernel, M <= 16 * TF.
+template <bool kF16, int TF>
 __global__ void __launch_bounds__(256)
 gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const float* __restrict__ xsum, int M, int64_t N, int64_t TQ,
                   const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
                   void* __restrict__ y, int y_dtype) {
-    __shared__ f32x4_t red[4][4][64];
+    __shared__ f32x4_t red[4][TF][4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
-    const int64_t j0 = int64_t(blockIdx.x) * 16;
-    const int64_t j = j0 + r;
-    const int64_t Kp = TQ * 128;
-    const int64_t steps = (TQ + 3) / 4;
-    f32x4_t acc[4];
+    const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
+    const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
+    f32x4_t acc[TF][4];
 #pragma unroll
-    for (int T = 0; T < 4; ++T) acc[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int64_t st = wave; st < steps; st += 4) {
-        const int64_t tq = st * 4 + g;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (tq < TQ && j < N) w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(P + (tq * N + j) * 4));
-        const bool bval = r < M && tq < TQ;
-        const u32x4_t* xb = reinterpret_cast<const u32x4_t*>(xp + int64_t(r) * Kp + tq * 128);
-        u32x4_t b[16];
+    for (int tf = 0; tf < TF; ++tf)
 #pragma unroll
-        for (int u = 0; u < 16; ++u) b[u] = bval ? xb[u] : u32x4_t{0u, 0u, 0u, 0u};
-        w1a16_mfma_u<kF16, 0>(w, b[0], acc);   w1a16_mfma_u<kF16, 1>(w, b[1], acc);
-        w1a16_mfma_u<kF16, 2>(w, b[2], acc);   w1a16_mfma_u<kF16, 3>(w, b[3], acc);
-        w1a16_mfma_u<kF16, 4>(w, b[4], acc);   w1a16_mfma_u<kF16, 5>(w, b[5], acc);
-        w1a16_mfma_u<kF16, 6>(w, b[6], acc);   w1a16_mfma_u<kF16, 7>(w, b[7], acc);
-        w1a16_mfma_u<kF16, 8>(w, b[8], acc);   w1a16_mfma_u<kF16, 9>(w, b[9], acc);
-        w1a16_mfma_u<kF16, 10>(w, b[10], acc); w1a16_mfma_u<kF16, 11>(w, b[11], acc);
-        w1a16_mfma_u<kF16, 12>(w, b[12], acc); w1a16_mfma_u<kF16, 13>(w, b[13], acc);
-        w1a16_mfma_u<kF16, 14>(w, b[14], acc); w1a16_mfma_u<kF16, 15>(w, b[15], acc);
+        for (int T = 0; T < 4; ++T) acc[tf][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int64_t base = wave; base < steps; base += 4 * kMaxSteps) {
+        u32x4_t w[kMaxSteps];
+        preload(w, P, base, steps, TQ, N, j, g);
+#pragma unroll
+        for (int i = 0; i < kMaxSteps; ++i) {
+            const int64_t st = base + 4 * i;
+            if (st >= steps) break;
+            const int64_t tq = st * 4 + g;
+            const bool tv = tq < TQ;
+            auto bsrc = [&](int u, int tf) -> u32x4_t {
+                const int m = 16 * tf + r;
+                if (!tv || m >= M) return u32x4_t{0u, 0u, 0u, 0u};
+                return reinterpret_cast<const u32x4_t*>(xp + int64_t(m) * Kp + tq * 128)[u];
+            };
+            w1a16_step<kF16, TF>(w[i], bsrc, acc);
+        }
     }
 #pragma unroll
-    for (int T = 0; T < 4; ++T) red[wave][T][lane] = acc[T];
+    for (int tf = 0; tf < TF; ++tf)
+#pragma unroll
+        for (int T = 0; T < 4; ++T) red[wave][tf][T][lane] = acc[tf][T];
     __syncthreads();
     if (wave != 0) return;
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf) {
+        const int mm = 16 * tf + r;
+        if (mm >= M) continue;
+        f32x4_t tot[4];
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+            tot[T] = ((red[0][tf][T][lane] + red[1][tf][T][lane]) + red[2][tf][T][lane]) + red[3][tf][T][lane];
+        const float X0 = xsum[4 * mm], X1 = xsum[4 * mm + 1], X2 = xsum[4 * mm + 2], X3 = xsum[4 * mm + 3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t col = j0 + 4 * g + i;
+            if (col >= N) continue;
+            store_y(y, y_dtype, int64_t(mm) * N + col, load_alpha(alpha, alpha_f16, col) * w1a16_out(tot, i, X0, X1, X2, X3));
+        }
+    }
+}
+
+// Single token, activation staging fused: the block permutes x into LDS and
+// computes the four X_T itself.
+template <bool kF16>
+__global__ void __launch_bounds__(256)
+fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
+                   const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
+    __shared__ f32x4_t red[4][4][64];
+    __shared__ double dscr[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
+    const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
+
+    u32x4_t w[kMaxSteps];
+    preload(w, P, wave, steps, TQ, N, j, g);
+
+    // stage: each thread moves 4 consecutive rows at a time (types 0..3 in order)
+    double xs4[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int64_t k = int64_t(tid) * 4; k < Kp; k += 1024) {
+        uint2 t = {0u, 0u};
+        if (k < K) t = *reinterpret_cast<const uint2*>(x + k);
+        const uint16_t e[4] = {uint16_t(t.x & 0xffffu), uint16_t(t.x >> 16), uint16_t(t.y & 0xffffu),
+                               uint16_t(t.y >> 16)};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            xs[x_pos(k + c)] = e[c];
+            xs4[c] += double(kF16 ? f16_to_f32(e[c]) : bf16_to_f32(e[c]));
+        }
+    }
+    float X[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) X[c] = float(block_sum<256>(xs4[c], dscr));   // barriers: xs complete
+
+    f32x4_t acc[1][4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) acc[0][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMaxSteps; ++i) {
+        const int64_t st = wave + 4 * i;
+        if (st >= steps) break;
+        const int64_t tq = st * 4 + g;
+        const bool bv = tq < TQ && r == 0;
+        auto bsrc = [&](int u, int) -> u32x4_t {
+            if (!bv) return u32x4_t{0u, 0u, 0u, 0u};
+            return reinterpret_cast<const u32x4_t*>(xs + tq * 128)[u];
+        };
+        w1a16_step<kF16, 1>(w[i], bsrc, acc);
+    }
+#pragma unroll
+    for (int T = 0; T < 4; ++T) red[wave][T][lane] = acc[0][T];
+    __syncthreads();
+    if (wave != 0 || r != 0) return;
     f32x4_t tot[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) tot[T] = ((red[0][T][lane] + red[1][T][lane]) + red[2][T][lane]) + red[3][T][lane];
-    const int mm = r;                          // C column = token
-    if (mm >= M) return;
-    const float X0 = xsum[4 * mm], X1 = xsum[4 * mm + 1], X2 = xsum[4 * mm + 2], X3 = xsum[4 * mm + 3];
-    const float xall = ((X0 + X1) + X2) + X3;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t col = j0 + 4 * g + i;    // C row = column
+        const int64_t col = j0 + 4 * g + i;
         if (col >= N) continue;
-        const float sb = ((8.0f * (tot[0][i] - X0) + 4.0f * (tot[1][i] - X1)) + 2.0f * (tot[2][i] - X2)) +
-                         2.0f * (tot[3][i] - 0.5f * X3);
-        const float s = 2.0f * sb - xall;
-        store_y(y, y_dtype, int64_t(mm) * N + col, load_alpha(alpha, alpha_f16, col) * s);
+        store_y(y, y_dtype, col, load_alpha(alpha, alpha_f16, col) * w1a16_out(tot, i, X[0], X[1], X[2], X[3]));
     }
+}
+
+bool w1a16_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
+
+hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    const unsigned grid = unsigned((N + 15) / 16);
+    const uint16_t* xx = static_cast<const uint16_t*>(x);
+    if (x_f16) fbi_decode1_kernel<true><<<grid, 256, 0, s>>>(xx, K, N, tiles_per_col(K), P, alpha, alpha_f16, y, y_dtype);
+    else fbi_decode1_kernel<false><<<grid, 256, 0, s>>>(xx, K, N, tiles_per_col(K), P, alpha, alpha_f16, y, y_dtype);
+    return hipGetLastError();
 }
 
 hipError_t launch_w1a16_gemv(const uint16_t* xp, const float* xsum, int x_f16, int64_t M, int64_t K, int64_t N,
@@ -182,81 +577,15 @@ hipError_t launch_w1a16_gemv(const uint16_t* xp, const float* xsum, int x_f16, i
                              hipStream_t s) {
     const unsigned grid = unsigned((N + 15) / 16);
     const int64_t TQ = tiles_per_col(K);
-    if (x_f16)
-        gemv_w1a16_kernel<true><<<grid, 256, 0, s>>>(xp, xsum, int(M), N, TQ, P, alpha, alpha_f16, y, y_dtype);
-    else
-        gemv_w1a16_kernel<false><<<grid, 256, 0, s>>>(xp, xsum, int(M), N, TQ, P, alpha, alpha_f16, y, y_dtype);
-    return hipGetLastError();
-}
-
-// ------------------------------------------------------------------- W1A8 ----
-template <int S>
-BGB_DEV void w1a8_mfma_s(const u32x4_t& w, const i32x4_t& b, i32x4_t* acc) {
-    constexpr uint32_t mask = 0x01010101u << S;
-    const i32x4_t a = {int(w.x & mask), int(w.y & mask), int(w.z & mask), int(w.w & mask)};
-    acc[S] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[S], 0, 0, 0);
-}
-
-__global__ void __launch_bounds__(256)
-gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsum, const float* __restrict__ gamma,
-                 const float* __restrict__ beta, float qb, int M, int64_t N, int64_t TQ,
-                 const uint32_t* __restrict__ P, float* __restrict__ y, int32_t* __restrict__ acc_opt) {
-    __shared__ i32x4_t red[4][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, r = lane & 15;
-    const int64_t j0 = int64_t(blockIdx.x) * 16;
-    const int64_t j = j0 + r;
-    const int64_t Kp = TQ * 128;
-    const int64_t steps = (TQ + 3) / 4;
-    i32x4_t acc[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc[s] = i32x4_t{0, 0, 0, 0};
-    for (int64_t st = wave; st < steps; st += 4) {
-        const int64_t tq = st * 4 + g;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (tq < TQ && j < N) w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(P + (tq * N + j) * 4));
-        const bool bval = r < M && tq < TQ;
-        const i32x4_t* qb4 = reinterpret_cast<const i32x4_t*>(q + int64_t(r) * Kp + tq * 128);
-        i32x4_t b[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) b[s] = bval ? qb4[s] : i32x4_t{0, 0, 0, 0};
-        w1a8_mfma_s<0>(w, b[0], acc); w1a8_mfma_s<1>(w, b[1], acc);
-        w1a8_mfma_s<2>(w, b[2], acc); w1a8_mfma_s<3>(w, b[3], acc);
-        w1a8_mfma_s<4>(w, b[4], acc); w1a8_mfma_s<5>(w, b[5], acc);
-        w1a8_mfma_s<6>(w, b[6], acc); w1a8_mfma_s<7>(w, b[7], acc);
+    const int tf = int((M + 15) / 16);
+#define BGB_G16(F16, TFV) \
+    gemv_w1a16_kernel<F16, TFV><<<grid, 256, 0, s>>>(xp, xsum, int(M), N, TQ, P, alpha, alpha_f16, y, y_dtype)
+    if (x_f16) {
+        if (tf == 1) BGB_G16(true, 1); else if (tf == 2) BGB_G16(true, 2); else if (tf == 3) BGB_G16(true, 3); else BGB_G16(true, 4);
+    } else {
+        if (tf == 1) BGB_G16(false, 1); else if (tf == 2) BGB_G16(false, 2); else if (tf == 3) BGB_G16(false, 3); else BGB_G16(false, 4);
     }
-    // sum_k b q = sum_{s<7} acc_s / 2^s - acc_7 / 128 (each division exact)
-    i32x4_t tot;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int t = 0;
-#pragma unroll
-        for (int s = 0; s < 7; ++s) t += acc[s][i] >> s;
-        tot[i] = t - (acc[7][i] >> 7);
-    }
-    red[wave][lane] = tot;
-    __syncthreads();
-    if (wave != 0) return;
-    const i32x4_t sum = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-    const int mm = r;
-    if (mm >= M) return;
-    const float scale = (beta[0] * gamma[0]) / qb;
-    const int32_t rs = rowsum[mm];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t col = j0 + 4 * g + i;
-        if (col >= N) continue;
-        const int32_t a = 2 * sum[i] - rs;
-        y[int64_t(mm) * N + col] = float(a) * scale;
-        if (acc_opt) acc_opt[int64_t(mm) * N + col] = a;
-    }
-}
-
-hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma, const float* beta, float qb,
-                            int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
-                            hipStream_t s) {
-    const unsigned grid = unsigned((N + 15) / 16);
-    gemv_w1a8_kernel<<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, tiles_per_col(K), P, y, acc_opt);
+#undef BGB_G16
     return hipGetLastError();
 }
 

@@ -88,7 +88,7 @@ lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double 
     __shared__ double dscr[16];
     __shared__ float fscr[16];
     __shared__ int iscr[16];
-    __shared__ float s_mu[kGemvMaxM], s_rs[kGemvMaxM];
+    __shared__ float s_mu[kSmallPrologueM], s_rs[kSmallPrologueM];
     float gmax = 0.0f;
     for (int m = 0; m < M; ++m) {
         const XT* xr = x + int64_t(m) * K;
@@ -167,7 +167,7 @@ static void launch_lnq_t(const XT* x, int64_t M, int64_t K, double eps, float qb
                          int8_t* q, int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
                          float* gamma_opt, hipStream_t s) {
     const int64_t Kp = padded_k(K);
-    if (M <= kGemvMaxM) {
+    if (M <= kSmallPrologueM) {
         lnq_small_kernel<XT><<<1, 1024, 0, s>>>(x, int(M), K, Kp, eps, qb, lim, layout, q, rowsum, stats,
                                                  gamma_ws, xq_opt, gamma_opt);
     } else {

@@ -53,7 +53,8 @@ def test_sizes(lib):
     assert bgb.packed_bytes(160, 3) == 2 * 3 * 16
     assert bgb.packed_bytes(4096, 11008) == 5636096
     assert bgb.packed_bytes(31, 5) == 0
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 64, 4096, 4096) == 0        # GEMM path needs none
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096) == 0        # GEMM path needs none
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 64, 4096, 4096) >= 64 * 4096 * 2
     assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 16, 4096, 4096) >= 16 * 4096 * 2
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 1, 4096, 11008) >= 4096
     assert bgb.workspace_bytes(99, 1, 32, 32) == 0

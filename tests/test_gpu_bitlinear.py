@@ -29,8 +29,8 @@ def _run(bgb, orc, W, x_host, x_dev, qp=None, bits=8):
     return to_bits(y), y_ref
 
 
-CASES = [(1, 4096, 11008), (1, 96, 65), (3, 160, 300), (16, 768, 260), (17, 96, 65), (40, 1024, 300),
-         (130, 256, 513), (5, 11008, 64)]
+CASES = [(1, 4096, 11008), (1, 96, 65), (1, 16416, 40), (3, 160, 300), (16, 768, 260), (17, 96, 65),
+         (40, 1024, 300), (64, 512, 100), (65, 256, 90), (130, 256, 513), (5, 11008, 64)]
 
 
 @pytest.mark.parametrize("M,K,N", CASES)
@@ -96,3 +96,24 @@ def test_bitlinear_empty_and_deterministic(bgb_gpu):
         torch.cuda.synchronize()
         for t in ys[1:]:
             assert torch.equal(ys[0], t)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 11008), (1, 768, 300), (9, 768, 300), (40, 512, 200), (70, 512, 200)])
+def test_stage_api_matches_single_call(bgb_gpu, M, K, N):
+    """bitlinear_quantize + bitlinear_matmul (two launches) and bitlinear_w1a8
+    (fused into one launch for a single token) give bit-identical results,
+    and one quantization serves several weights."""
+    say(f"bitlinear stage API M={M} K={K} N={N}")
+    x = dev_f32(syn.normal_f32(600 + M, 1, (M, K)))
+    Ws = [syn.normal_f32(600 + M, 10 + i, (K, N), mean=0.001, std=0.02) for i in range(2)]
+    packs = [bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_BITNET) for W in Ws]
+    ws = torch.empty(bgb_gpu.workspace_bytes(bgb_gpu.OP_BITLINEAR, M, K, N), dtype=torch.uint8, device="cuda")
+    taps = bgb_gpu.bitlinear_quantize(x, ws=ws, want_q=True, want_gamma=True)
+    outs = [bgb_gpu.bitlinear_matmul(M, K, P, beta, N, ws=ws, want_acc=True) for P, beta, _ in packs]
+    for (P, beta, _), (y2, acc2) in zip(packs, outs):
+        y1, ex = bgb_gpu.bitlinear_w1a8(x, P, beta, N, want_q=True, want_gamma=True, want_acc=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ex["q"], taps["q"])
+        assert torch.equal(ex["gamma"], taps["gamma"])
+        assert torch.equal(ex["acc"], acc2)
+        assert torch.equal(y1, y2)

@@ -29,9 +29,12 @@ def _run(bgb, orc, W, xb, x_kind, y_kind, adt="f32"):
 
 
 CASES = [
-    # (M, K, N): decode (M <= 16) and GEMM (M > 16) paths, ragged N and K tails
-    (1, 768, 768), (8, 768, 768), (3, 96, 65), (16, 160, 300), (5, 4096, 33), (1, 11008, 100),
-    (17, 96, 65), (40, 768, 260), (130, 256, 300), (64, 2048, 520), (200, 352, 513),
+    # (M, K, N) covering every dispatch path: single-token fused decode (M = 1,
+    # K <= 16384), single token beyond the fused size, decode with 1..4 token
+    # fragments (M <= 64), and the MFMA GEMM (M > 64); ragged N and K tails.
+    (1, 768, 768), (1, 11008, 100), (1, 16416, 40), (8, 768, 768), (3, 96, 65), (16, 160, 300),
+    (5, 4096, 33), (17, 96, 65), (40, 768, 260), (64, 2048, 520), (65, 256, 300), (130, 256, 300),
+    (200, 352, 513),
 ]
 
 
@@ -45,7 +48,8 @@ def test_fbi_linear_bf16_parity(bgb_gpu, orc, M, K, N, y_kind):
     check_w1a16(y, ref, y_kind, f"M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 768, 768), (7, 160, 300), (16, 4096, 64), (40, 768, 260), (129, 96, 65)])
+@pytest.mark.parametrize("M,K,N", [(1, 768, 768), (7, 160, 300), (16, 4096, 64), (40, 768, 260), (64, 96, 65),
+                                   (129, 96, 65)])
 @pytest.mark.parametrize("y_kind", ["f32", "f16"])
 def test_fbi_linear_f16_parity(bgb_gpu, orc, M, K, N, y_kind):
     say(f"fbi_linear f16 M={M} K={K} N={N} y={y_kind}")
@@ -55,7 +59,8 @@ def test_fbi_linear_f16_parity(bgb_gpu, orc, M, K, N, y_kind):
     check_w1a16(y, ref, y_kind, f"f16 M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 96, 65), (5, 1024, 300), (16, 4096, 70), (40, 1024, 300), (131, 96, 257)])
+@pytest.mark.parametrize("M,K,N", [(1, 96, 65), (1, 4096, 300), (5, 1024, 300), (16, 4096, 70), (40, 1024, 300),
+                                   (64, 512, 33), (131, 96, 257)])
 @pytest.mark.parametrize("x_kind", ["bf16", "f16"])
 def test_fbi_linear_integer_activations_bit_exact(bgb_gpu, orc, M, K, N, x_kind):
     """Integer-valued activations (|x| <= 16) make every partial sum exact in
@@ -76,7 +81,7 @@ def test_unit_vector_probes_read_back_signs(bgb_gpu, orc, K, N):
     say(f"fbi_linear unit probes K={K} N={N}")
     W = syn.normal_f32(400 + K, 0, (K, N), std=0.02)
     ks = sorted(set([0, 1, 15, 16, 17, 31, 32, 63, 64, 100 % K, K - 33, K - 1]))
-    for M in (len(ks[:16]), 40):
+    for M in (1, len(ks[:16]), 40, 100):
         rows = (ks * 4)[:M]
         e = np.zeros((M, K), np.float32)
         e[np.arange(M), rows] = 1.0
