@@ -247,6 +247,33 @@ def leg_decode_7b(torch, bgb, syn, steps):
             "bytes_per_layer": nbytes, "bound": "hbm", "layer_copies": L, "launches_per_layer": 14}
         log(f"decode 7B layer B={B}: {ms * 1e3:.1f} us/layer, {gbs:.0f} GB/s")
     del layers
+    torch.cuda.empty_cache()
+    # same layer with the same-input linears concatenated column-wise before
+    # packing (q|k|v -> N = 12288, gate|up -> N = 22016): 4 launches per layer
+    fshapes = [("qkv", 4096, 12288), ("o", 4096, 4096), ("gate_up", 4096, 22016), ("down", 11008, 4096)]
+    F1, FA = build_layer(torch, bgb, syn, cfg["seed"], fshapes, 50, torch.float16)
+    flayers = [(F1, FA)] + [([p.clone() for p in F1], FA) for _ in range(L - 1)]
+    for B in cfg["batches"]:
+        xs = {K: torch.randn((B, K), device="cuda").to(torch.bfloat16) for K in (4096, 11008)}
+        ys = {N: torch.empty((B, N), dtype=torch.bfloat16, device="cuda") for _, _, N in fshapes}
+        wsz = max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, B, K, N) for _, K, N in fshapes)
+        ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
+
+        def fbody(i, xs=xs, ys=ys, ws=ws):
+            Ps, As = flayers[i % L]
+            for li, (_, K, N) in enumerate(fshapes):
+                bgb.fbi_linear_w1a16(xs[K], Ps[li], As[li], N, y=ys[N], ws=ws)
+
+        ms = graph_time(torch, fbody, steps, 4) / steps
+        xb = sum(2 * B * K for _, K, N in fshapes)
+        yb = sum(2 * B * N for _, K, N in fshapes)
+        nbytes = pbytes + abytes + xb + yb
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"w1a16_decode_7b_layer_fused_b{B}"] = {
+            "us_per_layer": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_layer": nbytes, "bound": "hbm", "layer_copies": L, "linears": "qkv, o, gate_up, down"}
+        log(f"decode 7B layer fused B={B}: {ms * 1e3:.1f} us/layer, {gbs:.0f} GB/s")
+    del flayers
     return out
 
 
@@ -299,7 +326,8 @@ def leg_stack_1p3b(torch, bgb, syn):
     for name, M in (("decode_b64", cfg["decode_batch"]), ("prefill_2x1024", cfg["prefill_tokens"])):
         xs = {K: torch.randn((M, K), device="cuda").to(torch.bfloat16) for K in (2048, 5632)}
         ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N in (2048, 5632)}
-        ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+        wsz = max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, N) for _, K, N in shapes)
+        ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
 
         def body(i, xs=xs, ys=ys, ws=ws):
             for Ps, As in layers:

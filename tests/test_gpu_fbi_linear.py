@@ -82,7 +82,7 @@ def test_unit_vector_probes_read_back_signs(bgb_gpu, orc, K, N):
     W = syn.normal_f32(400 + K, 0, (K, N), std=0.02)
     ks = sorted(set([0, 1, 15, 16, 17, 31, 32, 63, 64, 100 % K, K - 33, K - 1]))
     for M in (1, len(ks[:16]), 40, 100):
-        rows = (ks * 4)[:M]
+        rows = (ks * (M // len(ks) + 1))[:M]
         e = np.zeros((M, K), np.float32)
         e[np.arange(M), rows] = 1.0
         y, ref, a = _run(bgb_gpu, orc, W, syn.f32_to_bf16_bits(e), "bf16", "f32")
