@@ -93,10 +93,10 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
         return finish(bgb::launch_w1a16_decode1(x, x_f16, K, N, P, alpha, a_f16, y, ydt, s));
     if (M <= bgb::kGemvMaxM) {
         uint16_t* xp = reinterpret_cast<uint16_t*>(carve(ws, lay.xp));
-        float* xsum = reinterpret_cast<float*>(carve(ws, lay.xsum));
-        hipError_t e = bgb::launch_w1a16_prep(x, x_f16, M, K, xp, xsum, s);
+        double* xpart = reinterpret_cast<double*>(carve(ws, lay.xpart));
+        hipError_t e = bgb::launch_w1a16_prep(x, x_f16, M, K, xp, xpart, s);
         if (e != hipSuccess) return finish(e);
-        return finish(bgb::launch_w1a16_gemv(xp, xsum, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
+        return finish(bgb::launch_w1a16_gemv(xp, xpart, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
     }
     return finish(bgb::launch_w1a16_gemm(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
 }

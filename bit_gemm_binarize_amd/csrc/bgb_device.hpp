@@ -63,6 +63,80 @@ BGB_DEV int wave_sum_i(int v) {
     return v;
 }
 
+// Wave reductions on the DPP network (gfx9 row/bank controls): quad swaps,
+// half-row and row mirrors, then row_bcast15 / row_bcast31 fold the four rows
+// of 16 lanes; the total lands in lane 63. Lanes outside a broadcast's row
+// mask add the identity (0). Fixed order, so the result is reproducible.
+template <int CTRL, int ROWMASK>
+BGB_DEV int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+}
+template <int CTRL, int ROWMASK>
+BGB_DEV double dpp_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp_i32<CTRL, ROWMASK>(int(b & 0xffffffffll));
+    const int hi = dpp_i32<CTRL, ROWMASK>(int(b >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+template <int CTRL, int ROWMASK>
+BGB_DEV float dpp_f32(float v) {
+    return __int_as_float(dpp_i32<CTRL, ROWMASK>(__float_as_int(v)));
+}
+// Sum over the 64 lanes, valid in lane 63.
+BGB_DEV double wave_sum63(double v) {
+    v += dpp_f64<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f64<0x141, 0xF>(v);   // row_half_mirror
+    v += dpp_f64<0x140, 0xF>(v);   // row_mirror
+    v += dpp_f64<0x142, 0xA>(v);   // row_bcast15 into rows 1, 3
+    v += dpp_f64<0x143, 0xC>(v);   // row_bcast31 into rows 2, 3
+    return v;
+}
+BGB_DEV int wave_sum63_i(int v) {
+    v += dpp_i32<0xB1, 0xF>(v);
+    v += dpp_i32<0x4E, 0xF>(v);
+    v += dpp_i32<0x141, 0xF>(v);
+    v += dpp_i32<0x140, 0xF>(v);
+    v += dpp_i32<0x142, 0xA>(v);
+    v += dpp_i32<0x143, 0xC>(v);
+    return v;
+}
+// Max of non-negative values over the 64 lanes, valid in lane 63.
+BGB_DEV float wave_max63_nonneg(float v) {
+    v = fmaxf(v, dpp_f32<0xB1, 0xF>(v));
+    v = fmaxf(v, dpp_f32<0x4E, 0xF>(v));
+    v = fmaxf(v, dpp_f32<0x141, 0xF>(v));
+    v = fmaxf(v, dpp_f32<0x140, 0xF>(v));
+    v = fmaxf(v, dpp_f32<0x142, 0xA>(v));
+    v = fmaxf(v, dpp_f32<0x143, 0xC>(v));
+    return v;
+}
+// Block (NT threads) sum / max through the DPP wave reductions: lane 63 of
+// each wave parks its value in `scratch`, then every thread adds the NT/64
+// values in wave order. Contains two barriers.
+template <int NT>
+BGB_DEV double block_sum_dpp(double v, double* scratch) {
+    v = wave_sum63(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 63) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double t = scratch[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) t += scratch[i];
+    return t;
+}
+template <int NT>
+BGB_DEV float block_max_dpp(float v, float* scratch) {
+    v = wave_max63_nonneg(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 63) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = scratch[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) t = fmaxf(t, scratch[i]);
+    return t;
+}
+
 // Block-wide reductions; `scratch` must hold blockDim.x/64 entries. All
 // threads get the result. Contains __syncthreads().
 template <int NT>

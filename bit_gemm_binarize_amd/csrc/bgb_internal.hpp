@@ -41,14 +41,15 @@ struct PackBitnetWs {       // fp64 (sum W, sum |W|) per reduction block
     }
 };
 
-struct FbiLinearWs {        // decode only: permuted activations + per-type sums
-    size_t xp, xsum, total;
+struct FbiLinearWs {        // decode only: permuted activations + per-chunk type sums
+    size_t xp, xpart, total;
     static FbiLinearWs make(int64_t M, int64_t K) {
         FbiLinearWs w{};
-        if (M > kGemvMaxM) { w.xp = w.xsum = w.total = 0; return w; }
+        if (M > kGemvMaxM) { w.xp = w.xpart = w.total = 0; return w; }
+        const size_t chunks = size_t((padded_k(K) + 1023) / 1024);
         w.xp = 0;
-        w.xsum = align256(size_t(M) * size_t(padded_k(K)) * 2);
-        w.total = w.xsum + align256(size_t(M) * 4 * sizeof(float));
+        w.xpart = align256(size_t(M) * size_t(padded_k(K)) * 2);
+        w.total = w.xpart + align256(size_t(M) * chunks * 4 * sizeof(double));
         return w;
     }
 };
@@ -78,9 +79,9 @@ hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, doub
                            hipStream_t s);
 
 hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp,
-                             float* xsum, hipStream_t s);
+                             double* xpart, hipStream_t s);
 
-hipError_t launch_w1a16_gemv(const uint16_t* xp, const float* xsum, int x_f16, int64_t M,
+hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M,
                              int64_t K, int64_t N, const uint32_t* P, const void* alpha,
                              int alpha_f16, void* y, int y_dtype, hipStream_t s);
 

@@ -42,7 +42,6 @@
 
 namespace bgb {
 
-constexpr int kMaxSteps = 8;   // steps preloaded per wave and pass (16384 rows per block pass)
 
 // ------------------------------------------------------------ shared bits ----
 
@@ -65,15 +64,30 @@ BGB_DEV u32x4_t load_tile(const uint32_t* P, int64_t tq, int64_t N, int64_t j) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(P + (tq * N + j) * 4));
 }
 
-// Preload the tiles of up to kMaxSteps steps of this wave (zeros past the end).
-BGB_DEV void preload(u32x4_t* w, const uint32_t* P, int64_t base, int64_t steps, int64_t TQ, int64_t N,
-                     int64_t j, int g) {
+// Preload the tiles of S steps of this wave (steps base, base + stride, ...;
+// zeros past the end). Every load is issued unconditionally -- an invalid
+// step reads tile 0 of column 0 and is zeroed by a select -- so the loads sit
+// in straight-line code and the compiler can wait for exactly the ones it
+// needs (a skipped load would force it to wait for all of them).
+template <int S>
+BGB_DEV void preload(u32x4_t* w, const uint32_t* P, int64_t base, int64_t stride, int64_t steps, int64_t TQ,
+                     int64_t N, int64_t j, int g) {
 #pragma unroll
-    for (int i = 0; i < kMaxSteps; ++i) {
-        const int64_t st = base + 4 * i;
+    for (int i = 0; i < S; ++i) {
+        const int64_t st = base + stride * i;
         const int64_t tq = st * 4 + g;
-        w[i] = (st < steps && tq < TQ && j < N) ? load_tile(P, tq, N, j) : u32x4_t{0u, 0u, 0u, 0u};
+        const bool ok = st < steps && tq < TQ && j < N;
+        const uint32_t keep = 0u - uint32_t(ok);
+        const u32x4_t t = load_tile(P, ok ? tq : 0, N, ok ? j : 0);
+        w[i] = t & keep;
     }
+}
+
+// 16 bytes at p if ok, else zeros -- branch-free (p must be readable either way).
+template <typename V>
+BGB_DEV V ld16_or0(const V* p, bool ok) {
+    const V t = *p;
+    return t & V(0 - int(ok));
 }
 
 BGB_DEV void store_y(void* y, int y_dtype, int64_t i, float v) {
@@ -120,12 +134,22 @@ BGB_DEV i32x4_t w1a8_combine(const i32x4_t* acc) {
 }
 
 // General decode: codes from the prologue in the decode layout, M <= 16 * TF.
-template <int TF>
-__global__ void __launch_bounds__(256)
+// A block of kGenWaves waves owns 16 columns; each wave takes up to
+// kGenSteps steps per pass, loads all their tiles first, decodes each step's
+// A operand once and reuses it for the TF token fragments.
+constexpr int kGenWaves = 8;
+// steps per wave and pass: the fewest that cover the column (at most 4)
+inline int gen_steps(int64_t TQ) {
+    const int64_t steps = (TQ + 3) / 4;
+    return steps <= kGenWaves ? 1 : (steps <= 2 * kGenWaves ? 2 : 4);
+}
+
+template <int TF, int GS>
+__global__ void __launch_bounds__(kGenWaves * 64)
 gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsum, const float* __restrict__ gamma,
                  const float* __restrict__ beta, float qb, int M, int64_t N, int64_t TQ,
                  const uint32_t* __restrict__ P, float* __restrict__ y, int32_t* __restrict__ acc_opt) {
-    __shared__ i32x4_t red[4][TF][64];
+    __shared__ i32x4_t red[kGenWaves][TF][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
@@ -134,23 +158,24 @@ gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsu
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) acc[tf][s] = i32x4_t{0, 0, 0, 0};
-    for (int64_t base = wave; base < steps; base += 4 * kMaxSteps) {
-        u32x4_t w[kMaxSteps];
-        preload(w, P, base, steps, TQ, N, j, g);
+        for (int s8 = 0; s8 < 8; ++s8) acc[tf][s8] = i32x4_t{0, 0, 0, 0};
+    for (int64_t base = wave; base < steps; base += kGenWaves * GS) {
+        u32x4_t w[GS];
+        preload<GS>(w, P, base, kGenWaves, steps, TQ, N, j, g);
 #pragma unroll
-        for (int i = 0; i < kMaxSteps; ++i) {
-            const int64_t st = base + 4 * i;
-            if (st >= steps) break;
+        for (int i = 0; i < GS; ++i) {
+            const int64_t st = base + kGenWaves * i;
             const int64_t tq = st * 4 + g;
+            const bool tv = st < steps && tq < TQ;
 #pragma unroll
             for (int tf = 0; tf < TF; ++tf) {
                 const int m = 16 * tf + r;
-                const bool bv = tq < TQ && m < M;
-                const i32x4_t* src = reinterpret_cast<const i32x4_t*>(q + int64_t(m) * Kp + tq * 128);
+                const bool bv = tv && m < M;
+                const i32x4_t* src = reinterpret_cast<const i32x4_t*>(q + int64_t(bv ? m : 0) * Kp + (bv ? tq : 0) * 128);
                 i32x4_t b[8];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) b[s] = bv ? src[s] : i32x4_t{0, 0, 0, 0};
+                for (int s8 = 0; s8 < 8; ++s8) b[s8] = ld16_or0(src + s8, bv);
+                __builtin_amdgcn_sched_barrier(0);   // all 8 operand loads in flight before the MFMAs
                 w1a8_step(w[i], b, acc[tf]);
             }
         }
@@ -164,7 +189,9 @@ gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsu
     for (int tf = 0; tf < TF; ++tf) {
         const int mm = 16 * tf + r;
         if (mm >= M) continue;
-        const i32x4_t sum = ((red[0][tf][lane] + red[1][tf][lane]) + red[2][tf][lane]) + red[3][tf][lane];
+        i32x4_t sum = red[0][tf][lane];
+#pragma unroll
+        for (int wv = 1; wv < kGenWaves; ++wv) sum += red[wv][tf][lane];
         const int32_t rs = rowsum[mm];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -207,25 +234,32 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
     const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
 
-    // 1. the signs: all of this wave's tiles in flight before anything else
-    u32x4_t w[kMaxSteps];
-    preload(w, P, wave, steps, TQ, N, j, g);
-
-    // 2. LayerNorm statistics and absmax of the token (identical in every block)
+    // 1. the token (an L2 hit after the first block) and then all of this
+    //    wave's sign tiles; issued in this order so that the prologue below
+    //    waits only for x while the tiles are still in flight
+    constexpr int S = NV / 2 > 0 ? NV / 2 : 1;        // steps per wave: 4 waves x S x 512 rows >= Kp
     float v[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int64_t e = (int64_t(i) * 256 + tid) * 4;
-        if (e < K) load4(x, e, v[i]);
-        else v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0f;
+        const bool ok = e < K;
+        const uint32_t keep = 0u - uint32_t(ok);      // masks (not selects): the load stays unconditional
+        load4(x, ok ? e : 0, v[i]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[i][c] = __uint_as_float(__float_as_uint(v[i][c]) & keep);
     }
+    u32x4_t w[S];
+    preload<S>(w, P, wave, 4, steps, TQ, N, j, g);
+    __builtin_amdgcn_sched_barrier(0);   // keep every load above the first use of x
+
+    // 2. LayerNorm statistics (two fp64 passes) and the absmax of the token;
+    //    every block computes the same values
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) s += double(v[i][c]);
-    s = block_sum<256>(s, dscr);
-    const double mu = s / double(K);
+    const double mu = block_sum_dpp<256>(s, dscr) / double(K);
     double s2 = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -236,7 +270,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
             s2 += d * d;
         }
     }
-    s2 = block_sum<256>(s2, dscr);
+    s2 = block_sum_dpp<256>(s2, dscr);
     const float mu32 = float(mu);
     const float rs32 = float(1.0 / sqrt(s2 / double(K) + eps));
     float lm = 0.0f;
@@ -244,10 +278,10 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            v[i][c] = (v[i][c] - mu32) * rs32;          // h; padded slots give |h| ignored below
+            v[i][c] = (v[i][c] - mu32) * rs32;          // h
             if ((int64_t(i) * 256 + tid) * 4 < K) lm = fmaxf(lm, fabsf(v[i][c]));
         }
-    const float gamma = block_max<256>(lm, fscr);
+    const float gamma = block_max_dpp<256>(lm, fscr);
 
     // 3. codes into LDS in the decode layout; zero padding rows K..Kp-1
     int sq = 0;
@@ -269,28 +303,31 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         }
     }
     for (int64_t k = K + tid; k < Kp; k += 256) qs[q_pos(k)] = 0;
-    const int rowsum = block_sum_i<256>(sq, iscr);     // ends with a barrier: qs is complete
     if (gamma_opt && blockIdx.x == 0 && tid == 0) gamma_opt[0] = gamma;
+    __syncthreads();
 
     // 4. the product: token 0 lives in lanes with r == 0, the rest are zero
     i32x4_t acc[8];
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < kMaxSteps; ++i) {
+    for (int i = 0; i < S; ++i) {
         const int64_t st = wave + 4 * i;
-        if (st >= steps) break;
         const int64_t tq = st * 4 + g;
-        const bool bv = tq < TQ && r == 0;
-        const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs + tq * 128);
+        const bool bv = st < steps && tq < TQ && r == 0;
+        const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs + (bv ? tq : 0) * 128);
         i32x4_t b[8];
 #pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) b[s8] = bv ? src[s8] : i32x4_t{0, 0, 0, 0};
+        for (int s8 = 0; s8 < 8; ++s8) b[s8] = ld16_or0(src + s8, bv);
         w1a8_step(w[i], b, acc);
     }
+    // 5. partial sums of the 4 waves and the code row sum, one barrier
     red[wave][lane] = w1a8_combine(acc);
+    sq = wave_sum63_i(sq);
+    if (lane == 63) iscr[wave] = sq;
     __syncthreads();
     if (wave != 0 || r != 0) return;
+    const int rowsum = ((iscr[0] + iscr[1]) + iscr[2]) + iscr[3];
     const i32x4_t sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
     const float scale = (beta[0] * gamma) / qb;
 #pragma unroll
@@ -335,10 +372,13 @@ hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float*
     const unsigned grid = unsigned((N + 15) / 16);
     const int64_t TQ = tiles_per_col(K);
     const int tf = int((M + 15) / 16);
-    if (tf == 1) gemv_w1a8_kernel<1><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
-    else if (tf == 2) gemv_w1a8_kernel<2><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
-    else if (tf == 3) gemv_w1a8_kernel<3><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
-    else gemv_w1a8_kernel<4><<<grid, 256, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt);
+    const int gs = gen_steps(TQ);
+    constexpr unsigned nt = kGenWaves * 64;
+#define BGB_G8(TFV, GSV) gemv_w1a8_kernel<TFV, GSV><<<grid, nt, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt)
+#define BGB_G8S(TFV) if (gs == 1) BGB_G8(TFV, 1); else if (gs == 2) BGB_G8(TFV, 2); else BGB_G8(TFV, 4);
+    if (tf == 1) { BGB_G8S(1) } else if (tf == 2) { BGB_G8S(2) } else if (tf == 3) { BGB_G8S(3) } else { BGB_G8S(4) }
+#undef BGB_G8S
+#undef BGB_G8
     return hipGetLastError();
 }
 
@@ -408,6 +448,17 @@ BGB_DEV void w1a16_step(const u32x4_t& w, BF&& bsrc, f32x4_t (*acc)[4]) {
     w1a16_u<kF16, TF, 14>(w, bsrc, acc); w1a16_u<kF16, TF, 15>(w, bsrc, acc);
 }
 
+// All 16 A operands of a step (64 registers), for reuse across token fragments.
+template <bool kF16>
+BGB_DEV void w1a16_decode(const u32x4_t& w, u32x4_t* a) {
+    a[0] = w1a16_a<kF16, 0>(w);   a[1] = w1a16_a<kF16, 1>(w);   a[2] = w1a16_a<kF16, 2>(w);
+    a[3] = w1a16_a<kF16, 3>(w);   a[4] = w1a16_a<kF16, 4>(w);   a[5] = w1a16_a<kF16, 5>(w);
+    a[6] = w1a16_a<kF16, 6>(w);   a[7] = w1a16_a<kF16, 7>(w);   a[8] = w1a16_a<kF16, 8>(w);
+    a[9] = w1a16_a<kF16, 9>(w);   a[10] = w1a16_a<kF16, 10>(w); a[11] = w1a16_a<kF16, 11>(w);
+    a[12] = w1a16_a<kF16, 12>(w); a[13] = w1a16_a<kF16, 13>(w); a[14] = w1a16_a<kF16, 14>(w);
+    a[15] = w1a16_a<kF16, 15>(w);
+}
+
 // Output for one token: s = 2 sum_k b x - sum_k x from the type accumulators.
 BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2, float X3) {
     const float sb = ((8.0f * (tot[0][i] - X0) + 4.0f * (tot[1][i] - X1)) + 2.0f * (tot[2][i] - X2)) +
@@ -415,38 +466,60 @@ BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2,
     return 2.0f * sb - (((X0 + X1) + X2) + X3);
 }
 
-// xp[m][x_pos(k)] = x[m][k] (0 beyond K); xsum[m][T] = fl32(sum over k%4 == T, fp64).
+// Prep for the multi-token decode: xp[m][x_pos(k)] = x[m][k] (0 beyond K), and
+// per 1024-row chunk c the fp64 partial sums xpart[m][c][T] of x over k % 4 == T.
+// Grid (chunks, M); each thread moves 4 consecutive rows.
 __global__ void __launch_bounds__(256)
 w1a16_prep_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t Kp, int is_f16, uint16_t* __restrict__ xp,
-                  float* __restrict__ xsum) {
-    __shared__ double dscr[4];
-    const int64_t m = blockIdx.x;
-    const uint16_t* xr = x + m * K;
-    uint16_t* out = xp + m * Kp;
-    for (int64_t k = threadIdx.x; k < Kp; k += 256) out[x_pos(k)] = k < K ? xr[k] : uint16_t(0);
-    for (int T = 0; T < 4; ++T) {
-        double s = 0.0;
-        for (int64_t k = 4 * int64_t(threadIdx.x) + T; k < K; k += 4 * 256)
-            s += double(is_f16 ? f16_to_f32(xr[k]) : bf16_to_f32(xr[k]));
-        s = block_sum<256>(s, dscr);
-        if (threadIdx.x == 0) xsum[4 * m + T] = float(s);
+                  double* __restrict__ xpart) {
+    __shared__ double dX[4][4];
+    const int64_t m = blockIdx.y;
+    const int64_t k = int64_t(blockIdx.x) * 1024 + int64_t(threadIdx.x) * 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double xs4[4] = {0.0, 0.0, 0.0, 0.0};
+    if (k < Kp) {
+        uint2 t = {0u, 0u};
+        if (k < K) t = *reinterpret_cast<const uint2*>(x + m * K + k);
+        const uint16_t e[4] = {uint16_t(t.x & 0xffffu), uint16_t(t.x >> 16), uint16_t(t.y & 0xffffu),
+                               uint16_t(t.y >> 16)};
+        uint16_t* out = xp + m * Kp;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            out[x_pos(k + c)] = e[c];
+            xs4[c] = double(is_f16 ? f16_to_f32(e[c]) : bf16_to_f32(e[c]));
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const double t = wave_sum63(xs4[c]);
+        if (lane == 63) dX[wave][c] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const int c = threadIdx.x;
+        xpart[(m * gridDim.x + blockIdx.x) * 4 + c] = ((dX[0][c] + dX[1][c]) + dX[2][c]) + dX[3][c];
     }
 }
 
-hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp, float* xsum,
+int w1a16_prep_chunks(int64_t K) { return int((padded_k(K) + 1023) / 1024); }
+
+hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp, double* xpart,
                              hipStream_t s) {
-    w1a16_prep_kernel<<<unsigned(M), 256, 0, s>>>(static_cast<const uint16_t*>(x), K, padded_k(K), is_f16, xp,
-                                                  xsum);
+    const dim3 grid(unsigned(w1a16_prep_chunks(K)), unsigned(M));
+    w1a16_prep_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), K, padded_k(K), is_f16, xp, xpart);
     return hipGetLastError();
 }
 
 // General decode: permuted activations from the prep kernel, M <= 16 * TF.
-template <bool kF16, int TF>
-__global__ void __launch_bounds__(256)
-gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const float* __restrict__ xsum, int M, int64_t N, int64_t TQ,
-                  const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
+// Same wave organisation as the W1A8 kernel. Each wave folds its four type
+// accumulators into z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3 (powers of two),
+// so sum_k b x = z - (8 X_0 + 4 X_1 + 2 X_2 + X_3) is applied once at the end.
+template <bool kF16, int TF, int GS>
+__global__ void __launch_bounds__(kGenWaves * 64)
+gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xpart, int nchunk, int M, int64_t N,
+                  int64_t TQ, const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
                   void* __restrict__ y, int y_dtype) {
-    __shared__ f32x4_t red[4][TF][4][64];
+    __shared__ f32x4_t red[kGenWaves][TF][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
@@ -456,100 +529,128 @@ gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const float* __restrict__ xsu
     for (int tf = 0; tf < TF; ++tf)
 #pragma unroll
         for (int T = 0; T < 4; ++T) acc[tf][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int64_t base = wave; base < steps; base += 4 * kMaxSteps) {
-        u32x4_t w[kMaxSteps];
-        preload(w, P, base, steps, TQ, N, j, g);
+    for (int64_t base = wave; base < steps; base += kGenWaves * GS) {
+        u32x4_t w[GS];
+        preload<GS>(w, P, base, kGenWaves, steps, TQ, N, j, g);
 #pragma unroll
-        for (int i = 0; i < kMaxSteps; ++i) {
-            const int64_t st = base + 4 * i;
-            if (st >= steps) break;
+        for (int i = 0; i < GS; ++i) {
+            const int64_t st = base + kGenWaves * i;
             const int64_t tq = st * 4 + g;
-            const bool tv = tq < TQ;
-            auto bsrc = [&](int u, int tf) -> u32x4_t {
+            const bool tv = st < steps && tq < TQ;
+            u32x4_t a[16];
+#pragma unroll
+            for (int tf = 0; tf < TF; ++tf) {
                 const int m = 16 * tf + r;
-                if (!tv || m >= M) return u32x4_t{0u, 0u, 0u, 0u};
-                return reinterpret_cast<const u32x4_t*>(xp + int64_t(m) * Kp + tq * 128)[u];
-            };
-            w1a16_step<kF16, TF>(w[i], bsrc, acc);
+                const bool bv = tv && m < M;
+                const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xp + int64_t(bv ? m : 0) * Kp + (bv ? tq : 0) * 128);
+                u32x4_t b[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) b[u] = ld16_or0(src + u, bv);
+                __builtin_amdgcn_sched_barrier(0);   // all 16 operand loads in flight before the MFMAs
+                if (tf == 0) w1a16_decode<kF16>(w[i], a);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) acc[tf][u & 3] = mfma16<kF16>(a[u], b[u], acc[tf][u & 3]);
+            }
         }
     }
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf)
-#pragma unroll
-        for (int T = 0; T < 4; ++T) red[wave][tf][T][lane] = acc[tf][T];
+        red[wave][tf][lane] = ((8.0f * acc[tf][0] + 4.0f * acc[tf][1]) + 2.0f * acc[tf][2]) + 2.0f * acc[tf][3];
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf) {
         const int mm = 16 * tf + r;
         if (mm >= M) continue;
-        f32x4_t tot[4];
+        f32x4_t z = red[0][tf][lane];
 #pragma unroll
-        for (int T = 0; T < 4; ++T)
-            tot[T] = ((red[0][tf][T][lane] + red[1][tf][T][lane]) + red[2][tf][T][lane]) + red[3][tf][T][lane];
-        const float X0 = xsum[4 * mm], X1 = xsum[4 * mm + 1], X2 = xsum[4 * mm + 2], X3 = xsum[4 * mm + 3];
+        for (int wv = 1; wv < kGenWaves; ++wv) z += red[wv][tf][lane];
+        double X[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int c = 0; c < nchunk; ++c)
+#pragma unroll
+            for (int T = 0; T < 4; ++T) X[T] += xpart[(int64_t(mm) * nchunk + c) * 4 + T];
+        const float X0 = float(X[0]), X1 = float(X[1]), X2 = float(X[2]), X3 = float(X[3]);
+        const float corr = ((8.0f * X0 + 4.0f * X1) + 2.0f * X2) + X3;
+        const float xall = ((X0 + X1) + X2) + X3;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t col = j0 + 4 * g + i;
             if (col >= N) continue;
-            store_y(y, y_dtype, int64_t(mm) * N + col, load_alpha(alpha, alpha_f16, col) * w1a16_out(tot, i, X0, X1, X2, X3));
+            const float sres = 2.0f * (z[i] - corr) - xall;
+            store_y(y, y_dtype, int64_t(mm) * N + col, load_alpha(alpha, alpha_f16, col) * sres);
         }
     }
 }
 
 // Single token, activation staging fused: the block permutes x into LDS and
 // computes the four X_T itself.
-template <bool kF16>
+template <bool kF16, int NV>
 __global__ void __launch_bounds__(256)
 fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
                    const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
     __shared__ f32x4_t red[4][4][64];
-    __shared__ double dscr[4];
+    __shared__ double dX[4][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
     const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
 
-    u32x4_t w[kMaxSteps];
-    preload(w, P, wave, steps, TQ, N, j, g);
+    // the token first (see the W1A8 kernel), then all of this wave's tiles
+    constexpr int S = NV / 2 > 0 ? NV / 2 : 1;
+    uint2 xv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t k = (int64_t(i) * 256 + tid) * 4;
+        const uint32_t keep = 0u - uint32_t(k < K);   // masks (not selects): the load stays unconditional
+        const uint2 t = *reinterpret_cast<const uint2*>(x + (k < K ? k : 0));
+        xv[i] = uint2{t.x & keep, t.y & keep};
+    }
+    u32x4_t w[S];
+    preload<S>(w, P, wave, 4, steps, TQ, N, j, g);
+    __builtin_amdgcn_sched_barrier(0);   // keep every load above the first use of x
 
     // stage: each thread moves 4 consecutive rows at a time (types 0..3 in order)
     double xs4[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int64_t k = int64_t(tid) * 4; k < Kp; k += 1024) {
-        uint2 t = {0u, 0u};
-        if (k < K) t = *reinterpret_cast<const uint2*>(x + k);
-        const uint16_t e[4] = {uint16_t(t.x & 0xffffu), uint16_t(t.x >> 16), uint16_t(t.y & 0xffffu),
-                               uint16_t(t.y >> 16)};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t k = (int64_t(i) * 256 + tid) * 4;
+        if (k >= Kp) continue;
+        const uint16_t e[4] = {uint16_t(xv[i].x & 0xffffu), uint16_t(xv[i].x >> 16), uint16_t(xv[i].y & 0xffffu),
+                               uint16_t(xv[i].y >> 16)};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             xs[x_pos(k + c)] = e[c];
             xs4[c] += double(kF16 ? f16_to_f32(e[c]) : bf16_to_f32(e[c]));
         }
     }
-    float X[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) X[c] = float(block_sum<256>(xs4[c], dscr));   // barriers: xs complete
+    __syncthreads();
 
     f32x4_t acc[1][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) acc[0][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kMaxSteps; ++i) {
+    for (int i = 0; i < S; ++i) {
         const int64_t st = wave + 4 * i;
-        if (st >= steps) break;
         const int64_t tq = st * 4 + g;
-        const bool bv = tq < TQ && r == 0;
-        auto bsrc = [&](int u, int) -> u32x4_t {
-            if (!bv) return u32x4_t{0u, 0u, 0u, 0u};
-            return reinterpret_cast<const u32x4_t*>(xs + tq * 128)[u];
-        };
+        const bool bv = st < steps && tq < TQ && r == 0;
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xs + (bv ? tq : 0) * 128);
+        auto bsrc = [&](int u, int) -> u32x4_t { return ld16_or0(src + u, bv); };
         w1a16_step<kF16, 1>(w[i], bsrc, acc);
     }
+    // partial sums of the 4 waves and the four X_T, one barrier
 #pragma unroll
     for (int T = 0; T < 4; ++T) red[wave][T][lane] = acc[0][T];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const double t = wave_sum63(xs4[c]);
+        if (lane == 63) dX[wave][c] = t;
+    }
     __syncthreads();
     if (wave != 0 || r != 0) return;
+    float X[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) X[c] = float(((dX[0][c] + dX[1][c]) + dX[2][c]) + dX[3][c]);
     f32x4_t tot[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) tot[T] = ((red[0][T][lane] + red[1][T][lane]) + red[2][T][lane]) + red[3][T][lane];
@@ -567,24 +668,38 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
     const unsigned grid = unsigned((N + 15) / 16);
     const uint16_t* xx = static_cast<const uint16_t*>(x);
-    if (x_f16) fbi_decode1_kernel<true><<<grid, 256, 0, s>>>(xx, K, N, tiles_per_col(K), P, alpha, alpha_f16, y, y_dtype);
-    else fbi_decode1_kernel<false><<<grid, 256, 0, s>>>(xx, K, N, tiles_per_col(K), P, alpha, alpha_f16, y, y_dtype);
+    const int64_t TQ = tiles_per_col(K);
+    const int nv = int((TQ * 128 + 1023) / 1024);
+#define BGB_F1(NVV)                                                                                             \
+    if (x_f16) fbi_decode1_kernel<true, NVV><<<grid, 256, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype); \
+    else fbi_decode1_kernel<false, NVV><<<grid, 256, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype);
+    if (nv <= 1) { BGB_F1(1) }
+    else if (nv <= 2) { BGB_F1(2) }
+    else if (nv <= 4) { BGB_F1(4) }
+    else if (nv <= 8) { BGB_F1(8) }
+    else { BGB_F1(16) }
+#undef BGB_F1
     return hipGetLastError();
 }
 
-hipError_t launch_w1a16_gemv(const uint16_t* xp, const float* xsum, int x_f16, int64_t M, int64_t K, int64_t N,
+hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M, int64_t K, int64_t N,
                              const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
                              hipStream_t s) {
     const unsigned grid = unsigned((N + 15) / 16);
     const int64_t TQ = tiles_per_col(K);
     const int tf = int((M + 15) / 16);
-#define BGB_G16(F16, TFV) \
-    gemv_w1a16_kernel<F16, TFV><<<grid, 256, 0, s>>>(xp, xsum, int(M), N, TQ, P, alpha, alpha_f16, y, y_dtype)
+    const int nch = w1a16_prep_chunks(K);
+    constexpr unsigned nt = kGenWaves * 64;
+    const int gs = gen_steps(TQ);
+#define BGB_G16(F16, TFV, GSV) \
+    gemv_w1a16_kernel<F16, TFV, GSV><<<grid, nt, 0, s>>>(xp, xpart, nch, int(M), N, TQ, P, alpha, alpha_f16, y, y_dtype)
+#define BGB_G16S(F16, TFV) if (gs == 1) BGB_G16(F16, TFV, 1); else if (gs == 2) BGB_G16(F16, TFV, 2); else BGB_G16(F16, TFV, 4);
     if (x_f16) {
-        if (tf == 1) BGB_G16(true, 1); else if (tf == 2) BGB_G16(true, 2); else if (tf == 3) BGB_G16(true, 3); else BGB_G16(true, 4);
+        if (tf == 1) { BGB_G16S(true, 1) } else if (tf == 2) { BGB_G16S(true, 2) } else if (tf == 3) { BGB_G16S(true, 3) } else { BGB_G16S(true, 4) }
     } else {
-        if (tf == 1) BGB_G16(false, 1); else if (tf == 2) BGB_G16(false, 2); else if (tf == 3) BGB_G16(false, 3); else BGB_G16(false, 4);
+        if (tf == 1) { BGB_G16S(false, 1) } else if (tf == 2) { BGB_G16S(false, 2) } else if (tf == 3) { BGB_G16S(false, 3) } else { BGB_G16S(false, 4) }
     }
+#undef BGB_G16S
 #undef BGB_G16
     return hipGetLastError();
 }
