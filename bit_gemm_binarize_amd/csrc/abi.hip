@@ -106,7 +106,7 @@ static int bitlinear_params(const bgb_quant_params* qp, bgb_quant_params* p, flo
     *p = bgb_quant_params{1e-5, 8, 1e-3f};
     if (qp) *p = *qp;
     if (p->bits < 2 || p->bits > 8) return BGB_EUNSUPPORTED;
-    if (!(p->ln_eps >= 0.0) || !(p->q_eps >= 0.0f) || !(p->q_eps < 1.0f)) return BGB_EINVAL;
+    if (!(p->ln_eps > 0.0) || !(p->q_eps > 0.0f) || !(p->q_eps < 1.0f)) return BGB_EINVAL;
     *qb = float(1 << (p->bits - 1));
     *lim = *qb - p->q_eps;                       // fl32(Q_b - eps), as the reference computes it
     return BGB_OK;

@@ -111,6 +111,53 @@ BGB_DEV float wave_max63_nonneg(float v) {
     v = fmaxf(v, dpp_f32<0x143, 0xC>(v));
     return v;
 }
+// Max / min over the 64 lanes (any values), valid in lane 63; disabled rows of
+// the broadcast steps contribute the identity (-inf / +inf).
+template <int CTRL, int ROWMASK>
+BGB_DEV float dpp_f32_id(float v, float id) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(v), CTRL, ROWMASK, 0xF,
+                                                      false));
+}
+BGB_DEV float wave_max63(float v) {
+    const float id = -__builtin_inff();
+    v = fmaxf(v, dpp_f32_id<0xB1, 0xF>(v, id));
+    v = fmaxf(v, dpp_f32_id<0x4E, 0xF>(v, id));
+    v = fmaxf(v, dpp_f32_id<0x141, 0xF>(v, id));
+    v = fmaxf(v, dpp_f32_id<0x140, 0xF>(v, id));
+    v = fmaxf(v, dpp_f32_id<0x142, 0xA>(v, id));
+    v = fmaxf(v, dpp_f32_id<0x143, 0xC>(v, id));
+    return v;
+}
+BGB_DEV float wave_min63(float v) {
+    const float id = __builtin_inff();
+    v = fminf(v, dpp_f32_id<0xB1, 0xF>(v, id));
+    v = fminf(v, dpp_f32_id<0x4E, 0xF>(v, id));
+    v = fminf(v, dpp_f32_id<0x141, 0xF>(v, id));
+    v = fminf(v, dpp_f32_id<0x140, 0xF>(v, id));
+    v = fminf(v, dpp_f32_id<0x142, 0xA>(v, id));
+    v = fminf(v, dpp_f32_id<0x143, 0xC>(v, id));
+    return v;
+}
+// One block pass reducing (sum, max, min) together; `scr` holds NT/64 entries.
+struct SumMaxMin { double s; float mx, mn; };
+template <int NT>
+BGB_DEV SumMaxMin block_sum_max_min(double s, float mx, float mn, SumMaxMin* scr) {
+    s = wave_sum63(s);
+    mx = wave_max63(mx);
+    mn = wave_min63(mn);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 63) scr[threadIdx.x >> 6] = SumMaxMin{s, mx, mn};
+    __syncthreads();
+    SumMaxMin t = scr[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) {
+        t.s += scr[i].s;
+        t.mx = fmaxf(t.mx, scr[i].mx);
+        t.mn = fminf(t.mn, scr[i].mn);
+    }
+    return t;
+}
+
 // Block (NT threads) sum / max through the DPP wave reductions: lane 63 of
 // each wave parks its value in `scratch`, then every thread adds the NT/64
 // values in wave order. Contains two barriers.

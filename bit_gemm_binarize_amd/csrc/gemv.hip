@@ -218,91 +218,125 @@ template <> BGB_DEV void load4<uint16_t>(const uint16_t* x, int64_t e, float* v)
 
 constexpr int kFusedMaxKp = 16384;
 
-template <int NV, typename XT>
-__global__ void __launch_bounds__(256)
+// Single-token kernels: a block of NW waves owns 16 * NW / 4 columns (wave w:
+// column fragment w % (NW/4), K quarter w / (NW/4), steps quarter, quarter + 4,
+// ...). Each block runs the activation prologue once for its columns.
+constexpr int kD1Waves = 4;
+
+// Code of one activation, h already LayerNormed: trunc(clip(fl32(h Q_b / gamma),
+// +-lim)) for lim in (Q_b - 1, Q_b). Fast path: u = (h Q_b) rcp(gamma) is within
+// 1.5 ulp of the exact quotient, so unless u lies within |u| 2^-20 of an
+// integer no integer separates u from fl32(h Q_b / gamma) and trunc(u) (kept
+// inside +-(Q_b - 1)) is the same code; otherwise the exact division decides.
+BGB_DEV int code_of(float h, float qb, float gamma, float rg, float lim, int qmax) {
+    const float t = h * qb;
+    const float u = t * rg;
+    if (fabsf(u - rintf(u)) > fabsf(u) * 0x1p-20f) return max(-qmax, min(qmax, int(u)));
+    const float v = fminf(fmaxf(t / gamma, -lim), lim);
+    return int(v);
+}
+
+template <int NV, int NW, typename XT>
+__global__ void __launch_bounds__(NW * 64)
 bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
                          const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
                          int32_t* __restrict__ acc_opt, int8_t* __restrict__ xq_opt,
                          float* __restrict__ gamma_opt) {
+    constexpr int NT = NW * 64;
+    constexpr int F = NW / 4;                          // 16-column fragments per block
+    constexpr int S = NV * NW / 8 > 0 ? NV * NW / 8 : 1;   // steps per wave: 4 quarters x S x 512 rows >= Kp
     __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
-    __shared__ i32x4_t red[4][64];
-    __shared__ double dscr[4];
-    __shared__ float fscr[4];
-    __shared__ int iscr[4];
+    __shared__ i32x4_t red[NW][64];
+    __shared__ double dscr[NW];
+    __shared__ SumMaxMin smm[NW];
+    __shared__ int iscr[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, r = lane & 15;
-    const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
-    const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
+    const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
+    const int64_t j0 = int64_t(blockIdx.x) * 16 * F, j = j0 + 16 * f + r;
+    const int Kp = int(TQ * 128);
+    const int64_t steps = (TQ + 3) / 4;
+    const int Ki = int(K);
 
-    // 1. the token (an L2 hit after the first block) and then all of this
-    //    wave's sign tiles; issued in this order so that the prologue below
-    //    waits only for x while the tiles are still in flight
-    constexpr int S = NV / 2 > 0 ? NV / 2 : 1;        // steps per wave: 4 waves x S x 512 rows >= Kp
+    // 1. the token (an L2 hit after the first block), then all of this wave's
+    //    sign tiles; the scheduling barrier keeps every load ahead of the first
+    //    use of x, so the prologue runs while the tiles are in flight
     float v[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t e = (int64_t(i) * 256 + tid) * 4;
-        const bool ok = e < K;
+        const int e = (i * NT + tid) * 4;
+        const bool ok = e < Ki;
         const uint32_t keep = 0u - uint32_t(ok);      // masks (not selects): the load stays unconditional
         load4(x, ok ? e : 0, v[i]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[i][c] = __uint_as_float(__float_as_uint(v[i][c]) & keep);
     }
     u32x4_t w[S];
-    preload<S>(w, P, wave, 4, steps, TQ, N, j, g);
-    __builtin_amdgcn_sched_barrier(0);   // keep every load above the first use of x
+    preload<S>(w, P, kq, 4, steps, TQ, N, j, g);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 2. LayerNorm statistics (two fp64 passes) and the absmax of the token;
-    //    every block computes the same values
+    //    every block computes the same values. h(x) = fl32(fl32(x - mu32) rs32)
+    //    is monotone in x, so max |h| is |h| at the largest or smallest x: the
+    //    extremes ride along with the first sum and gamma needs no extra pass.
     double s = 0.0;
+    float xmx = -__builtin_inff(), xmn = __builtin_inff();
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+    for (int i = 0; i < NV; ++i) {
+        const bool ok = (i * NT + tid) * 4 < Ki;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) s += double(v[i][c]);
-    const double mu = block_sum_dpp<256>(s, dscr) / double(K);
+        for (int c = 0; c < 4; ++c) {
+            s += double(v[i][c]);
+            if (ok) {
+                xmx = fmaxf(xmx, v[i][c]);
+                xmn = fminf(xmn, v[i][c]);
+            }
+        }
+    }
+    const SumMaxMin st1 = block_sum_max_min<NT>(s, xmx, xmn, smm);
+    const double mu = st1.s / double(K);
     double s2 = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        if ((int64_t(i) * 256 + tid) * 4 >= K) continue;
+        if ((i * NT + tid) * 4 >= Ki) continue;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const double d = double(v[i][c]) - mu;
             s2 += d * d;
         }
     }
-    s2 = block_sum_dpp<256>(s2, dscr);
+    s2 = block_sum_dpp<NT>(s2, dscr);
     const float mu32 = float(mu);
     const float rs32 = float(1.0 / sqrt(s2 / double(K) + eps));
-    float lm = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            v[i][c] = (v[i][c] - mu32) * rs32;          // h
-            if ((int64_t(i) * 256 + tid) * 4 < K) lm = fmaxf(lm, fabsf(v[i][c]));
-        }
-    const float gamma = block_max_dpp<256>(lm, fscr);
+        for (int c = 0; c < 4; ++c) v[i][c] = (v[i][c] - mu32) * rs32;          // h
+    const float gamma = fmaxf(fabsf((st1.mx - mu32) * rs32), fabsf((st1.mn - mu32) * rs32));
 
     // 3. codes into LDS in the decode layout; zero padding rows K..Kp-1
+    const float rg = gamma != 0.0f ? __builtin_amdgcn_rcpf(gamma) : 0.0f;
+    const int qmax = int(qb) - 1;
     int sq = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t e = (int64_t(i) * 256 + tid) * 4;
-        if (e >= K) continue;
+        const int e = (i * NT + tid) * 4;
+        if (e >= Ki) continue;
+        int codes[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            int code = 0;
-            if (gamma != 0.0f) {
-                float t = (v[i][c] * qb) / gamma;
-                t = fminf(fmaxf(t, -lim), lim);
-                code = int(t);
-            }
-            qs[q_pos(e + c)] = int8_t(code);
-            sq += code;
-            if (xq_opt && blockIdx.x == 0) xq_opt[e + c] = int8_t(code);
+            codes[c] = gamma != 0.0f ? code_of(v[i][c], qb, gamma, rg, lim, qmax) : 0;
+            sq += codes[c];
         }
+        // rows e..e+3 share t and d, and their s = (e % 8) + c sit 16 bytes apart
+        const int t = e >> 5, b = e & 31;
+        int8_t* dst = qs + (t >> 2) * 128 + (b & 7) * 16 + (t & 3) * 4 + (b >> 3);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[16 * c] = int8_t(codes[c]);
+        if (xq_opt && blockIdx.x == 0)
+            *reinterpret_cast<uint32_t*>(xq_opt + e) = uint32_t(uint8_t(codes[0])) | uint32_t(uint8_t(codes[1])) << 8 |
+                                                       uint32_t(uint8_t(codes[2])) << 16 | uint32_t(uint8_t(codes[3])) << 24;
     }
-    for (int64_t k = K + tid; k < Kp; k += 256) qs[q_pos(k)] = 0;
+    for (int k = Ki + tid; k < Kp; k += NT) qs[q_pos(k)] = 0;
     if (gamma_opt && blockIdx.x == 0 && tid == 0) gamma_opt[0] = gamma;
     __syncthreads();
 
@@ -312,7 +346,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-        const int64_t st = wave + 4 * i;
+        const int64_t st = kq + 4 * i;
         const int64_t tq = st * 4 + g;
         const bool bv = st < steps && tq < TQ && r == 0;
         const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs + (bv ? tq : 0) * 128);
@@ -321,18 +355,20 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int s8 = 0; s8 < 8; ++s8) b[s8] = ld16_or0(src + s8, bv);
         w1a8_step(w[i], b, acc);
     }
-    // 5. partial sums of the 4 waves and the code row sum, one barrier
+    // 5. partial sums of the 4 quarters and the code row sum, one barrier
     red[wave][lane] = w1a8_combine(acc);
     sq = wave_sum63_i(sq);
     if (lane == 63) iscr[wave] = sq;
     __syncthreads();
-    if (wave != 0 || r != 0) return;
-    const int rowsum = ((iscr[0] + iscr[1]) + iscr[2]) + iscr[3];
-    const i32x4_t sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    if (kq != 0 || r != 0) return;
+    int rowsum = 0;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
+    const i32x4_t sum = ((red[f][lane] + red[f + F][lane]) + red[f + 2 * F][lane]) + red[f + 3 * F][lane];
     const float scale = (beta[0] * gamma) / qb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t col = j0 + 4 * g + i;
+        const int64_t col = j0 + 16 * f + 4 * g + i;
         if (col >= N) continue;
         const int32_t a = 2 * sum[i] - rowsum;
         y[col] = float(a) * scale;
@@ -342,27 +378,35 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
 
 bool w1a8_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
 
-hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
-                               const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
-                               float* gamma_opt, hipStream_t s) {
-    const unsigned grid = unsigned((N + 15) / 16);
+template <int NW>
+static void launch_w1a8_decode1_nw(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
+                                   const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
+                                   float* gamma_opt, hipStream_t s) {
+    constexpr unsigned nt = NW * 64;
+    const unsigned grid = unsigned((N + 16 * (NW / 4) - 1) / (16 * (NW / 4)));
     const int64_t TQ = tiles_per_col(K);
-    const int nv = int((K + 1023) / 1024);
+    const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
 #define BGB_D1(NVV)                                                                                              \
     if (x_bf16)                                                                                                  \
-        bitlinear_decode1_kernel<NVV, uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), K, N, TQ,   \
-                                                                     eps, qb, lim, P, beta, y, acc_opt, xq_opt,  \
-                                                                     gamma_opt);                                 \
+        bitlinear_decode1_kernel<NVV, NW, uint16_t><<<grid, nt, 0, s>>>(static_cast<const uint16_t*>(x), K, N,   \
+                                                                        TQ, eps, qb, lim, P, beta, y, acc_opt,   \
+                                                                        xq_opt, gamma_opt);                      \
     else                                                                                                         \
-        bitlinear_decode1_kernel<NVV, float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), K, N, TQ, eps,    \
-                                                                  qb, lim, P, beta, y, acc_opt, xq_opt,          \
-                                                                  gamma_opt);
+        bitlinear_decode1_kernel<NVV, NW, float><<<grid, nt, 0, s>>>(static_cast<const float*>(x), K, N, TQ,      \
+                                                                     eps, qb, lim, P, beta, y, acc_opt, xq_opt,  \
+                                                                     gamma_opt);
     if (nv <= 1) { BGB_D1(1) }
     else if (nv <= 2) { BGB_D1(2) }
     else if (nv <= 4) { BGB_D1(4) }
     else if (nv <= 8) { BGB_D1(8) }
     else { BGB_D1(16) }
 #undef BGB_D1
+}
+
+hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
+                               const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
+                               float* gamma_opt, hipStream_t s) {
+    launch_w1a8_decode1_nw<kD1Waves>(x, x_bf16, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
     return hipGetLastError();
 }
 
@@ -584,43 +628,50 @@ gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xp
 
 // Single token, activation staging fused: the block permutes x into LDS and
 // computes the four X_T itself.
-template <bool kF16, int NV>
-__global__ void __launch_bounds__(256)
+template <bool kF16, int NV, int NW>
+__global__ void __launch_bounds__(NW * 64)
 fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
                    const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
+    constexpr int NT = NW * 64;
+    constexpr int F = NW / 4;
+    constexpr int S = NV * NW / 8 > 0 ? NV * NW / 8 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
-    __shared__ f32x4_t red[4][4][64];
-    __shared__ double dX[4][4];
+    __shared__ f32x4_t red[NW][64];
+    __shared__ double dX[NW][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, r = lane & 15;
-    const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
-    const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
+    const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
+    const int64_t j0 = int64_t(blockIdx.x) * 16 * F, j = j0 + 16 * f + r;
+    const int Kp = int(TQ * 128);
+    const int64_t steps = (TQ + 3) / 4;
+    const int Ki = int(K);
 
-    // the token first (see the W1A8 kernel), then all of this wave's tiles
-    constexpr int S = NV / 2 > 0 ? NV / 2 : 1;
+    // the token first, then all of this wave's tiles (see the W1A8 kernel)
     uint2 xv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t k = (int64_t(i) * 256 + tid) * 4;
-        const uint32_t keep = 0u - uint32_t(k < K);   // masks (not selects): the load stays unconditional
-        const uint2 t = *reinterpret_cast<const uint2*>(x + (k < K ? k : 0));
+        const int k = (i * NT + tid) * 4;
+        const uint32_t keep = 0u - uint32_t(k < Ki);  // masks (not selects): the load stays unconditional
+        const uint2 t = *reinterpret_cast<const uint2*>(x + (k < Ki ? k : 0));
         xv[i] = uint2{t.x & keep, t.y & keep};
     }
     u32x4_t w[S];
-    preload<S>(w, P, wave, 4, steps, TQ, N, j, g);
-    __builtin_amdgcn_sched_barrier(0);   // keep every load above the first use of x
+    preload<S>(w, P, kq, 4, steps, TQ, N, j, g);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // stage: each thread moves 4 consecutive rows at a time (types 0..3 in order)
+    // stage rows k..k+3 (types 0..3, all with the same t and d; their u =
+    // (k % 16) + c sit 8 elements apart) and sum each type in fp64
     double xs4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t k = (int64_t(i) * 256 + tid) * 4;
+        const int k = (i * NT + tid) * 4;
         if (k >= Kp) continue;
         const uint16_t e[4] = {uint16_t(xv[i].x & 0xffffu), uint16_t(xv[i].x >> 16), uint16_t(xv[i].y & 0xffffu),
                                uint16_t(xv[i].y >> 16)};
+        const int t = k >> 5, b = k & 31;
+        uint16_t* dst = xs + (t >> 2) * 128 + (b & 15) * 8 + (t & 3) * 2 + (b >> 4);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            xs[x_pos(k + c)] = e[c];
+            dst[8 * c] = e[c];
             xs4[c] += double(kF16 ? f16_to_f32(e[c]) : bf16_to_f32(e[c]));
         }
     }
@@ -631,54 +682,63 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     for (int T = 0; T < 4; ++T) acc[0][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-        const int64_t st = wave + 4 * i;
+        const int64_t st = kq + 4 * i;
         const int64_t tq = st * 4 + g;
         const bool bv = st < steps && tq < TQ && r == 0;
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xs + (bv ? tq : 0) * 128);
         auto bsrc = [&](int u, int) -> u32x4_t { return ld16_or0(src + u, bv); };
         w1a16_step<kF16, 1>(w[i], bsrc, acc);
     }
-    // partial sums of the 4 waves and the four X_T, one barrier
-#pragma unroll
-    for (int T = 0; T < 4; ++T) red[wave][T][lane] = acc[0][T];
+    // per wave z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3 and the X_T partials, one barrier
+    red[wave][lane] = ((8.0f * acc[0][0] + 4.0f * acc[0][1]) + 2.0f * acc[0][2]) + 2.0f * acc[0][3];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const double t = wave_sum63(xs4[c]);
         if (lane == 63) dX[wave][c] = t;
     }
     __syncthreads();
-    if (wave != 0 || r != 0) return;
-    float X[4];
+    if (kq != 0 || r != 0) return;
+    double Xd[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) X[c] = float(((dX[0][c] + dX[1][c]) + dX[2][c]) + dX[3][c]);
-    f32x4_t tot[4];
+    for (int wv = 0; wv < NW; ++wv)
 #pragma unroll
-    for (int T = 0; T < 4; ++T) tot[T] = ((red[0][T][lane] + red[1][T][lane]) + red[2][T][lane]) + red[3][T][lane];
+        for (int c = 0; c < 4; ++c) Xd[c] += dX[wv][c];
+    const float X0 = float(Xd[0]), X1 = float(Xd[1]), X2 = float(Xd[2]), X3 = float(Xd[3]);
+    const float corr = ((8.0f * X0 + 4.0f * X1) + 2.0f * X2) + X3;
+    const float xall = ((X0 + X1) + X2) + X3;
+    const f32x4_t z = ((red[f][lane] + red[f + F][lane]) + red[f + 2 * F][lane]) + red[f + 3 * F][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t col = j0 + 4 * g + i;
+        const int64_t col = j0 + 16 * f + 4 * g + i;
         if (col >= N) continue;
-        store_y(y, y_dtype, col, load_alpha(alpha, alpha_f16, col) * w1a16_out(tot, i, X[0], X[1], X[2], X[3]));
+        store_y(y, y_dtype, col, load_alpha(alpha, alpha_f16, col) * (2.0f * (z[i] - corr) - xall));
     }
 }
 
 bool w1a16_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
 
-hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
-                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
-    const unsigned grid = unsigned((N + 15) / 16);
+template <int NW>
+static void launch_w1a16_decode1_nw(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
+                                    const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    constexpr unsigned nt = NW * 64;
+    const unsigned grid = unsigned((N + 16 * (NW / 4) - 1) / (16 * (NW / 4)));
     const uint16_t* xx = static_cast<const uint16_t*>(x);
     const int64_t TQ = tiles_per_col(K);
-    const int nv = int((TQ * 128 + 1023) / 1024);
-#define BGB_F1(NVV)                                                                                             \
-    if (x_f16) fbi_decode1_kernel<true, NVV><<<grid, 256, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype); \
-    else fbi_decode1_kernel<false, NVV><<<grid, 256, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype);
+    const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
+#define BGB_F1(NVV)                                                                                                \
+    if (x_f16) fbi_decode1_kernel<true, NVV, NW><<<grid, nt, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype); \
+    else fbi_decode1_kernel<false, NVV, NW><<<grid, nt, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype);
     if (nv <= 1) { BGB_F1(1) }
     else if (nv <= 2) { BGB_F1(2) }
     else if (nv <= 4) { BGB_F1(4) }
     else if (nv <= 8) { BGB_F1(8) }
     else { BGB_F1(16) }
 #undef BGB_F1
+}
+
+hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    launch_w1a16_decode1_nw<kD1Waves>(x, x_f16, K, N, P, alpha, alpha_f16, y, y_dtype, s);
     return hipGetLastError();
 }
 

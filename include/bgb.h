@@ -79,9 +79,9 @@ typedef enum {
 /* Activation quantization parameters of BitLinear ("BitNet b1.58: 1bit LLM时代",
  * section 一, eq. (4), (5), (8)). */
 typedef struct {
-    double ln_eps;   /* LayerNorm epsilon added to the variance (1e-5) */
+    double ln_eps;   /* LayerNorm epsilon added to the variance, > 0 (1e-5) */
     int bits;        /* b in Q_b = 2^(b-1); 2..8 (8 -> Q_b = 128, int8 codes) */
-    float q_eps;     /* clip margin: codes are clipped to [-Q_b+eps, Q_b-eps] (1e-3) */
+    float q_eps;     /* clip margin in (0, 1): codes are clipped to [-Q_b+eps, Q_b-eps] (1e-3) */
 } bgb_quant_params;
 
 /* Size in bytes of the packed array P for a K x N weight (0 if K is invalid). */
