@@ -98,7 +98,10 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
         if (e != hipSuccess) return finish(e);
         return finish(bgb::launch_w1a16_gemv(xp, xpart, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
     }
-    return finish(bgb::launch_w1a16_gemm(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
+    uint16_t* xi = reinterpret_cast<uint16_t*>(carve(ws, 0));
+    hipError_t e = bgb::launch_w1a16_interleave(x, M, K, xi, s);
+    if (e != hipSuccess) return finish(e);
+    return finish(bgb::launch_w1a16_gemm(xi, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
 }
 
 // Shared checks of the BitLinear entry points; fills qb/lim from qp.

@@ -41,11 +41,15 @@ struct PackBitnetWs {       // fp64 (sum W, sum |W|) per reduction block
     }
 };
 
-struct FbiLinearWs {        // decode only: permuted activations + per-chunk type sums
+struct FbiLinearWs {        // permuted activations (+ per-chunk type sums when decoding)
     size_t xp, xpart, total;
     static FbiLinearWs make(int64_t M, int64_t K) {
         FbiLinearWs w{};
-        if (M > kGemvMaxM) { w.xp = w.xpart = w.total = 0; return w; }
+        if (M > kGemvMaxM) {    // GEMM: interleaved activations only
+            w.xp = w.xpart = 0;
+            w.total = align256(size_t(M) * size_t(padded_k(K)) * 2);
+            return w;
+        }
         const size_t chunks = size_t((padded_k(K) + 1023) / 1024);
         w.xp = 0;
         w.xpart = align256(size_t(M) * size_t(padded_k(K)) * 2);
@@ -85,7 +89,10 @@ hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16,
                              int64_t K, int64_t N, const uint32_t* P, const void* alpha,
                              int alpha_f16, void* y, int y_dtype, hipStream_t s);
 
-hipError_t launch_w1a16_gemm(const void* x, int x_f16, int64_t M, int64_t K, int64_t N,
+// GEMM activations: xi[m][Kp], element pairs (row i, row i+16) of each 32-row group
+hipError_t launch_w1a16_interleave(const void* x, int64_t M, int64_t K, uint16_t* xi, hipStream_t s);
+
+hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N,
                              const uint32_t* P, const void* alpha, int alpha_f16, void* y,
                              int y_dtype, hipStream_t s);
 

@@ -53,7 +53,9 @@ def test_sizes(lib):
     assert bgb.packed_bytes(160, 3) == 2 * 3 * 16
     assert bgb.packed_bytes(4096, 11008) == 5636096
     assert bgb.packed_bytes(31, 5) == 0
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096) == 0        # GEMM path needs none
+    # GEMM path: the interleaved copy of the activations, M x padded K x 2 bytes
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096) == 65 * 4096 * 2
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4000, 4096) == 65 * 4096 * 2
     assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 64, 4096, 4096) >= 64 * 4096 * 2
     assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 16, 4096, 4096) >= 16 * 4096 * 2
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 1, 4096, 11008) >= 4096
@@ -97,6 +99,7 @@ def test_fbi_linear_validation(lib):
     assert call_fbi(lib, x=None) == BAD
     assert call_fbi(lib, y=A + 2) == BAD
     assert call_fbi(lib, wsb=0) == BAD                 # decode path needs a workspace
+    assert call_fbi(lib, M=100, wsb=100 * 128 * 2 - 1) == BAD   # so does the GEMM path
     assert call_fbi(lib, M=1 << 25) == BAD
     assert call_fbi(lib, M=0) == 0 and call_fbi(lib, N=0) == 0
 

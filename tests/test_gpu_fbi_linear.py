@@ -35,6 +35,8 @@ CASES = [
     (1, 768, 768), (1, 11008, 100), (1, 16416, 40), (8, 768, 768), (3, 96, 65), (16, 160, 300),
     (5, 4096, 33), (17, 96, 65), (40, 768, 260), (64, 2048, 520), (65, 256, 300), (130, 256, 300),
     (200, 352, 513),
+    # GEMM pipeline: 4-stage ring with 0 or 2 tail stages, ragged M/N, padded K
+    (150, 640, 300), (257, 1024, 1000), (300, 4000, 257),
 ]
 
 
