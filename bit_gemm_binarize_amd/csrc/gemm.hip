@@ -60,6 +60,13 @@ BGB_DEV void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N>
+BGB_DEV void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 BGB_DEV void dma16(const void* src, uint8_t* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
@@ -194,41 +201,60 @@ gemm_w1a16_kernel(const uint16_t* __restrict__ xi, int64_t M, int64_t Kp, int64_
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[f][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](int s, auto Bc) {
-        constexpr int B = decltype(Bc)::value;
-        // 5 VMEM ops per stage per thread; stages s+1, s+2 were issued after stage s
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<10>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(s + 3, (B + 3) % kRing);
-        const uint8_t* lb = lds[B];
+    // Operands of the next MFMA group, carried between steps: the shifted sign
+    // words and the v = 0 B fragments of the stage.
+    uint32_t X[4];
+    u32x4_t b0[8];
+    auto load_head = [&](int s, int B) {
         const int wb = wbyte + 8 * (s & 1);
-        uint32_t X[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) X[f] = *reinterpret_cast<const uint32_t*>(wls[B] + wb + 256 * f) >> wshift;
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            u32x4_t b[8];
-            const int bo = v ? boff1 : boff0;
+        for (int n = 0; n < 8; ++n) b0[n] = *reinterpret_cast<const u32x4_t*>(lds[B] + n * 2048 + boff0);
+    };
+    auto mfma_half = [&](int v, const uint32_t (&Xv)[4], const u32x4_t (&b)[8]) {
 #pragma unroll
-            for (int n = 0; n < 8; ++n) b[n] = *reinterpret_cast<const u32x4_t*>(lb + n * 2048 + bo);
+        for (int f = 0; f < 4; ++f) {
+            u32x4_t a;   // (~(X << s) & 0x80008000) | one: sign bits of rows 4u+e, 4u+e+16
+            a.x = __builtin_amdgcn_bitop3_b32(Xv[f] << (15 - 8 * v), 0x80008000u, kOne, 0xAE);
+            a.y = __builtin_amdgcn_bitop3_b32(Xv[f] << (14 - 8 * v), 0x80008000u, kOne, 0xAE);
+            a.z = __builtin_amdgcn_bitop3_b32(Xv[f] << (13 - 8 * v), 0x80008000u, kOne, 0xAE);
+            a.w = __builtin_amdgcn_bitop3_b32(Xv[f] << (12 - 8 * v), 0x80008000u, kOne, 0xAE);
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                u32x4_t a;   // (~(X << s) & 0x80008000) | one: sign bits of rows 4u+e, 4u+e+16
-                a.x = __builtin_amdgcn_bitop3_b32(X[f] << (15 - 8 * v), 0x80008000u, kOne, 0xAE);
-                a.y = __builtin_amdgcn_bitop3_b32(X[f] << (14 - 8 * v), 0x80008000u, kOne, 0xAE);
-                a.z = __builtin_amdgcn_bitop3_b32(X[f] << (13 - 8 * v), 0x80008000u, kOne, 0xAE);
-                a.w = __builtin_amdgcn_bitop3_b32(X[f] << (12 - 8 * v), 0x80008000u, kOne, 0xAE);
-#pragma unroll
-                for (int n = 0; n < 8; ++n) acc[f][n] = mfma16g<kF16>(a, b[n], acc[f][n]);
-            }
+            for (int n = 0; n < 8; ++n) acc[f][n] = mfma16g<kF16>(a, b[n], acc[f][n]);
         }
+    };
+    // Step s: the v = 0 half of stage s runs on operands fetched during the
+    // previous step while the v = 1 fragments load; then, once every wave has
+    // its stage-s reads back and stage s+1 has landed, one barrier frees ring
+    // slot s%4 for stage s+4 and the v = 1 half runs while the next stage's
+    // head operands load. Each thread issues 5 DMA operations per stage, and
+    // stages s+2 and s+3 are in flight behind stage s+1 at the barrier.
+    auto step = [&](int s, auto Bc) {
+        constexpr int B = decltype(Bc)::value;
+        u32x4_t b1[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) b1[n] = *reinterpret_cast<const u32x4_t*>(lds[B] + n * 2048 + boff1);
+        uint32_t Xc[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) Xc[f] = X[f];
+        mfma_half(0, Xc, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt_lgkm0<10>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + 4, B);
+        load_head(s + 1, (B + 1) % kRing);
+        mfma_half(1, Xc, b1);
     };
 
     issue(0, 0);
     issue(1, 1);
     issue(2, 2);
+    issue(3, 3);
+    wait_vmcnt<15>();
+    __builtin_amdgcn_s_barrier();
+    load_head(0, 0);
     int s = 0;
     for (; s + 4 <= T; s += 4) {
         step(s, std::integral_constant<int, 0>{});
@@ -338,41 +364,54 @@ gemm_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsu
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[f][n] = i32x4_t{0, 0, 0, 0};
 
-    auto step = [&](int s, auto Bc) {
-        constexpr int B = decltype(Bc)::value;
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<10>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(s + 3, (B + 3) % kRing);
-        const uint8_t* lb = lds[B];
-        uint32_t W[4];
+    uint32_t W[4];
+    i32x4_t b0[8];
+    auto load_head = [&](int B) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) W[f] = *reinterpret_cast<const uint32_t*>(wls[B] + wbyte + 256 * f);
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            i32x4_t b[8];
-            const int bo = v ? boff1 : boff0;
+        for (int n = 0; n < 8; ++n) b0[n] = *reinterpret_cast<const i32x4_t*>(lds[B] + n * 2048 + boff0);
+    };
+    auto mfma_half = [&](int v, const uint32_t (&Wv)[4], const i32x4_t (&b)[8]) {
 #pragma unroll
-            for (int n = 0; n < 8; ++n) b[n] = *reinterpret_cast<const i32x4_t*>(lb + n * 2048 + bo);
+        for (int f = 0; f < 4; ++f) {
+            const uint32_t w = Wv[f];
+            i32x4_t a;
+            a.x = int((w >> (4 * v + 0)) & 0x01010101u);
+            a.y = int((w >> (4 * v + 1)) & 0x01010101u);
+            a.z = int((w >> (4 * v + 2)) & 0x01010101u);
+            a.w = int((w >> (4 * v + 3)) & 0x01010101u);
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const uint32_t w = W[f];
-                i32x4_t a;
-                a.x = int((w >> (4 * v + 0)) & 0x01010101u);
-                a.y = int((w >> (4 * v + 1)) & 0x01010101u);
-                a.z = int((w >> (4 * v + 2)) & 0x01010101u);
-                a.w = int((w >> (4 * v + 3)) & 0x01010101u);
-#pragma unroll
-                for (int n = 0; n < 8; ++n)
-                    acc[f][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[f][n], 0, 0, 0);
-            }
+            for (int n = 0; n < 8; ++n)
+                acc[f][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[f][n], 0, 0, 0);
         }
+    };
+    // Same step structure as the W1A16 kernel.
+    auto step = [&](int s, auto Bc) {
+        constexpr int B = decltype(Bc)::value;
+        i32x4_t b1[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) b1[n] = *reinterpret_cast<const i32x4_t*>(lds[B] + n * 2048 + boff1);
+        uint32_t Wc[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) Wc[f] = W[f];
+        mfma_half(0, Wc, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt_lgkm0<10>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + 4, B);
+        load_head((B + 1) % kRing);
+        mfma_half(1, Wc, b1);
     };
 
     issue(0, 0);
     issue(1, 1);
     issue(2, 2);
+    issue(3, 3);
+    wait_vmcnt<15>();
+    __builtin_amdgcn_s_barrier();
+    load_head(0);
     int s = 0;
     for (; s + 4 <= T; s += 4) {
         step(s, std::integral_constant<int, 0>{});
