@@ -46,8 +46,8 @@ size_t bgb_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
     switch (op) {
         case BGB_OP_PACK_FBI: return bgb::PackFbiWs::make(K, N).total;
         case BGB_OP_PACK_BITNET: return bgb::PackBitnetWs::make().total;
-        case BGB_OP_FBI_LINEAR: return bgb::FbiLinearWs::make(M, K).total;
-        case BGB_OP_BITLINEAR: return bgb::BitlinearWs::make(M, K).total;
+        case BGB_OP_FBI_LINEAR: return bgb::FbiLinearWs::make(M, K, N).total;
+        case BGB_OP_BITLINEAR: return bgb::BitlinearWs::make(M, K, N).total;
         default: return 0;
     }
 }
@@ -83,7 +83,7 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
     if (M == 0 || N == 0) return BGB_OK;          // empty: nothing is read or written
     if (!x || !P || !alpha || !y) return BGB_EINVAL;
     if (!aligned16(x) || !aligned16(P) || !aligned16(alpha) || !aligned16(y)) return BGB_EINVAL;
-    const bgb::FbiLinearWs lay = bgb::FbiLinearWs::make(M, K);
+    const bgb::FbiLinearWs lay = bgb::FbiLinearWs::make(M, K, N);
     if (lay.total && (!ws || ws_bytes < lay.total || !aligned16(ws))) return BGB_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int x_f16 = x_dtype == BGB_F16;
@@ -101,7 +101,7 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
     uint16_t* xi = reinterpret_cast<uint16_t*>(carve(ws, 0));
     hipError_t e = bgb::launch_w1a16_interleave(x, M, K, xi, s);
     if (e != hipSuccess) return finish(e);
-    return finish(bgb::launch_w1a16_gemm(xi, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
+    return finish(bgb::launch_w1a16_gemm(xi, x_f16, M, K, N, P, alpha, a_f16, y, ydt, carve(ws, lay.part), s));
 }
 
 // Shared checks of the BitLinear entry points; fills qb/lim from qp.
@@ -127,7 +127,7 @@ int bitlinear_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const b
     if (!x || !aligned16(x)) return BGB_EINVAL;
     if ((gamma_opt && (reinterpret_cast<uintptr_t>(gamma_opt) & 3u)) || (xq_opt && !aligned16(xq_opt)))
         return BGB_EINVAL;
-    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, 0);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     const bool decode = M <= bgb::kGemvMaxM;
     return finish(bgb::launch_ln_quant(x, x_dtype == BGB_BF16, M, K, p.ln_eps, qb, lim, decode ? 0 : 1,
@@ -150,14 +150,14 @@ int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const f
     if (!P || !beta || !y || !aligned16(P) || !aligned16(y)) return BGB_EINVAL;
     if (reinterpret_cast<uintptr_t>(beta) & 3u) return BGB_EINVAL;
     if (acc_opt && !aligned16(acc_opt)) return BGB_EINVAL;
-    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int8_t* q = reinterpret_cast<const int8_t*>(carve(ws, lay.q));
     const int32_t* rowsum = reinterpret_cast<const int32_t*>(carve(ws, lay.rowsum));
     const float* gamma = reinterpret_cast<const float*>(carve(ws, lay.gamma));
     if (M <= bgb::kGemvMaxM) return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
-    return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
+    return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, carve(ws, lay.part), s));
 }
 
 int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
@@ -175,7 +175,7 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, 
     if ((reinterpret_cast<uintptr_t>(beta) & 3u) || (gamma_opt && (reinterpret_cast<uintptr_t>(gamma_opt) & 3u)))
         return BGB_EINVAL;
     if ((xq_opt && !aligned16(xq_opt)) || (acc_opt && !aligned16(acc_opt))) return BGB_EINVAL;
-    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K);
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     if (M == 1 && bgb::w1a8_decode1_supported(K)) {
         return finish(bgb::launch_w1a8_decode1(x, x_dtype == BGB_BF16, K, N, p.ln_eps, qb, lim, P, beta, y, acc_opt,

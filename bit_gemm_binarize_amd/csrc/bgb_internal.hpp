@@ -41,15 +41,25 @@ struct PackBitnetWs {       // fp64 (sum W, sum |W|) per reduction block
     }
 };
 
-struct FbiLinearWs {        // permuted activations (+ per-chunk type sums when decoding)
-    size_t xp, xpart, total;
-    static FbiLinearWs make(int64_t M, int64_t K) {
+// GEMM launch plan (a pure function of the shape): token fragments per wave
+// (BM = 16 nn), K splits and stages per split, tile grid.
+struct GemmPlan {
+    int nn, splits, per, T, ntm, ntj;
+};
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8);
+size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8);   // [splits][M][N] x 4 bytes, or 0
+
+struct FbiLinearWs {        // permuted activations (+ per-chunk type sums when decoding,
+    size_t xp, xpart, part, total;   //  + split-K partial sums for the GEMM)
+    static FbiLinearWs make(int64_t M, int64_t K, int64_t N) {
         FbiLinearWs w{};
-        if (M > kGemvMaxM) {    // GEMM: interleaved activations only
+        if (M > kGemvMaxM) {    // GEMM: interleaved activations, then the partials
             w.xp = w.xpart = 0;
-            w.total = align256(size_t(M) * size_t(padded_k(K)) * 2);
+            w.part = align256(size_t(M) * size_t(padded_k(K)) * 2);
+            w.total = w.part + gemm_partial_bytes(M, K, N, false);
             return w;
         }
+        w.part = 0;
         const size_t chunks = size_t((padded_k(K) + 1023) / 1024);
         w.xp = 0;
         w.xpart = align256(size_t(M) * size_t(padded_k(K)) * 2);
@@ -59,14 +69,16 @@ struct FbiLinearWs {        // permuted activations (+ per-chunk type sums when 
 };
 
 struct BitlinearWs {
-    size_t stats, gamma, rowsum, q, total;
-    static BitlinearWs make(int64_t M, int64_t K) {
+    size_t stats, gamma, rowsum, q, part, total;
+    // N = 0: the prologue's regions only (what bitlinear_quantize touches)
+    static BitlinearWs make(int64_t M, int64_t K, int64_t N) {
         BitlinearWs w{};
         w.stats = 0;                                               // float [M][3] mu32, rstd32, rowmax
         w.gamma = w.stats + align256(size_t(M) * 3 * sizeof(float));
         w.rowsum = w.gamma + 256;                                  // int32 [M]
         w.q = w.rowsum + align256(size_t(M) * sizeof(int32_t));    // int8 [M][Kp], layout per path
-        w.total = w.q + align256(size_t(M) * size_t(padded_k(K)));
+        w.part = w.q + align256(size_t(M) * size_t(padded_k(K)));  // int32 split-K partials (GEMM)
+        w.total = w.part + (M > kGemvMaxM && N > 0 ? gemm_partial_bytes(M, K, N, true) : 0);
         return w;
     }
 };
@@ -94,7 +106,7 @@ hipError_t launch_w1a16_interleave(const void* x, int64_t M, int64_t K, uint16_t
 
 hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N,
                              const uint32_t* P, const void* alpha, int alpha_f16, void* y,
-                             int y_dtype, hipStream_t s);
+                             int y_dtype, void* part, hipStream_t s);
 
 hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             const float* beta, float qb, int64_t M, int64_t K, int64_t N,
@@ -111,6 +123,6 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             const float* beta, float qb, int64_t M, int64_t K, int64_t N,
-                            const uint32_t* P, float* y, int32_t* acc_opt, hipStream_t s);
+                            const uint32_t* P, float* y, int32_t* acc_opt, void* part, hipStream_t s);
 
 }  // namespace bgb

@@ -1,19 +1,23 @@
-// Prefill kernels (M > 64): a dense contraction, so it runs on the matrix
-// cores. FBI-linear W1A16 (FBI-LLM news rewrite, FBI-linear paragraph) on
-// bf16/f16 MFMA with fp32 accumulation; BitLinear W1A8 ("BitNet b1.58: 1bit
-// LLM时代", section 一, eq. (7)) on int8 MFMA with int32 accumulation.
+// Prefill kernels: a dense contraction, so it runs on the matrix cores.
+// FBI-linear W1A16 (FBI-LLM news rewrite, FBI-linear paragraph) on bf16/f16
+// MFMA with fp32 accumulation; BitLinear W1A8 ("BitNet b1.58: 1bit LLM时代",
+// section 一, eq. (7)) on int8 MFMA with int32 accumulation.
 //
-// Tiling: a block of 4 waves computes a 256-column x 128-token tile; wave w
-// owns columns 64w..64w+63 (four 16-column MFMA fragments) for all 128
-// tokens (eight 16-token fragments): 32 accumulators of 16x16.
+// Tiling: a block of 4 waves computes a 256-column x BM-token tile (BM = 128
+// or 64); wave w owns columns 64w..64w+63 (four 16-column MFMA fragments)
+// for all BM tokens (NN = BM/16 token fragments): 4 x NN accumulators of
+// 16x16. A launch may split the K range over gridDim.y blocks per tile; each
+// split then stores its raw sums and a second kernel adds the splits in a
+// fixed order (so results are identical from run to run) and applies the
+// epilogue.
 //
 // Pipeline: the K loop runs over stages of 128 bytes of activations per token
 // (64 rows of bf16/f16, 128 rows of int8). Activation stages go from global
 // memory straight into LDS with global_load_lds_dwordx4 (no VGPR staging),
-// four stages in flight in a ring of four 16 KB buffers; the block's 4 KB sign
-// tile of a stage goes the same way into a second ring. One s_waitcnt +
-// s_barrier per stage; the waits are explicit because only the kernel knows
-// how many DMA operations a stage issues.
+// four stages in flight in a ring of four buffers; the block's 4 KB sign tile
+// of a stage goes the same way into a second ring. One s_waitcnt + s_barrier
+// per stage; the waits are explicit because only the kernel knows how many
+// DMA operations a stage issues.
 //
 // LDS layout of a stage: token row t at t*128 bytes, its eight 16-byte chunks
 // XOR-swizzled by a function of t so that the B-operand reads (a half-wave of
@@ -37,9 +41,7 @@
 
 namespace bgb {
 
-constexpr int kBM = 128;            // tokens per block tile
 constexpr int kBJ = 256;            // output columns per block tile
-constexpr int kStageBytes = 16384;  // kBM rows x 128 bytes
 constexpr int kRing = 4;            // stages in the LDS rings
 constexpr int kWTileBytes = kBJ * 16;   // one 128-row sign tile of the block's columns
 
@@ -59,7 +61,6 @@ BGB_DEV void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-
 // s_waitcnt vmcnt(N) lgkmcnt(0).
 template <int N>
 BGB_DEV void wait_vmcnt_lgkm0() {
@@ -75,36 +76,6 @@ BGB_DEV void dma16(const void* src, uint8_t* lds_wave_base) {
 // involutions on 0..7 and depend only on bits 2..3 of the token row.
 BGB_DEV int swz16(int t) { return 2 * ((t >> 2) & 3); }
 BGB_DEV int swz8(int t) { return ((t >> 2) & 1) | (((t >> 3) & 1) << 2); }
-
-// Per-thread DMA plan: instruction i of wave w moves stage chunks
-// (4i+w)*64 .. +63; lane L takes chunk p = (4i+w)*64 + L -> token row p>>3,
-// LDS slot p&7, source chunk (p&7) ^ swz(row). Rows past M read row M-1
-// (their outputs are never stored).
-template <bool k16>
-BGB_DEV void dma_plan(const uint8_t* base, int64_t row_bytes, int64_t m0, int64_t M, int tid,
-                      const uint8_t* (&src)[4]) {
-    const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = (4 * i + wave) * 64 + lane;
-        const int t = p >> 3, slot = p & 7;
-        const int c = slot ^ (k16 ? swz16(t) : swz8(t));
-        const int64_t m = m0 + t < M ? m0 + t : M - 1;
-        src[i] = base + m * row_bytes + 16 * c;
-    }
-}
-
-BGB_DEV void dma_stage(const uint8_t* const (&src)[4], int64_t off, uint8_t* buf, int wave) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src[i] + off, buf + (4 * i + wave) * 1024);
-}
-
-// Sign tile tq of the block's 256 columns: 16 bytes per column, thread tid
-// moves column j0 + tid (clamped to N-1) to byte 16*tid of the LDS tile.
-BGB_DEV const uint8_t* wtile_src(const uint32_t* P, int64_t j0, int64_t N, int tid) {
-    const int64_t j = j0 + tid < N ? j0 + tid : N - 1;
-    return reinterpret_cast<const uint8_t*>(P + j * 4);
-}
 
 // ------------------------------------------------------------ W1A16 prep ----
 // xi[m][Kp]: within each 32-row group, element 2i = x[m][32t+i] and element
@@ -152,99 +123,258 @@ hipError_t launch_w1a16_interleave(const void* x, int64_t M, int64_t K, uint16_t
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ W1A16 ----
+// ------------------------------------------------------------------- plan ----
+// Cost model, in microseconds: a stage of a 128-token block (two blocks per
+// CU sharing the matrix cores) takes kStageUs, a 64-token one kStageUs * 0.6;
+// each block adds kFixedStages stages of pipeline fill and epilogue; a split
+// launch adds the reduce pass (its traffic at kReduceBytesPerUs plus one
+// launch).
+namespace {
+constexpr double kStageUs = 1.6;
+constexpr double kFixedStages = 3.0;
+constexpr double kReduceBytesPerUs = 5.0e6;
+constexpr double kLaunchUs = 2.0;
+constexpr int kSlots = 512;         // resident blocks: 2 per CU on 256 CUs
+}  // namespace
+
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8) {
+    const int T = int(w1a8 ? tiles_per_col(K) : 2 * tiles_per_col(K));
+    const int ntj = int((N + kBJ - 1) / kBJ);
+    GemmPlan best{};
+    double best_t = 1e300;
+    for (int nn : {8, 4}) {
+        const int ntm = int((M + 16 * nn - 1) / (16 * nn));
+        const int64_t tiles = int64_t(ntm) * ntj;
+        const double stage = nn == 8 ? 1.0 : 0.6;
+        for (int S : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}) {
+            const int per = (T + S - 1) / S;
+            const int splits = (T + per - 1) / per;
+            if (splits != S) continue;                       // no S-way split with equal ranges
+            if (S > 1 && per < 2) break;
+            const int64_t units = tiles * splits;
+            const double rounds = double((units + kSlots - 1) / kSlots);
+            double t = rounds * (per + kFixedStages) * stage * kStageUs;
+            if (splits > 1) t += (double(splits + 1) * double(M) * double(N) * 4.0) / kReduceBytesPerUs + kLaunchUs;
+            if (t < best_t) {
+                best_t = t;
+                best.nn = nn;
+                best.splits = splits;
+                best.per = per;
+                best.T = T;
+                best.ntm = ntm;
+                best.ntj = ntj;
+            }
+        }
+    }
+    return best;
+}
+
+size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8) {
+    const GemmPlan p = gemm_plan(M, K, N, w1a8);
+    return p.splits > 1 ? align256(size_t(p.splits) * size_t(M) * size_t(N) * 4) : 0;
+}
+
+// ------------------------------------------------------------------ kernel ----
+struct GemmArgs {
+    const uint8_t* act;        // xi (W1A16, [M][Kp] 16-bit) or q (W1A8, [M][Kp] int8)
+    int64_t row_bytes;
+    const uint32_t* P;
+    int64_t M, N;
+    int T, per, ntj, ntiles;
+    // W1A16 epilogue
+    const void* alpha;
+    int alpha_f16;
+    void* y;
+    int y_dtype;
+    // W1A8 epilogue
+    const int32_t* rowsum;
+    const float* gamma;
+    const float* beta;
+    float qb;
+    int32_t* acc_opt;
+    // raw sums per split when the K range is split: [splits][M][N]
+    void* part;
+};
+
 BGB_DEV float alpha_at(const void* alpha, int alpha_f16, int64_t j) {
     return alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[j]) : static_cast<const float*>(alpha)[j];
 }
 
-template <bool kF16>
-__global__ void __launch_bounds__(256, 2)
-gemm_w1a16_kernel(const uint16_t* __restrict__ xi, int64_t M, int64_t Kp, int64_t N,
-                  const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
-                  void* __restrict__ y, int y_dtype, int ntj, int ntiles) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStageBytes];
+// Four consecutive outputs jb..jb+3 of one token, o = m * N + jb.
+BGB_DEV void store_out16(void* y, int y_dtype, int64_t o, const float (&v)[4], bool full, int64_t jb, int64_t N) {
+    if (full && y_dtype == kDtF32) {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + o) = f32x4_t{v[0], v[1], v[2], v[3]};
+    } else if (full) {
+        uint16_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = y_dtype == kDtBF16 ? f32_to_bf16_rne(v[i]) : f32_to_f16_rne(v[i]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + o) =
+            uint2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (jb + i >= N) continue;
+            if (y_dtype == kDtF32) static_cast<float*>(y)[o + i] = v[i];
+            else if (y_dtype == kDtBF16) static_cast<uint16_t*>(y)[o + i] = f32_to_bf16_rne(v[i]);
+            else static_cast<uint16_t*>(y)[o + i] = f32_to_f16_rne(v[i]);
+        }
+    }
+}
+
+BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& s, bool full, int64_t jb) {
+    const float scale = (a.beta[0] * a.gamma[0]) / a.qb;
+    const int32_t rs = a.rowsum[m];
+    i32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = 2 * s[i] - rs;
+    float* y = static_cast<float*>(a.y);
+    if (full) {
+        *reinterpret_cast<f32x4_t*>(y + o) =
+            f32x4_t{float(v[0]) * scale, float(v[1]) * scale, float(v[2]) * scale, float(v[3]) * scale};
+        if (a.acc_opt) *reinterpret_cast<i32x4_t*>(a.acc_opt + o) = v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (jb + i >= a.N) continue;
+            y[o + i] = float(v[i]) * scale;
+            if (a.acc_opt) a.acc_opt[o + i] = v[i];
+        }
+    }
+}
+
+// NN token fragments per wave (BM = 16 NN); kW1A8 selects the int8 path.
+template <bool kW1A8, bool kF16, int NN>
+__global__ void __launch_bounds__(256, 2) gemm_kernel(const GemmArgs a) {
+    constexpr int BM = 16 * NN;
+    constexpr int kStage = BM * 128;            // bytes of one activation stage
+    constexpr int kXDma = BM / 32;              // activation DMA operations per thread per stage
+    constexpr int kOps = kXDma + 1;             // + the sign tile
+    using acc_t = std::conditional_t<kW1A8, i32x4_t, f32x4_t>;
+    using opd_t = std::conditional_t<kW1A8, i32x4_t, u32x4_t>;
+    constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t wl0[kWTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t wl1[kWTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t wl2[kWTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t wl3[kWTileBytes];
     uint8_t* const lds[kRing] = {lds0, lds1, lds2, lds3};
     uint8_t* const wls[kRing] = {wl0, wl1, wl2, wl3};
-    const int tile = xcd_tile(blockIdx.x, ntiles);
-    if (tile >= ntiles) return;
-    const int64_t m0 = int64_t(tile / ntj) * kBM, j0 = int64_t(tile % ntj) * kBJ;
+
+    const int tile = xcd_tile(blockIdx.x, a.ntiles);
+    if (tile >= a.ntiles) return;
+    const int64_t m0 = int64_t(tile / a.ntj) * BM, j0 = int64_t(tile % a.ntj) * kBJ;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
-    const int T = int(Kp / 64);                 // stages, even and >= 2
-    constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;
+    const int z = blockIdx.y;
+    const int s0 = z * a.per;
+    const int ns = (s0 + a.per < a.T ? s0 + a.per : a.T) - s0;   // >= 1 by the plan
+    const int64_t M = a.M, N = a.N;
 
-    const uint8_t* src[4];
-    dma_plan<true>(reinterpret_cast<const uint8_t*>(xi), Kp * 2, m0, M, tid, src);
-    const uint8_t* wsrc = wtile_src(P, j0, N, tid);
-    const int wbyte = (64 * wave + r) * 16 + 4 * (g >> 1);   // + 256 f + 8 (s & 1): this lane's word
-    // B-operand byte offsets in a stage: token row 16n + r, chunk of MFMA v
-    const int rsw = swz16(r);
-    const int boff0 = r * 128 + 16 * ((4 * (g >> 1) + (g & 1)) ^ rsw);
-    const int boff1 = r * 128 + 16 * ((4 * (g >> 1) + 2 + (g & 1)) ^ rsw);
-    const int wshift = 4 * (g & 1);
-
-    auto issue = [&](int s, int B) {            // stage s (clamped: the tail re-reads the last stage)
-        const int sc = s < T ? s : T - 1;
-        dma_stage(src, int64_t(sc) * 128, lds[B], wave);
-        dma16(wsrc + int64_t(sc >> 1) * N * 16, wls[B] + wave * 1024);
+    // DMA plan: activation instruction i of wave w moves stage chunks
+    // (4i+w)*64 .. +63; lane L takes chunk p -> token row p>>3, LDS slot p&7,
+    // source chunk (p&7) ^ swz(row); rows past M read row M-1 (never stored).
+    // Thread tid moves column j0 + tid (clamped to N-1) of the sign tile.
+    const uint8_t* src[kXDma];
+#pragma unroll
+    for (int i = 0; i < kXDma; ++i) {
+        const int p = (4 * i + wave) * 64 + lane;
+        const int t = p >> 3, slot = p & 7;
+        const int c = slot ^ (kW1A8 ? swz8(t) : swz16(t));
+        const int64_t m = m0 + t < M ? m0 + t : M - 1;
+        src[i] = a.act + m * a.row_bytes + 16 * c;
+    }
+    const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(a.P + (j0 + tid < N ? j0 + tid : N - 1) * 4);
+    auto issue = [&](int rel, int B) {          // stage s0 + rel, clamped: the tail re-reads the last one
+        const int s = s0 + (rel < ns ? rel : ns - 1);
+#pragma unroll
+        for (int i = 0; i < kXDma; ++i) dma16(src[i] + int64_t(s) * 128, lds[B] + (4 * i + wave) * 1024);
+        const int64_t tq = kW1A8 ? s : (s >> 1);
+        dma16(wsrc + tq * N * 16, wls[B] + wave * 1024);
     };
 
-    f32x4_t acc[4][8];
+    // B-operand byte offsets in a stage (token row 16n + r) and this lane's sign word
+    int boff0, boff1, wbyte;
+    if constexpr (kW1A8) {
+        const int rsw = swz8(r);
+        boff0 = r * 128 + 16 * ((2 * g) ^ rsw);
+        boff1 = r * 128 + 16 * ((2 * g + 1) ^ rsw);
+        wbyte = (64 * wave + r) * 16 + 4 * g;                       // + 256 f
+    } else {
+        const int rsw = swz16(r);
+        boff0 = r * 128 + 16 * ((4 * (g >> 1) + (g & 1)) ^ rsw);
+        boff1 = r * 128 + 16 * ((4 * (g >> 1) + 2 + (g & 1)) ^ rsw);
+        wbyte = (64 * wave + r) * 16 + 4 * (g >> 1);                // + 256 f + 8 (s & 1)
+    }
+    const int wshift = 4 * (g & 1);
+
+    acc_t acc[4][NN];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) acc[f][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NN; ++n) acc[f][n] = acc_t{0, 0, 0, 0};
 
-    // Operands of the next MFMA group, carried between steps: the shifted sign
-    // words and the v = 0 B fragments of the stage.
+    // Operands of the next MFMA group, carried between steps: the sign words
+    // (shifted for W1A16) and the v = 0 B fragments of the stage.
     uint32_t X[4];
-    u32x4_t b0[8];
-    auto load_head = [&](int s, int B) {
-        const int wb = wbyte + 8 * (s & 1);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) X[f] = *reinterpret_cast<const uint32_t*>(wls[B] + wb + 256 * f) >> wshift;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) b0[n] = *reinterpret_cast<const u32x4_t*>(lds[B] + n * 2048 + boff0);
-    };
-    auto mfma_half = [&](int v, const uint32_t (&Xv)[4], const u32x4_t (&b)[8]) {
+    opd_t b0[NN];
+    auto load_head = [&](int rel, int B) {
+        const int wb = kW1A8 ? wbyte : wbyte + 8 * ((s0 + rel) & 1);
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            u32x4_t a;   // (~(X << s) & 0x80008000) | one: sign bits of rows 4u+e, 4u+e+16
-            a.x = __builtin_amdgcn_bitop3_b32(Xv[f] << (15 - 8 * v), 0x80008000u, kOne, 0xAE);
-            a.y = __builtin_amdgcn_bitop3_b32(Xv[f] << (14 - 8 * v), 0x80008000u, kOne, 0xAE);
-            a.z = __builtin_amdgcn_bitop3_b32(Xv[f] << (13 - 8 * v), 0x80008000u, kOne, 0xAE);
-            a.w = __builtin_amdgcn_bitop3_b32(Xv[f] << (12 - 8 * v), 0x80008000u, kOne, 0xAE);
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(wls[B] + wb + 256 * f);
+            X[f] = kW1A8 ? w : (w >> wshift);
+        }
 #pragma unroll
-            for (int n = 0; n < 8; ++n) acc[f][n] = mfma16g<kF16>(a, b[n], acc[f][n]);
+        for (int n = 0; n < NN; ++n) b0[n] = *reinterpret_cast<const opd_t*>(lds[B] + n * 2048 + boff0);
+    };
+    auto mfma_half = [&](int v, const uint32_t (&Xv)[4], const opd_t (&b)[NN]) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            if constexpr (kW1A8) {
+                const uint32_t w = Xv[f];
+                i32x4_t av;
+                av.x = int((w >> (4 * v + 0)) & 0x01010101u);
+                av.y = int((w >> (4 * v + 1)) & 0x01010101u);
+                av.z = int((w >> (4 * v + 2)) & 0x01010101u);
+                av.w = int((w >> (4 * v + 3)) & 0x01010101u);
+#pragma unroll
+                for (int n = 0; n < NN; ++n)
+                    acc[f][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b[n], acc[f][n], 0, 0, 0);
+            } else {
+                u32x4_t av;   // (~(X << s) & 0x80008000) | one: sign bits of rows 4u+e, 4u+e+16
+                av.x = __builtin_amdgcn_bitop3_b32(Xv[f] << (15 - 8 * v), 0x80008000u, kOne, 0xAE);
+                av.y = __builtin_amdgcn_bitop3_b32(Xv[f] << (14 - 8 * v), 0x80008000u, kOne, 0xAE);
+                av.z = __builtin_amdgcn_bitop3_b32(Xv[f] << (13 - 8 * v), 0x80008000u, kOne, 0xAE);
+                av.w = __builtin_amdgcn_bitop3_b32(Xv[f] << (12 - 8 * v), 0x80008000u, kOne, 0xAE);
+#pragma unroll
+                for (int n = 0; n < NN; ++n) acc[f][n] = mfma16g<kF16>(av, b[n], acc[f][n]);
+            }
         }
     };
-    // Step s: the v = 0 half of stage s runs on operands fetched during the
-    // previous step while the v = 1 fragments load; then, once every wave has
-    // its stage-s reads back and stage s+1 has landed, one barrier frees ring
-    // slot s%4 for stage s+4 and the v = 1 half runs while the next stage's
-    // head operands load. Each thread issues 5 DMA operations per stage, and
-    // stages s+2 and s+3 are in flight behind stage s+1 at the barrier.
-    auto step = [&](int s, auto Bc) {
+    // Step rel: the v = 0 half of the stage runs on operands fetched during
+    // the previous step while the v = 1 fragments load; then, once every wave
+    // has its reads of this stage back and the next stage has landed, one
+    // barrier frees ring slot rel%4 for stage rel+4 and the v = 1 half runs
+    // while the next stage's head operands load. Two later stages are in
+    // flight behind the next one at that barrier.
+    auto step = [&](int rel, auto Bc) {
         constexpr int B = decltype(Bc)::value;
-        u32x4_t b1[8];
+        opd_t b1[NN];
 #pragma unroll
-        for (int n = 0; n < 8; ++n) b1[n] = *reinterpret_cast<const u32x4_t*>(lds[B] + n * 2048 + boff1);
+        for (int n = 0; n < NN; ++n) b1[n] = *reinterpret_cast<const opd_t*>(lds[B] + n * 2048 + boff1);
         uint32_t Xc[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) Xc[f] = X[f];
         mfma_half(0, Xc, b0);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt_lgkm0<10>();
+        wait_vmcnt_lgkm0<2 * kOps>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(s + 4, B);
-        load_head(s + 1, (B + 1) % kRing);
+        issue(rel + 4, B);
+        load_head(rel + 1, (B + 1) % kRing);
         mfma_half(1, Xc, b1);
     };
 
@@ -252,216 +382,151 @@ gemm_w1a16_kernel(const uint16_t* __restrict__ xi, int64_t M, int64_t Kp, int64_
     issue(1, 1);
     issue(2, 2);
     issue(3, 3);
-    wait_vmcnt<15>();
+    wait_vmcnt<3 * kOps>();
     __builtin_amdgcn_s_barrier();
     load_head(0, 0);
-    int s = 0;
-    for (; s + 4 <= T; s += 4) {
-        step(s, std::integral_constant<int, 0>{});
-        step(s + 1, std::integral_constant<int, 1>{});
-        step(s + 2, std::integral_constant<int, 2>{});
-        step(s + 3, std::integral_constant<int, 3>{});
+    int rel = 0;
+    for (; rel + 4 <= ns; rel += 4) {
+        step(rel, std::integral_constant<int, 0>{});
+        step(rel + 1, std::integral_constant<int, 1>{});
+        step(rel + 2, std::integral_constant<int, 2>{});
+        step(rel + 3, std::integral_constant<int, 3>{});
     }
-    if (s < T) {                                // T even: two stages left
-        step(s, std::integral_constant<int, 0>{});
-        step(s + 1, std::integral_constant<int, 1>{});
-    }
+    if (rel < ns) step(rel, std::integral_constant<int, 0>{});
+    if (rel + 1 < ns) step(rel + 1, std::integral_constant<int, 1>{});
+    if (rel + 2 < ns) step(rel + 2, std::integral_constant<int, 2>{});
     wait_vmcnt<0>();                            // no LDS DMA may outlive the block
 
+    // Epilogue: lane (g, r) holds columns jb..jb+3 of token 16n + r.
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         const int64_t jb = j0 + 64 * wave + 16 * f + 4 * g;
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = jb + i < N ? alpha_at(alpha, alpha_f16, jb + i) : 0.0f;
         const bool full = jb + 4 <= N && (N & 3) == 0;
+        float al[4] = {0.f, 0.f, 0.f, 0.f};
+        if (!kW1A8 && !a.part) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+            for (int i = 0; i < 4; ++i) al[i] = jb + i < N ? alpha_at(a.alpha, a.alpha_f16, jb + i) : 0.0f;
+        }
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
             const int64_t m = m0 + 16 * n + r;
             if (m >= M) continue;
             const int64_t o = m * N + jb;
-            const float v0 = al[0] * acc[f][n][0], v1 = al[1] * acc[f][n][1];
-            const float v2 = al[2] * acc[f][n][2], v3 = al[3] * acc[f][n][3];
-            if (full && y_dtype == kDtF32) {
-                *reinterpret_cast<f32x4_t*>(static_cast<float*>(y) + o) = f32x4_t{v0, v1, v2, v3};
-            } else if (full) {
-                uint16_t h[4];
-                if (y_dtype == kDtBF16) {
-                    h[0] = f32_to_bf16_rne(v0); h[1] = f32_to_bf16_rne(v1);
-                    h[2] = f32_to_bf16_rne(v2); h[3] = f32_to_bf16_rne(v3);
+            if (a.part) {                       // raw sums of this split
+                const int64_t po = int64_t(z) * M * N + o;
+                if (full) {
+                    *reinterpret_cast<acc_t*>(static_cast<char*>(a.part) + po * 4) = acc[f][n];
                 } else {
-                    h[0] = f32_to_f16_rne(v0); h[1] = f32_to_f16_rne(v1);
-                    h[2] = f32_to_f16_rne(v2); h[3] = f32_to_f16_rne(v3);
-                }
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + o) =
-                    uint2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-            } else {
-                const float vv[4] = {v0, v1, v2, v3};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (jb + i >= N) continue;
-                    if (y_dtype == kDtF32) static_cast<float*>(y)[o + i] = vv[i];
-                    else if (y_dtype == kDtBF16) static_cast<uint16_t*>(y)[o + i] = f32_to_bf16_rne(vv[i]);
-                    else static_cast<uint16_t*>(y)[o + i] = f32_to_f16_rne(vv[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        if (jb + i >= N) continue;
+                        if constexpr (kW1A8) static_cast<int32_t*>(a.part)[po + i] = acc[f][n][i];
+                        else static_cast<float*>(a.part)[po + i] = acc[f][n][i];
+                    }
                 }
+            } else if constexpr (kW1A8) {
+                store_out8(a, o, m, acc[f][n], full, jb);
+            } else {
+                const float v[4] = {al[0] * acc[f][n][0], al[1] * acc[f][n][1], al[2] * acc[f][n][2],
+                                    al[3] * acc[f][n][3]};
+                store_out16(a.y, a.y_dtype, o, v, full, jb, N);
             }
         }
     }
 }
 
-hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
-                             const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
-    const int ntj = int((N + kBJ - 1) / kBJ), ntm = int((M + kBM - 1) / kBM);
-    const int ntiles = ntj * ntm;
-    const unsigned grid = unsigned(xcd_grid(ntiles));
-    const int64_t Kp = padded_k(K);
-    if (x_f16)
-        gemm_w1a16_kernel<true><<<grid, 256, 0, s>>>(xi, M, Kp, N, P, alpha, alpha_f16, y, y_dtype, ntj, ntiles);
-    else
-        gemm_w1a16_kernel<false><<<grid, 256, 0, s>>>(xi, M, Kp, N, P, alpha, alpha_f16, y, y_dtype, ntj, ntiles);
+// Sum of the splits in split order, then the epilogue. One thread per 4
+// consecutive columns of one token.
+template <bool kW1A8>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs a, int splits) {
+    const int64_t M = a.M, N = a.N, nq = (N + 3) / 4;
+    const int64_t id = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (id >= M * nq) return;
+    const int64_t m = id / nq, jb = 4 * (id % nq), o = m * N + jb;
+    const bool full = jb + 4 <= N && (N & 3) == 0;
+    const int64_t MN = M * N;
+    if constexpr (kW1A8) {
+        const int32_t* p = static_cast<const int32_t*>(a.part);
+        i32x4_t s = {0, 0, 0, 0};
+        for (int z = 0; z < splits; ++z) {
+            if (full) {
+                s += *reinterpret_cast<const i32x4_t*>(p + z * MN + o);
+            } else {
+                for (int i = 0; i < 4; ++i)
+                    if (jb + i < N) s[i] += p[z * MN + o + i];
+            }
+        }
+        store_out8(a, o, m, s, full, jb);
+    } else {
+        const float* p = static_cast<const float*>(a.part);
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        for (int z = 0; z < splits; ++z) {
+            if (full) {
+                s += *reinterpret_cast<const f32x4_t*>(p + z * MN + o);
+            } else {
+                for (int i = 0; i < 4; ++i)
+                    if (jb + i < N) s[i] += p[z * MN + o + i];
+            }
+        }
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = jb + i < N ? alpha_at(a.alpha, a.alpha_f16, jb + i) * s[i] : 0.0f;
+        store_out16(a.y, a.y_dtype, o, v, full, jb, N);
+    }
+}
+
+template <bool kW1A8, bool kF16>
+static hipError_t launch_gemm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
+    const int ntiles = p.ntm * p.ntj;
+    a.T = p.T;
+    a.per = p.per;
+    a.ntj = p.ntj;
+    a.ntiles = ntiles;
+    const dim3 grid(unsigned(xcd_grid(ntiles)), unsigned(p.splits));
+    if (p.nn == 8) gemm_kernel<kW1A8, kF16, 8><<<grid, 256, 0, s>>>(a);
+    else gemm_kernel<kW1A8, kF16, 4><<<grid, 256, 0, s>>>(a);
+    if (p.splits > 1) {
+        const int64_t n = a.M * ((a.N + 3) / 4);
+        splitk_reduce_kernel<kW1A8><<<unsigned((n + 255) / 256), 256, 0, s>>>(a, p.splits);
+    }
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------- W1A8 ----
-__global__ void __launch_bounds__(256, 2)
-gemm_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsum, const float* __restrict__ gamma,
-                 const float* __restrict__ beta, float qb, int64_t M, int64_t N, int64_t TQ,
-                 const uint32_t* __restrict__ P, float* __restrict__ y, int32_t* __restrict__ acc_opt, int ntj,
-                 int ntiles) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl0[kWTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl1[kWTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl2[kWTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl3[kWTileBytes];
-    uint8_t* const lds[kRing] = {lds0, lds1, lds2, lds3};
-    uint8_t* const wls[kRing] = {wl0, wl1, wl2, wl3};
-    const int tile = xcd_tile(blockIdx.x, ntiles);
-    if (tile >= ntiles) return;
-    const int64_t m0 = int64_t(tile / ntj) * kBM, j0 = int64_t(tile % ntj) * kBJ;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
-    const int T = int(TQ);                      // one stage per 128-row tile, >= 1
-
-    const uint8_t* src[4];
-    dma_plan<false>(reinterpret_cast<const uint8_t*>(q), TQ * 128, m0, M, tid, src);
-    const uint8_t* wsrc = wtile_src(P, j0, N, tid);
-    const int wbyte = (64 * wave + r) * 16 + 4 * g;          // + 256 f: this lane's word
-    const int rsw = swz8(r);
-    const int boff0 = r * 128 + 16 * ((2 * g) ^ rsw);
-    const int boff1 = r * 128 + 16 * ((2 * g + 1) ^ rsw);
-
-    auto issue = [&](int s, int B) {
-        const int sc = s < T ? s : T - 1;
-        dma_stage(src, int64_t(sc) * 128, lds[B], wave);
-        dma16(wsrc + int64_t(sc) * N * 16, wls[B] + wave * 1024);
-    };
-
-    i32x4_t acc[4][8];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[f][n] = i32x4_t{0, 0, 0, 0};
-
-    uint32_t W[4];
-    i32x4_t b0[8];
-    auto load_head = [&](int B) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) W[f] = *reinterpret_cast<const uint32_t*>(wls[B] + wbyte + 256 * f);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) b0[n] = *reinterpret_cast<const i32x4_t*>(lds[B] + n * 2048 + boff0);
-    };
-    auto mfma_half = [&](int v, const uint32_t (&Wv)[4], const i32x4_t (&b)[8]) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const uint32_t w = Wv[f];
-            i32x4_t a;
-            a.x = int((w >> (4 * v + 0)) & 0x01010101u);
-            a.y = int((w >> (4 * v + 1)) & 0x01010101u);
-            a.z = int((w >> (4 * v + 2)) & 0x01010101u);
-            a.w = int((w >> (4 * v + 3)) & 0x01010101u);
-#pragma unroll
-            for (int n = 0; n < 8; ++n)
-                acc[f][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[n], acc[f][n], 0, 0, 0);
-        }
-    };
-    // Same step structure as the W1A16 kernel.
-    auto step = [&](int s, auto Bc) {
-        constexpr int B = decltype(Bc)::value;
-        i32x4_t b1[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) b1[n] = *reinterpret_cast<const i32x4_t*>(lds[B] + n * 2048 + boff1);
-        uint32_t Wc[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) Wc[f] = W[f];
-        mfma_half(0, Wc, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt_lgkm0<10>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(s + 4, B);
-        load_head((B + 1) % kRing);
-        mfma_half(1, Wc, b1);
-    };
-
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    issue(3, 3);
-    wait_vmcnt<15>();
-    __builtin_amdgcn_s_barrier();
-    load_head(0);
-    int s = 0;
-    for (; s + 4 <= T; s += 4) {
-        step(s, std::integral_constant<int, 0>{});
-        step(s + 1, std::integral_constant<int, 1>{});
-        step(s + 2, std::integral_constant<int, 2>{});
-        step(s + 3, std::integral_constant<int, 3>{});
-    }
-    if (s < T) step(s, std::integral_constant<int, 0>{});
-    if (s + 1 < T) step(s + 1, std::integral_constant<int, 1>{});
-    if (s + 2 < T) step(s + 2, std::integral_constant<int, 2>{});
-    wait_vmcnt<0>();
-
-    const float scale = (beta[0] * gamma[0]) / qb;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        const int64_t jb = j0 + 64 * wave + 16 * f + 4 * g;
-        const bool full = jb + 4 <= N && (N & 3) == 0;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            const int64_t m = m0 + 16 * n + r;
-            if (m >= M) continue;
-            const int32_t rs = rowsum[m];
-            const int64_t o = m * N + jb;
-            i32x4_t a;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = 2 * acc[f][n][i] - rs;
-            if (full) {
-                *reinterpret_cast<f32x4_t*>(y + o) =
-                    f32x4_t{float(a[0]) * scale, float(a[1]) * scale, float(a[2]) * scale, float(a[3]) * scale};
-                if (acc_opt) *reinterpret_cast<i32x4_t*>(acc_opt + o) = a;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (jb + i >= N) continue;
-                    y[o + i] = float(a[i]) * scale;
-                    if (acc_opt) acc_opt[o + i] = a[i];
-                }
-            }
-        }
-    }
+hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                             const void* alpha, int alpha_f16, void* y, int y_dtype, void* part, hipStream_t s) {
+    const GemmPlan p = gemm_plan(M, K, N, false);
+    GemmArgs a{};
+    a.act = reinterpret_cast<const uint8_t*>(xi);
+    a.row_bytes = padded_k(K) * 2;
+    a.P = P;
+    a.M = M;
+    a.N = N;
+    a.alpha = alpha;
+    a.alpha_f16 = alpha_f16;
+    a.y = y;
+    a.y_dtype = y_dtype;
+    a.part = p.splits > 1 ? part : nullptr;
+    return x_f16 ? launch_gemm<false, true>(a, p, s) : launch_gemm<false, false>(a, p, s);
 }
 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma, const float* beta, float qb,
                             int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
-                            hipStream_t s) {
-    const int ntj = int((N + kBJ - 1) / kBJ), ntm = int((M + kBM - 1) / kBM);
-    const int ntiles = ntj * ntm;
-    gemm_w1a8_kernel<<<unsigned(xcd_grid(ntiles)), 256, 0, s>>>(q, rowsum, gamma, beta, qb, M, N, tiles_per_col(K),
-                                                                  P, y, acc_opt, ntj, ntiles);
-    return hipGetLastError();
+                            void* part, hipStream_t s) {
+    const GemmPlan p = gemm_plan(M, K, N, true);
+    GemmArgs a{};
+    a.act = reinterpret_cast<const uint8_t*>(q);
+    a.row_bytes = padded_k(K);
+    a.P = P;
+    a.M = M;
+    a.N = N;
+    a.rowsum = rowsum;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.qb = qb;
+    a.y = y;
+    a.acc_opt = acc_opt;
+    a.part = p.splits > 1 ? part : nullptr;
+    return launch_gemm<true, false>(a, p, s);
 }
 
 }  // namespace bgb

@@ -53,9 +53,13 @@ def test_sizes(lib):
     assert bgb.packed_bytes(160, 3) == 2 * 3 * 16
     assert bgb.packed_bytes(4096, 11008) == 5636096
     assert bgb.packed_bytes(31, 5) == 0
-    # GEMM path: the interleaved copy of the activations, M x padded K x 2 bytes
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096) == 65 * 4096 * 2
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4000, 4096) == 65 * 4096 * 2
+    # GEMM path: the interleaved copy of the activations (M x padded K x 2 bytes),
+    # plus fp32 partial sums when the launch plan splits K (small M x N)
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 4096, 4096, 11008) == 4096 * 4096 * 2
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 4096, 4000, 11008) == 4096 * 4096 * 2
+    small = bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096)
+    assert small >= 65 * 4096 * 2 and (small - 65 * 4096 * 2) % (65 * 4096 * 4) == 0
+    assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 11008) == bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 0)
     assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 64, 4096, 4096) >= 64 * 4096 * 2
     assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 16, 4096, 4096) >= 16 * 4096 * 2
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 1, 4096, 11008) >= 4096
