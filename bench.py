@@ -358,6 +358,33 @@ def leg_stack_1p3b(torch, bgb, syn):
                                            "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops,
                                            "linears": L * len(shapes), "bound": "mfma"}
         log(f"1.3B stack {name}: {ms * 1e3:.0f} us/step, {tf:.0f} TFLOP/s")
+    del layers
+    torch.cuda.empty_cache()
+    # the same stack with each layer's same-input linears concatenated column-wise
+    # before packing (q|k|v -> N = 6144, gate|up -> N = 11264): 4 launches per layer
+    H, F = 2048, 5632
+    fshapes = [("qkv", H, 3 * H), ("o", H, H), ("gate_up", H, 2 * F), ("down", F, H)]
+    flayers = [build_layer(torch, bgb, syn, cfg["seed"], fshapes, 50 + l, torch.float16) for l in range(L)]
+    for name, M in (("decode_b64", cfg["decode_batch"]), ("prefill_2x1024", cfg["prefill_tokens"])):
+        xs = {K: torch.randn((M, K), device="cuda").to(torch.bfloat16) for K in (H, F)}
+        ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, _, N in fshapes}
+        wsz = max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, N) for _, K, N in fshapes)
+        ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
+
+        def fbody(i, xs=xs, ys=ys, ws=ws):
+            for Ps, As in flayers:
+                for li, (_, K, N) in enumerate(fshapes):
+                    bgb.fbi_linear_w1a16(xs[K], Ps[li], As[li], N, y=ys[N], ws=ws)
+
+        n = 10 if M <= 64 else 3
+        ms = graph_time(torch, fbody, n, 2) / n
+        flops = 2 * M * sum(K * N for _, K, N in fshapes) * L
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"w1a16_1p3b_stack_fused_{name}"] = {"ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                                 "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops,
+                                                 "linears": L * len(fshapes), "bound": "mfma"}
+        log(f"1.3B stack fused {name}: {ms * 1e3:.0f} us/step, {tf:.0f} TFLOP/s")
+    del flayers
     return out
 
 

@@ -9,7 +9,7 @@
 namespace bgb {
 
 constexpr int kWords4 = 4;             // words per 16-byte column tile (128 rows)
-constexpr int kGemvMaxM = 64;          // M <= 64 -> decode (streaming) kernels
+constexpr int kGemvMaxM = 32;          // M <= 32 -> decode (streaming) kernels, above: MFMA GEMM
 constexpr int kSmallPrologueM = 16;    // M <= 16 -> single-block LN + quant prologue
 constexpr int kMaxK = 524288;
 

@@ -1,4 +1,4 @@
-// Decode kernels (M <= 64): stream the packed signs once from HBM and run the
+// Decode kernels (M <= 32): stream the packed signs once from HBM and run the
 // contraction on the matrix cores, tokens padded to 16-token fragments.
 //
 // FBI-linear W1A16 (FBI-LLM news rewrite, FBI-linear paragraph):

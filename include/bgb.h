@@ -122,7 +122,7 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
  * accepted). y: [M][N] in y_dtype (F32, BF16 or F16; 16-bit outputs are
  * rounded to nearest even). Products of +-1 and x are exact; sums use fp32
  * accumulation on the matrix cores; alpha is applied once to the fp32 sum.
- * M <= 64 runs the memory-bound decode kernels, M > 64 the MFMA GEMM.
+ * M <= 32 runs the memory-bound decode kernels, M > 32 the MFMA GEMM.
  * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes (both paths keep
  * a re-ordered copy of x there: M x Kp x 2 bytes, Kp = K rounded up to 128,
  * plus fp64 partial sums when decoding).
@@ -147,7 +147,7 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
  * Optional outputs (NULL to skip): xq_opt int8 [M][K] codes, gamma_opt device
  * float scalar, acc_opt int32 [M][N].
  * ws: bgb_workspace_bytes(BGB_OP_BITLINEAR, M, K, N) bytes.
- * M <= 16 runs the memory-bound decode kernel, M > 16 the int8 MFMA GEMM.
+ * M <= 32 runs the memory-bound decode kernels, M > 32 the int8 MFMA GEMM.
  * Errors: BGB_EINVAL, BGB_EUNSUPPORTED, BGB_EHIP.
  */
 int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,

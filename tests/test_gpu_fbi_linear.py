@@ -1,4 +1,4 @@
-"""GPU parity: fbi_linear_w1a16 (decode kernel for M <= 16, MFMA GEMM above)
+"""GPU parity: fbi_linear_w1a16 (decode kernels for M <= 32, MFMA GEMM above)
 against the fp64 oracle, plus exactness probes that pin the bit layout."""
 import numpy as np
 import pytest
@@ -31,7 +31,8 @@ def _run(bgb, orc, W, xb, x_kind, y_kind, adt="f32"):
 CASES = [
     # (M, K, N) covering every dispatch path: single-token fused decode (M = 1,
     # K <= 16384), single token beyond the fused size, decode with 1..4 token
-    # fragments (M <= 64), and the MFMA GEMM (M > 64); ragged N and K tails.
+    # fragments (M <= 32), and the MFMA GEMM (M > 32, split-K plans for small
+    # M x N); ragged N and K tails.
     (1, 768, 768), (1, 11008, 100), (1, 16416, 40), (8, 768, 768), (3, 96, 65), (16, 160, 300),
     (5, 4096, 33), (17, 96, 65), (40, 768, 260), (64, 2048, 520), (65, 256, 300), (130, 256, 300),
     (200, 352, 513),
