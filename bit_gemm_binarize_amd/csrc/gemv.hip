@@ -205,208 +205,266 @@ gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsu
 }
 
 // Single token, prologue fused: x [K] (float or bf16 bits), K <= 1024 * NV.
-template <typename XT> BGB_DEV void load4(const XT* x, int64_t e, float* v);
-template <> BGB_DEV void load4<float>(const float* x, int64_t e, float* v) {
-    const float4 t = *reinterpret_cast<const float4*>(x + e);
-    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-}
-template <> BGB_DEV void load4<uint16_t>(const uint16_t* x, int64_t e, float* v) {
-    const uint2 t = *reinterpret_cast<const uint2*>(x + e);
-    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
-    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
-}
+template <typename XT> BGB_DEV float load1(const XT* x, int64_t k);
+template <> BGB_DEV float load1<float>(const float* x, int64_t k) { return x[k]; }
+template <> BGB_DEV float load1<uint16_t>(const uint16_t* x, int64_t k) { return __uint_as_float(uint32_t(x[k]) << 16); }
 
 constexpr int kFusedMaxKp = 16384;
 
 // Single-token kernels: a block of NW waves owns 16 * NW / 4 columns (wave w:
 // column fragment w % (NW/4), K quarter w / (NW/4), steps quarter, quarter + 4,
 // ...). Each block runs the activation prologue once for its columns.
-constexpr int kD1Waves = 4;
+constexpr int kD1Waves = 4;         // W1A16 single-token blocks
+constexpr int kD1WavesW1A8 = 8;     // W1A8: two 16-column fragments per group
 
 // Code of one activation, h already LayerNormed: trunc(clip(fl32(h Q_b / gamma),
-// +-lim)) for lim in (Q_b - 1, Q_b). Fast path: u = (h Q_b) rcp(gamma) is within
-// 1.5 ulp of the exact quotient, so unless u lies within |u| 2^-20 of an
-// integer no integer separates u from fl32(h Q_b / gamma) and trunc(u) (kept
-// inside +-(Q_b - 1)) is the same code; otherwise the exact division decides.
-BGB_DEV int code_of(float h, float qb, float gamma, float rg, float lim, int qmax) {
-    const float t = h * qb;
-    const float u = t * rg;
-    if (fabsf(u - rintf(u)) > fabsf(u) * 0x1p-20f) return max(-qmax, min(qmax, int(u)));
-    const float v = fminf(fmaxf(t / gamma, -lim), lim);
-    return int(v);
+// +-lim)), lim in (Q_b - 1, Q_b).
+BGB_DEV int exact_code(float h, float qb, float gamma, float lim) {
+    return int(fminf(fmaxf((h * qb) / gamma, -lim), lim));
 }
 
-template <int NV, int NW, typename XT>
+template <int NV, int NW, int IT, typename XT>
 __global__ void __launch_bounds__(NW * 64)
 bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
                          const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
                          int32_t* __restrict__ acc_opt, int8_t* __restrict__ xq_opt,
                          float* __restrict__ gamma_opt) {
     constexpr int NT = NW * 64;
-    constexpr int F = NW / 4;                          // 16-column fragments per block
+    constexpr int F = NW / 4;                          // 16-column fragments per column group
     constexpr int S = NV * NW / 8 > 0 ? NV * NW / 8 : 1;   // steps per wave: 4 quarters x S x 512 rows >= Kp
     __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
-    __shared__ i32x4_t red[NW][64];
+    __shared__ i32x4_t red[2][NW][64];
     __shared__ double dscr[NW];
     __shared__ SumMaxMin smm[NW];
     __shared__ int iscr[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
-    const int64_t j0 = int64_t(blockIdx.x) * 16 * F, j = j0 + 16 * f + r;
+    const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
     const int Kp = int(TQ * 128);
     const int64_t steps = (TQ + 3) / 4;
-    const int Ki = int(K);
+    const int pairs = int(K / 4);                      // (t, s): rows 32t + s + 8c, c = 0..3
 
-    // 1. the token (an L2 hit after the first block), then all of this wave's
-    //    sign tiles; the scheduling barrier keeps every load ahead of the first
-    //    use of x, so the prologue runs while the tiles are in flight
+    // 1. the token (an L2 hit after the first block): thread tid owns the
+    //    pairs p = i * NT + tid, i.e. the rows of one dword of the decode
+    //    layout each. The loads complete before any sign tile is requested, so
+    //    the token does not queue behind the layer's stream; the tiles are then
+    //    in flight during the whole prologue.
     float v[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int e = (i * NT + tid) * 4;
-        const bool ok = e < Ki;
-        const uint32_t keep = 0u - uint32_t(ok);      // masks (not selects): the load stays unconditional
-        load4(x, ok ? e : 0, v[i]);
+        const int p = i * NT + tid;
+        const bool ok = p < pairs;
+        const uint32_t keep = 0u - uint32_t(ok);      // masks (not selects): the loads stay unconditional
+        const int64_t k0 = ok ? int64_t(32 * (p >> 3) + (p & 7)) : 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[i][c] = __uint_as_float(__float_as_uint(v[i][c]) & keep);
+        for (int c = 0; c < 4; ++c) v[i][c] = __uint_as_float(__float_as_uint(load1(x, k0 + 8 * c)) & keep);
     }
-    u32x4_t w[S];
-    preload<S>(w, P, kq, 4, steps, TQ, N, j, g);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
+    // the sign tiles of all of this block's column groups (groups past the
+    // last one and columns past N load as zeros)
+    u32x4_t w[IT][S];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
+        preload<S>(w[it], P, kq, 4, steps, TQ, N, jj, g);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. LayerNorm statistics (two fp64 passes) and the absmax of the token;
     //    every block computes the same values. h(x) = fl32(fl32(x - mu32) rs32)
     //    is monotone in x, so max |h| is |h| at the largest or smallest x: the
     //    extremes ride along with the first sum and gamma needs no extra pass.
+    //    Pairs past K hold zeros: they add nothing to the sums and are left
+    //    out of the extremes a pair at a time.
+    double xd[NV][4];
     double s = 0.0;
     float xmx = -__builtin_inff(), xmn = __builtin_inff();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const bool ok = (i * NT + tid) * 4 < Ki;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            s += double(v[i][c]);
-            if (ok) {
-                xmx = fmaxf(xmx, v[i][c]);
-                xmn = fminf(xmn, v[i][c]);
-            }
+            xd[i][c] = double(v[i][c]);
+            s += xd[i][c];
+        }
+        const float gmx = fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3]));
+        const float gmn = fminf(fminf(v[i][0], v[i][1]), fminf(v[i][2], v[i][3]));
+        if (i * NT + tid < pairs) {
+            xmx = fmaxf(xmx, gmx);
+            xmn = fminf(xmn, gmn);
         }
     }
-    const SumMaxMin st1 = block_sum_max_min<NT>(s, xmx, xmn, smm);
+    s = wave_sum63(s);
+    xmx = wave_max63(xmx);
+    xmn = wave_min63(xmn);
+    if (lane == 63) smm[wave] = SumMaxMin{s, xmx, xmn};
+    __syncthreads();
+    SumMaxMin st1 = smm[0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) {
+        st1.s += smm[wv].s;
+        st1.mx = fmaxf(st1.mx, smm[wv].mx);
+        st1.mn = fminf(st1.mn, smm[wv].mn);
+    }
     const double mu = st1.s / double(K);
     double s2 = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        if ((i * NT + tid) * 4 >= Ki) continue;
+        const double keep = i * NT + tid < pairs ? 1.0 : 0.0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const double d = double(v[i][c]) - mu;
+            const double d = (xd[i][c] - mu) * keep;
             s2 += d * d;
         }
     }
-    s2 = block_sum_dpp<NT>(s2, dscr);
+    s2 = wave_sum63(s2);
+    if (lane == 63) dscr[wave] = s2;
+    __syncthreads();
+    double v2 = dscr[0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) v2 += dscr[wv];
     const float mu32 = float(mu);
-    const float rs32 = float(1.0 / sqrt(s2 / double(K) + eps));
+    const float rs32 = float(1.0 / sqrt(v2 / double(K) + eps));
+    const float gamma = fmaxf(fabsf((st1.mx - mu32) * rs32), fabsf((st1.mn - mu32) * rs32));
+
+    // 3. codes into LDS in the decode layout, one dword per pair; zero
+    //    padding rows K..Kp-1. Fast path u = h (Q_b rcp(gamma)) (Q_b is a power
+    //    of two, so this is fl32(fl32(h Q_b) rcp(gamma))), which is within 1.5
+    //    ulp of the exact quotient: unless u lies within |u| 2^-20 of an
+    //    integer, no integer separates them and trunc(u), kept inside
+    //    +-(Q_b - 1), is the code. Near-integer cases (rare; they include h = 0
+    //    and the extreme element) take the exact division.
+    const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
+    const int qmax = int(qb) - 1;
+    int codes[NV][4];
+    uint32_t slow = 0;                                 // bit 4i + c: needs the exact quotient
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[i][c] = (v[i][c] - mu32) * rs32;          // h
-    const float gamma = fmaxf(fabsf((st1.mx - mu32) * rs32), fabsf((st1.mn - mu32) * rs32));
-
-    // 3. codes into LDS in the decode layout; zero padding rows K..Kp-1
-    const float rg = gamma != 0.0f ? __builtin_amdgcn_rcpf(gamma) : 0.0f;
-    const int qmax = int(qb) - 1;
+        for (int c = 0; c < 4; ++c) {
+            const float h = (v[i][c] - mu32) * rs32;
+            v[i][c] = h;
+            const float u = h * cq;
+            slow |= uint32_t(fabsf(u - rintf(u)) <= fabsf(u) * 0x1p-20f) << (4 * i + c);
+            codes[i][c] = max(-qmax, min(qmax, int(u)));
+        }
+    if (slow && gamma != 0.0f) {                       // rare (gamma = 0: every h and code is 0)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (slow & (1u << (4 * i + c))) codes[i][c] = exact_code(v[i][c], qb, gamma, lim);
+    }
     int sq = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int e = (i * NT + tid) * 4;
-        if (e >= Ki) continue;
-        int codes[4];
+        const int p = i * NT + tid;
+        if (p >= pairs) continue;
+        const uint32_t word = uint32_t(uint8_t(codes[i][0])) | uint32_t(uint8_t(codes[i][1])) << 8 |
+                              uint32_t(uint8_t(codes[i][2])) << 16 | uint32_t(uint8_t(codes[i][3])) << 24;
+        sq += (codes[i][0] + codes[i][1]) + (codes[i][2] + codes[i][3]);
+        const int t = p >> 3, sr = p & 7;
+        *reinterpret_cast<uint32_t*>(qs + (t >> 2) * 128 + sr * 16 + (t & 3) * 4) = word;
+        if (xq_opt && blockIdx.x == 0) {
+            const int64_t k0 = 32 * t + sr;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            codes[c] = gamma != 0.0f ? code_of(v[i][c], qb, gamma, rg, lim, qmax) : 0;
-            sq += codes[c];
+            for (int c = 0; c < 4; ++c) xq_opt[k0 + 8 * c] = int8_t(codes[i][c]);
         }
-        // rows e..e+3 share t and d, and their s = (e % 8) + c sit 16 bytes apart
-        const int t = e >> 5, b = e & 31;
-        int8_t* dst = qs + (t >> 2) * 128 + (b & 7) * 16 + (t & 3) * 4 + (b >> 3);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dst[16 * c] = int8_t(codes[c]);
-        if (xq_opt && blockIdx.x == 0)
-            *reinterpret_cast<uint32_t*>(xq_opt + e) = uint32_t(uint8_t(codes[0])) | uint32_t(uint8_t(codes[1])) << 8 |
-                                                       uint32_t(uint8_t(codes[2])) << 16 | uint32_t(uint8_t(codes[3])) << 24;
     }
-    for (int k = Ki + tid; k < Kp; k += NT) qs[q_pos(k)] = 0;
+    for (int k = int(K) + tid; k < Kp; k += NT) qs[q_pos(k)] = 0;
     if (gamma_opt && blockIdx.x == 0 && tid == 0) gamma_opt[0] = gamma;
     __syncthreads();
 
-    // 4. the product: token 0 lives in lanes with r == 0, the rest are zero
-    i32x4_t acc[8];
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-        const int64_t st = kq + 4 * i;
-        const int64_t tq = st * 4 + g;
-        const bool bv = st < steps && tq < TQ && r == 0;
-        const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs + (bv ? tq : 0) * 128);
-        i32x4_t b[8];
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) b[s8] = ld16_or0(src + s8, bv);
-        w1a8_step(w[i], b, acc);
-    }
-    // 5. partial sums of the 4 quarters and the code row sum, one barrier
-    red[wave][lane] = w1a8_combine(acc);
+    // 4. per column group: the product (token 0 lives in lanes with r == 0,
+    //    the rest are zero), then the 4 quarters' partial sums and the code
+    //    row sum through LDS, one barrier per group
     sq = wave_sum63_i(sq);
     if (lane == 63) iscr[wave] = sq;
-    __syncthreads();
-    if (kq != 0 || r != 0) return;
-    int rowsum = 0;
-#pragma unroll
-    for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
-    const i32x4_t sum = ((red[f][lane] + red[f + F][lane]) + red[f + 2 * F][lane]) + red[f + 3 * F][lane];
     const float scale = (beta[0] * gamma) / qb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t col = j0 + 16 * f + 4 * g + i;
-        if (col >= N) continue;
-        const int32_t a = 2 * sum[i] - rowsum;
-        y[col] = float(a) * scale;
-        if (acc_opt) acc_opt[col] = a;
+    for (int it = 0; it < IT; ++it) {
+        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        if (grp >= ngroups) break;
+        i32x4_t acc[8];
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int64_t st = kq + 4 * i;
+            const int64_t tq = st * 4 + g;
+            // lanes r != 0 carry tokens whose outputs are never read, and steps
+            // past the column's tiles have all-zero signs: no masking needed
+            const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs + (st < steps && tq < TQ ? tq : 0) * 128);
+            i32x4_t b[8];
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) b[s8] = src[s8];
+            w1a8_step(w[it][i], b, acc);
+        }
+        red[it & 1][wave][lane] = w1a8_combine(acc);
+        __syncthreads();
+        if (kq == 0 && r == 0) {
+            int rowsum = 0;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
+            const i32x4_t (&rd)[NW][64] = red[it & 1];
+            const i32x4_t sum = ((rd[f][lane] + rd[f + F][lane]) + rd[f + 2 * F][lane]) + rd[f + 3 * F][lane];
+            const int64_t j0 = grp * 16 * F;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t col = j0 + 16 * f + 4 * g + i;
+                if (col >= N) continue;
+                const int32_t a = 2 * sum[i] - rowsum;
+                y[col] = float(a) * scale;
+                if (acc_opt) acc_opt[col] = a;
+            }
+        }
     }
 }
 
 bool w1a8_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
+
+// One block per CU runs the prologue once and then takes up to 4 column
+// groups, blockIdx.x + i * gridDim.x.
+constexpr int kD1MaxGrid = 256;
 
 template <int NW>
 static void launch_w1a8_decode1_nw(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
                                    const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                    float* gamma_opt, hipStream_t s) {
     constexpr unsigned nt = NW * 64;
-    const unsigned grid = unsigned((N + 16 * (NW / 4) - 1) / (16 * (NW / 4)));
     const int64_t TQ = tiles_per_col(K);
     const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
-#define BGB_D1(NVV)                                                                                              \
+    const int it_max = nv * NW >= 64 ? 2 : 4;          // keeps the preloaded tiles in registers
+    const int64_t ngroups = (N + 16 * (NW / 4) - 1) / (16 * (NW / 4));
+    int64_t grid = ngroups < kD1MaxGrid ? ngroups : kD1MaxGrid;
+    int it = int((ngroups + grid - 1) / grid);
+    if (it > it_max) {
+        it = it_max;
+        grid = (ngroups + it_max - 1) / it_max;
+    }
+#define BGB_D1X(NVV, ITV)                                                                                        \
     if (x_bf16)                                                                                                  \
-        bitlinear_decode1_kernel<NVV, NW, uint16_t><<<grid, nt, 0, s>>>(static_cast<const uint16_t*>(x), K, N,   \
-                                                                        TQ, eps, qb, lim, P, beta, y, acc_opt,   \
-                                                                        xq_opt, gamma_opt);                      \
+        bitlinear_decode1_kernel<NVV, NW, ITV, uint16_t><<<unsigned(grid), nt, 0, s>>>(                          \
+            static_cast<const uint16_t*>(x), K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt);    \
     else                                                                                                         \
-        bitlinear_decode1_kernel<NVV, NW, float><<<grid, nt, 0, s>>>(static_cast<const float*>(x), K, N, TQ,      \
-                                                                     eps, qb, lim, P, beta, y, acc_opt, xq_opt,  \
-                                                                     gamma_opt);
+        bitlinear_decode1_kernel<NVV, NW, ITV, float><<<unsigned(grid), nt, 0, s>>>(                             \
+            static_cast<const float*>(x), K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt);
+#define BGB_D1(NVV)                                                                                              \
+    if (it == 1) { BGB_D1X(NVV, 1) } else if (it == 2) { BGB_D1X(NVV, 2) } else if (it == 3) { BGB_D1X(NVV, 3) } \
+    else { BGB_D1X(NVV, 4) }
     if (nv <= 1) { BGB_D1(1) }
     else if (nv <= 2) { BGB_D1(2) }
     else if (nv <= 4) { BGB_D1(4) }
     else if (nv <= 8) { BGB_D1(8) }
     else { BGB_D1(16) }
 #undef BGB_D1
+#undef BGB_D1X
 }
 
 hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
                                const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                float* gamma_opt, hipStream_t s) {
-    launch_w1a8_decode1_nw<kD1Waves>(x, x_bf16, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+    launch_w1a8_decode1_nw<kD1WavesW1A8>(x, x_bf16, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
     return hipGetLastError();
 }
 
