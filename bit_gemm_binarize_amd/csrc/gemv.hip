@@ -214,7 +214,7 @@ constexpr int kFusedMaxKp = 16384;
 // Single-token kernels: a block of NW waves owns 16 * NW / 4 columns (wave w:
 // column fragment w % (NW/4), K quarter w / (NW/4), steps quarter, quarter + 4,
 // ...). Each block runs the activation prologue once for its columns.
-constexpr int kD1Waves = 4;         // W1A16 single-token blocks
+constexpr int kD1Waves = 8;         // W1A16 single-token blocks
 constexpr int kD1WavesW1A8 = 8;     // W1A8: two 16-column fragments per group
 
 // Code of one activation, h already LayerNormed: trunc(clip(fl32(h Q_b / gamma),
@@ -685,77 +685,76 @@ gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xp
 }
 
 // Single token, activation staging fused: the block permutes x into LDS and
-// computes the four X_T itself.
-template <bool kF16, int NV, int NW>
+// computes the four X_T itself, once, then takes up to IT column groups
+// (blockIdx.x + i * gridDim.x) of 16 * NW / 4 columns, as the W1A8 kernel.
+// Thread tid stages the chunks p = i * NT + tid of the decode layout: chunk
+// (tile Tt, u) holds rows 128 Tt + 32 d + u + 16 h at element 2 d + h, all of
+// type u % 4 = tid % 4.
+template <bool kF16, int NV, int NW, int IT>
 __global__ void __launch_bounds__(NW * 64)
 fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
                    const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
     constexpr int NT = NW * 64;
     constexpr int F = NW / 4;
-    constexpr int S = NV * NW / 8 > 0 ? NV * NW / 8 : 1;
+    constexpr int S = NV * NW / 4;     // steps per wave: TQ <= NV NT / 16 tiles, so 4 quarters x S x 4 tiles cover them
     __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
-    __shared__ f32x4_t red[NW][64];
+    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];   // B operand of steps past the last tile
+    __shared__ f32x4_t red[2][NW][64];
     __shared__ double dX[NW][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
-    const int64_t j0 = int64_t(blockIdx.x) * 16 * F, j = j0 + 16 * f + r;
-    const int Kp = int(TQ * 128);
+    const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
+    const int nchunks = int(TQ * 16);
     const int64_t steps = (TQ + 3) / 4;
     const int Ki = int(K);
 
-    // the token first, then all of this wave's tiles (see the W1A8 kernel)
-    uint2 xv[NV];
+    // 1. the token's chunks (loads complete before the sign stream starts)
+    uint32_t xv[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int k = (i * NT + tid) * 4;
-        const uint32_t keep = 0u - uint32_t(k < Ki);  // masks (not selects): the load stays unconditional
-        const uint2 t = *reinterpret_cast<const uint2*>(x + (k < Ki ? k : 0));
-        xv[i] = uint2{t.x & keep, t.y & keep};
-    }
-    u32x4_t w[S];
-    preload<S>(w, P, kq, 4, steps, TQ, N, j, g);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // stage rows k..k+3 (types 0..3, all with the same t and d; their u =
-    // (k % 16) + c sit 8 elements apart) and sum each type in fp64
-    double xs4[4] = {0.0, 0.0, 0.0, 0.0};
+        const int p = i * NT + tid;
+        const int row0 = 128 * (p >> 4) + (p & 15);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int k = (i * NT + tid) * 4;
-        if (k >= Kp) continue;
-        const uint16_t e[4] = {uint16_t(xv[i].x & 0xffffu), uint16_t(xv[i].x >> 16), uint16_t(xv[i].y & 0xffffu),
-                               uint16_t(xv[i].y >> 16)};
-        const int t = k >> 5, b = k & 31;
-        uint16_t* dst = xs + (t >> 2) * 128 + (b & 15) * 8 + (t & 3) * 2 + (b >> 4);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            dst[8 * c] = e[c];
-            xs4[c] += double(kF16 ? f16_to_f32(e[c]) : bf16_to_f32(e[c]));
+        for (int d = 0; d < 4; ++d) {
+            const int k0 = row0 + 32 * d, k1 = k0 + 16;
+            const uint32_t keep0 = 0u - uint32_t(p < nchunks && k0 < Ki);   // masks: the loads stay unconditional
+            const uint32_t keep1 = 0u - uint32_t(p < nchunks && k1 < Ki);
+            const uint32_t e0 = uint32_t(x[k0 < Ki ? k0 : 0]) & keep0;
+            const uint32_t e1 = uint32_t(x[k1 < Ki ? k1 : 0]) & keep1;
+            xv[i][d] = e0 | (e1 << 16);
         }
     }
-    __syncthreads();
-
-    f32x4_t acc[1][4];
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
+    u32x4_t w[IT][S];
 #pragma unroll
-    for (int T = 0; T < 4; ++T) acc[0][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-        const int64_t st = kq + 4 * i;
-        const int64_t tq = st * 4 + g;
-        const bool bv = st < steps && tq < TQ && r == 0;
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xs + (bv ? tq : 0) * 128);
-        auto bsrc = [&](int u, int) -> u32x4_t { return ld16_or0(src + u, bv); };
-        w1a16_step<kF16, 1>(w[i], bsrc, acc);
+    for (int it = 0; it < IT; ++it) {
+        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
+        preload<S>(w[it], P, kq, 4, steps, TQ, N, jj, g);
     }
-    // per wave z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3 and the X_T partials, one barrier
-    red[wave][lane] = ((8.0f * acc[0][0] + 4.0f * acc[0][1]) + 2.0f * acc[0][2]) + 2.0f * acc[0][3];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. stage the chunks, sum this thread's type in fp64
+    if (tid < 16) reinterpret_cast<u32x4_t*>(xzero)[tid] = u32x4_t{0u, 0u, 0u, 0u};
+    double xsum = 0.0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int p = i * NT + tid;
+        if (p >= nchunks) continue;
+        *reinterpret_cast<u32x4_t*>(xs + (p >> 4) * 128 + (p & 15) * 8) =
+            u32x4_t{xv[i][0], xv[i][1], xv[i][2], xv[i][3]};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint16_t lo = uint16_t(xv[i][d] & 0xffffu), hi = uint16_t(xv[i][d] >> 16);
+            xsum += double(kF16 ? f16_to_f32(lo) : bf16_to_f32(lo)) + double(kF16 ? f16_to_f32(hi) : bf16_to_f32(hi));
+        }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const double t = wave_sum63(xs4[c]);
+        const double t = wave_sum63((tid & 3) == c ? xsum : 0.0);
         if (lane == 63) dX[wave][c] = t;
     }
     __syncthreads();
-    if (kq != 0 || r != 0) return;
     double Xd[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv)
@@ -764,12 +763,40 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     const float X0 = float(Xd[0]), X1 = float(Xd[1]), X2 = float(Xd[2]), X3 = float(Xd[3]);
     const float corr = ((8.0f * X0 + 4.0f * X1) + 2.0f * X2) + X3;
     const float xall = ((X0 + X1) + X2) + X3;
-    const f32x4_t z = ((red[f][lane] + red[f + F][lane]) + red[f + 2 * F][lane]) + red[f + 3 * F][lane];
+
+    // 3. per column group: the product (token 0 lives in lanes with r == 0;
+    //    the other lanes' tokens are never read; tiles past the last one read
+    //    zero activations, since a zero sign word decodes to -1 weights), then
+    //    the quarters' sums through LDS
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t col = j0 + 16 * f + 4 * g + i;
-        if (col >= N) continue;
-        store_y(y, y_dtype, col, load_alpha(alpha, alpha_f16, col) * (2.0f * (z[i] - corr) - xall));
+    for (int it = 0; it < IT; ++it) {
+        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        if (grp >= ngroups) break;
+        f32x4_t acc[1][4];
+#pragma unroll
+        for (int T = 0; T < 4; ++T) acc[0][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int64_t st = kq + 4 * i;
+            const int64_t tq = st * 4 + g;
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(st < steps && tq < TQ ? xs + tq * 128 : xzero);
+            auto bsrc = [&](int u, int) -> u32x4_t { return src[u]; };
+            w1a16_step<kF16, 1>(w[it][i], bsrc, acc);
+        }
+        // per wave z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3
+        red[it & 1][wave][lane] = ((8.0f * acc[0][0] + 4.0f * acc[0][1]) + 2.0f * acc[0][2]) + 2.0f * acc[0][3];
+        __syncthreads();
+        if (kq == 0 && r == 0) {
+            const f32x4_t (&rd)[NW][64] = red[it & 1];
+            const f32x4_t z = ((rd[f][lane] + rd[f + F][lane]) + rd[f + 2 * F][lane]) + rd[f + 3 * F][lane];
+            const int64_t j0 = grp * 16 * F;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t col = j0 + 16 * f + 4 * g + i;
+                if (col >= N) continue;
+                store_y(y, y_dtype, col, load_alpha(alpha, alpha_f16, col) * (2.0f * (z[i] - corr) - xall));
+            }
+        }
     }
 }
 
@@ -779,19 +806,31 @@ template <int NW>
 static void launch_w1a16_decode1_nw(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
                                     const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
     constexpr unsigned nt = NW * 64;
-    const unsigned grid = unsigned((N + 16 * (NW / 4) - 1) / (16 * (NW / 4)));
     const uint16_t* xx = static_cast<const uint16_t*>(x);
     const int64_t TQ = tiles_per_col(K);
-    const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
-#define BGB_F1(NVV)                                                                                                \
-    if (x_f16) fbi_decode1_kernel<true, NVV, NW><<<grid, nt, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype); \
-    else fbi_decode1_kernel<false, NVV, NW><<<grid, nt, 0, s>>>(xx, K, N, TQ, P, alpha, alpha_f16, y, y_dtype);
+    const int nv = int((TQ * 16 + nt - 1) / nt);      // 16-byte chunks per thread
+    const int it_max = nv * NW >= 32 ? 2 : 4;          // keeps the preloaded tiles in registers
+    const int64_t ngroups = (N + 16 * (NW / 4) - 1) / (16 * (NW / 4));
+    int64_t grid = ngroups < kD1MaxGrid ? ngroups : kD1MaxGrid;
+    int it = int((ngroups + grid - 1) / grid);
+    if (it > it_max) {
+        it = it_max;
+        grid = (ngroups + it_max - 1) / it_max;
+    }
+#define BGB_F1X(NVV, ITV)                                                                                    \
+    if (x_f16) fbi_decode1_kernel<true, NVV, NW, ITV><<<unsigned(grid), nt, 0, s>>>(xx, K, N, TQ, P, alpha,  \
+                                                                                  alpha_f16, y, y_dtype);  \
+    else fbi_decode1_kernel<false, NVV, NW, ITV><<<unsigned(grid), nt, 0, s>>>(xx, K, N, TQ, P, alpha,      \
+                                                                             alpha_f16, y, y_dtype);
+#define BGB_F1(NVV)                                                                                          \
+    if (it == 1) { BGB_F1X(NVV, 1) } else if (it == 2) { BGB_F1X(NVV, 2) } else if (it == 3) { BGB_F1X(NVV, 3) } \
+    else { BGB_F1X(NVV, 4) }
     if (nv <= 1) { BGB_F1(1) }
     else if (nv <= 2) { BGB_F1(2) }
     else if (nv <= 4) { BGB_F1(4) }
-    else if (nv <= 8) { BGB_F1(8) }
-    else { BGB_F1(16) }
+    else { BGB_F1(8) }
 #undef BGB_F1
+#undef BGB_F1X
 }
 
 hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
