@@ -44,7 +44,7 @@ struct PackBitnetWs {       // fp64 (sum W, sum |W|) per reduction block
 // GEMM launch plan (a pure function of the shape): token fragments per wave
 // (BM = 16 nn), K splits and stages per split, tile grid.
 struct GemmPlan {
-    int nn, splits, per, T, ntm, ntj;
+    int nn, nw, splits, per, T, ntm, ntj;   // nw waves of 64 columns per block
 };
 GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8);
 size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8);   // [splits][M][N] x 4 bytes, or 0
@@ -74,7 +74,7 @@ struct BitlinearWs {
     static BitlinearWs make(int64_t M, int64_t K, int64_t N) {
         BitlinearWs w{};
         w.stats = 0;                                               // float [M][3] mu32, rstd32, rowmax
-        w.gamma = w.stats + align256(size_t(M) * 3 * sizeof(float));
+        w.gamma = w.stats + align256((size_t(M) * 3 + size_t(M + 3) / 4) * sizeof(float));  // + block maxima
         w.rowsum = w.gamma + 256;                                  // int32 [M]
         w.q = w.rowsum + align256(size_t(M) * sizeof(int32_t));    // int8 [M][Kp], layout per path
         w.part = w.q + align256(size_t(M) * size_t(padded_k(K)));  // int32 split-K partials (GEMM)

@@ -41,9 +41,7 @@
 
 namespace bgb {
 
-constexpr int kBJ = 256;            // output columns per block tile
 constexpr int kRing = 4;            // stages in the LDS rings
-constexpr int kWTileBytes = kBJ * 16;   // one 128-row sign tile of the block's columns
 
 template <bool kF16>
 BGB_DEV f32x4_t mfma16g(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
@@ -139,8 +137,9 @@ constexpr int kSlots = 512;         // resident blocks: 2 per CU on 256 CUs
 
 GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8) {
     const int T = int(w1a8 ? tiles_per_col(K) : 2 * tiles_per_col(K));
-    const int ntj = int((N + kBJ - 1) / kBJ);
+    const int ntj = int((N + 255) / 256);
     GemmPlan best{};
+    best.nw = 4;
     double best_t = 1e300;
     for (int nn : {8, 4}) {
         const int ntm = int((M + 16 * nn - 1) / (16 * nn));
@@ -243,11 +242,13 @@ BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& 
 }
 
 // NN token fragments per wave (BM = 16 NN); kW1A8 selects the int8 path.
-template <bool kW1A8, bool kF16, int NN>
-__global__ void __launch_bounds__(256, 2) gemm_kernel(const GemmArgs a) {
+template <bool kW1A8, bool kF16, int NN, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a) {
     constexpr int BM = 16 * NN;
+    constexpr int BJ = 64 * NW;                 // 64 columns per wave
     constexpr int kStage = BM * 128;            // bytes of one activation stage
-    constexpr int kXDma = BM / 32;              // activation DMA operations per thread per stage
+    constexpr int kWTileBytes = BJ * 16;        // one 128-row sign tile of the block's columns
+    constexpr int kXDma = BM / (8 * NW);        // activation DMA operations per thread per stage
     constexpr int kOps = kXDma + 1;             // + the sign tile
     using acc_t = std::conditional_t<kW1A8, i32x4_t, f32x4_t>;
     using opd_t = std::conditional_t<kW1A8, i32x4_t, u32x4_t>;
@@ -266,7 +267,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(const GemmArgs a) {
 
     const int tile = xcd_tile(blockIdx.x, a.ntiles);
     if (tile >= a.ntiles) return;
-    const int64_t m0 = int64_t(tile / a.ntj) * BM, j0 = int64_t(tile % a.ntj) * kBJ;
+    const int64_t m0 = int64_t(tile / a.ntj) * BM, j0 = int64_t(tile % a.ntj) * BJ;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
     const int z = blockIdx.y;
     const int s0 = z * a.per;
@@ -280,7 +281,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(const GemmArgs a) {
     const uint8_t* src[kXDma];
 #pragma unroll
     for (int i = 0; i < kXDma; ++i) {
-        const int p = (4 * i + wave) * 64 + lane;
+        const int p = (NW * i + wave) * 64 + lane;
         const int t = p >> 3, slot = p & 7;
         const int c = slot ^ (kW1A8 ? swz8(t) : swz16(t));
         const int64_t m = m0 + t < M ? m0 + t : M - 1;
@@ -290,7 +291,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(const GemmArgs a) {
     auto issue = [&](int rel, int B) {          // stage s0 + rel, clamped: the tail re-reads the last one
         const int s = s0 + (rel < ns ? rel : ns - 1);
 #pragma unroll
-        for (int i = 0; i < kXDma; ++i) dma16(src[i] + int64_t(s) * 128, lds[B] + (4 * i + wave) * 1024);
+        for (int i = 0; i < kXDma; ++i) dma16(src[i] + int64_t(s) * 128, lds[B] + (NW * i + wave) * 1024);
         const int64_t tq = kW1A8 ? s : (s >> 1);
         dma16(wsrc + tq * N * 16, wls[B] + wave * 1024);
     };
@@ -483,8 +484,9 @@ static hipError_t launch_gemm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
     a.ntj = p.ntj;
     a.ntiles = ntiles;
     const dim3 grid(unsigned(xcd_grid(ntiles)), unsigned(p.splits));
-    if (p.nn == 8) gemm_kernel<kW1A8, kF16, 8><<<grid, 256, 0, s>>>(a);
-    else gemm_kernel<kW1A8, kF16, 4><<<grid, 256, 0, s>>>(a);
+    if (p.nw == 8) gemm_kernel<kW1A8, kF16, 8, 8><<<grid, 512, 0, s>>>(a);
+    else if (p.nn == 8) gemm_kernel<kW1A8, kF16, 8, 4><<<grid, 256, 0, s>>>(a);
+    else gemm_kernel<kW1A8, kF16, 4, 4><<<grid, 256, 0, s>>>(a);
     if (p.splits > 1) {
         const int64_t n = a.M * ((a.N + 3) / 4);
         splitk_reduce_kernel<kW1A8><<<unsigned((n + 255) / 256), 256, 0, s>>>(a, p.splits);

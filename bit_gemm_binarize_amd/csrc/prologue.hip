@@ -120,46 +120,171 @@ lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double 
     }
 }
 
-// Large M, pass 1: one block per row -> mu32, rstd32, max |h|.
+// Large M: one wave per row, four rows per block, rows read in 16-byte
+// vectors (K % 32 == 0 keeps every row 16-byte aligned).
+template <typename XT> struct Vec16;
+template <> struct Vec16<float> {            // 4 elements per 16 bytes
+    static constexpr int E = 4;
+    static BGB_DEV void load(const float* p, float* v) {
+        const f32x4_t t = *reinterpret_cast<const f32x4_t*>(p);
+        v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    }
+};
+template <> struct Vec16<uint16_t> {         // 8 bf16 elements per 16 bytes
+    static constexpr int E = 8;
+    static BGB_DEV void load(const uint16_t* p, float* v) {
+        const u32x4_t t = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(t[i] << 16);
+            v[2 * i + 1] = __uint_as_float(t[i] & 0xffff0000u);
+        }
+    }
+};
+
+// Pass 1: mu32, rstd32 and max |h| of each row (|h| is largest at the row's
+// largest or smallest x, h being monotone in x), and the max over the
+// block's rows for pass 2.
 template <typename XT>
 __global__ void __launch_bounds__(256)
-lnq_stats_kernel(const XT* __restrict__ x, int64_t K, double eps, float* __restrict__ stats) {
-    __shared__ double dscr[4];
-    __shared__ float fscr[4];
-    const int64_t m = blockIdx.x;
-    const XT* xr = x + m * K;
-    float mu32, rs32;
-    row_stats<256>(xr, K, eps, dscr, mu32, rs32);
-    float lm = 0.0f;
-    for (int64_t i = threadIdx.x; i < K; i += 256) lm = fmaxf(lm, fabsf(ln_apply(load_x(xr, i), mu32, rs32)));
-    lm = block_max<256>(lm, fscr);
-    if (threadIdx.x == 0) {
-        stats[3 * m] = mu32;
-        stats[3 * m + 1] = rs32;
-        stats[3 * m + 2] = lm;
+lnq_stats_kernel(const XT* __restrict__ x, int64_t M, int64_t K, double eps, float* __restrict__ stats,
+                 float* __restrict__ blockmax) {
+    using V = Vec16<XT>;
+    constexpr int E = V::E;
+    __shared__ float bm[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t m = int64_t(blockIdx.x) * 4 + wave;
+    float rowmax = 0.0f;
+    if (m < M) {
+        const XT* xr = x + m * K;
+        const int64_t nvec = K / E;
+        double s = 0.0;
+        float mx = -__builtin_inff(), mn = __builtin_inff();
+        for (int64_t c = lane; c < nvec; c += 64) {
+            float v[E];
+            V::load(xr + c * E, v);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                s += double(v[e]);
+                mx = fmaxf(mx, v[e]);
+                mn = fminf(mn, v[e]);
+            }
+        }
+        s = wave_sum63(s);
+        mx = wave_max63(mx);
+        mn = wave_min63(mn);
+        const double mu = __shfl(s, 63) / double(K);
+        double s2 = 0.0;
+        for (int64_t c = lane; c < nvec; c += 64) {
+            float v[E];
+            V::load(xr + c * E, v);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const double d = double(v[e]) - mu;
+                s2 += d * d;
+            }
+        }
+        s2 = wave_sum63(s2);
+        const float mu32 = float(mu);
+        const float rs32 = float(1.0 / sqrt(__shfl(s2, 63) / double(K) + eps));
+        const float hx = __shfl(mx, 63), hn = __shfl(mn, 63);
+        rowmax = fmaxf(fabsf(ln_apply(hx, mu32, rs32)), fabsf(ln_apply(hn, mu32, rs32)));
+        if (lane == 0) {
+            stats[3 * m] = mu32;
+            stats[3 * m + 1] = rs32;
+            stats[3 * m + 2] = rowmax;
+        }
     }
+    if (lane == 0) bm[wave] = rowmax;
+    __syncthreads();
+    if (threadIdx.x == 0) blockmax[blockIdx.x] = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
 }
 
-// Large M, pass 2: gamma = max over the row maxima (every block computes the
-// same exact maximum), then one block per row quantizes.
+// Pass 2: gamma = max over the block maxima (every block computes the same
+// exact value), then one wave per row: lane t takes 32-row words t, t + 64,
+// ..., computes their 32 codes and stores the 8 code dwords of the word in
+// the requested layout (zeros for the padding words past K).
 template <typename XT>
 __global__ void __launch_bounds__(256)
 lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, float qb, float lim, int layout,
-                 const float* __restrict__ stats, int8_t* __restrict__ q, int32_t* __restrict__ rowsum,
-                 float* __restrict__ gamma_ws, int8_t* __restrict__ xq_opt, float* __restrict__ gamma_opt) {
-    __shared__ float fscr[4];
-    __shared__ int iscr[4];
-    float g = 0.0f;
-    for (int64_t i = threadIdx.x; i < M; i += 256) g = fmaxf(g, stats[3 * i + 2]);
-    const float gamma = block_max<256>(g, fscr);
-    const int64_t m = blockIdx.x;
-    if (m == 0 && threadIdx.x == 0) {
+                 const float* __restrict__ stats, const float* __restrict__ blockmax, int nblocks,
+                 int8_t* __restrict__ q, int32_t* __restrict__ rowsum, float* __restrict__ gamma_ws,
+                 int8_t* __restrict__ xq_opt, float* __restrict__ gamma_opt) {
+    using V = Vec16<XT>;
+    constexpr int E = V::E;
+    __shared__ float gscr[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float gm = 0.0f;
+    for (int i = threadIdx.x; i < nblocks; i += 256) gm = fmaxf(gm, blockmax[i]);
+    gm = wave_max63_nonneg(gm);
+    if (lane == 63) gscr[wave] = gm;
+    __syncthreads();
+    const float gamma = fmaxf(fmaxf(gscr[0], gscr[1]), fmaxf(gscr[2], gscr[3]));
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         gamma_ws[0] = gamma;
         if (gamma_opt) gamma_opt[0] = gamma;
     }
-    const int s = quant_row<256>(x + m * K, K, Kp, stats[3 * m], stats[3 * m + 1], qb, gamma, lim, layout,
-                                 reinterpret_cast<uint32_t*>(q + m * Kp), xq_opt ? xq_opt + m * K : nullptr, iscr);
-    if (threadIdx.x == 0) rowsum[m] = s;
+    const int64_t m = int64_t(blockIdx.x) * 4 + wave;
+    if (m >= M) return;
+    const XT* xr = x + m * K;
+    const float mu32 = stats[3 * m], rs32 = stats[3 * m + 1];
+    const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
+    const int qmax = int(qb) - 1;
+    const int64_t words = K / 32, pwords = Kp / 32;
+    int sum = 0;
+    for (int64_t t = lane; t < pwords; t += 64) {
+        uint32_t dw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if (t < words) {
+            float h[32];
+#pragma unroll
+            for (int c = 0; c < 32 / E; ++c) V::load(xr + 32 * t + c * E, h + c * E);
+            int code[32];
+            uint32_t slow = 0;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                h[j] = ln_apply(h[j], mu32, rs32);
+                // fast path: u = h (Q_b rcp(gamma)) is within 1.5 ulp of the exact
+                // quotient; only near-integer u (rare) can truncate differently
+                const float u = h[j] * cq;
+                slow |= uint32_t(fabsf(u - rintf(u)) <= fabsf(u) * 0x1p-20f) << j;
+                code[j] = max(-qmax, min(qmax, int(u)));
+            }
+            if (slow && gamma != 0.0f) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    if (slow & (1u << j)) code[j] = quant_code(h[j], qb, gamma, lim);
+            }
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                sum += code[j];
+                dw[j & 7] |= uint32_t(uint8_t(int8_t(code[j]))) << (8 * (j >> 3));   // rows w + 8e of dword w
+            }
+            if (xq_opt) {
+                u32x4_t nat[2];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    nat[i >> 2][i & 3] = uint32_t(uint8_t(int8_t(code[4 * i]))) | uint32_t(uint8_t(int8_t(code[4 * i + 1]))) << 8 |
+                                         uint32_t(uint8_t(int8_t(code[4 * i + 2]))) << 16 |
+                                         uint32_t(uint8_t(int8_t(code[4 * i + 3]))) << 24;
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(xq_opt + m * K + 32 * t);
+                dst[0] = nat[0];
+                dst[1] = nat[1];
+            }
+        }
+        int8_t* tile = q + m * Kp + (t >> 2) * 128;
+        const int d = int(t & 3);
+        if (layout == 1) {           // GEMM: dword 8d + w
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(tile + 32 * d);
+            dst[0] = u32x4_t{dw[0], dw[1], dw[2], dw[3]};
+            dst[1] = u32x4_t{dw[4], dw[5], dw[6], dw[7]};
+        } else {                     // decode: dword 4w + d
+            uint32_t* dst = reinterpret_cast<uint32_t*>(tile);
+#pragma unroll
+            for (int w = 0; w < 8; ++w) dst[4 * w + d] = dw[w];
+        }
+    }
+    sum = wave_sum63_i(sum);
+    if (lane == 63) rowsum[m] = sum;
 }
 
 template <typename XT>
@@ -171,9 +296,11 @@ static void launch_lnq_t(const XT* x, int64_t M, int64_t K, double eps, float qb
         lnq_small_kernel<XT><<<1, 1024, 0, s>>>(x, int(M), K, Kp, eps, qb, lim, layout, q, rowsum, stats,
                                                  gamma_ws, xq_opt, gamma_opt);
     } else {
-        lnq_stats_kernel<XT><<<unsigned(M), 256, 0, s>>>(x, K, eps, stats);
-        lnq_quant_kernel<XT><<<unsigned(M), 256, 0, s>>>(x, M, K, Kp, qb, lim, layout, stats, q, rowsum,
-                                                          gamma_ws, xq_opt, gamma_opt);
+        const unsigned blocks = unsigned((M + 3) / 4);
+        float* blockmax = stats + 3 * M;       // the workspace's stats region holds [M][3] + ceil(M/4)
+        lnq_stats_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, eps, stats, blockmax);
+        lnq_quant_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, Kp, qb, lim, layout, stats, blockmax, int(blocks), q,
+                                                     rowsum, gamma_ws, xq_opt, gamma_opt);
     }
 }
 
