@@ -523,11 +523,11 @@ BGB_DEV u32x4_t w1a16_a(const u32x4_t& w) {
     constexpr int sh = p - U;
     constexpr uint32_t mask = 0x00010001u << p;
     constexpr uint32_t base = (T == 3) ? F::kHalf : F::kOne;
-    u32x4_t a;
-    a.x = (shift_word<sh>(w.x) & mask) | base;
-    a.y = (shift_word<sh>(w.y) & mask) | base;
-    a.z = (shift_word<sh>(w.z) & mask) | base;
-    a.w = (shift_word<sh>(w.w) & mask) | base;
+    u32x4_t a;   // (shifted & mask) | base as one bitop3 (truth table 0xEA); the 4 shifts are shared by 4 U
+    a.x = __builtin_amdgcn_bitop3_b32(shift_word<sh>(w.x), mask, base, 0xEA);
+    a.y = __builtin_amdgcn_bitop3_b32(shift_word<sh>(w.y), mask, base, 0xEA);
+    a.z = __builtin_amdgcn_bitop3_b32(shift_word<sh>(w.z), mask, base, 0xEA);
+    a.w = __builtin_amdgcn_bitop3_b32(shift_word<sh>(w.w), mask, base, 0xEA);
     return a;
 }
 
@@ -613,60 +613,64 @@ hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, ui
 }
 
 // General decode: permuted activations from the prep kernel, M <= 16 * TF.
-// Same wave organisation as the W1A8 kernel. Each wave folds its four type
-// accumulators into z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3 (powers of two),
-// so sum_k b x = z - (8 X_0 + 4 X_1 + 2 X_2 + X_3) is applied once at the end.
-template <bool kF16, int TF, int GS>
+// A block of kGenWaves waves owns 16 * CF columns; wave w takes steps w,
+// w + 8, ... of all CF column fragments, so each activation fragment it loads
+// (from L2) feeds CF x 16 MFMAs. Each wave folds its four type accumulators
+// into z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3 (powers of two), so
+// sum_k b x = z - (8 X_0 + 4 X_1 + 2 X_2 + X_3) is applied once at the end.
+template <bool kF16, int TF, int CF, int GS>
 __global__ void __launch_bounds__(kGenWaves * 64)
 gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xpart, int nchunk, int M, int64_t N,
                   int64_t TQ, const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
                   void* __restrict__ y, int y_dtype) {
-    __shared__ f32x4_t red[kGenWaves][TF][64];
+    __shared__ f32x4_t red[kGenWaves][CF * TF][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
-    const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
+    const int64_t j0 = int64_t(blockIdx.x) * 16 * CF;
     const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
-    f32x4_t acc[TF][4];
+    f32x4_t acc[CF * TF][4];
 #pragma unroll
-    for (int tf = 0; tf < TF; ++tf)
+    for (int q = 0; q < CF * TF; ++q)
 #pragma unroll
-        for (int T = 0; T < 4; ++T) acc[tf][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int T = 0; T < 4; ++T) acc[q][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int64_t base = wave; base < steps; base += kGenWaves * GS) {
-        u32x4_t w[GS];
-        preload<GS>(w, P, base, kGenWaves, steps, TQ, N, j, g);
+        u32x4_t w[CF][GS];
+#pragma unroll
+        for (int cf = 0; cf < CF; ++cf) preload<GS>(w[cf], P, base, kGenWaves, steps, TQ, N, j0 + 16 * cf + r, g);
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
             const int64_t st = base + kGenWaves * i;
             const int64_t tq = st * 4 + g;
             const bool tv = st < steps && tq < TQ;
-            u32x4_t a[16];
 #pragma unroll
             for (int tf = 0; tf < TF; ++tf) {
                 const int m = 16 * tf + r;
                 const bool bv = tv && m < M;
                 const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xp + int64_t(bv ? m : 0) * Kp + (bv ? tq : 0) * 128);
-                u32x4_t b[16];
+                u32x4_t bb[16];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) b[u] = ld16_or0(src + u, bv);
+                for (int u = 0; u < 16; ++u) bb[u] = ld16_or0(src + u, bv);
                 __builtin_amdgcn_sched_barrier(0);   // all 16 operand loads in flight before the MFMAs
-                if (tf == 0) w1a16_decode<kF16>(w[i], a);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) acc[tf][u & 3] = mfma16<kF16>(a[u], b[u], acc[tf][u & 3]);
+                for (int cf = 0; cf < CF; ++cf) {
+                    auto bsrc = [&](int u, int) -> u32x4_t { return bb[u]; };
+                    w1a16_step<kF16, 1>(w[cf][i], bsrc, &acc[cf * TF + tf]);
+                }
             }
         }
     }
 #pragma unroll
-    for (int tf = 0; tf < TF; ++tf)
-        red[wave][tf][lane] = ((8.0f * acc[tf][0] + 4.0f * acc[tf][1]) + 2.0f * acc[tf][2]) + 2.0f * acc[tf][3];
+    for (int q = 0; q < CF * TF; ++q)
+        red[wave][q][lane] = ((8.0f * acc[q][0] + 4.0f * acc[q][1]) + 2.0f * acc[q][2]) + 2.0f * acc[q][3];
     __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int tf = 0; tf < TF; ++tf) {
+    // wave v < CF * TF finishes (column fragment, token fragment) pair v
+    for (int q = wave; q < CF * TF; q += kGenWaves) {
+        const int cf = q / TF, tf = q % TF;
         const int mm = 16 * tf + r;
         if (mm >= M) continue;
-        f32x4_t z = red[0][tf][lane];
+        f32x4_t z = red[0][q][lane];
 #pragma unroll
-        for (int wv = 1; wv < kGenWaves; ++wv) z += red[wv][tf][lane];
+        for (int wv = 1; wv < kGenWaves; ++wv) z += red[wv][q][lane];
         double X[4] = {0.0, 0.0, 0.0, 0.0};
         for (int c = 0; c < nchunk; ++c)
 #pragma unroll
@@ -676,7 +680,7 @@ gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xp
         const float xall = ((X0 + X1) + X2) + X3;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t col = j0 + 4 * g + i;
+            const int64_t col = j0 + 16 * cf + 4 * g + i;
             if (col >= N) continue;
             const float sres = 2.0f * (z[i] - corr) - xall;
             store_y(y, y_dtype, int64_t(mm) * N + col, load_alpha(alpha, alpha_f16, col) * sres);
@@ -842,19 +846,28 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
 hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M, int64_t K, int64_t N,
                              const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
                              hipStream_t s) {
-    const unsigned grid = unsigned((N + 15) / 16);
     const int64_t TQ = tiles_per_col(K);
     const int tf = int((M + 15) / 16);
     const int nch = w1a16_prep_chunks(K);
     constexpr unsigned nt = kGenWaves * 64;
     const int gs = gen_steps(TQ);
-#define BGB_G16(F16, TFV, GSV) \
-    gemv_w1a16_kernel<F16, TFV, GSV><<<grid, nt, 0, s>>>(xp, xpart, nch, int(M), N, TQ, P, alpha, alpha_f16, y, y_dtype)
-#define BGB_G16S(F16, TFV) if (gs == 1) BGB_G16(F16, TFV, 1); else if (gs == 2) BGB_G16(F16, TFV, 2); else BGB_G16(F16, TFV, 4);
+    // column fragments per block: as many (up to 4 for one token fragment, 1
+    // for two: registers) as keep at least 192 blocks streaming
+    const int cf = tf == 1 ? (N >= 4 * 16 * 192 ? 4 : (N >= 2 * 16 * 192 ? 2 : 1)) : 1;
+    const unsigned grid = unsigned((N + 16 * cf - 1) / (16 * cf));
+#define BGB_G16(F16, TFV, CFV, GSV)                                                                           \
+    gemv_w1a16_kernel<F16, TFV, CFV, GSV><<<grid, nt, 0, s>>>(xp, xpart, nch, int(M), N, TQ, P, alpha,       \
+                                                              alpha_f16, y, y_dtype)
+#define BGB_G16S(F16, TFV, CFV) \
+    if (gs == 1) BGB_G16(F16, TFV, CFV, 1); else if (gs == 2) BGB_G16(F16, TFV, CFV, 2); else BGB_G16(F16, TFV, CFV, 4);
     if (x_f16) {
-        if (tf == 1) { BGB_G16S(true, 1) } else if (tf == 2) { BGB_G16S(true, 2) } else if (tf == 3) { BGB_G16S(true, 3) } else { BGB_G16S(true, 4) }
+        if (tf == 1) {
+            if (cf == 4) { BGB_G16S(true, 1, 4) } else if (cf == 2) { BGB_G16S(true, 1, 2) } else { BGB_G16S(true, 1, 1) }
+        } else { BGB_G16S(true, 2, 1) }
     } else {
-        if (tf == 1) { BGB_G16S(false, 1) } else if (tf == 2) { BGB_G16S(false, 2) } else if (tf == 3) { BGB_G16S(false, 3) } else { BGB_G16S(false, 4) }
+        if (tf == 1) {
+            if (cf == 4) { BGB_G16S(false, 1, 4) } else if (cf == 2) { BGB_G16S(false, 1, 2) } else { BGB_G16S(false, 1, 1) }
+        } else { BGB_G16S(false, 2, 1) }
     }
 #undef BGB_G16S
 #undef BGB_G16
