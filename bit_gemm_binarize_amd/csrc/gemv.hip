@@ -691,9 +691,6 @@ gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xp
 // Single token, activation staging fused: the block permutes x into LDS and
 // computes the four X_T itself, once, then takes up to IT column groups
 // (blockIdx.x + i * gridDim.x) of 16 * NW / 4 columns, as the W1A8 kernel.
-// Thread tid stages the chunks p = i * NT + tid of the decode layout: chunk
-// (tile Tt, u) holds rows 128 Tt + 32 d + u + 16 h at element 2 d + h, all of
-// type u % 4 = tid % 4.
 template <bool kF16, int NV, int NW, int IT>
 __global__ void __launch_bounds__(NW * 64)
 fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
@@ -708,25 +705,19 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
     const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
-    const int nchunks = int(TQ * 16);
+    const int pieces = int(TQ * 16);                   // 16-byte pieces of the padded token
     const int64_t steps = (TQ + 3) / 4;
     const int Ki = int(K);
 
-    // 1. the token's chunks (loads complete before the sign stream starts)
-    uint32_t xv[NV][4];
+    // 1. the token, 16 bytes per load (K % 32 == 0: a piece is all inside K or
+    //    all padding); the loads complete before the sign stream starts
+    u32x4_t xv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int p = i * NT + tid;
-        const int row0 = 128 * (p >> 4) + (p & 15);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int k0 = row0 + 32 * d, k1 = k0 + 16;
-            const uint32_t keep0 = 0u - uint32_t(p < nchunks && k0 < Ki);   // masks: the loads stay unconditional
-            const uint32_t keep1 = 0u - uint32_t(p < nchunks && k1 < Ki);
-            const uint32_t e0 = uint32_t(x[k0 < Ki ? k0 : 0]) & keep0;
-            const uint32_t e1 = uint32_t(x[k1 < Ki ? k1 : 0]) & keep1;
-            xv[i][d] = e0 | (e1 << 16);
-        }
+        const bool ok = 8 * p < Ki;
+        const u32x4_t t = *reinterpret_cast<const u32x4_t*>(x + (ok ? 8 * p : 0));
+        xv[i] = t & u32x4_t(0u - uint32_t(ok));       // a mask (not a select): the load stays unconditional
     }
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
     u32x4_t w[IT][S];
@@ -738,24 +729,27 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. stage the chunks, sum this thread's type in fp64
+    // 2. scatter rows 8p..8p+7 into the decode layout (they share t, and
+    //    (k % 16) runs over 8 consecutive values 8 elements apart), sum each
+    //    type k % 4 in fp64
     if (tid < 16) reinterpret_cast<u32x4_t*>(xzero)[tid] = u32x4_t{0u, 0u, 0u, 0u};
-    double xsum = 0.0;
+    double xs4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int p = i * NT + tid;
-        if (p >= nchunks) continue;
-        *reinterpret_cast<u32x4_t*>(xs + (p >> 4) * 128 + (p & 15) * 8) =
-            u32x4_t{xv[i][0], xv[i][1], xv[i][2], xv[i][3]};
+        if (p >= pieces) continue;
+        const int k = 8 * p, t = k >> 5, bq = k & 31;
+        uint16_t* dst = xs + (t >> 2) * 128 + (bq & 15) * 8 + (t & 3) * 2 + (bq >> 4);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint16_t lo = uint16_t(xv[i][d] & 0xffffu), hi = uint16_t(xv[i][d] >> 16);
-            xsum += double(kF16 ? f16_to_f32(lo) : bf16_to_f32(lo)) + double(kF16 ? f16_to_f32(hi) : bf16_to_f32(hi));
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t v = uint16_t(e & 1 ? xv[i][e >> 1] >> 16 : xv[i][e >> 1] & 0xffffu);
+            dst[8 * e] = v;
+            xs4[e & 3] += double(kF16 ? f16_to_f32(v) : bf16_to_f32(v));
         }
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const double t = wave_sum63((tid & 3) == c ? xsum : 0.0);
+        const double t = wave_sum63(xs4[c]);
         if (lane == 63) dX[wave][c] = t;
     }
     __syncthreads();
@@ -812,7 +806,7 @@ static void launch_w1a16_decode1_nw(const void* x, int x_f16, int64_t K, int64_t
     constexpr unsigned nt = NW * 64;
     const uint16_t* xx = static_cast<const uint16_t*>(x);
     const int64_t TQ = tiles_per_col(K);
-    const int nv = int((TQ * 16 + nt - 1) / nt);      // 16-byte chunks per thread
+    const int nv = int((TQ * 16 + nt - 1) / nt);      // 16-byte pieces per thread
     const int it_max = nv * NW >= 32 ? 2 : 4;          // keeps the preloaded tiles in registers
     const int64_t ngroups = (N + 16 * (NW / 4) - 1) / (16 * (NW / 4));
     int64_t grid = ngroups < kD1MaxGrid ? ngroups : kD1MaxGrid;
