@@ -337,7 +337,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
     const int qmax = int(qb) - 1;
     int codes[NV][4];
-    uint32_t slow = 0;                                 // bit 4i + c: needs the exact quotient
+    uint64_t slow = 0;                                 // bit 4i + c (NV <= 16): needs the exact quotient
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -345,7 +345,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
             const float h = (v[i][c] - mu32) * rs32;
             v[i][c] = h;
             const float u = h * cq;
-            slow |= uint32_t(fabsf(u - rintf(u)) <= fabsf(u) * 0x1p-20f) << (4 * i + c);
+            slow |= uint64_t(fabsf(u - rintf(u)) <= fabsf(u) * 0x1p-20f) << (4 * i + c);
             codes[i][c] = max(-qmax, min(qmax, int(u)));
         }
     if (slow && gamma != 0.0f) {                       // rare (gamma = 0: every h and code is 0)
@@ -353,7 +353,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (slow & (1u << (4 * i + c))) codes[i][c] = exact_code(v[i][c], qb, gamma, lim);
+                if (slow & (uint64_t(1) << (4 * i + c))) codes[i][c] = exact_code(v[i][c], qb, gamma, lim);
     }
     int sq = 0;
 #pragma unroll
@@ -427,44 +427,70 @@ bool w1a8_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
 // groups, blockIdx.x + i * gridDim.x.
 constexpr int kD1MaxGrid = 256;
 
-template <int NW>
-static void launch_w1a8_decode1_nw(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
+// Preloaded sign tiles per thread are IT x S = IT x NV x NW / 8 x 16 bytes:
+// at most 2 groups per block once NV x NW reaches 64 keeps them in registers.
+constexpr int d1_it_cap(int nv, int nw) { return nv * nw >= 64 ? 2 : 4; }
+
+template <int NV, int NW, typename XT>
+static void launch_w1a8_decode1_it(int it, unsigned grid, const XT* x, int64_t K, int64_t N, int64_t TQ, double eps,
+                                   float qb, float lim, const uint32_t* P, const float* beta, float* y,
+                                   int32_t* acc_opt, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
+    constexpr unsigned nt = NW * 64;
+#define BGB_D1X(ITV) \
+    bitlinear_decode1_kernel<NV, NW, ITV, XT><<<grid, nt, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, \
+                                                                   xq_opt, gamma_opt)
+    if (it == 1) BGB_D1X(1);
+    else if (it == 2) BGB_D1X(2);
+    else if constexpr (d1_it_cap(NV, NW) >= 4) {
+        if (it == 3) BGB_D1X(3);
+        else BGB_D1X(4);
+    }
+#undef BGB_D1X
+}
+
+template <int NW, typename XT>
+static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps, float qb, float lim,
                                    const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                    float* gamma_opt, hipStream_t s) {
-    constexpr unsigned nt = NW * 64;
+    constexpr int nt = NW * 64;
+    constexpr int kMaxNv = kFusedMaxKp / (nt * 4);     // 16 for 4 waves, 8 for 8
     const int64_t TQ = tiles_per_col(K);
     const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
-    const int it_max = nv * NW >= 64 ? 2 : 4;          // keeps the preloaded tiles in registers
+    const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : 16;
     const int64_t ngroups = (N + 16 * (NW / 4) - 1) / (16 * (NW / 4));
     int64_t grid = ngroups < kD1MaxGrid ? ngroups : kD1MaxGrid;
     int it = int((ngroups + grid - 1) / grid);
+    const int it_max = d1_it_cap(nvp, NW);
     if (it > it_max) {
         it = it_max;
         grid = (ngroups + it_max - 1) / it_max;
     }
-#define BGB_D1X(NVV, ITV)                                                                                        \
-    if (x_bf16)                                                                                                  \
-        bitlinear_decode1_kernel<NVV, NW, ITV, uint16_t><<<unsigned(grid), nt, 0, s>>>(                          \
-            static_cast<const uint16_t*>(x), K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt);    \
-    else                                                                                                         \
-        bitlinear_decode1_kernel<NVV, NW, ITV, float><<<unsigned(grid), nt, 0, s>>>(                             \
-            static_cast<const float*>(x), K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt);
-#define BGB_D1(NVV)                                                                                              \
-    if (it == 1) { BGB_D1X(NVV, 1) } else if (it == 2) { BGB_D1X(NVV, 2) } else if (it == 3) { BGB_D1X(NVV, 3) } \
-    else { BGB_D1X(NVV, 4) }
-    if (nv <= 1) { BGB_D1(1) }
-    else if (nv <= 2) { BGB_D1(2) }
-    else if (nv <= 4) { BGB_D1(4) }
-    else if (nv <= 8) { BGB_D1(8) }
-    else { BGB_D1(16) }
+    const unsigned g = unsigned(grid);
+#define BGB_D1(NVV) \
+    launch_w1a8_decode1_it<NVV, NW, XT>(it, g, x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
+    if (nvp == 1) BGB_D1(1);
+    else if (nvp == 2) BGB_D1(2);
+    else if (nvp == 4) BGB_D1(4);
+    else if (nvp == 8) BGB_D1(8);
+    else if constexpr (kMaxNv >= 16) BGB_D1(16);
 #undef BGB_D1
-#undef BGB_D1X
 }
 
 hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
                                const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                float* gamma_opt, hipStream_t s) {
-    launch_w1a8_decode1_nw<kD1WavesW1A8>(x, x_bf16, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+    // 8-wave blocks (32 columns per group) while that still gives every CU a
+    // group; 4-wave blocks (16 columns) for narrower layers
+    const bool wide = (N + 31) / 32 >= kD1MaxGrid;
+    if (x_bf16) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        if (wide) launch_w1a8_decode1_nw<kD1WavesW1A8>(xb, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        else launch_w1a8_decode1_nw<4>(xb, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+    } else {
+        const float* xf = static_cast<const float*>(x);
+        if (wide) launch_w1a8_decode1_nw<kD1WavesW1A8>(xf, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        else launch_w1a8_decode1_nw<4>(xf, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+    }
     return hipGetLastError();
 }
 
@@ -800,40 +826,60 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
 
 bool w1a16_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
 
-template <int NW>
-static void launch_w1a16_decode1_nw(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
-                                    const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+template <bool kF16, int NV, int NW>
+static void launch_w1a16_decode1_it(int it, unsigned grid, const uint16_t* x, int64_t K, int64_t N, int64_t TQ,
+                                    const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
+                                    hipStream_t s) {
     constexpr unsigned nt = NW * 64;
-    const uint16_t* xx = static_cast<const uint16_t*>(x);
+#define BGB_F1X(ITV) \
+    fbi_decode1_kernel<kF16, NV, NW, ITV><<<grid, nt, 0, s>>>(x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype)
+    if (it == 1) BGB_F1X(1);
+    else if (it == 2) BGB_F1X(2);
+    else if constexpr (d1_it_cap(2 * NV, NW) >= 4) {
+        if (it == 3) BGB_F1X(3);
+        else BGB_F1X(4);
+    }
+#undef BGB_F1X
+}
+
+template <bool kF16, int NW>
+static void launch_w1a16_decode1_nw(const uint16_t* x, int64_t K, int64_t N, const uint32_t* P, const void* alpha,
+                                    int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    constexpr int nt = NW * 64;
+    constexpr int kMaxNv = kFusedMaxKp / (nt * 8);     // 16-byte pieces per thread: 8 for 4 waves, 4 for 8
     const int64_t TQ = tiles_per_col(K);
-    const int nv = int((TQ * 16 + nt - 1) / nt);      // 16-byte pieces per thread
-    const int it_max = nv * NW >= 32 ? 2 : 4;          // keeps the preloaded tiles in registers
+    const int nv = int((TQ * 16 + nt - 1) / nt);
+    const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : 8;
     const int64_t ngroups = (N + 16 * (NW / 4) - 1) / (16 * (NW / 4));
     int64_t grid = ngroups < kD1MaxGrid ? ngroups : kD1MaxGrid;
     int it = int((ngroups + grid - 1) / grid);
+    const int it_max = d1_it_cap(2 * nvp, NW);
     if (it > it_max) {
         it = it_max;
         grid = (ngroups + it_max - 1) / it_max;
     }
-#define BGB_F1X(NVV, ITV)                                                                                    \
-    if (x_f16) fbi_decode1_kernel<true, NVV, NW, ITV><<<unsigned(grid), nt, 0, s>>>(xx, K, N, TQ, P, alpha,  \
-                                                                                  alpha_f16, y, y_dtype);  \
-    else fbi_decode1_kernel<false, NVV, NW, ITV><<<unsigned(grid), nt, 0, s>>>(xx, K, N, TQ, P, alpha,      \
-                                                                             alpha_f16, y, y_dtype);
-#define BGB_F1(NVV)                                                                                          \
-    if (it == 1) { BGB_F1X(NVV, 1) } else if (it == 2) { BGB_F1X(NVV, 2) } else if (it == 3) { BGB_F1X(NVV, 3) } \
-    else { BGB_F1X(NVV, 4) }
-    if (nv <= 1) { BGB_F1(1) }
-    else if (nv <= 2) { BGB_F1(2) }
-    else if (nv <= 4) { BGB_F1(4) }
-    else { BGB_F1(8) }
+    const unsigned g = unsigned(grid);
+#define BGB_F1(NVV) launch_w1a16_decode1_it<kF16, NVV, NW>(it, g, x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
+    if (nvp == 1) BGB_F1(1);
+    else if (nvp == 2) BGB_F1(2);
+    else if (nvp == 4) BGB_F1(4);
+    else if constexpr (kMaxNv >= 8) BGB_F1(8);
 #undef BGB_F1
-#undef BGB_F1X
 }
 
 hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
-    launch_w1a16_decode1_nw<kD1Waves>(x, x_f16, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+    // 8-wave blocks (32 columns per group) while that still gives every CU a
+    // group; 4-wave blocks (16 columns) for narrower layers
+    const uint16_t* xx = static_cast<const uint16_t*>(x);
+    const bool wide = (N + 31) / 32 >= kD1MaxGrid;
+    if (x_f16) {
+        if (wide) launch_w1a16_decode1_nw<true, kD1Waves>(xx, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+        else launch_w1a16_decode1_nw<true, 4>(xx, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+    } else {
+        if (wide) launch_w1a16_decode1_nw<false, kD1Waves>(xx, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+        else launch_w1a16_decode1_nw<false, 4>(xx, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+    }
     return hipGetLastError();
 }
 

@@ -30,6 +30,9 @@ def _run(bgb, orc, W, x_host, x_dev, qp=None, bits=8):
 
 
 CASES = [(1, 4096, 11008), (1, 96, 65), (1, 16416, 40), (3, 160, 300), (16, 768, 260), (17, 96, 65),
+         # single token, 4-wave blocks (N < 8192) with up to 16 pieces per thread,
+         # and 8-wave blocks at the largest fused K
+         (1, 11008, 4096), (1, 16384, 300), (1, 8320, 8192), (1, 16384, 8200),
          (40, 1024, 300), (64, 512, 100), (65, 256, 90), (130, 256, 513), (5, 11008, 64),
          # GEMM pipeline: 1, 3 or 0 tail stages of the 4-stage ring, ragged M/N
          (150, 640, 300), (257, 896, 520), (300, 1024, 1000)]

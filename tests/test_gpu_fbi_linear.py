@@ -34,6 +34,7 @@ CASES = [
     # fragments (M <= 32), and the MFMA GEMM (M > 32, split-K plans for small
     # M x N); ragged N and K tails.
     (1, 768, 768), (1, 11008, 100), (1, 16416, 40), (8, 768, 768), (3, 96, 65), (16, 160, 300),
+    (1, 16384, 4000), (1, 16384, 8200), (1, 11008, 4096),
     (5, 4096, 33), (17, 96, 65), (40, 768, 260), (64, 2048, 520), (65, 256, 300), (130, 256, 300),
     (200, 352, 513),
     # GEMM pipeline: 4-stage ring with 0 or 2 tail stages, ragged M/N, padded K
