@@ -99,6 +99,11 @@ BGB_DEV void store_y(void* y, int y_dtype, int64_t i, float v) {
 BGB_DEV float load_alpha(const void* alpha, int alpha_f16, int64_t j) {
     return alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[j]) : static_cast<const float*>(alpha)[j];
 }
+BGB_DEV float load_alpha_ahead(const void* alpha, int alpha_f16, int64_t j) {
+    const int64_t off = alpha_f16 ? (2 * j) & ~int64_t(3) : 4 * j;
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(alpha) + off);
+    return alpha_f16 ? f16_to_f32(uint16_t(u >> (16 * (j & 1)))) : __uint_as_float(u);
+}
 
 // ------------------------------------------------------------------ W1A8 -----
 
@@ -330,30 +335,30 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     // 3. codes into LDS in the decode layout, one dword per pair; zero
     //    padding rows K..Kp-1. Fast path u = h (Q_b rcp(gamma)) (Q_b is a power
     //    of two, so this is fl32(fl32(h Q_b) rcp(gamma))), which is within 1.5
-    //    ulp of the exact quotient: unless u lies within |u| 2^-20 of an
-    //    integer, no integer separates them and trunc(u), kept inside
-    //    +-(Q_b - 1), is the code. Near-integer cases (rare; they include h = 0
-    //    and the extreme element) take the exact division.
+    //    ulp of the exact quotient: unless u lies within |u| 2^-20 of a
+    //    nonzero integer, no integer separates them and trunc(u) is the code.
+    //    u is first clamped to +-(Q_b - 1/2): beyond that both give +-(Q_b - 1),
+    //    so the extreme element needs no exact check (u = 0 needs none either).
+    //    A lane with a near-integer u (rare) redoes all its codes exactly.
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
-    const int qmax = int(qb) - 1;
+    const float ucl = qb - 0.5f;
     int codes[NV][4];
-    uint64_t slow = 0;                                 // bit 4i + c (NV <= 16): needs the exact quotient
+    bool slow = false;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float h = (v[i][c] - mu32) * rs32;
             v[i][c] = h;
-            const float u = h * cq;
-            slow |= uint64_t(fabsf(u - rintf(u)) <= fabsf(u) * 0x1p-20f) << (4 * i + c);
-            codes[i][c] = max(-qmax, min(qmax, int(u)));
+            const float u = fminf(fmaxf(h * cq, -ucl), ucl);
+            slow |= fabsf(u - rintf(u)) < fabsf(u) * 0x1p-20f;
+            codes[i][c] = int(u);
         }
-    if (slow && gamma != 0.0f) {                       // rare (gamma = 0: every h and code is 0)
+    if (slow && gamma != 0.0f) {                       // gamma = 0: every h and code is 0
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (slow & (uint64_t(1) << (4 * i + c))) codes[i][c] = exact_code(v[i][c], qb, gamma, lim);
+            for (int c = 0; c < 4; ++c) codes[i][c] = exact_code(v[i][c], qb, gamma, lim);
     }
     int sq = 0;
 #pragma unroll
@@ -753,6 +758,24 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
         const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
         preload<S>(w[it], P, kq, 4, steps, TQ, N, jj, g);
     }
+    // With one group per block, the scales of the 4 columns j0..j0+3 this
+    // lane writes are requested here, behind the sign tiles the epilogue
+    // waits for anyway, rather than after the last barrier (with several
+    // groups, measured slower: the epilogue lanes are read late instead, while
+    // the next group's tiles stream). Two 8-byte words: bytes 4 j0 and
+    // 4 j0 + 8 for fp32, byte 2 j0 twice for fp16. j0 is a multiple of 4 and
+    // alpha is 16-byte aligned, so a read past the N-th scale stays inside
+    // the aligned 16 bytes holding scale j0; a group past N reads scale 0.
+    constexpr bool kAlphaAhead = IT == 1;
+    uint2 araw[2] = {};
+    if constexpr (kAlphaAhead) {
+        int64_t j0 = int64_t(blockIdx.x) * 16 * F + 16 * f + 4 * g;
+        j0 = j0 < N ? j0 : 0;
+        const char* a8 = static_cast<const char*>(alpha);
+        const int64_t lo = alpha_f16 ? 2 * j0 : 4 * j0, hi = alpha_f16 ? 2 * j0 : 4 * j0 + 8;
+        araw[0] = *reinterpret_cast<const uint2*>(a8 + lo);
+        araw[1] = *reinterpret_cast<const uint2*>(a8 + hi);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. scatter rows 8p..8p+7 into the decode layout (they share t, and
@@ -814,11 +837,15 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
             const f32x4_t (&rd)[NW][64] = red[it & 1];
             const f32x4_t z = ((rd[f][lane] + rd[f + F][lane]) + rd[f + 2 * F][lane]) + rd[f + 3 * F][lane];
             const int64_t j0 = grp * 16 * F;
+            const uint32_t aw[4] = {araw[0].x, araw[0].y, araw[1].x, araw[1].y};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t col = j0 + 16 * f + 4 * g + i;
                 if (col >= N) continue;
-                store_y(y, y_dtype, col, load_alpha(alpha, alpha_f16, col) * (2.0f * (z[i] - corr) - xall));
+                const float a = !kAlphaAhead ? load_alpha(alpha, alpha_f16, col)
+                                : alpha_f16  ? f16_to_f32(uint16_t(aw[i >> 1] >> (16 * (i & 1))))
+                                             : __uint_as_float(aw[i]);
+                store_y(y, y_dtype, col, a * (2.0f * (z[i] - corr) - xall));
             }
         }
     }
