@@ -439,7 +439,7 @@ def main():
         "data": "synthetic: seeded N(0.001, 0.02) fp32 weights packed to 1 bit, N(0,1) fp32 activations",
         "config": {"workload": "bitlinear_w1a8_decode_4096x11008", "M": state["M"], "K": state["K"],
                    "N": state["N"], "x_dtype": "f32", "weight_copies": R,
-                   "step": "LN+absmax prologue kernel + packed GEMV kernel (one HIP graph of all steps)"},
+                   "step": "one fused kernel: LN + absmax quant prologue, packed GEMV, epilogue (HIP graph of all steps)"},
         "roofline": roof, "cpu_baseline": cpu, "legs": legs,
     }
     print(json.dumps(rec), flush=True)
