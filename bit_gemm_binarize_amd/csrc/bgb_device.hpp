@@ -69,7 +69,10 @@ BGB_DEV int wave_sum_i(int v) {
 // mask add the identity (0). Fixed order, so the result is reproducible.
 template <int CTRL, int ROWMASK>
 BGB_DEV int dpp_i32(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+    // all rows enabled (the quad swaps and mirrors read a valid lane for every
+    // lane): no old value to keep; else the disabled rows keep 0
+    if constexpr (ROWMASK == 0xF) return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+    else return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
 }
 template <int CTRL, int ROWMASK>
 BGB_DEV double dpp_f64(double v) {
@@ -99,6 +102,16 @@ BGB_DEV int wave_sum63_i(int v) {
     v += dpp_i32<0x140, 0xF>(v);
     v += dpp_i32<0x142, 0xA>(v);
     v += dpp_i32<0x143, 0xC>(v);
+    return v;
+}
+// Unsigned max over the 64 lanes, valid in lane 63 (0 is the identity).
+BGB_DEV uint32_t wave_umax63(uint32_t v) {
+    v = max(v, uint32_t(dpp_i32<0xB1, 0xF>(int(v))));
+    v = max(v, uint32_t(dpp_i32<0x4E, 0xF>(int(v))));
+    v = max(v, uint32_t(dpp_i32<0x141, 0xF>(int(v))));
+    v = max(v, uint32_t(dpp_i32<0x140, 0xF>(int(v))));
+    v = max(v, uint32_t(dpp_i32<0x142, 0xA>(int(v))));
+    v = max(v, uint32_t(dpp_i32<0x143, 0xC>(int(v))));
     return v;
 }
 // Max of non-negative values over the 64 lanes, valid in lane 63.

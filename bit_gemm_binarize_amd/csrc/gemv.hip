@@ -216,11 +216,13 @@ template <> BGB_DEV float load1<uint16_t>(const uint16_t* x, int64_t k) { return
 
 constexpr int kFusedMaxKp = 16384;
 
-// Single-token kernels: a block of NW waves owns 16 * NW / 4 columns (wave w:
-// column fragment w % (NW/4), K quarter w / (NW/4), steps quarter, quarter + 4,
-// ...). Each block runs the activation prologue once for its columns.
+// Single-token kernels: a block of NW waves takes column groups of F
+// 16-column fragments; wave w works on fragment w % F over the K part
+// kq = w / F of KQ = NW / F (steps kq, kq + KQ, ...). Each block runs the
+// activation prologue once and then its IT groups, blockIdx.x + i gridDim.x.
 constexpr int kD1Waves = 8;         // W1A16 single-token blocks
-constexpr int kD1WavesW1A8 = 8;     // W1A8: two 16-column fragments per group
+constexpr int kD1MaxGrid = 256;     // one block per CU
+constexpr int kD1MaxTiles = 8;      // preloaded 16-byte sign tiles per thread (IT x S)
 
 // Code of one activation, h already LayerNormed: trunc(clip(fl32(h Q_b / gamma),
 // +-lim)), lim in (Q_b - 1, Q_b).
@@ -228,19 +230,24 @@ BGB_DEV int exact_code(float h, float qb, float gamma, float lim) {
     return int(fminf(fmaxf((h * qb) / gamma, -lim), lim));
 }
 
-template <int NV, int NW, int IT, typename XT>
+// W1A8 steps per wave: NV dwords of codes per thread cover NV NW / 2 steps of
+// 512 rows, shared by KQ = NW / F waves.
+constexpr int w1a8_d1_steps(int nv, int f) { return (nv * f + 1) / 2; }
+
+template <int NV, int NW, int F, int IT, typename XT>
 __global__ void __launch_bounds__(NW * 64)
 bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
                          const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
                          int32_t* __restrict__ acc_opt, int8_t* __restrict__ xq_opt,
                          float* __restrict__ gamma_opt) {
     constexpr int NT = NW * 64;
-    constexpr int F = NW / 4;                          // 16-column fragments per column group
-    constexpr int S = NV * NW / 8 > 0 ? NV * NW / 8 : 1;   // steps per wave: 4 quarters x S x 512 rows >= Kp
+    constexpr int KQ = NW / F;
+    constexpr int S = w1a8_d1_steps(NV, F);
+    static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "single-token W1A8 shape");
     __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
-    __shared__ i32x4_t red[2][NW][64];
-    __shared__ double dscr[NW];
-    __shared__ SumMaxMin smm[NW];
+    __shared__ i32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
+    __shared__ double dsum[NW], dsq[NW];
+    __shared__ uint32_t dmax[NW];
     __shared__ int iscr[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
@@ -251,9 +258,8 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
 
     // 1. the token (an L2 hit after the first block): thread tid owns the
     //    pairs p = i * NT + tid, i.e. the rows of one dword of the decode
-    //    layout each. The loads complete before any sign tile is requested, so
-    //    the token does not queue behind the layer's stream; the tiles are then
-    //    in flight during the whole prologue.
+    //    layout each. The loads complete before any sign tile is requested;
+    //    the tiles are then in flight during the whole prologue.
     float v[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -272,65 +278,59 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
         const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
-        preload<S>(w[it], P, kq, 4, steps, TQ, N, jj, g);
+        preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. LayerNorm statistics (two fp64 passes) and the absmax of the token;
-    //    every block computes the same values. h(x) = fl32(fl32(x - mu32) rs32)
-    //    is monotone in x, so max |h| is |h| at the largest or smallest x: the
-    //    extremes ride along with the first sum and gamma needs no extra pass.
-    //    Pairs past K hold zeros: they add nothing to the sums and are left
-    //    out of the extremes a pair at a time.
-    double xd[NV][4];
-    double s = 0.0;
-    float xmx = -__builtin_inff(), xmn = __builtin_inff();
+    // 2. LayerNorm statistics, two fp64 passes; every block computes the same
+    //    values. gamma = max |h| with h = fl32(fl32(x - mu32) rs32): rounding
+    //    is monotone and sign-symmetric, so gamma = fl32(a rs32) with
+    //    a = max |fl32(x - mu32)|, which rides along with the second pass as
+    //    an unsigned max of the bit patterns (non-negative floats order like
+    //    their bits). Pairs past K hold zeros: they add nothing to the first
+    //    sum and are left out of the second pass.
+    double s1 = 0.0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            xd[i][c] = double(v[i][c]);
-            s += xd[i][c];
-        }
-        const float gmx = fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3]));
-        const float gmn = fminf(fminf(v[i][0], v[i][1]), fminf(v[i][2], v[i][3]));
-        if (i * NT + tid < pairs) {
-            xmx = fmaxf(xmx, gmx);
-            xmn = fminf(xmn, gmn);
-        }
-    }
-    s = wave_sum63(s);
-    xmx = wave_max63(xmx);
-    xmn = wave_min63(xmn);
-    if (lane == 63) smm[wave] = SumMaxMin{s, xmx, xmn};
+        for (int c = 0; c < 4; ++c) s1 += double(v[i][c]);
+    s1 = wave_sum63(s1);
+    if (lane == 63) dsum[wave] = s1;
     __syncthreads();
-    SumMaxMin st1 = smm[0];
+    double sx = dsum[0];
 #pragma unroll
-    for (int wv = 1; wv < NW; ++wv) {
-        st1.s += smm[wv].s;
-        st1.mx = fmaxf(st1.mx, smm[wv].mx);
-        st1.mn = fminf(st1.mn, smm[wv].mn);
-    }
-    const double mu = st1.s / double(K);
+    for (int wv = 1; wv < NW; ++wv) sx += dsum[wv];
+    const double mu = sx / double(K);
+    const float mu32 = float(mu);
     double s2 = 0.0;
+    uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const double keep = i * NT + tid < pairs ? 1.0 : 0.0;
+        if (i * NT + tid >= pairs) continue;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const double d = (xd[i][c] - mu) * keep;
+            const double d = double(v[i][c]) - mu;
             s2 += d * d;
+            v[i][c] -= mu32;                           // fl32(x - mu32), kept for the codes
+            amax = max(amax, __float_as_uint(fabsf(v[i][c])));
         }
     }
     s2 = wave_sum63(s2);
-    if (lane == 63) dscr[wave] = s2;
+    amax = wave_umax63(amax);
+    if (lane == 63) {
+        dsq[wave] = s2;
+        dmax[wave] = amax;
+    }
     __syncthreads();
-    double v2 = dscr[0];
+    double v2 = dsq[0];
+    uint32_t am = dmax[0];
 #pragma unroll
-    for (int wv = 1; wv < NW; ++wv) v2 += dscr[wv];
-    const float mu32 = float(mu);
+    for (int wv = 1; wv < NW; ++wv) {
+        v2 += dsq[wv];
+        am = max(am, dmax[wv]);
+    }
     const float rs32 = float(1.0 / sqrt(v2 / double(K) + eps));
-    const float gamma = fmaxf(fabsf((st1.mx - mu32) * rs32), fabsf((st1.mn - mu32) * rs32));
+    const float gamma = __uint_as_float(am) * rs32;
 
     // 3. codes into LDS in the decode layout, one dword per pair; zero
     //    padding rows K..Kp-1. Fast path u = h (Q_b rcp(gamma)) (Q_b is a power
@@ -348,7 +348,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const float h = (v[i][c] - mu32) * rs32;
+            const float h = v[i][c] * rs32;
             v[i][c] = h;
             const float u = fminf(fmaxf(h * cq, -ucl), ucl);
             slow |= fabsf(u - rintf(u)) < fabsf(u) * 0x1p-20f;
@@ -378,13 +378,16 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     }
     for (int k = int(K) + tid; k < Kp; k += NT) qs[q_pos(k)] = 0;
     if (gamma_opt && blockIdx.x == 0 && tid == 0) gamma_opt[0] = gamma;
+    sq = wave_sum63_i(sq);
+    if (lane == 63) iscr[wave] = sq;
     __syncthreads();
 
     // 4. per column group: the product (token 0 lives in lanes with r == 0,
-    //    the rest are zero), then the 4 quarters' partial sums and the code
-    //    row sum through LDS, one barrier per group
-    sq = wave_sum63_i(sq);
-    if (lane == 63) iscr[wave] = sq;
+    //    the rest are zero), then the KQ parts' sums through LDS (one barrier
+    //    per group; none when a wave covers all of K) and the epilogue
+    int rowsum = 0;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
     const float scale = (beta[0] * gamma) / qb;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -395,7 +398,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const int64_t st = kq + 4 * i;
+            const int64_t st = kq + int64_t(KQ) * i;
             const int64_t tq = st * 4 + g;
             // lanes r != 0 carry tokens whose outputs are never read, and steps
             // past the column's tiles have all-zero signs: no masking needed
@@ -405,52 +408,82 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
             for (int s8 = 0; s8 < 8; ++s8) b[s8] = src[s8];
             w1a8_step(w[it][i], b, acc);
         }
-        red[it & 1][wave][lane] = w1a8_combine(acc);
-        __syncthreads();
-        if (kq == 0 && r == 0) {
-            int rowsum = 0;
+        i32x4_t sum = w1a8_combine(acc);
+        if constexpr (KQ > 1) {
+            red[it & 1][wave][lane] = sum;
+            __syncthreads();
+            if (kq != 0 || r != 0) continue;
 #pragma unroll
-            for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
-            const i32x4_t (&rd)[NW][64] = red[it & 1];
-            const i32x4_t sum = ((rd[f][lane] + rd[f + F][lane]) + rd[f + 2 * F][lane]) + rd[f + 3 * F][lane];
-            const int64_t j0 = grp * 16 * F;
+            for (int q = 1; q < KQ; ++q) sum += red[it & 1][f + F * q][lane];
+        } else {
+            if (r != 0) continue;
+        }
+        const int64_t j0 = grp * 16 * F + 16 * f + 4 * g;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t col = j0 + 16 * f + 4 * g + i;
-                if (col >= N) continue;
-                const int32_t a = 2 * sum[i] - rowsum;
-                y[col] = float(a) * scale;
-                if (acc_opt) acc_opt[col] = a;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int64_t col = j0 + i;
+            if (col >= N) continue;
+            const int32_t a = 2 * sum[i] - rowsum;
+            y[col] = float(a) * scale;
+            if (acc_opt) acc_opt[col] = a;
         }
     }
 }
 
 bool w1a8_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
 
-// One block per CU runs the prologue once and then takes up to 4 column
-// groups, blockIdx.x + i * gridDim.x.
-constexpr int kD1MaxGrid = 256;
+// The fragments per group F (a divisor of NW whose steps fit the tile budget)
+// and the groups per block IT, for NV pieces per thread.
+template <int NV, int NW>
+constexpr bool w1a8_d1_ok(int f, int it) {
+    return f <= NW && NW % f == 0 && it * w1a8_d1_steps(NV, f) <= kD1MaxTiles;
+}
 
-// Preloaded sign tiles per thread are IT x S = IT x NV x NW / 8 x 16 bytes:
-// at most 2 groups per block once NV x NW reaches 64 keeps them in registers.
-constexpr int d1_it_cap(int nv, int nw) { return nv * nw >= 64 ? 2 : 4; }
-
-template <int NV, int NW, typename XT>
-static void launch_w1a8_decode1_it(int it, unsigned grid, const XT* x, int64_t K, int64_t N, int64_t TQ, double eps,
-                                   float qb, float lim, const uint32_t* P, const float* beta, float* y,
-                                   int32_t* acc_opt, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
-    constexpr unsigned nt = NW * 64;
+template <int NV, int NW, int F, typename XT>
+static void launch_w1a8_decode1_f(int it, unsigned grid, const XT* x, int64_t K, int64_t N, int64_t TQ, double eps,
+                                  float qb, float lim, const uint32_t* P, const float* beta, float* y,
+                                  int32_t* acc_opt, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
 #define BGB_D1X(ITV) \
-    bitlinear_decode1_kernel<NV, NW, ITV, XT><<<grid, nt, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, \
-                                                                   xq_opt, gamma_opt)
-    if (it == 1) BGB_D1X(1);
-    else if (it == 2) BGB_D1X(2);
-    else if constexpr (d1_it_cap(NV, NW) >= 4) {
-        if (it == 3) BGB_D1X(3);
-        else BGB_D1X(4);
+    bitlinear_decode1_kernel<NV, NW, F, ITV, XT><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, beta, y, \
+                                                                          acc_opt, xq_opt, gamma_opt)
+    if constexpr (w1a8_d1_ok<NV, NW>(F, 1)) {
+        if constexpr (w1a8_d1_ok<NV, NW>(F, 2)) {
+            if (it == 2) {
+                BGB_D1X(2);
+                return;
+            }
+        }
+        BGB_D1X(1);
     }
 #undef BGB_D1X
+}
+
+template <int NV, int NW, typename XT>
+static void launch_w1a8_decode1_nv(const XT* x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
+                                   const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
+                                   float* gamma_opt, hipStream_t s) {
+    // the fewest fragments per group that give each block (one per CU) a
+    // single group; failing that, the most allowed and up to 2 groups per
+    // block, then more blocks
+    const int64_t frags = (N + 15) / 16;
+    int F = 1;
+    while (2 * F <= NW && w1a8_d1_ok<NV, NW>(2 * F, 1) && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
+    const int64_t groups = (frags + F - 1) / F;
+    int64_t grid = groups < kD1MaxGrid ? groups : kD1MaxGrid;
+    int it = int((groups + grid - 1) / grid);
+    const int it_max = w1a8_d1_ok<NV, NW>(F, 2) ? 2 : 1;
+    if (it > it_max) {
+        it = it_max;
+        grid = (groups + it - 1) / it;
+    }
+    const unsigned gr = unsigned(grid);
+#define BGB_D1F(FV) \
+    launch_w1a8_decode1_f<NV, NW, FV, XT>(it, gr, x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
+    if (F == 1) BGB_D1F(1);
+    else if (F == 2) BGB_D1F(2);
+    else if (F == 4) BGB_D1F(4);
+    else BGB_D1F(8);
+#undef BGB_D1F
 }
 
 template <int NW, typename XT>
@@ -462,17 +495,7 @@ static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps
     const int64_t TQ = tiles_per_col(K);
     const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
     const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : 16;
-    const int64_t ngroups = (N + 16 * (NW / 4) - 1) / (16 * (NW / 4));
-    int64_t grid = ngroups < kD1MaxGrid ? ngroups : kD1MaxGrid;
-    int it = int((ngroups + grid - 1) / grid);
-    const int it_max = d1_it_cap(nvp, NW);
-    if (it > it_max) {
-        it = it_max;
-        grid = (ngroups + it_max - 1) / it_max;
-    }
-    const unsigned g = unsigned(grid);
-#define BGB_D1(NVV) \
-    launch_w1a8_decode1_it<NVV, NW, XT>(it, g, x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
+#define BGB_D1(NVV) launch_w1a8_decode1_nv<NVV, NW, XT>(x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
     if (nvp == 1) BGB_D1(1);
     else if (nvp == 2) BGB_D1(2);
     else if (nvp == 4) BGB_D1(4);
@@ -484,20 +507,24 @@ static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps
 hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
                                const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                float* gamma_opt, hipStream_t s) {
-    // 8-wave blocks (32 columns per group) while that still gives every CU a
-    // group; 4-wave blocks (16 columns) for narrower layers
+    // 8-wave blocks for layers of at least 8192 columns; 4-wave blocks (one
+    // wave per SIMD, so the per-wave prologue work is not repeated) below
     const bool wide = (N + 31) / 32 >= kD1MaxGrid;
     if (x_bf16) {
         const uint16_t* xb = static_cast<const uint16_t*>(x);
-        if (wide) launch_w1a8_decode1_nw<kD1WavesW1A8>(xb, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        if (wide) launch_w1a8_decode1_nw<8>(xb, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
         else launch_w1a8_decode1_nw<4>(xb, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
     } else {
         const float* xf = static_cast<const float*>(x);
-        if (wide) launch_w1a8_decode1_nw<kD1WavesW1A8>(xf, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        if (wide) launch_w1a8_decode1_nw<8>(xf, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
         else launch_w1a8_decode1_nw<4>(xf, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
     }
     return hipGetLastError();
 }
+
+// Preloaded tiles per thread for the single-token W1A16 kernel: IT x S with
+// S = NV x NW / 4; at most 2 groups per block once NV x NW reaches 32.
+constexpr int d1_it_cap(int nv, int nw) { return nv * nw >= 64 ? 2 : 4; }
 
 hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma, const float* beta, float qb,
                             int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
