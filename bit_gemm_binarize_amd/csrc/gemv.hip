@@ -522,10 +522,6 @@ hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, 
     return hipGetLastError();
 }
 
-// Preloaded tiles per thread for the single-token W1A16 kernel: IT x S with
-// S = NV x NW / 4; at most 2 groups per block once NV x NW reaches 32.
-constexpr int d1_it_cap(int nv, int nw) { return nv * nw >= 64 ? 2 : 4; }
-
 hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma, const float* beta, float qb,
                             int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
                             hipStream_t s) {
@@ -748,17 +744,18 @@ gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xp
 
 // Single token, activation staging fused: the block permutes x into LDS and
 // computes the four X_T itself, once, then takes up to IT column groups
-// (blockIdx.x + i * gridDim.x) of 16 * NW / 4 columns, as the W1A8 kernel.
-template <bool kF16, int NV, int NW, int IT>
+// (blockIdx.x + i * gridDim.x) of F 16-column fragments, as the W1A8 kernel.
+template <bool kF16, int NV, int NW, int F, int IT>
 __global__ void __launch_bounds__(NW * 64)
 fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
                    const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
     constexpr int NT = NW * 64;
-    constexpr int F = NW / 4;
-    constexpr int S = NV * NW / 4;     // steps per wave: TQ <= NV NT / 16 tiles, so 4 quarters x S x 4 tiles cover them
+    constexpr int KQ = NW / F;
+    constexpr int S = NV * F;          // steps per wave: TQ <= NV NT / 16 tiles = NV NW steps, over KQ waves
+    static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "single-token W1A16 shape");
     __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
     __shared__ __attribute__((aligned(16))) uint16_t xzero[128];   // B operand of steps past the last tile
-    __shared__ f32x4_t red[2][NW][64];
+    __shared__ f32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
     __shared__ double dX[NW][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
@@ -783,7 +780,7 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
         const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
-        preload<S>(w[it], P, kq, 4, steps, TQ, N, jj, g);
+        preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
     }
     // With one group per block, the scales of the 4 columns j0..j0+3 this
     // lane writes are requested here, behind the sign tiles the epilogue
@@ -841,7 +838,7 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     // 3. per column group: the product (token 0 lives in lanes with r == 0;
     //    the other lanes' tokens are never read; tiles past the last one read
     //    zero activations, since a zero sign word decodes to -1 weights), then
-    //    the quarters' sums through LDS
+    //    the KQ parts' sums through LDS (none when a wave covers all of K)
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
@@ -851,49 +848,86 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int T = 0; T < 4; ++T) acc[0][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const int64_t st = kq + 4 * i;
+            const int64_t st = kq + int64_t(KQ) * i;
             const int64_t tq = st * 4 + g;
             const u32x4_t* src = reinterpret_cast<const u32x4_t*>(st < steps && tq < TQ ? xs + tq * 128 : xzero);
             auto bsrc = [&](int u, int) -> u32x4_t { return src[u]; };
             w1a16_step<kF16, 1>(w[it][i], bsrc, acc);
         }
         // per wave z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3
-        red[it & 1][wave][lane] = ((8.0f * acc[0][0] + 4.0f * acc[0][1]) + 2.0f * acc[0][2]) + 2.0f * acc[0][3];
-        __syncthreads();
-        if (kq == 0 && r == 0) {
-            const f32x4_t (&rd)[NW][64] = red[it & 1];
-            const f32x4_t z = ((rd[f][lane] + rd[f + F][lane]) + rd[f + 2 * F][lane]) + rd[f + 3 * F][lane];
-            const int64_t j0 = grp * 16 * F;
-            const uint32_t aw[4] = {araw[0].x, araw[0].y, araw[1].x, araw[1].y};
+        f32x4_t z = ((8.0f * acc[0][0] + 4.0f * acc[0][1]) + 2.0f * acc[0][2]) + 2.0f * acc[0][3];
+        if constexpr (KQ > 1) {
+            red[it & 1][wave][lane] = z;
+            __syncthreads();
+            if (kq != 0 || r != 0) continue;
+            // the parts in a fixed order: kq = 0, 1, ..., KQ - 1
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t col = j0 + 16 * f + 4 * g + i;
-                if (col >= N) continue;
-                const float a = !kAlphaAhead ? load_alpha(alpha, alpha_f16, col)
-                                : alpha_f16  ? f16_to_f32(uint16_t(aw[i >> 1] >> (16 * (i & 1))))
-                                             : __uint_as_float(aw[i]);
-                store_y(y, y_dtype, col, a * (2.0f * (z[i] - corr) - xall));
-            }
+            for (int q = 1; q < KQ; ++q) z += red[it & 1][f + F * q][lane];
+        } else {
+            if (r != 0) continue;
+        }
+        const int64_t j0 = grp * 16 * F + 16 * f + 4 * g;
+        const uint32_t aw[4] = {araw[0].x, araw[0].y, araw[1].x, araw[1].y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t col = j0 + i;
+            if (col >= N) continue;
+            const float a = !kAlphaAhead ? load_alpha(alpha, alpha_f16, col)
+                            : alpha_f16  ? f16_to_f32(uint16_t(aw[i >> 1] >> (16 * (i & 1))))
+                                         : __uint_as_float(aw[i]);
+            store_y(y, y_dtype, col, a * (2.0f * (z[i] - corr) - xall));
         }
     }
 }
 
 bool w1a16_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
 
-template <bool kF16, int NV, int NW>
-static void launch_w1a16_decode1_it(int it, unsigned grid, const uint16_t* x, int64_t K, int64_t N, int64_t TQ,
-                                    const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
-                                    hipStream_t s) {
-    constexpr unsigned nt = NW * 64;
+template <int NV, int NW>
+constexpr bool w1a16_d1_ok(int f, int it) {
+    return f <= NW && NW % f == 0 && it * NV * f <= kD1MaxTiles;
+}
+
+template <bool kF16, int NV, int NW, int F>
+static void launch_w1a16_decode1_f(int it, unsigned grid, const uint16_t* x, int64_t K, int64_t N, int64_t TQ,
+                                   const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
+                                   hipStream_t s) {
 #define BGB_F1X(ITV) \
-    fbi_decode1_kernel<kF16, NV, NW, ITV><<<grid, nt, 0, s>>>(x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype)
-    if (it == 1) BGB_F1X(1);
-    else if (it == 2) BGB_F1X(2);
-    else if constexpr (d1_it_cap(2 * NV, NW) >= 4) {
-        if (it == 3) BGB_F1X(3);
-        else BGB_F1X(4);
+    fbi_decode1_kernel<kF16, NV, NW, F, ITV><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype)
+    if constexpr (w1a16_d1_ok<NV, NW>(F, 1)) {
+        if constexpr (w1a16_d1_ok<NV, NW>(F, 2)) {
+            if (it == 2) {
+                BGB_F1X(2);
+                return;
+            }
+        }
+        BGB_F1X(1);
     }
 #undef BGB_F1X
+}
+
+template <bool kF16, int NV, int NW>
+static void launch_w1a16_decode1_nv(const uint16_t* x, int64_t K, int64_t N, int64_t TQ, const uint32_t* P,
+                                    const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    // as for W1A8: the fewest fragments per group that give each block one
+    // group, else the most allowed and up to 2 groups per block
+    const int64_t frags = (N + 15) / 16;
+    int F = 1;
+    while (2 * F <= NW && w1a16_d1_ok<NV, NW>(2 * F, 1) && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
+    const int64_t groups = (frags + F - 1) / F;
+    int64_t grid = groups < kD1MaxGrid ? groups : kD1MaxGrid;
+    int it = int((groups + grid - 1) / grid);
+    const int it_max = w1a16_d1_ok<NV, NW>(F, 2) ? 2 : 1;
+    if (it > it_max) {
+        it = it_max;
+        grid = (groups + it - 1) / it;
+    }
+    const unsigned gr = unsigned(grid);
+#define BGB_F1F(FV) launch_w1a16_decode1_f<kF16, NV, NW, FV>(it, gr, x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
+    if (F == 1) BGB_F1F(1);
+    else if (F == 2) BGB_F1F(2);
+    else if (F == 4) BGB_F1F(4);
+    else BGB_F1F(8);
+#undef BGB_F1F
 }
 
 template <bool kF16, int NW>
@@ -904,16 +938,7 @@ static void launch_w1a16_decode1_nw(const uint16_t* x, int64_t K, int64_t N, con
     const int64_t TQ = tiles_per_col(K);
     const int nv = int((TQ * 16 + nt - 1) / nt);
     const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : 8;
-    const int64_t ngroups = (N + 16 * (NW / 4) - 1) / (16 * (NW / 4));
-    int64_t grid = ngroups < kD1MaxGrid ? ngroups : kD1MaxGrid;
-    int it = int((ngroups + grid - 1) / grid);
-    const int it_max = d1_it_cap(2 * nvp, NW);
-    if (it > it_max) {
-        it = it_max;
-        grid = (ngroups + it_max - 1) / it_max;
-    }
-    const unsigned g = unsigned(grid);
-#define BGB_F1(NVV) launch_w1a16_decode1_it<kF16, NVV, NW>(it, g, x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
+#define BGB_F1(NVV) launch_w1a16_decode1_nv<kF16, NVV, NW>(x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
     if (nvp == 1) BGB_F1(1);
     else if (nvp == 2) BGB_F1(2);
     else if (nvp == 4) BGB_F1(4);
@@ -923,8 +948,7 @@ static void launch_w1a16_decode1_nw(const uint16_t* x, int64_t K, int64_t N, con
 
 hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
-    // 8-wave blocks (32 columns per group) while that still gives every CU a
-    // group; 4-wave blocks (16 columns) for narrower layers
+    // 8-wave blocks for layers of at least 8192 columns, 4-wave blocks below
     const uint16_t* xx = static_cast<const uint16_t*>(x);
     const bool wide = (N + 31) / 32 >= kD1MaxGrid;
     if (x_f16) {
