@@ -118,6 +118,10 @@ hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, 
                                const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                float* gamma_opt, hipStream_t s);
 bool w1a16_decode1_supported(int64_t K);
+// 2 <= M <= 16 tokens staged in LDS by every block (M (Kp + 8) 2 bytes <= 140 KB)
+bool w1a16_decodem_supported(int64_t M, int64_t K);
+hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 

@@ -985,6 +985,204 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
     return hipGetLastError();
 }
 
+// A few tokens (2 <= M <= 16), activation staging fused: every block copies
+// the M tokens into LDS in the decode layout (per token, rows 32t + u and
+// 32t + u + 16 side by side), then takes its column group(s) as the
+// single-token kernel does. The signs decode to +-1 directly (no per-type
+// activation sums): for MFMA u, dword e of the A operand is word e's bit u as
+// the sign of the low 16-bit value and bit u + 16 as that of the high one,
+// over the bit pattern of 1.0.
+constexpr int kDmMaxTokens = 16;
+constexpr int kDmWaves = 8;
+constexpr int kDmLdsBytes = 140 * 1024;              // staged tokens: [M][Kp + 8] 16-bit values
+constexpr int kDmMaxPieces = 16;                     // 16-byte token pieces per thread
+
+template <bool kF16, int F, int S, int IT>
+__global__ void __launch_bounds__(kDmWaves * 64)
+fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
+                   const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
+                   void* __restrict__ y, int y_dtype) {
+    constexpr int NW = kDmWaves, NT = NW * 64;
+    constexpr int KQ = NW / F;
+    static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "few-token W1A16 shape");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kDmLdsBytes / 2];
+    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];   // B operand of steps past the last tile
+    __shared__ f32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
+    const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
+    const int Kp = int(TQ * 128);
+    const int stride = Kp + 8;                           // 16 bytes apart: token rows fall in different banks
+    const int ppt = Kp / 8;                              // 16-byte pieces per token
+    const int pieces = M * ppt;
+    const int64_t steps = (TQ + 3) / 4;
+    const int Ki = int(K);
+
+    // 1. the tokens, 16 bytes per load: piece p is token p / ppt, rows
+    //    8 (p % ppt) .. + 7 (all inside K or all padding)
+    u32x4_t xv[kDmMaxPieces];
+#pragma unroll
+    for (int i = 0; i < kDmMaxPieces; ++i) {
+        const int p = i * NT + tid;
+        if (i * NT >= pieces) break;                     // uniform
+        const int m = p / ppt, k = 8 * (p - m * ppt);
+        const bool ok = p < pieces && k < Ki;
+        const u32x4_t t = *reinterpret_cast<const u32x4_t*>(x + (ok ? int64_t(m) * Ki + k : 0));
+        xv[i] = t & u32x4_t(0u - uint32_t(ok));
+    }
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the tokens are in
+    u32x4_t w[IT][S];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
+        preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. scatter each piece's 8 rows into its token's decode layout (rows
+    //    32t + u and 32t + u + 16 side by side)
+    if (tid < 16) reinterpret_cast<u32x4_t*>(xzero)[tid] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kDmMaxPieces; ++i) {
+        const int p = i * NT + tid;
+        if (i * NT >= pieces) break;
+        if (p >= pieces) continue;
+        const int m = p / ppt, k = 8 * (p - m * ppt), t = k >> 5, bq = k & 31;
+        uint16_t* dst = xs + m * stride + (t >> 2) * 128 + (bq & 15) * 8 + (t & 3) * 2 + (bq >> 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[8 * e] = uint16_t(e & 1 ? xv[i][e >> 1] >> 16 : xv[i][e >> 1] & 0xffffu);
+    }
+    __syncthreads();
+
+    // 3. per column group: the product for this lane's token r (lanes r >= M
+    //    read token 0; their outputs are never stored), the KQ parts' sums
+    //    through LDS, the epilogue
+    constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;
+    const uint16_t* xrow = xs + (r < M ? r : 0) * stride;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        if (grp >= ngroups) break;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int64_t st = kq + int64_t(KQ) * i;
+            const int64_t tq = st * 4 + g;
+            // a step past the column's tiles has zero sign words (all -1): it
+            // must read zero activations
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(st < steps && tq < TQ ? xrow + tq * 128 : xzero);
+            const u32x4_t wv = w[it][i];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                u32x4_t a;   // (~(word << (15 - u)) & 0x80008000) | 1.0: signs of rows 32e + u, 32e + u + 16
+                a.x = __builtin_amdgcn_bitop3_b32(wv.x << (15 - u), 0x80008000u, kOne, 0xAE);
+                a.y = __builtin_amdgcn_bitop3_b32(wv.y << (15 - u), 0x80008000u, kOne, 0xAE);
+                a.z = __builtin_amdgcn_bitop3_b32(wv.z << (15 - u), 0x80008000u, kOne, 0xAE);
+                a.w = __builtin_amdgcn_bitop3_b32(wv.w << (15 - u), 0x80008000u, kOne, 0xAE);
+                acc = mfma16<kF16>(a, src[u], acc);
+            }
+        }
+        f32x4_t z = acc;
+        if constexpr (KQ > 1) {
+            red[it & 1][wave][lane] = z;
+            __syncthreads();
+            if (kq != 0 || r >= M) continue;
+            // the parts in a fixed order: kq = 0, 1, ..., KQ - 1
+#pragma unroll
+            for (int q = 1; q < KQ; ++q) z += red[it & 1][f + F * q][lane];
+        } else {
+            if (r >= M) continue;
+        }
+        const int64_t j0 = grp * 16 * F + 16 * f + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t col = j0 + i;
+            if (col >= N) continue;
+            store_y(y, y_dtype, int64_t(r) * N + col, load_alpha(alpha, alpha_f16, col) * z[i]);
+        }
+    }
+}
+
+bool w1a16_decodem_supported(int64_t M, int64_t K) {
+    if (M < 2 || M > kDmMaxTokens) return false;
+    const int64_t Kp = padded_k(K);
+    return M * (Kp + 8) * 2 <= kDmLdsBytes && M * (Kp / 8) <= int64_t(kDmMaxPieces) * kDmWaves * 64;
+}
+
+template <bool kF16, int F, int S>
+static void launch_w1a16_decodem_s(int it, unsigned grid, const uint16_t* x, int M, int64_t K, int64_t N,
+                                   int64_t TQ, const uint32_t* P, const void* alpha, int alpha_f16, void* y,
+                                   int y_dtype, hipStream_t s) {
+#define BGB_DMX(ITV)                                                                                           \
+    fbi_decodem_kernel<kF16, F, S, ITV><<<grid, kDmWaves * 64, 0, s>>>(x, M, K, N, TQ, P, alpha, alpha_f16, y, \
+                                                                        y_dtype)
+    if constexpr (2 * S <= kD1MaxTiles) {
+        if (it == 2) {
+            BGB_DMX(2);
+            return;
+        }
+    }
+    BGB_DMX(1);
+#undef BGB_DMX
+}
+
+template <bool kF16, int F>
+static void launch_w1a16_decodem_f(int S, int it, unsigned grid, const uint16_t* x, int M, int64_t K, int64_t N,
+                                   int64_t TQ, const uint32_t* P, const void* alpha, int alpha_f16, void* y,
+                                   int y_dtype, hipStream_t s) {
+#define BGB_DMS(SV) launch_w1a16_decodem_s<kF16, F, SV>(it, grid, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
+    if (S == 1) BGB_DMS(1);
+    else if (S == 2) BGB_DMS(2);
+    else if (S == 4) BGB_DMS(4);
+    else BGB_DMS(8);
+#undef BGB_DMS
+}
+
+template <bool kF16>
+static hipError_t launch_w1a16_decodem_t(const uint16_t* x, int M, int64_t K, int64_t N, const uint32_t* P,
+                                         const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    const int64_t TQ = tiles_per_col(K);
+    const int64_t steps = (TQ + 3) / 4;
+    const int64_t frags = (N + 15) / 16;
+    // steps per wave for F fragments per group: the NW / F waves of a
+    // fragment share the steps (a power of two, at most 8 tiles per thread)
+    auto steps_per_wave = [&](int f) {
+        const int64_t need = (steps + kDmWaves / f - 1) / (kDmWaves / f);
+        return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+    };
+    // the fewest fragments per group that give each block one group; else
+    // the most allowed and up to two groups per block
+    int F = 1;
+    while (2 * F <= kDmWaves && steps_per_wave(2 * F) <= kD1MaxTiles && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
+    const int S = steps_per_wave(F);
+    if (S > kD1MaxTiles) return hipErrorInvalidValue;   // K beyond the fused size (not reached: supported())
+    const int64_t groups = (frags + F - 1) / F;
+    int64_t grid = groups < kD1MaxGrid ? groups : kD1MaxGrid;
+    int it = int((groups + grid - 1) / grid);
+    const int it_max = 2 * S <= kD1MaxTiles ? 2 : 1;
+    if (it > it_max) {
+        it = it_max;
+        grid = (groups + it - 1) / it;
+    }
+    const unsigned gr = unsigned(grid);
+#define BGB_DMF(FV) launch_w1a16_decodem_f<kF16, FV>(S, it, gr, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
+    if (F == 1) BGB_DMF(1);
+    else if (F == 2) BGB_DMF(2);
+    else if (F == 4) BGB_DMF(4);
+    else BGB_DMF(8);
+#undef BGB_DMF
+    return hipGetLastError();
+}
+
+hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    if (!w1a16_decodem_supported(M, K)) return hipErrorInvalidValue;
+    const uint16_t* xx = static_cast<const uint16_t*>(x);
+    return x_f16 ? launch_w1a16_decodem_t<true>(xx, int(M), K, N, P, alpha, alpha_f16, y, y_dtype, s)
+                 : launch_w1a16_decodem_t<false>(xx, int(M), K, N, P, alpha, alpha_f16, y, y_dtype, s);
+}
+
 hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M, int64_t K, int64_t N,
                              const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
                              hipStream_t s) {

@@ -30,11 +30,15 @@ def _run(bgb, orc, W, xb, x_kind, y_kind, adt="f32"):
 
 CASES = [
     # (M, K, N) covering every dispatch path: single-token fused decode (M = 1,
-    # K <= 16384), single token beyond the fused size, decode with 1..4 token
-    # fragments (M <= 32), and the MFMA GEMM (M > 32, split-K plans for small
-    # M x N); ragged N and K tails.
+    # K <= 16384), single token beyond the fused size, 2..16 tokens staged in
+    # LDS, decode with 1..2 token fragments after a prep pass (M <= 32), and the
+    # MFMA GEMM (M > 32, split-K plans for small M x N); ragged N and K tails.
     (1, 768, 768), (1, 11008, 100), (1, 16416, 40), (8, 768, 768), (3, 96, 65), (16, 160, 300),
     (1, 16384, 4000), (1, 16384, 8200), (1, 11008, 4096),
+    # 2..16 tokens staged in LDS by every block (one group per block, two,
+    # K split over 1..8 waves), and sizes just past what fits (two launches)
+    (2, 16384, 300), (4, 11008, 4096), (5, 11008, 100), (6, 11008, 70), (12, 2048, 1000), (16, 4096, 4100),
+    (16, 4096, 12288), (2, 1024, 40000),
     (5, 4096, 33), (17, 96, 65), (40, 768, 260), (64, 2048, 520), (65, 256, 300), (130, 256, 300),
     (200, 352, 513),
     # GEMM pipeline: 4-stage ring with 0 or 2 tail stages, ragged M/N, padded K
