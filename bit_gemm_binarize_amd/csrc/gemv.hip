@@ -995,9 +995,9 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
 constexpr int kDmMaxTokens = 16;
 constexpr int kDmWaves = 8;
 constexpr int kDmLdsBytes = 140 * 1024;              // staged tokens: [M][Kp + 8] 16-bit values
-constexpr int kDmMaxPieces = 16;                     // 16-byte token pieces per thread
+constexpr int kDmMaxJobs = 2;                        // 256-byte token tiles per thread
 
-template <bool kF16, int F, int S, int IT>
+template <bool kF16, bool kTileJobs, int F, int S, int IT>
 __global__ void __launch_bounds__(kDmWaves * 64)
 fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
                    const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
@@ -1013,45 +1013,88 @@ fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
     const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
     const int Kp = int(TQ * 128);
     const int stride = Kp + 8;                           // 16 bytes apart: token rows fall in different banks
-    const int ppt = Kp / 8;                              // 16-byte pieces per token
-    const int pieces = M * ppt;
     const int64_t steps = (TQ + 3) / 4;
     const int Ki = int(K);
 
-    // 1. the tokens, 16 bytes per load: piece p is token p / ppt, rows
-    //    8 (p % ppt) .. + 7 (all inside K or all padding)
-    u32x4_t xv[kDmMaxPieces];
-#pragma unroll
-    for (int i = 0; i < kDmMaxPieces; ++i) {
-        const int p = i * NT + tid;
-        if (i * NT >= pieces) break;                     // uniform
-        const int m = p / ppt, k = 8 * (p - m * ppt);
-        const bool ok = p < pieces && k < Ki;
-        const u32x4_t t = *reinterpret_cast<const u32x4_t*>(x + (ok ? int64_t(m) * Ki + k : 0));
-        xv[i] = t & u32x4_t(0u - uint32_t(ok));
-    }
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the tokens are in
+    // 1.-2. the tokens into the decode layout (rows 32t + u and 32t + u + 16
+    //    side by side, see the single-token kernel). The sign tiles are
+    //    requested once the tokens are in. Rows past K read as zeros.
     u32x4_t w[IT][S];
+    auto preload_all = [&]() {
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the tokens are in
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
-        const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
-        preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 2. scatter each piece's 8 rows into its token's decode layout (rows
-    //    32t + u and 32t + u + 16 side by side)
+        for (int it = 0; it < IT; ++it) {
+            const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+            const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
+            preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load16 = [&](int m, int k, bool ok) {
+        ok = ok && k < Ki;
+        const u32x4_t t = *reinterpret_cast<const u32x4_t*>(x + (ok ? int64_t(m) * Ki + k : 0));
+        return t & u32x4_t(0u - uint32_t(ok));
+    };
     if (tid < 16) reinterpret_cast<u32x4_t*>(xzero)[tid] = u32x4_t{0u, 0u, 0u, 0u};
+    const int tiles = M * int(TQ);
+    if constexpr (kTileJobs) {
+        // at least one 128-row tile per thread: job J is tile J / M of token
+        // J % M (neighbouring lanes write different tokens' rows, different
+        // banks); chunk u of a tile holds, for e = 0..3, rows 32e + u and
+        // 32e + u + 16 as one dword, both in dword (u % 8) / 2, same half, of
+        // the 16-byte pieces 4e + u / 8 and 4e + 2 + u / 8: one v_perm per
+        // dword, 16 16-byte LDS writes per tile
+        u32x4_t xv[kDmMaxJobs][16];
 #pragma unroll
-    for (int i = 0; i < kDmMaxPieces; ++i) {
-        const int p = i * NT + tid;
-        if (i * NT >= pieces) break;
-        if (p >= pieces) continue;
-        const int m = p / ppt, k = 8 * (p - m * ppt), t = k >> 5, bq = k & 31;
-        uint16_t* dst = xs + m * stride + (t >> 2) * 128 + (bq & 15) * 8 + (t & 3) * 2 + (bq >> 4);
+        for (int i = 0; i < kDmMaxJobs; ++i) {
+            if (i * NT >= tiles) break;                  // uniform
+            const int J = i * NT + tid, m = J % M, tq = J / M;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[8 * e] = uint16_t(e & 1 ? xv[i][e >> 1] >> 16 : xv[i][e >> 1] & 0xffffu);
+            for (int j = 0; j < 16; ++j) xv[i][j] = load16(m, 128 * tq + 8 * j, J < tiles);
+        }
+        preload_all();
+#pragma unroll
+        for (int i = 0; i < kDmMaxJobs; ++i) {
+            if (i * NT >= tiles) break;
+            const int J = i * NT + tid;
+            if (J >= tiles) continue;
+            const int m = J % M, tq = J / M;
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + m * stride + tq * 128);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int d = (u % 8) / 2;
+                const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
+                u32x4_t o;
+                o.x = __builtin_amdgcn_perm(xv[i][2 + u / 8][d], xv[i][0 + u / 8][d], sel);
+                o.y = __builtin_amdgcn_perm(xv[i][6 + u / 8][d], xv[i][4 + u / 8][d], sel);
+                o.z = __builtin_amdgcn_perm(xv[i][10 + u / 8][d], xv[i][8 + u / 8][d], sel);
+                o.w = __builtin_amdgcn_perm(xv[i][14 + u / 8][d], xv[i][12 + u / 8][d], sel);
+                dst[u] = o;
+            }
+        }
+    } else {
+        // fewer tiles than threads: one 16-byte piece (8 rows) per job, piece p
+        // of token p / ppt, its 8 values scattered 16 bytes apart
+        const int ppt = int(TQ) * 16, pieces = M * ppt;
+        u32x4_t xv[kDmMaxJobs * 8];
+#pragma unroll
+        for (int i = 0; i < kDmMaxJobs * 8; ++i) {
+            if (i * NT >= pieces) break;
+            const int p = i * NT + tid, m = p / ppt;
+            xv[i] = load16(m, 8 * (p - m * ppt), p < pieces);
+        }
+        preload_all();
+#pragma unroll
+        for (int i = 0; i < kDmMaxJobs * 8; ++i) {
+            if (i * NT >= pieces) break;
+            const int p = i * NT + tid;
+            if (p >= pieces) continue;
+            const int m = p / ppt, k = 8 * (p - m * ppt), t = k >> 5, bq = k & 31;
+            uint16_t* dst = xs + m * stride + (t >> 2) * 128 + (bq & 15) * 8 + (t & 3) * 2 + (bq >> 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dst[8 * e] = uint16_t(e & 1 ? xv[i][e >> 1] >> 16 : xv[i][e >> 1] & 0xffffu);
+        }
     }
     __syncthreads();
 
@@ -1107,15 +1150,15 @@ fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
 bool w1a16_decodem_supported(int64_t M, int64_t K) {
     if (M < 2 || M > kDmMaxTokens) return false;
     const int64_t Kp = padded_k(K);
-    return M * (Kp + 8) * 2 <= kDmLdsBytes && M * (Kp / 8) <= int64_t(kDmMaxPieces) * kDmWaves * 64;
+    return M * (Kp + 8) * 2 <= kDmLdsBytes && M * (Kp / 128) <= int64_t(kDmMaxJobs) * kDmWaves * 64;
 }
 
-template <bool kF16, int F, int S>
+template <bool kF16, bool kTJ, int F, int S>
 static void launch_w1a16_decodem_s(int it, unsigned grid, const uint16_t* x, int M, int64_t K, int64_t N,
                                    int64_t TQ, const uint32_t* P, const void* alpha, int alpha_f16, void* y,
                                    int y_dtype, hipStream_t s) {
 #define BGB_DMX(ITV)                                                                                           \
-    fbi_decodem_kernel<kF16, F, S, ITV><<<grid, kDmWaves * 64, 0, s>>>(x, M, K, N, TQ, P, alpha, alpha_f16, y, \
+    fbi_decodem_kernel<kF16, kTJ, F, S, ITV><<<grid, kDmWaves * 64, 0, s>>>(x, M, K, N, TQ, P, alpha, alpha_f16, y, \
                                                                         y_dtype)
     if constexpr (2 * S <= kD1MaxTiles) {
         if (it == 2) {
@@ -1127,11 +1170,11 @@ static void launch_w1a16_decodem_s(int it, unsigned grid, const uint16_t* x, int
 #undef BGB_DMX
 }
 
-template <bool kF16, int F>
+template <bool kF16, bool kTJ, int F>
 static void launch_w1a16_decodem_f(int S, int it, unsigned grid, const uint16_t* x, int M, int64_t K, int64_t N,
                                    int64_t TQ, const uint32_t* P, const void* alpha, int alpha_f16, void* y,
                                    int y_dtype, hipStream_t s) {
-#define BGB_DMS(SV) launch_w1a16_decodem_s<kF16, F, SV>(it, grid, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
+#define BGB_DMS(SV) launch_w1a16_decodem_s<kF16, kTJ, F, SV>(it, grid, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
     if (S == 1) BGB_DMS(1);
     else if (S == 2) BGB_DMS(2);
     else if (S == 4) BGB_DMS(4);
@@ -1139,7 +1182,7 @@ static void launch_w1a16_decodem_f(int S, int it, unsigned grid, const uint16_t*
 #undef BGB_DMS
 }
 
-template <bool kF16>
+template <bool kF16, bool kTJ>
 static hipError_t launch_w1a16_decodem_t(const uint16_t* x, int M, int64_t K, int64_t N, const uint32_t* P,
                                          const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
     const int64_t TQ = tiles_per_col(K);
@@ -1166,7 +1209,7 @@ static hipError_t launch_w1a16_decodem_t(const uint16_t* x, int M, int64_t K, in
         grid = (groups + it - 1) / it;
     }
     const unsigned gr = unsigned(grid);
-#define BGB_DMF(FV) launch_w1a16_decodem_f<kF16, FV>(S, it, gr, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
+#define BGB_DMF(FV) launch_w1a16_decodem_f<kF16, kTJ, FV>(S, it, gr, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
     if (F == 1) BGB_DMF(1);
     else if (F == 2) BGB_DMF(2);
     else if (F == 4) BGB_DMF(4);
@@ -1179,8 +1222,13 @@ hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, 
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
     if (!w1a16_decodem_supported(M, K)) return hipErrorInvalidValue;
     const uint16_t* xx = static_cast<const uint16_t*>(x);
-    return x_f16 ? launch_w1a16_decodem_t<true>(xx, int(M), K, N, P, alpha, alpha_f16, y, y_dtype, s)
-                 : launch_w1a16_decodem_t<false>(xx, int(M), K, N, P, alpha, alpha_f16, y, y_dtype, s);
+    // whole tiles per thread once there is at least one per thread
+    const bool tj = M * tiles_per_col(K) >= kDmWaves * 64;
+    const int m = int(M);
+    if (x_f16) return tj ? launch_w1a16_decodem_t<true, true>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
+                         : launch_w1a16_decodem_t<true, false>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+    return tj ? launch_w1a16_decodem_t<false, true>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
+              : launch_w1a16_decodem_t<false, false>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
 }
 
 hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M, int64_t K, int64_t N,
