@@ -93,6 +93,8 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
         return finish(bgb::launch_w1a16_decode1(x, x_f16, K, N, P, alpha, a_f16, y, ydt, s));
     if (bgb::w1a16_decodem_supported(M, K))
         return finish(bgb::launch_w1a16_decodem(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
+    if (bgb::w1a16_decodek_supported(M, K))
+        return finish(bgb::launch_w1a16_decodek(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
     if (M <= bgb::kGemvMaxM) {
         uint16_t* xp = reinterpret_cast<uint16_t*>(carve(ws, lay.xp));
         double* xpart = reinterpret_cast<double*>(carve(ws, lay.xpart));

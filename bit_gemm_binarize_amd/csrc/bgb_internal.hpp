@@ -120,6 +120,10 @@ hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, 
 bool w1a16_decode1_supported(int64_t K);
 // 2 <= M <= 16 tokens staged in LDS by every block (M (Kp + 8) 2 bytes <= 140 KB)
 bool w1a16_decodem_supported(int64_t M, int64_t K);
+// 2 <= M <= 64 tokens, K staged in chunks (any K)
+bool w1a16_decodek_supported(int64_t M, int64_t K);
+hipError_t launch_w1a16_decodek(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,

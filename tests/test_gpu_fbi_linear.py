@@ -39,6 +39,9 @@ CASES = [
     # K split over 1..8 waves), and sizes just past what fits (two launches)
     (2, 16384, 300), (4, 11008, 4096), (5, 11008, 100), (6, 11008, 70), (12, 2048, 1000), (16, 4096, 4100),
     (16, 4096, 12288), (2, 1024, 40000),
+    # 2..64 tokens with K staged in chunks: 16 or 32 tokens per block, one or
+    # more token blocks, chunk tails, K beyond the fused single-token size
+    (16, 11008, 4096), (24, 1024, 520), (33, 5632, 300), (64, 2048, 6144), (48, 352, 100), (20, 16416, 70),
     (5, 4096, 33), (17, 96, 65), (40, 768, 260), (64, 2048, 520), (65, 256, 300), (130, 256, 300),
     (200, 352, 513),
     # GEMM pipeline: 4-stage ring with 0 or 2 tail stages, ragged M/N, padded K
