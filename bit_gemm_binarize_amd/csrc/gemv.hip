@@ -40,6 +40,8 @@
 #include "bgb_device.hpp"
 #include "bgb_internal.hpp"
 
+#include <type_traits>
+
 namespace bgb {
 
 
@@ -1252,77 +1254,90 @@ hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, 
               : launch_w1a16_decodem_t<false, false>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
 }
 
-// Up to 64 tokens, activation staging fused, K in chunks: blocks of 8 waves
-// take (column group, block of up to 32 tokens); each stages its tokens' rows
-// chunk by chunk (SC steps of 512 rows, <= 64 KB of LDS) in the decode layout,
-// loading chunk c + 1 into registers while the matrix cores work on chunk c.
-// The signs decode to +-1 as in the few-token kernel; a wave's K part is
-// every KQ-th step, and KQ <= SC keeps every wave busy in every chunk.
+// Up to 64 tokens, activation staging fused, K in chunks. A block of 8 waves
+// takes FB 16-column fragments and up to 32 tokens (TF fragments of 16); K
+// goes in chunks of 8 TPW tiles of 128 rows, staged through LDS in the decode
+// layout, and wave w takes tiles w, w + 8, ... of each chunk for all FB
+// fragments, so an activation operand read from LDS feeds FB MFMAs. Here a
+// tile is one MFMA step of its own: lane group g of MFMA v takes bit pair
+// (u, u + 16), u = 4v + g, of the tile's 4 words (+-1 over the bit pattern of
+// 1.0) and the matching activations, chunk u of the tile. The next chunk's
+// activations and sign tiles load while the matrix cores work on this one;
+// the 8 waves' partial sums meet in LDS in a fixed order.
 constexpr int kDkWaves = 8;
 constexpr int kDkChunkElems = 32768;                // tokens x rows staged per chunk
 
-template <bool kF16, int TF, int F, int S, int IT>
+template <bool kF16, int TF, int FB, int TPW>
 __global__ void __launch_bounds__(kDkWaves * 64)
-fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ, int SC,
+fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
                    const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
                    void* __restrict__ y, int y_dtype) {
     constexpr int NW = kDkWaves, NT = NW * 64;
-    constexpr int KQ = NW / F;
     constexpr int MB = 16 * TF;                         // tokens per block
-    static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "chunked W1A16 shape");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kDkChunkElems + MB * 8];
-    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];   // B operand of steps past the last tile
-    __shared__ f32x4_t red[KQ > 1 ? NW : 1][KQ > 1 ? TF : 1][64];
+    constexpr int CT = NW * TPW;                        // tiles per chunk
+    constexpr int Kc = 128 * CT;                        // rows per chunk
+    constexpr int stride = Kc + 16;                     // per token: 32 bytes apart modulo the banks
+    constexpr int words = MB * (Kc / 32);               // staging jobs per chunk: 32-row words
+    static_assert(MB * Kc <= kDkChunkElems && words <= 2 * NT, "chunk size");   // jobs per thread <= 2
+    __shared__ __attribute__((aligned(16))) uint16_t xs[MB * stride];
+    __shared__ f32x4_t red[NW][FB * TF][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
+    const int g = lane >> 4, r = lane & 15;
     const int m0 = int(blockIdx.y) * MB;                // first token of this block
     const int mb = M - m0 < MB ? M - m0 : MB;           // its tokens
-    const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
+    const int64_t j0 = int64_t(blockIdx.x) * 16 * FB;   // first column
     const int Ki = int(K);
-    const int64_t steps = (TQ + 3) / 4;
-    const int Kc = 512 * SC, stride = Kc + 8;          // token rows 16 bytes apart modulo the banks
-    const int nchunks = int((steps + SC - 1) / SC);
-    const int words = mb * (Kc / 32);                   // <= 2 NT
+    const int nchunks = int((TQ + CT - 1) / CT);
 
-    // the sign tiles of all of this block's groups first (they load during the
-    // first chunk's staging); groups past the last one load zeros
-    u32x4_t w[IT][S];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
-        const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
-        preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
-    }
-    // chunk c's rows of the block's tokens: job J is 32-row word J / mb of
-    // token m0 + J % mb (neighbouring lanes write different tokens' rows);
-    // rows past K load as zeros
-    // (the loads stay unconsumed until the chunk is stored: rows past K are
-    // zeroed then, from the chunk index alone, so the loads overlap the
-    // products of the previous chunk)
-    u32x4_t xv[2][4];
+    // chunk c's rows of the block's tokens (rows past K are zeroed when
+    // stored) and this wave's sign
+    // tiles of it (tile c CT + w + 8p, column j0 + 16f + r; past TQ or N they
+    // read tile 0 of column 0: their activations are zero, their outputs are
+    // never stored)
+    // Job J is the 32-row word t of token m with m % 4 = J % 4 and
+    // t % 4 = (J / 4) % 4, so that the 16-lane groups of a store write 16
+    // different banks (the token stride is 8 dwords modulo 32).
+    const int mq = (mb + 3) / 4;                        // token quads
+    auto job = [&](int J, int& m, int& t) {
+        const int rest = J >> 4;
+        m = 4 * (rest % mq) + (J & 3);
+        t = 4 * (rest / mq) + ((J >> 2) & 3);
+        return m < mb && t < Kc / 32;
+    };
+    u32x4_t xv[2][4], wn[TPW][FB];
     auto load_chunk = [&](int c) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int J = i * NT + tid, m = J % mb, t = J / mb;
+            int m, t;
+            const bool jv = job(i * NT + tid, m, t);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int k = c * Kc + 32 * t + 8 * j;
-                const bool ok = J < words && k < Ki;
+                const bool ok = jv && k < Ki;
                 xv[i][j] = *reinterpret_cast<const u32x4_t*>(x + (ok ? int64_t(m0 + m) * Ki + k : 0));
             }
         }
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+            const int64_t tq = int64_t(c) * CT + wave + NW * p;
+#pragma unroll
+            for (int f = 0; f < FB; ++f) {
+                const int64_t j = j0 + 16 * f + r;
+                const bool ok = tq < TQ && j < N;
+                wn[p][f] = load_tile(P, ok ? tq : 0, N, ok ? j : 0);
+            }
+        }
     };
-    // a word's 32 rows into the decode layout: dword u of chunk u holds rows
-    // u and u + 16 (dword (u % 8) / 2, same half, of pieces u / 8, 2 + u / 8)
     auto store_chunk = [&](int c) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int J = i * NT + tid;
-            if (J >= words) continue;
-            const int m = J % mb, t = J / mb;
+            int m, t;
+            if (!job(i * NT + tid, m, t)) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (c * Kc + 32 * t + 8 * j >= Ki) xv[i][j] = u32x4_t{0u, 0u, 0u, 0u};
+            // dword u of the tile's chunk u (here: 16 bytes apart) holds rows u, u + 16
+            // of the word: dword (u % 8) / 2, same half, of pieces u / 8 and 2 + u / 8
             uint32_t* dst = reinterpret_cast<uint32_t*>(xs + m * stride + (t >> 2) * 128 + (t & 3) * 2);
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
@@ -1332,19 +1347,16 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
         }
     };
     load_chunk(0);
-    uint2 araw[IT][2];                                  // this lane's 4 column scales per group
-#pragma unroll
-    for (int it = 0; it < IT; ++it)
-        alpha4_load(alpha, alpha_f16, (int64_t(blockIdx.x) + int64_t(it) * gridDim.x) * 16 * F + 16 * f + 4 * g, N,
-                    araw[it]);
-    if (tid < 16) reinterpret_cast<u32x4_t*>(xzero)[tid] = u32x4_t{0u, 0u, 0u, 0u};
+    // the reducing wave's 4 column scales (wave q < FB TF finishes fragment q / TF)
+    uint2 araw[2];
+    alpha4_load(alpha, alpha_f16, j0 + 16 * (wave / TF) + 4 * g, N, araw);
 
     constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;
-    f32x4_t acc[IT][TF][2];                             // by u parity: two independent MFMA chains
+    f32x4_t acc[FB][TF][2];                             // by MFMA parity: two chains each
 #pragma unroll
-    for (int it = 0; it < IT; ++it)
+    for (int f = 0; f < FB; ++f)
 #pragma unroll
-        for (int tf = 0; tf < TF; ++tf) acc[it][tf][0] = acc[it][tf][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int tf = 0; tf < TF; ++tf) acc[f][tf][0] = acc[f][tf][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const uint16_t* xrow[TF];                           // lanes past the block's tokens read its token 0
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf) xrow[tf] = xs + (16 * tf + r < mb ? 16 * tf + r : 0) * stride;
@@ -1352,73 +1364,57 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
     for (int c = 0; c < nchunks; ++c) {
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): chunk c is in
         store_chunk(c);
+        u32x4_t w[TPW][FB];
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+            for (int f = 0; f < FB; ++f) w[p][f] = wn[p][f];
         __syncthreads();
         if (c + 1 < nchunks) load_chunk(c + 1);
 #pragma unroll
-        for (int it = 0; it < IT; ++it) {
+        for (int p = 0; p < TPW; ++p) {
+            const int tl = wave + NW * p;                  // tile within the chunk (zero rows past K)
 #pragma unroll
-            for (int i = 0; i < S; ++i) {
-                const int64_t st = kq + int64_t(KQ) * i;
-                if (st < int64_t(c) * SC || st >= int64_t(c + 1) * SC) continue;   // uniform per wave
-                const int64_t tq = st * 4 + g;
-                const bool valid = st < steps && tq < TQ;
-                const int tl = int(tq - int64_t(c) * SC * 4);
-                u32x4_t wv = w[it][i];
-                // keeps the decoded operands inside the chunk loop (hoisted out
-                // of it, all steps' operands would be live at once)
-                asm volatile("" : "+v"(wv));
+            for (int v = 0; v < 4; ++v) {
+                const int u = 4 * v + g;
+                u32x4_t b[TF];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+                for (int tf = 0; tf < TF; ++tf) b[tf] = *reinterpret_cast<const u32x4_t*>(xrow[tf] + tl * 128 + u * 8);
+#pragma unroll
+                for (int f = 0; f < FB; ++f) {
                     u32x4_t a;   // (~(word << (15 - u)) & 0x80008000) | 1.0: signs of rows 32e + u, 32e + u + 16
-                    a.x = __builtin_amdgcn_bitop3_b32(wv.x << (15 - u), 0x80008000u, kOne, 0xAE);
-                    a.y = __builtin_amdgcn_bitop3_b32(wv.y << (15 - u), 0x80008000u, kOne, 0xAE);
-                    a.z = __builtin_amdgcn_bitop3_b32(wv.z << (15 - u), 0x80008000u, kOne, 0xAE);
-                    a.w = __builtin_amdgcn_bitop3_b32(wv.w << (15 - u), 0x80008000u, kOne, 0xAE);
+                    a.x = __builtin_amdgcn_bitop3_b32(w[p][f].x << (15 - u), 0x80008000u, kOne, 0xAE);
+                    a.y = __builtin_amdgcn_bitop3_b32(w[p][f].y << (15 - u), 0x80008000u, kOne, 0xAE);
+                    a.z = __builtin_amdgcn_bitop3_b32(w[p][f].z << (15 - u), 0x80008000u, kOne, 0xAE);
+                    a.w = __builtin_amdgcn_bitop3_b32(w[p][f].w << (15 - u), 0x80008000u, kOne, 0xAE);
 #pragma unroll
-                    for (int tf = 0; tf < TF; ++tf) {
-                        // a step past the column's tiles has zero sign words (all -1):
-                        // it must read zero activations
-                        const u32x4_t* src =
-                            reinterpret_cast<const u32x4_t*>(valid ? xrow[tf] + tl * 128 : xzero);
-                        acc[it][tf][u & 1] = mfma16<kF16>(a, src[u], acc[it][tf][u & 1]);
-                    }
+                    for (int tf = 0; tf < TF; ++tf)
+                        acc[f][tf][v & 1] = mfma16<kF16>(a, b[tf], acc[f][tf][v & 1]);
                 }
             }
         }
         __syncthreads();                                // chunk c's buffer is free again
     }
 
-    // the KQ parts' sums through LDS in a fixed order, then the epilogue
+    // the 8 waves' sums in wave order, by wave q < FB TF for (fragment q / TF,
+    // token fragment q % TF), then the epilogue
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
-        if (grp >= ngroups) break;
-        f32x4_t z[TF];
+    for (int f = 0; f < FB; ++f)
 #pragma unroll
-        for (int tf = 0; tf < TF; ++tf) z[tf] = acc[it][tf][0] + acc[it][tf][1];
-        if constexpr (KQ > 1) {
-            if (it > 0) __syncthreads();                // the previous group's reads are done
+        for (int tf = 0; tf < TF; ++tf) red[wave][f * TF + tf][lane] = acc[f][tf][0] + acc[f][tf][1];
+    __syncthreads();
+    if (wave >= FB * TF) return;
+    const int f = wave / TF, tf = wave % TF;
+    f32x4_t z = red[0][wave][lane];
 #pragma unroll
-            for (int tf = 0; tf < TF; ++tf) red[wave][tf][lane] = z[tf];
-            __syncthreads();
-            if (kq != 0) continue;
+    for (int q = 1; q < NW; ++q) z += red[q][wave][lane];
+    const int m = 16 * tf + r;
+    if (m >= mb) return;
 #pragma unroll
-            for (int q = 1; q < KQ; ++q)
-#pragma unroll
-                for (int tf = 0; tf < TF; ++tf) z[tf] += red[f + F * q][tf][lane];
-        }
-        const int64_t j0 = grp * 16 * F + 16 * f + 4 * g;
-#pragma unroll
-        for (int tf = 0; tf < TF; ++tf) {
-            const int m = 16 * tf + r;
-            if (m >= mb) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t col = j0 + i;
-                if (col >= N) continue;
-                store_y(y, y_dtype, int64_t(m0 + m) * N + col, alpha4_get(araw[it], alpha_f16, i) * z[tf][i]);
-            }
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int64_t col = j0 + 16 * f + 4 * g + i;
+        if (col >= N) continue;
+        store_y(y, y_dtype, int64_t(m0 + m) * N + col, alpha4_get(araw, alpha_f16, i) * z[i]);
     }
 }
 
@@ -1426,81 +1422,24 @@ constexpr int kDkMaxTokens = 64;
 
 bool w1a16_decodek_supported(int64_t M, int64_t K) { return M >= 2 && M <= kDkMaxTokens && K > 0; }
 
-template <bool kF16, int TF, int F, int S>
-static void launch_w1a16_decodek_s(int it, dim3 grid, int SC, const uint16_t* x, int M, int64_t K, int64_t N,
-                                   int64_t TQ, const uint32_t* P, const void* alpha, int alpha_f16, void* y,
-                                   int y_dtype, hipStream_t s) {
-#define BGB_DKX(ITV)                                                                                             \
-    fbi_decodek_kernel<kF16, TF, F, S, ITV><<<grid, kDkWaves * 64, 0, s>>>(x, M, K, N, TQ, SC, P, alpha, alpha_f16, \
-                                                                          y, y_dtype)
-    if constexpr (2 * S <= kD1MaxTiles) {
-        if (it == 2) {
-            BGB_DKX(2);
-            return;
-        }
-    }
-    BGB_DKX(1);
-#undef BGB_DKX
-}
-
-template <bool kF16, int TF, int F>
-static void launch_w1a16_decodek_f(int S, int it, dim3 grid, int SC, const uint16_t* x, int M, int64_t K, int64_t N,
-                                   int64_t TQ, const uint32_t* P, const void* alpha, int alpha_f16, void* y,
-                                   int y_dtype, hipStream_t s) {
-#define BGB_DKS(SV) \
-    launch_w1a16_decodek_s<kF16, TF, F, SV>(it, grid, SC, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
-    if (S == 1) BGB_DKS(1);
-    else if (S == 2) BGB_DKS(2);
-    else if (S == 4) BGB_DKS(4);
-    else BGB_DKS(8);
-#undef BGB_DKS
-}
-
-template <bool kF16, int TF>
+template <bool kF16, int TF, int TPW>
 static hipError_t launch_w1a16_decodek_t(const uint16_t* x, int M, int64_t K, int64_t N, const uint32_t* P,
                                          const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
     constexpr int MB = 16 * TF;
     const int64_t TQ = tiles_per_col(K);
-    const int64_t steps = (TQ + 3) / 4;
     const int64_t frags = (N + 15) / 16;
     const int tblocks = (M + MB - 1) / MB;
-    // chunk of SC steps: MB tokens x 512 SC rows <= kDkChunkElems
-    int SC = kDkChunkElems / (MB * 512);
-    if (SC > steps) SC = int(steps);
-    // fragments per group: at least enough that a fragment's KQ = 8 / F
-    // waves all have a step in every chunk (KQ <= SC), more while the grid
-    // would exceed one block per CU, within the preloaded-tile budget
-    auto steps_per_wave = [&](int f) {
-        const int64_t need = (steps + kDkWaves / f - 1) / (kDkWaves / f);
-        return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
-    };
-    int F = 1;
-    while (F < kDkWaves && kDkWaves / F > SC) F *= 2;
-    while (2 * F <= kDkWaves && steps_per_wave(2 * F) <= kD1MaxTiles &&
-           ((frags + F - 1) / F) * tblocks > kD1MaxGrid)
-        F *= 2;
-    int S = steps_per_wave(F);
-    while (S > kD1MaxTiles && F > 1) {                  // long K: more waves per fragment
-        F /= 2;
-        S = steps_per_wave(F);
-    }
-    if (S > kD1MaxTiles) return hipErrorInvalidValue;
-    const int64_t groups = (frags + F - 1) / F;
-    const int64_t cap = kD1MaxGrid / tblocks > 0 ? kD1MaxGrid / tblocks : 1;
-    int64_t gx = groups < cap ? groups : cap;
-    int it = int((groups + gx - 1) / gx);
-    const int it_max = 2 * S <= kD1MaxTiles ? 2 : 1;
-    if (it > it_max) {
-        it = it_max;
-        gx = (groups + it - 1) / it;
-    }
-    const dim3 grid = dim3(unsigned(gx), unsigned(tblocks), 1u);
-#define BGB_DKF(FV) launch_w1a16_decodek_f<kF16, TF, FV>(S, it, grid, SC, x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, s)
-    if (F == 1) BGB_DKF(1);
-    else if (F == 2) BGB_DKF(2);
-    else if (F == 4) BGB_DKF(4);
-    else BGB_DKF(8);
-#undef BGB_DKF
+    // fragments per block: the most (up to 4, each activation read feeds FB
+    // MFMAs) that still give at least 128 blocks
+    int FB = 4;
+    while (FB > 1 && ((frags + FB - 1) / FB) * tblocks < 128) FB /= 2;
+    const dim3 grid = dim3(unsigned((frags + FB - 1) / FB), unsigned(tblocks), 1u);
+#define BGB_DK(FBV) \
+    fbi_decodek_kernel<kF16, TF, FBV, TPW><<<grid, kDkWaves * 64, 0, s>>>(x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype)
+    if (FB == 4) BGB_DK(4);
+    else if (FB == 2) BGB_DK(2);
+    else BGB_DK(1);
+#undef BGB_DK
     return hipGetLastError();
 }
 
@@ -1509,11 +1448,12 @@ hipError_t launch_w1a16_decodek(const void* x, int x_f16, int64_t M, int64_t K, 
     if (!w1a16_decodek_supported(M, K)) return hipErrorInvalidValue;
     const uint16_t* xx = static_cast<const uint16_t*>(x);
     const int m = int(M);
+    // 16 tokens per block: chunks of 16 tiles (2 per wave); 32: chunks of 8
     if (M <= 16)
-        return x_f16 ? launch_w1a16_decodek_t<true, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
-                     : launch_w1a16_decodek_t<false, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
-    return x_f16 ? launch_w1a16_decodek_t<true, 2>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
-                 : launch_w1a16_decodek_t<false, 2>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+        return x_f16 ? launch_w1a16_decodek_t<true, 1, 2>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
+                     : launch_w1a16_decodek_t<false, 1, 2>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+    return x_f16 ? launch_w1a16_decodek_t<true, 2, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
+                 : launch_w1a16_decodek_t<false, 2, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
 }
 
 hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M, int64_t K, int64_t N,
