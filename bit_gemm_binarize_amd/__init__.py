@@ -20,7 +20,7 @@ from typing import Optional
 __all__ = [
     "load", "lib_path", "packed_bytes", "workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
     "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
-    "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M",
+    "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M", "W1A16_DECODE_MAX_M",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,8 @@ _LIB_PATH = os.path.join(_HERE, "libbgb.so")
 BGB_F32, BGB_F16, BGB_BF16 = 0, 1, 2
 MODE_FBI, MODE_BITNET = 0, 1
 OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR = 0, 1, 2, 3
-GEMV_MAX_M = 32          # M <= 32: decode kernels; above: the MFMA GEMM
+GEMV_MAX_M = 32          # BitLinear: M <= 32 runs the decode kernels, above: the MFMA GEMM
+W1A16_DECODE_MAX_M = 64  # FBI-linear: M <= 64 runs the decode kernels, above: the MFMA GEMM
 
 EXPORTS = ("bgb_packed_bytes", "bgb_workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
            "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bgb_status_string",

@@ -9,7 +9,8 @@
 namespace bgb {
 
 constexpr int kWords4 = 4;             // words per 16-byte column tile (128 rows)
-constexpr int kGemvMaxM = 32;          // M <= 32 -> decode (streaming) kernels, above: MFMA GEMM
+constexpr int kGemvMaxM = 32;          // W1A8: M <= 32 -> decode (streaming) kernels, above: MFMA GEMM
+constexpr int kW1A16DecodeMaxM = 64;   // W1A16: M <= 64 -> decode kernels, above: MFMA GEMM
 constexpr int kSmallPrologueM = 16;    // M <= 16 -> single-block LN + quant prologue
 constexpr int kMaxK = 524288;
 
@@ -49,21 +50,13 @@ struct GemmPlan {
 GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8);
 size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8);   // [splits][M][N] x 4 bytes, or 0
 
-struct FbiLinearWs {        // permuted activations (+ per-chunk type sums when decoding,
-    size_t xp, xpart, part, total;   //  + split-K partial sums for the GEMM)
+struct FbiLinearWs {        // GEMM only: interleaved activations, then split-K partial sums
+    size_t part, total;
     static FbiLinearWs make(int64_t M, int64_t K, int64_t N) {
         FbiLinearWs w{};
-        if (M > kGemvMaxM) {    // GEMM: interleaved activations, then the partials
-            w.xp = w.xpart = 0;
-            w.part = align256(size_t(M) * size_t(padded_k(K)) * 2);
-            w.total = w.part + gemm_partial_bytes(M, K, N, false);
-            return w;
-        }
-        w.part = 0;
-        const size_t chunks = size_t((padded_k(K) + 1023) / 1024);
-        w.xp = 0;
-        w.xpart = align256(size_t(M) * size_t(padded_k(K)) * 2);
-        w.total = w.xpart + align256(size_t(M) * chunks * 4 * sizeof(double));
+        if (M <= kW1A16DecodeMaxM) return w;   // the decode kernels stage in LDS
+        w.part = align256(size_t(M) * size_t(padded_k(K)) * 2);
+        w.total = w.part + gemm_partial_bytes(M, K, N, false);
         return w;
     }
 };
@@ -94,13 +87,6 @@ hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, doub
                            float* stats, float* gamma_ws, int8_t* xq_opt, float* gamma_opt,
                            hipStream_t s);
 
-hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp,
-                             double* xpart, hipStream_t s);
-
-hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M,
-                             int64_t K, int64_t N, const uint32_t* P, const void* alpha,
-                             int alpha_f16, void* y, int y_dtype, hipStream_t s);
-
 // GEMM activations: xi[m][Kp], element pairs (row i, row i+16) of each 32-row group
 hipError_t launch_w1a16_interleave(const void* x, int64_t M, int64_t K, uint16_t* xi, hipStream_t s);
 
@@ -120,7 +106,7 @@ hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, 
 bool w1a16_decode1_supported(int64_t K);
 // 2 <= M <= 16 tokens staged in LDS by every block (M (Kp + 8) 2 bytes <= 140 KB)
 bool w1a16_decodem_supported(int64_t M, int64_t K);
-// 2 <= M <= 64 tokens, K staged in chunks (any K)
+// 1 <= M <= 64 tokens, K staged in chunks (any K)
 bool w1a16_decodek_supported(int64_t M, int64_t K);
 hipError_t launch_w1a16_decodek(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);

@@ -631,126 +631,6 @@ BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2,
     return 2.0f * sb - (((X0 + X1) + X2) + X3);
 }
 
-// Prep for the multi-token decode: xp[m][x_pos(k)] = x[m][k] (0 beyond K), and
-// per 1024-row chunk c the fp64 partial sums xpart[m][c][T] of x over k % 4 == T.
-// Grid (chunks, M); each thread moves 4 consecutive rows.
-__global__ void __launch_bounds__(256)
-w1a16_prep_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t Kp, int is_f16, uint16_t* __restrict__ xp,
-                  double* __restrict__ xpart) {
-    __shared__ double dX[4][4];
-    const int64_t m = blockIdx.y;
-    const int64_t k = int64_t(blockIdx.x) * 1024 + int64_t(threadIdx.x) * 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    double xs4[4] = {0.0, 0.0, 0.0, 0.0};
-    if (k < Kp) {
-        uint2 t = {0u, 0u};
-        if (k < K) t = *reinterpret_cast<const uint2*>(x + m * K + k);
-        const uint16_t e[4] = {uint16_t(t.x & 0xffffu), uint16_t(t.x >> 16), uint16_t(t.y & 0xffffu),
-                               uint16_t(t.y >> 16)};
-        uint16_t* out = xp + m * Kp;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            out[x_pos(k + c)] = e[c];
-            xs4[c] = double(is_f16 ? f16_to_f32(e[c]) : bf16_to_f32(e[c]));
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const double t = wave_sum63(xs4[c]);
-        if (lane == 63) dX[wave][c] = t;
-    }
-    __syncthreads();
-    if (threadIdx.x < 4) {
-        const int c = threadIdx.x;
-        xpart[(m * gridDim.x + blockIdx.x) * 4 + c] = ((dX[0][c] + dX[1][c]) + dX[2][c]) + dX[3][c];
-    }
-}
-
-int w1a16_prep_chunks(int64_t K) { return int((padded_k(K) + 1023) / 1024); }
-
-hipError_t launch_w1a16_prep(const void* x, int is_f16, int64_t M, int64_t K, uint16_t* xp, double* xpart,
-                             hipStream_t s) {
-    const dim3 grid(unsigned(w1a16_prep_chunks(K)), unsigned(M));
-    w1a16_prep_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), K, padded_k(K), is_f16, xp, xpart);
-    return hipGetLastError();
-}
-
-// General decode: permuted activations from the prep kernel, M <= 16 * TF.
-// A block of kGenWaves waves owns 16 * CF columns; wave w takes steps w,
-// w + 8, ... of all CF column fragments, so each activation fragment it loads
-// (from L2) feeds CF x 16 MFMAs. Each wave folds its four type accumulators
-// into z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3 (powers of two), so
-// sum_k b x = z - (8 X_0 + 4 X_1 + 2 X_2 + X_3) is applied once at the end.
-template <bool kF16, int TF, int CF, int GS>
-__global__ void __launch_bounds__(kGenWaves * 64)
-gemv_w1a16_kernel(const uint16_t* __restrict__ xp, const double* __restrict__ xpart, int nchunk, int M, int64_t N,
-                  int64_t TQ, const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
-                  void* __restrict__ y, int y_dtype) {
-    __shared__ f32x4_t red[kGenWaves][CF * TF][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, r = lane & 15;
-    const int64_t j0 = int64_t(blockIdx.x) * 16 * CF;
-    const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
-    f32x4_t acc[CF * TF][4];
-#pragma unroll
-    for (int q = 0; q < CF * TF; ++q)
-#pragma unroll
-        for (int T = 0; T < 4; ++T) acc[q][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int64_t base = wave; base < steps; base += kGenWaves * GS) {
-        u32x4_t w[CF][GS];
-#pragma unroll
-        for (int cf = 0; cf < CF; ++cf) preload<GS>(w[cf], P, base, kGenWaves, steps, TQ, N, j0 + 16 * cf + r, g);
-#pragma unroll
-        for (int i = 0; i < GS; ++i) {
-            const int64_t st = base + kGenWaves * i;
-            const int64_t tq = st * 4 + g;
-            const bool tv = st < steps && tq < TQ;
-#pragma unroll
-            for (int tf = 0; tf < TF; ++tf) {
-                const int m = 16 * tf + r;
-                const bool bv = tv && m < M;
-                const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xp + int64_t(bv ? m : 0) * Kp + (bv ? tq : 0) * 128);
-                u32x4_t bb[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) bb[u] = ld16_or0(src + u, bv);
-                __builtin_amdgcn_sched_barrier(0);   // all 16 operand loads in flight before the MFMAs
-#pragma unroll
-                for (int cf = 0; cf < CF; ++cf) {
-                    auto bsrc = [&](int u, int) -> u32x4_t { return bb[u]; };
-                    w1a16_step<kF16, 1>(w[cf][i], bsrc, &acc[cf * TF + tf]);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < CF * TF; ++q)
-        red[wave][q][lane] = ((8.0f * acc[q][0] + 4.0f * acc[q][1]) + 2.0f * acc[q][2]) + 2.0f * acc[q][3];
-    __syncthreads();
-    // wave v < CF * TF finishes (column fragment, token fragment) pair v
-    for (int q = wave; q < CF * TF; q += kGenWaves) {
-        const int cf = q / TF, tf = q % TF;
-        const int mm = 16 * tf + r;
-        if (mm >= M) continue;
-        f32x4_t z = red[0][q][lane];
-#pragma unroll
-        for (int wv = 1; wv < kGenWaves; ++wv) z += red[wv][q][lane];
-        double X[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int c = 0; c < nchunk; ++c)
-#pragma unroll
-            for (int T = 0; T < 4; ++T) X[T] += xpart[(int64_t(mm) * nchunk + c) * 4 + T];
-        const float X0 = float(X[0]), X1 = float(X[1]), X2 = float(X[2]), X3 = float(X[3]);
-        const float corr = ((8.0f * X0 + 4.0f * X1) + 2.0f * X2) + X3;
-        const float xall = ((X0 + X1) + X2) + X3;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t col = j0 + 16 * cf + 4 * g + i;
-            if (col >= N) continue;
-            const float sres = 2.0f * (z[i] - corr) - xall;
-            store_y(y, y_dtype, int64_t(mm) * N + col, load_alpha(alpha, alpha_f16, col) * sres);
-        }
-    }
-}
-
 // Single token, activation staging fused: the block permutes x into LDS and
 // computes the four X_T itself, once, then takes up to IT column groups
 // (blockIdx.x + i * gridDim.x) of F 16-column fragments, as the W1A8 kernel.
@@ -1420,7 +1300,7 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
 
 constexpr int kDkMaxTokens = 64;
 
-bool w1a16_decodek_supported(int64_t M, int64_t K) { return M >= 2 && M <= kDkMaxTokens && K > 0; }
+bool w1a16_decodek_supported(int64_t M, int64_t K) { return M >= 1 && M <= kDkMaxTokens && K > 0; }
 
 template <bool kF16, int TF, int TPW>
 static hipError_t launch_w1a16_decodek_t(const uint16_t* x, int M, int64_t K, int64_t N, const uint32_t* P,
@@ -1454,37 +1334,6 @@ hipError_t launch_w1a16_decodek(const void* x, int x_f16, int64_t M, int64_t K, 
                      : launch_w1a16_decodek_t<false, 1, 2>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
     return x_f16 ? launch_w1a16_decodek_t<true, 2, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
                  : launch_w1a16_decodek_t<false, 2, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
-}
-
-hipError_t launch_w1a16_gemv(const uint16_t* xp, const double* xpart, int x_f16, int64_t M, int64_t K, int64_t N,
-                             const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
-                             hipStream_t s) {
-    const int64_t TQ = tiles_per_col(K);
-    const int tf = int((M + 15) / 16);
-    const int nch = w1a16_prep_chunks(K);
-    constexpr unsigned nt = kGenWaves * 64;
-    const int gs = gen_steps(TQ);
-    // column fragments per block: as many (up to 4 for one token fragment, 1
-    // for two: registers) as keep at least 192 blocks streaming
-    const int cf = tf == 1 ? (N >= 4 * 16 * 192 ? 4 : (N >= 2 * 16 * 192 ? 2 : 1)) : 1;
-    const unsigned grid = unsigned((N + 16 * cf - 1) / (16 * cf));
-#define BGB_G16(F16, TFV, CFV, GSV)                                                                           \
-    gemv_w1a16_kernel<F16, TFV, CFV, GSV><<<grid, nt, 0, s>>>(xp, xpart, nch, int(M), N, TQ, P, alpha,       \
-                                                              alpha_f16, y, y_dtype)
-#define BGB_G16S(F16, TFV, CFV) \
-    if (gs == 1) BGB_G16(F16, TFV, CFV, 1); else if (gs == 2) BGB_G16(F16, TFV, CFV, 2); else BGB_G16(F16, TFV, CFV, 4);
-    if (x_f16) {
-        if (tf == 1) {
-            if (cf == 4) { BGB_G16S(true, 1, 4) } else if (cf == 2) { BGB_G16S(true, 1, 2) } else { BGB_G16S(true, 1, 1) }
-        } else { BGB_G16S(true, 2, 1) }
-    } else {
-        if (tf == 1) {
-            if (cf == 4) { BGB_G16S(false, 1, 4) } else if (cf == 2) { BGB_G16S(false, 1, 2) } else { BGB_G16S(false, 1, 1) }
-        } else { BGB_G16S(false, 2, 1) }
-    }
-#undef BGB_G16S
-#undef BGB_G16
-    return hipGetLastError();
 }
 
 }  // namespace bgb

@@ -122,12 +122,12 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
  * accepted). y: [M][N] in y_dtype (F32, BF16 or F16; 16-bit outputs are
  * rounded to nearest even). Products of +-1 and x are exact; sums use fp32
  * accumulation on the matrix cores; alpha is applied once to the fp32 sum.
- * M <= 32 runs the memory-bound decode kernels, M > 32 the MFMA GEMM.
- * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes. The GEMM and the
- * two-pass decode keep a re-ordered copy of x there (M x Kp x 2 bytes, Kp = K
- * rounded up to 128, plus fp64 partial sums when decoding); one token (Kp <=
- * 16384), and 2..16 tokens with M x (Kp + 8) x 2 <= 140 KB, are staged on
- * chip by a single launch and leave ws untouched.
+ * M <= 64 runs the decode kernels (one launch each, activations staged in
+ * LDS), M > 64 the MFMA GEMM.
+ * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes: 0 for M <= 64
+ * (ws is then neither read nor written and may be NULL); above that the GEMM
+ * keeps a re-ordered copy of x there (M x Kp x 2 bytes, Kp = K rounded up to
+ * 128) plus, for shapes whose K range it splits, fp32 partial sums.
  * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP.
  */
 int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,

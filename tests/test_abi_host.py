@@ -60,8 +60,9 @@ def test_sizes(lib):
     small = bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096)
     assert small >= 65 * 4096 * 2 and (small - 65 * 4096 * 2) % (65 * 4096 * 4) == 0
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 11008) == bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 0)
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 64, 4096, 4096) >= 64 * 4096 * 2
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 16, 4096, 4096) >= 16 * 4096 * 2
+    # decode kernels (M <= 64) stage the activations on chip: no workspace
+    for M, K in ((1, 4096), (1, 20000), (16, 4096), (64, 11008)):
+        assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, 4096) == 0
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 1, 4096, 11008) >= 4096
     assert bgb.workspace_bytes(99, 1, 32, 32) == 0
     assert lib.bgb_version().decode().startswith("bgb")
@@ -102,8 +103,8 @@ def test_fbi_linear_validation(lib):
     assert call_fbi(lib, ydt=7) == UNSUP
     assert call_fbi(lib, x=None) == BAD
     assert call_fbi(lib, y=A + 2) == BAD
-    assert call_fbi(lib, wsb=0) == BAD                 # decode path needs a workspace
-    assert call_fbi(lib, M=100, wsb=100 * 128 * 2 - 1) == BAD   # so does the GEMM path
+    assert call_fbi(lib, M=100, wsb=100 * 128 * 2 - 1) == BAD   # the GEMM path needs a workspace
+    assert call_fbi(lib, M=100, ws=None) == BAD
     assert call_fbi(lib, M=1 << 25) == BAD
     assert call_fbi(lib, M=0) == 0 and call_fbi(lib, N=0) == 0
 

@@ -1,4 +1,4 @@
-"""GPU parity: fbi_linear_w1a16 (decode kernels for M <= 32, MFMA GEMM above)
+"""GPU parity: fbi_linear_w1a16 (decode kernels for M <= 64, MFMA GEMM above)
 against the fp64 oracle, plus exactness probes that pin the bit layout."""
 import numpy as np
 import pytest
@@ -30,9 +30,9 @@ def _run(bgb, orc, W, xb, x_kind, y_kind, adt="f32"):
 
 CASES = [
     # (M, K, N) covering every dispatch path: single-token fused decode (M = 1,
-    # K <= 16384), single token beyond the fused size, 2..16 tokens staged in
-    # LDS, decode with 1..2 token fragments after a prep pass (M <= 32), and the
-    # MFMA GEMM (M > 32, split-K plans for small M x N); ragged N and K tails.
+    # K <= 16384), single token beyond the fused size (K staged in chunks),
+    # 2..16 tokens staged whole in LDS, 2..64 tokens staged in chunks, and the
+    # MFMA GEMM (M > 64, split-K plans for small M x N); ragged N and K tails.
     (1, 768, 768), (1, 11008, 100), (1, 16416, 40), (8, 768, 768), (3, 96, 65), (16, 160, 300),
     (1, 16384, 4000), (1, 16384, 8200), (1, 11008, 4096),
     # 2..16 tokens staged in LDS by every block (one group per block, two,
