@@ -94,7 +94,8 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
     if (bgb::w1a16_decodem_supported(M, K))
         return finish(bgb::launch_w1a16_decodem(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
     if (M <= bgb::kW1A16DecodeMaxM)
-        return finish(bgb::launch_w1a16_decodek(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt, s));
+        return finish(bgb::launch_w1a16_decodek(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt,
+                                                static_cast<float*>(ws), s));
     uint16_t* xi = reinterpret_cast<uint16_t*>(carve(ws, 0));
     hipError_t e = bgb::launch_w1a16_interleave(x, M, K, xi, s);
     if (e != hipSuccess) return finish(e);

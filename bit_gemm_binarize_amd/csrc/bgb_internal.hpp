@@ -50,11 +50,26 @@ struct GemmPlan {
 GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8);
 size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8);   // [splits][M][N] x 4 bytes, or 0
 
-struct FbiLinearWs {        // GEMM only: interleaved activations, then split-K partial sums
+// Chunked W1A16 decode plan (a pure function of the shape): tokens per block
+// 16 tf, tiles per wave and chunk tpw, fragments per block fb, K splits (each
+// split takes cps chunks; splits > 1 store raw sums, then a reduce pass).
+struct DecodekPlan {
+    int tf, tpw, fb, splits, cps, nchunks;
+};
+DecodekPlan decodek_plan(int64_t M, int64_t K, int64_t N);
+// Which W1A16 decode kernel serves M <= kW1A16DecodeMaxM, and its workspace
+// (raw split sums, [splits][M][N] fp32; 0 when nothing is split).
+size_t w1a16_decode_ws_bytes(int64_t M, int64_t K, int64_t N);
+
+struct FbiLinearWs {        // decode: split-K sums (if any); GEMM: interleaved activations, then split-K sums
     size_t part, total;
     static FbiLinearWs make(int64_t M, int64_t K, int64_t N) {
         FbiLinearWs w{};
-        if (M <= kW1A16DecodeMaxM) return w;   // the decode kernels stage in LDS
+        if (M <= kW1A16DecodeMaxM) {
+            w.part = 0;
+            w.total = w1a16_decode_ws_bytes(M, K, N);
+            return w;
+        }
         w.part = align256(size_t(M) * size_t(padded_k(K)) * 2);
         w.total = w.part + gemm_partial_bytes(M, K, N, false);
         return w;
@@ -109,7 +124,11 @@ bool w1a16_decodem_supported(int64_t M, int64_t K);
 // 1 <= M <= 64 tokens, K staged in chunks (any K)
 bool w1a16_decodek_supported(int64_t M, int64_t K);
 hipError_t launch_w1a16_decodek(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
-                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, float* part,
+                                hipStream_t s);
+// y[m][j] = alpha_j * sum_z part[z][m][j], z in order (gemm.hip)
+hipError_t launch_w1a16_splitk_reduce(const float* part, int splits, int64_t M, int64_t N, const void* alpha,
+                                      int alpha_f16, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,

@@ -494,6 +494,21 @@ static hipError_t launch_gemm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_w1a16_splitk_reduce(const float* part, int splits, int64_t M, int64_t N, const void* alpha,
+                                      int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+    GemmArgs a{};
+    a.M = M;
+    a.N = N;
+    a.alpha = alpha;
+    a.alpha_f16 = alpha_f16;
+    a.y = y;
+    a.y_dtype = y_dtype;
+    a.part = const_cast<float*>(part);
+    const int64_t n = M * ((N + 3) / 4);
+    splitk_reduce_kernel<false><<<unsigned((n + 255) / 256), 256, 0, s>>>(a, splits);
+    return hipGetLastError();
+}
+
 hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
                              const void* alpha, int alpha_f16, void* y, int y_dtype, void* part, hipStream_t s) {
     const GemmPlan p = gemm_plan(M, K, N, false);

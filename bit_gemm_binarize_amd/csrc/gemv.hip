@@ -1151,7 +1151,7 @@ template <bool kF16, int TF, int FB, int TPW>
 __global__ void __launch_bounds__(kDkWaves * 64)
 fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
                    const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
-                   void* __restrict__ y, int y_dtype) {
+                   void* __restrict__ y, int y_dtype, int cps, float* __restrict__ part) {
     constexpr int NW = kDkWaves, NT = NW * 64;
     constexpr int MB = 16 * TF;                         // tokens per block
     constexpr int CT = NW * TPW;                        // tiles per chunk
@@ -1168,6 +1168,9 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
     const int64_t j0 = int64_t(blockIdx.x) * 16 * FB;   // first column
     const int Ki = int(K);
     const int nchunks = int((TQ + CT - 1) / CT);
+    // this block's chunks: split z = blockIdx.z takes [c0, c1)
+    const int c0 = int(blockIdx.z) * cps;
+    const int c1 = c0 + cps < nchunks ? c0 + cps : nchunks;
 
     // chunk c's rows of the block's tokens (rows past K are zeroed when
     // stored) and this wave's sign
@@ -1226,7 +1229,7 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
             }
         }
     };
-    load_chunk(0);
+    load_chunk(c0);
     // the reducing wave's 4 column scales (wave q < FB TF finishes fragment q / TF)
     uint2 araw[2];
     alpha4_load(alpha, alpha_f16, j0 + 16 * (wave / TF) + 4 * g, N, araw);
@@ -1241,7 +1244,7 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf) xrow[tf] = xs + (16 * tf + r < mb ? 16 * tf + r : 0) * stride;
 
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = c0; c < c1; ++c) {
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): chunk c is in
         store_chunk(c);
         u32x4_t w[TPW][FB];
@@ -1250,7 +1253,7 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
 #pragma unroll
             for (int f = 0; f < FB; ++f) w[p][f] = wn[p][f];
         __syncthreads();
-        if (c + 1 < nchunks) load_chunk(c + 1);
+        if (c + 1 < c1) load_chunk(c + 1);
 #pragma unroll
         for (int p = 0; p < TPW; ++p) {
             const int tl = wave + NW * p;                  // tile within the chunk (zero rows past K)
@@ -1290,6 +1293,15 @@ fbi_decodek_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
     for (int q = 1; q < NW; ++q) z += red[q][wave][lane];
     const int m = 16 * tf + r;
     if (m >= mb) return;
+    if (part) {                                         // raw sums of split z, [z][M][N]
+        float* dst = part + (int64_t(blockIdx.z) * M + m0 + m) * N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t col = j0 + 16 * f + 4 * g + i;
+            if (col < N) dst[col] = z[i];
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t col = j0 + 16 * f + 4 * g + i;
@@ -1302,38 +1314,94 @@ constexpr int kDkMaxTokens = 64;
 
 bool w1a16_decodek_supported(int64_t M, int64_t K) { return M >= 1 && M <= kDkMaxTokens && K > 0; }
 
+// Launch plan. Measured on the chunked kernel: about 3.6 us of fixed cost
+// (launch, first loads, epilogue) plus about 2.4 us per chunk a block stages,
+// at up to one block per CU; a split adds the reduce pass (a launch plus its
+// traffic). Splits are chosen to cut the chunks per block while the grid
+// stays within one block per CU; more fragments per block (each activation
+// read feeding more MFMAs) are preferred at equal cost.
+namespace {
+constexpr double kDkFixedUs = 3.6, kDkChunkUs = 2.4, kDkReduceUs = 2.5, kDkReduceBytesPerUs = 4.0e6;
+constexpr int kDkMaxBlocks = 256;
+}  // namespace
+
+DecodekPlan decodek_plan(int64_t M, int64_t K, int64_t N) {
+    DecodekPlan p{};
+    p.tf = M <= 16 ? 1 : 2;                  // 16 tokens per block: chunks of 16 tiles (2 per wave); 32: of 8
+    p.tpw = p.tf == 1 ? 2 : 1;
+    const int64_t TQ = tiles_per_col(K);
+    const int CT = kDkWaves * p.tpw;
+    p.nchunks = int((TQ + CT - 1) / CT);
+    const int64_t frags = (N + 15) / 16;
+    const int64_t tblocks = (M + 16 * p.tf - 1) / (16 * p.tf);
+    double best = 1e300;
+    for (int fb : {4, 2, 1}) {
+        const int64_t cb = (frags + fb - 1) / fb;
+        for (int S = 1; S <= p.nchunks; ++S) {
+            const int cps = (p.nchunks + S - 1) / S;
+            const int splits = (p.nchunks + cps - 1) / cps;
+            if (splits != S) continue;                       // same split count as a smaller S
+            const int64_t blocks = cb * tblocks * splits;
+            const double rounds = double((blocks + kDkMaxBlocks - 1) / kDkMaxBlocks);
+            double t = kDkFixedUs + rounds * cps * kDkChunkUs;
+            if (splits > 1) t += kDkReduceUs + double(splits + 1) * double(M) * double(N) * 4.0 / kDkReduceBytesPerUs;
+            if (blocks < 128 && fb > 1) t += blocks < 64 ? 1.0 : 0.3;   // few CUs streaming the signs
+            if (t < best - 1e-9) {
+                best = t;
+                p.fb = fb;
+                p.splits = splits;
+                p.cps = cps;
+            }
+        }
+    }
+    return p;
+}
+
+size_t w1a16_decode_ws_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || M > kW1A16DecodeMaxM || N < 1) return 0;
+    if ((M == 1 && w1a16_decode1_supported(K)) || w1a16_decodem_supported(M, K)) return 0;
+    const DecodekPlan p = decodek_plan(M, K, N);
+    return p.splits > 1 ? align256(size_t(p.splits) * size_t(M) * size_t(N) * 4) : 0;
+}
+
 template <bool kF16, int TF, int TPW>
-static hipError_t launch_w1a16_decodek_t(const uint16_t* x, int M, int64_t K, int64_t N, const uint32_t* P,
-                                         const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+static hipError_t launch_w1a16_decodek_t(const DecodekPlan& p, const uint16_t* x, int M, int64_t K, int64_t N,
+                                         const uint32_t* P, const void* alpha, int alpha_f16, void* y, int y_dtype,
+                                         float* part, hipStream_t s) {
     constexpr int MB = 16 * TF;
     const int64_t TQ = tiles_per_col(K);
     const int64_t frags = (N + 15) / 16;
     const int tblocks = (M + MB - 1) / MB;
-    // fragments per block: the most (up to 4, each activation read feeds FB
-    // MFMAs) that still give at least 128 blocks
-    int FB = 4;
-    while (FB > 1 && ((frags + FB - 1) / FB) * tblocks < 128) FB /= 2;
-    const dim3 grid = dim3(unsigned((frags + FB - 1) / FB), unsigned(tblocks), 1u);
-#define BGB_DK(FBV) \
-    fbi_decodek_kernel<kF16, TF, FBV, TPW><<<grid, kDkWaves * 64, 0, s>>>(x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype)
-    if (FB == 4) BGB_DK(4);
-    else if (FB == 2) BGB_DK(2);
+    const dim3 grid = dim3(unsigned((frags + p.fb - 1) / p.fb), unsigned(tblocks), unsigned(p.splits));
+    float* pt = p.splits > 1 ? part : nullptr;
+#define BGB_DK(FBV)                                                                                              \
+    fbi_decodek_kernel<kF16, TF, FBV, TPW><<<grid, kDkWaves * 64, 0, s>>>(x, M, K, N, TQ, P, alpha, alpha_f16, y, \
+                                                                           y_dtype, p.cps, pt)
+    if (p.fb == 4) BGB_DK(4);
+    else if (p.fb == 2) BGB_DK(2);
     else BGB_DK(1);
 #undef BGB_DK
+    if (p.splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_w1a16_splitk_reduce(part, p.splits, M, N, alpha, alpha_f16, y, y_dtype, s);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_w1a16_decodek(const void* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
-                                const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s) {
+                                const void* alpha, int alpha_f16, void* y, int y_dtype, float* part,
+                                hipStream_t s) {
     if (!w1a16_decodek_supported(M, K)) return hipErrorInvalidValue;
+    const DecodekPlan p = decodek_plan(M, K, N);
+    if (p.splits > 1 && !part) return hipErrorInvalidValue;
     const uint16_t* xx = static_cast<const uint16_t*>(x);
     const int m = int(M);
-    // 16 tokens per block: chunks of 16 tiles (2 per wave); 32: chunks of 8
-    if (M <= 16)
-        return x_f16 ? launch_w1a16_decodek_t<true, 1, 2>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
-                     : launch_w1a16_decodek_t<false, 1, 2>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
-    return x_f16 ? launch_w1a16_decodek_t<true, 2, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
-                 : launch_w1a16_decodek_t<false, 2, 1>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+    if (p.tf == 1)
+        return x_f16 ? launch_w1a16_decodek_t<true, 1, 2>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s)
+                     : launch_w1a16_decodek_t<false, 1, 2>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s);
+    return x_f16 ? launch_w1a16_decodek_t<true, 2, 1>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s)
+                 : launch_w1a16_decodek_t<false, 2, 1>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s);
 }
 
 }  // namespace bgb

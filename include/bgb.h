@@ -122,12 +122,16 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
  * accepted). y: [M][N] in y_dtype (F32, BF16 or F16; 16-bit outputs are
  * rounded to nearest even). Products of +-1 and x are exact; sums use fp32
  * accumulation on the matrix cores; alpha is applied once to the fp32 sum.
- * M <= 64 runs the decode kernels (one launch each, activations staged in
- * LDS), M > 64 the MFMA GEMM.
- * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes: 0 for M <= 64
- * (ws is then neither read nor written and may be NULL); above that the GEMM
- * keeps a re-ordered copy of x there (M x Kp x 2 bytes, Kp = K rounded up to
- * 128) plus, for shapes whose K range it splits, fp32 partial sums.
+ * M <= 64 runs the decode kernels (activations staged in LDS), M > 64 the
+ * MFMA GEMM.
+ * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes. When that is 0
+ * (one token with K <= 16384, up to 16 tokens whose activations fit on chip
+ * whole, and decode shapes whose K range is not split) ws is neither read nor
+ * written and may be NULL. Decode shapes whose K range is split over several
+ * blocks keep fp32 partial sums there ([splits][M][N]), added in a fixed
+ * order by a second launch; the GEMM keeps a re-ordered copy of x there
+ * (M x Kp x 2 bytes, Kp = K rounded up to 128) plus, for shapes whose K range
+ * it splits, fp32 partial sums.
  * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP.
  */
 int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,

@@ -60,9 +60,13 @@ def test_sizes(lib):
     small = bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096)
     assert small >= 65 * 4096 * 2 and (small - 65 * 4096 * 2) % (65 * 4096 * 4) == 0
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 11008) == bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 0)
-    # decode kernels (M <= 64) stage the activations on chip: no workspace
-    for M, K in ((1, 4096), (1, 20000), (16, 4096), (64, 11008)):
+    # decode kernels (M <= 64) stage the activations on chip: no workspace,
+    # except fp32 sums [splits][M][N] where the K range is split (long K)
+    for M, K in ((1, 4096), (1, 16384), (16, 4096), (4, 11008), (64, 2048)):
         assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, 4096) == 0
+    for M, K, N in ((1, 20000, 4096), (16, 11008, 4096), (64, 5632, 2048), (20, 16416, 70)):
+        w = bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, N)
+        assert w >= 2 * M * N * 4 and w - (w // (M * N * 4)) * M * N * 4 < 256
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 1, 4096, 11008) >= 4096
     assert bgb.workspace_bytes(99, 1, 32, 32) == 0
     assert lib.bgb_version().decode().startswith("bgb")

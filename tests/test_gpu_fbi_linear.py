@@ -40,7 +40,8 @@ CASES = [
     (2, 16384, 300), (4, 11008, 4096), (5, 11008, 100), (6, 11008, 70), (12, 2048, 1000), (16, 4096, 4100),
     (16, 4096, 12288), (2, 1024, 40000),
     # 2..64 tokens with K staged in chunks: 16 or 32 tokens per block, one or
-    # more token blocks, chunk tails, K beyond the fused single-token size
+    # more token blocks, chunk tails, K beyond the fused single-token size, K
+    # split over 3..17 blocks per column block (raw sums, then the reduce pass)
     (16, 11008, 4096), (24, 1024, 520), (33, 5632, 300), (64, 2048, 6144), (48, 352, 100), (20, 16416, 70),
     (5, 4096, 33), (17, 96, 65), (40, 768, 260), (64, 2048, 520), (65, 256, 300), (130, 256, 300),
     (200, 352, 513),
@@ -60,7 +61,7 @@ def test_fbi_linear_bf16_parity(bgb_gpu, orc, M, K, N, y_kind):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 768, 768), (7, 160, 300), (16, 4096, 64), (40, 768, 260), (64, 96, 65),
-                                   (129, 96, 65)])
+                                   (24, 11008, 200), (129, 96, 65)])
 @pytest.mark.parametrize("y_kind", ["f32", "f16"])
 def test_fbi_linear_f16_parity(bgb_gpu, orc, M, K, N, y_kind):
     say(f"fbi_linear f16 M={M} K={K} N={N} y={y_kind}")
@@ -71,7 +72,7 @@ def test_fbi_linear_f16_parity(bgb_gpu, orc, M, K, N, y_kind):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 96, 65), (1, 4096, 300), (5, 1024, 300), (16, 4096, 70), (40, 1024, 300),
-                                   (64, 512, 33), (131, 96, 257)])
+                                   (64, 512, 33), (20, 16416, 70), (131, 96, 257)])
 @pytest.mark.parametrize("x_kind", ["bf16", "f16"])
 def test_fbi_linear_integer_activations_bit_exact(bgb_gpu, orc, M, K, N, x_kind):
     """Integer-valued activations (|x| <= 16) make every partial sum exact in

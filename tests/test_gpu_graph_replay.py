@@ -11,10 +11,10 @@ from gpu_util import dev_bits16, dev_f32, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M", [1, 16, 40])
-def test_graph_replays_match_eager(bgb_gpu, M):
-    say(f"graph replay M={M}")
-    K, N = 1024, 700
+@pytest.mark.parametrize("M,K", [(1, 1024), (16, 1024), (40, 1024), (24, 8192)])   # the last: K split
+def test_graph_replays_match_eager(bgb_gpu, M, K):
+    say(f"graph replay M={M} K={K}")
+    N = 700
     W = dev_f32(syn.normal_f32(31, 0, (K, N), mean=0.001, std=0.02))
     Pf, alpha = bgb_gpu.binarize_pack(W, bgb_gpu.MODE_FBI)
     Pb, beta, _ = bgb_gpu.binarize_pack(W, bgb_gpu.MODE_BITNET)
