@@ -54,7 +54,7 @@ def _load():
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
     lib.oracle_fbi_linear.argtypes = [P, ctypes.c_int, I64, I64, P, I64, P, P]
     lib.oracle_ln_absmax_quant.argtypes = [P, I64, I64, ctypes.c_double, ctypes.c_int,
-                                           ctypes.c_float, P, P, P, P]
+                                           ctypes.c_float, ctypes.c_int, ctypes.c_int, P, P, P, P]
     lib.oracle_bitlinear_acc.argtypes = [P, I64, I64, P, I64, ctypes.c_float, P]
     lib.oracle_bitlinear_out.argtypes = [P, I64, I64, ctypes.c_float, ctypes.c_float,
                                          ctypes.c_int, P]
@@ -157,18 +157,23 @@ def fbi_linear(x_bits: np.ndarray, W: np.ndarray, alpha: np.ndarray, x_kind: str
     return y
 
 
-def ln_absmax_quant(x: np.ndarray, ln_eps: float = 1e-5, bits: int = 8, q_eps: float = 1e-3):
-    """Returns (q int8 [M][K], gamma float32, mu32 [M], rstd32 [M])."""
+def ln_absmax_quant(x: np.ndarray, ln_eps: float = 1e-5, bits: int = 8, q_eps: float = 1e-3,
+                    round_mode: int = 0, gamma_scope: int = 0):
+    """Returns (q int8 [M][K], gamma, mu32 [M], rstd32 [M]); gamma is a float32
+    scalar for the tensor scope (0) and a float32 [M] array for the token scope (1).
+    round_mode 0 truncates toward zero, 1 rounds to nearest even and clamps."""
     x = _f32(x)
     M, K = x.shape
     q = np.empty((M, K), np.int8)
-    g = np.zeros(1, np.float32)
+    g = np.zeros(max(M, 1), np.float32)
     mu = np.empty(M, np.float32)
     rs = np.empty(M, np.float32)
     _check(_load().oracle_ln_absmax_quant(_ptr(x), M, K, ctypes.c_double(ln_eps), bits,
-                                          ctypes.c_float(q_eps), _ptr(q), _ptr(g), _ptr(mu), _ptr(rs)),
+                                          ctypes.c_float(q_eps), round_mode, gamma_scope, _ptr(q), _ptr(g),
+                                          _ptr(mu), _ptr(rs)),
            "ln_absmax_quant")
-    return q, np.float32(g[0]), mu, rs
+    gamma = g[:M].copy() if gamma_scope == 1 else np.float32(g[0])
+    return q, gamma, mu, rs
 
 
 def bitlinear_acc(q: np.ndarray, W: np.ndarray, c: float) -> np.ndarray:
@@ -184,10 +189,20 @@ def bitlinear_acc(q: np.ndarray, W: np.ndarray, c: float) -> np.ndarray:
     return acc
 
 
-def bitlinear_out(acc: np.ndarray, beta: float, gamma: float, bits: int = 8) -> np.ndarray:
+def bitlinear_out(acc: np.ndarray, beta: float, gamma, bits: int = 8) -> np.ndarray:
+    """y = acc * beta * gamma / Q_b in fp64; gamma is a scalar or one value per row."""
     acc = np.ascontiguousarray(acc, dtype=np.int64)
     M, N = acc.shape
     y = np.empty((M, N), np.float64)
-    _check(_load().oracle_bitlinear_out(_ptr(acc), M, N, ctypes.c_float(beta), ctypes.c_float(gamma),
-                                        bits, _ptr(y)), "bitlinear_out")
+    g = np.asarray(gamma, np.float32)
+    if g.ndim == 0:
+        _check(_load().oracle_bitlinear_out(_ptr(acc), M, N, ctypes.c_float(beta), ctypes.c_float(float(g)),
+                                            bits, _ptr(y)), "bitlinear_out")
+        return y
+    for m in range(M):
+        row = np.ascontiguousarray(acc[m:m + 1])
+        ym = np.empty((1, N), np.float64)
+        _check(_load().oracle_bitlinear_out(_ptr(row), 1, N, ctypes.c_float(beta), ctypes.c_float(float(g[m])),
+                                            bits, _ptr(ym)), "bitlinear_out")
+        y[m] = ym[0]
     return y

@@ -181,13 +181,18 @@ int oracle_fbi_linear(const uint16_t* x, int x_kind, int64_t M, int64_t K,
  *                         q inside [-(Q_b-1), Q_b-1], its stated purpose)
  *  - gamma == 0 (every h is zero) gives q == 0. */
 int oracle_ln_absmax_quant(const float* x, int64_t M, int64_t K, double ln_eps, int bits,
-                           float q_eps, int8_t* q, float* gamma, float* mu32, float* rstd32) {
+                           float q_eps, int round_mode, int gamma_scope, int8_t* q, float* gamma,
+                           float* mu32, float* rstd32) {
     if (!x || !q || !gamma || M < 0 || K <= 0 || bits < 2 || bits > 8) return -1;
+    if (round_mode < 0 || round_mode > 1 || gamma_scope < 0 || gamma_scope > 1) return -1;
     const float Qb = (float)(1 << (bits - 1));
-    float* mu_f = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
-    float* rs_f = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
-    if (!mu_f || !rs_f) { free(mu_f); free(rs_f); return -2; }
-    /* statistics per token, then gamma over the whole tensor */
+    const int qmax = (1 << (bits - 1)) - 1;
+    const size_t nm = (size_t)(M > 0 ? M : 1);
+    float* mu_f = (float*)malloc(sizeof(float) * nm);
+    float* rs_f = (float*)malloc(sizeof(float) * nm);
+    float* gm = (float*)malloc(sizeof(float) * nm);
+    if (!mu_f || !rs_f || !gm) { free(mu_f); free(rs_f); free(gm); return -2; }
+    /* statistics per token; each token's max |h|, then gamma over the tensor */
     float g = 0.0f;
     for (int64_t m = 0; m < M; ++m) {
         const float* xr = x + m * K;
@@ -202,31 +207,45 @@ int oracle_ln_absmax_quant(const float* x, int64_t M, int64_t K, double ln_eps, 
         double var = v2 / (double)K;
         mu_f[m] = (float)mu;
         rs_f[m] = (float)(1.0 / sqrt(var + ln_eps));
+        float rowmax = 0.0f;
         for (int64_t i = 0; i < K; ++i) {
             float d = xr[i] - mu_f[m];
             float h = d * rs_f[m];
             float a = fabsf(h);
-            if (a > g) g = a;
+            if (a > rowmax) rowmax = a;
         }
+        gm[m] = rowmax;
+        if (rowmax > g) g = rowmax;
     }
-    *gamma = g;
-    /* quantize */
+    if (gamma_scope == 0) gamma[0] = g;
+    /* quantize with the token's gamma (scope 1) or the tensor's (scope 0) */
     const float lim = Qb - q_eps;
     for (int64_t m = 0; m < M; ++m) {
         const float* xr = x + m * K;
+        const float gr = gamma_scope == 1 ? gm[m] : g;
+        if (gamma_scope == 1) gamma[m] = gr;
         for (int64_t i = 0; i < K; ++i) {
-            if (g == 0.0f) { q[m * K + i] = 0; continue; }
+            if (gr == 0.0f) { q[m * K + i] = 0; continue; }
             float d = xr[i] - mu_f[m];
             float h = d * rs_f[m];
-            float v = (h * Qb) / g;
+            float v = (h * Qb) / gr;
             float vc = v > lim ? lim : (v < -lim ? -lim : v);
-            q[m * K + i] = (int8_t)(int)vc;
+            int c;
+            if (round_mode == 0) {
+                c = (int)vc;                       /* toward zero */
+            } else {
+                c = (int)nearbyintf(vc);           /* nearest, ties to even (default FP environment) */
+                if (c > qmax) c = qmax;
+                if (c < -qmax) c = -qmax;
+            }
+            q[m * K + i] = (int8_t)c;
         }
         if (mu32) mu32[m] = mu_f[m];
         if (rstd32) rstd32[m] = rs_f[m];
     }
     free(mu_f);
     free(rs_f);
+    free(gm);
     return 0;
 }
 

@@ -55,9 +55,14 @@ int oracle_fbi_linear(const uint16_t* x, int x_kind, int64_t M, int64_t K,
 /* BitLinear prologue: per-token LayerNorm (no affine), then absmax quantization to
  * [-Q_b+eps, Q_b-eps] with Q_b = 2^(bits-1), gamma = max |LN(x)| over the tensor.
  * Statistics in fp64; the quantization decision in fp32 (see oracle.c).
- * Outputs: q [M][K], gamma, and per-row mu32/rstd32 (optional, may be NULL). */
+ * round_mode: 0 = truncate toward zero (the reading of eq. (4)), 1 = round to
+ * nearest even, then clamp to +-(Q_b - 1). gamma_scope: 0 = one gamma over the
+ * whole tensor (the reading of section 一), 1 = one gamma per token.
+ * Outputs: q [M][K], gamma ([1] for scope 0, [M] for scope 1), and per-row
+ * mu32/rstd32 (optional, may be NULL). */
 int oracle_ln_absmax_quant(const float* x, int64_t M, int64_t K, double ln_eps, int bits,
-                           float q_eps, int8_t* q, float* gamma, float* mu32, float* rstd32);
+                           float q_eps, int round_mode, int gamma_scope, int8_t* q, float* gamma,
+                           float* mu32, float* rstd32);
 
 /* BitLinear integer product acc[m][j] = sum_i sign(W_ij - c) * q[m][i] (exact). */
 int oracle_bitlinear_acc(const int8_t* q, int64_t M, int64_t K, const float* W, int64_t N,

@@ -339,3 +339,55 @@ def test_f16_conversion_matches_ieee_library(orc):
     assert np.array_equal(mine, ref)
     back = orc.f16_to_f32(ref)
     assert np.array_equal(back, ref.view(np.float16).astype(np.float32))
+
+
+def test_quant_rne_closed_forms(orc):
+    """Round-to-nearest option: hand-derived codes (golden file), the argmax
+    still clamps to Q_b - 1, and every code is the truncated one or one step
+    away from zero from it."""
+    g = read_golden("quant_closed_forms.txt")
+    for pat, key, bits in (("pattern_a", "rne_q_a", 8), ("pattern_c", "rne_q_c", 8), ("pattern_a", "rne4_q_a", 4)):
+        period = np.array([float(v) for v in g[pat]], np.float32)
+        expect = np.array([int(v) for v in g[key]], np.int8)
+        x = np.tile(period, (2, 96 // period.size))
+        q, _, _, _ = orc.ln_absmax_quant(x, bits=bits, round_mode=1)
+        assert np.array_equal(q, np.tile(expect, (2, 96 // period.size))), key
+    x = syn.normal_f32(12, 1, (5, 768)) * np.float32(2.0)
+    qt, gt, _, _ = orc.ln_absmax_quant(x)
+    qr, gr, _, _ = orc.ln_absmax_quant(x, round_mode=1)
+    assert gt == gr
+    d = qr.astype(np.int32) - qt.astype(np.int32)
+    assert np.all((d == 0) | (d == np.sign(qt.astype(np.int32)) + (qt == 0) * np.sign(x - x.mean(1, keepdims=True)).astype(np.int32)))
+    assert np.all(np.abs(qr.astype(np.int32)) <= 127) and np.any(d != 0)
+
+
+def test_quant_token_scope(orc):
+    """Per-token gamma: the closed form of the golden file, and quantizing a
+    tensor per token equals quantizing each token alone with one gamma."""
+    g = read_golden("quant_closed_forms.txt")
+    x = np.stack([np.tile(np.array([-3, -1, 1, 3], np.float32), 24),
+                  np.tile(np.array([-0.7, 0.7], np.float32), 48)])
+    qa = np.array([int(v) for v in g["q_a"]], np.int8)
+    qt, gt, _, _ = orc.ln_absmax_quant(x)
+    qk, gk, _, _ = orc.ln_absmax_quant(x, gamma_scope=1)
+    assert np.array_equal(qt[0], np.tile(qa, 24)) and np.array_equal(qk[0], np.tile(qa, 24))
+    assert np.array_equal(qt[1], np.tile(np.array([int(v) for v in g["tensor_q1"]], np.int8), 48))
+    assert np.array_equal(qk[1], np.tile(np.array([int(v) for v in g["token_q1"]], np.int8), 48))
+    assert gk.shape == (2,) and gk[0] == gt and gk[1] < gt
+    xs = syn.normal_f32(13, 1, (6, 512)) * (np.arange(1, 7, dtype=np.float32)[:, None] ** 2)
+    xs[3] = 0.5                                            # constant token: gamma 0, codes 0
+    for rm in (0, 1):
+        qk, gk, _, _ = orc.ln_absmax_quant(xs, round_mode=rm, gamma_scope=1)
+        for m in range(xs.shape[0]):
+            q1, g1, _, _ = orc.ln_absmax_quant(xs[m:m + 1], round_mode=rm)
+            assert np.array_equal(qk[m], q1[0]) and gk[m] == g1
+    # one token: both scopes agree
+    q1t, g1t, _, _ = orc.ln_absmax_quant(xs[:1])
+    q1k, g1k, _, _ = orc.ln_absmax_quant(xs[:1], gamma_scope=1)
+    assert np.array_equal(q1t, q1k) and g1k[0] == g1t
+
+
+def test_bitlinear_out_per_token_gamma(orc):
+    acc = np.array([[3, -5, 0], [7, 1, -2]], np.int64)
+    y = orc.bitlinear_out(acc, 0.25, np.array([0.5, 2.0], np.float32))
+    assert np.array_equal(y, np.array([[3, -5, 0], [7 * 4, 4, -8]], np.float64) * 0.25 * 0.5 / 128)
