@@ -21,6 +21,7 @@ __all__ = [
     "load", "lib_path", "packed_bytes", "workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
     "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
     "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M", "W1A16_DECODE_MAX_M",
+    "ROUND_TRUNC", "ROUND_RNE", "GAMMA_TENSOR", "GAMMA_TOKEN",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +45,12 @@ class BgbError(RuntimeError):
 
 
 class _QP(ctypes.Structure):
-    _fields_ = [("ln_eps", ctypes.c_double), ("bits", ctypes.c_int), ("q_eps", ctypes.c_float)]
+    _fields_ = [("ln_eps", ctypes.c_double), ("bits", ctypes.c_int), ("q_eps", ctypes.c_float),
+                ("round_mode", ctypes.c_int), ("gamma_scope", ctypes.c_int)]
+
+
+ROUND_TRUNC, ROUND_RNE = 0, 1
+GAMMA_TENSOR, GAMMA_TOKEN = 0, 1
 
 
 @dataclass
@@ -52,6 +58,12 @@ class QuantParams:
     ln_eps: float = 1e-5
     bits: int = 8
     q_eps: float = 1e-3
+    round_mode: int = ROUND_TRUNC
+    gamma_scope: int = GAMMA_TENSOR
+
+    def c(self) -> "_QP":
+        return _QP(float(self.ln_eps), int(self.bits), float(self.q_eps), int(self.round_mode),
+                   int(self.gamma_scope))
 
 
 _lib = None
@@ -187,12 +199,13 @@ def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=No
     dev = x.device
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    qp = qp or QuantParams()
+    ng = M if qp.gamma_scope == GAMMA_TOKEN else 1    # gamma: one per token, or one
     q = torch.empty((M, K), dtype=torch.int8, device=dev) if want_q else None
-    g = torch.empty(4, dtype=torch.float32, device=dev) if want_gamma else None
+    g = torch.empty(max(ng, 4), dtype=torch.float32, device=dev) if want_gamma else None
     acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
     ws = _workspace(OP_BITLINEAR, M, K, N, ws, dev)
-    qp = qp or QuantParams()
-    cqp = _QP(float(qp.ln_eps), int(qp.bits), float(qp.q_eps))
+    cqp = qp.c()
     _check(load().bitlinear_w1a8(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y),
                                  _ptr(q), _ptr(g), _ptr(acc), _ptr(ws), ws.numel(), _stream(stream)))
     if not (want_q or want_gamma or want_acc):
@@ -201,7 +214,7 @@ def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=No
     if want_q:
         extras["q"] = q
     if want_gamma:
-        extras["gamma"] = g[:1]
+        extras["gamma"] = g[:ng]
     if want_acc:
         extras["acc"] = acc
     return y, extras
@@ -212,13 +225,14 @@ def bitlinear_quantize(x, qp: Optional[QuantParams] = None, *, ws, N_max: int = 
     """Prologue only: leaves the codes in `ws` for bitlinear_matmul. Returns the requested taps."""
     torch = _torch()
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if want_q else None
-    g = torch.empty(4, dtype=torch.float32, device=x.device) if want_gamma else None
     qp = qp or QuantParams()
-    cqp = _QP(float(qp.ln_eps), int(qp.bits), float(qp.q_eps))
+    ng = M if qp.gamma_scope == GAMMA_TOKEN else 1
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if want_q else None
+    g = torch.empty(max(ng, 4), dtype=torch.float32, device=x.device) if want_gamma else None
+    cqp = qp.c()
     _check(load().bitlinear_quantize(_ptr(x), _dt(x), M, K, ctypes.byref(cqp), _ptr(q), _ptr(g), _ptr(ws),
                                      ws.numel(), _stream(stream)))
-    return {"q": q, "gamma": None if g is None else g[:1]}
+    return {"q": q, "gamma": None if g is None else g[:ng]}
 
 
 def bitlinear_matmul(M: int, K: int, P, beta, N: int, qp: Optional[QuantParams] = None, *, ws, y=None,
@@ -229,7 +243,7 @@ def bitlinear_matmul(M: int, K: int, P, beta, N: int, qp: Optional[QuantParams] 
         y = torch.empty((M, N), dtype=torch.float32, device=ws.device)
     acc = torch.empty((M, N), dtype=torch.int32, device=ws.device) if want_acc else None
     qp = qp or QuantParams()
-    cqp = _QP(float(qp.ln_eps), int(qp.bits), float(qp.q_eps))
+    cqp = qp.c()
     _check(load().bitlinear_matmul(M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y), _ptr(acc), _ptr(ws),
                                    ws.numel(), _stream(stream)))
     return (y, acc) if want_acc else y

@@ -104,9 +104,12 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
 
 // Shared checks of the BitLinear entry points; fills qb/lim from qp.
 static int bitlinear_params(const bgb_quant_params* qp, bgb_quant_params* p, float* qb, float* lim) {
-    *p = bgb_quant_params{1e-5, 8, 1e-3f};
+    *p = bgb_quant_params{1e-5, 8, 1e-3f, BGB_ROUND_TRUNC, BGB_GAMMA_TENSOR};
     if (qp) *p = *qp;
     if (p->bits < 2 || p->bits > 8) return BGB_EUNSUPPORTED;
+    if ((p->round_mode != BGB_ROUND_TRUNC && p->round_mode != BGB_ROUND_RNE) ||
+        (p->gamma_scope != BGB_GAMMA_TENSOR && p->gamma_scope != BGB_GAMMA_TOKEN))
+        return BGB_EUNSUPPORTED;
     if (!(p->ln_eps > 0.0) || !(p->q_eps > 0.0f) || !(p->q_eps < 1.0f)) return BGB_EINVAL;
     *qb = float(1 << (p->bits - 1));
     *lim = *qb - p->q_eps;                       // fl32(Q_b - eps), as the reference computes it
@@ -128,7 +131,8 @@ int bitlinear_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const b
     const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, 0);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     const bool decode = M <= bgb::kGemvMaxM;
-    return finish(bgb::launch_ln_quant(x, x_dtype == BGB_BF16, M, K, p.ln_eps, qb, lim, decode ? 0 : 1,
+    return finish(bgb::launch_ln_quant(x, x_dtype == BGB_BF16, M, K, p.ln_eps, qb, lim,
+                                       p.round_mode == BGB_ROUND_RNE, p.gamma_scope == BGB_GAMMA_TOKEN, decode ? 0 : 1,
                                        reinterpret_cast<int8_t*>(carve(ws, lay.q)),
                                        reinterpret_cast<int32_t*>(carve(ws, lay.rowsum)),
                                        reinterpret_cast<float*>(carve(ws, lay.stats)),
@@ -153,9 +157,16 @@ int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const f
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int8_t* q = reinterpret_cast<const int8_t*>(carve(ws, lay.q));
     const int32_t* rowsum = reinterpret_cast<const int32_t*>(carve(ws, lay.rowsum));
-    const float* gamma = reinterpret_cast<const float*>(carve(ws, lay.gamma));
-    if (M <= bgb::kGemvMaxM) return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, s));
-    return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, beta, qb, M, K, N, P, y, acc_opt, carve(ws, lay.part), s));
+    // one gamma for the tensor, or each token's own: the row maxima the
+    // prologue keeps in its statistics ([M][3]: mu32, rstd32, max |h|)
+    const bool token = p.gamma_scope == BGB_GAMMA_TOKEN;
+    const float* gamma = token ? reinterpret_cast<const float*>(carve(ws, lay.stats)) + 2
+                               : reinterpret_cast<const float*>(carve(ws, lay.gamma));
+    const int gstride = token ? 3 : 0;
+    if (M <= bgb::kGemvMaxM)
+        return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, gstride, beta, qb, M, K, N, P, y, acc_opt, s));
+    return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, gstride, beta, qb, M, K, N, P, y, acc_opt,
+                                        carve(ws, lay.part), s));
 }
 
 int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
@@ -176,7 +187,9 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, 
     const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     if (M == 1 && bgb::w1a8_decode1_supported(K)) {
-        return finish(bgb::launch_w1a8_decode1(x, x_dtype == BGB_BF16, K, N, p.ln_eps, qb, lim, P, beta, y, acc_opt,
+        // one token: its gamma is the tensor's, whatever the scope
+        return finish(bgb::launch_w1a8_decode1(x, x_dtype == BGB_BF16, K, N, p.ln_eps, qb, lim,
+                                               p.round_mode == BGB_ROUND_RNE, P, beta, y, acc_opt,
                                                xq_opt, gamma_opt, static_cast<hipStream_t>(stream)));
     }
     rc = bitlinear_quantize(x, x_dtype, M, K, qp, xq_opt, gamma_opt, ws, ws_bytes, stream);

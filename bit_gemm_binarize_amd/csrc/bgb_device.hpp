@@ -104,6 +104,21 @@ BGB_DEV int wave_sum63_i(int v) {
     v += dpp_i32<0x143, 0xC>(v);
     return v;
 }
+// Integer code of a quantizer input v: truncation toward zero, or (rne)
+// rounding to nearest, ties to even; clamped to +-qmax either way (a no-op for
+// truncation of a value already clipped to +-(Q_b - eps)).
+BGB_DEV int round_code(float v, bool rne, int qmax) {
+    const int c = rne ? int(__builtin_rintf(v)) : int(v);
+    return c > qmax ? qmax : (c < -qmax ? -qmax : c);
+}
+// Whether a fast quotient u, within 1.5 ulp of the exact one, lies so close to
+// a point where the code changes (a nonzero integer for truncation, a
+// half-integer for rounding) that the exact division has to decide.
+BGB_DEV bool code_near_boundary(float u, bool rne) {
+    const float d = __builtin_fabsf(u - __builtin_rintf(u));
+    return (rne ? __builtin_fabsf(d - 0.5f) : d) < __builtin_fabsf(u) * 0x1p-20f;
+}
+
 // Unsigned max over the 64 lanes, valid in lane 63 (0 is the identity).
 BGB_DEV uint32_t wave_umax63(uint32_t v) {
     v = max(v, uint32_t(dpp_i32<0xB1, 0xF>(int(v))));

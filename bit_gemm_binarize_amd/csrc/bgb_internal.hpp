@@ -98,9 +98,9 @@ hipError_t launch_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t*
 
 // q layout written by the prologue: 0 = decode kernel layout, 1 = GEMM layout
 hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, double ln_eps,
-                           float qb, float lim, int layout, int8_t* q, int32_t* rowsum,
-                           float* stats, float* gamma_ws, int8_t* xq_opt, float* gamma_opt,
-                           hipStream_t s);
+                           float qb, float lim, int rne, int token, int layout, int8_t* q,
+                           int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
+                           float* gamma_opt, hipStream_t s);
 
 // GEMM activations: xi[m][Kp], element pairs (row i, row i+16) of each 32-row group
 hipError_t launch_w1a16_interleave(const void* x, int64_t M, int64_t K, uint16_t* xi, hipStream_t s);
@@ -110,14 +110,14 @@ hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K
                              int y_dtype, void* part, hipStream_t s);
 
 hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma,
-                            const float* beta, float qb, int64_t M, int64_t K, int64_t N,
-                            const uint32_t* P, float* y, int32_t* acc_opt, hipStream_t s);
+                            int gstride, const float* beta, float qb, int64_t M, int64_t K,
+                            int64_t N, const uint32_t* P, float* y, int32_t* acc_opt, hipStream_t s);
 
 // Single-token fused kernels (prologue / activation staging inside the GEMV).
 bool w1a8_decode1_supported(int64_t K);
 hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
-                               const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
-                               float* gamma_opt, hipStream_t s);
+                               int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt,
+                               int8_t* xq_opt, float* gamma_opt, hipStream_t s);
 bool w1a16_decode1_supported(int64_t K);
 // 2 <= M <= 16 tokens staged in LDS by every block (M (Kp + 8) 2 bytes <= 140 KB)
 bool w1a16_decodem_supported(int64_t M, int64_t K);
@@ -135,7 +135,8 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
-                            const float* beta, float qb, int64_t M, int64_t K, int64_t N,
-                            const uint32_t* P, float* y, int32_t* acc_opt, void* part, hipStream_t s);
+                            int gstride, const float* beta, float qb, int64_t M, int64_t K,
+                            int64_t N, const uint32_t* P, float* y, int32_t* acc_opt, void* part,
+                            hipStream_t s);
 
 }  // namespace bgb

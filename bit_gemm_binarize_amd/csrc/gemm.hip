@@ -187,7 +187,8 @@ struct GemmArgs {
     int y_dtype;
     // W1A8 epilogue
     const int32_t* rowsum;
-    const float* gamma;
+    const float* gamma;        // gamma of token m at gamma[m * gstride] (gstride 0: one for the tensor)
+    int gstride;
     const float* beta;
     float qb;
     int32_t* acc_opt;
@@ -221,7 +222,7 @@ BGB_DEV void store_out16(void* y, int y_dtype, int64_t o, const float (&v)[4], b
 }
 
 BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& s, bool full, int64_t jb) {
-    const float scale = (a.beta[0] * a.gamma[0]) / a.qb;
+    const float scale = (a.beta[0] * a.gamma[m * a.gstride]) / a.qb;
     const int32_t rs = a.rowsum[m];
     i32x4_t v;
 #pragma unroll
@@ -526,7 +527,8 @@ hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K
     return x_f16 ? launch_gemm<false, true>(a, p, s) : launch_gemm<false, false>(a, p, s);
 }
 
-hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma, const float* beta, float qb,
+hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma, int gstride,
+                            const float* beta, float qb,
                             int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
                             void* part, hipStream_t s) {
     const GemmPlan p = gemm_plan(M, K, N, true);
@@ -538,6 +540,7 @@ hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float*
     a.N = N;
     a.rowsum = rowsum;
     a.gamma = gamma;
+    a.gstride = gstride;
     a.beta = beta;
     a.qb = qb;
     a.y = y;

@@ -154,7 +154,7 @@ inline int gen_steps(int64_t TQ) {
 template <int TF, int GS>
 __global__ void __launch_bounds__(kGenWaves * 64)
 gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsum, const float* __restrict__ gamma,
-                 const float* __restrict__ beta, float qb, int M, int64_t N, int64_t TQ,
+                 int gstride, const float* __restrict__ beta, float qb, int M, int64_t N, int64_t TQ,
                  const uint32_t* __restrict__ P, float* __restrict__ y, int32_t* __restrict__ acc_opt) {
     __shared__ i32x4_t red[kGenWaves][TF][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -191,11 +191,11 @@ gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsu
     for (int tf = 0; tf < TF; ++tf) red[wave][tf][lane] = w1a8_combine(acc[tf]);
     __syncthreads();
     if (wave != 0) return;
-    const float scale = (beta[0] * gamma[0]) / qb;
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf) {
         const int mm = 16 * tf + r;
         if (mm >= M) continue;
+        const float scale = (beta[0] * gamma[int64_t(mm) * gstride]) / qb;   // the tensor's or the token's gamma
         i32x4_t sum = red[0][tf][lane];
 #pragma unroll
         for (int wv = 1; wv < kGenWaves; ++wv) sum += red[wv][tf][lane];
@@ -226,10 +226,10 @@ constexpr int kD1Waves = 8;         // W1A16 single-token blocks
 constexpr int kD1MaxGrid = 256;     // one block per CU
 constexpr int kD1MaxTiles = 8;      // preloaded 16-byte sign tiles per thread (IT x S)
 
-// Code of one activation, h already LayerNormed: trunc(clip(fl32(h Q_b / gamma),
-// +-lim)), lim in (Q_b - 1, Q_b).
-BGB_DEV int exact_code(float h, float qb, float gamma, float lim) {
-    return int(fminf(fmaxf((h * qb) / gamma, -lim), lim));
+// Code of one activation, h already LayerNormed: trunc (or, rne, the nearest
+// integer, clamped) of clip(fl32(h Q_b / gamma), +-lim), lim in (Q_b - 1, Q_b).
+BGB_DEV int exact_code(float h, float qb, float gamma, float lim, bool rne) {
+    return round_code(fminf(fmaxf((h * qb) / gamma, -lim), lim), rne, int(qb) - 1);
 }
 
 // W1A8 steps per wave: NV dwords of codes per thread cover NV NW / 2 steps of
@@ -239,7 +239,7 @@ constexpr int w1a8_d1_steps(int nv, int f) { return (nv * f + 1) / 2; }
 template <int NV, int NW, int F, int IT, typename XT>
 __global__ void __launch_bounds__(NW * 64)
 bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
-                         const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
+                         int rne, const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
                          int32_t* __restrict__ acc_opt, int8_t* __restrict__ xq_opt,
                          float* __restrict__ gamma_opt) {
     constexpr int NT = NW * 64;
@@ -344,6 +344,8 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     //    A lane with a near-integer u (rare) redoes all its codes exactly.
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
     const float ucl = qb - 0.5f;
+    const bool rn = rne != 0;
+    const int qmax = int(qb) - 1;
     int codes[NV][4];
     bool slow = false;
 #pragma unroll
@@ -353,14 +355,14 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
             const float h = v[i][c] * rs32;
             v[i][c] = h;
             const float u = fminf(fmaxf(h * cq, -ucl), ucl);
-            slow |= fabsf(u - rintf(u)) < fabsf(u) * 0x1p-20f;
-            codes[i][c] = int(u);
+            slow |= code_near_boundary(u, rn);
+            codes[i][c] = round_code(u, rn, qmax);
         }
     if (slow && gamma != 0.0f) {                       // gamma = 0: every h and code is 0
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) codes[i][c] = exact_code(v[i][c], qb, gamma, lim);
+            for (int c = 0; c < 4; ++c) codes[i][c] = exact_code(v[i][c], qb, gamma, lim, rn);
     }
     int sq = 0;
 #pragma unroll
@@ -450,10 +452,10 @@ constexpr bool w1a8_d1_ok(int f, int it) {
 
 template <int NV, int NW, int F, typename XT>
 static void launch_w1a8_decode1_f(int it, unsigned grid, const XT* x, int64_t K, int64_t N, int64_t TQ, double eps,
-                                  float qb, float lim, const uint32_t* P, const float* beta, float* y,
+                                  float qb, float lim, int rne, const uint32_t* P, const float* beta, float* y,
                                   int32_t* acc_opt, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
 #define BGB_D1X(ITV) \
-    bitlinear_decode1_kernel<NV, NW, F, ITV, XT><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, beta, y, \
+    bitlinear_decode1_kernel<NV, NW, F, ITV, XT><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, rne, P, beta, y, \
                                                                           acc_opt, xq_opt, gamma_opt)
     if constexpr (w1a8_d1_ok<NV, NW>(F, 1)) {
         if constexpr (w1a8_d1_ok<NV, NW>(F, 2)) {
@@ -469,7 +471,7 @@ static void launch_w1a8_decode1_f(int it, unsigned grid, const XT* x, int64_t K,
 
 template <int NV, int NW, typename XT>
 static void launch_w1a8_decode1_nv(const XT* x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
-                                   const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
+                                   int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                    float* gamma_opt, hipStream_t s) {
     // the fewest fragments per group that give each block (one per CU) a
     // single group; failing that, the most allowed and up to 2 groups per
@@ -487,7 +489,7 @@ static void launch_w1a8_decode1_nv(const XT* x, int64_t K, int64_t N, int64_t TQ
     }
     const unsigned gr = unsigned(grid);
 #define BGB_D1F(FV) \
-    launch_w1a8_decode1_f<NV, NW, FV, XT>(it, gr, x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
+    launch_w1a8_decode1_f<NV, NW, FV, XT>(it, gr, x, K, N, TQ, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
     if (F == 1) BGB_D1F(1);
     else if (F == 2) BGB_D1F(2);
     else if (F == 4) BGB_D1F(4);
@@ -496,7 +498,7 @@ static void launch_w1a8_decode1_nv(const XT* x, int64_t K, int64_t N, int64_t TQ
 }
 
 template <int NW, typename XT>
-static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps, float qb, float lim,
+static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps, float qb, float lim, int rne,
                                    const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                    float* gamma_opt, hipStream_t s) {
     constexpr int nt = NW * 64;
@@ -504,7 +506,7 @@ static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps
     const int64_t TQ = tiles_per_col(K);
     const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
     const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : 16;
-#define BGB_D1(NVV) launch_w1a8_decode1_nv<NVV, NW, XT>(x, K, N, TQ, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
+#define BGB_D1(NVV) launch_w1a8_decode1_nv<NVV, NW, XT>(x, K, N, TQ, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
     if (nvp == 1) BGB_D1(1);
     else if (nvp == 2) BGB_D1(2);
     else if (nvp == 4) BGB_D1(4);
@@ -514,32 +516,33 @@ static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps
 }
 
 hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
-                               const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
+                               int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                float* gamma_opt, hipStream_t s) {
     // 8-wave blocks for layers of at least 8192 columns; 4-wave blocks (one
     // wave per SIMD, so the per-wave prologue work is not repeated) below
     const bool wide = (N + 31) / 32 >= kD1MaxGrid;
     if (x_bf16) {
         const uint16_t* xb = static_cast<const uint16_t*>(x);
-        if (wide) launch_w1a8_decode1_nw<8>(xb, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
-        else launch_w1a8_decode1_nw<4>(xb, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        if (wide) launch_w1a8_decode1_nw<8>(xb, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        else launch_w1a8_decode1_nw<4>(xb, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
     } else {
         const float* xf = static_cast<const float*>(x);
-        if (wide) launch_w1a8_decode1_nw<8>(xf, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
-        else launch_w1a8_decode1_nw<4>(xf, K, N, eps, qb, lim, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        if (wide) launch_w1a8_decode1_nw<8>(xf, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+        else launch_w1a8_decode1_nw<4>(xf, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma, const float* beta, float qb,
-                            int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
-                            hipStream_t s) {
+hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma, int gstride,
+                            const float* beta, float qb, int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y,
+                            int32_t* acc_opt, hipStream_t s) {
     const unsigned grid = unsigned((N + 15) / 16);
     const int64_t TQ = tiles_per_col(K);
     const int tf = int((M + 15) / 16);
     const int gs = gen_steps(TQ);
     constexpr unsigned nt = kGenWaves * 64;
-#define BGB_G8(TFV, GSV) gemv_w1a8_kernel<TFV, GSV><<<grid, nt, 0, s>>>(q, rowsum, gamma, beta, qb, int(M), N, TQ, P, y, acc_opt)
+#define BGB_G8(TFV, GSV) gemv_w1a8_kernel<TFV, GSV><<<grid, nt, 0, s>>>(q, rowsum, gamma, gstride, beta, qb, int(M), N, TQ, P, y, \
+                                                                     acc_opt)
 #define BGB_G8S(TFV) if (gs == 1) BGB_G8(TFV, 1); else if (gs == 2) BGB_G8(TFV, 2); else BGB_G8(TFV, 4);
     if (tf == 1) { BGB_G8S(1) } else if (tf == 2) { BGB_G8S(2) } else if (tf == 3) { BGB_G8S(3) } else { BGB_G8S(4) }
 #undef BGB_G8S

@@ -7,8 +7,10 @@
 // Numerics (fixed so that codes are reproducible and identical to the
 // reference): E x and Var x (biased, two passes) in fp64; mu32 = fl32(E x),
 // rstd32 = fl32(1 / sqrt(Var x + eps)); h = fl32(fl32(x - mu32) * rstd32);
-// gamma = max |h|; v = fl32(h Q_b / gamma) (h Q_b exact, one rounding);
-// clip to +-lim with lim = fl32(Q_b - q_eps); truncate toward zero.
+// gamma = max |h| (over the tensor, or per token as an option);
+// v = fl32(h Q_b / gamma) (h Q_b exact, one rounding); clip to +-lim with
+// lim = fl32(Q_b - q_eps); truncate toward zero (or, as an option, round to
+// nearest even and clamp to +-(Q_b - 1)).
 //
 // The codes are written in the order the product kernels read them (one
 // 128-row tile at a time, zero-padded to whole tiles):
@@ -26,11 +28,11 @@ template <> BGB_DEV float load_x<uint16_t>(const uint16_t* p, int64_t i) { retur
 
 BGB_DEV float ln_apply(float x, float mu32, float rs32) { return (x - mu32) * rs32; }
 
-BGB_DEV int quant_code(float h, float qb, float gamma, float lim) {
+BGB_DEV int quant_code(float h, float qb, float gamma, float lim, bool rne, int qmax) {
     if (gamma == 0.0f) return 0;
     float v = (h * qb) / gamma;
     v = fminf(fmaxf(v, -lim), lim);
-    return int(v);   // truncation toward zero
+    return round_code(v, rne, qmax);
 }
 
 // First row (within a 128-row tile) of the four codes packed in dword `dw`.
@@ -58,7 +60,8 @@ BGB_DEV void row_stats(const XT* xr, int64_t K, double eps, double* dscr, float&
 // Quantize one row with a block of NT threads; returns the row's code sum.
 template <int NT, typename XT>
 BGB_DEV int quant_row(const XT* xr, int64_t K, int64_t Kp, float mu32, float rs32, float qb, float gamma,
-                      float lim, int layout, uint32_t* qrow, int8_t* natrow, int* iscr) {
+                      float lim, bool rne, int layout, uint32_t* qrow, int8_t* natrow, int* iscr) {
+    const int qmax = int(qb) - 1;
     int sum = 0;
     for (int64_t dwi = threadIdx.x; dwi < Kp / 4; dwi += NT) {
         const int64_t k0 = (dwi / 32) * 128 + code_base(layout, int(dwi % 32));
@@ -68,7 +71,7 @@ BGB_DEV int quant_row(const XT* xr, int64_t K, int64_t Kp, float mu32, float rs3
             const int64_t k = k0 + 8 * e;
             int c = 0;
             if (k < K) {
-                c = quant_code(ln_apply(load_x(xr, k), mu32, rs32), qb, gamma, lim);
+                c = quant_code(ln_apply(load_x(xr, k), mu32, rs32), qb, gamma, lim, rne, qmax);
                 if (natrow) natrow[k] = int8_t(c);
             }
             sum += c;
@@ -83,12 +86,13 @@ BGB_DEV int quant_row(const XT* xr, int64_t K, int64_t Kp, float mu32, float rs3
 template <typename XT>
 __global__ void __launch_bounds__(1024)
 lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double eps, float qb, float lim,
-                 int layout, int8_t* __restrict__ q, int32_t* __restrict__ rowsum, float* __restrict__ stats,
-                 float* __restrict__ gamma_ws, int8_t* __restrict__ xq_opt, float* __restrict__ gamma_opt) {
+                 int rne, int token, int layout, int8_t* __restrict__ q, int32_t* __restrict__ rowsum,
+                 float* __restrict__ stats, float* __restrict__ gamma_ws, int8_t* __restrict__ xq_opt,
+                 float* __restrict__ gamma_opt) {
     __shared__ double dscr[16];
     __shared__ float fscr[16];
     __shared__ int iscr[16];
-    __shared__ float s_mu[kSmallPrologueM], s_rs[kSmallPrologueM];
+    __shared__ float s_mu[kSmallPrologueM], s_rs[kSmallPrologueM], s_lm[kSmallPrologueM];
     float gmax = 0.0f;
     for (int m = 0; m < M; ++m) {
         const XT* xr = x + int64_t(m) * K;
@@ -100,6 +104,7 @@ lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double 
         if (threadIdx.x == 0) {
             s_mu[m] = mu32;
             s_rs[m] = rs32;
+            s_lm[m] = lm;
             stats[3 * m] = mu32;
             stats[3 * m + 1] = rs32;
             stats[3 * m + 2] = lm;
@@ -107,13 +112,14 @@ lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double 
         gmax = fmaxf(gmax, lm);
     }
     __syncthreads();
-    const float gamma = gmax;
     if (threadIdx.x == 0) {
-        gamma_ws[0] = gamma;
-        if (gamma_opt) gamma_opt[0] = gamma;
+        gamma_ws[0] = gmax;
+        if (gamma_opt && !token) gamma_opt[0] = gmax;
     }
+    if (gamma_opt && token && threadIdx.x < M) gamma_opt[threadIdx.x] = s_lm[threadIdx.x];
     for (int m = 0; m < M; ++m) {
-        const int s = quant_row<1024>(x + int64_t(m) * K, K, Kp, s_mu[m], s_rs[m], qb, gamma, lim, layout,
+        const float gamma = token ? s_lm[m] : gmax;     // the token's own, or the tensor's
+        const int s = quant_row<1024>(x + int64_t(m) * K, K, Kp, s_mu[m], s_rs[m], qb, gamma, lim, rne != 0, layout,
                                       reinterpret_cast<uint32_t*>(q + int64_t(m) * Kp),
                                       xq_opt ? xq_opt + int64_t(m) * K : nullptr, iscr);
         if (threadIdx.x == 0) rowsum[m] = s;
@@ -206,8 +212,9 @@ lnq_stats_kernel(const XT* __restrict__ x, int64_t M, int64_t K, double eps, flo
 // the requested layout (zeros for the padding words past K).
 template <typename XT>
 __global__ void __launch_bounds__(256)
-lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, float qb, float lim, int layout,
-                 const float* __restrict__ stats, const float* __restrict__ blockmax, int nblocks,
+lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, float qb, float lim, int rne,
+                 int token, int layout, const float* __restrict__ stats, const float* __restrict__ blockmax,
+                 int nblocks,
                  int8_t* __restrict__ q, int32_t* __restrict__ rowsum, float* __restrict__ gamma_ws,
                  int8_t* __restrict__ xq_opt, float* __restrict__ gamma_opt) {
     using V = Vec16<XT>;
@@ -219,15 +226,18 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
     gm = wave_max63_nonneg(gm);
     if (lane == 63) gscr[wave] = gm;
     __syncthreads();
-    const float gamma = fmaxf(fmaxf(gscr[0], gscr[1]), fmaxf(gscr[2], gscr[3]));
+    const float gt = fmaxf(fmaxf(gscr[0], gscr[1]), fmaxf(gscr[2], gscr[3]));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        gamma_ws[0] = gamma;
-        if (gamma_opt) gamma_opt[0] = gamma;
+        gamma_ws[0] = gt;
+        if (gamma_opt && !token) gamma_opt[0] = gt;
     }
     const int64_t m = int64_t(blockIdx.x) * 4 + wave;
     if (m >= M) return;
     const XT* xr = x + m * K;
     const float mu32 = stats[3 * m], rs32 = stats[3 * m + 1];
+    const float gamma = token ? stats[3 * m + 2] : gt;      // the token's own, or the tensor's
+    if (gamma_opt && token && lane == 0) gamma_opt[m] = gamma;
+    const bool rn = rne != 0;
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
     const int qmax = int(qb) - 1;
     const int64_t words = K / 32, pwords = Kp / 32;
@@ -244,15 +254,15 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
             for (int j = 0; j < 32; ++j) {
                 h[j] = ln_apply(h[j], mu32, rs32);
                 // fast path: u = h (Q_b rcp(gamma)) is within 1.5 ulp of the exact
-                // quotient; only near-integer u (rare) can truncate differently
+                // quotient; only u near a code boundary (rare) can round differently
                 const float u = h[j] * cq;
-                slow |= uint32_t(fabsf(u - rintf(u)) <= fabsf(u) * 0x1p-20f) << j;
-                code[j] = max(-qmax, min(qmax, int(u)));
+                slow |= uint32_t(code_near_boundary(u, rn)) << j;
+                code[j] = round_code(u, rn, qmax);
             }
             if (slow && gamma != 0.0f) {
 #pragma unroll
                 for (int j = 0; j < 32; ++j)
-                    if (slow & (1u << j)) code[j] = quant_code(h[j], qb, gamma, lim);
+                    if (slow & (1u << j)) code[j] = quant_code(h[j], qb, gamma, lim, rn, qmax);
             }
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
@@ -288,31 +298,31 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
 }
 
 template <typename XT>
-static void launch_lnq_t(const XT* x, int64_t M, int64_t K, double eps, float qb, float lim, int layout,
-                         int8_t* q, int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
+static void launch_lnq_t(const XT* x, int64_t M, int64_t K, double eps, float qb, float lim, int rne, int token,
+                         int layout, int8_t* q, int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
                          float* gamma_opt, hipStream_t s) {
     const int64_t Kp = padded_k(K);
     if (M <= kSmallPrologueM) {
-        lnq_small_kernel<XT><<<1, 1024, 0, s>>>(x, int(M), K, Kp, eps, qb, lim, layout, q, rowsum, stats,
-                                                 gamma_ws, xq_opt, gamma_opt);
+        lnq_small_kernel<XT><<<1, 1024, 0, s>>>(x, int(M), K, Kp, eps, qb, lim, rne, token, layout, q, rowsum,
+                                                 stats, gamma_ws, xq_opt, gamma_opt);
     } else {
         const unsigned blocks = unsigned((M + 3) / 4);
         float* blockmax = stats + 3 * M;       // the workspace's stats region holds [M][3] + ceil(M/4)
         lnq_stats_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, eps, stats, blockmax);
-        lnq_quant_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, Kp, qb, lim, layout, stats, blockmax, int(blocks), q,
-                                                     rowsum, gamma_ws, xq_opt, gamma_opt);
+        lnq_quant_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, Kp, qb, lim, rne, token, layout, stats, blockmax,
+                                                     int(blocks), q, rowsum, gamma_ws, xq_opt, gamma_opt);
     }
 }
 
 hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, double ln_eps, float qb, float lim,
-                           int layout, int8_t* q, int32_t* rowsum, float* stats, float* gamma_ws,
-                           int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
+                           int rne, int token, int layout, int8_t* q, int32_t* rowsum, float* stats,
+                           float* gamma_ws, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
     if (x_bf16)
-        launch_lnq_t(static_cast<const uint16_t*>(x), M, K, ln_eps, qb, lim, layout, q, rowsum, stats, gamma_ws,
-                     xq_opt, gamma_opt, s);
+        launch_lnq_t(static_cast<const uint16_t*>(x), M, K, ln_eps, qb, lim, rne, token, layout, q, rowsum, stats,
+                     gamma_ws, xq_opt, gamma_opt, s);
     else
-        launch_lnq_t(static_cast<const float*>(x), M, K, ln_eps, qb, lim, layout, q, rowsum, stats, gamma_ws,
-                     xq_opt, gamma_opt, s);
+        launch_lnq_t(static_cast<const float*>(x), M, K, ln_eps, qb, lim, rne, token, layout, q, rowsum, stats,
+                     gamma_ws, xq_opt, gamma_opt, s);
     return hipGetLastError();
 }
 

@@ -76,12 +76,23 @@ typedef enum {
     BGB_OP_BITLINEAR = 3
 } bgb_op;
 
+/* Integer conversion of the clipped quantizer input v_c (eq. (4) gives none):
+ * truncation toward zero (the default; it keeps |q| <= Q_b - 1 through the
+ * clip margin) or round to nearest, ties to even, then clamp to +-(Q_b - 1). */
+typedef enum { BGB_ROUND_TRUNC = 0, BGB_ROUND_RNE = 1 } bgb_round_mode;
+
+/* What gamma = ||LN(x)||_inf is taken over: the whole M x K input (the
+ * default; section 一 speaks of the input matrix's maximum) or each token. */
+typedef enum { BGB_GAMMA_TENSOR = 0, BGB_GAMMA_TOKEN = 1 } bgb_gamma_scope;
+
 /* Activation quantization parameters of BitLinear ("BitNet b1.58: 1bit LLM时代",
  * section 一, eq. (4), (5), (8)). */
 typedef struct {
     double ln_eps;   /* LayerNorm epsilon added to the variance, > 0 (1e-5) */
     int bits;        /* b in Q_b = 2^(b-1); 2..8 (8 -> Q_b = 128, int8 codes) */
     float q_eps;     /* clip margin in (0, 1): codes are clipped to [-Q_b+eps, Q_b-eps] (1e-3) */
+    int round_mode;  /* bgb_round_mode (BGB_ROUND_TRUNC) */
+    int gamma_scope; /* bgb_gamma_scope (BGB_GAMMA_TENSOR) */
 } bgb_quant_params;
 
 /* Size in bytes of the packed array P for a K x N weight (0 if K is invalid). */
@@ -142,16 +153,19 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
  * bitlinear_w1a8 -- BitLinear forward (BitNet blog, section 一, eq. (4)-(8)).
  *   h = LN(x) per token (biased variance, no affine): E(x), Var(x) in fp64,
  *       then h = fl32(fl32(x - fl32(E)) * fl32(1/sqrt(Var + ln_eps)))
- *   gamma = max |h| over the whole M x K tensor
+ *   gamma = max |h| over the whole M x K tensor (qp->gamma_scope TENSOR),
+ *       or gamma_m = max_i |h[m][i]| per token (TOKEN)
  *   q = trunc(clip(fl32(h * Q_b / gamma), -(Q_b - q_eps), Q_b - q_eps))
- *       (q = 0 when gamma == 0); |q| <= Q_b - 1
+ *       (qp->round_mode TRUNC; RNE rounds to nearest even instead and
+ *       clamps to +-(Q_b - 1)); q = 0 when gamma == 0; |q| <= Q_b - 1
  *   acc[m][j] = sum_i s_ij * q[m][i]           (exact int32)
  *   y[m][j] = fl32(float(acc) * fl32(fl32(beta * gamma) / Q_b))
+ *       (gamma_m of the row's token for the TOKEN scope)
  * x: [M][K] F32 or BF16. P: packed signs of W - c (binarize_pack BITNET).
  * beta: device scalar from binarize_pack. qp: host pointer (NULL = defaults
- * ln_eps 1e-5, bits 8, q_eps 1e-3). y: [M][N] float32.
+ * ln_eps 1e-5, bits 8, q_eps 1e-3, TRUNC, TENSOR). y: [M][N] float32.
  * Optional outputs (NULL to skip): xq_opt int8 [M][K] codes, gamma_opt device
- * float scalar, acc_opt int32 [M][N].
+ * float [1] (TENSOR) or [M] (TOKEN), acc_opt int32 [M][N].
  * ws: bgb_workspace_bytes(BGB_OP_BITLINEAR, M, K, N) bytes.
  * M <= 32 runs the memory-bound decode kernels, M > 32 the int8 MFMA GEMM.
  * Errors: BGB_EINVAL, BGB_EUNSUPPORTED, BGB_EHIP.
@@ -170,7 +184,8 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
  * bgb_workspace_bytes(BGB_OP_BITLINEAR, M, K, N) for the largest N used);
  * xq_opt / gamma_opt are optional copies as above.
  * bitlinear_matmul then computes y (and optionally acc) for one packed weight
- * from that workspace; M, K and qp->bits must match the quantize call, and
+ * from that workspace; M, K, qp->bits and qp->gamma_scope must match the
+ * quantize call, and
  * the two calls must be ordered on one stream. bitlinear_w1a8 is exactly
  * bitlinear_quantize followed by bitlinear_matmul.
  */

@@ -129,4 +129,6 @@ def test_bitlinear_validation(lib):
     assert call_bl(lib, qp=ctypes.pointer(bad_bits)) == UNSUP
     bad_eps = bgb._QP(1e-5, 8, 2.0)
     assert call_bl(lib, qp=ctypes.pointer(bad_eps)) == BAD
+    assert call_bl(lib, qp=ctypes.pointer(bgb._QP(1e-5, 8, 1e-3, 2, 0))) == UNSUP   # round mode
+    assert call_bl(lib, qp=ctypes.pointer(bgb._QP(1e-5, 8, 1e-3, 0, 5))) == UNSUP   # gamma scope
     assert call_bl(lib, M=0) == 0

@@ -17,9 +17,10 @@ def _run(bgb, orc, W, x_host, x_dev, qp=None, bits=8):
     y, ex = bgb.bitlinear_w1a8(x_dev, P, beta, N, qp, want_q=True, want_gamma=True, want_acc=True)
     torch.cuda.synchronize()
     c_ref, b_ref = orc.bitnet_scalars(W)
-    q_ref, g_ref, _, _ = orc.ln_absmax_quant(x_host, bits=bits)
-    g = np.float32(host_f32(ex["gamma"])[0])
-    assert g.view(np.uint32) == g_ref.view(np.uint32), (g, g_ref)
+    rm, gs = (qp.round_mode, qp.gamma_scope) if qp else (0, 0)
+    q_ref, g_ref, _, _ = orc.ln_absmax_quant(x_host, bits=bits, round_mode=rm, gamma_scope=gs)
+    g = host_f32(ex["gamma"]).astype(np.float32)
+    assert np.array_equal(g.view(np.uint32), np.atleast_1d(g_ref).view(np.uint32)), (g, g_ref)
     q = ex["q"].cpu().numpy()
     assert np.array_equal(q, q_ref), f"{int((q != q_ref).sum())} codes differ"
     acc_ref = orc.bitlinear_acc(q_ref, W, c_ref)
@@ -122,3 +123,65 @@ def test_stage_api_matches_single_call(bgb_gpu, M, K, N):
         assert torch.equal(ex["gamma"], taps["gamma"])
         assert torch.equal(ex["acc"], acc2)
         assert torch.equal(y1, y2)
+
+
+OPT_CASES = [(1, 4096, 11008), (1, 16416, 40), (5, 768, 260), (16, 1024, 300), (17, 512, 65), (40, 1024, 300),
+             (150, 640, 300)]
+
+
+@pytest.mark.parametrize("M,K,N", OPT_CASES)
+@pytest.mark.parametrize("rm,gs", [(1, 0), (0, 1), (1, 1)])
+def test_bitlinear_quantizer_options(bgb_gpu, orc, M, K, N, rm, gs):
+    """Round-to-nearest codes and per-token gamma through every prologue and
+    product path (fused single token, one-block prologue + GEMV, two-pass
+    prologue + GEMV, GEMM): gamma(s) and codes bit-exact, acc exact, y to 1e-5
+    of the fp64 epilogue with each token's own gamma."""
+    from bit_gemm_binarize_amd import QuantParams
+    say(f"bitlinear options round={rm} scope={gs} M={M} K={K} N={N}")
+    seed = 700 + M + K
+    W = syn.normal_f32(seed, 0, (K, N), mean=0.001, std=0.02)
+    xf = syn.normal_f32(seed, 1, (M, K))
+    xf[:, ::7] *= np.float32(1.5)                     # heavier tails, token maxima spread out
+    y, y_ref = _run(bgb_gpu, orc, W, xf, dev_f32(xf), qp=QuantParams(round_mode=rm, gamma_scope=gs))
+    check_w1a8(y, y_ref, f"round={rm} scope={gs} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M", [2, 40])
+def test_bitlinear_option_closed_forms(bgb_gpu, orc, M):
+    """Hand-derived codes: rows (-3,-1,1,3) round to (-127,-43,43,127);
+    rows (-0.7,0.7) beside them give +-95 with one gamma and +-127 with
+    their own."""
+    from bit_gemm_binarize_amd import QuantParams
+    say(f"bitlinear option closed forms M={M}")
+    K, N = 96, 40
+    x = np.empty((M, K), np.float32)
+    x[0::2] = np.tile(np.array([-3, -1, 1, 3], np.float32), K // 4)
+    x[1::2] = np.tile(np.array([-0.7, 0.7], np.float32), K // 2)
+    W = syn.normal_f32(8, 0, (K, N), mean=0.001, std=0.02)
+    P, beta, _ = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_BITNET)
+    expect = {(1, 0): ([-127, -43, 43, 127], [-95, 95]), (0, 1): ([-127, -42, 42, 127], [-127, 127]),
+              (1, 1): ([-127, -43, 43, 127], [-127, 127])}
+    for (rm, gs), (e0, e1) in expect.items():
+        _, ex = bgb_gpu.bitlinear_w1a8(dev_f32(x), P, beta, N, QuantParams(round_mode=rm, gamma_scope=gs),
+                                       want_q=True)
+        q = ex["q"].cpu().numpy()
+        assert np.array_equal(q[0::2], np.tile(np.array(e0, np.int8), (q[0::2].shape[0], K // 4))), (rm, gs)
+        assert np.array_equal(q[1::2], np.tile(np.array(e1, np.int8), (q[1::2].shape[0], K // 2))), (rm, gs)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 768, 300), (9, 768, 300), (40, 512, 200)])
+def test_stage_api_token_scope(bgb_gpu, M, K, N):
+    """The two-stage API with per-token gamma and rounding matches the single call."""
+    from bit_gemm_binarize_amd import QuantParams
+    say(f"bitlinear stage API options M={M}")
+    qp = QuantParams(round_mode=1, gamma_scope=1)
+    x = dev_f32(syn.normal_f32(650 + M, 1, (M, K)))
+    P, beta, _ = bgb_gpu.binarize_pack(dev_f32(syn.normal_f32(650 + M, 2, (K, N), mean=0.001, std=0.02)),
+                                       bgb_gpu.MODE_BITNET)
+    ws = torch.empty(bgb_gpu.workspace_bytes(bgb_gpu.OP_BITLINEAR, M, K, N), dtype=torch.uint8, device="cuda")
+    taps = bgb_gpu.bitlinear_quantize(x, qp, ws=ws, want_q=True, want_gamma=True)
+    y2, acc2 = bgb_gpu.bitlinear_matmul(M, K, P, beta, N, qp, ws=ws, want_acc=True)
+    y1, ex = bgb_gpu.bitlinear_w1a8(x, P, beta, N, qp, want_q=True, want_gamma=True, want_acc=True)
+    torch.cuda.synchronize()
+    assert taps["gamma"].shape == (M,) and torch.equal(ex["gamma"], taps["gamma"])
+    assert torch.equal(ex["q"], taps["q"]) and torch.equal(ex["acc"], acc2) and torch.equal(y1, y2)
