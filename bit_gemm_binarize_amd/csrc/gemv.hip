@@ -228,18 +228,21 @@ constexpr int kD1MaxTiles = 8;      // preloaded 16-byte sign tiles per thread (
 
 // Code of one activation, h already LayerNormed: trunc (or, rne, the nearest
 // integer, clamped) of clip(fl32(h Q_b / gamma), +-lim), lim in (Q_b - 1, Q_b).
-BGB_DEV int exact_code(float h, float qb, float gamma, float lim, bool rne) {
-    return round_code(fminf(fmaxf((h * qb) / gamma, -lim), lim), rne, int(qb) - 1);
+template <bool kRne>
+BGB_DEV int exact_code(float h, float qb, float gamma, float lim) {
+    const float v = fminf(fmaxf((h * qb) / gamma, -lim), lim);
+    if constexpr (kRne) return round_code(v, true, int(qb) - 1);
+    else return int(v);
 }
 
 // W1A8 steps per wave: NV dwords of codes per thread cover NV NW / 2 steps of
 // 512 rows, shared by KQ = NW / F waves.
 constexpr int w1a8_d1_steps(int nv, int f) { return (nv * f + 1) / 2; }
 
-template <int NV, int NW, int F, int IT, typename XT>
+template <int NV, int NW, int F, int IT, typename XT, bool kRne>
 __global__ void __launch_bounds__(NW * 64)
 bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
-                         int rne, const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
+                         const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
                          int32_t* __restrict__ acc_opt, int8_t* __restrict__ xq_opt,
                          float* __restrict__ gamma_opt) {
     constexpr int NT = NW * 64;
@@ -344,25 +347,38 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     //    A lane with a near-integer u (rare) redoes all its codes exactly.
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
     const float ucl = qb - 0.5f;
-    const bool rn = rne != 0;
-    const int qmax = int(qb) - 1;
+    constexpr bool rn = kRne;
     int codes[NV][4];
     bool slow = false;
+    if constexpr (!rn) {                               // truncation (the default): int(u) needs no clamp
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+        for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float h = v[i][c] * rs32;
-            v[i][c] = h;
-            const float u = fminf(fmaxf(h * cq, -ucl), ucl);
-            slow |= code_near_boundary(u, rn);
-            codes[i][c] = round_code(u, rn, qmax);
-        }
+            for (int c = 0; c < 4; ++c) {
+                const float h = v[i][c] * rs32;
+                v[i][c] = h;
+                const float u = fminf(fmaxf(h * cq, -ucl), ucl);
+                slow |= fabsf(u - rintf(u)) < fabsf(u) * 0x1p-20f;
+                codes[i][c] = int(u);
+            }
+    } else {                                           // rounding: boundaries at half-integers
+        const int qmax = int(qb) - 1;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float h = v[i][c] * rs32;
+                v[i][c] = h;
+                const float u = fminf(fmaxf(h * cq, -ucl), ucl);
+                slow |= code_near_boundary(u, true);
+                codes[i][c] = round_code(u, true, qmax);
+            }
+    }
     if (slow && gamma != 0.0f) {                       // gamma = 0: every h and code is 0
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) codes[i][c] = exact_code(v[i][c], qb, gamma, lim, rn);
+            for (int c = 0; c < 4; ++c) codes[i][c] = exact_code<rn>(v[i][c], qb, gamma, lim);
     }
     int sq = 0;
 #pragma unroll
@@ -454,9 +470,15 @@ template <int NV, int NW, int F, typename XT>
 static void launch_w1a8_decode1_f(int it, unsigned grid, const XT* x, int64_t K, int64_t N, int64_t TQ, double eps,
                                   float qb, float lim, int rne, const uint32_t* P, const float* beta, float* y,
                                   int32_t* acc_opt, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
-#define BGB_D1X(ITV) \
-    bitlinear_decode1_kernel<NV, NW, F, ITV, XT><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, rne, P, beta, y, \
-                                                                          acc_opt, xq_opt, gamma_opt)
+#define BGB_D1X(ITV)                                                                                             \
+    if (rne)                                                                                                     \
+        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, true><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, \
+                                                                                   beta, y, acc_opt, xq_opt,    \
+                                                                                   gamma_opt);                  \
+    else                                                                                                         \
+        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, false><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, \
+                                                                                    beta, y, acc_opt, xq_opt,   \
+                                                                                    gamma_opt)
     if constexpr (w1a8_d1_ok<NV, NW>(F, 1)) {
         if constexpr (w1a8_d1_ok<NV, NW>(F, 2)) {
             if (it == 2) {
