@@ -58,7 +58,10 @@ def _load():
     lib.oracle_bitlinear_acc.argtypes = [P, I64, I64, P, I64, ctypes.c_float, P]
     lib.oracle_bitlinear_out.argtypes = [P, I64, I64, ctypes.c_float, ctypes.c_float,
                                          ctypes.c_int, P]
-    for name in ("oracle_sign_fbi", "oracle_sign_bitnet", "oracle_fbi_alpha",
+    lib.oracle_ternary.argtypes = [P, I64, I64, ctypes.c_float, P, P]
+    lib.oracle_int8_acc.argtypes = [P, I64, I64, P, I64, P]
+    for name in ("oracle_ternary", "oracle_int8_acc",
+                 "oracle_sign_fbi", "oracle_sign_bitnet", "oracle_fbi_alpha",
                  "oracle_bitnet_scalars", "oracle_pack", "oracle_fbi_linear",
                  "oracle_ln_absmax_quant", "oracle_bitlinear_acc", "oracle_bitlinear_out"):
         getattr(lib, name).restype = ctypes.c_int
@@ -206,3 +209,36 @@ def bitlinear_out(acc: np.ndarray, beta: float, gamma, bits: int = 8) -> np.ndar
                                             bits, _ptr(ym)), "bitlinear_out")
         y[m] = ym[0]
     return y
+
+
+# ------------------------------------------------- BitNet b1.58 (ternary) ----
+
+def ternary(W: np.ndarray, eps_w: float = 1e-5):
+    """BitNet b1.58 weights ([BitNet] section 二, eq. (9)-(11)): returns
+    (T int8 [K][N] in {-1, 0, 1}, gamma_w = mean |W| as float32)."""
+    W = _f32(W)
+    K, N = W.shape
+    T = np.empty((K, N), np.int8)
+    g = np.zeros(1, np.float32)
+    _check(_load().oracle_ternary(_ptr(W), K, N, ctypes.c_float(eps_w), _ptr(T), _ptr(g)), "ternary")
+    return T, np.float32(g[0])
+
+
+def pack_ternary(T: np.ndarray) -> np.ndarray:
+    """Two sign planes in the binary packed format, one after the other: the
+    +1 plane, then the -1 plane."""
+    T = np.asarray(T)
+    return np.concatenate([pack((T > 0).astype(np.int8)), pack((T < 0).astype(np.int8))])
+
+
+def int8_acc(q: np.ndarray, T: np.ndarray) -> np.ndarray:
+    """acc[m][j] = sum_i T[i][j] q[m][i], exact."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    T = np.ascontiguousarray(T, dtype=np.int8)
+    M, K = q.shape
+    K2, N = T.shape
+    if K2 != K:
+        raise ValueError("shape mismatch")
+    acc = np.empty((M, N), np.int64)
+    _check(_load().oracle_int8_acc(_ptr(q), M, K, _ptr(T), N, _ptr(acc)), "int8_acc")
+    return acc

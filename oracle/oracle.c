@@ -277,3 +277,38 @@ int oracle_bitlinear_out(const int64_t* acc, int64_t M, int64_t N, float beta, f
         y[i] = (double)acc[i] * (double)beta * (double)gamma / Qb;
     return 0;
 }
+
+/* ------------------------------------------------- BitNet b1.58 (ternary) -- */
+
+/* [BitNet] section 二, eq. (9)-(11). The page leaves the rounding of round()
+ * and the value of eps open; round to nearest even is taken, eps is an input. */
+int oracle_ternary(const float* W, int64_t K, int64_t N, float eps_w, int8_t* T, float* gamma_w) {
+    if (!W || !T || !gamma_w || K <= 0 || N <= 0 || !(eps_w >= 0.0f)) return -1;
+    double a = 0.0;
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t j = 0; j < N; ++j) a += fabs((double)W[i * N + j]);
+    const float g = (float)(a / ((double)K * (double)N));   /* eq. (11) */
+    const float den = g + eps_w;                              /* gamma + eps in fp32 */
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            float t = W[i * N + j] / den;                     /* eq. (9), fp32 quotient */
+            float r = nearbyintf(t);                          /* round, ties to even */
+            T[i * N + j] = (int8_t)(r > 1.0f ? 1 : (r < -1.0f ? -1 : (int)r));   /* eq. (10) clip */
+        }
+    *gamma_w = g;
+    return 0;
+}
+
+int oracle_int8_acc(const int8_t* q, int64_t M, int64_t K, const int8_t* T, int64_t N, int64_t* acc) {
+    if (!q || !T || !acc || M < 0 || K < 0 || N < 0) return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t* row = acc + m * N;
+        for (int64_t j = 0; j < N; ++j) row[j] = 0;
+        for (int64_t i = 0; i < K; ++i) {
+            const int64_t qi = q[m * K + i];
+            const int8_t* trow = T + i * N;
+            for (int64_t j = 0; j < N; ++j) row[j] += (int64_t)trow[j] * qi;
+        }
+    }
+    return 0;
+}

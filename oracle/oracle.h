@@ -67,6 +67,16 @@ int oracle_ln_absmax_quant(const float* x, int64_t M, int64_t K, double ln_eps, 
 /* BitLinear integer product acc[m][j] = sum_i sign(W_ij - c) * q[m][i] (exact). */
 int oracle_bitlinear_acc(const int8_t* q, int64_t M, int64_t K, const float* W, int64_t N,
                          float c, int64_t* acc);
+/* BitNet b1.58 ternary weights ([BitNet] section 二, eq. (9)-(11)):
+ * gamma_w = mean |W| (fp64 sum rounded once to fp32), then
+ * T_ij = RoundClip(W_ij / (gamma_w + eps_w), -1, 1): the divisor and the
+ * quotient in fp32, round to nearest even, clip to [-1, 1]. */
+int oracle_ternary(const float* W, int64_t K, int64_t N, float eps_w, int8_t* T, float* gamma_w);
+
+/* Integer product acc[m][j] = sum_i T_ij * q[m][i] for int8 weights T [K][N]
+ * (the ternary BitLinear product), exact in int64, i ascending. */
+int oracle_int8_acc(const int8_t* q, int64_t M, int64_t K, const int8_t* T, int64_t N, int64_t* acc);
+
 /* BitLinear output y = acc * beta * gamma / Q_b in fp64 ([BitNet] eq. (7)). */
 int oracle_bitlinear_out(const int64_t* acc, int64_t M, int64_t N, float beta, float gamma,
                          int bits, double* y);

@@ -391,3 +391,75 @@ def test_bitlinear_out_per_token_gamma(orc):
     acc = np.array([[3, -5, 0], [7, 1, -2]], np.int64)
     y = orc.bitlinear_out(acc, 0.25, np.array([0.5, 2.0], np.float32))
     assert np.array_equal(y, np.array([[3, -5, 0], [7 * 4, 4, -8]], np.float64) * 0.25 * 0.5 / 128)
+
+
+# ------------------------------------------------- BitNet b1.58 (ternary) --
+
+def test_ternary_closed_form(orc):
+    """W = c * pattern, pattern in {-1, 0, 1} with a fraction f of nonzeros:
+    gamma_w = c f and W / gamma_w = pattern / f, which rounds and clips back
+    to the pattern (|1/f| >= 1)."""
+    rng = syn.rng_for(41, 0)
+    for f_keep in (0.55, 0.8, 1.0):
+        K, N = 96, 7
+        pat = np.where(rng.random((K, N)) < f_keep, np.where(rng.random((K, N)) < 0.5, -1, 1), 0).astype(np.int8)
+        pat[0, 0] = 1                                             # at least one nonzero
+        c = np.float32(0.0371)
+        T, g = orc.ternary(pat.astype(np.float32) * c)
+        assert np.array_equal(T, pat)
+        f = np.count_nonzero(pat) / pat.size
+        assert abs(float(g) - float(c) * f) <= 1e-6 * float(c)
+
+
+def test_ternary_round_half_to_even(orc):
+    """The tie rule of round() (eq. (10)): with eps = 0 and |W| taking the
+    values 0.5 and 1.5 equally often, gamma_w = 1 exactly; W / gamma_w = 0.5
+    rounds to 0 under ties-to-even (half away from zero would give 1), 1.5
+    rounds to 2 and clips to 1."""
+    w = np.array([0.5] * 16 + [1.5] * 16 + [-0.5] * 16 + [-1.5] * 16, np.float32).reshape(64, 1)
+    T, g = orc.ternary(np.repeat(w, 3, axis=1), eps_w=0.0)
+    assert g == 1.0
+    assert np.array_equal(T[:, 0], np.array([0] * 16 + [1] * 16 + [0] * 16 + [-1] * 16, np.int8))
+
+
+def test_ternary_exact_brute_force(orc):
+    """RoundClip(W / (gamma + eps), -1, 1) against exact rationals: gamma_w from
+    an exact sum rounded once, the divisor rounded to fp32, the quotient exact;
+    entries whose exact quotient sits within 2^-20 of a half-integer are
+    skipped (the fp32 quotient may round either way there)."""
+    W = syn.normal_f32(42, 0, (64, 9), std=0.02)
+    W[3, 2] = 0.0
+    T, g = orc.ternary(W, eps_w=1e-5)
+    n = W.size
+    g_exact = sum(Fraction(float(abs(v))) for v in W.ravel()) / n
+    assert g == frac_to_f32(g_exact)
+    den = Fraction(float(np.float32(g) + np.float32(1e-5)))
+    checked = 0
+    for (i, j), v in np.ndenumerate(W):
+        t = Fraction(float(v)) / den
+        frac_part = abs(t - int(t))
+        if abs(frac_part - Fraction(1, 2)) < Fraction(1, 2 ** 20):
+            continue
+        r = round(t)                                              # Fraction: half to even
+        assert T[i, j] == max(-1, min(1, r)), (i, j, float(t))
+        checked += 1
+    assert checked > n - 3 and T[3, 2] == 0
+
+
+def test_ternary_pack_and_product(orc):
+    """Two planes in the packed format (+1 plane, then -1 plane) read back by
+    the independent reader; the int8 product against an int64 matmul."""
+    rng = syn.rng_for(43, 0)
+    K, N, M = 160, 11, 3
+    T = rng.integers(-1, 2, size=(K, N)).astype(np.int8)
+    P2 = orc.pack_ternary(T)
+    half = P2.size // 2
+    pos = unpack_format(P2[:half], K, N)
+    neg = unpack_format(P2[half:], K, N)
+    assert not np.any((pos > 0) & (neg > 0))
+    assert np.array_equal((pos > 0).astype(np.int8) - (neg > 0).astype(np.int8), T)
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    acc = orc.int8_acc(q, T)
+    assert np.array_equal(acc, q.astype(np.int64) @ T.astype(np.int64))
+    assert np.all(orc.int8_acc(q, np.zeros((K, N), np.int8)) == 0)
+    assert np.array_equal(orc.int8_acc(q, np.ones((K, N), np.int8))[:, 0], q.astype(np.int64).sum(1))
