@@ -18,8 +18,9 @@ from dataclasses import dataclass
 from typing import Optional
 
 __all__ = [
-    "load", "lib_path", "packed_bytes", "workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
-    "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
+    "load", "lib_path", "packed_bytes", "MODE_TERNARY", "workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
+    "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bitlinear158_w1a8", "bitlinear158_matmul",
+    "OP_BITLINEAR158", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
     "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M", "W1A16_DECODE_MAX_M",
     "ROUND_TRUNC", "ROUND_RNE", "GAMMA_TENSOR", "GAMMA_TOKEN",
 ]
@@ -28,13 +29,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbgb.so")
 
 BGB_F32, BGB_F16, BGB_BF16 = 0, 1, 2
-MODE_FBI, MODE_BITNET = 0, 1
-OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR = 0, 1, 2, 3
+MODE_FBI, MODE_BITNET, MODE_TERNARY = 0, 1, 2
+OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR, OP_BITLINEAR158 = 0, 1, 2, 3, 4
 GEMV_MAX_M = 32          # BitLinear: M <= 32 runs the decode kernels, above: the MFMA GEMM
 W1A16_DECODE_MAX_M = 64  # FBI-linear: M <= 64 runs the decode kernels, above: the MFMA GEMM
 
 EXPORTS = ("bgb_packed_bytes", "bgb_workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
-           "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bgb_status_string",
+           "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bitlinear158_w1a8",
+           "bitlinear158_matmul", "bgb_status_string",
            "bgb_last_hip_error", "bgb_version")
 
 
@@ -96,6 +98,10 @@ def load():
     lib.bitlinear_quantize.restype = I
     lib.bitlinear_matmul.argtypes = [I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, SZ, P]
     lib.bitlinear_matmul.restype = I
+    lib.bitlinear158_w1a8.argtypes = lib.bitlinear_w1a8.argtypes
+    lib.bitlinear158_w1a8.restype = I
+    lib.bitlinear158_matmul.argtypes = lib.bitlinear_matmul.argtypes
+    lib.bitlinear158_matmul.restype = I
     lib.bgb_status_string.argtypes = [I]
     lib.bgb_status_string.restype = ctypes.c_char_p
     lib.bgb_last_hip_error.argtypes = []
@@ -153,13 +159,15 @@ def _workspace(op, M, K, N, ws, device):
 
 def binarize_pack(W, mode: int = MODE_FBI, alpha_dtype=None, *, P=None, alpha=None, beta=None, centre=None,
                   ws=None, stream=None):
-    """W: float32 [K][N] on the GPU. Returns (P, alpha) for FBI or (P, beta, centre) for BitNet.
+    """W: float32 [K][N] on the GPU. Returns (P, alpha) for FBI or (P, beta, centre) for BitNet
+    and ternary (b1.58; beta = mean |W|, P holds the +1 plane then the -1 plane).
     P is an int32 tensor holding the uint32 words of the packed format."""
     torch = _torch()
     K, N = W.shape
     dev = W.device
     if P is None:
-        P = torch.empty(max(packed_bytes(K, N) // 4, 4), dtype=torch.int32, device=dev)
+        planes = 2 if mode == MODE_TERNARY else 1
+        P = torch.empty(max(planes * packed_bytes(K, N) // 4, 4), dtype=torch.int32, device=dev)
     op = OP_PACK_FBI if mode == MODE_FBI else OP_PACK_BITNET
     ws = _workspace(op, 0, K, N, ws, dev)
     if mode == MODE_FBI:
@@ -191,7 +199,7 @@ def fbi_linear_w1a16(x, P, alpha, N: int, y_dtype=None, *, y=None, ws=None, stre
 
 
 def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=None, want_q=False,
-                   want_gamma=False, want_acc=False, ws=None, stream=None):
+                   want_gamma=False, want_acc=False, ws=None, stream=None, _ternary=False):
     """x: f32/bf16 [M][K]; P: packed signs of W - c; beta: device scalar.
     Returns y, or (y, extras) with the requested taps (q, gamma, acc)."""
     torch = _torch()
@@ -204,9 +212,10 @@ def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=No
     q = torch.empty((M, K), dtype=torch.int8, device=dev) if want_q else None
     g = torch.empty(max(ng, 4), dtype=torch.float32, device=dev) if want_gamma else None
     acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
-    ws = _workspace(OP_BITLINEAR, M, K, N, ws, dev)
+    ws = _workspace(OP_BITLINEAR158 if _ternary else OP_BITLINEAR, M, K, N, ws, dev)
     cqp = qp.c()
-    _check(load().bitlinear_w1a8(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y),
+    fn = load().bitlinear158_w1a8 if _ternary else load().bitlinear_w1a8
+    _check(fn(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y),
                                  _ptr(q), _ptr(g), _ptr(acc), _ptr(ws), ws.numel(), _stream(stream)))
     if not (want_q or want_gamma or want_acc):
         return y
@@ -236,7 +245,7 @@ def bitlinear_quantize(x, qp: Optional[QuantParams] = None, *, ws, N_max: int = 
 
 
 def bitlinear_matmul(M: int, K: int, P, beta, N: int, qp: Optional[QuantParams] = None, *, ws, y=None,
-                     want_acc=False, stream=None):
+                     want_acc=False, stream=None, _ternary=False):
     """Product + epilogue from the codes a previous bitlinear_quantize left in `ws`."""
     torch = _torch()
     if y is None:
@@ -244,6 +253,18 @@ def bitlinear_matmul(M: int, K: int, P, beta, N: int, qp: Optional[QuantParams] 
     acc = torch.empty((M, N), dtype=torch.int32, device=ws.device) if want_acc else None
     qp = qp or QuantParams()
     cqp = qp.c()
-    _check(load().bitlinear_matmul(M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y), _ptr(acc), _ptr(ws),
+    fn = load().bitlinear158_matmul if _ternary else load().bitlinear_matmul
+    _check(fn(M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y), _ptr(acc), _ptr(ws),
                                    ws.numel(), _stream(stream)))
     return (y, acc) if want_acc else y
+
+
+def bitlinear158_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, **kw):
+    """BitNet b1.58 forward: P holds the two ternary planes from
+    binarize_pack(MODE_TERNARY), beta its mean |W|. Same taps as bitlinear_w1a8."""
+    return bitlinear_w1a8(x, P, beta, N, qp, _ternary=True, **kw)
+
+
+def bitlinear158_matmul(M: int, K: int, P, beta, N: int, qp: Optional[QuantParams] = None, **kw):
+    """Ternary product + epilogue from the codes a previous bitlinear_quantize left in `ws`."""
+    return bitlinear_matmul(M, K, P, beta, N, qp, _ternary=True, **kw)

@@ -48,6 +48,7 @@ size_t bgb_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
         case BGB_OP_PACK_BITNET: return bgb::PackBitnetWs::make().total;
         case BGB_OP_FBI_LINEAR: return bgb::FbiLinearWs::make(M, K, N).total;
         case BGB_OP_BITLINEAR: return bgb::BitlinearWs::make(M, K, N).total;
+        case BGB_OP_BITLINEAR158: return bgb::BitlinearWs::make(M, K, N, true).total;
         default: return 0;
     }
 }
@@ -56,14 +57,16 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P, v
                   float* beta, float* centre, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_shape(0, K, N);
     if (rc) return rc;
-    if (mode != BGB_MODE_FBI && mode != BGB_MODE_BITNET) return BGB_EUNSUPPORTED;
+    if (mode != BGB_MODE_FBI && mode != BGB_MODE_BITNET && mode != BGB_MODE_TERNARY) return BGB_EUNSUPPORTED;
     if (mode == BGB_MODE_FBI && alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
     if (N == 0) return BGB_OK;                    // empty: nothing is read or written
     if (!W || !P || !aligned16(W) || !aligned16(P)) return BGB_EINVAL;
     if (mode == BGB_MODE_FBI) {
         if (!alpha || !aligned16(alpha)) return BGB_EINVAL;
-    } else {
+    } else if (mode == BGB_MODE_BITNET) {
         if (!beta || !centre || !aligned16(beta) || !aligned16(centre)) return BGB_EINVAL;
+    } else {                                      // ternary: centre optional
+        if (!beta || !aligned16(beta) || (centre && !aligned16(centre))) return BGB_EINVAL;
     }
     const int op = mode == BGB_MODE_FBI ? BGB_OP_PACK_FBI : BGB_OP_PACK_BITNET;
     const size_t need = bgb_workspace_bytes(op, 0, K, N);
@@ -140,9 +143,13 @@ int bitlinear_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const b
                                        static_cast<hipStream_t>(stream)));
 }
 
-int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
-                     const bgb_quant_params* qp, float* y, int32_t* acc_opt, void* ws, size_t ws_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Product + epilogue from the codes in the workspace (binary or ternary weights).
+int matmul_impl(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta, const bgb_quant_params* qp,
+                float* y, int32_t* acc_opt, void* ws, size_t ws_bytes, void* stream, bool tern) {
     int rc = check_shape(M, K, N);
     if (rc) return rc;
     bgb_quant_params p;
@@ -152,7 +159,7 @@ int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const f
     if (!P || !beta || !y || !aligned16(P) || !aligned16(y)) return BGB_EINVAL;
     if (reinterpret_cast<uintptr_t>(beta) & 3u) return BGB_EINVAL;
     if (acc_opt && !aligned16(acc_opt)) return BGB_EINVAL;
-    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N);
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N, tern);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int8_t* q = reinterpret_cast<const int8_t*>(carve(ws, lay.q));
@@ -164,14 +171,15 @@ int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const f
                                : reinterpret_cast<const float*>(carve(ws, lay.gamma));
     const int gstride = token ? 3 : 0;
     if (M <= bgb::kGemvMaxM)
-        return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, gstride, beta, qb, M, K, N, P, y, acc_opt, s));
+        return finish(bgb::launch_w1a8_gemv(q, rowsum, gamma, gstride, beta, qb, M, K, N, P, y, acc_opt, tern, s));
     return finish(bgb::launch_w1a8_gemm(q, rowsum, gamma, gstride, beta, qb, M, K, N, P, y, acc_opt,
-                                        carve(ws, lay.part), s));
+                                        carve(ws, lay.part), tern, s));
 }
 
-int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
-                   const float* beta, const bgb_quant_params* qp, float* y, int8_t* xq_opt, float* gamma_opt,
-                   int32_t* acc_opt, void* ws, size_t ws_bytes, void* stream) {
+// Prologue + product (one fused launch for a single token).
+int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
+                 const bgb_quant_params* qp, float* y, int8_t* xq_opt, float* gamma_opt, int32_t* acc_opt, void* ws,
+                 size_t ws_bytes, void* stream, bool tern) {
     int rc = check_shape(M, K, N);
     if (rc) return rc;
     if (x_dtype != BGB_F32 && x_dtype != BGB_BF16) return BGB_EUNSUPPORTED;
@@ -184,17 +192,45 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, 
     if ((reinterpret_cast<uintptr_t>(beta) & 3u) || (gamma_opt && (reinterpret_cast<uintptr_t>(gamma_opt) & 3u)))
         return BGB_EINVAL;
     if ((xq_opt && !aligned16(xq_opt)) || (acc_opt && !aligned16(acc_opt))) return BGB_EINVAL;
-    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N);
+    const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N, tern);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     if (M == 1 && bgb::w1a8_decode1_supported(K)) {
         // one token: its gamma is the tensor's, whatever the scope
         return finish(bgb::launch_w1a8_decode1(x, x_dtype == BGB_BF16, K, N, p.ln_eps, qb, lim,
-                                               p.round_mode == BGB_ROUND_RNE, P, beta, y, acc_opt,
-                                               xq_opt, gamma_opt, static_cast<hipStream_t>(stream)));
+                                               p.round_mode == BGB_ROUND_RNE, P, beta, y, acc_opt, xq_opt, gamma_opt,
+                                               tern, static_cast<hipStream_t>(stream)));
     }
     rc = bitlinear_quantize(x, x_dtype, M, K, qp, xq_opt, gamma_opt, ws, ws_bytes, stream);
     if (rc) return rc;
-    return bitlinear_matmul(M, K, N, P, beta, qp, y, acc_opt, ws, ws_bytes, stream);
+    return matmul_impl(M, K, N, P, beta, qp, y, acc_opt, ws, ws_bytes, stream, tern);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
+                     const bgb_quant_params* qp, float* y, int32_t* acc_opt, void* ws, size_t ws_bytes,
+                     void* stream) {
+    return matmul_impl(M, K, N, P, beta, qp, y, acc_opt, ws, ws_bytes, stream, false);
+}
+
+int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                   const float* beta, const bgb_quant_params* qp, float* y, int8_t* xq_opt, float* gamma_opt,
+                   int32_t* acc_opt, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(x, x_dtype, M, K, N, P, beta, qp, y, xq_opt, gamma_opt, acc_opt, ws, ws_bytes, stream, false);
+}
+
+int bitlinear158_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
+                        const bgb_quant_params* qp, float* y, int32_t* acc_opt, void* ws, size_t ws_bytes,
+                        void* stream) {
+    return matmul_impl(M, K, N, P, beta, qp, y, acc_opt, ws, ws_bytes, stream, true);
+}
+
+int bitlinear158_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                      const float* beta, const bgb_quant_params* qp, float* y, int8_t* xq_opt, float* gamma_opt,
+                      int32_t* acc_opt, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(x, x_dtype, M, K, N, P, beta, qp, y, xq_opt, gamma_opt, acc_opt, ws, ws_bytes, stream, true);
 }
 
 const char* bgb_status_string(int status) {

@@ -32,23 +32,27 @@ struct PackFbiWs {          // fp64 partial |W| sums per (tile, column)
 };
 
 constexpr int kBitnetReduceBlocks = 1024;
-struct PackBitnetWs {       // fp64 (sum W, sum |W|) per reduction block
-    size_t partial, total;
+struct PackBitnetWs {       // fp64 (sum W, sum |W|) per reduction block, then a float scratch (mean W
+    size_t partial, scratch, total;   //  when the caller does not ask for it)
     static PackBitnetWs make() {
         PackBitnetWs w{};
         w.partial = 0;
-        w.total = align256(size_t(kBitnetReduceBlocks) * 2 * sizeof(double));
+        w.scratch = align256(size_t(kBitnetReduceBlocks) * 2 * sizeof(double));
+        w.total = w.scratch + 256;
         return w;
     }
 };
+
+// BitNet b1.58 weights: RoundClip(W / (mean|W| + eps), -1, 1) with this eps.
+constexpr float kTernaryEps = 1e-5f;
 
 // GEMM launch plan (a pure function of the shape): token fragments per wave
 // (BM = 16 nn), K splits and stages per split, tile grid.
 struct GemmPlan {
     int nn, nw, splits, per, T, ntm, ntj;   // nw waves of 64 columns per block
 };
-GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8);
-size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8);   // [splits][M][N] x 4 bytes, or 0
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8, bool tern);
+size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8, bool tern);   // [splits][M][N] x 4 B, or 0
 
 // Chunked W1A16 decode plan (a pure function of the shape): tokens per block
 // 16 tf, tiles per wave and chunk tpw, fragments per block fb, K splits (each
@@ -71,7 +75,7 @@ struct FbiLinearWs {        // decode: split-K sums (if any); GEMM: interleaved 
             return w;
         }
         w.part = align256(size_t(M) * size_t(padded_k(K)) * 2);
-        w.total = w.part + gemm_partial_bytes(M, K, N, false);
+        w.total = w.part + gemm_partial_bytes(M, K, N, false, false);
         return w;
     }
 };
@@ -79,14 +83,15 @@ struct FbiLinearWs {        // decode: split-K sums (if any); GEMM: interleaved 
 struct BitlinearWs {
     size_t stats, gamma, rowsum, q, part, total;
     // N = 0: the prologue's regions only (what bitlinear_quantize touches)
-    static BitlinearWs make(int64_t M, int64_t K, int64_t N) {
+    // tern: ternary weights (their GEMM plan, hence split partials, differ)
+    static BitlinearWs make(int64_t M, int64_t K, int64_t N, bool tern = false) {
         BitlinearWs w{};
         w.stats = 0;                                               // float [M][3] mu32, rstd32, rowmax
         w.gamma = w.stats + align256((size_t(M) * 3 + size_t(M + 3) / 4) * sizeof(float));  // + block maxima
         w.rowsum = w.gamma + 256;                                  // int32 [M]
         w.q = w.rowsum + align256(size_t(M) * sizeof(int32_t));    // int8 [M][Kp], layout per path
         w.part = w.q + align256(size_t(M) * size_t(padded_k(K)));  // int32 split-K partials (GEMM)
-        w.total = w.part + (M > kGemvMaxM && N > 0 ? gemm_partial_bytes(M, K, N, true) : 0);
+        w.total = w.part + (M > kGemvMaxM && N > 0 ? gemm_partial_bytes(M, K, N, true, tern) : 0);
         return w;
     }
 };
@@ -111,13 +116,14 @@ hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K
 
 hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             int gstride, const float* beta, float qb, int64_t M, int64_t K,
-                            int64_t N, const uint32_t* P, float* y, int32_t* acc_opt, hipStream_t s);
+                            int64_t N, const uint32_t* P, float* y, int32_t* acc_opt, int tern,
+                            hipStream_t s);
 
 // Single-token fused kernels (prologue / activation staging inside the GEMV).
 bool w1a8_decode1_supported(int64_t K);
 hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
                                int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt,
-                               int8_t* xq_opt, float* gamma_opt, hipStream_t s);
+                               int8_t* xq_opt, float* gamma_opt, int tern, hipStream_t s);
 bool w1a16_decode1_supported(int64_t K);
 // 2 <= M <= 16 tokens staged in LDS by every block (M (Kp + 8) 2 bytes <= 140 KB)
 bool w1a16_decodem_supported(int64_t M, int64_t K);
@@ -137,6 +143,6 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             int gstride, const float* beta, float qb, int64_t M, int64_t K,
                             int64_t N, const uint32_t* P, float* y, int32_t* acc_opt, void* part,
-                            hipStream_t s);
+                            int tern, hipStream_t s);
 
 }  // namespace bgb

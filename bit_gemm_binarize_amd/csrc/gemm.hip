@@ -135,13 +135,14 @@ constexpr double kLaunchUs = 2.0;
 constexpr int kSlots = 512;         // resident blocks: 2 per CU on 256 CUs
 }  // namespace
 
-GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8) {
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8, bool tern) {
     const int T = int(w1a8 ? tiles_per_col(K) : 2 * tiles_per_col(K));
     const int ntj = int((N + 255) / 256);
     GemmPlan best{};
     best.nw = 4;
     double best_t = 1e300;
     for (int nn : {8, 4}) {
+        if (tern && nn == 8) continue;     // ternary: two accumulator sets, 64-token tiles only
         const int ntm = int((M + 16 * nn - 1) / (16 * nn));
         const int64_t tiles = int64_t(ntm) * ntj;
         const double stage = nn == 8 ? 1.0 : 0.6;
@@ -168,8 +169,8 @@ GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, bool w1a8) {
     return best;
 }
 
-size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8) {
-    const GemmPlan p = gemm_plan(M, K, N, w1a8);
+size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8, bool tern) {
+    const GemmPlan p = gemm_plan(M, K, N, w1a8, tern);
     return p.splits > 1 ? align256(size_t(p.splits) * size_t(M) * size_t(N) * 4) : 0;
 }
 
@@ -192,6 +193,7 @@ struct GemmArgs {
     const float* beta;
     float qb;
     int32_t* acc_opt;
+    int tern;                  // ternary weights: the raw sum is already sum t q (no 2 s - rowsum)
     // raw sums per split when the K range is split: [splits][M][N]
     void* part;
 };
@@ -223,10 +225,10 @@ BGB_DEV void store_out16(void* y, int y_dtype, int64_t o, const float (&v)[4], b
 
 BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& s, bool full, int64_t jb) {
     const float scale = (a.beta[0] * a.gamma[m * a.gstride]) / a.qb;
-    const int32_t rs = a.rowsum[m];
+    const int32_t rs = a.tern ? 0 : a.rowsum[m];
     i32x4_t v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = 2 * s[i] - rs;
+    for (int i = 0; i < 4; ++i) v[i] = a.tern ? s[i] : 2 * s[i] - rs;   // binary: 2 sum b q - sum q
     float* y = static_cast<float*>(a.y);
     if (full) {
         *reinterpret_cast<f32x4_t*>(y + o) =
@@ -242,15 +244,19 @@ BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& 
     }
 }
 
-// NN token fragments per wave (BM = 16 NN); kW1A8 selects the int8 path.
-template <bool kW1A8, bool kF16, int NN, int NW>
+// NN token fragments per wave (BM = 16 NN); kW1A8 selects the int8 path;
+// kTern (int8 path only) takes ternary weights as two sign planes (+1 plane,
+// then -1 plane, each in the binary format) and keeps two accumulator sets.
+template <bool kW1A8, bool kF16, int NN, int NW, bool kTern = false>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a) {
+    static_assert(!kTern || kW1A8, "ternary weights take the int8 path");
     constexpr int BM = 16 * NN;
     constexpr int BJ = 64 * NW;                 // 64 columns per wave
     constexpr int kStage = BM * 128;            // bytes of one activation stage
     constexpr int kWTileBytes = BJ * 16;        // one 128-row sign tile of the block's columns
+    constexpr int kPlanes = kTern ? 2 : 1;
     constexpr int kXDma = BM / (8 * NW);        // activation DMA operations per thread per stage
-    constexpr int kOps = kXDma + 1;             // + the sign tile
+    constexpr int kOps = kXDma + kPlanes;       // + the sign tile(s)
     using acc_t = std::conditional_t<kW1A8, i32x4_t, f32x4_t>;
     using opd_t = std::conditional_t<kW1A8, i32x4_t, u32x4_t>;
     constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;
@@ -259,10 +265,10 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl0[kWTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl1[kWTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl2[kWTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t wl3[kWTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t wl0[kWTileBytes * kPlanes];
+    __shared__ __attribute__((aligned(1024))) uint8_t wl1[kWTileBytes * kPlanes];
+    __shared__ __attribute__((aligned(1024))) uint8_t wl2[kWTileBytes * kPlanes];
+    __shared__ __attribute__((aligned(1024))) uint8_t wl3[kWTileBytes * kPlanes];
     uint8_t* const lds[kRing] = {lds0, lds1, lds2, lds3};
     uint8_t* const wls[kRing] = {wl0, wl1, wl2, wl3};
 
@@ -295,6 +301,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
         for (int i = 0; i < kXDma; ++i) dma16(src[i] + int64_t(s) * 128, lds[B] + (NW * i + wave) * 1024);
         const int64_t tq = kW1A8 ? s : (s >> 1);
         dma16(wsrc + tq * N * 16, wls[B] + wave * 1024);
+        if constexpr (kTern) dma16(wsrc + (int64_t(a.T) + tq) * N * 16, wls[B] + kWTileBytes + wave * 1024);
     };
 
     // B-operand byte offsets in a stage (token row 16n + r) and this lane's sign word
@@ -312,15 +319,21 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
     }
     const int wshift = 4 * (g & 1);
 
-    acc_t acc[4][NN];
+    acc_t acc[4][NN], accn[kTern ? 4 : 1][kTern ? NN : 1];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int n = 0; n < NN; ++n) acc[f][n] = acc_t{0, 0, 0, 0};
+    if constexpr (kTern) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int n = 0; n < NN; ++n) accn[f][n] = acc_t{0, 0, 0, 0};
+    }
 
     // Operands of the next MFMA group, carried between steps: the sign words
     // (shifted for W1A16) and the v = 0 B fragments of the stage.
-    uint32_t X[4];
+    uint32_t X[4], Xn[kTern ? 4 : 1];
     opd_t b0[NN];
     auto load_head = [&](int rel, int B) {
         const int wb = kW1A8 ? wbyte : wbyte + 8 * ((s0 + rel) & 1);
@@ -328,11 +341,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
         for (int f = 0; f < 4; ++f) {
             const uint32_t w = *reinterpret_cast<const uint32_t*>(wls[B] + wb + 256 * f);
             X[f] = kW1A8 ? w : (w >> wshift);
+            if constexpr (kTern) Xn[f] = *reinterpret_cast<const uint32_t*>(wls[B] + kWTileBytes + wb + 256 * f);
         }
 #pragma unroll
         for (int n = 0; n < NN; ++n) b0[n] = *reinterpret_cast<const opd_t*>(lds[B] + n * 2048 + boff0);
     };
-    auto mfma_half = [&](int v, const uint32_t (&Xv)[4], const opd_t (&b)[NN]) {
+    auto mfma_half = [&](int v, const uint32_t (&Xv)[4], const uint32_t (&Xnv)[kTern ? 4 : 1], const opd_t (&b)[NN]) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
             if constexpr (kW1A8) {
@@ -345,6 +359,17 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
 #pragma unroll
                 for (int n = 0; n < NN; ++n)
                     acc[f][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b[n], acc[f][n], 0, 0, 0);
+                if constexpr (kTern) {         // the -1 plane into its own accumulators
+                    const uint32_t wn = Xnv[f];
+                    i32x4_t an;
+                    an.x = int((wn >> (4 * v + 0)) & 0x01010101u);
+                    an.y = int((wn >> (4 * v + 1)) & 0x01010101u);
+                    an.z = int((wn >> (4 * v + 2)) & 0x01010101u);
+                    an.w = int((wn >> (4 * v + 3)) & 0x01010101u);
+#pragma unroll
+                    for (int n = 0; n < NN; ++n)
+                        accn[f][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an, b[n], accn[f][n], 0, 0, 0);
+                }
             } else {
                 u32x4_t av;   // (~(X << s) & 0x80008000) | one: sign bits of rows 4u+e, 4u+e+16
                 av.x = __builtin_amdgcn_bitop3_b32(Xv[f] << (15 - 8 * v), 0x80008000u, kOne, 0xAE);
@@ -367,17 +392,21 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
         opd_t b1[NN];
 #pragma unroll
         for (int n = 0; n < NN; ++n) b1[n] = *reinterpret_cast<const opd_t*>(lds[B] + n * 2048 + boff1);
-        uint32_t Xc[4];
+        uint32_t Xc[4], Xnc[kTern ? 4 : 1];
 #pragma unroll
         for (int f = 0; f < 4; ++f) Xc[f] = X[f];
-        mfma_half(0, Xc, b0);
+        if constexpr (kTern) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) Xnc[f] = Xn[f];
+        }
+        mfma_half(0, Xc, Xnc, b0);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt_lgkm0<2 * kOps>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue(rel + 4, B);
         load_head(rel + 1, (B + 1) % kRing);
-        mfma_half(1, Xc, b1);
+        mfma_half(1, Xc, Xnc, b1);
     };
 
     issue(0, 0);
@@ -399,6 +428,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
     if (rel + 2 < ns) step(rel + 2, std::integral_constant<int, 2>{});
     wait_vmcnt<0>();                            // no LDS DMA may outlive the block
 
+    if constexpr (kTern) {                      // sum t q = sum over the +1 plane - sum over the -1 plane
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int n = 0; n < NN; ++n) acc[f][n] -= accn[f][n];
+    }
     // Epilogue: lane (g, r) holds columns jb..jb+3 of token 16n + r.
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -485,6 +520,16 @@ static hipError_t launch_gemm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
     a.ntj = p.ntj;
     a.ntiles = ntiles;
     const dim3 grid(unsigned(xcd_grid(ntiles)), unsigned(p.splits));
+    if constexpr (kW1A8) {
+        if (a.tern) {                           // the plan gives 64-token tiles
+            gemm_kernel<true, false, 4, 4, true><<<grid, 256, 0, s>>>(a);
+            if (p.splits > 1) {
+                const int64_t n = a.M * ((a.N + 3) / 4);
+                splitk_reduce_kernel<true><<<unsigned((n + 255) / 256), 256, 0, s>>>(a, p.splits);
+            }
+            return hipGetLastError();
+        }
+    }
     if (p.nw == 8) gemm_kernel<kW1A8, kF16, 8, 8><<<grid, 512, 0, s>>>(a);
     else if (p.nn == 8) gemm_kernel<kW1A8, kF16, 8, 4><<<grid, 256, 0, s>>>(a);
     else gemm_kernel<kW1A8, kF16, 4, 4><<<grid, 256, 0, s>>>(a);
@@ -512,7 +557,7 @@ hipError_t launch_w1a16_splitk_reduce(const float* part, int splits, int64_t M, 
 
 hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
                              const void* alpha, int alpha_f16, void* y, int y_dtype, void* part, hipStream_t s) {
-    const GemmPlan p = gemm_plan(M, K, N, false);
+    const GemmPlan p = gemm_plan(M, K, N, false, false);
     GemmArgs a{};
     a.act = reinterpret_cast<const uint8_t*>(xi);
     a.row_bytes = padded_k(K) * 2;
@@ -530,8 +575,8 @@ hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma, int gstride,
                             const float* beta, float qb,
                             int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y, int32_t* acc_opt,
-                            void* part, hipStream_t s) {
-    const GemmPlan p = gemm_plan(M, K, N, true);
+                            void* part, int tern, hipStream_t s) {
+    const GemmPlan p = gemm_plan(M, K, N, true, tern != 0);
     GemmArgs a{};
     a.act = reinterpret_cast<const uint8_t*>(q);
     a.row_bytes = padded_k(K);
@@ -545,6 +590,7 @@ hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float*
     a.qb = qb;
     a.y = y;
     a.acc_opt = acc_opt;
+    a.tern = tern;
     a.part = p.splits > 1 ? part : nullptr;
     return launch_gemm<true, false>(a, p, s);
 }

@@ -151,24 +151,34 @@ inline int gen_steps(int64_t TQ) {
     return steps <= kGenWaves ? 1 : (steps <= 2 * kGenWaves ? 2 : 4);
 }
 
-template <int TF, int GS>
+// kTern: ternary weights as two planes (+1 at P, -1 at Pn); the product is
+// then sum_plus - sum_minus and needs no code row sums.
+template <int TF, int GS, bool kTern>
 __global__ void __launch_bounds__(kGenWaves * 64)
 gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsum, const float* __restrict__ gamma,
                  int gstride, const float* __restrict__ beta, float qb, int M, int64_t N, int64_t TQ,
                  const uint32_t* __restrict__ P, float* __restrict__ y, int32_t* __restrict__ acc_opt) {
     __shared__ i32x4_t red[kGenWaves][TF][64];
+    const uint32_t* Pn = P + TQ * N * 4;                // -1 plane (ternary)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int64_t j0 = int64_t(blockIdx.x) * 16, j = j0 + r;
     const int64_t Kp = TQ * 128, steps = (TQ + 3) / 4;
-    i32x4_t acc[TF][8];
+    i32x4_t acc[TF][8], accn[kTern ? TF : 1][8];
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf)
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) acc[tf][s8] = i32x4_t{0, 0, 0, 0};
+    if constexpr (kTern) {
+#pragma unroll
+        for (int tf = 0; tf < TF; ++tf)
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) accn[tf][s8] = i32x4_t{0, 0, 0, 0};
+    }
     for (int64_t base = wave; base < steps; base += kGenWaves * GS) {
-        u32x4_t w[GS];
+        u32x4_t w[GS], wn[kTern ? GS : 1];
         preload<GS>(w, P, base, kGenWaves, steps, TQ, N, j, g);
+        if constexpr (kTern) preload<GS>(wn, Pn, base, kGenWaves, steps, TQ, N, j, g);
 #pragma unroll
         for (int i = 0; i < GS; ++i) {
             const int64_t st = base + kGenWaves * i;
@@ -184,11 +194,15 @@ gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsu
                 for (int s8 = 0; s8 < 8; ++s8) b[s8] = ld16_or0(src + s8, bv);
                 __builtin_amdgcn_sched_barrier(0);   // all 8 operand loads in flight before the MFMAs
                 w1a8_step(w[i], b, acc[tf]);
+                if constexpr (kTern) w1a8_step(wn[i], b, accn[tf]);
             }
         }
     }
 #pragma unroll
-    for (int tf = 0; tf < TF; ++tf) red[wave][tf][lane] = w1a8_combine(acc[tf]);
+    for (int tf = 0; tf < TF; ++tf) {
+        red[wave][tf][lane] = w1a8_combine(acc[tf]);
+        if constexpr (kTern) red[wave][tf][lane] -= w1a8_combine(accn[tf]);
+    }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
@@ -199,12 +213,12 @@ gemv_w1a8_kernel(const int8_t* __restrict__ q, const int32_t* __restrict__ rowsu
         i32x4_t sum = red[0][tf][lane];
 #pragma unroll
         for (int wv = 1; wv < kGenWaves; ++wv) sum += red[wv][tf][lane];
-        const int32_t rs = rowsum[mm];
+        const int32_t rs = kTern ? 0 : rowsum[mm];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t col = j0 + 4 * g + i;
             if (col >= N) continue;
-            const int32_t a = 2 * sum[i] - rs;
+            const int32_t a = kTern ? sum[i] : 2 * sum[i] - rs;   // binary: sum s q = 2 sum b q - sum q
             y[int64_t(mm) * N + col] = float(a) * scale;
             if (acc_opt) acc_opt[int64_t(mm) * N + col] = a;
         }
@@ -239,7 +253,9 @@ BGB_DEV int exact_code(float h, float qb, float gamma, float lim) {
 // 512 rows, shared by KQ = NW / F waves.
 constexpr int w1a8_d1_steps(int nv, int f) { return (nv * f + 1) / 2; }
 
-template <int NV, int NW, int F, int IT, typename XT, bool kRne>
+// kTern: ternary weights (BitNet b1.58) as two planes, +1 at P and -1 at
+// P + TQ N 4 words; the product is sum_plus - sum_minus (no code row sum).
+template <int NV, int NW, int F, int IT, typename XT, bool kRne, bool kTern>
 __global__ void __launch_bounds__(NW * 64)
 bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
                          const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
@@ -248,7 +264,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     constexpr int NT = NW * 64;
     constexpr int KQ = NW / F;
     constexpr int S = w1a8_d1_steps(NV, F);
-    static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "single-token W1A8 shape");
+    static_assert(NW % F == 0 && IT * S * (kTern ? 2 : 1) <= kD1MaxTiles, "single-token W1A8 shape");
     __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
     __shared__ i32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
     __shared__ double dsum[NW], dsq[NW];
@@ -278,12 +294,13 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
     // the sign tiles of all of this block's column groups (groups past the
     // last one and columns past N load as zeros)
-    u32x4_t w[IT][S];
+    u32x4_t w[IT][S], wn[kTern ? IT : 1][S];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
         const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
         preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
+        if constexpr (kTern) preload<S>(wn[it], P + TQ * N * 4, kq, KQ, steps, TQ, N, jj, g);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -416,9 +433,13 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
         if (grp >= ngroups) break;
-        i32x4_t acc[8];
+        i32x4_t acc[8], accn[kTern ? 8 : 1];
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
+        if constexpr (kTern) {
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) accn[s8] = i32x4_t{0, 0, 0, 0};
+        }
         // only lanes r == 0 (token 0) read the codes: the other lanes' token
         // columns are never read, so their B operand may hold anything (zeros
         // at first, then whatever it held); steps past the column's tiles have
@@ -434,8 +455,10 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
                 for (int s8 = 0; s8 < 8; ++s8) bk[s8] = src[s8];
             }
             w1a8_step(w[it][i], bk, acc);
+            if constexpr (kTern) w1a8_step(wn[it][i], bk, accn);
         }
         i32x4_t sum = w1a8_combine(acc);
+        if constexpr (kTern) sum -= w1a8_combine(accn);
         if constexpr (KQ > 1) {
             red[it & 1][wave][lane] = sum;
             __syncthreads();
@@ -450,7 +473,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int i = 0; i < 4; ++i) {
             const int64_t col = j0 + i;
             if (col >= N) continue;
-            const int32_t a = 2 * sum[i] - rowsum;
+            const int32_t a = kTern ? sum[i] : 2 * sum[i] - rowsum;   // binary: 2 sum b q - sum q
             y[col] = float(a) * scale;
             if (acc_opt) acc_opt[col] = a;
         }
@@ -461,26 +484,28 @@ bool w1a8_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
 
 // The fragments per group F (a divisor of NW whose steps fit the tile budget)
 // and the groups per block IT, for NV pieces per thread.
-template <int NV, int NW>
+template <int NV, int NW, bool kTern>
 constexpr bool w1a8_d1_ok(int f, int it) {
-    return f <= NW && NW % f == 0 && it * w1a8_d1_steps(NV, f) <= kD1MaxTiles;
+    return f <= NW && NW % f == 0 && it * w1a8_d1_steps(NV, f) * (kTern ? 2 : 1) <= kD1MaxTiles;
 }
 
-template <int NV, int NW, int F, typename XT>
+template <int NV, int NW, int F, typename XT, bool kTern>
 static void launch_w1a8_decode1_f(int it, unsigned grid, const XT* x, int64_t K, int64_t N, int64_t TQ, double eps,
                                   float qb, float lim, int rne, const uint32_t* P, const float* beta, float* y,
                                   int32_t* acc_opt, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
 #define BGB_D1X(ITV)                                                                                             \
     if (rne)                                                                                                     \
-        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, true><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, \
-                                                                                   beta, y, acc_opt, xq_opt,    \
-                                                                                   gamma_opt);                  \
+        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, true, kTern><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb,  \
+                                                                                          lim, P, beta, y,      \
+                                                                                          acc_opt, xq_opt,      \
+                                                                                          gamma_opt);           \
     else                                                                                                         \
-        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, false><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, lim, P, \
-                                                                                    beta, y, acc_opt, xq_opt,   \
-                                                                                    gamma_opt)
-    if constexpr (w1a8_d1_ok<NV, NW>(F, 1)) {
-        if constexpr (w1a8_d1_ok<NV, NW>(F, 2)) {
+        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, false, kTern><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, \
+                                                                                           lim, P, beta, y,     \
+                                                                                           acc_opt, xq_opt,     \
+                                                                                           gamma_opt)
+    if constexpr (w1a8_d1_ok<NV, NW, kTern>(F, 1)) {
+        if constexpr (w1a8_d1_ok<NV, NW, kTern>(F, 2)) {
             if (it == 2) {
                 BGB_D1X(2);
                 return;
@@ -491,27 +516,28 @@ static void launch_w1a8_decode1_f(int it, unsigned grid, const XT* x, int64_t K,
 #undef BGB_D1X
 }
 
-template <int NV, int NW, typename XT>
+template <int NV, int NW, typename XT, bool kTern>
 static void launch_w1a8_decode1_nv(const XT* x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
-                                   int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
-                                   float* gamma_opt, hipStream_t s) {
+                                   int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt,
+                                   int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
     // the fewest fragments per group that give each block (one per CU) a
     // single group; failing that, the most allowed and up to 2 groups per
     // block, then more blocks
     const int64_t frags = (N + 15) / 16;
     int F = 1;
-    while (2 * F <= NW && w1a8_d1_ok<NV, NW>(2 * F, 1) && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
+    while (2 * F <= NW && w1a8_d1_ok<NV, NW, kTern>(2 * F, 1) && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
     const int64_t groups = (frags + F - 1) / F;
     int64_t grid = groups < kD1MaxGrid ? groups : kD1MaxGrid;
     int it = int((groups + grid - 1) / grid);
-    const int it_max = w1a8_d1_ok<NV, NW>(F, 2) ? 2 : 1;
+    const int it_max = w1a8_d1_ok<NV, NW, kTern>(F, 2) ? 2 : 1;
     if (it > it_max) {
         it = it_max;
         grid = (groups + it - 1) / it;
     }
     const unsigned gr = unsigned(grid);
-#define BGB_D1F(FV) \
-    launch_w1a8_decode1_f<NV, NW, FV, XT>(it, gr, x, K, N, TQ, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
+#define BGB_D1F(FV)                                                                                              \
+    launch_w1a8_decode1_f<NV, NW, FV, XT, kTern>(it, gr, x, K, N, TQ, eps, qb, lim, rne, P, beta, y, acc_opt,    \
+                                                 xq_opt, gamma_opt, s)
     if (F == 1) BGB_D1F(1);
     else if (F == 2) BGB_D1F(2);
     else if (F == 4) BGB_D1F(4);
@@ -519,7 +545,7 @@ static void launch_w1a8_decode1_nv(const XT* x, int64_t K, int64_t N, int64_t TQ
 #undef BGB_D1F
 }
 
-template <int NW, typename XT>
+template <int NW, typename XT, bool kTern>
 static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps, float qb, float lim, int rne,
                                    const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
                                    float* gamma_opt, hipStream_t s) {
@@ -528,45 +554,68 @@ static void launch_w1a8_decode1_nw(const XT* x, int64_t K, int64_t N, double eps
     const int64_t TQ = tiles_per_col(K);
     const int nv = int((TQ * 128 + nt * 4 - 1) / (nt * 4));
     const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : 16;
-#define BGB_D1(NVV) launch_w1a8_decode1_nv<NVV, NW, XT>(x, K, N, TQ, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s)
+#define BGB_D1(NVV)                                                                                              \
+    launch_w1a8_decode1_nv<NVV, NW, XT, kTern>(x, K, N, TQ, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt,      \
+                                               gamma_opt, s)
     if (nvp == 1) BGB_D1(1);
     else if (nvp == 2) BGB_D1(2);
     else if (nvp == 4) BGB_D1(4);
     else if (nvp == 8) BGB_D1(8);
-    else if constexpr (kMaxNv >= 16) BGB_D1(16);
+    else if constexpr (kMaxNv >= 16 && !kTern) BGB_D1(16);   // ternary takes 8-wave blocks there
 #undef BGB_D1
+}
+
+template <bool kTern>
+static void launch_w1a8_decode1_t(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
+                                  int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt,
+                                  int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
+    // 8-wave blocks for layers of at least 8192 columns; 4-wave blocks (one
+    // wave per SIMD, so the per-wave prologue work is not repeated) below.
+    // Ternary weights take two tiles per step, so K > 8192 (16 code dwords
+    // per thread of a 4-wave block) also goes to 8-wave blocks.
+    const bool wide = (N + 31) / 32 >= kD1MaxGrid || (kTern && padded_k(K) > 8192);
+    if (x_bf16) {
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        if (wide) launch_w1a8_decode1_nw<8, uint16_t, kTern>(xb, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt,
+                                                             gamma_opt, s);
+        else launch_w1a8_decode1_nw<4, uint16_t, kTern>(xb, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt,
+                                                        gamma_opt, s);
+    } else {
+        const float* xf = static_cast<const float*>(x);
+        if (wide) launch_w1a8_decode1_nw<8, float, kTern>(xf, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt,
+                                                          gamma_opt, s);
+        else launch_w1a8_decode1_nw<4, float, kTern>(xf, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt,
+                                                     gamma_opt, s);
+    }
 }
 
 hipError_t launch_w1a8_decode1(const void* x, int x_bf16, int64_t K, int64_t N, double eps, float qb, float lim,
                                int rne, const uint32_t* P, const float* beta, float* y, int32_t* acc_opt, int8_t* xq_opt,
-                               float* gamma_opt, hipStream_t s) {
-    // 8-wave blocks for layers of at least 8192 columns; 4-wave blocks (one
-    // wave per SIMD, so the per-wave prologue work is not repeated) below
-    const bool wide = (N + 31) / 32 >= kD1MaxGrid;
-    if (x_bf16) {
-        const uint16_t* xb = static_cast<const uint16_t*>(x);
-        if (wide) launch_w1a8_decode1_nw<8>(xb, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
-        else launch_w1a8_decode1_nw<4>(xb, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
-    } else {
-        const float* xf = static_cast<const float*>(x);
-        if (wide) launch_w1a8_decode1_nw<8>(xf, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
-        else launch_w1a8_decode1_nw<4>(xf, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
-    }
+                               float* gamma_opt, int tern, hipStream_t s) {
+    if (tern) launch_w1a8_decode1_t<true>(x, x_bf16, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
+    else launch_w1a8_decode1_t<false>(x, x_bf16, K, N, eps, qb, lim, rne, P, beta, y, acc_opt, xq_opt, gamma_opt, s);
     return hipGetLastError();
 }
 
 hipError_t launch_w1a8_gemv(const int8_t* q, const int32_t* rowsum, const float* gamma, int gstride,
                             const float* beta, float qb, int64_t M, int64_t K, int64_t N, const uint32_t* P, float* y,
-                            int32_t* acc_opt, hipStream_t s) {
+                            int32_t* acc_opt, int tern, hipStream_t s) {
     const unsigned grid = unsigned((N + 15) / 16);
     const int64_t TQ = tiles_per_col(K);
     const int tf = int((M + 15) / 16);
-    const int gs = gen_steps(TQ);
+    int gs = gen_steps(TQ);
+    if (tern && gs > 2) gs = 2;      // two sign planes: fewer steps per pass keep the registers in bounds
     constexpr unsigned nt = kGenWaves * 64;
-#define BGB_G8(TFV, GSV) gemv_w1a8_kernel<TFV, GSV><<<grid, nt, 0, s>>>(q, rowsum, gamma, gstride, beta, qb, int(M), N, TQ, P, y, \
-                                                                     acc_opt)
-#define BGB_G8S(TFV) if (gs == 1) BGB_G8(TFV, 1); else if (gs == 2) BGB_G8(TFV, 2); else BGB_G8(TFV, 4);
-    if (tf == 1) { BGB_G8S(1) } else if (tf == 2) { BGB_G8S(2) } else if (tf == 3) { BGB_G8S(3) } else { BGB_G8S(4) }
+#define BGB_G8(TFV, GSV)                                                                                          \
+    if (tern) gemv_w1a8_kernel<TFV, GSV, true><<<grid, nt, 0, s>>>(q, rowsum, gamma, gstride, beta, qb, int(M), N, TQ, \
+                                                                   P, y, acc_opt);                               \
+    else gemv_w1a8_kernel<TFV, GSV, false><<<grid, nt, 0, s>>>(q, rowsum, gamma, gstride, beta, qb, int(M), N, TQ, \
+                                                                P, y, acc_opt)
+#define BGB_G8S(TFV)                                                                                              \
+    if (gs == 1) { BGB_G8(TFV, 1); } else if (gs == 2) { BGB_G8(TFV, 2); }                                      \
+    else { gemv_w1a8_kernel<TFV, 4, false><<<grid, nt, 0, s>>>(q, rowsum, gamma, gstride, beta, qb, int(M), N, TQ, \
+                                                                 P, y, acc_opt); }
+    if (tf == 1) { BGB_G8S(1) } else { BGB_G8S(2) }       // M <= 32: at most two token fragments
 #undef BGB_G8S
 #undef BGB_G8
     return hipGetLastError();

@@ -6,8 +6,12 @@
 // BitNet (same blog, eq. (1)-(3), (8)): sign of W - c with c = mean(W), and
 // beta = mean |W|.
 //
-// Both are single passes over fp32 W (HBM-bound: 4 bytes read per weight,
-// 1/8 byte written). Sums are fp64 over fixed partitions combined in a fixed
+// BitNet b1.58 (same blog, section 二, eq. (9)-(11)): ternary weights
+// RoundClip(W / (gamma_w + eps), -1, 1) with gamma_w = mean |W|, stored as two
+// sign planes in the same format (the +1 plane, then the -1 plane).
+//
+// All are single passes over fp32 W after the reductions (HBM-bound: 4 bytes
+// read per weight, 1/8 or 1/4 byte written). Sums are fp64 over fixed partitions combined in a fixed
 // order, so every output is reproducible bit for bit.
 #include "bgb_device.hpp"
 #include "bgb_internal.hpp"
@@ -47,6 +51,38 @@ pack_signs_kernel(const float* __restrict__ W, int64_t K, int64_t N, uint32_t* _
     u32x4_t out = {words[0], words[1], words[2], words[3]};
     *reinterpret_cast<u32x4_t*>(P + (tq * N + j) * 4) = out;
     if (!kBitnet) colsum[tq * N + j] = s;
+}
+
+// Ternary planes: one thread per (128-row tile, column), as above. The
+// quotient W / (gamma_w + eps) is a correctly rounded fp32 division; round()
+// is to nearest even. Plane 0 (+1) at P, plane 1 (-1) at P + TQ N 4 words.
+__global__ void __launch_bounds__(256)
+pack_ternary_kernel(const float* __restrict__ W, int64_t K, int64_t N, uint32_t* __restrict__ P,
+                    const float* __restrict__ gamma_w) {
+    const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t tq = blockIdx.y;
+    if (j >= N) return;
+    const int64_t T = K / 32, TQ = gridDim.y;
+    const float den = gamma_w[0] + kTernaryEps;
+    uint32_t pos[4], neg[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int64_t t = tq * 4 + w;
+        uint32_t wp = 0, wn = 0;
+        if (t < T) {
+            const float* col = W + (32 * t) * N + j;
+#pragma unroll 8
+            for (int b = 0; b < 32; ++b) {
+                const float r = __builtin_rintf(__builtin_nontemporal_load(col + int64_t(b) * N) / den);
+                wp |= uint32_t(r >= 1.0f) << b;
+                wn |= uint32_t(r <= -1.0f) << b;
+            }
+        }
+        pos[w] = wp;
+        neg[w] = wn;
+    }
+    *reinterpret_cast<u32x4_t*>(P + (tq * N + j) * 4) = u32x4_t{pos[0], pos[1], pos[2], pos[3]};
+    *reinterpret_cast<u32x4_t*>(P + (TQ * N + tq * N + j) * 4) = u32x4_t{neg[0], neg[1], neg[2], neg[3]};
 }
 
 // alpha_j = fl32((sum over tiles of the tile sums, in tile order) / K).
@@ -110,13 +146,16 @@ hipError_t launch_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t*
         pack_signs_kernel<false><<<grid, 256, 0, s>>>(W, K, N, P, colsum, nullptr);
         fbi_alpha_kernel<<<unsigned((N + 255) / 256), 256, 0, s>>>(colsum, TQ, N, K, alpha, alpha_f16);
     } else {
-        double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + PackBitnetWs::make().partial);
+        const PackBitnetWs lay = PackBitnetWs::make();
+        double* partial = reinterpret_cast<double*>(static_cast<char*>(ws) + lay.partial);
+        float* c = centre ? centre : reinterpret_cast<float*>(static_cast<char*>(ws) + lay.scratch);
         const int64_t n = K * N;
         int64_t nb = (n + 256 * 4 - 1) / (256 * 4);
         if (nb > kBitnetReduceBlocks) nb = kBitnetReduceBlocks;
         bitnet_reduce_kernel<<<unsigned(nb), 256, 0, s>>>(W, n, partial);
-        bitnet_finalize_kernel<<<1, 256, 0, s>>>(partial, int(nb), double(K) * double(N), centre, beta);
-        pack_signs_kernel<true><<<grid, 256, 0, s>>>(W, K, N, P, nullptr, centre);
+        bitnet_finalize_kernel<<<1, 256, 0, s>>>(partial, int(nb), double(K) * double(N), c, beta);
+        if (mode == 1) pack_signs_kernel<true><<<grid, 256, 0, s>>>(W, K, N, P, nullptr, c);
+        else pack_ternary_kernel<<<grid, 256, 0, s>>>(W, K, N, P, beta);    // beta = mean |W| = gamma_w
     }
     return hipGetLastError();
 }

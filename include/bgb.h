@@ -67,13 +67,14 @@ typedef enum {
 
 typedef enum { BGB_F32 = 0, BGB_F16 = 1, BGB_BF16 = 2 } bgb_dtype;
 
-typedef enum { BGB_MODE_FBI = 0, BGB_MODE_BITNET = 1 } bgb_mode;
+typedef enum { BGB_MODE_FBI = 0, BGB_MODE_BITNET = 1, BGB_MODE_TERNARY = 2 } bgb_mode;
 
 typedef enum {
     BGB_OP_PACK_FBI = 0,
     BGB_OP_PACK_BITNET = 1,
     BGB_OP_FBI_LINEAR = 2,
-    BGB_OP_BITLINEAR = 3
+    BGB_OP_BITLINEAR = 3,
+    BGB_OP_BITLINEAR158 = 4
 } bgb_op;
 
 /* Integer conversion of the clipped quantizer input v_c (eq. (4) gives none):
@@ -116,8 +117,17 @@ size_t bgb_workspace_bytes(int op, int64_t M, int64_t K, int64_t N);
  *   fp32 and written to device scalars `centre` and `beta`;
  *   s_ij = +1 iff W_ij > c (compared exactly in fp32), else -1.
  *   alpha/alpha_dtype are ignored (may be NULL).
- * W: [K][N] float32 (input). P: bgb_packed_bytes(K, N) bytes (output).
- * ws: bgb_workspace_bytes(BGB_OP_PACK_FBI or _BITNET, 0, K, N) bytes.
+ * mode BGB_MODE_TERNARY (BitNet b1.58, same blog, section 二, eq. (9)-(11)):
+ *   gamma_w = mean |W| (fp64 sum rounded once to fp32), written to `beta`
+ *   (it is the beta of eq. (8) for these weights); t_ij = RoundClip(
+ *   W_ij / (gamma_w + 1e-5), -1, 1), the divisor and quotient in fp32 and
+ *   round() to nearest even. P holds two planes of the binary format, each
+ *   bgb_packed_bytes(K, N) bytes: bit 1 in the first iff t_ij = +1, in the
+ *   second iff t_ij = -1. `centre` (mean W) is written when not NULL.
+ * W: [K][N] float32 (input). P: bgb_packed_bytes(K, N) bytes (output; twice
+ * that for BGB_MODE_TERNARY).
+ * ws: bgb_workspace_bytes(BGB_OP_PACK_FBI or _BITNET, 0, K, N) bytes (the
+ * ternary mode uses the BITNET size).
  * Errors: BGB_EINVAL (null, K % 32 != 0, sizes, alignment, workspace),
  *         BGB_EUNSUPPORTED (alpha dtype not F32/F16, unknown mode), BGB_EHIP.
  */
@@ -195,6 +205,28 @@ int bitlinear_quantize(const void* x, int x_dtype, int64_t M, int64_t K,
 int bitlinear_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
                      const bgb_quant_params* qp, float* y, int32_t* acc_opt,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bitlinear158_w1a8 + bitlinear158_matmul -- BitNet b1.58 forward: ternary
+ * weights with 8-bit activations ("BitNet b1.58: 1bit LLM时代", section 二:
+ * weights by eq. (9)-(11); activations quantized as in section 一, which
+ * section 二 keeps).
+ *   h, gamma, q: exactly as bitlinear_w1a8 (same qp options)
+ *   acc[m][j] = sum_i t_ij * q[m][i], t in {-1, 0, 1}      (exact int32)
+ *   y[m][j] = fl32(float(acc) * fl32(fl32(beta * gamma) / Q_b))
+ * P: the two planes from binarize_pack(BGB_MODE_TERNARY) (2 x
+ * bgb_packed_bytes(K, N) bytes); beta: its gamma_w = mean |W|, which is the
+ * beta of eq. (8) for the weights. ws: bgb_workspace_bytes(
+ * BGB_OP_BITLINEAR158, M, K, N) bytes. Everything else (taps, errors, the M
+ * dispatch, pairing with bitlinear_quantize) is as for the binary weights.
+ */
+int bitlinear158_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
+                      const uint32_t* P, const float* beta, const bgb_quant_params* qp,
+                      float* y, int8_t* xq_opt, float* gamma_opt, int32_t* acc_opt,
+                      void* ws, size_t ws_bytes, void* stream);
+int bitlinear158_matmul(int64_t M, int64_t K, int64_t N, const uint32_t* P, const float* beta,
+                        const bgb_quant_params* qp, float* y, int32_t* acc_opt,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Message for a status code (static string). */
 const char* bgb_status_string(int status);
