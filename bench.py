@@ -10,14 +10,15 @@ The timed region replays a HIP graph of exactly K captured steps.
 
 Extra objects on the same line:
   roofline      the decode GEMV kernel: algorithmic bytes per launch over its
-                average launch duration (per-launch HIP event pairs on the
-                launch stream, queued behind a busy kernel so the GPU never
-                idles between them), against 8 TB/s.
+                average launch duration (one launch per step, so the timed
+                region's HIP-event time over the K launches), against 8 TB/s.
   cpu_baseline  the CPU oracle on the same workload (one thread, bounded sample).
   legs          every other hot-path row at its workload: the two weight
                 conversions, W1A16 decode over a 7B-shaped layer (B = 1, 4, 16),
-                the W1A16 and W1A8 prefill GEMMs at 4096 x 4096 x 11008, and a
-                1.3B-shaped 24-layer stack (decode B = 64, prefill 2 x 1024).
+                the W1A16 and W1A8 prefill GEMMs at 4096 x 4096 x 11008, a
+                1.3B-shaped 24-layer stack (decode B = 64, prefill 2 x 1024),
+                and BitNet b1.58 ternary weights (decode and prefill at the
+                BitLinear shapes).
 Progress lines go to stderr.
 """
 from __future__ import annotations
@@ -332,6 +333,52 @@ def leg_prefill(torch, bgb, syn):
     return out
 
 
+def leg_ternary(torch, bgb, syn, rotate_mb):
+    """BitNet b1.58 ternary weights (two sign planes) at the BitLinear shapes:
+    decode of one token through 4096 x 11008 (rotated copies, as the headline)
+    and the prefill product at 4096 x 4096 x 11008."""
+    cfg = syn.CONFIGS["bitlinear_decode_4096x11008"]
+    K, N, seed = cfg["K"], cfg["N"], cfg["seed"]
+    W = syn.gpu_normal(seed, 0, (K, N), mean=cfg["w_mean"], std=cfg["w_std"])
+    P0, beta, _ = bgb.binarize_pack(W, bgb.MODE_TERNARY)
+    pbytes = 2 * bgb.packed_bytes(K, N)
+    R = max(2, math.ceil(rotate_mb * 1e6 / pbytes))
+    Ps = [P0] + [P0.clone() for _ in range(R - 1)]
+    x1 = syn.gpu_normal(seed, 1, (1, K))
+    y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    ws1 = torch.empty(max(bgb.workspace_bytes(bgb.OP_BITLINEAR158, 1, K, N), 256), dtype=torch.uint8, device="cuda")
+
+    def dec(i):
+        bgb.bitlinear158_w1a8(x1, Ps[i % R], beta, N, y=y1, ws=ws1)
+
+    ms = graph_time(torch, dec, 2000, 200) / 2000
+    step_bytes = pbytes + K * 4 + N * 4
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {"ternary_decode_4096x11008": {"us_per_step": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": step_bytes,
+                                         "weight_copies": R, "bound": "hbm"}}
+    log(f"ternary decode 4096x11008: {ms * 1e3:.2f} us/step, {gbs:.0f} GB/s")
+    del Ps
+    pc = syn.CONFIGS["w1_prefill_4096x4096x11008"]
+    M = pc["M"]
+    x = syn.gpu_normal(pc["seed"], 1, (M, K)).to(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bgb.workspace_bytes(bgb.OP_BITLINEAR158, M, K, N), dtype=torch.uint8, device="cuda")
+    bgb.bitlinear_quantize(x, ws=ws)
+
+    def mm(i):
+        bgb.bitlinear158_matmul(M, K, P0, beta, N, ws=ws, y=y)
+
+    ms_mm = graph_time(torch, mm, 10, 3) / 10
+    ops = 2 * M * K * N
+    t = ops / (ms_mm * 1e-3) / 1e12
+    out["ternary_prefill_gemm_4096x4096x11008"] = {"ms_gemm": round(ms_mm, 4), "TOP/s": round(t, 1),
+                                                   "frac_mfma_int8": round(t / INT8_PEAK_TOPS, 4), "ops": ops,
+                                                   "mfma_per_weight_bit_plane": 2, "bound": "mfma"}
+    log(f"ternary prefill product: {ms_mm * 1e3:.0f} us, {t:.0f} TOP/s")
+    return out
+
+
 def leg_stack_1p3b(torch, bgb, syn):
     cfg = syn.CONFIGS["w1a16_1p3b_stack"]
     shapes, L = cfg["shapes"], cfg["layers"]
@@ -416,7 +463,7 @@ def main():
 
     legs = {}
     want = set() if args.legs == "none" else (
-        {"pack", "decode7b", "prefill", "stack"} if args.legs == "all" else set(args.legs.split(",")))
+        {"pack", "decode7b", "prefill", "stack", "ternary"} if args.legs == "all" else set(args.legs.split(",")))
     if "pack" in want:
         legs.update(leg_pack(torch, bgb, syn))
         torch.cuda.empty_cache()
@@ -428,6 +475,8 @@ def main():
         torch.cuda.empty_cache()
     if "stack" in want:
         legs.update(leg_stack_1p3b(torch, bgb, syn))
+    if "ternary" in want:
+        legs.update(leg_ternary(torch, bgb, syn, args.rotate_mb))
         torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(state, args.cpu_seconds)
