@@ -99,10 +99,8 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
     if (M <= bgb::kW1A16DecodeMaxM)
         return finish(bgb::launch_w1a16_decodek(x, x_f16, M, K, N, P, alpha, a_f16, y, ydt,
                                                 static_cast<float*>(ws), s));
-    uint16_t* xi = reinterpret_cast<uint16_t*>(carve(ws, 0));
-    hipError_t e = bgb::launch_w1a16_interleave(x, M, K, xi, s);
-    if (e != hipSuccess) return finish(e);
-    return finish(bgb::launch_w1a16_gemm(xi, x_f16, M, K, N, P, alpha, a_f16, y, ydt, carve(ws, lay.part), s));
+    return finish(bgb::launch_w1a16_gemm(static_cast<const uint16_t*>(x), x_f16, M, K, N, P, alpha, a_f16, y, ydt,
+                                         lay.total ? carve(ws, lay.part) : nullptr, s));
 }
 
 // Shared checks of the BitLinear entry points; fills qb/lim from qp.

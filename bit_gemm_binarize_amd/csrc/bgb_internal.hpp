@@ -65,17 +65,12 @@ DecodekPlan decodek_plan(int64_t M, int64_t K, int64_t N);
 // (raw split sums, [splits][M][N] fp32; 0 when nothing is split).
 size_t w1a16_decode_ws_bytes(int64_t M, int64_t K, int64_t N);
 
-struct FbiLinearWs {        // decode: split-K sums (if any); GEMM: interleaved activations, then split-K sums
+struct FbiLinearWs {        // split-K partial sums (decode or GEMM), when the plan splits K
     size_t part, total;
     static FbiLinearWs make(int64_t M, int64_t K, int64_t N) {
         FbiLinearWs w{};
-        if (M <= kW1A16DecodeMaxM) {
-            w.part = 0;
-            w.total = w1a16_decode_ws_bytes(M, K, N);
-            return w;
-        }
-        w.part = align256(size_t(M) * size_t(padded_k(K)) * 2);
-        w.total = w.part + gemm_partial_bytes(M, K, N, false, false);
+        w.part = 0;
+        w.total = M <= kW1A16DecodeMaxM ? w1a16_decode_ws_bytes(M, K, N) : gemm_partial_bytes(M, K, N, false, false);
         return w;
     }
 };
@@ -107,10 +102,7 @@ hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, doub
                            int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
                            float* gamma_opt, hipStream_t s);
 
-// GEMM activations: xi[m][Kp], element pairs (row i, row i+16) of each 32-row group
-hipError_t launch_w1a16_interleave(const void* x, int64_t M, int64_t K, uint16_t* xi, hipStream_t s);
-
-hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N,
+hipError_t launch_w1a16_gemm(const uint16_t* x, int x_f16, int64_t M, int64_t K, int64_t N,
                              const uint32_t* P, const void* alpha, int alpha_f16, void* y,
                              int y_dtype, void* part, hipStream_t s);
 

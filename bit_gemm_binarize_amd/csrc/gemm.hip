@@ -20,17 +20,19 @@
 // DMA operations a stage issues.
 //
 // LDS layout of a stage: token row t at t*128 bytes, its eight 16-byte chunks
-// XOR-swizzled by a function of t so that the B-operand reads (a half-wave of
-// 32 lanes = 16 token rows x 2 chunks per pass on gfx950's 128-bank LDS) hit
-// 32 distinct bank groups. The DMA writes lane L of an instruction to chunk
+// XOR-swizzled by a function of bits 2..3 of t, so that the B-operand reads of
+// a wave (W1A8: 16 token rows x 4 chunks of 16 bytes; W1A16: 16 rows x 4
+// pieces of 8 bytes) fall on distinct banks of gfx950's 128-bank LDS. The DMA writes lane L of an instruction to chunk
 // base+L, so the swizzle is applied by choosing the source chunk per lane.
 //
 // Sign decoding (A operand, rows = output columns), per MFMA:
-// * W1A16: lane group g takes word g>>1 of the stage and the rows 4u+e and
-//   4u+e+16 (u = 2v + (g&1)) as dword e of its operand: one bitop3 of the
-//   shifted word gives the two sign bits over the bit pattern of 1.0. The
-//   activations were interleaved to match by the prep kernel: within each
-//   32-row group, element pair i holds rows i and i+16.
+// * W1A16: lane group g takes word g>>1 of the stage and, for MFMA half v,
+//   its 16-byte chunk u = 2v + (g&1): rows 8u..8u+7 in their natural order,
+//   dword e holding rows 8u+2e and 8u+2e+1. The lane's half of the sign
+//   word is regrouped once per stage (gather_pairs: the two rows of each
+//   pair 16 bits apart), so that one bitop3 of the shifted word gives both
+//   sign bits of dword e over the bit pattern of 1.0. The activations are
+//   read from x itself, no reordered copy.
 // * W1A8: lane group g takes word g, MFMA v = 0..1, dword d carries rows
 //   4v+d+8e (byte e) as 0/1 bytes; sum s q = 2 sum b q - sum q with the row
 //   sums of the codes from the prologue, which writes the codes in this order.
@@ -75,51 +77,22 @@ BGB_DEV void dma16(const void* src, uint8_t* lds_wave_base) {
 BGB_DEV int swz16(int t) { return 2 * ((t >> 2) & 3); }
 BGB_DEV int swz8(int t) { return ((t >> 2) & 1) | (((t >> 3) & 1) << 2); }
 
-// ------------------------------------------------------------ W1A16 prep ----
-// xi[m][Kp]: within each 32-row group, element 2i = x[m][32t+i] and element
-// 2i+1 = x[m][32t+i+16]; rows >= K are zero. One thread per (m, group).
-__global__ void __launch_bounds__(256)
-w1a16_interleave_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t Kp,
-                        uint16_t* __restrict__ xi) {
-    const int64_t groups = Kp / 32;
-    const int64_t id = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (id >= M * groups) return;
-    const int64_t m = id / groups, t = id % groups, k0 = 32 * t;
-    const uint16_t* row = x + m * K;
-    u32x4_t o[4];
-    if ((K & 7) == 0 && k0 + 32 <= K) {
-        const u32x4_t* s = reinterpret_cast<const u32x4_t*>(row + k0);
-        const u32x4_t l0 = s[0], l1 = s[1], h0 = s[2], h1 = s[3];
-        const uint32_t lo[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const uint32_t hi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            o[q].x = __builtin_amdgcn_perm(hi[2 * q], lo[2 * q], 0x05040100u);
-            o[q].y = __builtin_amdgcn_perm(hi[2 * q], lo[2 * q], 0x07060302u);
-            o[q].z = __builtin_amdgcn_perm(hi[2 * q + 1], lo[2 * q + 1], 0x05040100u);
-            o[q].w = __builtin_amdgcn_perm(hi[2 * q + 1], lo[2 * q + 1], 0x07060302u);
-        }
-    } else {
-        uint32_t d[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t a = k0 + i < K ? row[k0 + i] : 0u;
-            const uint32_t b = k0 + i + 16 < K ? row[k0 + i + 16] : 0u;
-            d[i] = a | (b << 16);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = u32x4_t{d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]};
-    }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xi + m * Kp + k0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = o[q];
+// The sign bits a W1A16 lane needs from a 32-row word w, placed for the
+// decode: with sel picking bytes (h, h + 2, h, h + 2) of w (rows 8h..8h+7 and
+// 16+8h..16+8h+7), the result holds the even rows of byte h at bits 0..3,
+// those of byte h + 2 at bits 8..11, and the odd rows of the two bytes at
+// bits 16..19 and 24..27 -- so rows 2i and 2i + 1 of a chunk sit 16 bits
+// apart. One byte permute, then two halving steps compress each byte's
+// even (low half) or odd (high half) bits into its low nibble.
+BGB_DEV uint32_t gather_pairs(uint32_t w, uint32_t sel) {
+    const uint32_t z = __builtin_amdgcn_perm(w, w, sel);
+    uint32_t m = ((z & 0x0000FFFFu) | ((z >> 1) & 0xFFFF0000u)) & 0x55555555u;
+    m = (m | (m >> 1)) & 0x33333333u;
+    return (m | (m >> 2)) & 0x0F0F0F0Fu;
 }
 
-hipError_t launch_w1a16_interleave(const void* x, int64_t M, int64_t K, uint16_t* xi, hipStream_t s) {
-    const int64_t Kp = padded_k(K), n = M * (Kp / 32);
-    w1a16_interleave_kernel<<<unsigned((n + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(x), M, K, Kp, xi);
-    return hipGetLastError();
-}
+// 16 zero bytes in global memory: the DMA source for activation chunks past K.
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
 // ------------------------------------------------------------------- plan ----
 // Cost model, in microseconds: a stage of a 128-token block (two blocks per
@@ -176,8 +149,9 @@ size_t gemm_partial_bytes(int64_t M, int64_t K, int64_t N, bool w1a8, bool tern)
 
 // ------------------------------------------------------------------ kernel ----
 struct GemmArgs {
-    const uint8_t* act;        // xi (W1A16, [M][Kp] 16-bit) or q (W1A8, [M][Kp] int8)
+    const uint8_t* act;        // x (W1A16, [M][K] 16-bit) or q (W1A8, [M][Kp] int8)
     int64_t row_bytes;
+    int64_t K;
     const uint32_t* P;
     int64_t M, N;
     int T, per, ntj, ntiles;
@@ -247,9 +221,12 @@ BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& 
 // NN token fragments per wave (BM = 16 NN); kW1A8 selects the int8 path;
 // kTern (int8 path only) takes ternary weights as two sign planes (+1 plane,
 // then -1 plane, each in the binary format) and keeps two accumulator sets.
-template <bool kW1A8, bool kF16, int NN, int NW, bool kTern = false>
+// kKTail (W1A16, K not a multiple of 128): the stages reaching past K take
+// zeros for those activation chunks.
+template <bool kW1A8, bool kF16, int NN, int NW, bool kTern = false, bool kKTail = false>
 __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a) {
     static_assert(!kTern || kW1A8, "ternary weights take the int8 path");
+    static_assert(!kKTail || !kW1A8, "the int8 codes arrive zero-padded");
     constexpr int BM = 16 * NN;
     constexpr int BJ = 64 * NW;                 // 64 columns per wave
     constexpr int kStage = BM * 128;            // bytes of one activation stage
@@ -285,12 +262,19 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
     // (4i+w)*64 .. +63; lane L takes chunk p -> token row p>>3, LDS slot p&7,
     // source chunk (p&7) ^ swz(row); rows past M read row M-1 (never stored).
     // Thread tid moves column j0 + tid (clamped to N-1) of the sign tile.
+    // W1A16 reads x itself: chunks past K (the tail of the last 64-row
+    // stage, and stages past K) come from a zero chunk, as their sign bits
+    // (0 -> -1) must meet zero activations.
     const uint8_t* src[kXDma];
+    auto chunk_of = [&](int i, int& t) {        // source chunk of instruction i for this lane
+        const int p = (NW * i + wave) * 64 + lane;
+        t = p >> 3;
+        return (p & 7) ^ (kW1A8 ? swz8(t) : swz16(t));
+    };
 #pragma unroll
     for (int i = 0; i < kXDma; ++i) {
-        const int p = (NW * i + wave) * 64 + lane;
-        const int t = p >> 3, slot = p & 7;
-        const int c = slot ^ (kW1A8 ? swz8(t) : swz16(t));
+        int t;
+        const int c = chunk_of(i, t);
         const int64_t m = m0 + t < M ? m0 + t : M - 1;
         src[i] = a.act + m * a.row_bytes + 16 * c;
     }
@@ -298,13 +282,22 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
     auto issue = [&](int rel, int B) {          // stage s0 + rel, clamped: the tail re-reads the last one
         const int s = s0 + (rel < ns ? rel : ns - 1);
 #pragma unroll
-        for (int i = 0; i < kXDma; ++i) dma16(src[i] + int64_t(s) * 128, lds[B] + (NW * i + wave) * 1024);
+        for (int i = 0; i < kXDma; ++i) {
+            const uint8_t* sp = src[i] + int64_t(s) * 128;
+            if constexpr (kKTail) {              // W1A16 with K % 128 != 0: chunks past K read zeros
+                int t;
+                if (int64_t(s) * 64 + 8 * chunk_of(i, t) >= a.K) sp = reinterpret_cast<const uint8_t*>(g_zero16);
+            }
+            dma16(sp, lds[B] + (NW * i + wave) * 1024);
+        }
         const int64_t tq = kW1A8 ? s : (s >> 1);
         dma16(wsrc + tq * N * 16, wls[B] + wave * 1024);
         if constexpr (kTern) dma16(wsrc + (int64_t(a.T) + tq) * N * 16, wls[B] + kWTileBytes + wave * 1024);
     };
 
-    // B-operand byte offsets in a stage (token row 16n + r) and this lane's sign word
+    // B-operand byte offsets in a stage (token row 16n + r) and this lane's
+    // sign word. W1A16: half v takes chunk u = 2v + (g & 1) of word g >> 1,
+    // i.e. rows 8u..8u+7 of that 32-row word in their natural order.
     int boff0, boff1, wbyte;
     if constexpr (kW1A8) {
         const int rsw = swz8(r);
@@ -317,7 +310,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
         boff1 = r * 128 + 16 * ((4 * (g >> 1) + 2 + (g & 1)) ^ rsw);
         wbyte = (64 * wave + r) * 16 + 4 * (g >> 1);                // + 256 f + 8 (s & 1)
     }
-    const int wshift = 4 * (g & 1);
+    const uint32_t psel = (g & 1) ? 0x03010301u : 0x02000200u;   // W1A16: bytes (h, h + 2, h, h + 2)
 
     acc_t acc[4][NN], accn[kTern ? 4 : 1][kTern ? NN : 1];
 #pragma unroll
@@ -340,7 +333,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
             const uint32_t w = *reinterpret_cast<const uint32_t*>(wls[B] + wb + 256 * f);
-            X[f] = kW1A8 ? w : (w >> wshift);
+            X[f] = (kW1A8 || kKTail) ? w : gather_pairs(w, psel);   // W1A16 with a K tail: at use (registers)
             if constexpr (kTern) Xn[f] = *reinterpret_cast<const uint32_t*>(wls[B] + kWTileBytes + wb + 256 * f);
         }
 #pragma unroll
@@ -371,7 +364,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
                         accn[f][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an, b[n], accn[f][n], 0, 0, 0);
                 }
             } else {
-                u32x4_t av;   // (~(X << s) & 0x80008000) | one: sign bits of rows 4u+e, 4u+e+16
+                // (~(X << s) & 0x80008000) | one: X holds the lane's rows of
+                // the word with rows 8u + 2e and 8u + 2e + 1 (u = 2v + (g & 1))
+                // at bits 8v + e and 16 + 8v + e, so dword e gets the sign pair
+                // the B operand holds
+                u32x4_t av;
                 av.x = __builtin_amdgcn_bitop3_b32(Xv[f] << (15 - 8 * v), 0x80008000u, kOne, 0xAE);
                 av.y = __builtin_amdgcn_bitop3_b32(Xv[f] << (14 - 8 * v), 0x80008000u, kOne, 0xAE);
                 av.z = __builtin_amdgcn_bitop3_b32(Xv[f] << (13 - 8 * v), 0x80008000u, kOne, 0xAE);
@@ -394,7 +391,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
         for (int n = 0; n < NN; ++n) b1[n] = *reinterpret_cast<const opd_t*>(lds[B] + n * 2048 + boff1);
         uint32_t Xc[4], Xnc[kTern ? 4 : 1];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) Xc[f] = X[f];
+        for (int f = 0; f < 4; ++f) Xc[f] = (kW1A8 || !kKTail) ? X[f] : gather_pairs(X[f], psel);
         if constexpr (kTern) {
 #pragma unroll
             for (int f = 0; f < 4; ++f) Xnc[f] = Xn[f];
@@ -530,8 +527,18 @@ static hipError_t launch_gemm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
             return hipGetLastError();
         }
     }
-    if (p.nw == 8) gemm_kernel<kW1A8, kF16, 8, 8><<<grid, 512, 0, s>>>(a);
-    else if (p.nn == 8) gemm_kernel<kW1A8, kF16, 8, 4><<<grid, 256, 0, s>>>(a);
+    if constexpr (!kW1A8) {
+        if (a.K % 128 != 0) {
+            if (p.nn == 8) gemm_kernel<false, kF16, 8, 4, false, true><<<grid, 256, 0, s>>>(a);
+            else gemm_kernel<false, kF16, 4, 4, false, true><<<grid, 256, 0, s>>>(a);
+            if (p.splits > 1) {
+                const int64_t n = a.M * ((a.N + 3) / 4);
+                splitk_reduce_kernel<kW1A8><<<unsigned((n + 255) / 256), 256, 0, s>>>(a, p.splits);
+            }
+            return hipGetLastError();
+        }
+    }
+    if (p.nn == 8) gemm_kernel<kW1A8, kF16, 8, 4><<<grid, 256, 0, s>>>(a);
     else gemm_kernel<kW1A8, kF16, 4, 4><<<grid, 256, 0, s>>>(a);
     if (p.splits > 1) {
         const int64_t n = a.M * ((a.N + 3) / 4);
@@ -555,12 +562,13 @@ hipError_t launch_w1a16_splitk_reduce(const float* part, int splits, int64_t M, 
     return hipGetLastError();
 }
 
-hipError_t launch_w1a16_gemm(const uint16_t* xi, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+hipError_t launch_w1a16_gemm(const uint16_t* x, int x_f16, int64_t M, int64_t K, int64_t N, const uint32_t* P,
                              const void* alpha, int alpha_f16, void* y, int y_dtype, void* part, hipStream_t s) {
     const GemmPlan p = gemm_plan(M, K, N, false, false);
     GemmArgs a{};
-    a.act = reinterpret_cast<const uint8_t*>(xi);
-    a.row_bytes = padded_k(K) * 2;
+    a.act = reinterpret_cast<const uint8_t*>(x);
+    a.row_bytes = K * 2;
+    a.K = K;
     a.P = P;
     a.M = M;
     a.N = N;
@@ -580,6 +588,7 @@ hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float*
     GemmArgs a{};
     a.act = reinterpret_cast<const uint8_t*>(q);
     a.row_bytes = padded_k(K);
+    a.K = padded_k(K);
     a.P = P;
     a.M = M;
     a.N = N;

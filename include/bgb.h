@@ -150,9 +150,8 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
  * whole, and decode shapes whose K range is not split) ws is neither read nor
  * written and may be NULL. Decode shapes whose K range is split over several
  * blocks keep fp32 partial sums there ([splits][M][N]), added in a fixed
- * order by a second launch; the GEMM keeps a re-ordered copy of x there
- * (M x Kp x 2 bytes, Kp = K rounded up to 128) plus, for shapes whose K range
- * it splits, fp32 partial sums.
+ * order by a second launch; likewise the GEMM for shapes whose K range it
+ * splits (fp32 partial sums [splits][M][N]). The GEMM reads x in place.
  * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP.
  */
 int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,

@@ -53,12 +53,12 @@ def test_sizes(lib):
     assert bgb.packed_bytes(160, 3) == 2 * 3 * 16
     assert bgb.packed_bytes(4096, 11008) == 5636096
     assert bgb.packed_bytes(31, 5) == 0
-    # GEMM path: the interleaved copy of the activations (M x padded K x 2 bytes),
-    # plus fp32 partial sums when the launch plan splits K (small M x N)
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 4096, 4096, 11008) == 4096 * 4096 * 2
-    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 4096, 4000, 11008) == 4096 * 4096 * 2
+    # GEMM path: the activations are read in place; fp32 partial sums
+    # [splits][M][N] only when the launch plan splits K (small M x N)
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 4096, 4096, 11008) == 0
+    assert bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 4096, 4000, 11008) == 0
     small = bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096)
-    assert small >= 65 * 4096 * 2 and (small - 65 * 4096 * 2) % (65 * 4096 * 4) == 0
+    assert small >= 2 * 65 * 4096 * 4 and small % (65 * 4096 * 4) < 256
     assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 11008) == bgb.workspace_bytes(bgb.OP_BITLINEAR, 4096, 4096, 0)
     # decode kernels (M <= 64) stage the activations on chip: no workspace,
     # except fp32 sums [splits][M][N] where the K range is split (long K)
@@ -107,8 +107,9 @@ def test_fbi_linear_validation(lib):
     assert call_fbi(lib, ydt=7) == UNSUP
     assert call_fbi(lib, x=None) == BAD
     assert call_fbi(lib, y=A + 2) == BAD
-    assert call_fbi(lib, M=100, wsb=100 * 128 * 2 - 1) == BAD   # the GEMM path needs a workspace
-    assert call_fbi(lib, M=100, ws=None) == BAD
+    need = bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 65, 4096, 4096)   # a GEMM plan that splits K
+    assert call_fbi(lib, M=65, K=4096, N=4096, wsb=need - 1) == BAD
+    assert call_fbi(lib, M=65, K=4096, N=4096, ws=None) == BAD
     assert call_fbi(lib, M=1 << 25) == BAD
     assert call_fbi(lib, M=0) == 0 and call_fbi(lib, N=0) == 0
 
