@@ -288,6 +288,24 @@ def leg_decode_7b(torch, bgb, syn, steps):
             "us_per_layer": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
             "bytes_per_layer": nbytes, "bound": "hbm", "layer_copies": L, "linears": "qkv, o, gate_up, down"}
         log(f"decode 7B layer fused B={B}: {ms * 1e3:.1f} us/layer, {gbs:.0f} GB/s")
+        if B != 1:
+            continue
+        # the 4 linears of the layer as one group: one launch for a single
+        # token (the linears' inputs are independent synthetic tensors here)
+        gys = [torch.empty((B, N), dtype=torch.bfloat16, device="cuda") for _, _, N in fshapes]
+
+        def gbody(i, xs=xs, gys=gys):
+            Ps, As = flayers[i % L]
+            bgb.fbi_linear_w1a16_group([(xs[K], Ps[li], As[li], N) for li, (_, K, N) in enumerate(fshapes)],
+                                       ys=gys)
+
+        ms = graph_time(torch, gbody, steps, 4) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"w1a16_decode_7b_layer_grouped_b{B}"] = {
+            "us_per_layer": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_layer": nbytes, "bound": "hbm", "layer_copies": L, "linears": "qkv, o, gate_up, down",
+            "launches_per_layer": 1}
+        log(f"decode 7B layer grouped B={B}: {ms * 1e3:.1f} us/layer, {gbs:.0f} GB/s")
     del flayers
     return out
 

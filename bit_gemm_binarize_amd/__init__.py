@@ -22,7 +22,8 @@ __all__ = [
     "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bitlinear158_w1a8", "bitlinear158_matmul",
     "OP_BITLINEAR158", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
     "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M", "W1A16_DECODE_MAX_M",
-    "ROUND_TRUNC", "ROUND_RNE", "GAMMA_TENSOR", "GAMMA_TOKEN",
+    "ROUND_TRUNC", "ROUND_RNE", "GAMMA_TENSOR", "GAMMA_TOKEN", "fbi_linear_w1a16_group", "group_workspace_bytes",
+    "GROUP_MAX",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,8 +34,10 @@ MODE_FBI, MODE_BITNET, MODE_TERNARY = 0, 1, 2
 OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR, OP_BITLINEAR158 = 0, 1, 2, 3, 4
 GEMV_MAX_M = 32          # BitLinear: M <= 32 runs the decode kernels, above: the MFMA GEMM
 W1A16_DECODE_MAX_M = 64  # FBI-linear: M <= 64 runs the decode kernels, above: the MFMA GEMM
+GROUP_MAX = 8            # linears per fbi_linear_w1a16_group call
 
 EXPORTS = ("bgb_packed_bytes", "bgb_workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
+           "fbi_linear_w1a16_group", "bgb_group_workspace_bytes",
            "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bitlinear158_w1a8",
            "bitlinear158_matmul", "bgb_status_string",
            "bgb_last_hip_error", "bgb_version")
@@ -44,6 +47,12 @@ class BgbError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"bgb status {status}: {msg}")
         self.status = status
+
+
+class _Item(ctypes.Structure):
+    """bgb_w1a16_item."""
+    _fields_ = [("x", ctypes.c_void_p), ("P", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("K", ctypes.c_int64), ("N", ctypes.c_int64)]
 
 
 class _QP(ctypes.Structure):
@@ -92,6 +101,10 @@ def load():
     lib.binarize_pack.restype = I
     lib.fbi_linear_w1a16.argtypes = [P, I, I64, I64, I64, P, P, I, P, I, P, SZ, P]
     lib.fbi_linear_w1a16.restype = I
+    lib.fbi_linear_w1a16_group.argtypes = [ctypes.POINTER(_Item), I, I64, I, I, I, P, SZ, P]
+    lib.fbi_linear_w1a16_group.restype = I
+    lib.bgb_group_workspace_bytes.argtypes = [ctypes.POINTER(_Item), I, I64]
+    lib.bgb_group_workspace_bytes.restype = SZ
     lib.bitlinear_w1a8.argtypes = [P, I, I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, P, P, SZ, P]
     lib.bitlinear_w1a8.restype = I
     lib.bitlinear_quantize.argtypes = [P, I, I64, I64, ctypes.POINTER(_QP), P, P, P, SZ, P]
@@ -184,6 +197,41 @@ def binarize_pack(W, mode: int = MODE_FBI, alpha_dtype=None, *, P=None, alpha=No
     _check(load().binarize_pack(_ptr(W), K, N, mode, _ptr(P), None, BGB_F32, _ptr(beta), _ptr(centre),
                                 _ptr(ws), ws.numel(), _stream(stream)))
     return P, beta[:1], centre[:1]
+
+
+def _items(entries):
+    arr = (_Item * max(len(entries), 1))()
+    for i, (x, P, alpha, y) in enumerate(entries):
+        arr[i] = _Item(_ptr(x), _ptr(P), _ptr(alpha), _ptr(y), x.shape[1], y.shape[1])
+    return arr
+
+
+def group_workspace_bytes(entries, M: int) -> int:
+    """entries: (x, P, alpha, y) per linear (shapes only are read)."""
+    return int(load().bgb_group_workspace_bytes(_items(entries), len(entries), M))
+
+
+def fbi_linear_w1a16_group(linears, y_dtype=None, *, ys=None, ws=None, stream=None):
+    """linears: list of (x, P, alpha, N), x bf16/f16 [M][K] (the same M and dtypes for all).
+    Independent linears: one launch for a single token, else one after another.
+    Returns the list of outputs y [M][N]."""
+    torch = _torch()
+    if not linears:
+        return []
+    M = linears[0][0].shape[0]
+    dev = linears[0][0].device
+    if ys is None:
+        ydt = torch.float32 if y_dtype is None else y_dtype
+        ys = [torch.empty((M, N), dtype=ydt, device=dev) for (_, _, _, N) in linears]
+    entries = [(x, P, a, y) for (x, P, a, _), y in zip(linears, ys)]
+    arr = _items(entries)
+    need = int(load().bgb_group_workspace_bytes(arr, len(entries), M))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    x0, a0, y0 = linears[0][0], linears[0][2], ys[0]
+    _check(load().fbi_linear_w1a16_group(arr, len(entries), M, _dt(x0), _dt(a0), _dt(y0), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
+    return ys
 
 
 def fbi_linear_w1a16(x, P, alpha, N: int, y_dtype=None, *, y=None, ws=None, stream=None):

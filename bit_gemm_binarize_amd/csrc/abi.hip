@@ -75,20 +75,30 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P, v
                                    static_cast<hipStream_t>(stream)));
 }
 
-int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
-                     const void* alpha, int alpha_dtype, void* y, int y_dtype, void* ws, size_t ws_bytes,
-                     void* stream) {
+// Argument checks of one FBI-linear (the dtypes are checked by the caller):
+// BGB_OK with *empty set when nothing is to be done.
+static int fbi_check(const void* x, int64_t M, int64_t K, int64_t N, const uint32_t* P, const void* alpha,
+                     const void* y, bool* empty) {
     int rc = check_shape(M, K, N);
     if (rc) return rc;
+    *empty = M == 0 || N == 0;
+    if (*empty) return BGB_OK;                    // empty: nothing is read or written
+    if (!x || !P || !alpha || !y) return BGB_EINVAL;
+    if (!aligned16(x) || !aligned16(P) || !aligned16(alpha) || !aligned16(y)) return BGB_EINVAL;
+    return BGB_OK;
+}
+
+static int fbi_dtypes(int x_dtype, int alpha_dtype, int y_dtype) {
     if (x_dtype != BGB_BF16 && x_dtype != BGB_F16) return BGB_EUNSUPPORTED;
     if (alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
     if (y_dtype != BGB_F32 && y_dtype != BGB_BF16 && y_dtype != BGB_F16) return BGB_EUNSUPPORTED;
-    if (M == 0 || N == 0) return BGB_OK;          // empty: nothing is read or written
-    if (!x || !P || !alpha || !y) return BGB_EINVAL;
-    if (!aligned16(x) || !aligned16(P) || !aligned16(alpha) || !aligned16(y)) return BGB_EINVAL;
+    return BGB_OK;
+}
+
+// The launches of one checked, non-empty FBI-linear (ws already checked).
+static int fbi_run(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                   const void* alpha, int alpha_dtype, void* y, int y_dtype, void* ws, hipStream_t s) {
     const bgb::FbiLinearWs lay = bgb::FbiLinearWs::make(M, K, N);
-    if (lay.total && (!ws || ws_bytes < lay.total || !aligned16(ws))) return BGB_EINVAL;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const int x_f16 = x_dtype == BGB_F16;
     const int a_f16 = alpha_dtype == BGB_F16;
     const int ydt = y_dtype == BGB_F32 ? 0 : (y_dtype == BGB_F16 ? 1 : 2);
@@ -101,6 +111,99 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
                                                 static_cast<float*>(ws), s));
     return finish(bgb::launch_w1a16_gemm(static_cast<const uint16_t*>(x), x_f16, M, K, N, P, alpha, a_f16, y, ydt,
                                          lay.total ? carve(ws, lay.part) : nullptr, s));
+}
+
+int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, const uint32_t* P,
+                     const void* alpha, int alpha_dtype, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                     void* stream) {
+    bool empty = false;
+    int rc = check_shape(M, K, N);
+    if (rc) return rc;
+    rc = fbi_dtypes(x_dtype, alpha_dtype, y_dtype);
+    if (rc) return rc;
+    rc = fbi_check(x, M, K, N, P, alpha, y, &empty);
+    if (rc || empty) return rc;
+    const size_t need = bgb::FbiLinearWs::make(M, K, N).total;
+    if (need && (!ws || ws_bytes < need || !aligned16(ws))) return BGB_EINVAL;
+    return fbi_run(x, x_dtype, M, K, N, P, alpha, alpha_dtype, y, y_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+// Byte ranges [a, a + na) and [b, b + nb) share a byte.
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+static bool group_one_launch(const bgb_w1a16_item* items, int count, int64_t M) {
+    if (M != 1) return false;
+    for (int i = 0; i < count; ++i)
+        if (items[i].N > 0 && !bgb::w1a16_decode1_supported(items[i].K)) return false;
+    return true;
+}
+
+size_t bgb_group_workspace_bytes(const bgb_w1a16_item* items, int count, int64_t M) {
+    if (!items || count <= 0 || count > BGB_GROUP_MAX || M <= 0) return 0;
+    if (group_one_launch(items, count, M)) return 0;
+    size_t need = 0;
+    for (int i = 0; i < count; ++i) {
+        const size_t n = bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, items[i].K, items[i].N);
+        need = n > need ? n : need;
+    }
+    return need;
+}
+
+static_assert(BGB_GROUP_MAX == bgb::kGroupMax, "group size");
+
+int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, int x_dtype, int alpha_dtype,
+                           int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+    if (count < 0 || count > BGB_GROUP_MAX || (count > 0 && !items) || M < 0) return BGB_EINVAL;
+    int rc = fbi_dtypes(x_dtype, alpha_dtype, y_dtype);
+    if (rc) return rc;
+    bool live[BGB_GROUP_MAX] = {};
+    int nlive = 0;
+    for (int i = 0; i < count; ++i) {
+        const bgb_w1a16_item& it = items[i];
+        bool empty = false;
+        rc = fbi_check(it.x, M, it.K, it.N, it.P, it.alpha, it.y, &empty);
+        if (rc) return rc;
+        live[i] = !empty;
+        nlive += live[i];
+    }
+    if (nlive == 0) return BGB_OK;
+    const size_t ysz = y_dtype == BGB_F32 ? 4 : 2, asz = alpha_dtype == BGB_F32 ? 4 : 2;
+    for (int i = 0; i < count; ++i) {
+        if (!live[i]) continue;
+        const size_t ybytes = size_t(M) * size_t(items[i].N) * ysz;
+        for (int k = 0; k < count; ++k) {
+            if (!live[k]) continue;
+            const bgb_w1a16_item& o = items[k];
+            if (overlaps(items[i].y, ybytes, o.x, size_t(M) * size_t(o.K) * 2) ||
+                overlaps(items[i].y, ybytes, o.P, bgb_packed_bytes(o.K, o.N)) ||
+                overlaps(items[i].y, ybytes, o.alpha, size_t(o.N) * asz) ||
+                (k != i && overlaps(items[i].y, ybytes, o.y, size_t(M) * size_t(o.N) * ysz)))
+                return BGB_EINVAL;
+        }
+    }
+    const size_t need = bgb_group_workspace_bytes(items, count, M);
+    if (need && (!ws || ws_bytes < need || !aligned16(ws))) return BGB_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (group_one_launch(items, count, M)) {
+        bgb::W1a16Item in[BGB_GROUP_MAX];
+        int n = 0;
+        for (int i = 0; i < count; ++i) {
+            if (!live[i]) continue;
+            in[n++] = bgb::W1a16Item{items[i].x, items[i].P, items[i].alpha, items[i].y, items[i].K, items[i].N};
+        }
+        const int ydt = y_dtype == BGB_F32 ? 0 : (y_dtype == BGB_F16 ? 1 : 2);
+        return finish(bgb::launch_w1a16_decode1_group(in, n, x_dtype == BGB_F16, alpha_dtype == BGB_F16, ydt, s));
+    }
+    for (int i = 0; i < count; ++i) {
+        if (!live[i]) continue;
+        const bgb_w1a16_item& it = items[i];
+        rc = fbi_run(it.x, x_dtype, M, it.K, it.N, it.P, it.alpha, alpha_dtype, it.y, y_dtype, ws, s);
+        if (rc) return rc;
+    }
+    return BGB_OK;
 }
 
 // Shared checks of the BitLinear entry points; fills qb/lim from qp.

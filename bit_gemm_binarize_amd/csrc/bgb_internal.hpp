@@ -131,6 +131,19 @@ hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, 
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, const uint32_t* P,
                                 const void* alpha, int alpha_f16, void* y, int y_dtype, hipStream_t s);
+// Several independent single-token linears (at most kGroupMax, each with
+// w1a16_decode1_supported(K)) in one launch; empty ones (N = 0) are skipped.
+constexpr int kGroupMax = 8;
+struct W1a16Item {
+    const void* x;
+    const uint32_t* P;
+    const void* alpha;
+    void* y;
+    int64_t K, N;
+};
+bool w1a16_decode1_group_supported(const W1a16Item* items, int count);
+hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f16, int alpha_f16, int y_dtype,
+                                      hipStream_t s);
 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             int gstride, const float* beta, float qb, int64_t M, int64_t K,

@@ -291,6 +291,12 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[i][c] = __uint_as_float(__float_as_uint(load1(x, k0 + 8 * c)) & keep);
     }
+    // beta is requested now, beside the token; it and the output pointers
+    // (argument slots on a later cache line than the first ones) are pinned
+    // in registers after the first barrier below. Left alone, the compiler
+    // loads them after the last product, two scalar round trips in front of
+    // the stores.
+    const float beta0 = beta[0];
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
     // the sign tiles of all of this block's column groups (groups past the
     // last one and columns past N load as zeros)
@@ -319,6 +325,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     s1 = wave_sum63(s1);
     if (lane == 63) dsum[wave] = s1;
     __syncthreads();
+    asm volatile("" ::"s"(beta0), "s"(y), "s"(acc_opt));
     double sx = dsum[0];
 #pragma unroll
     for (int wv = 1; wv < NW; ++wv) sx += dsum[wv];
@@ -425,7 +432,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     int rowsum = 0;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
-    const float scale = (beta[0] * gamma) / qb;
+    const float scale = (beta0 * gamma) / qb;
     i32x4_t bk[8];
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) bk[s8] = i32x4_t{0, 0, 0, 0};
@@ -707,19 +714,20 @@ BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2,
 
 // Single token, activation staging fused: the block permutes x into LDS and
 // computes the four X_T itself, once, then takes up to IT column groups
-// (blockIdx.x + i * gridDim.x) of F 16-column fragments, as the W1A8 kernel.
+// (bid + i * nblk) of F 16-column fragments, as the W1A8 kernel. The body is
+// shared by the one-linear kernel (bid, nblk = the block index and count)
+// and the grouped one (the block's rank and count within its linear). LDS:
+// xs [kFusedMaxKp], xzero [128] (the B operand of steps past the last tile),
+// red [2 NW 64] when KQ > 1 (the K parts' sums), dX [NW 4].
 template <bool kF16, int NV, int NW, int F, int IT>
-__global__ void __launch_bounds__(NW * 64)
-fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
-                   const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
+BGB_DEV void fbi_decode1_body(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ,
+                              const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
+                              void* __restrict__ y, int y_dtype, int64_t bid, int64_t nblk, uint16_t* xs,
+                              uint16_t* xzero, f32x4_t* red, double* dX) {
     constexpr int NT = NW * 64;
     constexpr int KQ = NW / F;
     constexpr int S = NV * F;          // steps per wave: TQ <= NV NT / 16 tiles = NV NW steps, over KQ waves
     static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "single-token W1A16 shape");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
-    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];   // B operand of steps past the last tile
-    __shared__ f32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
-    __shared__ double dX[NW][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
     const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
@@ -738,10 +746,15 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
         xv[i] = t & u32x4_t(0u - uint32_t(ok));       // a mask (not a select): the load stays unconditional
     }
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
+    // the epilogue's arguments (on a later cache line of the argument block
+    // than the first ones) pinned in registers from here on, so that they are
+    // requested with the first ones; left alone, the compiler loads them after
+    // the last product, in front of the stores
+    asm volatile("" ::"s"(y), "s"(y_dtype), "s"(alpha_f16));
     u32x4_t w[IT][S];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        const int64_t grp = bid + int64_t(it) * nblk;
         const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
         preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
     }
@@ -756,7 +769,7 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     constexpr bool kAlphaAhead = IT == 1;
     uint2 araw[2] = {};
     if constexpr (kAlphaAhead) {
-        int64_t j0 = int64_t(blockIdx.x) * 16 * F + 16 * f + 4 * g;
+        int64_t j0 = bid * 16 * F + 16 * f + 4 * g;
         j0 = j0 < N ? j0 : 0;
         const char* a8 = static_cast<const char*>(alpha);
         const int64_t lo = alpha_f16 ? 2 * j0 : 4 * j0, hi = alpha_f16 ? 2 * j0 : 4 * j0 + 8;
@@ -786,14 +799,14 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const double t = wave_sum63(xs4[c]);
-        if (lane == 63) dX[wave][c] = t;
+        if (lane == 63) dX[wave * 4 + c] = t;
     }
     __syncthreads();
     double Xd[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) Xd[c] += dX[wv][c];
+        for (int c = 0; c < 4; ++c) Xd[c] += dX[wv * 4 + c];
     const float X0 = float(Xd[0]), X1 = float(Xd[1]), X2 = float(Xd[2]), X3 = float(Xd[3]);
     const float corr = ((8.0f * X0 + 4.0f * X1) + 2.0f * X2) + X3;
     const float xall = ((X0 + X1) + X2) + X3;
@@ -807,7 +820,7 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
     //    the KQ parts' sums through LDS (none when a wave covers all of K)
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        const int64_t grp = bid + int64_t(it) * nblk;
         if (grp >= ngroups) break;
         f32x4_t acc[1][4];
 #pragma unroll
@@ -837,12 +850,12 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
         // per wave z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3
         f32x4_t z = ((8.0f * acc[0][0] + 4.0f * acc[0][1]) + 2.0f * acc[0][2]) + 2.0f * acc[0][3];
         if constexpr (KQ > 1) {
-            red[it & 1][wave][lane] = z;
+            red[((it & 1) * NW + wave) * 64 + lane] = z;
             __syncthreads();
             if (kq != 0 || r != 0) continue;
             // the parts in a fixed order: kq = 0, 1, ..., KQ - 1
 #pragma unroll
-            for (int q = 1; q < KQ; ++q) z += red[it & 1][f + F * q][lane];
+            for (int q = 1; q < KQ; ++q) z += red[((it & 1) * NW + f + F * q) * 64 + lane];
         } else {
             if (r != 0) continue;
         }
@@ -858,6 +871,19 @@ fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t
             store_y(y, y_dtype, col, a * (2.0f * (z[i] - corr) - xall));
         }
     }
+}
+
+template <bool kF16, int NV, int NW, int F, int IT>
+__global__ void __launch_bounds__(NW * 64)
+fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
+                   const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
+    constexpr int KQ = NW / F;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
+    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];
+    __shared__ f32x4_t red[(KQ > 1 ? 2 * NW : 1) * 64];
+    __shared__ double dX[NW * 4];
+    fbi_decode1_body<kF16, NV, NW, F, IT>(x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, blockIdx.x, gridDim.x, xs,
+                                          xzero, red, dX);
 }
 
 bool w1a16_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
@@ -938,6 +964,118 @@ hipError_t launch_w1a16_decode1(const void* x, int x_f16, int64_t K, int64_t N, 
         if (wide) launch_w1a16_decode1_nw<false, kD1Waves>(xx, K, N, P, alpha, alpha_f16, y, y_dtype, s);
         else launch_w1a16_decode1_nw<false, 4>(xx, K, N, P, alpha, alpha_f16, y, y_dtype, s);
     }
+    return hipGetLastError();
+}
+
+// Several independent single-token linears in one launch. Each linear is
+// split into column groups of F fragments with 8-wave blocks, one group per
+// block: the fewest fragments per group that give at most one block per CU,
+// within at most kGroupSteps sign tiles per thread (the shapes that stay
+// under 96 VGPRs, so that three blocks share a CU: the grid holds several
+// rounds of blocks). The grid is the concatenation of the linears' blocks,
+// those with the most sign bytes per block first. A block finds its linear
+// from the table in the kernel arguments (uniform selects, no indexing) and
+// runs the same body as the one-linear kernel.
+constexpr int kGroupSteps = 4;
+struct D1Item {
+    const uint16_t* x;
+    const uint32_t* P;
+    const void* alpha;
+    void* y;
+    int64_t K, N, TQ;
+    int first, nblk, cfg;   // first block, block count, (NV, F) case
+};
+struct D1Group {
+    D1Item it[kGroupMax];
+    int count, alpha_f16, y_dtype;
+};
+
+template <bool kF16>
+__global__ void __launch_bounds__(kD1Waves * 64)
+fbi_decode1_group_kernel(const D1Group g) {
+    constexpr int NW = kD1Waves;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
+    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];
+    __shared__ f32x4_t red[2 * NW * 64];
+    __shared__ double dX[NW * 4];
+    D1Item it = g.it[0];
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < g.count && int(blockIdx.x) >= g.it[i].first) it = g.it[i];
+    const int64_t bid = int64_t(blockIdx.x) - it.first;
+#define BGB_G1(C, NVV, FV)                                                                                      \
+    case C:                                                                                                  \
+        fbi_decode1_body<kF16, NVV, NW, FV, 1>(it.x, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y,    \
+                                               g.y_dtype, bid, it.nblk, xs, xzero, red, dX);                  \
+        break;
+    switch (it.cfg) {
+        BGB_G1(0, 1, 1)
+        BGB_G1(1, 1, 2)
+        BGB_G1(2, 1, 4)
+        BGB_G1(3, 2, 1)
+        BGB_G1(4, 2, 2)
+        BGB_G1(5, 4, 1)
+        default: break;
+    }
+#undef BGB_G1
+}
+
+bool w1a16_decode1_group_supported(const W1a16Item* items, int count) {
+    if (count < 0 || count > kGroupMax) return false;
+    for (int i = 0; i < count; ++i)
+        if (!w1a16_decode1_supported(items[i].K)) return false;
+    return true;
+}
+
+hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f16, int alpha_f16, int y_dtype,
+                                      hipStream_t s) {
+    if (!w1a16_decode1_group_supported(items, count)) return hipErrorInvalidValue;
+    constexpr int NW = kD1Waves, NT = NW * 64;
+    D1Group g{};
+    int order[kGroupMax], n = 0;
+    int64_t cost[kGroupMax];
+    for (int i = 0; i < count; ++i) {
+        if (items[i].N <= 0) continue;                   // an empty linear takes no blocks
+        const W1a16Item& in = items[i];
+        D1Item& d = g.it[n];
+        d.x = static_cast<const uint16_t*>(in.x);
+        d.P = in.P;
+        d.alpha = in.alpha;
+        d.y = in.y;
+        d.K = in.K;
+        d.N = in.N;
+        d.TQ = tiles_per_col(in.K);
+        const int nv = int((d.TQ * 16 + NT - 1) / NT);
+        const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : 4;
+        const int64_t frags = (in.N + 15) / 16;
+        int F = 1;
+        while (nvp * 2 * F <= kGroupSteps && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
+        d.nblk = int((frags + F - 1) / F);
+        d.cfg = nvp == 1 ? (F == 1 ? 0 : F == 2 ? 1 : 2) : nvp == 2 ? (F == 1 ? 3 : 4) : 5;
+        cost[n] = int64_t(F) * d.TQ;
+        order[n] = n;
+        ++n;
+    }
+    if (n == 0) return hipSuccess;
+    // heaviest blocks first (stable), then the prefix sums of the block counts
+    for (int a = 1; a < n; ++a)
+        for (int b = a; b > 0 && cost[order[b]] > cost[order[b - 1]]; --b) {
+            const int t = order[b];
+            order[b] = order[b - 1];
+            order[b - 1] = t;
+        }
+    D1Group h{};
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        h.it[i] = g.it[order[i]];
+        h.it[i].first = int(total);
+        total += h.it[i].nblk;
+    }
+    h.count = n;
+    h.alpha_f16 = alpha_f16;
+    h.y_dtype = y_dtype;
+    if (x_f16) fbi_decode1_group_kernel<true><<<unsigned(total), NT, 0, s>>>(h);
+    else fbi_decode1_group_kernel<false><<<unsigned(total), NT, 0, s>>>(h);
     return hipGetLastError();
 }
 

@@ -158,6 +158,48 @@ int fbi_linear_w1a16(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N
                      const uint32_t* P, const void* alpha, int alpha_dtype,
                      void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream);
 
+/* One FBI-linear of a group: its activations, packed signs, scales, output
+ * and shape, with the layouts of fbi_linear_w1a16. */
+typedef struct {
+    const void* x;        /* [M][K] 16-bit */
+    const uint32_t* P;    /* packed signs of the K x N weight */
+    const void* alpha;    /* [N] */
+    void* y;              /* [M][N] */
+    int64_t K, N;
+} bgb_w1a16_item;
+
+#define BGB_GROUP_MAX 8
+
+/*
+ * fbi_linear_w1a16_group -- several independent FBI-linears (FBI-linear
+ * paragraph of the FBI-LLM news rewrite; the model replaces every linear of a
+ * layer) over the same number of tokens M and the same dtypes: for each item,
+ * the result of fbi_linear_w1a16(item.x, x_dtype, M, item.K, item.N, item.P,
+ * item.alpha, alpha_dtype, item.y, y_dtype, ...). For a single token (M = 1)
+ * with every K <= 16384 all items run in one launch (each item split into
+ * column groups of its own, one per block); otherwise they run one after
+ * another in the order given. Sums are accumulated in fp32 in a fixed order,
+ * so results are the same from run to run; the one-launch form may group a
+ * linear's K range differently from fbi_linear_w1a16 (a different rounding
+ * order of the fp32 sum, not bit-identical to it).
+ * items: a host array of `count` items (0 <= count <= BGB_GROUP_MAX), read
+ * during the call only. Items with N = 0 are skipped; every other item is
+ * checked as fbi_linear_w1a16 checks its arguments. No output may overlap
+ * any item's x, P, alpha or another item's y (the items may run
+ * concurrently): BGB_EINVAL otherwise.
+ * ws: bgb_group_workspace_bytes(items, count, M) bytes (0 for the one-launch
+ * form, where ws may be NULL).
+ * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP; a rejected call
+ * launches nothing.
+ */
+int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, int x_dtype,
+                           int alpha_dtype, int y_dtype, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Workspace bytes of fbi_linear_w1a16_group for these items (the largest
+ * item's fbi_linear_w1a16 workspace, 0 for the one-launch form). */
+size_t bgb_group_workspace_bytes(const bgb_w1a16_item* items, int count, int64_t M);
+
 /*
  * bitlinear_w1a8 -- BitLinear forward (BitNet blog, section 一, eq. (4)-(8)).
  *   h = LN(x) per token (biased variance, no affine): E(x), Var(x) in fp64,

@@ -114,6 +114,61 @@ def test_fbi_linear_validation(lib):
     assert call_fbi(lib, M=0) == 0 and call_fbi(lib, N=0) == 0
 
 
+def group(specs):
+    """specs: (x, P, alpha, y, K, N) per item, fake addresses."""
+    arr = (bgb._Item * max(len(specs), 1))()
+    for i, sp in enumerate(specs):
+        arr[i] = bgb._Item(*sp)
+    return arr
+
+
+def call_group(lib, specs, M=1, xdt=2, adt=1, ydt=2, ws=A, wsb=1 << 30, count=None):
+    n = len(specs) if count is None else count
+    return lib.fbi_linear_w1a16_group(group(specs), n, M, xdt, adt, ydt, ws, wsb, None)
+
+
+MB = 1 << 20
+
+
+def test_group_validation(lib):
+    # four independent linears, each on its own megabyte-aligned fake region
+    base = [(A + (4 * i) * 64 * MB, A + (4 * i + 1) * 64 * MB, A + (4 * i + 2) * 64 * MB,
+             A + (4 * i + 3) * 64 * MB, 4096, 4096) for i in range(4)]
+    assert bgb.group_workspace_bytes([], 1) == 0
+    assert lib.bgb_group_workspace_bytes(group(base), 4, 1) == 0          # one launch
+    assert call_group(lib, [], count=0) == 0
+    assert call_group(lib, base, count=bgb.GROUP_MAX + 1) == BAD
+    assert call_group(lib, base, count=-1) == BAD
+    assert call_group(lib, base, xdt=0) == UNSUP
+    assert call_group(lib, base, adt=2) == UNSUP
+    assert call_group(lib, base, M=-1) == BAD
+    bad = list(base)
+    bad[2] = (0,) + bad[2][1:]                                             # null x
+    assert call_group(lib, bad) == BAD
+    bad = list(base)
+    bad[1] = bad[1][:4] + (40, 4096)                                       # K % 32 != 0
+    assert call_group(lib, bad) == BAD
+    bad = list(base)
+    bad[3] = bad[3][:3] + (bad[0][1] + 256,) + bad[3][4:]                  # y inside another item's P
+    assert call_group(lib, bad) == BAD
+    bad = list(base)
+    bad[3] = bad[3][:3] + (bad[0][3] + 4096,) + bad[3][4:]                 # two outputs overlap
+    assert call_group(lib, bad) == BAD
+    bad = list(base)
+    bad[0] = bad[0][:3] + (bad[0][0] + 16,) + bad[0][4:]                   # y over its own x
+    assert call_group(lib, bad) == BAD
+    empty = list(base)
+    empty[1] = (0, 0, 0, 0, 4096, 0)                                        # N = 0: skipped, unchecked
+    assert call_group(lib, empty, M=0) == 0
+    # several tokens: the items run one after another on the largest item's workspace
+    split = [b[:4] + (11008, 4096) for b in base]
+    need = lib.bgb_group_workspace_bytes(group(split), 4, 16)
+    assert need == max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, 16, 11008, 4096), 0)
+    if need:
+        assert call_group(lib, split, M=16, wsb=need - 1) == BAD
+        assert call_group(lib, split, M=16, ws=None) == BAD
+
+
 def call_bl(lib, x=A, xdt=0, M=1, K=64, N=8, P=A, beta=A, qp=None, y=A, xq=None, g=None, acc=None, ws=A,
             wsb=1 << 30):
     return lib.bitlinear_w1a8(x, xdt, M, K, N, P, beta, qp, y, xq, g, acc, ws, wsb, None)
