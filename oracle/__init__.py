@@ -53,6 +53,7 @@ def _load():
     lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
     lib.oracle_fbi_linear.argtypes = [P, ctypes.c_int, I64, I64, P, I64, P, P]
+    lib.oracle_fbi_backward.argtypes = [P, P, ctypes.c_int, I64, I64, P, I64, P, P, P, P]
     lib.oracle_ln_absmax_quant.argtypes = [P, I64, I64, ctypes.c_double, ctypes.c_int,
                                            ctypes.c_float, ctypes.c_int, ctypes.c_int, P, P, P, P]
     lib.oracle_bitlinear_acc.argtypes = [P, I64, I64, P, I64, ctypes.c_float, P]
@@ -60,7 +61,7 @@ def _load():
                                          ctypes.c_int, P]
     lib.oracle_ternary.argtypes = [P, I64, I64, ctypes.c_float, P, P]
     lib.oracle_int8_acc.argtypes = [P, I64, I64, P, I64, P]
-    for name in ("oracle_ternary", "oracle_int8_acc",
+    for name in ("oracle_ternary", "oracle_int8_acc", "oracle_fbi_backward",
                  "oracle_sign_fbi", "oracle_sign_bitnet", "oracle_fbi_alpha",
                  "oracle_bitnet_scalars", "oracle_pack", "oracle_fbi_linear",
                  "oracle_ln_absmax_quant", "oracle_bitlinear_acc", "oracle_bitlinear_out"):
@@ -158,6 +159,27 @@ def fbi_linear(x_bits: np.ndarray, W: np.ndarray, alpha: np.ndarray, x_kind: str
     _check(_load().oracle_fbi_linear(_ptr(x_bits), kind, M, K, _ptr(W), N, _ptr(alpha), _ptr(y)),
            "fbi_linear")
     return y
+
+
+def fbi_backward(x_bits: np.ndarray, dy_bits: np.ndarray, W: np.ndarray, alpha: np.ndarray,
+                 x_kind: str = "bf16"):
+    """FBI-linear backward through the identity STE: (dX [M][K], dalpha [N], dW [K][N]) in fp64,
+    for 16-bit x and dY given as bit patterns of the same kind."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    dy_bits = np.ascontiguousarray(dy_bits, dtype=np.uint16)
+    W = _f32(W)
+    alpha = np.ascontiguousarray(alpha, dtype=np.float32)
+    M, K = x_bits.shape
+    K2, N = W.shape
+    if K2 != K or alpha.shape != (N,) or dy_bits.shape != (M, N):
+        raise ValueError("shape mismatch")
+    dx = np.empty((M, K), np.float64)
+    da = np.empty(N, np.float64)
+    dw = np.empty((K, N), np.float64)
+    kind = {"bf16": 0, "f16": 1}[x_kind]
+    _check(_load().oracle_fbi_backward(_ptr(x_bits), _ptr(dy_bits), kind, M, K, _ptr(W), N, _ptr(alpha),
+                                       _ptr(dx), _ptr(da), _ptr(dw)), "fbi_backward")
+    return dx, da, dw
 
 
 def ln_absmax_quant(x: np.ndarray, ln_eps: float = 1e-5, bits: int = 8, q_eps: float = 1e-3,

@@ -161,6 +161,56 @@ int oracle_fbi_linear(const uint16_t* x, int x_kind, int64_t M, int64_t K,
     return 0;
 }
 
+/* [FBI-news], training paragraph: gradients pass the sign function through
+ * the straight-through estimator, taken as the identity (no clipping is
+ * stated). With y = alpha_j sum_i s_ij x_mi: dX = (dY * alpha) S^T,
+ * dalpha_j = sum_m dY_mj z_mj with z = x S, and the gradient of W_b =
+ * alpha * sign(W) passed to W, dW_ij = alpha_j sum_m x_mi dY_mj. One loop
+ * nest per output, fp64, ascending index order. */
+int oracle_fbi_backward(const uint16_t* x, const uint16_t* dy, int kind, int64_t M, int64_t K,
+                        const float* W, int64_t N, const float* alpha, double* dx, double* dalpha,
+                        double* dw) {
+    if (M < 0 || K < 0 || N < 0 || !W || !alpha || !dy) return -1;
+    if (kind != 0 && kind != 1) return -1;
+    if ((dalpha || dw) && !x) return -1;
+#define ORC_V16(b) ((double)(kind == 0 ? oracle_bf16_to_f32(b) : oracle_f16_to_f32(b)))
+    if (dx) {
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t i = 0; i < K; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < N; ++j) {
+                    const double g = ORC_V16(dy[m * N + j]) * (double)alpha[j];
+                    acc += (W[i * N + j] > 0.0f) ? g : -g;
+                }
+                dx[m * K + i] = acc;
+            }
+    }
+    if (dalpha) {
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double z = 0.0;
+                for (int64_t i = 0; i < K; ++i) {
+                    const double xv = ORC_V16(x[m * K + i]);
+                    z += (W[i * N + j] > 0.0f) ? xv : -xv;
+                }
+                acc += ORC_V16(dy[m * N + j]) * z;
+            }
+            dalpha[j] = acc;
+        }
+    }
+    if (dw) {
+        for (int64_t i = 0; i < K; ++i)
+            for (int64_t j = 0; j < N; ++j) {
+                double acc = 0.0;
+                for (int64_t m = 0; m < M; ++m) acc += ORC_V16(x[m * K + i]) * ORC_V16(dy[m * N + j]);
+                dw[i * N + j] = (double)alpha[j] * acc;
+            }
+    }
+#undef ORC_V16
+    return 0;
+}
+
 /* ------------------------------------------------------ BitLinear prologue -- */
 
 /* [BitNet] eq. (8): LN(x) = (x - E(x)) / sqrt(Var(x) + eps), per token over K,

@@ -52,6 +52,19 @@ float oracle_bf16_to_f32(uint16_t b);
 int oracle_fbi_linear(const uint16_t* x, int x_kind, int64_t M, int64_t K,
                       const float* W, int64_t N, const float* alpha, double* y);
 
+/* FBI-linear backward through the straight-through estimator ([FBI-news],
+ * training paragraph: the STE carries gradients through the sign function).
+ * Given dY [M][N] (16-bit, bit patterns of the same kind as x):
+ *   dX[m][i]  = sum_j dY[m][j] alpha_j s_ij                       [M][K]
+ *   dalpha_j  = sum_m dY[m][j] z[m][j],  z = x S (unscaled forward) [N]
+ *   dW[i][j]  = alpha_j sum_m x[m][i] dY[m][j]                    [K][N]
+ * (dW: the gradient reaching W_b = alpha * sign(W), passed through sign as
+ * the identity, since the pages state no clipping). fp64; any output may be
+ * NULL. */
+int oracle_fbi_backward(const uint16_t* x, const uint16_t* dy, int kind, int64_t M, int64_t K,
+                        const float* W, int64_t N, const float* alpha, double* dx, double* dalpha,
+                        double* dw);
+
 /* BitLinear prologue: per-token LayerNorm (no affine), then absmax quantization to
  * [-Q_b+eps, Q_b-eps] with Q_b = 2^(bits-1), gamma = max |LN(x)| over the tensor.
  * Statistics in fp64; the quantization decision in fp32 (see oracle.c).

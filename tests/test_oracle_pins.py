@@ -463,3 +463,83 @@ def test_ternary_pack_and_product(orc):
     assert np.array_equal(acc, q.astype(np.int64) @ T.astype(np.int64))
     assert np.all(orc.int8_acc(q, np.zeros((K, N), np.int8)) == 0)
     assert np.array_equal(orc.int8_acc(q, np.ones((K, N), np.int8))[:, 0], q.astype(np.int64).sum(1))
+
+
+# ------------------------------------------------ FBI-linear backward (STE) --
+
+def _bwd_case(seed, M, K, N):
+    W = syn.normal_f32(seed, 0, (K, N), std=0.02)
+    x = syn.f32_to_bf16_bits(syn.normal_f32(seed, 1, (M, K)))
+    dy = syn.f32_to_bf16_bits(syn.normal_f32(seed, 2, (M, N)))
+    alpha = np.linspace(0.25, 1.75, N).astype(np.float32)   # distinct per column: a swapped axis shows
+    return W, x, dy, alpha
+
+
+@pytest.mark.parametrize("M,K,N", [(3, 64, 40), (5, 96, 33)])
+def test_fbi_backward_against_the_forward(orc, M, K, N):
+    """The forward is linear in x and in alpha, so its gradients are read off the
+    forward oracle itself: with L = <dY, y(x, alpha)>, dX[m][i] = L at x = e_mi,
+    i.e. dY times the forward of the identity batch transposed; dalpha_j = L at
+    alpha = e_j, i.e. sum_m dY z with z the forward at alpha = 1."""
+    W, x, dy, alpha = _bwd_case(11 + M, M, K, N)
+    dx, da, dw = orc.fbi_backward(x, dy, W, alpha)
+    dyf = syn.bf16_bits_to_f32(dy).astype(np.float64)
+    eye = syn.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    rows = orc.fbi_linear(eye, W, alpha)                    # [K][N]: alpha_j s_ij, through the forward
+    assert np.allclose(dx, dyf @ rows.T, rtol=1e-12, atol=1e-12)
+    z = orc.fbi_linear(x, W, np.ones(N, np.float32))        # [M][N]: x S
+    assert np.allclose(da, (dyf * z).sum(0), rtol=1e-12, atol=1e-12)
+    # Euler: each argument enters linearly, so <dX, x> = <dalpha, alpha> =
+    # <dW, S> = <dY, y>
+    y = orc.fbi_linear(x, W, alpha)
+    L = float((dyf * y).sum())
+    xf = syn.bf16_bits_to_f32(x).astype(np.float64)
+    S = orc.sign_fbi(W).astype(np.float64)
+    for v in (float((dx * xf).sum()), float((da * alpha).sum()), float((dw * S).sum())):
+        assert abs(v - L) <= 1e-10 * max(1.0, abs(L))
+
+
+def test_fbi_backward_unit_probes(orc):
+    """x = e_i and dY = e_j (one token) give dW = alpha_j at (i, j) and zero
+    elsewhere, dX = alpha_j s_(., j) and dalpha_j = s_ij: pins the index order of
+    all three outputs."""
+    K, N = 64, 40
+    W = syn.normal_f32(21, 0, (K, N), std=0.02)
+    alpha = np.linspace(0.5, 2.0, N).astype(np.float32)
+    S = orc.sign_fbi(W)
+    for i, j in [(0, 0), (5, 17), (63, 39), (31, 1)]:
+        x = np.zeros((1, K), np.float32)
+        x[0, i] = 1.0
+        dy = np.zeros((1, N), np.float32)
+        dy[0, j] = 1.0
+        dx, da, dw = orc.fbi_backward(syn.f32_to_bf16_bits(x), syn.f32_to_bf16_bits(dy), W, alpha)
+        want = np.zeros((K, N))
+        want[i, j] = alpha[j]
+        assert np.array_equal(dw, want)
+        assert np.array_equal(dx[0], alpha[j] * S[:, j].astype(np.float64))
+        want_da = np.zeros(N)
+        want_da[j] = S[i, j]
+        assert np.array_equal(da, want_da)
+
+
+def test_fbi_backward_exact_rational(orc):
+    """Tiny case recomputed in exact rationals by this test's own loops; the fp64
+    oracle must agree to fp64 rounding."""
+    M, K, N = 2, 32, 5
+    W, x, dy, alpha = _bwd_case(31, M, K, N)
+    dx, da, dw = orc.fbi_backward(x, dy, W, alpha)
+    xf = [[Fraction(float(v)) for v in row] for row in syn.bf16_bits_to_f32(x)]
+    gf = [[Fraction(float(v)) for v in row] for row in syn.bf16_bits_to_f32(dy)]
+    af = [Fraction(float(a)) for a in alpha]
+    s = [[1 if W[i, j] > 0 else -1 for j in range(N)] for i in range(K)]
+    for m in range(M):
+        for i in range(K):
+            e = sum(gf[m][j] * af[j] * s[i][j] for j in range(N))
+            assert abs(Fraction(dx[m, i]) - e) <= abs(e) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+    for j in range(N):
+        e = sum(gf[m][j] * sum(xf[m][i] * s[i][j] for i in range(K)) for m in range(M))
+        assert abs(Fraction(da[j]) - e) <= abs(e) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+    for i in range(K):
+        for j in range(N):
+            e = af[j] * sum(xf[m][i] * gf[m][j] for m in range(M))
+            assert abs(Fraction(dw[i, j]) - e) <= abs(e) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
