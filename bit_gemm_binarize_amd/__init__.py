@@ -23,7 +23,7 @@ __all__ = [
     "OP_BITLINEAR158", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
     "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M", "W1A16_DECODE_MAX_M",
     "ROUND_TRUNC", "ROUND_RNE", "GAMMA_TENSOR", "GAMMA_TOKEN", "fbi_linear_w1a16_group", "group_workspace_bytes",
-    "GROUP_MAX",
+    "GROUP_MAX", "fbi_pack_transposed", "fbi_linear_w1a16_backward", "OP_FBI_BACKWARD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,13 +31,14 @@ _LIB_PATH = os.path.join(_HERE, "libbgb.so")
 
 BGB_F32, BGB_F16, BGB_BF16 = 0, 1, 2
 MODE_FBI, MODE_BITNET, MODE_TERNARY = 0, 1, 2
-OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR, OP_BITLINEAR158 = 0, 1, 2, 3, 4
+OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR, OP_BITLINEAR158, OP_FBI_BACKWARD = 0, 1, 2, 3, 4, 5
 GEMV_MAX_M = 32          # BitLinear: M <= 32 runs the decode kernels, above: the MFMA GEMM
 W1A16_DECODE_MAX_M = 64  # FBI-linear: M <= 64 runs the decode kernels, above: the MFMA GEMM
 GROUP_MAX = 8            # linears per fbi_linear_w1a16_group call
 
 EXPORTS = ("bgb_packed_bytes", "bgb_workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
-           "fbi_linear_w1a16_group", "bgb_group_workspace_bytes",
+           "fbi_linear_w1a16_group", "bgb_group_workspace_bytes", "fbi_pack_transposed",
+           "fbi_linear_w1a16_backward",
            "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bitlinear158_w1a8",
            "bitlinear158_matmul", "bgb_status_string",
            "bgb_last_hip_error", "bgb_version")
@@ -105,6 +106,10 @@ def load():
     lib.fbi_linear_w1a16_group.restype = I
     lib.bgb_group_workspace_bytes.argtypes = [ctypes.POINTER(_Item), I, I64]
     lib.bgb_group_workspace_bytes.restype = SZ
+    lib.fbi_pack_transposed.argtypes = [P, I64, I64, P, P]
+    lib.fbi_pack_transposed.restype = I
+    lib.fbi_linear_w1a16_backward.argtypes = [P, P, I, I64, I64, I64, P, P, P, I, P, I, P, P, P, SZ, P]
+    lib.fbi_linear_w1a16_backward.restype = I
     lib.bitlinear_w1a8.argtypes = [P, I, I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, P, P, SZ, P]
     lib.bitlinear_w1a8.restype = I
     lib.bitlinear_quantize.argtypes = [P, I, I64, I64, ctypes.POINTER(_QP), P, P, P, SZ, P]
@@ -244,6 +249,35 @@ def fbi_linear_w1a16(x, P, alpha, N: int, y_dtype=None, *, y=None, ws=None, stre
     _check(load().fbi_linear_w1a16(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(alpha), _dt(alpha), _ptr(y), _dt(y),
                                    _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def fbi_pack_transposed(P, K: int, N: int, *, PT=None, stream=None):
+    """Packed signs of [S^T; S^T] (2N x K) for the backward product; N % 32 == 0."""
+    torch = _torch()
+    if PT is None:
+        PT = torch.empty(max(packed_bytes(2 * N, K) // 4, 4), dtype=torch.int32, device=P.device)
+    _check(load().fbi_pack_transposed(_ptr(P), K, N, _ptr(PT), _stream(stream)))
+    return PT
+
+
+def fbi_linear_w1a16_backward(dy, x, P, PT, alpha, *, want=("dx", "dalpha", "dw"), dx_dtype=None, ws=None,
+                              stream=None):
+    """FBI-linear backward (identity straight-through estimator). dy: [M][N], x: [M][K] (bf16 or f16,
+    the same); P / PT: packed signs and their transposed copy. Returns (dx, dalpha, dw), None for
+    what is not in `want`."""
+    torch = _torch()
+    M, N = dy.shape
+    K = x.shape[1]
+    dev = dy.device
+    dx = (torch.empty((M, K), dtype=torch.float32 if dx_dtype is None else dx_dtype, device=dev)
+          if "dx" in want else None)
+    da = torch.empty(max(N, 4), dtype=torch.float32, device=dev)[:N] if "dalpha" in want else None
+    dw = torch.empty((K, N), dtype=torch.float32, device=dev) if "dw" in want else None
+    ws = _workspace(OP_FBI_BACKWARD, M, K, N, ws, dev)
+    _check(load().fbi_linear_w1a16_backward(_ptr(dy), _ptr(x), _dt(dy), M, K, N, _ptr(P), _ptr(PT), _ptr(alpha),
+                                            _dt(alpha), _ptr(dx), _dt(dx) if dx is not None else BGB_F32,
+                                            _ptr(da), _ptr(dw), _ptr(ws), ws.numel(), _stream(stream)))
+    return dx, da, dw
 
 
 def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=None, want_q=False,

@@ -49,6 +49,7 @@ size_t bgb_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
         case BGB_OP_FBI_LINEAR: return bgb::FbiLinearWs::make(M, K, N).total;
         case BGB_OP_BITLINEAR: return bgb::BitlinearWs::make(M, K, N).total;
         case BGB_OP_BITLINEAR158: return bgb::BitlinearWs::make(M, K, N, true).total;
+        case BGB_OP_FBI_BACKWARD: return bgb::FbiBackwardWs::make(M, K, N).total;
         default: return 0;
     }
 }
@@ -204,6 +205,53 @@ int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, in
         if (rc) return rc;
     }
     return BGB_OK;
+}
+
+int fbi_pack_transposed(const uint32_t* P, int64_t K, int64_t N, uint32_t* PT, void* stream) {
+    int rc = check_shape(0, K, N);
+    if (rc) return rc;
+    if (N % 32 != 0 || 2 * N > bgb::kMaxK) return BGB_EINVAL;
+    if (N == 0) return BGB_OK;
+    if (!P || !PT || !aligned16(P) || !aligned16(PT)) return BGB_EINVAL;
+    if (overlaps(P, bgb_packed_bytes(K, N), PT, bgb_packed_bytes(2 * N, K))) return BGB_EINVAL;
+    return finish(bgb::launch_pack_transpose(P, K, N, PT, static_cast<hipStream_t>(stream)));
+}
+
+int fbi_linear_w1a16_backward(const void* dy, const void* x, int dtype, int64_t M, int64_t K, int64_t N,
+                              const uint32_t* P, const uint32_t* PT, const void* alpha, int alpha_dtype, void* dx,
+                              int dx_dtype, float* dalpha, float* dw, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(M, K, N);
+    if (rc) return rc;
+    if (dtype != BGB_BF16 && dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (dx && dx_dtype != BGB_F32 && dx_dtype != BGB_BF16 && dx_dtype != BGB_F16) return BGB_EUNSUPPORTED;
+    if (N % 32 != 0 || 2 * N > bgb::kMaxK || M * 2 * N > kMaxElems) return BGB_EINVAL;
+    if (M == 0 || N == 0) return BGB_OK;          // empty: nothing is read or written
+    if (!dy || !alpha || !aligned16(dy) || !aligned16(alpha)) return BGB_EINVAL;
+    if (dx && (!PT || !aligned16(PT) || !aligned16(dx))) return BGB_EINVAL;
+    if ((dalpha || dw) && (!x || !aligned16(x))) return BGB_EINVAL;
+    if (dalpha && (!P || !aligned16(P) || !aligned16(dalpha))) return BGB_EINVAL;
+    if (dw && !aligned16(dw)) return BGB_EINVAL;
+    const bgb::FbiBackwardWs lay = bgb::FbiBackwardWs::make(M, K, N);
+    if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int f16 = dtype == BGB_F16, a_f16 = alpha_dtype == BGB_F16;
+    uint16_t* g2 = dx ? reinterpret_cast<uint16_t*>(carve(ws, lay.g2)) : nullptr;
+    float* ones = reinterpret_cast<float*>(carve(ws, lay.ones));
+    void* inner = carve(ws, lay.inner);
+    rc = finish(bgb::launch_fbi_backward_parts(dy, f16, x, M, K, N, alpha, a_f16, g2, ones, K > N ? K : N, dw, s));
+    if (rc) return rc;
+    if (dx) {                                     // dX = [g_hi g_lo] [S^T; S^T]
+        rc = fbi_run(g2, BGB_BF16, M, 2 * N, K, PT, ones, BGB_F32, dx, dx_dtype, inner, s);
+        if (rc) return rc;
+    }
+    if (dalpha) {                                 // z = x S, then dalpha = sum_m dY z
+        float* z = reinterpret_cast<float*>(carve(ws, lay.z));
+        rc = fbi_run(x, dtype, M, K, N, P, ones, BGB_F32, z, BGB_F32, inner, s);
+        if (rc) return rc;
+        rc = finish(bgb::launch_dalpha(dy, f16, z, M, N, dalpha, s));
+    }
+    return rc;
 }
 
 // Shared checks of the BitLinear entry points; fills qb/lim from qp.

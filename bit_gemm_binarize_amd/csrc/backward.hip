@@ -1,0 +1,245 @@
+// FBI-linear backward through the straight-through estimator (FBI-LLM news
+// rewrite, training paragraph: the STE carries gradients through the sign
+// function, taken here as the identity since no clipping is stated). With
+// y = alpha_j sum_i s_ij x_mi and the output gradient dY:
+//   dX[m][i] = sum_j s_ij (alpha_j dY[m][j])      -- a product with S^T
+//   dalpha_j = sum_m dY[m][j] z[m][j], z = x S     -- the forward at alpha = 1
+//   dW[i][j] = alpha_j sum_m x[m][i] dY[m][j]      -- a dense product over tokens
+//
+// dX runs on the forward kernels: S^T is packed once (pack_transpose_kernel)
+// in the forward's format, twice along its contraction axis, and the scaled
+// gradient g = alpha * dY (fp32) enters as two 16-bit halves g_hi = bf16(g),
+// g_lo = bf16(g - g_hi) laid side by side ([M][2N]): sum_j s_ij (g_hi + g_lo)
+// carries g to about 16 significant bits, where a single bf16 copy of g would
+// carry 8.
+#include "bgb_device.hpp"
+#include "bgb_internal.hpp"
+
+namespace bgb {
+
+// ---------------------------------------------------------- S^T, packed ----
+// One wave per (32-row word t of S, 64 columns j0..j0+63): lane L holds word
+// (t, j0 + L); the 32 ballots over bit b give, for row i = 32 t + b of S,
+// the bits of columns j0..j0+63, i.e. words (j0 / 32, i) and (j0 / 32 + 1, i)
+// of S^T, stored in both copies (rows j and N + j of the doubled matrix).
+// Requires N % 32 == 0 (whole words per copy).
+__global__ void __launch_bounds__(256)
+pack_transpose_kernel(const uint32_t* __restrict__ P, int64_t K, int64_t N, uint32_t* __restrict__ PT) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t nj = (N + 63) / 64, T = K / 32;
+    if (wid >= T * nj) return;                          // uniform per wave
+    const int64_t t = wid / nj, j0 = (wid % nj) * 64;
+    const int64_t j = j0 + lane;
+    const uint32_t w = j < N ? P[((t >> 2) * N + j) * 4 + (t & 3)] : 0u;
+    uint64_t mine = 0;                                  // lane b < 32 keeps the ballot of bit b
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+        const uint64_t m = __ballot((w >> b) & 1u);
+        mine = lane == b ? m : mine;
+    }
+    if (lane >= 32) return;
+    const int64_t i = 32 * t + lane;                    // column of S^T
+    const int64_t half = N / 32;                        // words per copy along the contraction axis
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t tw = j0 / 32 + h;                 // word of S^T in the first copy
+        if (tw >= half) break;
+        const uint32_t word = uint32_t(mine >> (32 * h));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int64_t tt = tw + c * half;
+            PT[((tt >> 2) * K + i) * 4 + (tt & 3)] = word;
+        }
+    }
+}
+
+// Zero words of the last 128-row tile past the doubled contraction axis
+// (2N / 32 words when that is not a multiple of 4).
+__global__ void __launch_bounds__(256)
+pack_transpose_pad_kernel(int64_t K, int64_t T2, int64_t TQ2, uint32_t* __restrict__ PT) {
+    const int64_t n = (4 * TQ2 - T2) * K;
+    const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= n) return;
+    const int64_t tt = T2 + e / K, i = e % K;
+    PT[((tt >> 2) * K + i) * 4 + (tt & 3)] = 0u;
+}
+
+hipError_t launch_pack_transpose(const uint32_t* P, int64_t K, int64_t N, uint32_t* PT, hipStream_t s) {
+    const int64_t waves = (K / 32) * ((N + 63) / 64);
+    pack_transpose_kernel<<<unsigned((waves + 3) / 4), 256, 0, s>>>(P, K, N, PT);
+    const int64_t T2 = 2 * N / 32, TQ2 = tiles_per_col(2 * N);
+    const int64_t pad = (4 * TQ2 - T2) * K;
+    if (pad > 0) pack_transpose_pad_kernel<<<unsigned((pad + 255) / 256), 256, 0, s>>>(K, T2, TQ2, PT);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ g = alpha * dY -----
+// g = fl32(dY alpha_j); row m of the output holds bf16(g) for j < N and
+// bf16(g - bf16(g)) at N + j (g - bf16(g) is exact in fp32).
+__global__ void __launch_bounds__(256)
+split_scaled_grad_kernel(const uint16_t* __restrict__ dy, int dy_f16, int64_t M, int64_t N,
+                         const void* __restrict__ alpha, int alpha_f16, uint16_t* __restrict__ g2) {
+    const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= M * N) return;
+    const int64_t m = e / N, j = e % N;
+    const float d = dy_f16 ? f16_to_f32(dy[e]) : bf16_to_f32(dy[e]);
+    const float a = alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[j]) : static_cast<const float*>(alpha)[j];
+    const float g = d * a;
+    const uint16_t hi = f32_to_bf16_rne(g);
+    g2[m * 2 * N + j] = hi;
+    g2[m * 2 * N + N + j] = f32_to_bf16_rne(g - bf16_to_f32(hi));
+}
+
+__global__ void __launch_bounds__(256) fill_ones_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (e < n) p[e] = 1.0f;
+}
+
+// ------------------------------------------------ dalpha = sum_m dY z ------
+// One thread per column, tokens in ascending order, fp64 sum of the fp32
+// products of dY (exact in fp32) and z.
+__global__ void __launch_bounds__(256)
+dalpha_kernel(const uint16_t* __restrict__ dy, int dy_f16, const float* __restrict__ z, int64_t M, int64_t N,
+              float* __restrict__ dalpha) {
+    const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (j >= N) return;
+    double acc = 0.0;
+    for (int64_t m = 0; m < M; ++m) {
+        const float d = dy_f16 ? f16_to_f32(dy[m * N + j]) : bf16_to_f32(dy[m * N + j]);
+        acc += double(d) * double(z[m * N + j]);
+    }
+    dalpha[j] = float(acc);
+}
+
+// ------------------------------------------- dW = alpha * (x^T dY) --------
+// Dense 16-bit product over the tokens. A block of 4 waves computes a
+// 128 (i) x 128 (j) tile of dW, wave w the 64 x 64 quarter (w & 1, w >> 1),
+// as 4 x 4 MFMA fragments with A = dY^T (rows j) and B = x (columns i), so a
+// lane's 4 outputs are 4 consecutive j of one i (one 16-byte store). Each
+// chunk of 32 tokens is staged in LDS transposed (row = feature, 32 tokens
+// contiguous), so that an operand is one 16-byte read; the next chunk is
+// loaded into registers while the current one is multiplied. Tokens past M
+// and features past K or N read as zeros.
+constexpr int kDwTile = 128, kDwChunk = 32, kDwRow = kDwChunk + 8;   // LDS row: 32 tokens + 16 bytes of padding
+
+template <bool kF16>
+__global__ void __launch_bounds__(256)
+dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64_t M, int64_t K, int64_t N,
+          const void* __restrict__ alpha, int alpha_f16, float* __restrict__ dw) {
+    __shared__ __attribute__((aligned(16))) uint16_t xt[kDwTile * kDwRow];
+    __shared__ __attribute__((aligned(16))) uint16_t gt[kDwTile * kDwRow];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+    const int64_t i0 = int64_t(blockIdx.x) * kDwTile, j0 = int64_t(blockIdx.y) * kDwTile;
+    const int wi = (wave & 1) * 64, wj = (wave >> 1) * 64;
+
+    // loader: thread tid moves token row m0 + (tid >> 4) + 16 h (h = 0, 1),
+    // features 8 (tid & 15) .. + 7 of both tiles
+    const int lrow = tid >> 4, lcol = 8 * (tid & 15);
+    u32x4_t vx[2], vg[2];
+    auto load = [&](int64_t m0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t m = m0 + lrow + 16 * h;
+            const bool okm = m < M;
+            const int64_t ix = i0 + lcol, jg = j0 + lcol;    // K, N multiples of 32: 8-feature pieces are whole
+            const bool okx = okm && ix < K, okg = okm && jg < N;
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(x + (okx ? m * K + ix : 0));
+            const u32x4_t b = *reinterpret_cast<const u32x4_t*>(dy + (okg ? m * N + jg : 0));
+            vx[h] = a & u32x4_t(0u - uint32_t(okx));
+            vg[h] = b & u32x4_t(0u - uint32_t(okg));
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = lrow + 16 * h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t wx = vx[h][e >> 1], wg = vg[h][e >> 1];
+                xt[(lcol + e) * kDwRow + t] = uint16_t(e & 1 ? wx >> 16 : wx & 0xffffu);
+                gt[(lcol + e) * kDwRow + t] = uint16_t(e & 1 ? wg >> 16 : wg & 0xffffu);
+            }
+        }
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load(0);
+    for (int64_t m0 = 0; m0 < M; m0 += kDwChunk) {
+        __syncthreads();                                   // the previous chunk's reads are done
+        store();
+        __syncthreads();
+        if (m0 + kDwChunk < M) load(m0 + kDwChunk);
+        u32x4_t av[4], bv[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            av[f] = *reinterpret_cast<const u32x4_t*>(gt + (wj + 16 * f + r) * kDwRow + 8 * g);
+            bv[f] = *reinterpret_cast<const u32x4_t*>(xt + (wi + 16 * f + r) * kDwRow + 8 * g);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if constexpr (kF16)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av[a]),
+                                                                       __builtin_bit_cast(f16x8_t, bv[b]),
+                                                                       acc[a][b], 0, 0, 0);
+                else
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
+                                                                        __builtin_bit_cast(bf16x8_t, bv[b]),
+                                                                        acc[a][b], 0, 0, 0);
+            }
+    }
+    // lane (g, r) of fragment (a, b): j = j0 + wj + 16 a + 4 g + e, i = i0 + wi + 16 b + r
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int64_t jb = j0 + wj + 16 * a + 4 * g;
+        if (jb >= N) continue;                             // N % 32 == 0: 4 columns are all in or all out
+        float al[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            al[e] = alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[jb + e])
+                              : static_cast<const float*>(alpha)[jb + e];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t i = i0 + wi + 16 * b + r;
+            if (i >= K) continue;
+            *reinterpret_cast<f32x4_t*>(dw + i * N + jb) =
+                f32x4_t{al[0] * acc[a][b][0], al[1] * acc[a][b][1], al[2] * acc[a][b][2], al[3] * acc[a][b][3]};
+        }
+    }
+}
+
+hipError_t launch_fbi_backward_parts(const void* dy, int dy_f16, const void* x, int64_t M, int64_t K, int64_t N,
+                                     const void* alpha, int alpha_f16, uint16_t* g2, float* ones, int64_t nones,
+                                     float* dw, hipStream_t s) {
+    if (g2) {
+        const int64_t n = M * N;
+        split_scaled_grad_kernel<<<unsigned((n + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(dy), dy_f16,
+                                                                            M, N, alpha, alpha_f16, g2);
+    }
+    if (ones) fill_ones_kernel<<<unsigned((nones + 255) / 256), 256, 0, s>>>(ones, nones);
+    if (dw) {
+        const dim3 grid(unsigned((K + kDwTile - 1) / kDwTile), unsigned((N + kDwTile - 1) / kDwTile));
+        if (dy_f16)
+            dw_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), M,
+                                                 K, N, alpha, alpha_f16, dw);
+        else
+            dw_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), M,
+                                                  K, N, alpha, alpha_f16, dw);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dalpha(const void* dy, int dy_f16, const float* z, int64_t M, int64_t N, float* dalpha,
+                         hipStream_t s) {
+    dalpha_kernel<<<unsigned((N + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(dy), dy_f16, z, M, N, dalpha);
+    return hipGetLastError();
+}
+
+}  // namespace bgb

@@ -75,6 +75,22 @@ struct FbiLinearWs {        // split-K partial sums (decode or GEMM), when the p
     }
 };
 
+// FBI-linear backward: the split scaled gradient [M][2N] bf16, z [M][N] fp32,
+// a vector of ones (max(K, N) fp32), then the forward calls' own workspace.
+struct FbiBackwardWs {
+    size_t g2, z, ones, inner, total;
+    static FbiBackwardWs make(int64_t M, int64_t K, int64_t N) {
+        FbiBackwardWs w{};
+        w.g2 = 0;
+        w.z = align256(size_t(M) * size_t(2 * N) * 2);
+        w.ones = w.z + align256(size_t(M) * size_t(N) * 4);
+        w.inner = w.ones + align256(size_t(K > N ? K : N) * 4);
+        const size_t a = FbiLinearWs::make(M, 2 * N, K).total, b = FbiLinearWs::make(M, K, N).total;
+        w.total = w.inner + align256(a > b ? a : b);
+        return w;
+    }
+};
+
 struct BitlinearWs {
     size_t stats, gamma, rowsum, q, part, total;
     // N = 0: the prologue's regions only (what bitlinear_quantize touches)
@@ -144,6 +160,14 @@ struct W1a16Item {
 bool w1a16_decode1_group_supported(const W1a16Item* items, int count);
 hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f16, int alpha_f16, int y_dtype,
                                       hipStream_t s);
+
+// FBI-linear backward pieces (backward.hip).
+hipError_t launch_pack_transpose(const uint32_t* P, int64_t K, int64_t N, uint32_t* PT, hipStream_t s);
+hipError_t launch_fbi_backward_parts(const void* dy, int dy_f16, const void* x, int64_t M, int64_t K, int64_t N,
+                                     const void* alpha, int alpha_f16, uint16_t* g2, float* ones, int64_t nones,
+                                     float* dw, hipStream_t s);
+hipError_t launch_dalpha(const void* dy, int dy_f16, const float* z, int64_t M, int64_t N, float* dalpha,
+                         hipStream_t s);
 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             int gstride, const float* beta, float qb, int64_t M, int64_t K,

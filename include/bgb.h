@@ -74,7 +74,8 @@ typedef enum {
     BGB_OP_PACK_BITNET = 1,
     BGB_OP_FBI_LINEAR = 2,
     BGB_OP_BITLINEAR = 3,
-    BGB_OP_BITLINEAR158 = 4
+    BGB_OP_BITLINEAR158 = 4,
+    BGB_OP_FBI_BACKWARD = 5
 } bgb_op;
 
 /* Integer conversion of the clipped quantizer input v_c (eq. (4) gives none):
@@ -199,6 +200,41 @@ int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, in
 /* Workspace bytes of fbi_linear_w1a16_group for these items (the largest
  * item's fbi_linear_w1a16 workspace, 0 for the one-launch form). */
 size_t bgb_group_workspace_bytes(const bgb_w1a16_item* items, int count, int64_t M);
+
+/*
+ * fbi_pack_transposed -- the signs of S^T for the backward product (FBI-LLM
+ * news rewrite, training paragraph: gradients pass the sign function by the
+ * straight-through estimator, so dX needs the same signs transposed).
+ * P: the packed signs of a K x N weight (binarize_pack, FBI mode). PT
+ * (output): the packed format of the 2N x K matrix [S^T; S^T] (the
+ * transposed signs twice along the contraction axis),
+ * bgb_packed_bytes(2 N, K) bytes, 16-byte aligned. N % 32 == 0.
+ * Errors: BGB_EINVAL (null, sizes, alignment), BGB_EHIP.
+ */
+int fbi_pack_transposed(const uint32_t* P, int64_t K, int64_t N, uint32_t* PT, void* stream);
+
+/*
+ * fbi_linear_w1a16_backward -- FBI-linear backward through the identity
+ * straight-through estimator (the pages state no clipping):
+ *   dX[m][i] = sum_j s_ij alpha_j dY[m][j]            [M][K], dx_dtype
+ *   dalpha_j = sum_m dY[m][j] sum_i s_ij x[m][i]      [N] fp32
+ *   dW[i][j] = alpha_j sum_m x[m][i] dY[m][j]         [K][N] fp32
+ * (dW is the gradient of W_b = alpha * sign(W) passed to the latent W.)
+ * dy: [M][N], x: [M][K], both of `dtype` (BF16 or F16). Any of dx, dalpha,
+ * dw may be NULL (not computed); dx needs PT (fbi_pack_transposed), dalpha
+ * needs x and P, dw needs x. N % 32 == 0.
+ * Numerics: dX runs the forward product on g = fl32(alpha_j dY) carried as
+ * two bf16 halves (g_hi + g_lo, about 16 significant bits), fp32
+ * accumulation; dalpha is the forward at alpha = 1 (fp32 sums) times dY,
+ * summed over tokens in fp64 in token order; dW is a 16-bit matrix-core
+ * product over the tokens with fp32 accumulation, times alpha_j in fp32.
+ * ws: bgb_workspace_bytes(BGB_OP_FBI_BACKWARD, M, K, N) bytes.
+ * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP.
+ */
+int fbi_linear_w1a16_backward(const void* dy, const void* x, int dtype, int64_t M, int64_t K, int64_t N,
+                              const uint32_t* P, const uint32_t* PT, const void* alpha, int alpha_dtype,
+                              void* dx, int dx_dtype, float* dalpha, float* dw, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * bitlinear_w1a8 -- BitLinear forward (BitNet blog, section 一, eq. (4)-(8)).

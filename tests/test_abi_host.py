@@ -169,6 +169,34 @@ def test_group_validation(lib):
         assert call_group(lib, split, M=16, ws=None) == BAD
 
 
+def call_bwd(lib, dy=A, x=A, dt=2, M=4, K=64, N=64, P=A, PT=A, alpha=A, adt=0, dx=A, dxdt=0, da=A, dw=A, ws=A,
+             wsb=1 << 30):
+    return lib.fbi_linear_w1a16_backward(dy, x, dt, M, K, N, P, PT, alpha, adt, dx, dxdt, da, dw, ws, wsb, None)
+
+
+def test_backward_validation(lib):
+    assert lib.fbi_pack_transposed(A, 64, 48, A + 64 * MB, None) == BAD          # N % 32 != 0
+    assert lib.fbi_pack_transposed(A, 40, 64, A + 64 * MB, None) == BAD          # K % 32 != 0
+    assert lib.fbi_pack_transposed(None, 64, 64, A + 64 * MB, None) == BAD
+    assert lib.fbi_pack_transposed(A, 64, 64, A + 256, None) == BAD              # PT over P
+    assert lib.fbi_pack_transposed(A, 64, 0, A + 64 * MB, None) == 0             # empty
+    need = bgb.workspace_bytes(bgb.OP_FBI_BACKWARD, 4, 64, 64)
+    assert need >= 4 * 2 * 64 * 2 + 4 * 64 * 4                                     # split gradient + z
+    assert call_bwd(lib, N=48) == BAD
+    assert call_bwd(lib, K=40) == BAD
+    assert call_bwd(lib, dt=0) == UNSUP                                            # f32 gradients not offered
+    assert call_bwd(lib, adt=2) == UNSUP
+    assert call_bwd(lib, dxdt=7) == UNSUP
+    assert call_bwd(lib, dy=None) == BAD
+    assert call_bwd(lib, PT=None) == BAD                                           # dx needs the transposed signs
+    assert call_bwd(lib, x=None) == BAD                                            # dalpha / dw need x
+    assert call_bwd(lib, P=None) == BAD                                            # dalpha needs P
+    assert call_bwd(lib, dx=A + 4) == BAD
+    assert call_bwd(lib, wsb=need - 1) == BAD
+    assert call_bwd(lib, ws=None) == BAD
+    assert call_bwd(lib, M=0) == 0 and call_bwd(lib, N=0) == 0
+
+
 def call_bl(lib, x=A, xdt=0, M=1, K=64, N=8, P=A, beta=A, qp=None, y=A, xq=None, g=None, acc=None, ws=A,
             wsb=1 << 30):
     return lib.bitlinear_w1a8(x, xdt, M, K, N, P, beta, qp, y, xq, g, acc, ws, wsb, None)
