@@ -397,6 +397,33 @@ def leg_ternary(torch, bgb, syn, rotate_mb):
     return out
 
 
+def leg_backward(torch, bgb, syn):
+    """FBI-linear backward at the prefill shape (4096 tokens, 4096 x 11008): dX, dalpha and dW
+    (identity straight-through estimator) from a synthetic output gradient."""
+    cfg = syn.CONFIGS["w1_prefill_4096x4096x11008"]
+    M, K, N, seed = cfg["M"], cfg["K"], cfg["N"], cfg["seed"]
+    W = syn.gpu_normal(seed, 0, (K, N), std=cfg["w_std"])
+    x = syn.gpu_normal(seed, 1, (M, K)).to(torch.bfloat16)
+    dy = syn.gpu_normal(seed, 5, (M, N)).to(torch.bfloat16)
+    P, alpha = bgb.binarize_pack(W, bgb.MODE_FBI)
+    del W
+    PT = bgb.fbi_pack_transposed(P, K, N)
+    ms = graph_time(torch, lambda i: bgb.fbi_pack_transposed(P, K, N, PT=PT), 10, 2) / 10
+    out = {"fbi_pack_transposed_4096x11008": {"us": round(ms * 1e3, 2)}}
+    ws = torch.empty(bgb.workspace_bytes(bgb.OP_FBI_BACKWARD, M, K, N), dtype=torch.uint8, device="cuda")
+    flops = 2 * M * K * N
+    for name, want in (("dx", ("dx",)), ("dalpha", ("dalpha",)), ("dw", ("dw",)), ("all", ("dx", "dalpha", "dw"))):
+        ms = graph_time(torch, lambda i, want=want: bgb.fbi_linear_w1a16_backward(dy, x, P, PT, alpha, want=want,
+                                                                                  ws=ws), 5, 2) / 5
+        f = flops * len(want)
+        tf = f / (ms * 1e-3) / 1e12
+        out[f"fbi_backward_{name}_4096x4096x11008"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                                       "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
+                                                       "flops": f, "bound": "mfma"}
+        log(f"FBI backward {name}: {ms * 1e3:.0f} us, {tf:.0f} TFLOP/s")
+    return out
+
+
 def leg_stack_1p3b(torch, bgb, syn):
     cfg = syn.CONFIGS["w1a16_1p3b_stack"]
     shapes, L = cfg["shapes"], cfg["layers"]
@@ -481,7 +508,8 @@ def main():
 
     legs = {}
     want = set() if args.legs == "none" else (
-        {"pack", "decode7b", "prefill", "stack", "ternary"} if args.legs == "all" else set(args.legs.split(",")))
+        {"pack", "decode7b", "prefill", "stack", "ternary", "backward"} if args.legs == "all"
+        else set(args.legs.split(",")))
     if "pack" in want:
         legs.update(leg_pack(torch, bgb, syn))
         torch.cuda.empty_cache()
@@ -495,6 +523,9 @@ def main():
         legs.update(leg_stack_1p3b(torch, bgb, syn))
     if "ternary" in want:
         legs.update(leg_ternary(torch, bgb, syn, args.rotate_mb))
+        torch.cuda.empty_cache()
+    if "backward" in want:
+        legs.update(leg_backward(torch, bgb, syn))
         torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(state, args.cpu_seconds)

@@ -249,7 +249,8 @@ int fbi_linear_w1a16_backward(const void* dy, const void* x, int dtype, int64_t 
         float* z = reinterpret_cast<float*>(carve(ws, lay.z));
         rc = fbi_run(x, dtype, M, K, N, P, ones, BGB_F32, z, BGB_F32, inner, s);
         if (rc) return rc;
-        rc = finish(bgb::launch_dalpha(dy, f16, z, M, N, dalpha, s));
+        double* part = reinterpret_cast<double*>(carve(ws, lay.part));
+        rc = finish(bgb::launch_dalpha(dy, f16, z, M, N, part, dalpha, s));
     }
     return rc;
 }

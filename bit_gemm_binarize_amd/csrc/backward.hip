@@ -97,18 +97,38 @@ __global__ void __launch_bounds__(256) fill_ones_kernel(float* __restrict__ p, i
 }
 
 // ------------------------------------------------ dalpha = sum_m dY z ------
-// One thread per column, tokens in ascending order, fp64 sum of the fp32
-// products of dY (exact in fp32) and z.
+// Two passes, fixed order: a block takes 64 columns and a chunk of
+// kDaChunk tokens; thread (c, q) sums tokens q, q + 4, ... of the chunk for
+// column c in fp64 (the fp32 products of dY, exact in fp32, and z), the four
+// q parts are added in order through LDS, and the chunk sums are added in
+// chunk order by a second kernel.
+constexpr int kDaChunk = 256;
+
 __global__ void __launch_bounds__(256)
-dalpha_kernel(const uint16_t* __restrict__ dy, int dy_f16, const float* __restrict__ z, int64_t M, int64_t N,
-              float* __restrict__ dalpha) {
+dalpha_part_kernel(const uint16_t* __restrict__ dy, int dy_f16, const float* __restrict__ z, int64_t M, int64_t N,
+                   double* __restrict__ part) {
+    __shared__ double red[4][64];
+    const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int64_t j = int64_t(blockIdx.x) * 64 + c, m0 = int64_t(blockIdx.y) * kDaChunk;
+    double acc = 0.0;
+    if (j < N) {
+        const int64_t m1 = m0 + kDaChunk < M ? m0 + kDaChunk : M;
+        for (int64_t m = m0 + q; m < m1; m += 4) {
+            const float d = dy_f16 ? f16_to_f32(dy[m * N + j]) : bf16_to_f32(dy[m * N + j]);
+            acc += double(d) * double(z[m * N + j]);
+        }
+    }
+    red[q][c] = acc;
+    __syncthreads();
+    if (q == 0 && j < N) part[int64_t(blockIdx.y) * N + j] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+}
+
+__global__ void __launch_bounds__(256)
+dalpha_sum_kernel(const double* __restrict__ part, int64_t chunks, int64_t N, float* __restrict__ dalpha) {
     const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (j >= N) return;
     double acc = 0.0;
-    for (int64_t m = 0; m < M; ++m) {
-        const float d = dy_f16 ? f16_to_f32(dy[m * N + j]) : bf16_to_f32(dy[m * N + j]);
-        acc += double(d) * double(z[m * N + j]);
-    }
+    for (int64_t c = 0; c < chunks; ++c) acc += part[c * N + j];
     dalpha[j] = float(acc);
 }
 
@@ -117,11 +137,14 @@ dalpha_kernel(const uint16_t* __restrict__ dy, int dy_f16, const float* __restri
 // 128 (i) x 128 (j) tile of dW, wave w the 64 x 64 quarter (w & 1, w >> 1),
 // as 4 x 4 MFMA fragments with A = dY^T (rows j) and B = x (columns i), so a
 // lane's 4 outputs are 4 consecutive j of one i (one 16-byte store). Each
-// chunk of 32 tokens is staged in LDS transposed (row = feature, 32 tokens
-// contiguous), so that an operand is one 16-byte read; the next chunk is
-// loaded into registers while the current one is multiplied. Tokens past M
+// chunk of 64 tokens is staged in LDS transposed (row = feature, the chunk's
+// tokens contiguous), so that an operand is one 16-byte read: threads 0..127
+// load 8 tokens x 8 features of x, threads 128..255 the same of dY (16-byte
+// loads, 16 threads per 256-byte row piece), transpose the 8 x 8 block in
+// registers (one v_perm per output dword) and store 8 rows of 16 bytes. The
+// next chunk is loaded while the current one is multiplied. Tokens past M
 // and features past K or N read as zeros.
-constexpr int kDwTile = 128, kDwChunk = 32, kDwRow = kDwChunk + 8;   // LDS row: 32 tokens + 16 bytes of padding
+constexpr int kDwTile = 128, kDwChunk = 64, kDwRow = kDwChunk + 8;   // LDS row: 64 tokens + 16 bytes
 
 template <bool kF16>
 __global__ void __launch_bounds__(256)
@@ -133,33 +156,34 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
     const int64_t i0 = int64_t(blockIdx.x) * kDwTile, j0 = int64_t(blockIdx.y) * kDwTile;
     const int wi = (wave & 1) * 64, wj = (wave >> 1) * 64;
 
-    // loader: thread tid moves token row m0 + (tid >> 4) + 16 h (h = 0, 1),
-    // features 8 (tid & 15) .. + 7 of both tiles
-    const int lrow = tid >> 4, lcol = 8 * (tid & 15);
-    u32x4_t vx[2], vg[2];
+    // loader: half h = tid >> 7 (0: x, 1: dY), token rows 8 mb .. 8 mb + 7 of
+    // the chunk, features 8 fb .. 8 fb + 7 of the tile
+    const int h = tid >> 7, mb = (tid & 127) >> 4, fb = tid & 15;
+    const uint16_t* src = h ? dy : x;
+    const int64_t ld = h ? N : K;
+    const int64_t f0 = (h ? j0 : i0) + 8 * fb;          // K, N multiples of 32: 8-feature pieces are whole
+    const bool okf = f0 < ld;
+    uint16_t* const tile = h ? gt : xt;
+    u32x4_t v[8];
     auto load = [&](int64_t m0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t m = m0 + lrow + 16 * h;
-            const bool okm = m < M;
-            const int64_t ix = i0 + lcol, jg = j0 + lcol;    // K, N multiples of 32: 8-feature pieces are whole
-            const bool okx = okm && ix < K, okg = okm && jg < N;
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(x + (okx ? m * K + ix : 0));
-            const u32x4_t b = *reinterpret_cast<const u32x4_t*>(dy + (okg ? m * N + jg : 0));
-            vx[h] = a & u32x4_t(0u - uint32_t(okx));
-            vg[h] = b & u32x4_t(0u - uint32_t(okg));
+        for (int e = 0; e < 8; ++e) {
+            const int64_t m = m0 + 8 * mb + e;
+            const bool ok = okf && m < M;
+            const u32x4_t t = *reinterpret_cast<const u32x4_t*>(src + (ok ? m * ld + f0 : 0));
+            v[e] = t & u32x4_t(0u - uint32_t(ok));
         }
     };
     auto store = [&]() {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int t = lrow + 16 * h;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t wx = vx[h][e >> 1], wg = vg[h][e >> 1];
-                xt[(lcol + e) * kDwRow + t] = uint16_t(e & 1 ? wx >> 16 : wx & 0xffffu);
-                gt[(lcol + e) * kDwRow + t] = uint16_t(e & 1 ? wg >> 16 : wg & 0xffffu);
-            }
+        for (int f = 0; f < 8; ++f) {
+            const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t o;
+            o.x = __builtin_amdgcn_perm(v[1][f >> 1], v[0][f >> 1], sel);
+            o.y = __builtin_amdgcn_perm(v[3][f >> 1], v[2][f >> 1], sel);
+            o.z = __builtin_amdgcn_perm(v[5][f >> 1], v[4][f >> 1], sel);
+            o.w = __builtin_amdgcn_perm(v[7][f >> 1], v[6][f >> 1], sel);
+            *reinterpret_cast<u32x4_t*>(tile + (8 * fb + f) * kDwRow + 8 * mb) = o;
         }
     };
 
@@ -175,25 +199,28 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
         store();
         __syncthreads();
         if (m0 + kDwChunk < M) load(m0 + kDwChunk);
-        u32x4_t av[4], bv[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            av[f] = *reinterpret_cast<const u32x4_t*>(gt + (wj + 16 * f + r) * kDwRow + 8 * g);
-            bv[f] = *reinterpret_cast<const u32x4_t*>(xt + (wi + 16 * f + r) * kDwRow + 8 * g);
-        }
+        for (int ks = 0; ks < kDwChunk / 32; ++ks) {
+            u32x4_t av[4], bv[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if constexpr (kF16)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av[a]),
-                                                                       __builtin_bit_cast(f16x8_t, bv[b]),
-                                                                       acc[a][b], 0, 0, 0);
-                else
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
-                                                                        __builtin_bit_cast(bf16x8_t, bv[b]),
-                                                                        acc[a][b], 0, 0, 0);
+            for (int f = 0; f < 4; ++f) {
+                av[f] = *reinterpret_cast<const u32x4_t*>(gt + (wj + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
+                bv[f] = *reinterpret_cast<const u32x4_t*>(xt + (wi + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
             }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    if constexpr (kF16)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av[a]),
+                                                                           __builtin_bit_cast(f16x8_t, bv[b]),
+                                                                           acc[a][b], 0, 0, 0);
+                    else
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[a]),
+                                                                            __builtin_bit_cast(bf16x8_t, bv[b]),
+                                                                            acc[a][b], 0, 0, 0);
+                }
+        }
     }
     // lane (g, r) of fragment (a, b): j = j0 + wj + 16 a + 4 g + e, i = i0 + wi + 16 b + r
 #pragma unroll
@@ -236,10 +263,15 @@ hipError_t launch_fbi_backward_parts(const void* dy, int dy_f16, const void* x, 
     return hipGetLastError();
 }
 
-hipError_t launch_dalpha(const void* dy, int dy_f16, const float* z, int64_t M, int64_t N, float* dalpha,
-                         hipStream_t s) {
-    dalpha_kernel<<<unsigned((N + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(dy), dy_f16, z, M, N, dalpha);
+hipError_t launch_dalpha(const void* dy, int dy_f16, const float* z, int64_t M, int64_t N, double* part,
+                         float* dalpha, hipStream_t s) {
+    const int64_t chunks = (M + kDaChunk - 1) / kDaChunk;
+    dalpha_part_kernel<<<dim3(unsigned((N + 63) / 64), unsigned(chunks)), 256, 0, s>>>(
+        static_cast<const uint16_t*>(dy), dy_f16, z, M, N, part);
+    dalpha_sum_kernel<<<unsigned((N + 255) / 256), 256, 0, s>>>(part, chunks, N, dalpha);
     return hipGetLastError();
 }
+
+size_t dalpha_part_bytes(int64_t M, int64_t N) { return size_t((M + kDaChunk - 1) / kDaChunk) * size_t(N) * 8; }
 
 }  // namespace bgb

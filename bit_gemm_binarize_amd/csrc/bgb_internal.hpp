@@ -76,14 +76,17 @@ struct FbiLinearWs {        // split-K partial sums (decode or GEMM), when the p
 };
 
 // FBI-linear backward: the split scaled gradient [M][2N] bf16, z [M][N] fp32,
-// a vector of ones (max(K, N) fp32), then the forward calls' own workspace.
+// the fp64 chunk sums of dalpha, a vector of ones (max(K, N) fp32), then the
+// forward calls' own workspace.
+size_t dalpha_part_bytes(int64_t M, int64_t N);
 struct FbiBackwardWs {
-    size_t g2, z, ones, inner, total;
+    size_t g2, z, part, ones, inner, total;
     static FbiBackwardWs make(int64_t M, int64_t K, int64_t N) {
         FbiBackwardWs w{};
         w.g2 = 0;
         w.z = align256(size_t(M) * size_t(2 * N) * 2);
-        w.ones = w.z + align256(size_t(M) * size_t(N) * 4);
+        w.part = w.z + align256(size_t(M) * size_t(N) * 4);
+        w.ones = w.part + align256(dalpha_part_bytes(M, N));
         w.inner = w.ones + align256(size_t(K > N ? K : N) * 4);
         const size_t a = FbiLinearWs::make(M, 2 * N, K).total, b = FbiLinearWs::make(M, K, N).total;
         w.total = w.inner + align256(a > b ? a : b);
@@ -166,8 +169,9 @@ hipError_t launch_pack_transpose(const uint32_t* P, int64_t K, int64_t N, uint32
 hipError_t launch_fbi_backward_parts(const void* dy, int dy_f16, const void* x, int64_t M, int64_t K, int64_t N,
                                      const void* alpha, int alpha_f16, uint16_t* g2, float* ones, int64_t nones,
                                      float* dw, hipStream_t s);
-hipError_t launch_dalpha(const void* dy, int dy_f16, const float* z, int64_t M, int64_t N, float* dalpha,
-                         hipStream_t s);
+hipError_t launch_dalpha(const void* dy, int dy_f16, const float* z, int64_t M, int64_t N, double* part,
+                         float* dalpha, hipStream_t s);
+size_t dalpha_part_bytes(int64_t M, int64_t N);     // fp64 chunk sums [chunks][N]
 
 hipError_t launch_w1a8_gemm(const int8_t* q, const int32_t* rowsum, const float* gamma,
                             int gstride, const float* beta, float qb, int64_t M, int64_t K,
