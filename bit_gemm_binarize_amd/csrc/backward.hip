@@ -141,17 +141,18 @@ dalpha_sum_kernel(const double* __restrict__ part, int64_t chunks, int64_t N, fl
 // tokens contiguous), so that an operand is one 16-byte read: threads 0..127
 // load 8 tokens x 8 features of x, threads 128..255 the same of dY (16-byte
 // loads, 16 threads per 256-byte row piece), transpose the 8 x 8 block in
-// registers (one v_perm per output dword) and store 8 rows of 16 bytes. The
-// next chunk is loaded while the current one is multiplied. Tokens past M
-// and features past K or N read as zeros.
+// registers (one v_perm per output dword) and store 8 rows of 16 bytes. Two
+// LDS buffers: the next chunk is stored while the current one is multiplied
+// and the one after it is loaded. Tokens past M and features past K or N
+// read as zeros.
 constexpr int kDwTile = 128, kDwChunk = 64, kDwRow = kDwChunk + 8;   // LDS row: 64 tokens + 16 bytes
 
 template <bool kF16>
 __global__ void __launch_bounds__(256)
 dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64_t M, int64_t K, int64_t N,
           const void* __restrict__ alpha, int alpha_f16, float* __restrict__ dw) {
-    __shared__ __attribute__((aligned(16))) uint16_t xt[kDwTile * kDwRow];
-    __shared__ __attribute__((aligned(16))) uint16_t gt[kDwTile * kDwRow];
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2][kDwTile * kDwRow];
+    __shared__ __attribute__((aligned(16))) uint16_t gt[2][kDwTile * kDwRow];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
     const int64_t i0 = int64_t(blockIdx.x) * kDwTile, j0 = int64_t(blockIdx.y) * kDwTile;
     const int wi = (wave & 1) * 64, wj = (wave >> 1) * 64;
@@ -163,7 +164,6 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
     const int64_t ld = h ? N : K;
     const int64_t f0 = (h ? j0 : i0) + 8 * fb;          // K, N multiples of 32: 8-feature pieces are whole
     const bool okf = f0 < ld;
-    uint16_t* const tile = h ? gt : xt;
     u32x4_t v[8];
     auto load = [&](int64_t m0) {
 #pragma unroll
@@ -174,7 +174,8 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
             v[e] = t & u32x4_t(0u - uint32_t(ok));
         }
     };
-    auto store = [&]() {
+    auto store = [&](int buf) {
+        uint16_t* const tile = h ? gt[buf] : xt[buf];
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
             const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
@@ -193,19 +194,26 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // two LDS buffers: chunk c + 1 is stored into one while chunk c is
+    // multiplied from the other, and chunk c + 2 is loaded meanwhile; one
+    // barrier per chunk
     load(0);
-    for (int64_t m0 = 0; m0 < M; m0 += kDwChunk) {
-        __syncthreads();                                   // the previous chunk's reads are done
-        store();
-        __syncthreads();
-        if (m0 + kDwChunk < M) load(m0 + kDwChunk);
+    store(0);
+    if (kDwChunk < M) load(kDwChunk);
+    __syncthreads();
+    int buf = 0;
+    for (int64_t m0 = 0; m0 < M; m0 += kDwChunk, buf ^= 1) {
+        if (m0 + kDwChunk < M) store(buf ^ 1);
+        if (m0 + 2 * kDwChunk < M) load(m0 + 2 * kDwChunk);
+        const uint16_t* const gb = gt[buf];
+        const uint16_t* const xb = xt[buf];
 #pragma unroll
         for (int ks = 0; ks < kDwChunk / 32; ++ks) {
             u32x4_t av[4], bv[4];
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                av[f] = *reinterpret_cast<const u32x4_t*>(gt + (wj + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
-                bv[f] = *reinterpret_cast<const u32x4_t*>(xt + (wi + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
+                av[f] = *reinterpret_cast<const u32x4_t*>(gb + (wj + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
+                bv[f] = *reinterpret_cast<const u32x4_t*>(xb + (wi + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a)
@@ -221,6 +229,7 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
                                                                             acc[a][b], 0, 0, 0);
                 }
         }
+        __syncthreads();                                   // chunk c + 1 is in; chunk c's buffer is free
     }
     // lane (g, r) of fragment (a, b): j = j0 + wj + 16 a + 4 g + e, i = i0 + wi + 16 b + r
 #pragma unroll
