@@ -76,19 +76,47 @@ hipError_t launch_pack_transpose(const uint32_t* P, int64_t K, int64_t N, uint32
 
 // ------------------------------------------------------ g = alpha * dY -----
 // g = fl32(dY alpha_j); row m of the output holds bf16(g) for j < N and
-// bf16(g - bf16(g)) at N + j (g - bf16(g) is exact in fp32).
+// bf16(g - bf16(g)) at N + j (g - bf16(g) is exact in fp32). A thread takes
+// 8 consecutive columns (16-byte loads and stores; N % 8 == 0).
 __global__ void __launch_bounds__(256)
 split_scaled_grad_kernel(const uint16_t* __restrict__ dy, int dy_f16, int64_t M, int64_t N,
                          const void* __restrict__ alpha, int alpha_f16, uint16_t* __restrict__ g2) {
     const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= M * N) return;
-    const int64_t m = e / N, j = e % N;
-    const float d = dy_f16 ? f16_to_f32(dy[e]) : bf16_to_f32(dy[e]);
-    const float a = alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[j]) : static_cast<const float*>(alpha)[j];
-    const float g = d * a;
-    const uint16_t hi = f32_to_bf16_rne(g);
-    g2[m * 2 * N + j] = hi;
-    g2[m * 2 * N + N + j] = f32_to_bf16_rne(g - bf16_to_f32(hi));
+    const int64_t n8 = N / 8;
+    if (e >= M * n8) return;
+    const int64_t m = e / n8, j0 = (e % n8) * 8;
+    const u32x4_t d = *reinterpret_cast<const u32x4_t*>(dy + m * N + j0);
+    float a[8];
+    if (alpha_f16) {
+        const u32x4_t h = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(alpha) + j0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = f16_to_f32(uint16_t(h[k >> 1] >> (16 * (k & 1))));
+    } else {
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(alpha) + j0);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(alpha) + j0 + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[k] = lo[k];
+            a[4 + k] = hi[k];
+        }
+    }
+    u32x4_t oh, ol;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint16_t b = uint16_t(d[k >> 1] >> (16 * (k & 1)));
+        const float g = (dy_f16 ? f16_to_f32(b) : bf16_to_f32(b)) * a[k];
+        const uint16_t h = f32_to_bf16_rne(g);
+        const uint16_t l = f32_to_bf16_rne(g - bf16_to_f32(h));
+        if (k & 1) {
+            oh[k >> 1] |= uint32_t(h) << 16;
+            ol[k >> 1] |= uint32_t(l) << 16;
+        } else {
+            oh[k >> 1] = h;
+            ol[k >> 1] = l;
+        }
+    }
+    *reinterpret_cast<u32x4_t*>(g2 + m * 2 * N + j0) = oh;
+    *reinterpret_cast<u32x4_t*>(g2 + m * 2 * N + N + j0) = ol;
 }
 
 __global__ void __launch_bounds__(256) fill_ones_kernel(float* __restrict__ p, int64_t n) {
@@ -97,30 +125,41 @@ __global__ void __launch_bounds__(256) fill_ones_kernel(float* __restrict__ p, i
 }
 
 // ------------------------------------------------ dalpha = sum_m dY z ------
-// Two passes, fixed order: a block takes 64 columns and a chunk of
+// Two passes, fixed order: a block takes 256 columns and a chunk of
 // kDaChunk tokens; thread (c, q) sums tokens q, q + 4, ... of the chunk for
-// column c in fp64 (the fp32 products of dY, exact in fp32, and z), the four
-// q parts are added in order through LDS, and the chunk sums are added in
-// chunk order by a second kernel.
+// columns 4c .. 4c + 3 in fp64 (the products of dY and z), the four q parts
+// are added in order through LDS, and the chunk sums are added in chunk
+// order by a second kernel.
 constexpr int kDaChunk = 256;
 
 __global__ void __launch_bounds__(256)
 dalpha_part_kernel(const uint16_t* __restrict__ dy, int dy_f16, const float* __restrict__ z, int64_t M, int64_t N,
                    double* __restrict__ part) {
-    __shared__ double red[4][64];
+    __shared__ double red[4][64][4];
     const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const int64_t j = int64_t(blockIdx.x) * 64 + c, m0 = int64_t(blockIdx.y) * kDaChunk;
-    double acc = 0.0;
-    if (j < N) {
+    const int64_t j = int64_t(blockIdx.x) * 256 + 4 * c, m0 = int64_t(blockIdx.y) * kDaChunk;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    if (j < N) {                                        // N % 4 == 0: 4 columns are all in or all out
         const int64_t m1 = m0 + kDaChunk < M ? m0 + kDaChunk : M;
         for (int64_t m = m0 + q; m < m1; m += 4) {
-            const float d = dy_f16 ? f16_to_f32(dy[m * N + j]) : bf16_to_f32(dy[m * N + j]);
-            acc += double(d) * double(z[m * N + j]);
+            const uint2 d = *reinterpret_cast<const uint2*>(dy + m * N + j);
+            const f32x4_t zv = *reinterpret_cast<const f32x4_t*>(z + m * N + j);
+            const uint32_t dw[2] = {d.x, d.y};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint16_t b = uint16_t(dw[k >> 1] >> (16 * (k & 1)));
+                acc[k] += double(dy_f16 ? f16_to_f32(b) : bf16_to_f32(b)) * double(zv[k]);
+            }
         }
     }
-    red[q][c] = acc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red[q][c][k] = acc[k];
     __syncthreads();
-    if (q == 0 && j < N) part[int64_t(blockIdx.y) * N + j] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    if (q == 0 && j < N) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            part[int64_t(blockIdx.y) * N + j + k] = ((red[0][c][k] + red[1][c][k]) + red[2][c][k]) + red[3][c][k];
+    }
 }
 
 __global__ void __launch_bounds__(256)
@@ -255,7 +294,7 @@ hipError_t launch_fbi_backward_parts(const void* dy, int dy_f16, const void* x, 
                                      const void* alpha, int alpha_f16, uint16_t* g2, float* ones, int64_t nones,
                                      float* dw, hipStream_t s) {
     if (g2) {
-        const int64_t n = M * N;
+        const int64_t n = M * (N / 8);
         split_scaled_grad_kernel<<<unsigned((n + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(dy), dy_f16,
                                                                             M, N, alpha, alpha_f16, g2);
     }
@@ -275,7 +314,7 @@ hipError_t launch_fbi_backward_parts(const void* dy, int dy_f16, const void* x, 
 hipError_t launch_dalpha(const void* dy, int dy_f16, const float* z, int64_t M, int64_t N, double* part,
                          float* dalpha, hipStream_t s) {
     const int64_t chunks = (M + kDaChunk - 1) / kDaChunk;
-    dalpha_part_kernel<<<dim3(unsigned((N + 63) / 64), unsigned(chunks)), 256, 0, s>>>(
+    dalpha_part_kernel<<<dim3(unsigned((N + 255) / 256), unsigned(chunks)), 256, 0, s>>>(
         static_cast<const uint16_t*>(dy), dy_f16, z, M, N, part);
     dalpha_sum_kernel<<<unsigned((N + 255) / 256), 256, 0, s>>>(part, chunks, N, dalpha);
     return hipGetLastError();
