@@ -216,3 +216,17 @@ def test_bitlinear_validation(lib):
     assert call_bl(lib, qp=ctypes.pointer(bgb._QP(1e-5, 8, 1e-3, 2, 0))) == UNSUP   # round mode
     assert call_bl(lib, qp=ctypes.pointer(bgb._QP(1e-5, 8, 1e-3, 0, 5))) == UNSUP   # gamma scope
     assert call_bl(lib, M=0) == 0
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    """The boundary is a C ABI: the header must compile on its own as C and C++."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "bgb.h"\nint main(void) { return (int)sizeof(bgb_w1a16_item) + BGB_GROUP_MAX; }\n')
+    for exe, lang, std in (("gcc", "c", "-std=c11"), ("g++", "c++", "-std=c++17")):
+        if shutil.which(exe) is None:
+            pytest.skip(f"{exe} not available")
+        r = subprocess.run([exe, "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                            "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
