@@ -53,6 +53,8 @@ def _load():
     lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
     lib.oracle_fbi_linear.argtypes = [P, ctypes.c_int, I64, I64, P, I64, P, P]
+    lib.oracle_ln_nonneg_quant.argtypes = [P, I64, I64, ctypes.c_double, ctypes.c_int, ctypes.c_float,
+                                           ctypes.c_int, ctypes.c_int, P, P, P]
     lib.oracle_fbi_backward.argtypes = [P, P, ctypes.c_int, I64, I64, P, I64, P, P, P, P]
     lib.oracle_ln_absmax_quant.argtypes = [P, I64, I64, ctypes.c_double, ctypes.c_int,
                                            ctypes.c_float, ctypes.c_int, ctypes.c_int, P, P, P, P]
@@ -61,7 +63,7 @@ def _load():
                                          ctypes.c_int, P]
     lib.oracle_ternary.argtypes = [P, I64, I64, ctypes.c_float, P, P]
     lib.oracle_int8_acc.argtypes = [P, I64, I64, P, I64, P]
-    for name in ("oracle_ternary", "oracle_int8_acc", "oracle_fbi_backward",
+    for name in ("oracle_ternary", "oracle_int8_acc", "oracle_fbi_backward", "oracle_ln_nonneg_quant",
                  "oracle_sign_fbi", "oracle_sign_bitnet", "oracle_fbi_alpha",
                  "oracle_bitnet_scalars", "oracle_pack", "oracle_fbi_linear",
                  "oracle_ln_absmax_quant", "oracle_bitlinear_acc", "oracle_bitlinear_out"):
@@ -199,6 +201,23 @@ def ln_absmax_quant(x: np.ndarray, ln_eps: float = 1e-5, bits: int = 8, q_eps: f
            "ln_absmax_quant")
     gamma = g[:M].copy() if gamma_scope == 1 else np.float32(g[0])
     return q, gamma, mu, rs
+
+
+def ln_nonneg_quant(x: np.ndarray, ln_eps: float = 1e-5, bits: int = 8, q_eps: float = 1e-3,
+                    round_mode: int = 0, gamma_scope: int = 0):
+    """eq. (6): returns (q int8 [M][K] in [0, Q_b - 1], gamma, eta); gamma and eta are float32
+    scalars for the tensor scope (0) and float32 [M] arrays for the token scope (1)."""
+    x = _f32(x)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    g = np.zeros(max(M, 1), np.float32)
+    e = np.zeros(max(M, 1), np.float32)
+    _check(_load().oracle_ln_nonneg_quant(_ptr(x), M, K, ctypes.c_double(ln_eps), bits, ctypes.c_float(q_eps),
+                                          round_mode, gamma_scope, _ptr(q), _ptr(g), _ptr(e)),
+           "ln_nonneg_quant")
+    if gamma_scope == 1:
+        return q, g[:M].copy(), e[:M].copy()
+    return q, np.float32(g[0]), np.float32(e[0])
 
 
 def bitlinear_acc(q: np.ndarray, W: np.ndarray, c: float) -> np.ndarray:

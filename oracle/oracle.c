@@ -299,6 +299,73 @@ int oracle_ln_absmax_quant(const float* x, int64_t M, int64_t K, double ln_eps, 
     return 0;
 }
 
+/* [BitNet] eq. (6): for activations ahead of a non-linear function the codes
+ * are shifted to be non-negative: Quant(x) = Clip((x - eta) Q_b / gamma,
+ * eps, Q_b - eps) with eta = min x. Readings: x is the LayerNorm output h
+ * (eq. (7) quantizes LN(x)); gamma keeps its one definition, eq. (5),
+ * ||h||_inf; eta and gamma are taken over the tensor (scope 0) or the token
+ * (scope 1). Decided in fp32 like eq. (4): d = fl32(h - eta),
+ * v = fl32((d * Q_b) / gamma), v_c = min(fl32(Q_b - eps), max(fl32(eps), v)),
+ * then truncation (or round to nearest even, clamped to Q_b - 1); gamma == 0
+ * (every h zero) gives q == 0. eta: [1] or [M]. */
+int oracle_ln_nonneg_quant(const float* x, int64_t M, int64_t K, double ln_eps, int bits, float q_eps,
+                           int round_mode, int gamma_scope, int8_t* q, float* gamma, float* eta) {
+    if (!x || !q || !gamma || !eta || M < 0 || K <= 0 || bits < 2 || bits > 8) return -1;
+    if (round_mode < 0 || round_mode > 1 || gamma_scope < 0 || gamma_scope > 1) return -1;
+    const float Qb = (float)(1 << (bits - 1));
+    const int qmax = (1 << (bits - 1)) - 1;
+    const size_t n = (size_t)(M > 0 ? M : 1) * (size_t)K;
+    float* h = (float*)malloc(sizeof(float) * n);
+    if (!h) return -2;
+    /* LayerNorm per token (fp64 statistics, fp32 application), as for eq. (4) */
+    for (int64_t m = 0; m < M; ++m) {
+        const float* xr = x + m * K;
+        double s = 0.0;
+        for (int64_t i = 0; i < K; ++i) s += (double)xr[i];
+        const double mu = s / (double)K;
+        double v2 = 0.0;
+        for (int64_t i = 0; i < K; ++i) {
+            const double d = (double)xr[i] - mu;
+            v2 += d * d;
+        }
+        const float mu32 = (float)mu;
+        const float rs32 = (float)(1.0 / sqrt(v2 / (double)K + ln_eps));
+        for (int64_t i = 0; i < K; ++i) {
+            const float d = xr[i] - mu32;
+            h[m * K + i] = d * rs32;
+        }
+    }
+    const float lo = q_eps, hi = Qb - q_eps;
+    for (int64_t m = 0; m < M; ++m) {
+        /* the scope's gamma = max |h| and eta = min h */
+        const int64_t b = gamma_scope == 1 ? m * K : 0, e = gamma_scope == 1 ? (m + 1) * K : M * K;
+        float g = 0.0f, mn = h[b];
+        for (int64_t i = b; i < e; ++i) {
+            const float a = fabsf(h[i]);
+            if (a > g) g = a;
+            if (h[i] < mn) mn = h[i];
+        }
+        if (gamma_scope == 1) {
+            gamma[m] = g;
+            eta[m] = mn;
+        } else if (m == 0) {
+            gamma[0] = g;
+            eta[0] = mn;
+        }
+        for (int64_t i = 0; i < K; ++i) {
+            if (g == 0.0f) { q[m * K + i] = 0; continue; }
+            const float d = h[m * K + i] - mn;
+            const float v = (d * Qb) / g;
+            const float vc = v > hi ? hi : (v < lo ? lo : v);
+            int c = round_mode == 0 ? (int)vc : (int)nearbyintf(vc);
+            if (c > qmax) c = qmax;
+            q[m * K + i] = (int8_t)c;
+        }
+    }
+    free(h);
+    return 0;
+}
+
 /* ------------------------------------------------------- BitLinear product -- */
 
 /* [BitNet] eq. (7): the integer part W~ . Quant(LN(x)), with W~ = Sign(W - c).

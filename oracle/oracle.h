@@ -77,6 +77,14 @@ int oracle_ln_absmax_quant(const float* x, int64_t M, int64_t K, double ln_eps, 
                            float q_eps, int round_mode, int gamma_scope, int8_t* q, float* gamma,
                            float* mu32, float* rstd32);
 
+/* [BitNet] eq. (6): the non-negative quantizer, codes in [0, Q_b - 1]:
+ * q = Clip((h - eta) Q_b / gamma, eps, Q_b - eps) with h = LN(x) as above,
+ * gamma = max |h| (eq. (5)) and eta = min h over the tensor (scope 0) or the
+ * token (scope 1); fp32 decisions, truncation or round to nearest even.
+ * gamma, eta: [1] or [M]. */
+int oracle_ln_nonneg_quant(const float* x, int64_t M, int64_t K, double ln_eps, int bits, float q_eps,
+                           int round_mode, int gamma_scope, int8_t* q, float* gamma, float* eta);
+
 /* BitLinear integer product acc[m][j] = sum_i sign(W_ij - c) * q[m][i] (exact). */
 int oracle_bitlinear_acc(const int8_t* q, int64_t M, int64_t K, const float* W, int64_t N,
                          float c, int64_t* acc);

@@ -543,3 +543,44 @@ def test_fbi_backward_exact_rational(orc):
         for j in range(N):
             e = af[j] * sum(xf[m][i] * gf[m][j] for m in range(M))
             assert abs(Fraction(dw[i, j]) - e) <= abs(e) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+
+
+# ------------------------------------------------ non-negative quantizer (6) --
+
+def test_nonneg_quant_golden_closed_forms(orc):
+    g = read_golden("quant_nonneg_closed_forms.txt")
+    cases = [("pattern_a", "nn_q_a", 8, 0), ("pattern_a", "nn4_q_a", 4, 0), ("pattern_a", "nn4_q_a", 4, 1),
+             ("pattern_d", "nn4_q_d", 4, 0), ("pattern_d", "nn4_rne_q_d", 4, 1), ("pattern_d", "nn_q_d", 8, 0),
+             ("pattern_d", "nn_q_d", 8, 1)]
+    for pat, qk, bits, rm in cases:
+        period = np.array([float(v) for v in g[pat]], np.float32)
+        expect = np.array([int(v) for v in g[qk]], np.int8)
+        reps = 64 // period.size
+        x = np.tile(period, (3, reps))
+        x[1] *= 10.0                                   # LN removes the scale: same codes
+        for scope in (0, 1):
+            q, gamma, eta = orc.ln_nonneg_quant(x, bits=bits, round_mode=rm, gamma_scope=scope)
+            assert np.array_equal(q, np.tile(expect, (3, reps))), (pat, qk, rm, scope)
+    q, gamma, eta = orc.ln_nonneg_quant(np.full((2, 64), 0.37, np.float32))
+    assert not q.any() and gamma == 0
+
+
+def test_nonneg_quant_invariants(orc):
+    """Codes lie in [0, Q_b - 1]; the minimum of the scope maps to 0; codes are
+    monotone in the LayerNorm output (hence in x within a token); the symmetric
+    quantizer's gamma is the same quantity."""
+    x = syn.normal_f32(90, 1, (5, 256)) * np.float32(3.0)
+    x[2, 7] = 40.0                                     # an outlier sets gamma
+    for scope in (0, 1):
+        q, gamma, eta = orc.ln_nonneg_quant(x, gamma_scope=scope)
+        q0, g0, _, _ = orc.ln_absmax_quant(x, gamma_scope=scope)
+        assert np.array_equal(np.asarray(gamma), np.asarray(g0))
+        assert q.min() == 0 and q.max() <= 127
+        for m in range(x.shape[0]):
+            order = np.argsort(x[m], kind="stable")
+            assert np.all(np.diff(q[m][order].astype(int)) >= 0)
+        if scope == 1:
+            assert all(q[m][np.argmin(x[m])] == 0 for m in range(x.shape[0]))
+        else:
+            m, i = np.unravel_index(np.argmin((x - x.mean(1, keepdims=True)) / x.std(1, keepdims=True)), x.shape)
+            assert q[m, i] == 0
