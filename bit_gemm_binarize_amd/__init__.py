@@ -23,7 +23,7 @@ __all__ = [
     "OP_BITLINEAR158", "BgbError", "QuantParams", "MODE_FBI", "MODE_BITNET",
     "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M", "W1A16_DECODE_MAX_M",
     "ROUND_TRUNC", "ROUND_RNE", "GAMMA_TENSOR", "GAMMA_TOKEN", "fbi_linear_w1a16_group", "group_workspace_bytes",
-    "GROUP_MAX", "fbi_pack_transposed", "fbi_linear_w1a16_backward", "OP_FBI_BACKWARD",
+    "GROUP_MAX", "RANGE_SYMMETRIC", "RANGE_NONNEG", "fbi_pack_transposed", "fbi_linear_w1a16_backward", "OP_FBI_BACKWARD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,11 +58,12 @@ class _Item(ctypes.Structure):
 
 class _QP(ctypes.Structure):
     _fields_ = [("ln_eps", ctypes.c_double), ("bits", ctypes.c_int), ("q_eps", ctypes.c_float),
-                ("round_mode", ctypes.c_int), ("gamma_scope", ctypes.c_int)]
+                ("round_mode", ctypes.c_int), ("gamma_scope", ctypes.c_int), ("act_range", ctypes.c_int)]
 
 
 ROUND_TRUNC, ROUND_RNE = 0, 1
 GAMMA_TENSOR, GAMMA_TOKEN = 0, 1
+RANGE_SYMMETRIC, RANGE_NONNEG = 0, 1
 
 
 @dataclass
@@ -72,10 +73,11 @@ class QuantParams:
     q_eps: float = 1e-3
     round_mode: int = ROUND_TRUNC
     gamma_scope: int = GAMMA_TENSOR
+    act_range: int = RANGE_SYMMETRIC
 
     def c(self) -> "_QP":
         return _QP(float(self.ln_eps), int(self.bits), float(self.q_eps), int(self.round_mode),
-                   int(self.gamma_scope))
+                   int(self.gamma_scope), int(self.act_range))
 
 
 _lib = None

@@ -257,11 +257,12 @@ int fbi_linear_w1a16_backward(const void* dy, const void* x, int dtype, int64_t 
 
 // Shared checks of the BitLinear entry points; fills qb/lim from qp.
 static int bitlinear_params(const bgb_quant_params* qp, bgb_quant_params* p, float* qb, float* lim) {
-    *p = bgb_quant_params{1e-5, 8, 1e-3f, BGB_ROUND_TRUNC, BGB_GAMMA_TENSOR};
+    *p = bgb_quant_params{1e-5, 8, 1e-3f, BGB_ROUND_TRUNC, BGB_GAMMA_TENSOR, BGB_RANGE_SYMMETRIC};
     if (qp) *p = *qp;
     if (p->bits < 2 || p->bits > 8) return BGB_EUNSUPPORTED;
     if ((p->round_mode != BGB_ROUND_TRUNC && p->round_mode != BGB_ROUND_RNE) ||
-        (p->gamma_scope != BGB_GAMMA_TENSOR && p->gamma_scope != BGB_GAMMA_TOKEN))
+        (p->gamma_scope != BGB_GAMMA_TENSOR && p->gamma_scope != BGB_GAMMA_TOKEN) ||
+        (p->act_range != BGB_RANGE_SYMMETRIC && p->act_range != BGB_RANGE_NONNEG))
         return BGB_EUNSUPPORTED;
     if (!(p->ln_eps > 0.0) || !(p->q_eps > 0.0f) || !(p->q_eps < 1.0f)) return BGB_EINVAL;
     *qb = float(1 << (p->bits - 1));
@@ -284,8 +285,10 @@ int bitlinear_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const b
     const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, 0);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
     const bool decode = M <= bgb::kGemvMaxM;
+    float* mins = p.act_range == BGB_RANGE_NONNEG ? reinterpret_cast<float*>(carve(ws, lay.mins)) : nullptr;
     return finish(bgb::launch_ln_quant(x, x_dtype == BGB_BF16, M, K, p.ln_eps, qb, lim,
-                                       p.round_mode == BGB_ROUND_RNE, p.gamma_scope == BGB_GAMMA_TOKEN, decode ? 0 : 1,
+                                       p.round_mode == BGB_ROUND_RNE, p.gamma_scope == BGB_GAMMA_TOKEN, mins,
+                                       p.q_eps, decode ? 0 : 1,
                                        reinterpret_cast<int8_t*>(carve(ws, lay.q)),
                                        reinterpret_cast<int32_t*>(carve(ws, lay.rowsum)),
                                        reinterpret_cast<float*>(carve(ws, lay.stats)),
@@ -344,8 +347,9 @@ int forward_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N, co
     if ((xq_opt && !aligned16(xq_opt)) || (acc_opt && !aligned16(acc_opt))) return BGB_EINVAL;
     const bgb::BitlinearWs lay = bgb::BitlinearWs::make(M, K, N, tern);
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return BGB_EINVAL;
-    if (M == 1 && bgb::w1a8_decode1_supported(K)) {
-        // one token: its gamma is the tensor's, whatever the scope
+    if (M == 1 && bgb::w1a8_decode1_supported(K) && p.act_range == BGB_RANGE_SYMMETRIC) {
+        // one token: its gamma is the tensor's, whatever the scope (the
+        // non-negative range runs the two-stage path)
         return finish(bgb::launch_w1a8_decode1(x, x_dtype == BGB_BF16, K, N, p.ln_eps, qb, lim,
                                                p.round_mode == BGB_ROUND_RNE, P, beta, y, acc_opt, xq_opt, gamma_opt,
                                                tern, static_cast<hipStream_t>(stream)));

@@ -95,7 +95,7 @@ struct FbiBackwardWs {
 };
 
 struct BitlinearWs {
-    size_t stats, gamma, rowsum, q, part, total;
+    size_t stats, gamma, rowsum, q, mins, part, total;
     // N = 0: the prologue's regions only (what bitlinear_quantize touches)
     // tern: ternary weights (their GEMM plan, hence split partials, differ)
     static BitlinearWs make(int64_t M, int64_t K, int64_t N, bool tern = false) {
@@ -104,7 +104,8 @@ struct BitlinearWs {
         w.gamma = w.stats + align256((size_t(M) * 3 + size_t(M + 3) / 4) * sizeof(float));  // + block maxima
         w.rowsum = w.gamma + 256;                                  // int32 [M]
         w.q = w.rowsum + align256(size_t(M) * sizeof(int32_t));    // int8 [M][Kp], layout per path
-        w.part = w.q + align256(size_t(M) * size_t(padded_k(K)));  // int32 split-K partials (GEMM)
+        w.mins = w.q + align256(size_t(M) * size_t(padded_k(K)));  // float [M] + block minima (eq. (6) range)
+        w.part = w.mins + align256((size_t(M) + size_t(M + 3) / 4) * sizeof(float));   // int32 split-K partials
         w.total = w.part + (M > kGemvMaxM && N > 0 ? gemm_partial_bytes(M, K, N, true, tern) : 0);
         return w;
     }
@@ -116,9 +117,11 @@ hipError_t launch_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t*
                        void* ws, hipStream_t s);
 
 // q layout written by the prologue: 0 = decode kernel layout, 1 = GEMM layout
+// mins != NULL: the non-negative range of eq. (6) (row minima [M] and block
+// minima there; lo = fl32(q_eps) is the lower clip)
 hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, double ln_eps,
-                           float qb, float lim, int rne, int token, int layout, int8_t* q,
-                           int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
+                           float qb, float lim, int rne, int token, float* mins, float lo, int layout,
+                           int8_t* q, int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
                            float* gamma_opt, hipStream_t s);
 
 hipError_t launch_w1a16_gemm(const uint16_t* x, int x_f16, int64_t M, int64_t K, int64_t N,

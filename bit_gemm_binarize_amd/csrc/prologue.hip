@@ -12,6 +12,12 @@
 // lim = fl32(Q_b - q_eps); truncate toward zero (or, as an option, round to
 // nearest even and clamp to +-(Q_b - 1)).
 //
+// The non-negative range (eq. (6), for activations ahead of a non-linear
+// function): the codes are Clip((h - eta) Q_b / gamma, eps, Q_b - eps) with
+// eta = min h over the same scope as gamma (which keeps eq. (5)'s
+// definition), decided in fp32 as d = fl32(h - eta), v = fl32(d Q_b / gamma);
+// codes lie in [0, Q_b - 1]. The product and eq. (7)'s output are unchanged.
+//
 // The codes are written in the order the product kernels read them (one
 // 128-row tile at a time, zero-padded to whole tiles):
 //   layout 0 (decode kernel): dword (4s + d) of a tile holds rows 32d + s + 8e
@@ -32,6 +38,14 @@ BGB_DEV int quant_code(float h, float qb, float gamma, float lim, bool rne, int 
     if (gamma == 0.0f) return 0;
     float v = (h * qb) / gamma;
     v = fminf(fmaxf(v, -lim), lim);
+    return round_code(v, rne, qmax);
+}
+
+// eq. (6): d = fl32(h - eta) >= 0; the lower clip at eps never changes a code.
+BGB_DEV int quant_code_nn(float d, float qb, float gamma, float lo, float lim, bool rne, int qmax) {
+    if (gamma == 0.0f) return 0;
+    float v = (d * qb) / gamma;
+    v = fminf(fmaxf(v, lo), lim);
     return round_code(v, rne, qmax);
 }
 
@@ -60,7 +74,8 @@ BGB_DEV void row_stats(const XT* xr, int64_t K, double eps, double* dscr, float&
 // Quantize one row with a block of NT threads; returns the row's code sum.
 template <int NT, typename XT>
 BGB_DEV int quant_row(const XT* xr, int64_t K, int64_t Kp, float mu32, float rs32, float qb, float gamma,
-                      float lim, bool rne, int layout, uint32_t* qrow, int8_t* natrow, int* iscr) {
+                      float lim, bool rne, bool nonneg, float eta, float lo, int layout, uint32_t* qrow,
+                      int8_t* natrow, int* iscr) {
     const int qmax = int(qb) - 1;
     int sum = 0;
     for (int64_t dwi = threadIdx.x; dwi < Kp / 4; dwi += NT) {
@@ -71,7 +86,9 @@ BGB_DEV int quant_row(const XT* xr, int64_t K, int64_t Kp, float mu32, float rs3
             const int64_t k = k0 + 8 * e;
             int c = 0;
             if (k < K) {
-                c = quant_code(ln_apply(load_x(xr, k), mu32, rs32), qb, gamma, lim, rne, qmax);
+                const float h = ln_apply(load_x(xr, k), mu32, rs32);
+                c = nonneg ? quant_code_nn(h - eta, qb, gamma, lo, lim, rne, qmax)
+                           : quant_code(h, qb, gamma, lim, rne, qmax);
                 if (natrow) natrow[k] = int8_t(c);
             }
             sum += c;
@@ -86,14 +103,15 @@ BGB_DEV int quant_row(const XT* xr, int64_t K, int64_t Kp, float mu32, float rs3
 template <typename XT>
 __global__ void __launch_bounds__(1024)
 lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double eps, float qb, float lim,
-                 int rne, int token, int layout, int8_t* __restrict__ q, int32_t* __restrict__ rowsum,
+                 int rne, int token, int nonneg, float lo, int layout, int8_t* __restrict__ q,
+                 int32_t* __restrict__ rowsum,
                  float* __restrict__ stats, float* __restrict__ gamma_ws, int8_t* __restrict__ xq_opt,
                  float* __restrict__ gamma_opt) {
     __shared__ double dscr[16];
     __shared__ float fscr[16];
     __shared__ int iscr[16];
-    __shared__ float s_mu[kSmallPrologueM], s_rs[kSmallPrologueM], s_lm[kSmallPrologueM];
-    float gmax = 0.0f;
+    __shared__ float s_mu[kSmallPrologueM], s_rs[kSmallPrologueM], s_lm[kSmallPrologueM], s_mn[kSmallPrologueM];
+    float gmax = 0.0f, gmin = __builtin_inff();
     for (int m = 0; m < M; ++m) {
         const XT* xr = x + int64_t(m) * K;
         float mu32, rs32;
@@ -101,15 +119,22 @@ lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double 
         float lm = 0.0f;
         for (int64_t i = threadIdx.x; i < K; i += 1024) lm = fmaxf(lm, fabsf(ln_apply(load_x(xr, i), mu32, rs32)));
         lm = block_max<1024>(lm, fscr);
+        float mn = __builtin_inff();                 // eq. (6): the row's min h (min x, h monotone in x)
+        if (nonneg) {
+            for (int64_t i = threadIdx.x; i < K; i += 1024) mn = fminf(mn, ln_apply(load_x(xr, i), mu32, rs32));
+            mn = -block_max<1024>(-mn, fscr);
+        }
         if (threadIdx.x == 0) {
             s_mu[m] = mu32;
             s_rs[m] = rs32;
             s_lm[m] = lm;
+            s_mn[m] = mn;
             stats[3 * m] = mu32;
             stats[3 * m + 1] = rs32;
             stats[3 * m + 2] = lm;
         }
         gmax = fmaxf(gmax, lm);
+        gmin = fminf(gmin, mn);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -119,7 +144,9 @@ lnq_small_kernel(const XT* __restrict__ x, int M, int64_t K, int64_t Kp, double 
     if (gamma_opt && token && threadIdx.x < M) gamma_opt[threadIdx.x] = s_lm[threadIdx.x];
     for (int m = 0; m < M; ++m) {
         const float gamma = token ? s_lm[m] : gmax;     // the token's own, or the tensor's
-        const int s = quant_row<1024>(x + int64_t(m) * K, K, Kp, s_mu[m], s_rs[m], qb, gamma, lim, rne != 0, layout,
+        const float eta = token ? s_mn[m] : gmin;
+        const int s = quant_row<1024>(x + int64_t(m) * K, K, Kp, s_mu[m], s_rs[m], qb, gamma, lim, rne != 0,
+                                      nonneg != 0, eta, lo, layout,
                                       reinterpret_cast<uint32_t*>(q + int64_t(m) * Kp),
                                       xq_opt ? xq_opt + int64_t(m) * K : nullptr, iscr);
         if (threadIdx.x == 0) rowsum[m] = s;
@@ -154,13 +181,13 @@ template <> struct Vec16<uint16_t> {         // 8 bf16 elements per 16 bytes
 template <typename XT>
 __global__ void __launch_bounds__(256)
 lnq_stats_kernel(const XT* __restrict__ x, int64_t M, int64_t K, double eps, float* __restrict__ stats,
-                 float* __restrict__ blockmax) {
+                 float* __restrict__ blockmax, float* __restrict__ mins) {
     using V = Vec16<XT>;
     constexpr int E = V::E;
-    __shared__ float bm[4];
+    __shared__ float bm[4], bn[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t m = int64_t(blockIdx.x) * 4 + wave;
-    float rowmax = 0.0f;
+    float rowmax = 0.0f, rowmin = __builtin_inff();
     if (m < M) {
         const XT* xr = x + m * K;
         const int64_t nvec = K / E;
@@ -195,15 +222,23 @@ lnq_stats_kernel(const XT* __restrict__ x, int64_t M, int64_t K, double eps, flo
         const float rs32 = float(1.0 / sqrt(__shfl(s2, 63) / double(K) + eps));
         const float hx = __shfl(mx, 63), hn = __shfl(mn, 63);
         rowmax = fmaxf(fabsf(ln_apply(hx, mu32, rs32)), fabsf(ln_apply(hn, mu32, rs32)));
+        rowmin = ln_apply(hn, mu32, rs32);                  // h is monotone in x
+        if (mins && lane == 0) mins[m] = rowmin;
         if (lane == 0) {
             stats[3 * m] = mu32;
             stats[3 * m + 1] = rs32;
             stats[3 * m + 2] = rowmax;
         }
     }
-    if (lane == 0) bm[wave] = rowmax;
+    if (lane == 0) {
+        bm[wave] = rowmax;
+        bn[wave] = rowmin;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) blockmax[blockIdx.x] = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
+    if (threadIdx.x == 0) {
+        blockmax[blockIdx.x] = fmaxf(fmaxf(bm[0], bm[1]), fmaxf(bm[2], bm[3]));
+        if (mins) mins[M + blockIdx.x] = fminf(fminf(bn[0], bn[1]), fminf(bn[2], bn[3]));
+    }
 }
 
 // Pass 2: gamma = max over the block maxima (every block computes the same
@@ -213,20 +248,28 @@ lnq_stats_kernel(const XT* __restrict__ x, int64_t M, int64_t K, double eps, flo
 template <typename XT>
 __global__ void __launch_bounds__(256)
 lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, float qb, float lim, int rne,
-                 int token, int layout, const float* __restrict__ stats, const float* __restrict__ blockmax,
-                 int nblocks,
+                 int token, float lo, int layout, const float* __restrict__ stats, const float* __restrict__ blockmax,
+                 const float* __restrict__ mins, int nblocks,
                  int8_t* __restrict__ q, int32_t* __restrict__ rowsum, float* __restrict__ gamma_ws,
                  int8_t* __restrict__ xq_opt, float* __restrict__ gamma_opt) {
     using V = Vec16<XT>;
     constexpr int E = V::E;
-    __shared__ float gscr[4];
+    __shared__ float gscr[4], nscr[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float gm = 0.0f;
-    for (int i = threadIdx.x; i < nblocks; i += 256) gm = fmaxf(gm, blockmax[i]);
+    float gm = 0.0f, gn = __builtin_inff();
+    for (int i = threadIdx.x; i < nblocks; i += 256) {
+        gm = fmaxf(gm, blockmax[i]);
+        if (mins) gn = fminf(gn, mins[M + i]);
+    }
     gm = wave_max63_nonneg(gm);
-    if (lane == 63) gscr[wave] = gm;
+    gn = wave_min63(gn);
+    if (lane == 63) {
+        gscr[wave] = gm;
+        nscr[wave] = gn;
+    }
     __syncthreads();
     const float gt = fmaxf(fmaxf(gscr[0], gscr[1]), fmaxf(gscr[2], gscr[3]));
+    const float nt = fminf(fminf(nscr[0], nscr[1]), fminf(nscr[2], nscr[3]));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         gamma_ws[0] = gt;
         if (gamma_opt && !token) gamma_opt[0] = gt;
@@ -236,6 +279,8 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
     const XT* xr = x + m * K;
     const float mu32 = stats[3 * m], rs32 = stats[3 * m + 1];
     const float gamma = token ? stats[3 * m + 2] : gt;      // the token's own, or the tensor's
+    const bool nonneg = mins != nullptr;
+    const float eta = nonneg ? (token ? mins[m] : nt) : 0.0f;
     if (gamma_opt && token && lane == 0) gamma_opt[m] = gamma;
     const bool rn = rne != 0;
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
@@ -253,6 +298,7 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
                 h[j] = ln_apply(h[j], mu32, rs32);
+                if (nonneg) h[j] = h[j] - eta;               // eq. (6): d = fl32(h - eta)
                 // fast path: u = h (Q_b rcp(gamma)) is within 1.5 ulp of the exact
                 // quotient; only u near a code boundary (rare) can round differently
                 const float u = h[j] * cq;
@@ -262,7 +308,9 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
             if (slow && gamma != 0.0f) {
 #pragma unroll
                 for (int j = 0; j < 32; ++j)
-                    if (slow & (1u << j)) code[j] = quant_code(h[j], qb, gamma, lim, rn, qmax);
+                    if (slow & (1u << j))
+                        code[j] = nonneg ? quant_code_nn(h[j], qb, gamma, lo, lim, rn, qmax)
+                                         : quant_code(h[j], qb, gamma, lim, rn, qmax);
             }
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
@@ -299,30 +347,30 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
 
 template <typename XT>
 static void launch_lnq_t(const XT* x, int64_t M, int64_t K, double eps, float qb, float lim, int rne, int token,
-                         int layout, int8_t* q, int32_t* rowsum, float* stats, float* gamma_ws, int8_t* xq_opt,
-                         float* gamma_opt, hipStream_t s) {
+                         float* mins, float lo, int layout, int8_t* q, int32_t* rowsum, float* stats,
+                         float* gamma_ws, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
     const int64_t Kp = padded_k(K);
     if (M <= kSmallPrologueM) {
-        lnq_small_kernel<XT><<<1, 1024, 0, s>>>(x, int(M), K, Kp, eps, qb, lim, rne, token, layout, q, rowsum,
-                                                 stats, gamma_ws, xq_opt, gamma_opt);
+        lnq_small_kernel<XT><<<1, 1024, 0, s>>>(x, int(M), K, Kp, eps, qb, lim, rne, token, mins != nullptr, lo,
+                                                 layout, q, rowsum, stats, gamma_ws, xq_opt, gamma_opt);
     } else {
         const unsigned blocks = unsigned((M + 3) / 4);
         float* blockmax = stats + 3 * M;       // the workspace's stats region holds [M][3] + ceil(M/4)
-        lnq_stats_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, eps, stats, blockmax);
-        lnq_quant_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, Kp, qb, lim, rne, token, layout, stats, blockmax,
-                                                     int(blocks), q, rowsum, gamma_ws, xq_opt, gamma_opt);
+        lnq_stats_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, eps, stats, blockmax, mins);
+        lnq_quant_kernel<XT><<<blocks, 256, 0, s>>>(x, M, K, Kp, qb, lim, rne, token, lo, layout, stats, blockmax,
+                                                     mins, int(blocks), q, rowsum, gamma_ws, xq_opt, gamma_opt);
     }
 }
 
 hipError_t launch_ln_quant(const void* x, int x_bf16, int64_t M, int64_t K, double ln_eps, float qb, float lim,
-                           int rne, int token, int layout, int8_t* q, int32_t* rowsum, float* stats,
-                           float* gamma_ws, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
+                           int rne, int token, float* mins, float lo, int layout, int8_t* q, int32_t* rowsum,
+                           float* stats, float* gamma_ws, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
     if (x_bf16)
-        launch_lnq_t(static_cast<const uint16_t*>(x), M, K, ln_eps, qb, lim, rne, token, layout, q, rowsum, stats,
-                     gamma_ws, xq_opt, gamma_opt, s);
+        launch_lnq_t(static_cast<const uint16_t*>(x), M, K, ln_eps, qb, lim, rne, token, mins, lo, layout, q, rowsum,
+                     stats, gamma_ws, xq_opt, gamma_opt, s);
     else
-        launch_lnq_t(static_cast<const float*>(x), M, K, ln_eps, qb, lim, rne, token, layout, q, rowsum, stats,
-                     gamma_ws, xq_opt, gamma_opt, s);
+        launch_lnq_t(static_cast<const float*>(x), M, K, ln_eps, qb, lim, rne, token, mins, lo, layout, q, rowsum,
+                     stats, gamma_ws, xq_opt, gamma_opt, s);
     return hipGetLastError();
 }
 

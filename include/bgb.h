@@ -87,14 +87,22 @@ typedef enum { BGB_ROUND_TRUNC = 0, BGB_ROUND_RNE = 1 } bgb_round_mode;
  * default; section 一 speaks of the input matrix's maximum) or each token. */
 typedef enum { BGB_GAMMA_TENSOR = 0, BGB_GAMMA_TOKEN = 1 } bgb_gamma_scope;
 
+/* The codes' range: symmetric (eq. (4), the default) or non-negative (eq. (6),
+ * for activations ahead of a non-linear function): Clip((h - eta) Q_b / gamma,
+ * eps, Q_b - eps) with eta = min h over gamma's scope and gamma = ||h||_inf as
+ * eq. (5) defines it, codes in [0, Q_b - 1]. The page gives eq. (7) only, so
+ * the output is W~ q beta gamma / Q_b for both ranges (eta is not added back). */
+typedef enum { BGB_RANGE_SYMMETRIC = 0, BGB_RANGE_NONNEG = 1 } bgb_act_range;
+
 /* Activation quantization parameters of BitLinear ("BitNet b1.58: 1bit LLM时代",
- * section 一, eq. (4), (5), (8)). */
+ * section 一, eq. (4)-(6), (8)). */
 typedef struct {
     double ln_eps;   /* LayerNorm epsilon added to the variance, > 0 (1e-5) */
     int bits;        /* b in Q_b = 2^(b-1); 2..8 (8 -> Q_b = 128, int8 codes) */
     float q_eps;     /* clip margin in (0, 1): codes are clipped to [-Q_b+eps, Q_b-eps] (1e-3) */
     int round_mode;  /* bgb_round_mode (BGB_ROUND_TRUNC) */
     int gamma_scope; /* bgb_gamma_scope (BGB_GAMMA_TENSOR) */
+    int act_range;   /* bgb_act_range (BGB_RANGE_SYMMETRIC) */
 } bgb_quant_params;
 
 /* Size in bytes of the packed array P for a K x N weight (0 if K is invalid). */

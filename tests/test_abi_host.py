@@ -215,6 +215,9 @@ def test_bitlinear_validation(lib):
     assert call_bl(lib, qp=ctypes.pointer(bad_eps)) == BAD
     assert call_bl(lib, qp=ctypes.pointer(bgb._QP(1e-5, 8, 1e-3, 2, 0))) == UNSUP   # round mode
     assert call_bl(lib, qp=ctypes.pointer(bgb._QP(1e-5, 8, 1e-3, 0, 5))) == UNSUP   # gamma scope
+    assert call_bl(lib, qp=ctypes.pointer(bgb._QP(1e-5, 8, 1e-3, 0, 0, 2))) == UNSUP   # activation range
+    # the non-negative range keeps its row and block minima in the workspace
+    assert bgb.workspace_bytes(bgb.OP_BITLINEAR, 100, 4096, 0) >= 100 * 4096 + (100 + 25) * 4
     assert call_bl(lib, M=0) == 0
 
 
