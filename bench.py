@@ -288,10 +288,10 @@ def leg_decode_7b(torch, bgb, syn, steps):
             "us_per_layer": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
             "bytes_per_layer": nbytes, "bound": "hbm", "layer_copies": L, "linears": "qkv, o, gate_up, down"}
         log(f"decode 7B layer fused B={B}: {ms * 1e3:.1f} us/layer, {gbs:.0f} GB/s")
-        if B != 1:
+        if B > 4:
             continue
-        # the 4 linears of the layer as one group: one launch for a single
-        # token (the linears' inputs are independent synthetic tensors here)
+        # the 4 linears of the layer as one group: one launch for 1 and 4
+        # tokens (the linears' inputs are independent synthetic tensors here)
         gys = [torch.empty((B, N), dtype=torch.bfloat16, device="cuda") for _, _, N in fshapes]
 
         def gbody(i, xs=xs, gys=gys):

@@ -135,11 +135,20 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return na && nb && pa < pb + nb && pb < pa + na;
 }
 
-static bool group_one_launch(const bgb_w1a16_item* items, int count, int64_t M) {
-    if (M != 1) return false;
+static int group_live(const bgb_w1a16_item* items, int count, bgb::W1a16Item* out) {
+    int n = 0;
     for (int i = 0; i < count; ++i)
-        if (items[i].N > 0 && !bgb::w1a16_decode1_supported(items[i].K)) return false;
-    return true;
+        if (items[i].N > 0) out[n++] = bgb::W1a16Item{items[i].x, items[i].P, items[i].alpha, items[i].y, items[i].K,
+                                                      items[i].N};
+    return n;
+}
+
+// 1: one single-token launch; 2: one few-token launch; 0: item by item.
+static int group_one_launch(const bgb_w1a16_item* items, int count, int64_t M) {
+    bgb::W1a16Item in[BGB_GROUP_MAX];
+    const int n = group_live(items, count, in);
+    if (M == 1) return bgb::w1a16_decode1_group_supported(in, n) ? 1 : 0;
+    return bgb::w1a16_decodem_group_supported(in, n, M) ? 2 : 0;
 }
 
 size_t bgb_group_workspace_bytes(const bgb_w1a16_item* items, int count, int64_t M) {
@@ -188,15 +197,14 @@ int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, in
     const size_t need = bgb_group_workspace_bytes(items, count, M);
     if (need && (!ws || ws_bytes < need || !aligned16(ws))) return BGB_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (group_one_launch(items, count, M)) {
+    const int one = group_one_launch(items, count, M);
+    if (one) {
         bgb::W1a16Item in[BGB_GROUP_MAX];
-        int n = 0;
-        for (int i = 0; i < count; ++i) {
-            if (!live[i]) continue;
-            in[n++] = bgb::W1a16Item{items[i].x, items[i].P, items[i].alpha, items[i].y, items[i].K, items[i].N};
-        }
+        const int n = group_live(items, count, in);
         const int ydt = y_dtype == BGB_F32 ? 0 : (y_dtype == BGB_F16 ? 1 : 2);
-        return finish(bgb::launch_w1a16_decode1_group(in, n, x_dtype == BGB_F16, alpha_dtype == BGB_F16, ydt, s));
+        const int xf = x_dtype == BGB_F16, af = alpha_dtype == BGB_F16;
+        return finish(one == 1 ? bgb::launch_w1a16_decode1_group(in, n, xf, af, ydt, s)
+                               : bgb::launch_w1a16_decodem_group(in, n, M, xf, af, ydt, s));
     }
     for (int i = 0; i < count; ++i) {
         if (!live[i]) continue;

@@ -1112,17 +1112,18 @@ constexpr int kDmWaves = 8;
 constexpr int kDmLdsBytes = 140 * 1024;              // staged tokens: [M][Kp + 8] 16-bit values
 constexpr int kDmMaxJobs = 2;                        // 256-byte token tiles per thread
 
+// The body is shared by the one-linear kernel (bid, nblk = the block index
+// and count) and the grouped one (the block's rank and count within its
+// linear). LDS: xs [kDmLdsBytes / 2], xzero [128] (the B operand of steps
+// past the last tile), red [2 NW 64] when KQ > 1.
 template <bool kF16, bool kTileJobs, int F, int S, int IT>
-__global__ void __launch_bounds__(kDmWaves * 64)
-fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
-                   const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
-                   void* __restrict__ y, int y_dtype) {
+BGB_DEV void fbi_decodem_body(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
+                              const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
+                              void* __restrict__ y, int y_dtype, int64_t bid, int64_t nblk, uint16_t* xs,
+                              uint16_t* xzero, f32x4_t* red) {
     constexpr int NW = kDmWaves, NT = NW * 64;
     constexpr int KQ = NW / F;
     static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "few-token W1A16 shape");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kDmLdsBytes / 2];
-    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];   // B operand of steps past the last tile
-    __shared__ f32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
     const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
@@ -1139,7 +1140,7 @@ fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the tokens are in
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+            const int64_t grp = bid + int64_t(it) * nblk;
             const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
             preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
         }
@@ -1221,11 +1222,11 @@ fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
     uint2 araw[IT][2];                                  // this lane's 4 column scales per group
 #pragma unroll
     for (int it = 0; it < IT; ++it)
-        alpha4_load(alpha, alpha_f16, (int64_t(blockIdx.x) + int64_t(it) * gridDim.x) * 16 * F + 16 * f + 4 * g, N,
+        alpha4_load(alpha, alpha_f16, (bid + int64_t(it) * nblk) * 16 * F + 16 * f + 4 * g, N,
                     araw[it]);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
+        const int64_t grp = bid + int64_t(it) * nblk;
         if (grp >= ngroups) break;
         f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};   // by u parity
 #pragma unroll
@@ -1248,12 +1249,12 @@ fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
         }
         f32x4_t z = acc[0] + acc[1];
         if constexpr (KQ > 1) {
-            red[it & 1][wave][lane] = z;
+            red[((it & 1) * NW + wave) * 64 + lane] = z;
             __syncthreads();
             if (kq != 0 || r >= M) continue;
             // the parts in a fixed order: kq = 0, 1, ..., KQ - 1
 #pragma unroll
-            for (int q = 1; q < KQ; ++q) z += red[it & 1][f + F * q][lane];
+            for (int q = 1; q < KQ; ++q) z += red[((it & 1) * NW + f + F * q) * 64 + lane];
         } else {
             if (r >= M) continue;
         }
@@ -1267,10 +1268,26 @@ fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, 
     }
 }
 
+template <bool kF16, bool kTileJobs, int F, int S, int IT>
+__global__ void __launch_bounds__(kDmWaves * 64)
+fbi_decodem_kernel(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
+                   const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
+                   void* __restrict__ y, int y_dtype) {
+    constexpr int KQ = kDmWaves / F;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kDmLdsBytes / 2];
+    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];
+    __shared__ f32x4_t red[(KQ > 1 ? 2 * kDmWaves : 1) * 64];
+    fbi_decodem_body<kF16, kTileJobs, F, S, IT>(x, M, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, blockIdx.x,
+                                                gridDim.x, xs, xzero, red);
+}
+
 bool w1a16_decodem_supported(int64_t M, int64_t K) {
     if (M < 2 || M > kDmMaxTokens) return false;
     const int64_t Kp = padded_k(K);
-    return M * (Kp + 8) * 2 <= kDmLdsBytes && M * (Kp / 128) <= int64_t(kDmMaxJobs) * kDmWaves * 64;
+    // the tokens fit in LDS; at most 2 tiles per thread to stage; and at most
+    // kD1MaxTiles steps per wave when the 8 waves share one fragment's K range
+    return M * (Kp + 8) * 2 <= kDmLdsBytes && M * (Kp / 128) <= int64_t(kDmMaxJobs) * kDmWaves * 64 &&
+           Kp <= int64_t(kD1MaxTiles) * kDmWaves * 4 * 128;
 }
 
 template <bool kF16, bool kTJ, int F, int S>
@@ -1349,6 +1366,117 @@ hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, 
                          : launch_w1a16_decodem_t<true, false>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
     return tj ? launch_w1a16_decodem_t<false, true>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s)
               : launch_w1a16_decodem_t<false, false>(xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, s);
+}
+
+// Several independent linears of 2..16 tokens in one launch: each linear
+// keeps the split of its own launch (F fragments per group, S steps per
+// wave, one group per block), the grid is the concatenation of the linears'
+// blocks (most sign bytes per block first), and a block finds its linear by
+// uniform selects over the table in the kernel arguments. Only shapes whose
+// tokens are staged in pieces (fewer 128-row tiles than threads, M TQ < 512)
+// take this form.
+struct DmItem {
+    const uint16_t* x;
+    const uint32_t* P;
+    const void* alpha;
+    void* y;
+    int64_t K, N, TQ;
+    int first, nblk, cfg;   // first block, block count, (F, S) case
+};
+struct DmGroup {
+    DmItem it[kGroupMax];
+    int count, M, alpha_f16, y_dtype;
+};
+
+template <bool kF16>
+__global__ void __launch_bounds__(kDmWaves * 64)
+fbi_decodem_group_kernel(const DmGroup g) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kDmLdsBytes / 2];
+    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];
+    __shared__ f32x4_t red[2 * kDmWaves * 64];
+    DmItem it = g.it[0];
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < g.count && int(blockIdx.x) >= g.it[i].first) it = g.it[i];
+    const int64_t bid = int64_t(blockIdx.x) - it.first;
+#define BGB_GM(C, FV, SV)                                                                                         \
+    case C:                                                                                                    \
+        fbi_decodem_body<kF16, false, FV, SV, 1>(it.x, g.M, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y, \
+                                                 g.y_dtype, bid, it.nblk, xs, xzero, red);                     \
+        break;
+    switch (it.cfg) {
+        BGB_GM(0, 1, 1) BGB_GM(1, 1, 2) BGB_GM(2, 1, 4) BGB_GM(3, 1, 8)
+        BGB_GM(4, 2, 1) BGB_GM(5, 2, 2) BGB_GM(6, 2, 4) BGB_GM(7, 2, 8)
+        BGB_GM(8, 4, 1) BGB_GM(9, 4, 2) BGB_GM(10, 4, 4) BGB_GM(11, 4, 8)
+        BGB_GM(12, 8, 1) BGB_GM(13, 8, 2) BGB_GM(14, 8, 4) BGB_GM(15, 8, 8)
+        default: break;
+    }
+#undef BGB_GM
+}
+
+bool w1a16_decodem_group_supported(const W1a16Item* items, int count, int64_t M) {
+    if (count < 0 || count > kGroupMax) return false;
+    for (int i = 0; i < count; ++i) {
+        if (items[i].N <= 0) continue;
+        if (!w1a16_decodem_supported(M, items[i].K)) return false;
+        if (M * tiles_per_col(items[i].K) >= kDmWaves * 64) return false;   // whole-tile staging: not grouped
+    }
+    return true;
+}
+
+hipError_t launch_w1a16_decodem_group(const W1a16Item* items, int count, int64_t M, int x_f16, int alpha_f16,
+                                      int y_dtype, hipStream_t s) {
+    if (!w1a16_decodem_group_supported(items, count, M)) return hipErrorInvalidValue;
+    DmGroup g{};
+    int order[kGroupMax], n = 0;
+    int64_t cost[kGroupMax];
+    for (int i = 0; i < count; ++i) {
+        if (items[i].N <= 0) continue;
+        const W1a16Item& in = items[i];
+        DmItem& d = g.it[n];
+        d.x = static_cast<const uint16_t*>(in.x);
+        d.P = in.P;
+        d.alpha = in.alpha;
+        d.y = in.y;
+        d.K = in.K;
+        d.N = in.N;
+        d.TQ = tiles_per_col(in.K);
+        const int64_t steps = (d.TQ + 3) / 4, frags = (in.N + 15) / 16;
+        auto spw = [&](int f) {                              // as the one-linear launcher
+            const int64_t need = (steps + kDmWaves / f - 1) / (kDmWaves / f);
+            return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+        };
+        int F = 1;
+        while (2 * F <= kDmWaves && spw(2 * F) <= kD1MaxTiles && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
+        const int S = spw(F);
+        if (S > kD1MaxTiles) return hipErrorInvalidValue;  // not reached: supported()
+        d.nblk = int((frags + F - 1) / F);
+        d.cfg = 4 * (F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3) + (S == 1 ? 0 : S == 2 ? 1 : S == 4 ? 2 : 3);
+        cost[n] = int64_t(F) * d.TQ;
+        order[n] = n;
+        ++n;
+    }
+    if (n == 0) return hipSuccess;
+    for (int a = 1; a < n; ++a)
+        for (int b = a; b > 0 && cost[order[b]] > cost[order[b - 1]]; --b) {
+            const int t = order[b];
+            order[b] = order[b - 1];
+            order[b - 1] = t;
+        }
+    DmGroup h{};
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        h.it[i] = g.it[order[i]];
+        h.it[i].first = int(total);
+        total += h.it[i].nblk;
+    }
+    h.count = n;
+    h.M = int(M);
+    h.alpha_f16 = alpha_f16;
+    h.y_dtype = y_dtype;
+    if (x_f16) fbi_decodem_group_kernel<true><<<unsigned(total), kDmWaves * 64, 0, s>>>(h);
+    else fbi_decodem_group_kernel<false><<<unsigned(total), kDmWaves * 64, 0, s>>>(h);
+    return hipGetLastError();
 }
 
 // Up to 64 tokens, activation staging fused, K in chunks. A block of 8 waves

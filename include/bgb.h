@@ -184,10 +184,11 @@ typedef struct {
  * paragraph of the FBI-LLM news rewrite; the model replaces every linear of a
  * layer) over the same number of tokens M and the same dtypes: for each item,
  * the result of fbi_linear_w1a16(item.x, x_dtype, M, item.K, item.N, item.P,
- * item.alpha, alpha_dtype, item.y, y_dtype, ...). For a single token (M = 1)
- * with every K <= 16384 all items run in one launch (each item split into
- * column groups of its own, one per block); otherwise they run one after
- * another in the order given. Sums are accumulated in fp32 in a fixed order,
+ * item.alpha, alpha_dtype, item.y, y_dtype, ...). All items run in one
+ * launch (each item split into column groups of its own, one per block) for a
+ * single token (M = 1) with every K <= 16384, and for 2 <= M <= 16 tokens
+ * when every item's tokens fit in LDS and M * ceil(K / 128) < 512; otherwise
+ * they run one after another in the order given. Sums are accumulated in fp32 in a fixed order,
  * so results are the same from run to run; the one-launch form may group a
  * linear's K range differently from fbi_linear_w1a16 (a different rounding
  * order of the fp32 sum, not bit-identical to it).

@@ -39,6 +39,9 @@ CASES = [
     # K split over 1..8 waves), and sizes just past what fits (two launches)
     (2, 16384, 300), (4, 11008, 4096), (5, 11008, 100), (6, 11008, 70), (12, 2048, 1000), (16, 4096, 4100),
     (16, 4096, 12288), (2, 1024, 40000),
+    # two tokens whose K fits in LDS but needs more than 8 steps per wave:
+    # the chunked kernel takes them
+    (2, 33024, 40),
     # 2..64 tokens with K staged in chunks: 16 or 32 tokens per block, one or
     # more token blocks, chunk tails, K beyond the fused single-token size, K
     # split over 3..17 blocks per column block (raw sums, then the reduce pass)

@@ -74,10 +74,12 @@ def test_group_integer_activations_bit_exact(bgb_gpu, orc, x_kind):
     _check_items(orc, items, ys, x_kind, "f32", exact=True)
 
 
-@pytest.mark.parametrize("M", [4, 40, 70])
+@pytest.mark.parametrize("M", [2, 4, 16, 40, 70])
 def test_group_several_tokens_parity(bgb_gpu, orc, M):
-    """More than one token: the items run one after another through the
-    single-linear dispatch, sharing the largest item's workspace."""
+    """More than one token: one launch for 2..16 tokens staged in pieces (M = 2,
+    4), otherwise the items one after another through the single-linear
+    dispatch (M = 16 with K = 11008 stages whole tiles; 40, 70), sharing the
+    largest item's workspace."""
     shapes = [(1024, 300), (11008, 200), (96, 65), (2048, 520)]
     say(f"group M={M} shapes={shapes}")
     items = _items(bgb_gpu, shapes, M, "bf16", "f32", 700 + M)
@@ -131,3 +133,26 @@ def test_group_single_token_beyond_fused_size(bgb_gpu, orc):
     ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items])
     torch.cuda.synchronize()
     _check_items(orc, items, ys, "bf16", "f32")
+
+
+@pytest.mark.parametrize("M", [2, 3, 8])
+def test_group_few_tokens_every_shape(bgb_gpu, orc, M):
+    """A few tokens over shapes that take (fragments per block, steps per wave)
+    = (8, 8), (4, 4), (4, 1), (2, 4), (2, 2), (1, 4), (1, 1), with ragged N:
+    one launch for M = 2 and 3; at M = 8 the 12288- and 8192-row items stage
+    whole tiles, so the group runs item by item."""
+    shapes = [(4096, 22016), (4096, 12288), (1024, 8200), (8192, 5000), (4096, 5000), (12288, 100), (96, 65),
+              (2048, 300)]
+    say(f"group M={M} few-token shapes={shapes}")
+    items = _items(bgb_gpu, shapes, M, "bf16", "f16", 1100 + M)
+    ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items], torch.bfloat16)
+    torch.cuda.synchronize()
+    _check_items(orc, items, ys, "bf16", "bf16")
+
+
+def test_group_few_tokens_integer_bit_exact(bgb_gpu, orc):
+    say("group M=4 integer-exact")
+    items = _items(bgb_gpu, SHAPES[:6], 4, "bf16", "f32", 1200, int_x=True)
+    ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items])
+    torch.cuda.synchronize()
+    _check_items(orc, items, ys, "bf16", "f32", exact=True)
