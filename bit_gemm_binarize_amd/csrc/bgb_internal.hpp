@@ -166,8 +166,8 @@ struct W1a16Item {
 bool w1a16_decode1_group_supported(const W1a16Item* items, int count);
 hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f16, int alpha_f16, int y_dtype,
                                       hipStream_t s);
-// 2 <= M <= 16 tokens, each item staged whole in LDS in 16-byte pieces
-// (w1a16_decodem_supported and M tiles_per_col(K) < 512), one launch.
+// 2 <= M <= 16 tokens, every item's tokens staged whole in LDS
+// (w1a16_decodem_supported), one launch.
 bool w1a16_decodem_group_supported(const W1a16Item* items, int count, int64_t M);
 hipError_t launch_w1a16_decodem_group(const W1a16Item* items, int count, int64_t M, int x_f16, int alpha_f16,
                                       int y_dtype, hipStream_t s);

@@ -1372,16 +1372,16 @@ hipError_t launch_w1a16_decodem(const void* x, int x_f16, int64_t M, int64_t K, 
 // keeps the split of its own launch (F fragments per group, S steps per
 // wave, one group per block), the grid is the concatenation of the linears'
 // blocks (most sign bytes per block first), and a block finds its linear by
-// uniform selects over the table in the kernel arguments. Only shapes whose
-// tokens are staged in pieces (fewer 128-row tiles than threads, M TQ < 512)
-// take this form.
+// uniform selects over the table in the kernel arguments. Each item keeps its
+// own staging form too (16-byte pieces, or whole 128-row tiles once there
+// are as many tiles as threads).
 struct DmItem {
     const uint16_t* x;
     const uint32_t* P;
     const void* alpha;
     void* y;
     int64_t K, N, TQ;
-    int first, nblk, cfg;   // first block, block count, (F, S) case
+    int first, nblk, cfg;   // first block, block count, (staging, F, S) case
 };
 struct DmGroup {
     DmItem it[kGroupMax];
@@ -1399,16 +1399,20 @@ fbi_decodem_group_kernel(const DmGroup g) {
     for (int i = 1; i < kGroupMax; ++i)
         if (i < g.count && int(blockIdx.x) >= g.it[i].first) it = g.it[i];
     const int64_t bid = int64_t(blockIdx.x) - it.first;
-#define BGB_GM(C, FV, SV)                                                                                         \
+#define BGB_GM(C, TJ, FV, SV)                                                                                     \
     case C:                                                                                                    \
-        fbi_decodem_body<kF16, false, FV, SV, 1>(it.x, g.M, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y, \
-                                                 g.y_dtype, bid, it.nblk, xs, xzero, red);                     \
+        fbi_decodem_body<kF16, TJ, FV, SV, 1>(it.x, g.M, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y,   \
+                                              g.y_dtype, bid, it.nblk, xs, xzero, red);                        \
         break;
     switch (it.cfg) {
-        BGB_GM(0, 1, 1) BGB_GM(1, 1, 2) BGB_GM(2, 1, 4) BGB_GM(3, 1, 8)
-        BGB_GM(4, 2, 1) BGB_GM(5, 2, 2) BGB_GM(6, 2, 4) BGB_GM(7, 2, 8)
-        BGB_GM(8, 4, 1) BGB_GM(9, 4, 2) BGB_GM(10, 4, 4) BGB_GM(11, 4, 8)
-        BGB_GM(12, 8, 1) BGB_GM(13, 8, 2) BGB_GM(14, 8, 4) BGB_GM(15, 8, 8)
+        BGB_GM(0, false, 1, 1) BGB_GM(1, false, 1, 2) BGB_GM(2, false, 1, 4) BGB_GM(3, false, 1, 8)
+        BGB_GM(4, false, 2, 1) BGB_GM(5, false, 2, 2) BGB_GM(6, false, 2, 4) BGB_GM(7, false, 2, 8)
+        BGB_GM(8, false, 4, 1) BGB_GM(9, false, 4, 2) BGB_GM(10, false, 4, 4) BGB_GM(11, false, 4, 8)
+        BGB_GM(12, false, 8, 1) BGB_GM(13, false, 8, 2) BGB_GM(14, false, 8, 4) BGB_GM(15, false, 8, 8)
+        BGB_GM(16, true, 1, 1) BGB_GM(17, true, 1, 2) BGB_GM(18, true, 1, 4) BGB_GM(19, true, 1, 8)
+        BGB_GM(20, true, 2, 1) BGB_GM(21, true, 2, 2) BGB_GM(22, true, 2, 4) BGB_GM(23, true, 2, 8)
+        BGB_GM(24, true, 4, 1) BGB_GM(25, true, 4, 2) BGB_GM(26, true, 4, 4) BGB_GM(27, true, 4, 8)
+        BGB_GM(28, true, 8, 1) BGB_GM(29, true, 8, 2) BGB_GM(30, true, 8, 4) BGB_GM(31, true, 8, 8)
         default: break;
     }
 #undef BGB_GM
@@ -1419,7 +1423,6 @@ bool w1a16_decodem_group_supported(const W1a16Item* items, int count, int64_t M)
     for (int i = 0; i < count; ++i) {
         if (items[i].N <= 0) continue;
         if (!w1a16_decodem_supported(M, items[i].K)) return false;
-        if (M * tiles_per_col(items[i].K) >= kDmWaves * 64) return false;   // whole-tile staging: not grouped
     }
     return true;
 }
@@ -1451,7 +1454,8 @@ hipError_t launch_w1a16_decodem_group(const W1a16Item* items, int count, int64_t
         const int S = spw(F);
         if (S > kD1MaxTiles) return hipErrorInvalidValue;  // not reached: supported()
         d.nblk = int((frags + F - 1) / F);
-        d.cfg = 4 * (F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3) + (S == 1 ? 0 : S == 2 ? 1 : S == 4 ? 2 : 3);
+        const bool tj = M * d.TQ >= kDmWaves * 64;          // whole tiles per thread, as the one-linear launcher
+        d.cfg = 16 * tj + 4 * (F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3) + (S == 1 ? 0 : S == 2 ? 1 : S == 4 ? 2 : 3);
         cost[n] = int64_t(F) * d.TQ;
         order[n] = n;
         ++n;

@@ -187,8 +187,8 @@ typedef struct {
  * item.alpha, alpha_dtype, item.y, y_dtype, ...). All items run in one
  * launch (each item split into column groups of its own, one per block) for a
  * single token (M = 1) with every K <= 16384, and for 2 <= M <= 16 tokens
- * when every item's tokens fit in LDS and M * ceil(K / 128) < 512; otherwise
- * they run one after another in the order given. Sums are accumulated in fp32 in a fixed order,
+ * when every item's tokens fit in LDS (about 140 KB for M (K + 136) 16-bit
+ * values); otherwise they run one after another in the order given. Sums are accumulated in fp32 in a fixed order,
  * so results are the same from run to run; the one-launch form may group a
  * linear's K range differently from fbi_linear_w1a16 (a different rounding
  * order of the fp32 sum, not bit-identical to it).

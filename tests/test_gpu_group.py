@@ -76,10 +76,9 @@ def test_group_integer_activations_bit_exact(bgb_gpu, orc, x_kind):
 
 @pytest.mark.parametrize("M", [2, 4, 16, 40, 70])
 def test_group_several_tokens_parity(bgb_gpu, orc, M):
-    """More than one token: one launch for 2..16 tokens staged in pieces (M = 2,
-    4), otherwise the items one after another through the single-linear
-    dispatch (M = 16 with K = 11008 stages whole tiles; 40, 70), sharing the
-    largest item's workspace."""
+    """More than one token: one launch for 2..16 tokens (pieces or whole tiles
+    staged per item), otherwise the items one after another through the
+    single-linear dispatch (40, 70), sharing the largest item's workspace."""
     shapes = [(1024, 300), (11008, 200), (96, 65), (2048, 520)]
     say(f"group M={M} shapes={shapes}")
     items = _items(bgb_gpu, shapes, M, "bf16", "f32", 700 + M)
@@ -138,9 +137,10 @@ def test_group_single_token_beyond_fused_size(bgb_gpu, orc):
 @pytest.mark.parametrize("M", [2, 3, 8])
 def test_group_few_tokens_every_shape(bgb_gpu, orc, M):
     """A few tokens over shapes that take (fragments per block, steps per wave)
-    = (8, 8), (4, 4), (4, 1), (2, 4), (2, 2), (1, 4), (1, 1), with ragged N:
-    one launch for M = 2 and 3; at M = 8 the 12288- and 8192-row items stage
-    whole tiles, so the group runs item by item."""
+    = (8, 8), (4, 4), (4, 1), (2, 4), (2, 2), (1, 4), (1, 1), with ragged N,
+    in one launch for M = 2 and 3 (the 12288-row item staging whole tiles at
+    M = 3); at M = 8 that item's tokens do not fit in LDS, so the group runs
+    item by item."""
     shapes = [(4096, 22016), (4096, 12288), (1024, 8200), (8192, 5000), (4096, 5000), (12288, 100), (96, 65),
               (2048, 300)]
     say(f"group M={M} few-token shapes={shapes}")
