@@ -172,33 +172,38 @@ dalpha_sum_kernel(const double* __restrict__ part, int64_t chunks, int64_t N, fl
 }
 
 // ------------------------------------------- dW = alpha * (x^T dY) --------
-// Dense 16-bit product over the tokens. A block of 4 waves computes a
-// 128 (i) x 128 (j) tile of dW, wave w the 64 x 64 quarter (w & 1, w >> 1),
-// as 4 x 4 MFMA fragments with A = dY^T (rows j) and B = x (columns i), so a
-// lane's 4 outputs are 4 consecutive j of one i (one 16-byte store). Each
+// Dense 16-bit product over the tokens. A block computes a T x T tile of dW
+// (T = 256: 8 waves, each 64 j x 128 i as 4 x 8 MFMA fragments) with A =
+// dY^T (rows j) and B = x (columns i), so a lane's 4 outputs are 4
+// consecutive j of one i (one 16-byte store). The tile size sets how often x
+// and dY are re-read (by N / T and K / T blocks). Each
 // chunk of 64 tokens is staged in LDS transposed (row = feature, the chunk's
-// tokens contiguous), so that an operand is one 16-byte read: threads 0..127
-// load 8 tokens x 8 features of x, threads 128..255 the same of dY (16-byte
-// loads, 16 threads per 256-byte row piece), transpose the 8 x 8 block in
+// tokens contiguous), so that an operand is one 16-byte read: the first T
+// threads load 8 tokens x 8 features of x, the other T the same of dY
+// (16-byte loads, T / 8 threads per row piece), transpose the 8 x 8 block in
 // registers (one v_perm per output dword) and store 8 rows of 16 bytes. Two
 // LDS buffers: the next chunk is stored while the current one is multiplied
 // and the one after it is loaded. Tokens past M and features past K or N
 // read as zeros.
-constexpr int kDwTile = 128, kDwChunk = 64, kDwRow = kDwChunk + 8;   // LDS row: 64 tokens + 16 bytes
+constexpr int kDwChunk = 64, kDwRow = kDwChunk + 8;   // LDS row: 64 tokens + 16 bytes
 
-template <bool kF16>
-__global__ void __launch_bounds__(256)
+// T: the square output tile (128 or 256), 2 T threads (T / 32 waves); wave w
+// takes 64 j x 64 BI i (BI = T / 128): 4 x 4 BI MFMA fragments.
+template <bool kF16, int T>
+__global__ void __launch_bounds__(2 * T)
 dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64_t M, int64_t K, int64_t N,
           const void* __restrict__ alpha, int alpha_f16, float* __restrict__ dw) {
-    __shared__ __attribute__((aligned(16))) uint16_t xt[2][kDwTile * kDwRow];
-    __shared__ __attribute__((aligned(16))) uint16_t gt[2][kDwTile * kDwRow];
+    constexpr int BI = T / 128;
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2][T * kDwRow];
+    __shared__ __attribute__((aligned(16))) uint16_t gt[2][T * kDwRow];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
-    const int64_t i0 = int64_t(blockIdx.x) * kDwTile, j0 = int64_t(blockIdx.y) * kDwTile;
-    const int wi = (wave & 1) * 64, wj = (wave >> 1) * 64;
+    const int64_t i0 = int64_t(blockIdx.x) * T, j0 = int64_t(blockIdx.y) * T;
+    // waves: T / 64 columns of 64 j, 2 rows of 64 BI i
+    const int wj = (wave % (T / 64)) * 64, wi = (wave / (T / 64)) * 64 * BI;
 
-    // loader: half h = tid >> 7 (0: x, 1: dY), token rows 8 mb .. 8 mb + 7 of
-    // the chunk, features 8 fb .. 8 fb + 7 of the tile
-    const int h = tid >> 7, mb = (tid & 127) >> 4, fb = tid & 15;
+    // loader: half h (0: x, 1: dY), token rows 8 mb .. 8 mb + 7 of the chunk,
+    // features 8 fb .. 8 fb + 7 of the tile (T / 8 threads per token row)
+    const int h = tid / T, mb = (tid % T) / (T / 8), fb = tid % (T / 8);
     const uint16_t* src = h ? dy : x;
     const int64_t ld = h ? N : K;
     const int64_t f0 = (h ? j0 : i0) + 8 * fb;          // K, N multiples of 32: 8-feature pieces are whole
@@ -227,11 +232,11 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
         }
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][4 * BI];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 4 * BI; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // two LDS buffers: chunk c + 1 is stored into one while chunk c is
     // multiplied from the other, and chunk c + 2 is loaded meanwhile; one
@@ -248,16 +253,17 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
         const uint16_t* const xb = xt[buf];
 #pragma unroll
         for (int ks = 0; ks < kDwChunk / 32; ++ks) {
-            u32x4_t av[4], bv[4];
+            u32x4_t av[4], bv[4 * BI];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
+            for (int f = 0; f < 4; ++f)
                 av[f] = *reinterpret_cast<const u32x4_t*>(gb + (wj + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
+#pragma unroll
+            for (int f = 0; f < 4 * BI; ++f)
                 bv[f] = *reinterpret_cast<const u32x4_t*>(xb + (wi + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
-            }
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
+                for (int b = 0; b < 4 * BI; ++b) {
                     if constexpr (kF16)
                         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av[a]),
                                                                            __builtin_bit_cast(f16x8_t, bv[b]),
@@ -281,7 +287,7 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
             al[e] = alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[jb + e])
                               : static_cast<const float*>(alpha)[jb + e];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 4 * BI; ++b) {
             const int64_t i = i0 + wi + 16 * b + r;
             if (i >= K) continue;
             *reinterpret_cast<f32x4_t*>(dw + i * N + jb) =
@@ -300,13 +306,12 @@ hipError_t launch_fbi_backward_parts(const void* dy, int dy_f16, const void* x, 
     }
     if (ones) fill_ones_kernel<<<unsigned((nones + 255) / 256), 256, 0, s>>>(ones, nones);
     if (dw) {
-        const dim3 grid(unsigned((K + kDwTile - 1) / kDwTile), unsigned((N + kDwTile - 1) / kDwTile));
-        if (dy_f16)
-            dw_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), M,
-                                                 K, N, alpha, alpha_f16, dw);
-        else
-            dw_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), M,
-                                                  K, N, alpha, alpha_f16, dw);
+        constexpr int T = 256;                   // 8 waves, one block per CU (231 VGPRs; 128: 935 us, 256: 710 us)
+        const dim3 grid(unsigned((K + T - 1) / T), unsigned((N + T - 1) / T));
+        const uint16_t* xx = static_cast<const uint16_t*>(x);
+        const uint16_t* gg = static_cast<const uint16_t*>(dy);
+        if (dy_f16) dw_kernel<true, T><<<grid, 2 * T, 0, s>>>(xx, gg, M, K, N, alpha, alpha_f16, dw);
+        else dw_kernel<false, T><<<grid, 2 * T, 0, s>>>(xx, gg, M, K, N, alpha, alpha_f16, dw);
     }
     return hipGetLastError();
 }
