@@ -115,3 +115,27 @@ def test_backward_deterministic(bgb_gpu):
     for r in runs[1:]:
         for a, b in zip(runs[0], r):
             assert torch.equal(a, b)
+
+
+def test_backward_prefill_size_sampled(bgb_gpu, orc):
+    """The benchmark's backward shape (4096 tokens, 4096 x 11008, the GEMM paths
+    of dX and z, the 256-tile dW) against the oracle on samples: dX on 8 rows
+    (tile edges and seeded rows), dalpha and dW on 24 columns (each computed by
+    the oracle from those columns alone)."""
+    M, K, N = 4096, 4096, 11008
+    say(f"fbi backward sampled M={M} K={K} N={N}")
+    W, xb, gb, P, PT, alpha = _case(bgb_gpu, 77, M, K, N)
+    dx, da, dw = bgb_gpu.fbi_linear_w1a16_backward(dev_bits16(gb, torch.bfloat16), dev_bits16(xb, torch.bfloat16),
+                                                   P, PT, alpha)
+    torch.cuda.synchronize()
+    a_host = alpha.detach().float().cpu().numpy().astype(np.float32)
+    rng = syn.rng_for(77, 9)
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, M - 1], rng.choice(M, 3, replace=False)]))
+    rdx, _, _ = orc.fbi_backward(xb[rows], gb[rows], W, a_host)
+    check_w1a16(to_bits(dx)[rows], rdx, "f32", "dX sampled rows")
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.choice(N, 20, replace=False)]))
+    _, rda, rdw = orc.fbi_backward(xb, np.ascontiguousarray(gb[:, cols]), np.ascontiguousarray(W[:, cols]),
+                                   a_host[cols])
+    _normwise(to_bits(da)[cols], rda, "dalpha sampled columns")
+    got = dw[:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+    check_w1a16(got, rdw, "f32", "dW sampled columns")
