@@ -155,6 +155,54 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _need(t, name: str, dtypes=None, shape=None, nbytes: int = 0):
+    """Reject what the kernels cannot take before any pointer reaches the C ABI:
+    a wrong dtype, shape or size, or a non-contiguous view. Raises ValueError.
+    Where the tensors live is checked afterwards, for all of a call's tensors
+    together (_on_device)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {', '.join(str(d) for d in dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes; at least {nbytes} are needed")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _on_device(device, **tensors):
+    """Every tensor handed to the kernels must be a device tensor on the call's
+    device (a host pointer would fault the GPU). None entries are skipped."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) device tensor, got device {t.device}")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}; the call runs on {device}")
+
+
+def _f16s():
+    torch = _torch()
+    return (torch.bfloat16, torch.float16)
+
+
+def _scales():
+    torch = _torch()
+    return (torch.float32, torch.float16)
+
+
+def _ws_ok(ws, device):
+    """A caller's workspace: a contiguous device buffer (its size is checked by the library)."""
+    if ws is not None:
+        _need(ws, "ws")
+        _on_device(device, ws=ws)
+
+
 def _stream(stream) -> Optional[int]:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -170,6 +218,7 @@ def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
 
 
 def _workspace(op, M, K, N, ws, device):
+    _ws_ok(ws, device)
     need = workspace_bytes(op, M, K, N)
     if ws is None:
         torch = _torch()
@@ -183,17 +232,26 @@ def binarize_pack(W, mode: int = MODE_FBI, alpha_dtype=None, *, P=None, alpha=No
     and ternary (b1.58; beta = mean |W|, P holds the +1 plane then the -1 plane).
     P is an int32 tensor holding the uint32 words of the packed format."""
     torch = _torch()
+    if getattr(W, "dim", lambda: 0)() != 2:
+        raise ValueError("W must be a 2-D float32 tensor [K][N]")
     K, N = W.shape
+    _need(W, "W", (torch.float32,))
     dev = W.device
+    planes = 2 if mode == MODE_TERNARY else 1
     if P is None:
-        planes = 2 if mode == MODE_TERNARY else 1
         P = torch.empty(max(planes * packed_bytes(K, N) // 4, 4), dtype=torch.int32, device=dev)
+    _need(P, "P", nbytes=planes * packed_bytes(K, N))
+    for t, nm in ((beta, "beta"), (centre, "centre")):
+        if t is not None:
+            _need(t, nm, (torch.float32,), nbytes=4)
     op = OP_PACK_FBI if mode == MODE_FBI else OP_PACK_BITNET
     ws = _workspace(op, 0, K, N, ws, dev)
     if mode == MODE_FBI:
         adt = torch.float32 if alpha_dtype is None else alpha_dtype
         if alpha is None:
             alpha = torch.empty(max(N, 8), dtype=adt, device=dev)[:N]
+        _need(alpha, "alpha", _scales(), nbytes=N * alpha.element_size())
+        _on_device(dev, W=W, P=P, alpha=alpha, ws=ws)
         _check(load().binarize_pack(_ptr(W), K, N, mode, _ptr(P), _ptr(alpha), _dt(alpha), None, None,
                                     _ptr(ws), ws.numel(), _stream(stream)))
         return P, alpha
@@ -201,6 +259,7 @@ def binarize_pack(W, mode: int = MODE_FBI, alpha_dtype=None, *, P=None, alpha=No
         beta = torch.empty(4, dtype=torch.float32, device=dev)
     if centre is None:
         centre = torch.empty(4, dtype=torch.float32, device=dev)
+    _on_device(dev, W=W, P=P, beta=beta, centre=centre, ws=ws)
     _check(load().binarize_pack(_ptr(W), K, N, mode, _ptr(P), None, BGB_F32, _ptr(beta), _ptr(centre),
                                 _ptr(ws), ws.numel(), _stream(stream)))
     return P, beta[:1], centre[:1]
@@ -225,17 +284,34 @@ def fbi_linear_w1a16_group(linears, y_dtype=None, *, ys=None, ws=None, stream=No
     torch = _torch()
     if not linears:
         return []
-    M = linears[0][0].shape[0]
-    dev = linears[0][0].device
+    x0 = linears[0][0]
+    _need(x0, "x of item 0", _f16s())
+    if x0.dim() != 2:
+        raise ValueError("x of item 0 must be 2-D [M][K]")
+    M = x0.shape[0]
+    dev = x0.device
     if ys is None:
         ydt = torch.float32 if y_dtype is None else y_dtype
         ys = [torch.empty((M, N), dtype=ydt, device=dev) for (_, _, _, N) in linears]
+    if len(ys) != len(linears):
+        raise ValueError(f"{len(ys)} outputs for {len(linears)} linears")
+    a0, y0 = linears[0][2], ys[0]
+    for i, ((x, P, a, N), y) in enumerate(zip(linears, ys)):
+        if x.dim() != 2 or x.shape[0] != M:
+            raise ValueError(f"x of item {i} has shape {tuple(x.shape)}; every item needs [{M}][K]")
+        K = x.shape[1]
+        _need(x, f"x of item {i}", (x0.dtype,))
+        _need(P, f"P of item {i}", nbytes=packed_bytes(K, N))
+        _need(a, f"alpha of item {i}", (a0.dtype,) if i else _scales(), nbytes=N * a0.element_size())
+        _need(y, f"y of item {i}", (y0.dtype,) if i else (torch.float32,) + _f16s(), shape=(M, N))
     entries = [(x, P, a, y) for (x, P, a, _), y in zip(linears, ys)]
     arr = _items(entries)
+    _ws_ok(ws, dev)
     need = int(load().bgb_group_workspace_bytes(arr, len(entries), M))
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    x0, a0, y0 = linears[0][0], linears[0][2], ys[0]
+    for i, ((x, P, a, _), y) in enumerate(zip(linears, ys)):
+        _on_device(dev, **{f"x of item {i}": x, f"P of item {i}": P, f"alpha of item {i}": a, f"y of item {i}": y})
     _check(load().fbi_linear_w1a16_group(arr, len(entries), M, _dt(x0), _dt(a0), _dt(y0), _ptr(ws), ws.numel(),
                                          _stream(stream)))
     return ys
@@ -244,10 +320,18 @@ def fbi_linear_w1a16_group(linears, y_dtype=None, *, ys=None, ws=None, stream=No
 def fbi_linear_w1a16(x, P, alpha, N: int, y_dtype=None, *, y=None, ws=None, stream=None):
     """x: bf16/f16 [M][K]; P: packed signs; alpha: [N] f32/f16. Returns y [M][N]."""
     torch = _torch()
+    _need(x, "x", _f16s())
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M][K]")
     M, K = x.shape
+    dev = x.device
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32 if y_dtype is None else y_dtype, device=x.device)
-    ws = _workspace(OP_FBI_LINEAR, M, K, N, ws, x.device)
+        y = torch.empty((M, N), dtype=torch.float32 if y_dtype is None else y_dtype, device=dev)
+    _need(P, "P", nbytes=packed_bytes(K, N))
+    _need(alpha, "alpha", _scales(), nbytes=N * alpha.element_size())
+    _need(y, "y", (torch.float32,) + _f16s(), shape=(M, N))
+    ws = _workspace(OP_FBI_LINEAR, M, K, N, ws, dev)
+    _on_device(dev, x=x, P=P, alpha=alpha, y=y, ws=ws)
     _check(load().fbi_linear_w1a16(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(alpha), _dt(alpha), _ptr(y), _dt(y),
                                    _ptr(ws), ws.numel(), _stream(stream)))
     return y
@@ -256,8 +340,11 @@ def fbi_linear_w1a16(x, P, alpha, N: int, y_dtype=None, *, y=None, ws=None, stre
 def fbi_pack_transposed(P, K: int, N: int, *, PT=None, stream=None):
     """Packed signs of [S^T; S^T] (2N x K) for the backward product; N % 32 == 0."""
     torch = _torch()
+    _need(P, "P", nbytes=packed_bytes(K, N))
     if PT is None:
         PT = torch.empty(max(packed_bytes(2 * N, K) // 4, 4), dtype=torch.int32, device=P.device)
+    _need(PT, "PT", nbytes=packed_bytes(2 * N, K))
+    _on_device(P.device, P=P, PT=PT)
     _check(load().fbi_pack_transposed(_ptr(P), K, N, _ptr(PT), _stream(stream)))
     return PT
 
@@ -268,14 +355,23 @@ def fbi_linear_w1a16_backward(dy, x, P, PT, alpha, *, want=("dx", "dalpha", "dw"
     the same); P / PT: packed signs and their transposed copy. Returns (dx, dalpha, dw), None for
     what is not in `want`."""
     torch = _torch()
+    _need(dy, "dy", _f16s())
+    if dy.dim() != 2 or x.dim() != 2 or x.shape[0] != dy.shape[0]:
+        raise ValueError(f"dy {tuple(dy.shape)} and x {tuple(x.shape)} must be [M][N] and [M][K]")
     M, N = dy.shape
     K = x.shape[1]
     dev = dy.device
+    _need(x, "x", (dy.dtype,))
+    _need(P, "P", nbytes=packed_bytes(K, N))
+    if "dx" in want:
+        _need(PT, "PT", nbytes=packed_bytes(2 * N, K))
+    _need(alpha, "alpha", _scales(), nbytes=N * alpha.element_size())
     dx = (torch.empty((M, K), dtype=torch.float32 if dx_dtype is None else dx_dtype, device=dev)
           if "dx" in want else None)
     da = torch.empty(max(N, 4), dtype=torch.float32, device=dev)[:N] if "dalpha" in want else None
     dw = torch.empty((K, N), dtype=torch.float32, device=dev) if "dw" in want else None
     ws = _workspace(OP_FBI_BACKWARD, M, K, N, ws, dev)
+    _on_device(dev, dy=dy, x=x, P=P, PT=PT if "dx" in want else None, alpha=alpha, dx=dx, dalpha=da, dw=dw, ws=ws)
     _check(load().fbi_linear_w1a16_backward(_ptr(dy), _ptr(x), _dt(dy), M, K, N, _ptr(P), _ptr(PT), _ptr(alpha),
                                             _dt(alpha), _ptr(dx), _dt(dx) if dx is not None else BGB_F32,
                                             _ptr(da), _ptr(dw), _ptr(ws), ws.numel(), _stream(stream)))
@@ -287,10 +383,16 @@ def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=No
     """x: f32/bf16 [M][K]; P: packed signs of W - c; beta: device scalar.
     Returns y, or (y, extras) with the requested taps (q, gamma, acc)."""
     torch = _torch()
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M][K]")
     M, K = x.shape
     dev = x.device
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(P, "P", nbytes=(2 if _ternary else 1) * packed_bytes(K, N))
+    _need(beta, "beta", (torch.float32,), nbytes=4)
+    _need(y, "y", (torch.float32,), shape=(M, N))
     qp = qp or QuantParams()
     ng = M if qp.gamma_scope == GAMMA_TOKEN else 1    # gamma: one per token, or one
     q = torch.empty((M, K), dtype=torch.int8, device=dev) if want_q else None
@@ -299,6 +401,7 @@ def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=No
     ws = _workspace(OP_BITLINEAR158 if _ternary else OP_BITLINEAR, M, K, N, ws, dev)
     cqp = qp.c()
     fn = load().bitlinear158_w1a8 if _ternary else load().bitlinear_w1a8
+    _on_device(dev, x=x, P=P, beta=beta, y=y, ws=ws)
     _check(fn(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y),
                                  _ptr(q), _ptr(g), _ptr(acc), _ptr(ws), ws.numel(), _stream(stream)))
     if not (want_q or want_gamma or want_acc):
@@ -317,12 +420,17 @@ def bitlinear_quantize(x, qp: Optional[QuantParams] = None, *, ws, N_max: int = 
                        stream=None):
     """Prologue only: leaves the codes in `ws` for bitlinear_matmul. Returns the requested taps."""
     torch = _torch()
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M][K]")
     M, K = x.shape
+    _need(ws, "ws")
     qp = qp or QuantParams()
     ng = M if qp.gamma_scope == GAMMA_TOKEN else 1
     q = torch.empty((M, K), dtype=torch.int8, device=x.device) if want_q else None
     g = torch.empty(max(ng, 4), dtype=torch.float32, device=x.device) if want_gamma else None
     cqp = qp.c()
+    _on_device(x.device, x=x, ws=ws)
     _check(load().bitlinear_quantize(_ptr(x), _dt(x), M, K, ctypes.byref(cqp), _ptr(q), _ptr(g), _ptr(ws),
                                      ws.numel(), _stream(stream)))
     return {"q": q, "gamma": None if g is None else g[:ng]}
@@ -332,12 +440,18 @@ def bitlinear_matmul(M: int, K: int, P, beta, N: int, qp: Optional[QuantParams] 
                      want_acc=False, stream=None, _ternary=False):
     """Product + epilogue from the codes a previous bitlinear_quantize left in `ws`."""
     torch = _torch()
+    _need(ws, "ws")
+    dev = ws.device
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=ws.device)
-    acc = torch.empty((M, N), dtype=torch.int32, device=ws.device) if want_acc else None
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(P, "P", nbytes=(2 if _ternary else 1) * packed_bytes(K, N))
+    _need(beta, "beta", (torch.float32,), nbytes=4)
+    _need(y, "y", (torch.float32,), shape=(M, N))
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
     qp = qp or QuantParams()
     cqp = qp.c()
     fn = load().bitlinear158_matmul if _ternary else load().bitlinear_matmul
+    _on_device(dev, P=P, beta=beta, y=y, ws=ws)
     _check(fn(M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y), _ptr(acc), _ptr(ws),
                                    ws.numel(), _stream(stream)))
     return (y, acc) if want_acc else y

@@ -234,6 +234,9 @@ int fbi_linear_w1a16_backward(const void* dy, const void* x, int dtype, int64_t 
     if (alpha_dtype != BGB_F32 && alpha_dtype != BGB_F16) return BGB_EUNSUPPORTED;
     if (dx && dx_dtype != BGB_F32 && dx_dtype != BGB_BF16 && dx_dtype != BGB_F16) return BGB_EUNSUPPORTED;
     if (N % 32 != 0 || 2 * N > bgb::kMaxK || M * 2 * N > kMaxElems) return BGB_EINVAL;
+    // dX runs the forward product over [S^T; S^T], a 2N x K operand: it must
+    // meet the forward's own shape limits too
+    if (dx && N > 0 && (rc = check_shape(M, 2 * N, K))) return rc;
     if (M == 0 || N == 0) return BGB_OK;          // empty: nothing is read or written
     if (!dy || !alpha || !aligned16(dy) || !aligned16(alpha)) return BGB_EINVAL;
     if (dx && (!PT || !aligned16(PT) || !aligned16(dx))) return BGB_EINVAL;

@@ -369,11 +369,14 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     //    u is first clamped to +-(Q_b - 1/2): beyond that both give +-(Q_b - 1),
     //    so the extreme element needs no exact check (u = 0 needs none either).
     //    A lane with a near-integer u (rare) redoes all its codes exactly.
+    //    For gamma below about Q_b / FLT_MAX (activations at subnormal scale)
+    //    Q_b rcp(gamma) overflows and u means nothing: every lane then takes
+    //    the exact division for all of its codes.
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
     const float ucl = qb - 0.5f;
     constexpr bool rn = kRne;
     int codes[NV][4];
-    bool slow = false;
+    bool slow = !(cq <= 0x1.fffffep127f);
     if constexpr (!rn) {                               // truncation (the default): int(u) needs no clamp
 #pragma unroll
         for (int i = 0; i < NV; ++i)

@@ -284,6 +284,9 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
     if (gamma_opt && token && lane == 0) gamma_opt[m] = gamma;
     const bool rn = rne != 0;
     const float cq = gamma != 0.0f ? qb * __builtin_amdgcn_rcpf(gamma) : 0.0f;
+    // gamma below about Q_b / FLT_MAX overflows Q_b rcp(gamma): no fast quotient
+    // is meaningful then, and every code comes from the exact division
+    const uint32_t all_slow = cq <= 0x1.fffffep127f ? 0u : 0xffffffffu;
     const int qmax = int(qb) - 1;
     const int64_t words = K / 32, pwords = Kp / 32;
     int sum = 0;
@@ -294,7 +297,7 @@ lnq_quant_kernel(const XT* __restrict__ x, int64_t M, int64_t K, int64_t Kp, flo
 #pragma unroll
             for (int c = 0; c < 32 / E; ++c) V::load(xr + 32 * t + c * E, h + c * E);
             int code[32];
-            uint32_t slow = 0;
+            uint32_t slow = all_slow;
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
                 h[j] = ln_apply(h[j], mu32, rs32);

@@ -231,7 +231,8 @@ int fbi_pack_transposed(const uint32_t* P, int64_t K, int64_t N, uint32_t* PT, v
  * (dW is the gradient of W_b = alpha * sign(W) passed to the latent W.)
  * dy: [M][N], x: [M][K], both of `dtype` (BF16 or F16). Any of dx, dalpha,
  * dw may be NULL (not computed); dx needs PT (fbi_pack_transposed), dalpha
- * needs x and P, dw needs x. N % 32 == 0.
+ * needs x and P, dw needs x. N % 32 == 0. When dx is requested, 2 N K < 2^31
+ * as well (dX runs the forward product over the 2N x K operand [S^T; S^T]).
  * Numerics: dX runs the forward product on g = fl32(alpha_j dY) carried as
  * two bf16 halves (g_hi + g_lo, about 16 significant bits), fp32
  * accumulation; dalpha is the forward at alpha = 1 (fp32 sums) times dY,

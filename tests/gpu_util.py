@@ -6,7 +6,11 @@ Comparison rules (tolerances from the stated targets):
   <= 2e-3 (fp32 accumulation of exact +-x products against the fp64 oracle);
   16-bit outputs additionally within one unit in the last place of y_ref;
 * W1A8 outputs: elementwise |y - y_ref| <= 1e-5 |y_ref| against the fp64
-  product acc * beta * gamma / Q_b (acc == 0 gives exactly 0).
+  product acc * beta * gamma / Q_b (acc == 0 gives exactly 0). Where the
+  epilogue's scale s = fl32(fl32(beta gamma) / Q_b) or y itself falls below
+  FLT_MIN (activations at subnormal scale), each fp32 rounding adds up to
+  2^-150 absolute instead of a relative error, so the bound gains
+  (|acc| + 1) 2^-149 when the caller passes acc (negligible for normal values).
 """
 import sys
 
@@ -79,10 +83,15 @@ def check_w1a16(y: np.ndarray, ref: np.ndarray, y_kind: str, tag: str = ""):
     return float(err.max()) if err.size else 0.0
 
 
-def check_w1a8(y: np.ndarray, ref: np.ndarray, tag: str = ""):
+def check_w1a8(y: np.ndarray, ref: np.ndarray, tag: str = "", acc=None):
     zero = ref == 0
     assert np.all(y[zero] == 0), f"{tag} nonzero output where acc == 0"
-    rel = np.abs(y[~zero] - ref[~zero]) / np.abs(ref[~zero])
+    err = np.abs(y[~zero] - ref[~zero])
+    if acc is not None:
+        floor = (np.abs(np.asarray(acc, np.float64)[~zero]) + 1.0) * 2.0 ** -149
+        assert np.all(err <= W1A8_REL_TOL * np.abs(ref[~zero]) + floor), f"{tag} beyond 1e-5 rel + subnormal floor"
+        err = np.maximum(err - floor, 0.0)
+    rel = err / np.abs(ref[~zero])
     assert rel.size == 0 or rel.max() <= W1A8_REL_TOL, f"{tag} rel err {rel.max():.3e}"
     return float(rel.max()) if rel.size else 0.0
 

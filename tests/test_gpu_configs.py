@@ -77,9 +77,9 @@ def test_w1a16_decode_7b_layer_config(bgb_gpu, orc, B):
         P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI, torch.float16)
         y = bgb_gpu.fbi_linear_w1a16(dev_bits16(xb, torch.bfloat16), P, alpha, N, torch.bfloat16)
         torch.cuda.synchronize()
-        a_host = alpha.float().cpu().numpy().astype(np.float32)
-        assert np.array_equal(host_bits16(alpha), orc.f32_to_f16(orc.fbi_alpha(W)))
-        check_w1a16(to_bits(y), orc.fbi_linear(xb, W, a_host), "bf16", f"7B {name} B={B}")
+        a16 = orc.f32_to_f16(orc.fbi_alpha(W))
+        assert np.array_equal(host_bits16(alpha), a16)
+        check_w1a16(to_bits(y), orc.fbi_linear(xb, W, orc.f16_to_f32(a16)), "bf16", f"7B {name} B={B}")
 
 
 def test_w1a16_prefill_config(bgb_gpu, orc):
@@ -91,8 +91,10 @@ def test_w1a16_prefill_config(bgb_gpu, orc):
     P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI)
     y = bgb_gpu.fbi_linear_w1a16(dev_bits16(xb, torch.bfloat16), P, alpha, N, torch.bfloat16)
     torch.cuda.synchronize()
+    a_ref = orc.fbi_alpha(W)
+    assert np.array_equal(host_f32(alpha), a_ref)
     rows = sample_rows(M, c["seed"])
-    ref = orc.fbi_linear(np.ascontiguousarray(xb[rows]), W, host_f32(alpha))
+    ref = orc.fbi_linear(np.ascontiguousarray(xb[rows]), W, a_ref)
     check_w1a16(to_bits(y)[rows], ref, "bf16", "prefill W1A16")
 
 
@@ -131,6 +133,8 @@ def test_1p3b_stack_config(bgb_gpu, orc, phase):
         P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI, torch.float16)
         y = bgb_gpu.fbi_linear_w1a16(dev_bits16(xb, torch.bfloat16), P, alpha, N, torch.bfloat16)
         torch.cuda.synchronize()
+        a16 = orc.f32_to_f16(orc.fbi_alpha(W))                     # the stored f16 scale
+        assert np.array_equal(host_bits16(alpha), a16)
         rows = np.arange(M) if M <= 64 else sample_rows(M, c["seed"], 8)
-        ref = orc.fbi_linear(np.ascontiguousarray(xb[rows]), W, alpha.float().cpu().numpy().astype(np.float32))
+        ref = orc.fbi_linear(np.ascontiguousarray(xb[rows]), W, orc.f16_to_f32(a16))
         check_w1a16(to_bits(y)[rows], ref, "bf16", f"1.3B {name} {phase}")

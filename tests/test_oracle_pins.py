@@ -584,3 +584,52 @@ def test_nonneg_quant_invariants(orc):
         else:
             m, i = np.unravel_index(np.argmin((x - x.mean(1, keepdims=True)) / x.std(1, keepdims=True)), x.shape)
             assert q[m, i] == 0
+
+
+# ------------------------------------- exact quotients and subnormal scale --
+
+def subnormal_rows(M: int, K: int, exponent: int) -> np.ndarray:
+    """Token m: x = 2^exponent at index (37 m) mod K, zeros elsewhere."""
+    x = np.zeros((M, K), np.float32)
+    for m in range(M):
+        x[m, (37 * m) % K] = np.float32(2.0 ** exponent)
+    return x
+
+
+def test_quant_golden_exact_quotients(orc):
+    """Rows whose quotients h Q_b / gamma are exact integers (truncation boundary)
+    or exact half-integers (rounding boundary), hand-derived in the golden file."""
+    g = read_golden("quant_closed_forms.txt")
+    gn = read_golden("quant_nonneg_closed_forms.txt")
+    for pat, keys in (("pattern_e", ("q_e", "rne_q_e")), ("pattern_f", ("q_f", "rne_q_f"))):
+        period = np.array([float(v) for v in g[pat]], np.float32)
+        x = np.tile(period, (3, 64 // period.size))
+        for rm, key in enumerate(keys):
+            for scope in (0, 1):
+                q, gamma, _, _ = orc.ln_absmax_quant(x, round_mode=rm, gamma_scope=scope)
+                expect = np.tile(np.array([int(v) for v in g[key]], np.int8), (3, 64 // period.size))
+                assert np.array_equal(q, expect), (pat, key, scope)
+    x = np.tile(np.array([float(v) for v in gn["pattern_e"]], np.float32), (2, 16))
+    for rm in (0, 1):
+        q, _, _ = orc.ln_nonneg_quant(x, round_mode=rm)
+        assert np.array_equal(q, np.tile(np.array([int(v) for v in gn["nn_q_e"]], np.int8), (2, 16)))
+
+
+def test_quant_golden_subnormal_scale(orc):
+    """gamma below Q_b / FLT_MAX: the codes are still those of eq. (4)."""
+    g = read_golden("quant_closed_forms.txt")
+    gn = read_golden("quant_nonneg_closed_forms.txt")
+    e, K = int(g["subnormal_exponent"][0]), int(g["subnormal_K"][0])
+    x = subnormal_rows(3, K, e)
+    assert x[0, 0] == np.float32(2.0 ** e) and x[0, 0] < np.finfo(np.float32).tiny   # a subnormal
+    qb_over_max = np.float32(128.0) / np.finfo(np.float32).max
+    for rm in (0, 1):
+        for scope in (0, 1):
+            q, gamma, _, _ = orc.ln_absmax_quant(x, round_mode=rm, gamma_scope=scope)
+            assert np.all(np.asarray(gamma) < qb_over_max)
+            hot = q[np.arange(3), (37 * np.arange(3)) % K]
+            assert np.all(hot == int(g["subnormal_q0"][0]))
+            assert np.count_nonzero(q) == 3 and int(g["subnormal_qrest"][0]) == 0
+            qn, gn_, eta = orc.ln_nonneg_quant(x, round_mode=rm, gamma_scope=scope)
+            assert np.all(qn[np.arange(3), (37 * np.arange(3)) % K] == int(gn["nn_subnormal_q0"][0]))
+            assert np.count_nonzero(qn) == 3 and int(gn["nn_subnormal_qrest"][0]) == 0
