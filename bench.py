@@ -51,8 +51,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate-mb", type=float, default=640.0, help="packed weight bytes in the rotation")
     ap.add_argument("--legs", default="all", help="comma list of extra legs, 'all' or 'none'")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="bound on the one-core CPU-oracle samples (split over the workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also run the ceiling microbenchmarks (part of --legs all)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes for the all-core CPU oracle timing (0: min(16, cores))")
     ap.add_argument("--calib-copy-mb", type=float, default=0.0,
                     help="only run a plain device copy of this many MB (HBM counter calibration) and exit")
     return ap.parse_args()
@@ -60,9 +65,24 @@ def parse():
 
 # ----------------------------------------------------------------- timing ----
 
-def graph_time(torch, body, steps, warmup):
+MALL_FLUSH_BYTES = 1 << 30          # read before a timed region: 4x the 256 MB Infinity Cache
+_flush_buf = None
+
+
+def flush_mall(torch):
+    """Stream 1 GiB through the memory-side cache (a read-only reduction), so
+    that nothing a timed region reads is left in the 256 MB MALL or the L2s."""
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    _flush_buf.sum()
+    torch.cuda.synchronize()
+
+
+def graph_time(torch, body, steps, warmup, flush=True):
     """Capture `steps` calls of body(i) into one HIP graph; replay once untimed
-    (warm-up, also `warmup` eager calls before capture) and once timed.
+    (warm-up, also `warmup` eager calls before capture), stream 1 GiB through
+    the MALL (flush=True), then replay once timed.
     Returns milliseconds for the timed replay."""
     for i in range(warmup):
         body(i)
@@ -73,6 +93,8 @@ def graph_time(torch, body, steps, warmup):
             body(i)
     g.replay()
     torch.cuda.synchronize()
+    if flush:
+        flush_mall(torch)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -106,11 +128,21 @@ def per_launch_ms(torch, launch, n, busy_mb=1024):  # pragma: no cover - diagnos
 
 # ---------------------------------------------------------- headline leg ----
 
+def headline_host_state(syn):
+    """The headline workload's host inputs (numpy only: no GPU is touched)."""
+    cfg = syn.CONFIGS["bitlinear_decode_4096x11008"]
+    K, N, M, seed = cfg["K"], cfg["N"], cfg["M"], cfg["seed"]
+    W = syn.normal_f32(seed, 0, (K, N), mean=cfg["w_mean"], std=cfg["w_std"])
+    x = syn.normal_f32(seed, 1, (M, K))
+    pbytes = 16 * ((K + 127) // 128) * N          # the packed format: one 16-byte tile per 128 rows per column
+    return dict(W=W, x=x, K=K, N=N, M=M, step_bytes=pbytes + M * K * 4 + M * N * 4)
+
+
 def headline(torch, bgb, syn, args):
     cfg = syn.CONFIGS["bitlinear_decode_4096x11008"]
     K, N, M, seed = cfg["K"], cfg["N"], cfg["M"], cfg["seed"]
-    W_host = syn.normal_f32(seed, 0, (K, N), mean=cfg["w_mean"], std=cfg["w_std"])
-    x_host = syn.normal_f32(seed, 1, (M, K))
+    host = headline_host_state(syn)
+    W_host, x_host = host["W"], host["x"]
     P0, beta, centre = bgb.binarize_pack(torch.from_numpy(W_host).cuda(), bgb.MODE_BITNET)
     pbytes = bgb.packed_bytes(K, N)
     R = max(2, math.ceil(args.rotate_mb * 1e6 / pbytes))
@@ -123,9 +155,13 @@ def headline(torch, bgb, syn, args):
         bgb.bitlinear_w1a8(x, Ps[i % R], beta, N, y=y, ws=ws)
 
     log(f"headline: BitLinear W1A8 decode M={M} K={K} N={N}, {R} weight copies ({R * pbytes / 1e6:.0f} MB)")
+    # the MALL is flushed between the warm and the timed replay, so each copy
+    # the timed replay reads comes from HBM at any --steps; a copy is read
+    # again only after the other R - 1 (643 MB) have been
     ms = graph_time(torch, step, args.steps, args.warmup)
     ms_step = ms / args.steps
     step_bytes = pbytes + M * K * 4 + M * N * 4          # packed signs + x (f32) + y (f32)
+    assert step_bytes == host["step_bytes"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"headline: {ms_step * 1e3:.2f} us/step, {value:.1f} GB/s")
 
@@ -146,7 +182,8 @@ def headline(torch, bgb, syn, args):
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref), "rotated copy disagrees"
 
-    state = dict(W=W_host, x=x_host, K=K, N=N, M=M, step_bytes=step_bytes)
+    state = dict(W=W_host, x=x_host, K=K, N=N, M=M, step_bytes=step_bytes,
+                 distinct_bytes=min(args.steps, R) * pbytes)
     del Ps
     return ms_step, value, roof, R, state
 
@@ -170,26 +207,159 @@ def traffic_bytes(kernel):
 
 # ------------------------------------------------------------ cpu baseline ----
 
-def cpu_baseline(state, seconds):
+def host_info():
+    """CPU model, logical CPUs and whether SMT is on (Linux /proc and /sys)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    smt = None
+    try:
+        smt = open("/sys/devices/system/cpu/smt/active").read().strip() == "1"
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "smt": smt}
+
+
+_JOBS = []          # per-worker closures, inherited by forked workers
+
+
+def _run_job(i):
+    t0 = time.perf_counter()
+    _JOBS[i]()
+    return time.perf_counter() - t0
+
+
+def _oracle_cases(state):
+    """The oracle on each workload, as (name, unit work, fn(cols) -> callable,
+    columns, work per full config, sample note). fn(cols) returns a closure
+    that computes the sample for output columns `cols` only; run over all
+    columns it is the whole sample."""
     import numpy as np
     import oracle
-    W, x = state["W"], state["x"]
-    c, beta = oracle.bitnet_scalars(W)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        q, g, _, _ = oracle.ln_absmax_quant(x)
-        acc = oracle.bitlinear_acc(q, W, c)
-        oracle.bitlinear_out(acc, beta, g)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = (time.perf_counter() - t0) / n
+    import bgb_synth as syn
+    cases = []
+    # 768 x 768 FBI-linear, 8 bf16 tokens (whole workload)
+    c = syn.CONFIGS["fbi_768"]
+    W1 = syn.normal_f32(c["seed"], 0, (c["K"], c["N"]), std=c["w_std"])
+    x1 = syn.f32_to_bf16_bits(syn.normal_f32(c["seed"], 1, (c["M"], c["K"])))
+    a1 = oracle.fbi_alpha(W1)
+    cases.append(("fbi_w1a16_768x768_m8", lambda cols: (lambda: oracle.fbi_linear(
+        x1, np.ascontiguousarray(W1[:, cols]), a1[cols])), c["N"], 1.0, "the whole workload"))
+    # BitLinear decode 4096 x 11008 (whole workload: LN + quant, product, output)
+    W2, xf2 = state["W"], state["x"]
+    c2, b2 = oracle.bitnet_scalars(W2)
+
+    def bl(cols):
+        Wc = np.ascontiguousarray(W2[:, cols])
+
+        def f():
+            q, g, _, _ = oracle.ln_absmax_quant(xf2)
+            acc = oracle.bitlinear_acc(q, Wc, c2)
+            oracle.bitlinear_out(acc, b2, g)
+        return f
+    cases.append(("bitlinear_w1a8_decode_4096x11008", bl, W2.shape[1], 1.0, "the whole workload"))
+    # 7B layer at one token: the q (4096 x 4096) and gate (4096 x 11008) shapes;
+    # a layer is 4 of the first (q, k, v, o) and 3 of the second's size (gate, up, down)
+    Wq = syn.normal_f32(2, 0, (4096, 4096), std=0.02)
+    Wg = syn.normal_f32(2, 4, (4096, 11008), std=0.02)
+    xq = syn.f32_to_bf16_bits(syn.normal_f32(2, 100, (1, 4096)))
+    aq, ag = oracle.fbi_alpha(Wq), oracle.fbi_alpha(Wg)
+
+    def layer7b(cols):
+        cq = cols[cols < 4096]
+        Wqc, Wgc = np.ascontiguousarray(Wq[:, cq]), np.ascontiguousarray(Wg[:, cols])
+
+        def f():
+            oracle.fbi_linear(xq, Wqc, aq[cq])
+            oracle.fbi_linear(xq, Wgc, ag[cols])
+        return f
+    layer_adds = 4 * 4096 * 4096 + 3 * 4096 * 11008
+    cases.append(("w1a16_decode_7b_layer_b1", layer7b, 11008, layer_adds / (4096 * 4096 + 4096 * 11008),
+                  "one q-shaped and one gate-shaped linear at one token, scaled to the layer's 7 linears"))
+    # 4096 x 4096 x 11008 prefill, W1A16: 8 of the 4096 token rows, scaled by 512
+    xp = syn.f32_to_bf16_bits(syn.normal_f32(3, 1, (8, 4096)))
+    Wp = syn.normal_f32(3, 0, (4096, 11008), std=0.02)
+    ap_ = oracle.fbi_alpha(Wp)
+    cases.append(("w1a16_prefill_4096x4096x11008", lambda cols: (lambda: oracle.fbi_linear(
+        xp, np.ascontiguousarray(Wp[:, cols]), ap_[cols])), 11008, 4096 / 8,
+        "8 of the 4096 token rows, scaled by 512"))
+    # 1.3B stack decode at batch 64: one layer's q and gate shapes for 8 tokens, scaled to 7 linears x 24 layers x 64 tokens
+    Wq5 = syn.normal_f32(4, 0, (2048, 2048), std=0.02)
+    Wg5 = syn.normal_f32(4, 4, (2048, 5632), std=0.02)
+    x5 = syn.f32_to_bf16_bits(syn.normal_f32(4, 100, (8, 2048)))
+    aq5, ag5 = oracle.fbi_alpha(Wq5), oracle.fbi_alpha(Wg5)
+
+    def stack(cols):
+        cq = cols[cols < 2048]
+        Wqc, Wgc = np.ascontiguousarray(Wq5[:, cq]), np.ascontiguousarray(Wg5[:, cols])
+
+        def f():
+            oracle.fbi_linear(x5, Wqc, aq5[cq])
+            oracle.fbi_linear(x5, Wgc, ag5[cols])
+        return f
+    stack_adds = 24 * 64 * (4 * 2048 * 2048 + 3 * 2048 * 5632)
+    cases.append(("w1a16_1p3b_stack_decode_b64", stack, 5632, stack_adds / (8 * (2048 * 2048 + 2048 * 5632)),
+                  "8 tokens through one q-shaped and one gate-shaped linear, scaled to 7 linears x 24 layers x 64 tokens"))
+    return cases
+
+
+def cpu_baseline(state, seconds, workers):
+    """The oracle as it stands (plain single-threaded C), timed on this host:
+    every workload on one core, and on `workers` cores by running the same
+    oracle in forked processes on disjoint slices of the output columns (each
+    output is computed exactly as in the one-core run). The headline's value
+    is the one-core BitLinear decode rate."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import numpy as np
+    cases = _oracle_cases(state)
+    info = host_info()
+    budget = seconds / len(cases)
+    per = {}
+    head = None
+    for name, fn, ncols, scale, note in cases:
+        allc = np.arange(ncols)
+        f = fn(allc)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            f()
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        t1 = (time.perf_counter() - t0) / n
+        rec = {"ms_1core": round(t1 * scale * 1e3, 3), "sample": note, "sample_ms_1core": round(t1 * 1e3, 3),
+               "repeats": n}
+        if workers > 1:
+            global _JOBS
+            _JOBS = [fn(sl) for sl in np.array_split(allc, workers)]
+            with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("fork")) as ex:
+                list(ex.map(_run_job, range(workers)))              # warm the workers
+                reps = max(1, n)
+                tw = []
+                for _ in range(reps):
+                    w0 = time.perf_counter()
+                    list(ex.map(_run_job, range(workers)))
+                    tw.append(time.perf_counter() - w0)
+            _JOBS = []
+            tmin = min(tw)
+            rec.update({"ms_all_cores": round(tmin * scale * 1e3, 3), "cores": workers,
+                        "speedup": round(t1 / tmin, 2)})
+        per[name] = rec
+        log(f"cpu oracle {name}: {rec['ms_1core']:.1f} ms on 1 core"
+            + (f", {rec['ms_all_cores']:.1f} ms on {workers}" if workers > 1 else ""))
+        if name == "bitlinear_w1a8_decode_4096x11008":
+            head = (t1, n)
+    dt, n = head
     value = state["step_bytes"] / dt / 1e9
-    log(f"cpu oracle: {dt * 1e3:.1f} ms/step over {n} steps")
     return {"value": round(value, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} full decode steps (M=1, K=4096, N=11008: LN+quant, integer product, output) "
-                      f"in {n * dt:.1f} s, plain single-thread C oracle", "ms_per_step": round(dt * 1e3, 2)}
+                      f"in {n * dt:.1f} s, plain single-thread C oracle", "ms_per_step": round(dt * 1e3, 2),
+            **info, "all_core_workers": workers, "per_config": per}
 
 
 # ------------------------------------------------------------------ legs ----
@@ -218,6 +388,62 @@ def leg_pack(torch, bgb, syn):
                      "bytes": nbytes, "bound": "hbm"}
         log(f"{name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
     return out
+
+
+def leg_fbi_768(torch, bgb, syn):
+    """The 768 x 768 FBI-linear (130M-class hidden size): 8 bf16 tokens, fp32
+    output, fp32 alpha. 113,664 algorithmic bytes per call: bound by launch
+    latency, so it reports microseconds per call (back-to-back in a graph,
+    and one call at a time between HIP events)."""
+    c = syn.CONFIGS["fbi_768"]
+    K, N, M = c["K"], c["N"], c["M"]
+    W = torch.from_numpy(syn.normal_f32(c["seed"], 0, (K, N), std=c["w_std"])).cuda()
+    xb = syn.f32_to_bf16_bits(syn.normal_f32(c["seed"], 1, (M, K)))
+    import numpy as np
+    x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+    P, alpha = bgb.binarize_pack(W, bgb.MODE_FBI)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, N), 256), dtype=torch.uint8, device="cuda")
+
+    def body(i):
+        bgb.fbi_linear_w1a16(x, P, alpha, N, y=y, ws=ws)
+
+    n = 1000
+    ms = graph_time(torch, body, n, 20) / n
+    avg, med = per_launch_ms(torch, body, 200)
+    nbytes = bgb.packed_bytes(K, N) + 4 * N + 2 * M * K + 4 * M * N
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"fbi 768x768 M=8: {ms * 1e3:.2f} us/call back-to-back, {med * 1e3:.2f} us one call at a time")
+    return {"fbi_w1a16_768x768_m8": {"us_per_call": round(ms * 1e3, 3), "us_single_call_median": round(med * 1e3, 3),
+                                     "us_single_call_mean": round(avg * 1e3, 3), "GB/s": round(gbs, 1),
+                                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 5), "bytes": nbytes,
+                                     "bound": "launch latency (113,664 B per call)"}}
+
+
+def cold_step_ms(torch, body, n):
+    """Milliseconds of one step (body(0), captured once as a HIP graph) with
+    the MALL flushed before each of n timed replays: the median and the
+    spread over the replays."""
+    body(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body(0)
+    g.replay()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(n):
+        flush_mall(torch)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1))
+    del g
+    t.sort()
+    return t[len(t) // 2], t[0], t[-1]
 
 
 def build_layer(torch, bgb, syn, seed, shapes, layer, alpha_dtype):
@@ -441,15 +667,19 @@ def leg_stack_1p3b(torch, bgb, syn):
                     bgb.fbi_linear_w1a16(xs[K], Ps[li], As[li], N, y=ys[N], ws=ws)
 
         n = 10 if M <= 64 else 3
-        # cold: flush the MALL between steps is not possible inside one graph;
-        # this is the warm number (154 MB of signs stay resident across steps)
-        ms = graph_time(torch, body, n, 2) / n
+        # warm: the 154 MB of signs stay in the MALL from step to step (no
+        # flush); cold: the MALL is flushed before each timed step
+        ms = graph_time(torch, body, n, 2, flush=False) / n
+        cold, cmin, cmax = cold_step_ms(torch, body, 5 if M <= 64 else 3)
         flops = 2 * M * sum(K * N for _, K, N in shapes) * L
         tf = flops / (ms * 1e-3) / 1e12
         out[f"w1a16_1p3b_stack_{name}"] = {"ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1),
-                                           "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops,
-                                           "linears": L * len(shapes), "bound": "mfma"}
-        log(f"1.3B stack {name}: {ms * 1e3:.0f} us/step, {tf:.0f} TFLOP/s")
+                                           "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
+                                           "ms_per_step_cold_mall": round(cold, 4),
+                                           "cold_range_ms": [round(cmin, 4), round(cmax, 4)],
+                                           "frac_mfma_bf16_cold": round(flops / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                           "flops": flops, "linears": L * len(shapes), "bound": "mfma"}
+        log(f"1.3B stack {name}: {ms * 1e3:.0f} us/step warm, {cold * 1e3:.0f} cold, {tf:.0f} TFLOP/s")
     del layers
     torch.cuda.empty_cache()
     # the same stack with each layer's same-input linears concatenated column-wise
@@ -469,15 +699,86 @@ def leg_stack_1p3b(torch, bgb, syn):
                     bgb.fbi_linear_w1a16(xs[K], Ps[li], As[li], N, y=ys[N], ws=ws)
 
         n = 10 if M <= 64 else 3
-        ms = graph_time(torch, fbody, n, 2) / n
+        ms = graph_time(torch, fbody, n, 2, flush=False) / n
+        cold, cmin, cmax = cold_step_ms(torch, fbody, 5 if M <= 64 else 3)
         flops = 2 * M * sum(K * N for _, K, N in fshapes) * L
         tf = flops / (ms * 1e-3) / 1e12
         out[f"w1a16_1p3b_stack_fused_{name}"] = {"ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1),
-                                                 "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4), "flops": flops,
-                                                 "linears": L * len(fshapes), "bound": "mfma"}
-        log(f"1.3B stack fused {name}: {ms * 1e3:.0f} us/step, {tf:.0f} TFLOP/s")
+                                                 "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
+                                                 "ms_per_step_cold_mall": round(cold, 4),
+                                                 "cold_range_ms": [round(cmin, 4), round(cmax, 4)],
+                                                 "frac_mfma_bf16_cold": round(flops / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                                 "flops": flops, "linears": L * len(fshapes), "bound": "mfma"}
+        log(f"1.3B stack fused {name}: {ms * 1e3:.0f} us/step warm, {cold * 1e3:.0f} cold, {tf:.0f} TFLOP/s")
     del flayers
     return out
+
+
+def leg_ceilings(torch):
+    """Ceilings measured on this GPU (include/bgb_ceilings.h): streaming-read
+    bandwidth per launch size (each launch reads a window of a 2 GiB buffer
+    that no recent launch has read), the empty-kernel launch cost, and the
+    sustained dense MFMA rates on random operand values (bf16 16x16x32, int8
+    16x16x64), each a HIP graph of back-to-back launches."""
+    import ctypes
+    path = os.path.join(ROOT, "bit_gemm_binarize_amd", "ceilings", "libbgb_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (python -m bit_gemm_binarize_amd.build)")
+    lib = ctypes.CDLL(path)
+    V, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.ceil_stream_read.argtypes = [V, SZ, I, V, V]
+    lib.ceil_empty.argtypes = [I, I, V]
+    lib.ceil_mfma_bf16.argtypes = [V, I, I, V, V]
+    lib.ceil_mfma_i8.argtypes = [V, I, I, V, V]
+    for f in (lib.ceil_stream_read, lib.ceil_empty, lib.ceil_mfma_bf16, lib.ceil_mfma_i8):
+        f.restype = I
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel failed: {rc} (hip {lib.ceil_last_hip_error()})")
+
+    st = lambda: torch.cuda.current_stream().cuda_stream
+    out = {}
+    big = torch.empty((2 << 30) // 4, dtype=torch.int32, device="cuda").random_()
+    blocks = 2048
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    for label, nbytes in (("2MB", 2 << 20), ("5.6MB", 5636096), ("25MB", 25296896), ("800MB", 800 << 20)):
+        nbytes -= nbytes % 16
+        windows = max(1, (2 << 30) // nbytes)
+        n = min(400, max(4, windows * 2))
+
+        def body(i, nbytes=nbytes, windows=windows):
+            ok(lib.ceil_stream_read(big.data_ptr() + (i % windows) * nbytes, nbytes, blocks, sink.data_ptr(), st()))
+
+        ms = graph_time(torch, body, n, 2) / n
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"stream_read_{label}"] = {"us_per_launch": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+        log(f"ceiling stream read {label}: {ms * 1e3:.2f} us/launch, {gbs:.0f} GB/s")
+    del big
+    ms = graph_time(torch, lambda i: ok(lib.ceil_empty(256, 512, st())), 2000, 20, flush=False) / 2000
+    out["empty_kernel_256x512"] = {"us_per_launch": round(ms * 1e3, 3)}
+    log(f"ceiling empty kernel: {ms * 1e3:.2f} us/launch")
+    # operands: N(0,1) bf16 values (finite, every mantissa bit toggling) and
+    # uniform int8 values, 8192 x 16 bytes each
+    rnd_bf16 = torch.randn(8192 * 8, device="cuda").to(torch.bfloat16)
+    rnd_i8 = torch.randint(-128, 128, (8192 * 16,), dtype=torch.int8, device="cuda")
+    fsink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    for name, fn, opd, per, peak in (("mfma_bf16_16x16x32", lib.ceil_mfma_bf16, rnd_bf16, 16384, BF16_PEAK_TFLOPS),
+                                     ("mfma_i8_16x16x64", lib.ceil_mfma_i8, rnd_i8, 32768, INT8_PEAK_TOPS)):
+        iters = 2000
+        n = 20
+
+        def body(i, fn=fn, opd=opd, iters=iters):
+            ok(fn(opd.data_ptr(), blocks, iters, fsink.data_ptr(), st()))
+
+        ms = graph_time(torch, body, n, 2, flush=False) / n
+        work = blocks * 4 * iters * 8 * per
+        rate = work / (ms * 1e-3) / 1e12
+        out[name] = {"T_per_s": round(rate, 1), "frac_peak": round(rate / peak, 4), "ms_per_launch": round(ms, 4),
+                     "operands": "random values, fixed per lane"}
+        log(f"ceiling {name}: {rate:.0f} T/s ({rate / peak:.2f} of peak)")
+    return {"ceilings": out}
 
 
 def main():
@@ -486,6 +787,14 @@ def main():
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path; see DESIGN.md for how the layer would shard).", file=sys.stderr)
         sys.exit(2)
+    # the CPU oracle first, before anything touches the GPU: its all-core leg
+    # forks worker processes, which must not inherit a HIP context
+    cpu = None
+    if not args.no_cpu_baseline and args.calib_copy_mb <= 0:
+        import bgb_synth as syn
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(headline_host_state(syn), args.cpu_seconds, workers)
+
     import torch
 
     if args.calib_copy_mb > 0:
@@ -508,8 +817,12 @@ def main():
 
     legs = {}
     want = set() if args.legs == "none" else (
-        {"pack", "decode7b", "prefill", "stack", "ternary", "backward"} if args.legs == "all"
+        {"fbi768", "pack", "decode7b", "prefill", "stack", "ternary", "backward", "ceilings"} if args.legs == "all"
         else set(args.legs.split(",")))
+    if args.ceilings:
+        want.add("ceilings")
+    if "fbi768" in want:
+        legs.update(leg_fbi_768(torch, bgb, syn))
     if "pack" in want:
         legs.update(leg_pack(torch, bgb, syn))
         torch.cuda.empty_cache()
@@ -527,8 +840,10 @@ def main():
     if "backward" in want:
         legs.update(leg_backward(torch, bgb, syn))
         torch.cuda.empty_cache()
+    if "ceilings" in want:
+        legs.update(leg_ceilings(torch))
+        torch.cuda.empty_cache()
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(state, args.cpu_seconds)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -537,6 +852,7 @@ def main():
         "data": "synthetic: seeded N(0.001, 0.02) fp32 weights packed to 1 bit, N(0,1) fp32 activations",
         "config": {"workload": "bitlinear_w1a8_decode_4096x11008", "M": state["M"], "K": state["K"],
                    "N": state["N"], "x_dtype": "f32", "weight_copies": R,
+                   "distinct_weight_bytes_timed": state["distinct_bytes"], "mall_flush_bytes": MALL_FLUSH_BYTES,
                    "step": "one fused kernel: LN + absmax quant prologue, packed GEMV, epilogue (HIP graph of all steps)"},
         "roofline": roof, "cpu_baseline": cpu, "legs": legs,
     }

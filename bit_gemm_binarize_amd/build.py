@@ -12,6 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbgb.so")
+CEIL_SRC = os.path.join(HERE, "ceilings", "ceilings.hip")
+CEIL_LIB = os.path.join(HERE, "ceilings", "libbgb_ceilings.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
@@ -40,11 +42,26 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_ceilings(verbose: bool = True) -> str:
+    """The ceiling microbenchmarks (measurement only; not linked into libbgb.so)."""
+    tmp = CEIL_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *COMMON, "-shared", CEIL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEIL_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEIL_LIB)
+    if verbose:
+        print(f"built {CEIL_LIB}")
+    return CEIL_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        ceil = ex.submit(build_ceilings, verbose)
         objs = list(ex.map(_compile, srcs))
+        ceil.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

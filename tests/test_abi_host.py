@@ -195,6 +195,11 @@ def test_backward_validation(lib):
     assert call_bwd(lib, wsb=need - 1) == BAD
     assert call_bwd(lib, ws=None) == BAD
     assert call_bwd(lib, M=0) == 0 and call_bwd(lib, N=0) == 0
+    # dX multiplies by [S^T; S^T], a 2N x K operand: K N < 2^31 but 2 N K > 2^31 - 1
+    assert 65536 * 16416 < 2 ** 31 - 1 < 2 * 65536 * 16416
+    assert call_bwd(lib, M=1, K=65536, N=16416) == BAD
+    assert call_bwd(lib, M=0, K=65536, N=16416) == BAD                            # shapes are checked when empty too
+    assert call_bwd(lib, M=0, K=65536, N=16416, dx=None) == 0                     # no dX: that operand is not formed
 
 
 def call_bl(lib, x=A, xdt=0, M=1, K=64, N=8, P=A, beta=A, qp=None, y=A, xq=None, g=None, acc=None, ws=A,
@@ -233,3 +238,29 @@ def test_header_compiles_as_c_and_cpp(tmp_path):
         r = subprocess.run([exe, "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
                             "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_ceilings_library_exports_and_rejects():
+    """libbgb_ceilings.so (measurement kernels) exports what bgb_ceilings.h
+    declares; bad arguments return -1 before any launch."""
+    path = os.path.join(ROOT, "bit_gemm_binarize_amd", "ceilings", "libbgb_ceilings.so")
+    if not os.path.exists(path):
+        pytest.fail("libbgb_ceilings.so is not built (python -m bit_gemm_binarize_amd.build)")
+    src = open(os.path.join(ROOT, "include", "bgb_ceilings.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"^\s*int\s+([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M))
+    assert {"ceil_stream_read", "ceil_empty", "ceil_mfma_bf16", "ceil_mfma_i8", "ceil_last_hip_error"} <= names
+    lib = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(lib, n), n
+    V, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.ceil_stream_read.argtypes = [V, SZ, I, V, V]
+    lib.ceil_empty.argtypes = [I, I, V]
+    lib.ceil_mfma_bf16.argtypes = [V, I, I, V, V]
+    assert lib.ceil_stream_read(None, 1024, 8, A, None) == -1
+    assert lib.ceil_stream_read(A + 4, 1024, 8, A, None) == -1          # misaligned
+    assert lib.ceil_stream_read(A, 1000, 8, A, None) == -1              # not a multiple of 16
+    assert lib.ceil_empty(0, 64, None) == -1
+    assert lib.ceil_empty(8, 2048, None) == -1
+    assert lib.ceil_mfma_bf16(None, 8, 10, A, None) == -1
+    assert lib.ceil_mfma_bf16(A, 8, 0, A, None) == -1
