@@ -24,6 +24,7 @@ __all__ = [
     "OP_PACK_FBI", "OP_PACK_BITNET", "OP_FBI_LINEAR", "OP_BITLINEAR", "GEMV_MAX_M", "W1A16_DECODE_MAX_M",
     "ROUND_TRUNC", "ROUND_RNE", "GAMMA_TENSOR", "GAMMA_TOKEN", "fbi_linear_w1a16_group", "group_workspace_bytes",
     "GROUP_MAX", "RANGE_SYMMETRIC", "RANGE_NONNEG", "fbi_pack_transposed", "fbi_linear_w1a16_backward", "OP_FBI_BACKWARD",
+    "bitlinear_w1a8_noalloc", "noalloc_scratch_bytes", "ESCRATCH",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,12 +36,13 @@ OP_PACK_FBI, OP_PACK_BITNET, OP_FBI_LINEAR, OP_BITLINEAR, OP_BITLINEAR158, OP_FB
 GEMV_MAX_M = 32          # BitLinear: M <= 32 runs the decode kernels, above: the MFMA GEMM
 W1A16_DECODE_MAX_M = 64  # FBI-linear: M <= 64 runs the decode kernels, above: the MFMA GEMM
 GROUP_MAX = 8            # linears per fbi_linear_w1a16_group call
+ESCRATCH = -4            # bitlinear_w1a8_noalloc: the call does not fit the library's static scratch
 
 EXPORTS = ("bgb_packed_bytes", "bgb_workspace_bytes", "binarize_pack", "fbi_linear_w1a16",
            "fbi_linear_w1a16_group", "bgb_group_workspace_bytes", "fbi_pack_transposed",
            "fbi_linear_w1a16_backward",
            "bitlinear_w1a8", "bitlinear_quantize", "bitlinear_matmul", "bitlinear158_w1a8",
-           "bitlinear158_matmul", "bgb_status_string",
+           "bitlinear158_matmul", "bitlinear_w1a8_noalloc", "bgb_noalloc_scratch_bytes", "bgb_status_string",
            "bgb_last_hip_error", "bgb_version")
 
 
@@ -118,6 +120,10 @@ def load():
     lib.bitlinear_quantize.restype = I
     lib.bitlinear_matmul.argtypes = [I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, SZ, P]
     lib.bitlinear_matmul.restype = I
+    lib.bitlinear_w1a8_noalloc.argtypes = [P, I, I64, I64, I64, P, P, ctypes.POINTER(_QP), P, P, P, P, P]
+    lib.bitlinear_w1a8_noalloc.restype = I
+    lib.bgb_noalloc_scratch_bytes.argtypes = []
+    lib.bgb_noalloc_scratch_bytes.restype = SZ
     lib.bitlinear158_w1a8.argtypes = lib.bitlinear_w1a8.argtypes
     lib.bitlinear158_w1a8.restype = I
     lib.bitlinear158_matmul.argtypes = lib.bitlinear_matmul.argtypes
@@ -414,6 +420,42 @@ def bitlinear_w1a8(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y=No
     if want_acc:
         extras["acc"] = acc
     return y, extras
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static device array behind bitlinear_w1a8_noalloc."""
+    return int(load().bgb_noalloc_scratch_bytes())
+
+
+def bitlinear_w1a8_noalloc(x, P, beta, N: int, qp: Optional[QuantParams] = None, *, y, q=None, gamma=None,
+                           acc=None, stream=None):
+    """bitlinear_w1a8 for callers that cannot allocate: the library's static
+    device scratch is the workspace and every output is the caller's (y, and
+    the optional taps q [M][K] int8, gamma [1] or [M] float32, acc [M][N]
+    int32). Nothing is allocated here either. Calls that overlap on one GPU
+    race on the shared scratch."""
+    torch = _torch()
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M][K]")
+    M, K = x.shape
+    dev = x.device
+    qp = qp or QuantParams()
+    ng = M if qp.gamma_scope == GAMMA_TOKEN else 1
+    _need(P, "P", nbytes=packed_bytes(K, N))
+    _need(beta, "beta", (torch.float32,), nbytes=4)
+    _need(y, "y", (torch.float32,), shape=(M, N))
+    if q is not None:
+        _need(q, "q", (torch.int8,), shape=(M, K))
+    if gamma is not None:
+        _need(gamma, "gamma", (torch.float32,), nbytes=4 * ng)
+    if acc is not None:
+        _need(acc, "acc", (torch.int32,), shape=(M, N))
+    _on_device(dev, x=x, P=P, beta=beta, y=y, q=q, gamma=gamma, acc=acc)
+    cqp = qp.c()
+    _check(load().bitlinear_w1a8_noalloc(_ptr(x), _dt(x), M, K, N, _ptr(P), _ptr(beta), ctypes.byref(cqp), _ptr(y),
+                                         _ptr(q), _ptr(gamma), _ptr(acc), _stream(stream)))
+    return y
 
 
 def bitlinear_quantize(x, qp: Optional[QuantParams] = None, *, ws, N_max: int = 0, want_q=False, want_gamma=False,

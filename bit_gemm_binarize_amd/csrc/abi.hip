@@ -34,6 +34,10 @@ char* carve(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 }  // namespace
 
+namespace bgb {
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace bgb
+
 extern "C" {
 
 size_t bgb_packed_bytes(int64_t K, int64_t N) {
@@ -404,6 +408,7 @@ const char* bgb_status_string(int status) {
         case BGB_EINVAL: return "invalid argument (null pointer, shape, alignment or workspace size)";
         case BGB_EUNSUPPORTED: return "unsupported dtype or mode";
         case BGB_EHIP: return "HIP launch failed (see bgb_last_hip_error)";
+        case BGB_ESCRATCH: return "the call needs more workspace than the no-alloc entry point's static scratch holds";
         default: return "unknown status";
     }
 }

@@ -111,6 +111,9 @@ struct BitlinearWs {
     }
 };
 
+// Record a HIP error for bgb_last_hip_error() (entry points outside abi.hip).
+void set_last_hip_error(int e);
+
 // ---- launchers (each returns hipGetLastError() after its launches) -----------
 hipError_t launch_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
                        void* alpha, int alpha_f16, float* beta, float* centre,

@@ -62,7 +62,8 @@ typedef enum {
     BGB_OK = 0,
     BGB_EINVAL = -1,        /* null pointer, bad shape, misalignment, small workspace */
     BGB_EUNSUPPORTED = -2,  /* dtype or mode combination not implemented */
-    BGB_EHIP = -3           /* a HIP launch failed; see bgb_last_hip_error() */
+    BGB_EHIP = -3,          /* a HIP launch failed; see bgb_last_hip_error() */
+    BGB_ESCRATCH = -4       /* bitlinear_w1a8_noalloc: the call needs more scratch than its static array */
 } bgb_status;
 
 typedef enum { BGB_F32 = 0, BGB_F16 = 1, BGB_BF16 = 2 } bgb_dtype;
@@ -271,6 +272,30 @@ int bitlinear_w1a8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
                    const uint32_t* P, const float* beta, const bgb_quant_params* qp,
                    float* y, int8_t* xq_opt, float* gamma_opt, int32_t* acc_opt,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bitlinear_w1a8_noalloc -- bitlinear_w1a8 for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments, results and
+ * kernels as bitlinear_w1a8, minus (ws, ws_bytes): the workspace is a static
+ * device array of BGB_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's load until the process ends. The call allocates
+ * nothing; its first call on a device looks the array's address up once.
+ * Calls that overlap on one GPU (concurrent streams, or host threads) share
+ * that array and race: order them, or use bitlinear_w1a8 with workspaces of
+ * their own. No call relies on what a previous one left in the array.
+ * Errors: as bitlinear_w1a8, and BGB_ESCRATCH (nothing launched) when
+ * bgb_workspace_bytes(BGB_OP_BITLINEAR, M, K, N) exceeds
+ * BGB_NOALLOC_SCRATCH_BYTES (e.g. 2048 tokens x 4096 features need 8.1 MiB,
+ * 4096 x 4096 need 16.1 MiB; calls whose launch plan splits K also hold their
+ * partial sums there).
+ */
+#define BGB_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t bgb_noalloc_scratch_bytes(void);
+int bitlinear_w1a8_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t N,
+                           const uint32_t* P, const float* beta, const bgb_quant_params* qp,
+                           float* y, int8_t* xq_opt, float* gamma_opt, int32_t* acc_opt,
+                           void* stream);
 
 /*
  * bitlinear_quantize + bitlinear_matmul -- the two stages of bitlinear_w1a8,

@@ -264,3 +264,19 @@ def test_ceilings_library_exports_and_rejects():
     assert lib.ceil_empty(8, 2048, None) == -1
     assert lib.ceil_mfma_bf16(None, 8, 10, A, None) == -1
     assert lib.ceil_mfma_bf16(A, 8, 0, A, None) == -1
+
+
+def test_noalloc_rejects_oversize_before_touching_the_gpu(lib):
+    """bitlinear_w1a8_noalloc checks its workspace need against the static
+    scratch first: a call that does not fit returns BGB_ESCRATCH (-4) with no
+    device call (so it runs without a GPU)."""
+    assert lib.bgb_noalloc_scratch_bytes() == 64 << 20
+    lib.bitlinear_w1a8_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64] + [ctypes.c_void_p] * 8
+    M, K, N = 8192, 8192, 64
+    assert bgb.workspace_bytes(bgb.OP_BITLINEAR, M, K, N) > 64 << 20
+    assert lib.bitlinear_w1a8_noalloc(A, 0, M, K, N, A, A, None, A, None, None, None, None) == -4
+    assert b"scratch" in lib.bgb_status_string(-4)
+    # an empty call is validated and launches nothing
+    assert lib.bitlinear_w1a8_noalloc(None, 0, 0, 64, 8, None, None, None, None, None, None, None, None) == 0
+    assert lib.bitlinear_w1a8_noalloc(None, 0, 0, 40, 8, None, None, None, None, None, None, None, None) == BAD
