@@ -650,12 +650,16 @@ def leg_backward(torch, bgb, syn):
     return out
 
 
-def leg_stack_1p3b(torch, bgb, syn):
+def leg_stack_1p3b(torch, bgb, syn, only_grouped=False):
+    """only_grouped: just the grouped batch-64 decode step (a focused run for
+    kernel traces)."""
     cfg = syn.CONFIGS["w1a16_1p3b_stack"]
     shapes, L = cfg["shapes"], cfg["layers"]
-    layers = [build_layer(torch, bgb, syn, cfg["seed"], shapes, l, torch.float16) for l in range(L)]
+    layers = [] if only_grouped else [build_layer(torch, bgb, syn, cfg["seed"], shapes, l, torch.float16)
+                                      for l in range(L)]
     out = {}
-    for name, M in (("decode_b64", cfg["decode_batch"]), ("prefill_2x1024", cfg["prefill_tokens"])):
+    for name, M in (() if only_grouped else
+                    (("decode_b64", cfg["decode_batch"]), ("prefill_2x1024", cfg["prefill_tokens"]))):
         xs = {K: torch.randn((M, K), device="cuda").to(torch.bfloat16) for K in (2048, 5632)}
         ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N in (2048, 5632)}
         wsz = max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, N) for _, K, N in shapes)
@@ -687,7 +691,8 @@ def leg_stack_1p3b(torch, bgb, syn):
     H, F = 2048, 5632
     fshapes = [("qkv", H, 3 * H), ("o", H, H), ("gate_up", H, 2 * F), ("down", F, H)]
     flayers = [build_layer(torch, bgb, syn, cfg["seed"], fshapes, 50 + l, torch.float16) for l in range(L)]
-    for name, M in (("decode_b64", cfg["decode_batch"]), ("prefill_2x1024", cfg["prefill_tokens"])):
+    for name, M in ((("decode_b64", cfg["decode_batch"]),) if only_grouped else
+                    (("decode_b64", cfg["decode_batch"]), ("prefill_2x1024", cfg["prefill_tokens"]))):
         xs = {K: torch.randn((M, K), device="cuda").to(torch.bfloat16) for K in (H, F)}
         ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, _, N in fshapes}
         wsz = max(bgb.workspace_bytes(bgb.OP_FBI_LINEAR, M, K, N) for _, K, N in fshapes)
@@ -699,17 +704,41 @@ def leg_stack_1p3b(torch, bgb, syn):
                     bgb.fbi_linear_w1a16(xs[K], Ps[li], As[li], N, y=ys[N], ws=ws)
 
         n = 10 if M <= 64 else 3
-        ms = graph_time(torch, fbody, n, 2, flush=False) / n
-        cold, cmin, cmax = cold_step_ms(torch, fbody, 5 if M <= 64 else 3)
         flops = 2 * M * sum(K * N for _, K, N in fshapes) * L
+        if not only_grouped:
+            ms = graph_time(torch, fbody, n, 2, flush=False) / n
+            cold, cmin, cmax = cold_step_ms(torch, fbody, 5 if M <= 64 else 3)
+            tf = flops / (ms * 1e-3) / 1e12
+            out[f"w1a16_1p3b_stack_fused_{name}"] = {
+                "ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
+                "ms_per_step_cold_mall": round(cold, 4), "cold_range_ms": [round(cmin, 4), round(cmax, 4)],
+                "frac_mfma_bf16_cold": round(flops / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "flops": flops,
+                "linears": L * len(fshapes), "bound": "mfma"}
+            log(f"1.3B stack fused {name}: {ms * 1e3:.0f} us/step warm, {cold * 1e3:.0f} cold, {tf:.0f} TFLOP/s")
+        if M > 64:
+            continue
+        # the layer's four fused linears as one group call: one launch per
+        # layer (the linears' inputs are independent synthetic tensors here)
+        gys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, _, N in fshapes]
+        glin0 = [(xs[K], flayers[0][0][li], flayers[0][1][li], N) for li, (_, K, N) in enumerate(fshapes)]
+        gws = torch.empty(max(bgb.group_workspace_bytes([(x, P, a, y) for (x, P, a, _), y in zip(glin0, gys)], M),
+                              256), dtype=torch.uint8, device="cuda")
+
+        def gbody(i, xs=xs, gys=gys, gws=gws):
+            for Ps, As in flayers:
+                bgb.fbi_linear_w1a16_group([(xs[K], Ps[li], As[li], N) for li, (_, K, N) in enumerate(fshapes)],
+                                           ys=gys, ws=gws)
+
+        ms = graph_time(torch, gbody, n, 2, flush=False) / n
+        cold, cmin, cmax = cold_step_ms(torch, gbody, 5)
         tf = flops / (ms * 1e-3) / 1e12
-        out[f"w1a16_1p3b_stack_fused_{name}"] = {"ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1),
-                                                 "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
-                                                 "ms_per_step_cold_mall": round(cold, 4),
-                                                 "cold_range_ms": [round(cmin, 4), round(cmax, 4)],
-                                                 "frac_mfma_bf16_cold": round(flops / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                                                 "flops": flops, "linears": L * len(fshapes), "bound": "mfma"}
-        log(f"1.3B stack fused {name}: {ms * 1e3:.0f} us/step warm, {cold * 1e3:.0f} cold, {tf:.0f} TFLOP/s")
+        out[f"w1a16_1p3b_stack_grouped_{name}"] = {
+            "ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
+            "ms_per_step_cold_mall": round(cold, 4), "cold_range_ms": [round(cmin, 4), round(cmax, 4)],
+            "frac_mfma_bf16_cold": round(flops / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4), "flops": flops,
+            "launches": L * (2 if gws.numel() > 256 else 1),
+            "linears": "qkv, o, gate_up, down as one group per layer (GEMM + reduce of the K parts)", "bound": "mfma"}
+        log(f"1.3B stack grouped {name}: {ms * 1e3:.0f} us/step warm, {cold * 1e3:.0f} cold, {tf:.0f} TFLOP/s")
     del flayers
     return out
 
@@ -834,6 +863,8 @@ def main():
         torch.cuda.empty_cache()
     if "stack" in want:
         legs.update(leg_stack_1p3b(torch, bgb, syn))
+    elif "stack_grouped" in want:
+        legs.update(leg_stack_1p3b(torch, bgb, syn, only_grouped=True))
     if "ternary" in want:
         legs.update(leg_ternary(torch, bgb, syn, args.rotate_mb))
         torch.cuda.empty_cache()

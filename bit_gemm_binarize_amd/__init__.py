@@ -285,8 +285,10 @@ def group_workspace_bytes(entries, M: int) -> int:
 
 def fbi_linear_w1a16_group(linears, y_dtype=None, *, ys=None, ws=None, stream=None):
     """linears: list of (x, P, alpha, N), x bf16/f16 [M][K] (the same M and dtypes for all).
-    Independent linears: one launch for a single token, else one after another.
-    Returns the list of outputs y [M][N]."""
+    Independent linears: one launch for 1 to 64 tokens where the shapes allow it
+    (plus one reduce launch when 17..64 tokens split K; see
+    fbi_linear_w1a16_group in bgb.h), else one after another. Returns the
+    outputs y [M][N]."""
     torch = _torch()
     if not linears:
         return []

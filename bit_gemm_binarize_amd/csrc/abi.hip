@@ -147,17 +147,25 @@ static int group_live(const bgb_w1a16_item* items, int count, bgb::W1a16Item* ou
     return n;
 }
 
-// 1: one single-token launch; 2: one few-token launch; 0: item by item.
+// 1: one single-token launch; 2: one few-token launch; 3: one launch of the
+// grouped GEMM (17 to 64 tokens); 0: item by item.
 static int group_one_launch(const bgb_w1a16_item* items, int count, int64_t M) {
     bgb::W1a16Item in[BGB_GROUP_MAX];
     const int n = group_live(items, count, in);
     if (M == 1) return bgb::w1a16_decode1_group_supported(in, n) ? 1 : 0;
+    if (M > 16) return bgb::w1a16_gemm_group_supported(in, n, M) ? 3 : 0;
     return bgb::w1a16_decodem_group_supported(in, n, M) ? 2 : 0;
 }
 
 size_t bgb_group_workspace_bytes(const bgb_w1a16_item* items, int count, int64_t M) {
     if (!items || count <= 0 || count > BGB_GROUP_MAX || M <= 0) return 0;
-    if (group_one_launch(items, count, M)) return 0;
+    const int one = group_one_launch(items, count, M);
+    if (one == 3) {
+        bgb::W1a16Item in[BGB_GROUP_MAX];
+        const int n = group_live(items, count, in);
+        return bgb::w1a16_gemm_group_ws_bytes(in, n, M);
+    }
+    if (one) return 0;
     size_t need = 0;
     for (int i = 0; i < count; ++i) {
         const size_t n = bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, items[i].K, items[i].N);
@@ -207,6 +215,7 @@ int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, in
         const int n = group_live(items, count, in);
         const int ydt = y_dtype == BGB_F32 ? 0 : (y_dtype == BGB_F16 ? 1 : 2);
         const int xf = x_dtype == BGB_F16, af = alpha_dtype == BGB_F16;
+        if (one == 3) return finish(bgb::launch_w1a16_gemm_group(in, n, M, xf, af, ydt, ws, s));
         return finish(one == 1 ? bgb::launch_w1a16_decode1_group(in, n, xf, af, ydt, s)
                                : bgb::launch_w1a16_decodem_group(in, n, M, xf, af, ydt, s));
     }

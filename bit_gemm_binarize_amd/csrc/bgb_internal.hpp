@@ -169,6 +169,13 @@ struct W1a16Item {
 bool w1a16_decode1_group_supported(const W1a16Item* items, int count);
 hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f16, int alpha_f16, int y_dtype,
                                       hipStream_t s);
+// 17 <= M <= 64 tokens: the MFMA GEMM tile per item in one launch, K split
+// per item, the parts' raw sums (workspace, w1a16_gemm_group_ws_bytes) added
+// in part order by one reduce launch for the whole group.
+bool w1a16_gemm_group_supported(const W1a16Item* items, int count, int64_t M);
+size_t w1a16_gemm_group_ws_bytes(const W1a16Item* items, int count, int64_t M);
+hipError_t launch_w1a16_gemm_group(const W1a16Item* items, int count, int64_t M, int x_f16, int alpha_f16,
+                                   int y_dtype, void* ws, hipStream_t s);
 // 2 <= M <= 16 tokens, every item's tokens staged whole in LDS
 // (w1a16_decodem_supported), one launch.
 bool w1a16_decodem_group_supported(const W1a16Item* items, int count, int64_t M);

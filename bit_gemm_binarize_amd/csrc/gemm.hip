@@ -224,7 +224,7 @@ BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& 
 // kKTail (W1A16, K not a multiple of 128): the stages reaching past K take
 // zeros for those activation chunks.
 template <bool kW1A8, bool kF16, int NN, int NW, bool kTern = false, bool kKTail = false>
-__global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a) {
+BGB_DEV void gemm_tile(const GemmArgs& a, const int tile, const int z) {
     static_assert(!kTern || kW1A8, "ternary weights take the int8 path");
     static_assert(!kKTail || !kW1A8, "the int8 codes arrive zero-padded");
     constexpr int BM = 16 * NN;
@@ -249,11 +249,8 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
     uint8_t* const lds[kRing] = {lds0, lds1, lds2, lds3};
     uint8_t* const wls[kRing] = {wl0, wl1, wl2, wl3};
 
-    const int tile = xcd_tile(blockIdx.x, a.ntiles);
-    if (tile >= a.ntiles) return;
     const int64_t m0 = int64_t(tile / a.ntj) * BM, j0 = int64_t(tile % a.ntj) * BJ;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
-    const int z = blockIdx.y;
     const int s0 = z * a.per;
     const int ns = (s0 + a.per < a.T ? s0 + a.per : a.T) - s0;   // >= 1 by the plan
     const int64_t M = a.M, N = a.N;
@@ -469,6 +466,13 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
     }
 }
 
+template <bool kW1A8, bool kF16, int NN, int NW, bool kTern = false, bool kKTail = false>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a) {
+    const int tile = xcd_tile(blockIdx.x, a.ntiles);
+    if (tile >= a.ntiles) return;
+    gemm_tile<kW1A8, kF16, NN, NW, kTern, kKTail>(a, tile, blockIdx.y);
+}
+
 // Sum of the splits in split order, then the epilogue. One thread per 4
 // consecutive columns of one token.
 template <bool kW1A8>
@@ -543,6 +547,234 @@ static hipError_t launch_gemm(GemmArgs a, const GemmPlan& p, hipStream_t s) {
     if (p.splits > 1) {
         const int64_t n = a.M * ((a.N + 3) / 4);
         splitk_reduce_kernel<kW1A8><<<unsigned((n + 255) / 256), 256, 0, s>>>(a, p.splits);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- grouped, 17..64 ----
+// Several independent W1A16 linears of 17 to 64 tokens in one launch (the
+// linears of a decoder layer at a decode step). Each item runs the GEMM tile
+// above with 64-token tiles (NN = 4); its K range is split into S_i parts so
+// that the launch holds enough units of about equal length to fill the chip.
+// Items with S_i = 1 write y directly; the others store raw sums, which one
+// reduce launch for the whole group adds in part order (so results are the
+// same from run to run) before applying the epilogue. Units are numbered
+// split-major within an item (the units of one part share activation rows).
+struct GemmGroupItem {
+    GemmArgs a;
+    int first;
+};
+struct GemmGroup {
+    GemmGroupItem it[kGroupMax];
+    int count, units;
+};
+
+template <bool kF16, bool kKTail>
+__global__ void __launch_bounds__(256, 2) gemm_group_kernel(const GemmGroup g) {
+    const int u = xcd_tile(blockIdx.x, g.units);
+    if (u >= g.units) return;
+    GemmGroupItem it = g.it[0];
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < g.count && u >= g.it[i].first) it = g.it[i];
+    const int rel = u - it.first;
+    const int z = rel / it.a.ntiles, tile = rel - z * it.a.ntiles;
+    gemm_tile<false, kF16, 4, 4, false, kKTail>(it.a, tile, z);
+}
+
+// The reduce pass of a group: the items with split K ranges, each over its
+// own range of blocks; one thread per 4 consecutive columns of one token.
+struct ReduceItem {
+    const float* part;
+    const void* alpha;
+    void* y;
+    int64_t M, N;
+    int splits, first;      // first block
+};
+struct ReduceGroup {
+    ReduceItem it[kGroupMax];
+    int count, alpha_f16, y_dtype;
+};
+
+__global__ void __launch_bounds__(256) group_reduce_kernel(const ReduceGroup g) {
+    ReduceItem it = g.it[0];
+#pragma unroll
+    for (int i = 1; i < kGroupMax; ++i)
+        if (i < g.count && int(blockIdx.x) >= g.it[i].first) it = g.it[i];
+    const int64_t M = it.M, N = it.N, nq = (N + 3) / 4;
+    const int64_t id = int64_t(int(blockIdx.x) - it.first) * 256 + threadIdx.x;
+    if (id >= M * nq) return;
+    const int64_t m = id / nq, jb = 4 * (id % nq), o = m * N + jb;
+    const bool full = jb + 4 <= N && (N & 3) == 0;
+    const int64_t MN = M * N;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < it.splits; ++z) {
+        if (full) {
+            s += *reinterpret_cast<const f32x4_t*>(it.part + z * MN + o);
+        } else {
+            for (int i = 0; i < 4; ++i)
+                if (jb + i < N) s[i] += it.part[z * MN + o + i];
+        }
+    }
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = jb + i < N ? alpha_at(it.alpha, g.alpha_f16, jb + i) * s[i] : 0.0f;
+    store_out16(it.y, g.y_dtype, o, v, full, jb, N);
+}
+
+namespace {
+// Cost model of a grouped launch, in microseconds: per CU, the stages of the
+// units it holds (units dealt round-robin to kGroupCUs CUs, kFixedStages of
+// fill and epilogue each) at kGroupStageUs per 64-token stage, one unit
+// alone on a CU, kGroupSharedUs per stage when two share it; with any split,
+// the reduce pass (a launch plus S_i + 1 passes over M x N_i fp32 at
+// kGroupReduceBytesPerUs). Fitted to the 1.3B-shaped layer at 64 tokens
+// (K split targets of 4 to 32 stages): a stage there costs several times its
+// matrix-core work.
+constexpr int kGroupCUs = 256;
+constexpr double kGroupStageUs = 0.85, kGroupSharedUs = 0.75, kGroupReduceBytesPerUs = 4.0e6;
+struct GroupPlan {
+    int n, units, order[kGroupMax], splits[kGroupMax], per[kGroupMax], T[kGroupMax], ntj[kGroupMax];
+    size_t part_off[kGroupMax], total;
+};
+
+GroupPlan group_plan(const W1a16Item* items, int count, int64_t M) {
+    GroupPlan g{};
+    int tmax = 1;
+    for (int i = 0; i < count; ++i) {
+        g.T[i] = int(2 * tiles_per_col(items[i].K));           // 64-row stages
+        g.ntj[i] = int((items[i].N + 255) / 256);
+        tmax = g.T[i] > tmax ? g.T[i] : tmax;
+    }
+    double best = 1e300;
+    int bestP = tmax;
+    for (int P = 2; P <= tmax; ++P) {
+        int64_t units = 0;
+        int maxper = 0;
+        double fix = 0.0;
+        bool any = false;
+        for (int i = 0; i < count; ++i) {
+            int S = (g.T[i] + P - 1) / P;
+            const int per = (g.T[i] + S - 1) / S;
+            S = (g.T[i] + per - 1) / per;
+            units += int64_t(g.ntj[i]) * S;
+            maxper = per > maxper ? per : maxper;
+            if (S > 1) {
+                fix += double(S + 1) * double(M) * double(items[i].N) * 4.0;
+                any = true;
+            }
+        }
+        const int64_t per_cu = (units + kGroupCUs - 1) / kGroupCUs;      // units on the busiest CU
+        double t = per_cu <= 1 ? (maxper + kFixedStages) * kGroupStageUs
+                               : double(per_cu) * (maxper + kFixedStages) * kGroupSharedUs;
+        if (any) t += kLaunchUs + fix / kGroupReduceBytesPerUs;
+        if (t < best - 1e-9) {
+            best = t;
+            bestP = P;
+        }
+    }
+    for (int i = 0; i < count; ++i) {
+        const int S = (g.T[i] + bestP - 1) / bestP;
+        g.per[i] = (g.T[i] + S - 1) / S;
+        g.splits[i] = (g.T[i] + g.per[i] - 1) / g.per[i];
+        g.order[i] = i;
+    }
+    // the longest units first
+    for (int a = 1; a < count; ++a)
+        for (int b = a; b > 0 && g.per[g.order[b]] > g.per[g.order[b - 1]]; --b) {
+            const int t = g.order[b];
+            g.order[b] = g.order[b - 1];
+            g.order[b - 1] = t;
+        }
+    size_t part = 0;
+    int64_t units = 0;
+    for (int i = 0; i < count; ++i) {
+        g.part_off[i] = part;
+        if (g.splits[i] > 1) part += align256(size_t(g.splits[i]) * size_t(M) * size_t(items[i].N) * 4);
+        units += int64_t(g.ntj[i]) * g.splits[i];
+    }
+    g.n = count;
+    g.total = part;
+    g.units = int(units);
+    return g;
+}
+}  // namespace
+
+bool w1a16_gemm_group_supported(const W1a16Item* items, int count, int64_t M) {
+    if (M < 17 || M > 64 || count < 1 || count > kGroupMax) return false;
+    int64_t units = 0;
+    for (int i = 0; i < count; ++i) {
+        if (items[i].K <= 0 || items[i].N <= 0) return false;
+        units += (items[i].N + 255) / 256 * 2 * tiles_per_col(items[i].K);
+    }
+    return units < (int64_t(1) << 30);
+}
+
+size_t w1a16_gemm_group_ws_bytes(const W1a16Item* items, int count, int64_t M) {
+    if (!w1a16_gemm_group_supported(items, count, M)) return 0;
+    return group_plan(items, count, M).total;
+}
+
+hipError_t launch_w1a16_gemm_group(const W1a16Item* items, int count, int64_t M, int x_f16, int alpha_f16,
+                                   int y_dtype, void* ws, hipStream_t s) {
+    if (!w1a16_gemm_group_supported(items, count, M)) return hipErrorInvalidValue;
+    const GroupPlan p = group_plan(items, count, M);
+    if (p.total && !ws) return hipErrorInvalidValue;
+    GemmGroup h{};
+    ReduceGroup rg{};
+    int first = 0, rfirst = 0, nr = 0;
+    bool tail = false;
+    for (int k = 0; k < count; ++k) {
+        const int i = p.order[k];
+        const W1a16Item& in = items[i];
+        GemmArgs& a = h.it[k].a;
+        a.act = static_cast<const uint8_t*>(in.x);
+        a.row_bytes = in.K * 2;
+        a.K = in.K;
+        a.P = in.P;
+        a.M = M;
+        a.N = in.N;
+        a.T = p.T[i];
+        a.per = p.per[i];
+        a.ntj = p.ntj[i];
+        a.ntiles = p.ntj[i];                              // one 64-token tile row
+        a.alpha = in.alpha;
+        a.alpha_f16 = alpha_f16;
+        a.y = in.y;
+        a.y_dtype = y_dtype;
+        a.part = p.splits[i] > 1 ? static_cast<char*>(ws) + p.part_off[i] : nullptr;
+        h.it[k].first = first;
+        first += p.ntj[i] * p.splits[i];
+        tail |= (in.K % 128) != 0;
+        if (p.splits[i] > 1) {
+            ReduceItem& r = rg.it[nr++];
+            r.part = static_cast<const float*>(a.part);
+            r.alpha = in.alpha;
+            r.y = in.y;
+            r.M = M;
+            r.N = in.N;
+            r.splits = p.splits[i];
+            r.first = rfirst;
+            rfirst += int((M * ((in.N + 3) / 4) + 255) / 256);
+        }
+    }
+    h.count = count;
+    h.units = first;
+    const unsigned grid = unsigned(xcd_grid(first));
+    if (x_f16) {
+        if (tail) gemm_group_kernel<true, true><<<grid, 256, 0, s>>>(h);
+        else gemm_group_kernel<true, false><<<grid, 256, 0, s>>>(h);
+    } else {
+        if (tail) gemm_group_kernel<false, true><<<grid, 256, 0, s>>>(h);
+        else gemm_group_kernel<false, false><<<grid, 256, 0, s>>>(h);
+    }
+    if (nr) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        rg.count = nr;
+        rg.alpha_f16 = alpha_f16;
+        rg.y_dtype = y_dtype;
+        group_reduce_kernel<<<unsigned(rfirst), 256, 0, s>>>(rg);
     }
     return hipGetLastError();
 }

@@ -267,8 +267,8 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     static_assert(NW % F == 0 && IT * S * (kTern ? 2 : 1) <= kD1MaxTiles, "single-token W1A8 shape");
     __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
     __shared__ i32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
-    __shared__ double dsum[NW], dsq[NW];
-    __shared__ uint32_t dmax[NW];
+    __shared__ double dsum[NW], dsq[NW], dsq2[NW];
+    __shared__ float dmx[NW], dmn[NW];
     __shared__ int iscr[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
@@ -310,56 +310,91 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. LayerNorm statistics, two fp64 passes; every block computes the same
-    //    values. gamma = max |h| with h = fl32(fl32(x - mu32) rs32): rounding
-    //    is monotone and sign-symmetric, so gamma = fl32(a rs32) with
-    //    a = max |fl32(x - mu32)|, which rides along with the second pass as
-    //    an unsigned max of the bit patterns (non-negative floats order like
-    //    their bits). Pairs past K hold zeros: they add nothing to the first
-    //    sum and are left out of the second pass.
-    double s1 = 0.0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) s1 += double(v[i][c]);
-    s1 = wave_sum63(s1);
-    if (lane == 63) dsum[wave] = s1;
-    __syncthreads();
-    asm volatile("" ::"s"(beta0), "s"(y), "s"(acc_opt));
-    double sx = dsum[0];
-#pragma unroll
-    for (int wv = 1; wv < NW; ++wv) sx += dsum[wv];
-    const double mu = sx / double(K);
-    const float mu32 = float(mu);
-    double s2 = 0.0;
-    uint32_t amax = 0;
+    // 2. LayerNorm statistics; every block computes the same values. One pass
+    //    gives sum x and sum x^2 in fp64 (x^2 is exact there) and the row's
+    //    extreme x. Var = E x^2 - (E x)^2 differs from the exact variance by
+    //    at most dv = (3 K + 8) 2^-53 E x^2 (each sum's error is below
+    //    K 2^-53 times its sum of magnitudes, |E x| E|x| <= E x^2, plus the
+    //    roundings of the quotients, the square and the difference), so
+    //    rs32 = fl32(1/sqrt(Var + eps)) is the two-pass value unless
+    //    1/sqrt(Var + eps) lies within its propagated error of a point where
+    //    the fp32 rounding changes; then (rare, and the same decision in every
+    //    thread) the second fp64 pass over (x - mu)^2 decides, as before.
+    //    gamma = max |h| with h = fl32(fl32(x - mu32) rs32): rounding is
+    //    monotone and sign-symmetric, so gamma = fl32(a rs32) with
+    //    a = max |fl32(x - mu32)|, which sits at the largest or smallest x.
+    //    Pairs past K hold zeros: they add nothing to the sums and are left
+    //    out of the extremes.
+    double s1 = 0.0, s2 = 0.0;
+    float xmx = -__builtin_inff(), xmn = __builtin_inff();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        if (i * NT + tid >= pairs) continue;
+        const bool ok = i * NT + tid < pairs;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const double d = double(v[i][c]) - mu;
+            const double d = double(v[i][c]);
+            s1 += d;
             s2 += d * d;
-            v[i][c] -= mu32;                           // fl32(x - mu32), kept for the codes
-            amax = max(amax, __float_as_uint(fabsf(v[i][c])));
+            xmx = ok ? fmaxf(xmx, v[i][c]) : xmx;
+            xmn = ok ? fminf(xmn, v[i][c]) : xmn;
         }
     }
+    s1 = wave_sum63(s1);
     s2 = wave_sum63(s2);
-    amax = wave_umax63(amax);
+    xmx = wave_max63(xmx);
+    xmn = wave_min63(xmn);
     if (lane == 63) {
+        dsum[wave] = s1;
         dsq[wave] = s2;
-        dmax[wave] = amax;
+        dmx[wave] = xmx;
+        dmn[wave] = xmn;
     }
     __syncthreads();
-    double v2 = dsq[0];
-    uint32_t am = dmax[0];
+    asm volatile("" ::"s"(beta0), "s"(y), "s"(acc_opt));
+    double sx = dsum[0], sxx = dsq[0];
+    float hx = dmx[0], lx = dmn[0];
 #pragma unroll
     for (int wv = 1; wv < NW; ++wv) {
-        v2 += dsq[wv];
-        am = max(am, dmax[wv]);
+        sx += dsum[wv];
+        sxx += dsq[wv];
+        hx = fmaxf(hx, dmx[wv]);
+        lx = fminf(lx, dmn[wv]);
     }
-    const float rs32 = float(1.0 / sqrt(v2 / double(K) + eps));
-    const float gamma = __uint_as_float(am) * rs32;
+    const double mu = sx / double(K);
+    const float mu32 = float(mu);
+    const double ex2 = sxx / double(K);
+    const double ve = fmax(ex2 - mu * mu, 0.0) + eps;
+    const double rd = 1.0 / sqrt(ve);
+    float rs32 = float(rd);
+    {
+        // rd's relative error bound, and its distance to the fl32 rounding
+        // boundaries around rs32 (the midpoints to its two neighbours)
+        const double rerr = (1.5 * double(K) + 4.0) * 0x1p-53 * ex2 / ve + 0x1p-50;
+        const double up = double(__uint_as_float(__float_as_uint(rs32) + 1u));
+        const double dn = double(__uint_as_float(__float_as_uint(rs32) - 1u));
+        const double r = double(rs32);
+        if (fmin(rd - 0.5 * (r + dn), 0.5 * (r + up) - rd) <= rd * rerr) {
+            double q2 = 0.0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                if (i * NT + tid >= pairs) continue;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const double d = double(v[i][c]) - mu;
+                    q2 += d * d;
+                }
+            }
+            q2 = wave_sum63(q2);
+            if (lane == 63) dsq2[wave] = q2;
+            __syncthreads();
+            double v2 = dsq2[0];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) v2 += dsq2[wv];
+            rs32 = float(1.0 / sqrt(v2 / double(K) + eps));
+        }
+    }
+    const float amx = fmaxf(fabsf(hx - mu32), fabsf(lx - mu32));
+    const float gamma = amx * rs32;
 
     // 3. codes into LDS in the decode layout, one dword per pair; zero
     //    padding rows K..Kp-1. Fast path u = h (Q_b rcp(gamma)) (Q_b is a power
@@ -382,7 +417,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float h = v[i][c] * rs32;
+                const float h = (i * NT + tid < pairs ? v[i][c] - mu32 : 0.0f) * rs32;   // fl32(fl32(x - mu32) rs32)
                 v[i][c] = h;
                 const float u = fminf(fmaxf(h * cq, -ucl), ucl);
                 slow |= fabsf(u - rintf(u)) < fabsf(u) * 0x1p-20f;
@@ -394,7 +429,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float h = v[i][c] * rs32;
+                const float h = (i * NT + tid < pairs ? v[i][c] - mu32 : 0.0f) * rs32;
                 v[i][c] = h;
                 const float u = fminf(fmaxf(h * cq, -ucl), ucl);
                 slow |= code_near_boundary(u, true);

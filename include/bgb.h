@@ -187,9 +187,12 @@ typedef struct {
  * the result of fbi_linear_w1a16(item.x, x_dtype, M, item.K, item.N, item.P,
  * item.alpha, alpha_dtype, item.y, y_dtype, ...). All items run in one
  * launch (each item split into column groups of its own, one per block) for a
- * single token (M = 1) with every K <= 16384, and for 2 <= M <= 16 tokens
+ * single token (M = 1) with every K <= 16384, for 2 <= M <= 16 tokens
  * when every item's tokens fit in LDS (about 140 KB for M (K + 136) 16-bit
- * values); otherwise they run one after another in the order given. Sums are accumulated in fp32 in a fixed order,
+ * values), and for 17 <= M <= 64 tokens (each item as 64-token x 256-column
+ * matrix-core tiles, its K range split into equal parts whose fp32 sums one
+ * reduce launch for the whole group adds in part order);
+ * otherwise they run one after another in the order given. Sums are accumulated in fp32 in a fixed order,
  * so results are the same from run to run; the one-launch form may group a
  * linear's K range differently from fbi_linear_w1a16 (a different rounding
  * order of the fp32 sum, not bit-identical to it).
@@ -198,8 +201,9 @@ typedef struct {
  * checked as fbi_linear_w1a16 checks its arguments. No output may overlap
  * any item's x, P, alpha or another item's y (the items may run
  * concurrently): BGB_EINVAL otherwise.
- * ws: bgb_group_workspace_bytes(items, count, M) bytes (0 for the one-launch
- * form, where ws may be NULL).
+ * ws: bgb_group_workspace_bytes(items, count, M) bytes (0 for the one- and
+ * few-token one-launch forms, where ws may be NULL; for 17 <= M <= 64 the
+ * parts' raw sums).
  * Errors: BGB_EINVAL, BGB_EUNSUPPORTED (dtypes), BGB_EHIP; a rejected call
  * launches nothing.
  */

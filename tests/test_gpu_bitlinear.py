@@ -185,3 +185,34 @@ def test_stage_api_token_scope(bgb_gpu, M, K, N):
     torch.cuda.synchronize()
     assert taps["gamma"].shape == (M,) and torch.equal(ex["gamma"], taps["gamma"])
     assert torch.equal(ex["q"], taps["q"]) and torch.equal(ex["acc"], acc2) and torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("kind", ["n01", "shift3", "shift1000", "near_const"])
+@pytest.mark.parametrize("K", [96, 4096, 16384])
+@pytest.mark.parametrize("x_kind", ["f32", "bf16"])
+def test_bitlinear_single_token_statistics_paths(bgb_gpu, orc, kind, K, x_kind):
+    """One token through the fused kernel. Its LayerNorm statistics take one
+    fp64 pass (sum x, sum x^2) and fall back to the two-pass variance when the
+    one-pass value could round differently in fp32: rows with a mean far from
+    zero (N(1000, 1)) and nearly constant rows take the fallback, N(0, 1) and
+    N(3, 0.5) rows the single pass. gamma, codes and acc must be bit-exact."""
+    say(f"bitlinear single token statistics {kind} K={K} x={x_kind}")
+    N = 200
+    seed = 1500 + K
+    W = syn.normal_f32(seed, 0, (K, N), mean=0.001, std=0.02)
+    xf = syn.normal_f32(seed, 1 + len(kind), (1, K))
+    if kind == "shift3":
+        xf = xf * np.float32(0.5) + np.float32(3.0)
+    elif kind == "shift1000":
+        xf = xf + np.float32(1000.0)
+    elif kind == "near_const":
+        xf = np.full((1, K), np.float32(0.37), np.float32)
+        xf[0, K // 3] = np.float32(0.375)
+    xf = np.ascontiguousarray(xf, np.float32)
+    if x_kind == "bf16":
+        xb = syn.f32_to_bf16_bits(xf)
+        x_host, x_dev = syn.bf16_bits_to_f32(xb), dev_bits16(xb, torch.bfloat16)
+    else:
+        x_host, x_dev = xf, dev_f32(xf)
+    y, y_ref = _run(bgb_gpu, orc, W, x_host, x_dev)
+    check_w1a8(y, y_ref, f"{kind} K={K}")

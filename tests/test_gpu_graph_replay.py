@@ -46,9 +46,10 @@ def test_graph_replays_match_eager(bgb_gpu, M, K):
 
 @pytest.mark.parametrize("M", [1, 4, 40])
 def test_graph_replays_group_and_backward(bgb_gpu, M):
-    """The group call (one launch at 1 and 4 tokens, item by item at 40) and the
-    FBI backward (split gradient, forward kernels, token sums, dW) replayed
-    from a graph: bit for bit equal to the eager calls on every replay."""
+    """The group call (one launch at 1 and 4 tokens; at 40 the grouped GEMM
+    and its reduce pass over the parts' sums in the workspace) and the FBI
+    backward (split gradient, forward kernels, token sums, dW) replayed from
+    a graph: bit for bit equal to the eager calls on every replay."""
     say(f"graph replay group + backward M={M}")
     shapes = [(1024, 512), (2048, 256), (512, 1024)]
     lin, Ps = [], []

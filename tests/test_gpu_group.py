@@ -156,3 +156,82 @@ def test_group_few_tokens_integer_bit_exact(bgb_gpu, orc):
     ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items])
     torch.cuda.synchronize()
     _check_items(orc, items, ys, "bf16", "f32", exact=True)
+
+
+# ---------------------------------------------------- 17 to 64 tokens ----
+# One launch of 64-token x 256-column matrix-core tiles per item, each item's
+# K range split into parts whose fp32 sums one reduce launch adds in part
+# order.
+GEMM_SHAPES = [(2048, 6144), (2048, 2048), (5632, 2048), (96, 65), (352, 300), (4000, 520), (11008, 40),
+               (1024, 8200)]
+
+
+@pytest.mark.parametrize("M", [17, 40, 64])
+@pytest.mark.parametrize("x_kind,adt,y_kind", [("bf16", "f16", "bf16"), ("f16", "f32", "f32"),
+                                               ("bf16", "f32", "f16")])
+def test_group_tokens_17_to_64_parity(bgb_gpu, orc, M, x_kind, adt, y_kind):
+    say(f"group M={M} {x_kind} alpha={adt} y={y_kind} shapes={GEMM_SHAPES}")
+    items = _items(bgb_gpu, GEMM_SHAPES, M, x_kind, adt, 1300 + M)
+    ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items], TORCH_DT[y_kind])
+    torch.cuda.synchronize()
+    _check_items(orc, items, ys, x_kind, y_kind)
+
+
+def test_group_tokens_17_to_64_integer_bit_exact(bgb_gpu, orc):
+    """Integer activations (|x| <= 16): every partial and split sum is exact
+    in fp32, so y = fl32(alpha S) bit for bit."""
+    say("group M=33 integer-exact")
+    items = _items(bgb_gpu, GEMM_SHAPES, 33, "bf16", "f32", 1400, int_x=True)
+    ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items])
+    torch.cuda.synchronize()
+    _check_items(orc, items, ys, "bf16", "f32", exact=True)
+
+
+def test_group_tokens_17_to_64_workspace_reuse(bgb_gpu, orc):
+    """One workspace (holding stale sums of another group between calls)
+    serves repeated calls: results are bit-identical from call to call."""
+    say("group M=64 workspace reuse")
+    shapes_a = [(2048, 6144), (2048, 2048), (2048, 11264), (5632, 2048)]
+    shapes_b = [(4096, 4096), (160, 1000)]
+    ia = _items(bgb_gpu, shapes_a, 64, "bf16", "f16", 1500)
+    ib = _items(bgb_gpu, shapes_b, 50, "bf16", "f16", 1600)
+    la = [(x, P, a, W.shape[1]) for (W, _, x, P, a) in ia]
+    lb = [(x, P, a, W.shape[1]) for (W, _, x, P, a) in ib]
+    ys_a = [torch.empty((64, W.shape[1]), dtype=torch.bfloat16, device="cuda") for (W, *_) in ia]
+    ys_b = [torch.empty((50, W.shape[1]), dtype=torch.bfloat16, device="cuda") for (W, *_) in ib]
+    need = max(bgb_gpu.group_workspace_bytes([(x, P, a, y) for (x, P, a, _), y in zip(la, ys_a)], 64),
+               bgb_gpu.group_workspace_bytes([(x, P, a, y) for (x, P, a, _), y in zip(lb, ys_b)], 50))
+    assert need > 0                                   # the plan splits K for these shapes
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")     # arbitrary prior contents
+    first = [y.clone() for y in bgb_gpu.fbi_linear_w1a16_group(la, ys=ys_a, ws=ws)]
+    bgb_gpu.fbi_linear_w1a16_group(lb, ys=ys_b, ws=ws)
+    for _ in range(3):
+        again = bgb_gpu.fbi_linear_w1a16_group(la, ys=ys_a, ws=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+    _check_items(orc, ia, first, "bf16", "bf16")
+    _check_items(orc, ib, ys_b, "bf16", "bf16")
+
+
+def test_group_1p3b_fused_layer_decode_b64(bgb_gpu, orc):
+    """The four same-input-fused linears of a 1.3B-shaped layer (qkv 2048 x
+    6144, o 2048 x 2048, gate_up 2048 x 11264, down 5632 x 2048) for 64 tokens
+    in one launch, as the decode benchmark runs them: 128 sampled columns of
+    each against the oracle, all 64 tokens."""
+    shapes = [(2048, 6144), (2048, 2048), (2048, 11264), (5632, 2048)]
+    say(f"group 1.3B fused layer M=64 shapes={shapes}")
+    lin, refs = [], []
+    for i, (K, N) in enumerate(shapes):
+        W = syn.normal_f32(1700 + i, 0, (K, N), std=0.02)
+        xb = _x_bits("bf16", 1700 + i, 64, K)
+        P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI, torch.float16)
+        a16 = orc.f32_to_f16(orc.fbi_alpha(W))
+        assert np.array_equal(alpha.detach().cpu().view(torch.int16).numpy().view(np.uint16), a16)
+        cols = np.sort(syn.rng_for(1700 + i, 3).choice(N, 128, replace=False))
+        refs.append((cols, orc.fbi_linear(xb, np.ascontiguousarray(W[:, cols]), orc.f16_to_f32(a16)[cols], "bf16")))
+        lin.append((dev_bits16(xb, torch.bfloat16), P, alpha, N))
+    ys = bgb_gpu.fbi_linear_w1a16_group(lin, torch.bfloat16)
+    torch.cuda.synchronize()
+    for (cols, ref), y in zip(refs, ys):
+        check_w1a16(to_bits(y)[:, cols], ref, "bf16", f"1.3B group N={y.shape[1]}")
