@@ -1,5 +1,6 @@
 // Device-side helpers shared by the kernels (gfx950, wave64).
 #pragma once
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -95,6 +96,12 @@ BGB_DEV double wave_sum63(double v) {
     v += dpp_f64<0x143, 0xC>(v);   // row_bcast31 into rows 2, 3
     return v;
 }
+// Sum of n (a power of two) values in a fixed pairwise tree order.
+template <int n>
+BGB_DEV double tree_sum(const double* a) {
+    if constexpr (n == 1) return a[0];
+    else return tree_sum<n / 2>(a) + tree_sum<n / 2>(a + n / 2);
+}
 BGB_DEV int wave_sum63_i(int v) {
     v += dpp_i32<0xB1, 0xF>(v);
     v += dpp_i32<0x4E, 0xF>(v);
@@ -117,6 +124,17 @@ BGB_DEV int round_code(float v, bool rne, int qmax) {
 BGB_DEV bool code_near_boundary(float u, bool rne) {
     const float d = __builtin_fabsf(u - __builtin_rintf(u));
     return (rne ? __builtin_fabsf(d - 0.5f) : d) < __builtin_fabsf(u) * 0x1p-20f;
+}
+
+// Order-preserving map of fp32 bit patterns onto uint32: for non-NaN x < y,
+// key(x) < key(y) (-0 sorts just below +0). Negative values are complemented,
+// non-negative ones get the top bit set.
+BGB_DEV uint32_t f32_sort_key(float x) {
+    const uint32_t b = __float_as_uint(x);
+    return b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u);
+}
+BGB_DEV float f32_from_sort_key(uint32_t k) {
+    return __uint_as_float(k ^ (~uint32_t(int32_t(k) >> 31) | 0x80000000u));
 }
 
 // Unsigned max over the 64 lanes, valid in lane 63 (0 is the identity).

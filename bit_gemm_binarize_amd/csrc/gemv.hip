@@ -257,7 +257,8 @@ constexpr int w1a8_d1_steps(int nv, int f) { return (nv * f + 1) / 2; }
 // P + TQ N 4 words; the product is sum_plus - sum_minus (no code row sum).
 template <int NV, int NW, int F, int IT, typename XT, bool kRne, bool kTern>
 __global__ void __launch_bounds__(NW * 64)
-bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t TQ, double eps, float qb, float lim,
+bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t N, int64_t TQ, double eps, float qb,
+                         float lim,
                          const uint32_t* __restrict__ P, const float* __restrict__ beta, float* __restrict__ y,
                          int32_t* __restrict__ acc_opt, int8_t* __restrict__ xq_opt,
                          float* __restrict__ gamma_opt) {
@@ -268,7 +269,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
     __shared__ i32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
     __shared__ double dsum[NW], dsq[NW], dsq2[NW];
-    __shared__ float dmx[NW], dmn[NW];
+    __shared__ uint32_t dmx[NW], dmn[NW];
     __shared__ int iscr[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
@@ -279,17 +280,18 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
 
     // 1. the token (an L2 hit after the first block): thread tid owns the
     //    pairs p = i * NT + tid, i.e. the rows of one dword of the decode
-    //    layout each. The loads complete before any sign tile is requested;
+    //    layout each. A pair past K loads rows 0, 8, 16, 24 instead (K is a
+    //    multiple of 32): real values of the row, so they may enter the
+    //    extremes unmasked; the sums take them as zeros, and their codes are
+    //    never stored. The loads complete before any sign tile is requested;
     //    the tiles are then in flight during the whole prologue.
     float v[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int p = i * NT + tid;
-        const bool ok = p < pairs;
-        const uint32_t keep = 0u - uint32_t(ok);      // masks (not selects): the loads stay unconditional
-        const int64_t k0 = ok ? int64_t(32 * (p >> 3) + (p & 7)) : 0;
+        const int64_t k0 = p < pairs ? int64_t(32 * (p >> 3) + (p & 7)) : 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[i][c] = __uint_as_float(__float_as_uint(load1(x, k0 + 8 * c)) & keep);
+        for (int c = 0; c < 4; ++c) v[i][c] = load1(x, k0 + 8 * c);
     }
     // beta is requested now, beside the token; it and the output pointers
     // (argument slots on a later cache line than the first ones) are pinned
@@ -311,7 +313,8 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. LayerNorm statistics; every block computes the same values. One pass
-    //    gives sum x and sum x^2 in fp64 (x^2 is exact there) and the row's
+    //    gives sum x and sum x^2 in fp64 (x^2 is exact there, so the fused
+    //    multiply-add rounds once, as a product and a sum would) and the row's
     //    extreme x. Var = E x^2 - (E x)^2 differs from the exact variance by
     //    at most dv = (3 K + 8) 2^-53 E x^2 (each sum's error is below
     //    K 2^-53 times its sum of magnitudes, |E x| E|x| <= E x^2, plus the
@@ -323,74 +326,93 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
     //    gamma = max |h| with h = fl32(fl32(x - mu32) rs32): rounding is
     //    monotone and sign-symmetric, so gamma = fl32(a rs32) with
     //    a = max |fl32(x - mu32)|, which sits at the largest or smallest x.
-    //    Pairs past K hold zeros: they add nothing to the sums and are left
-    //    out of the extremes.
+    //    The extremes travel as order-preserving integer keys (the minimum as
+    //    the maximum of complemented keys), one max per DPP step.
     double s1 = 0.0, s2 = 0.0;
-    float xmx = -__builtin_inff(), xmn = __builtin_inff();
+    float xmx = v[0][0], xmn = v[0][0];
+    auto pass1 = [&](auto masked) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const bool ok = i * NT + tid < pairs;
+        for (int i = 0; i < NV; ++i) {
+            const bool ok = !decltype(masked)::value || i * NT + tid < pairs;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const double d = double(v[i][c]);
-            s1 += d;
-            s2 += d * d;
-            xmx = ok ? fmaxf(xmx, v[i][c]) : xmx;
-            xmn = ok ? fminf(xmn, v[i][c]) : xmn;
+            for (int c = 0; c < 4; ++c) {
+                const double d = ok ? double(v[i][c]) : 0.0;
+                s1 += d;
+                s2 = __builtin_fma(d, d, s2);
+                xmx = fmaxf(xmx, v[i][c]);
+                xmn = fminf(xmn, v[i][c]);
+            }
         }
-    }
+    };
+    if (pairs >= NV * NT) pass1(std::false_type{});      // every pair inside K (uniform)
+    else pass1(std::true_type{});
     s1 = wave_sum63(s1);
     s2 = wave_sum63(s2);
-    xmx = wave_max63(xmx);
-    xmn = wave_min63(xmn);
+    const uint32_t kmx = wave_umax63(f32_sort_key(xmx));
+    const uint32_t kmn = wave_umax63(~f32_sort_key(xmn));
     if (lane == 63) {
         dsum[wave] = s1;
         dsq[wave] = s2;
-        dmx[wave] = xmx;
-        dmn[wave] = xmn;
+        dmx[wave] = kmx;
+        dmn[wave] = kmn;
     }
     __syncthreads();
     asm volatile("" ::"s"(beta0), "s"(y), "s"(acc_opt));
-    double sx = dsum[0], sxx = dsq[0];
-    float hx = dmx[0], lx = dmn[0];
+    const double sx = tree_sum<NW>(dsum), sxx = tree_sum<NW>(dsq);
+    uint32_t khx = dmx[0], klx = dmn[0];
 #pragma unroll
     for (int wv = 1; wv < NW; ++wv) {
-        sx += dsum[wv];
-        sxx += dsq[wv];
-        hx = fmaxf(hx, dmx[wv]);
-        lx = fminf(lx, dmn[wv]);
+        khx = max(khx, dmx[wv]);
+        klx = max(klx, dmn[wv]);
     }
-    const double mu = sx / double(K);
+    const float hx = f32_from_sort_key(khx), lx = f32_from_sort_key(~klx);
+    // the quotients by K correctly rounded without a division: q = sx rk
+    // with rk = fl(1/K) is within an ulp, and one correction with the exact
+    // remainder fma(-q, K, sx) gives the rounded quotient (Markstein)
+    const double kd = double(K);
+    const double q1 = sx * rk, q2 = sxx * rk;
+    const double mu = __builtin_fma(__builtin_fma(-q1, kd, sx), rk, q1);
     const float mu32 = float(mu);
-    const double ex2 = sxx / double(K);
+    const double ex2 = __builtin_fma(__builtin_fma(-q2, kd, sxx), rk, q2);
     const double ve = fmax(ex2 - mu * mu, 0.0) + eps;
-    const double rd = 1.0 / sqrt(ve);
-    float rs32 = float(rd);
+    // 1/sqrt(ve): the hardware estimate r0 and one third-order step,
+    // r = r0 (1 + e/2 + 3 e^2/8) with e = 1 - ve r0^2. Whatever r0's
+    // accuracy, the residual e1 = 1 - ve r^2 bounds r's relative error by
+    // 0.5000001 |e1| + 2^-52 while |e1| <= 2^-30; a larger residual (or a
+    // non-finite ve) counts as near a boundary and takes the second pass.
+    const double r0 = __builtin_amdgcn_rsq(ve);
+    const double e0 = __builtin_fma(-(ve * r0), r0, 1.0);
+    const double rd = __builtin_fma(r0 * e0, __builtin_fma(e0, 0.375, 0.5), r0);
+    const double e1 = fabs(__builtin_fma(-(ve * rd), rd, 1.0));
+    float rs32;
     {
-        // rd's relative error bound, and its distance to the fl32 rounding
-        // boundaries around rs32 (the midpoints to its two neighbours)
-        const double rerr = (1.5 * double(K) + 4.0) * 0x1p-53 * ex2 / ve + 0x1p-50;
-        const double up = double(__uint_as_float(__float_as_uint(rs32) + 1u));
-        const double dn = double(__uint_as_float(__float_as_uint(rs32) - 1u));
-        const double r = double(rs32);
-        if (fmin(rd - 0.5 * (r + dn), 0.5 * (r + up) - rd) <= rd * rerr) {
-            double q2 = 0.0;
+        // rd's relative error bound: the one-pass variance's (ex2 rd^2
+        // stands for ex2 / ve; the half-unit in the constant covers that),
+        // the refinement's, 2^-50 for the eps sum, and 2^-51 for forming the
+        // interval's ends. If both ends round to the same fp32 value, so
+        // does every point between them (rounding is monotone).
+        const double rerr = (1.5 * kd + 4.5) * 0x1p-53 * (ex2 * (rd * rd)) + 0.5000001 * e1 + (0x1p-50 + 0x1p-51);
+        const double dr = rd * rerr;
+        const float lo = float(rd - dr), hi = float(rd + dr);
+        rs32 = hi;
+        if (!(lo == hi && e1 <= 0x1p-30)) {
+            double q2s = 0.0;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 if (i * NT + tid >= pairs) continue;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const double d = double(v[i][c]) - mu;
-                    q2 += d * d;
+                    q2s += d * d;
                 }
             }
-            q2 = wave_sum63(q2);
-            if (lane == 63) dsq2[wave] = q2;
+            q2s = wave_sum63(q2s);
+            if (lane == 63) dsq2[wave] = q2s;
             __syncthreads();
             double v2 = dsq2[0];
 #pragma unroll
             for (int wv = 1; wv < NW; ++wv) v2 += dsq2[wv];
-            rs32 = float(1.0 / sqrt(v2 / double(K) + eps));
+            rs32 = float(1.0 / sqrt(v2 / kd + eps));
         }
     }
     const float amx = fmaxf(fabsf(hx - mu32), fabsf(lx - mu32));
@@ -417,9 +439,9 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float h = (i * NT + tid < pairs ? v[i][c] - mu32 : 0.0f) * rs32;   // fl32(fl32(x - mu32) rs32)
+                const float h = (v[i][c] - mu32) * rs32;        // fl32(fl32(x - mu32) rs32)
                 v[i][c] = h;
-                const float u = fminf(fmaxf(h * cq, -ucl), ucl);
+                const float u = __builtin_amdgcn_fmed3f(h * cq, -ucl, ucl);
                 slow |= fabsf(u - rintf(u)) < fabsf(u) * 0x1p-20f;
                 codes[i][c] = int(u);
             }
@@ -429,9 +451,9 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, int64_t N, int64_t
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float h = (i * NT + tid < pairs ? v[i][c] - mu32 : 0.0f) * rs32;
+                const float h = (v[i][c] - mu32) * rs32;
                 v[i][c] = h;
-                const float u = fminf(fmaxf(h * cq, -ucl), ucl);
+                const float u = __builtin_amdgcn_fmed3f(h * cq, -ucl, ucl);
                 slow |= code_near_boundary(u, true);
                 codes[i][c] = round_code(u, true, qmax);
             }
@@ -538,15 +560,16 @@ template <int NV, int NW, int F, typename XT, bool kTern>
 static void launch_w1a8_decode1_f(int it, unsigned grid, const XT* x, int64_t K, int64_t N, int64_t TQ, double eps,
                                   float qb, float lim, int rne, const uint32_t* P, const float* beta, float* y,
                                   int32_t* acc_opt, int8_t* xq_opt, float* gamma_opt, hipStream_t s) {
+    const double rk = 1.0 / double(K);
 #define BGB_D1X(ITV)                                                                                             \
     if (rne)                                                                                                     \
-        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, true, kTern><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb,  \
-                                                                                          lim, P, beta, y,      \
+        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, true, kTern><<<grid, NW * 64, 0, s>>>(x, K, rk, N, TQ, eps, \
+                                                                                          qb, lim, P, beta, y,  \
                                                                                           acc_opt, xq_opt,      \
                                                                                           gamma_opt);           \
     else                                                                                                         \
-        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, false, kTern><<<grid, NW * 64, 0, s>>>(x, K, N, TQ, eps, qb, \
-                                                                                           lim, P, beta, y,     \
+        bitlinear_decode1_kernel<NV, NW, F, ITV, XT, false, kTern><<<grid, NW * 64, 0, s>>>(x, K, rk, N, TQ, eps, \
+                                                                                           qb, lim, P, beta, y, \
                                                                                            acc_opt, xq_opt,     \
                                                                                            gamma_opt)
     if constexpr (w1a8_d1_ok<NV, NW, kTern>(F, 1)) {
