@@ -85,6 +85,27 @@ BGB_DEV void preload(u32x4_t* w, const uint32_t* P, int64_t base, int64_t stride
     }
 }
 
+// Tiles as preload() reads them, but never masked: a tile past the column's
+// last one, or of a column past N, is read from tile 0 of column 0 instead
+// (always in bounds). The caller pairs such steps with zero codes and never
+// stores such columns. One 64-bit lane address, wave-uniform strides (base and
+// stride must be wave-uniform), one select per tile.
+template <int S>
+BGB_DEV void preload_nomask(u32x4_t* w, const uint32_t* P, int base, int stride, int steps, int TQ, int64_t N,
+                            int64_t j, int g) {
+    const char* pb = reinterpret_cast<const char*>(P);
+    const char* lane0 = pb + ((int64_t(base) * 4 + g) * N + j) * 16;
+    const int64_t sb = int64_t(stride) * 64 * N;
+    const bool jok = j < N;
+    const int room = TQ - g;                           // tile 4 st + g exists iff 4 st < room
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        const int st = base + stride * i;
+        const bool ok = jok && st < steps && 4 * st < room;
+        w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ok ? lane0 + sb * i : pb));
+    }
+}
+
 // 16 bytes at p if ok, else zeros -- branch-free (p must be readable either way).
 template <typename V>
 BGB_DEV V ld16_or0(const V* p, bool ok) {
@@ -266,12 +287,12 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
     constexpr int KQ = NW / F;
     constexpr int S = w1a8_d1_steps(NV, F);
     static_assert(NW % F == 0 && IT * S * (kTern ? 2 : 1) <= kD1MaxTiles, "single-token W1A8 shape");
-    __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp];
+    __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp + 128];   // codes, then one zero tile
     __shared__ i32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
     __shared__ double dsum[NW], dsq[NW], dsq2[NW];
     __shared__ uint32_t dmx[NW], dmn[NW];
     __shared__ int iscr[NW];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
     const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
     const int Kp = int(TQ * 128);
@@ -300,15 +321,15 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
     // the stores.
     const float beta0 = beta[0];
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
-    // the sign tiles of all of this block's column groups (groups past the
-    // last one and columns past N load as zeros)
+    // the sign tiles of all of this block's column groups (unmasked: steps
+    // past the column's tiles meet the zero code tile, columns past N are
+    // never stored)
     u32x4_t w[IT][S], wn[kTern ? IT : 1][S];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
-        const int64_t jj = grp < ngroups ? grp * 16 * F + 16 * f + r : N;
-        preload<S>(w[it], P, kq, KQ, steps, TQ, N, jj, g);
-        if constexpr (kTern) preload<S>(wn[it], P + TQ * N * 4, kq, KQ, steps, TQ, N, jj, g);
+        const int64_t jj = (int64_t(blockIdx.x) + int64_t(it) * gridDim.x) * 16 * F + 16 * f + r;
+        preload_nomask<S>(w[it], P, kq, KQ, int(steps), int(TQ), N, jj, g);
+        if constexpr (kTern) preload_nomask<S>(wn[it], P + TQ * N * 4, kq, KQ, int(steps), int(TQ), N, jj, g);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -481,6 +502,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
         }
     }
     for (int k = int(K) + tid; k < Kp; k += NT) qs[q_pos(k)] = 0;
+    if (tid < 32) reinterpret_cast<uint32_t*>(qs + kFusedMaxKp)[tid] = 0u;
     if (gamma_opt && blockIdx.x == 0 && tid == 0) gamma_opt[0] = gamma;
     sq = wave_sum63_i(sq);
     if (lane == 63) iscr[wave] = sq;
@@ -493,9 +515,12 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
     const float scale = (beta0 * gamma) / qb;
+    // the B operand: lanes r != 0 never load it, and whatever their registers
+    // hold only reaches token columns that are never read (an empty asm
+    // defines the registers without spending instructions on zeros)
     i32x4_t bk[8];
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) bk[s8] = i32x4_t{0, 0, 0, 0};
+    for (int s8 = 0; s8 < 8; ++s8) asm volatile("" : "=v"(bk[s8]));
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
@@ -508,15 +533,15 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
             for (int s8 = 0; s8 < 8; ++s8) accn[s8] = i32x4_t{0, 0, 0, 0};
         }
         // only lanes r == 0 (token 0) read the codes: the other lanes' token
-        // columns are never read, so their B operand may hold anything (zeros
-        // at first, then whatever it held); steps past the column's tiles have
-        // all-zero signs. Reading for 4 lanes instead of 64 saves LDS return
-        // bandwidth.
+        // columns are never read, so their B operand may hold anything; steps
+        // past the column's tiles read the zero code tile, which cancels
+        // their unmasked signs. Reading for 4 lanes instead of 64 saves LDS
+        // return bandwidth.
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const int64_t st = kq + int64_t(KQ) * i;
-            const int64_t tq = st * 4 + g;
-            const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs + (st < steps && tq < TQ ? tq : 0) * 128);
+            const int st = kq + KQ * i, tq = st * 4 + g;
+            const i32x4_t* src =
+                reinterpret_cast<const i32x4_t*>(qs + (st < steps && tq < int(TQ) ? tq : kFusedMaxKp / 128) * 128);
             if (r == 0) {
 #pragma unroll
                 for (int s8 = 0; s8 < 8; ++s8) bk[s8] = src[s8];
