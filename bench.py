@@ -199,8 +199,13 @@ def traffic_bytes(kernel):
     rec = json.load(open(path)).get(kernel)
     if not rec:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    h = hashlib.sha256()
+    for rel in rec["sources"]:                   # the kernel's source file and the headers it includes
+        src = os.path.join(ROOT, rel)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
         return None
     return int(round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024))
 
