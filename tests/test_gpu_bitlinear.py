@@ -194,8 +194,10 @@ def test_bitlinear_single_token_statistics_paths(bgb_gpu, orc, kind, K, x_kind):
     """One token through the fused kernel. Its LayerNorm statistics take one
     fp64 pass (sum x, sum x^2) and fall back to the two-pass variance when the
     one-pass value could round differently in fp32: rows with a mean far from
-    zero (N(1000, 1)) and nearly constant rows take the fallback, N(0, 1) and
-    N(3, 0.5) rows the single pass. gamma, codes and acc must be bit-exact."""
+    zero (N(1000, 1)) always take the fallback (the one-pass error bound spans
+    several fp32 values there), nearly constant rows sit where the bound is a
+    fraction of an fp32 ulp, N(0, 1) and N(3, 0.5) rows take the single pass.
+    gamma, codes and acc must be bit-exact."""
     say(f"bitlinear single token statistics {kind} K={K} x={x_kind}")
     N = 200
     seed = 1500 + K
