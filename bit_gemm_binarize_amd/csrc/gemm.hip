@@ -176,6 +176,18 @@ BGB_DEV float alpha_at(const void* alpha, int alpha_f16, int64_t j) {
     return alpha_f16 ? f16_to_f32(static_cast<const uint16_t*>(alpha)[j]) : static_cast<const float*>(alpha)[j];
 }
 
+// alpha[jb..jb+3] (jb a multiple of 4, jb + 4 <= N), branch-free: two 8-byte
+// loads (the second repeats the first for f16, where 8 bytes hold all four).
+BGB_DEV void alpha4(const void* alpha, int alpha_f16, int64_t jb, float (&al)[4]) {
+    const char* ap = static_cast<const char*>(alpha) + (alpha_f16 ? 2 * jb : 4 * jb);
+    const uint2 u0 = *reinterpret_cast<const uint2*>(ap);
+    const uint2 u1 = *reinterpret_cast<const uint2*>(ap + (alpha_f16 ? 0 : 8));
+    al[0] = alpha_f16 ? f16_to_f32(uint16_t(u0.x)) : __uint_as_float(u0.x);
+    al[1] = alpha_f16 ? f16_to_f32(uint16_t(u0.x >> 16)) : __uint_as_float(u0.y);
+    al[2] = alpha_f16 ? f16_to_f32(uint16_t(u0.y)) : __uint_as_float(u1.x);
+    al[3] = alpha_f16 ? f16_to_f32(uint16_t(u0.y >> 16)) : __uint_as_float(u1.y);
+}
+
 // Four consecutive outputs jb..jb+3 of one token, o = m * N + jb.
 BGB_DEV void store_out16(void* y, int y_dtype, int64_t o, const float (&v)[4], bool full, int64_t jb, int64_t N) {
     if (full && y_dtype == kDtF32) {
@@ -475,6 +487,26 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) gemm_kernel(const GemmArgs a)
 
 // Sum of the splits in split order, then the epilogue. One thread per 4
 // consecutive columns of one token.
+// The K splits' raw sums of one thread's 4 outputs, 8 splits at a time: the
+// loads of a batch are in flight together, and the additions run in split
+// order (the same sequence as a plain loop). An index past the last split
+// re-reads the last one and is not added: branch-free, so the loads stay in
+// straight-line code (with a branch per load the compiler waits after each).
+template <typename V, typename T>
+BGB_DEV void load_splits8(V (&v)[8], const T* p, int z0, int splits, int64_t MN, int64_t o) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int z = z0 + q < splits ? z0 + q : splits - 1;
+        v[q] = *reinterpret_cast<const V*>(p + z * MN + o);
+    }
+}
+template <typename V>
+BGB_DEV void add_splits8(V& s, const V (&v)[8], int z0, int splits) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (z0 + q < splits) s += v[q];
+}
+
 template <bool kW1A8>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs a, int splits) {
     const int64_t M = a.M, N = a.N, nq = (N + 3) / 4;
@@ -486,29 +518,41 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs a, in
     if constexpr (kW1A8) {
         const int32_t* p = static_cast<const int32_t*>(a.part);
         i32x4_t s = {0, 0, 0, 0};
-        for (int z = 0; z < splits; ++z) {
-            if (full) {
-                s += *reinterpret_cast<const i32x4_t*>(p + z * MN + o);
-            } else {
+        if (full) {
+            i32x4_t v[8];
+            for (int z0 = 0; z0 < splits; z0 += 8) {
+                load_splits8(v, p, z0, splits, MN, o);
+                add_splits8(s, v, z0, splits);
+            }
+        } else {
+            for (int z = 0; z < splits; ++z)
                 for (int i = 0; i < 4; ++i)
                     if (jb + i < N) s[i] += p[z * MN + o + i];
-            }
         }
         store_out8(a, o, m, s, full, jb);
     } else {
         const float* p = static_cast<const float*>(a.part);
+        float al[4];
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-        for (int z = 0; z < splits; ++z) {
-            if (full) {
-                s += *reinterpret_cast<const f32x4_t*>(p + z * MN + o);
-            } else {
+        if (full) {
+            f32x4_t v[8];
+            load_splits8(v, p, 0, splits, MN, o);
+            alpha4(a.alpha, a.alpha_f16, jb, al);          // in flight with the first batch
+            add_splits8(s, v, 0, splits);
+            for (int z0 = 8; z0 < splits; z0 += 8) {
+                load_splits8(v, p, z0, splits, MN, o);
+                add_splits8(s, v, z0, splits);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = jb + i < N ? alpha_at(a.alpha, a.alpha_f16, jb + i) : 0.0f;
+            for (int z = 0; z < splits; ++z)
                 for (int i = 0; i < 4; ++i)
                     if (jb + i < N) s[i] += p[z * MN + o + i];
-            }
         }
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = jb + i < N ? alpha_at(a.alpha, a.alpha_f16, jb + i) * s[i] : 0.0f;
+        for (int i = 0; i < 4; ++i) v[i] = jb + i < N ? al[i] * s[i] : 0.0f;
         store_out16(a.y, a.y_dtype, o, v, full, jb, N);
     }
 }
@@ -607,18 +651,27 @@ __global__ void __launch_bounds__(256) group_reduce_kernel(const ReduceGroup g) 
     const int64_t m = id / nq, jb = 4 * (id % nq), o = m * N + jb;
     const bool full = jb + 4 <= N && (N & 3) == 0;
     const int64_t MN = M * N;
+    float al[4];
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < it.splits; ++z) {
-        if (full) {
-            s += *reinterpret_cast<const f32x4_t*>(it.part + z * MN + o);
-        } else {
+    if (full) {
+        f32x4_t v[8];
+        load_splits8(v, it.part, 0, it.splits, MN, o);
+        alpha4(it.alpha, g.alpha_f16, jb, al);              // in flight with the first batch
+        add_splits8(s, v, 0, it.splits);
+        for (int z0 = 8; z0 < it.splits; z0 += 8) {
+            load_splits8(v, it.part, z0, it.splits, MN, o);
+            add_splits8(s, v, z0, it.splits);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = jb + i < N ? alpha_at(it.alpha, g.alpha_f16, jb + i) : 0.0f;
+        for (int z = 0; z < it.splits; ++z)
             for (int i = 0; i < 4; ++i)
                 if (jb + i < N) s[i] += it.part[z * MN + o + i];
-        }
     }
     float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = jb + i < N ? alpha_at(it.alpha, g.alpha_f16, jb + i) * s[i] : 0.0f;
+    for (int i = 0; i < 4; ++i) v[i] = jb + i < N ? al[i] * s[i] : 0.0f;
     store_out16(it.y, g.y_dtype, o, v, full, jb, N);
 }
 
