@@ -1093,19 +1093,22 @@ fbi_decode1_group_kernel(const D1Group g) {
     for (int i = 1; i < kGroupMax; ++i)
         if (i < g.count && int(blockIdx.x) >= g.it[i].first) it = g.it[i];
     const int64_t bid = int64_t(blockIdx.x) - it.first;
-#define BGB_G1(C, NVV, FV)                                                                                      \
+#define BGB_G1(C, NVV, FV, ITV)                                                                                 \
     case C:                                                                                                  \
-        fbi_decode1_body<kF16, NVV, NW, FV, 1>(it.x, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y,    \
-                                               g.y_dtype, bid, it.nblk, xs, xzero, red, dX);                  \
+        fbi_decode1_body<kF16, NVV, NW, FV, ITV>(it.x, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y,  \
+                                                 g.y_dtype, bid, it.nblk, xs, xzero, red, dX);                \
         break;
     static_assert(kGroupSteps == 4, "the cases below are the shapes with NV F <= 4");
     switch (it.cfg) {
-        BGB_G1(0, 1, 1)
-        BGB_G1(1, 1, 2)
-        BGB_G1(2, 1, 4)
-        BGB_G1(3, 2, 1)
-        BGB_G1(4, 2, 2)
-        BGB_G1(5, 4, 1)
+        BGB_G1(0, 1, 1, 1)
+        BGB_G1(1, 1, 2, 1)
+        BGB_G1(2, 1, 4, 1)
+        BGB_G1(3, 2, 1, 1)
+        BGB_G1(4, 2, 2, 1)
+        BGB_G1(5, 4, 1, 1)
+        BGB_G1(6, 1, 4, 2)
+        BGB_G1(7, 2, 2, 2)
+        BGB_G1(8, 4, 1, 2)
         default: break;
     }
 #undef BGB_G1
@@ -1124,7 +1127,10 @@ hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f
     constexpr int NW = kD1Waves, NT = NW * 64;
     D1Group g{};
     int order[kGroupMax], n = 0;
-    int64_t cost[kGroupMax];
+    int nvps[kGroupMax], Fs[kGroupMax], ITs[kGroupMax];
+    int64_t frag[kGroupMax], cost[kGroupMax];
+    auto blocks = [&](int i) { return ((frag[i] + Fs[i] - 1) / Fs[i] + ITs[i] - 1) / ITs[i]; };
+    int64_t total_blocks = 0;
     for (int i = 0; i < count; ++i) {
         if (items[i].N <= 0) continue;                   // an empty linear takes no blocks
         const W1a16Item& in = items[i];
@@ -1137,15 +1143,39 @@ hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f
         d.N = in.N;
         d.TQ = tiles_per_col(in.K);
         const int nv = int((d.TQ * 16 + NT - 1) / NT);
-        const int nvp = nv <= 1 ? 1 : nv <= 2 ? 2 : 4;
-        const int64_t frags = (in.N + 15) / 16;
-        int F = 1;
-        while (nvp * 2 * F <= kGroupSteps && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
-        d.nblk = int((frags + F - 1) / F);
-        d.cfg = nvp == 1 ? (F == 1 ? 0 : F == 2 ? 1 : 2) : nvp == 2 ? (F == 1 ? 3 : 4) : 5;
-        cost[n] = int64_t(F) * d.TQ;
+        nvps[n] = nv <= 1 ? 1 : nv <= 2 ? 2 : 4;
+        frag[n] = (in.N + 15) / 16;
+        int F = 1;                                       // enough blocks for the linear alone to fill the chip
+        while (nvps[n] * 2 * F <= kGroupSteps && (frag[n] + F - 1) / F > kD1MaxGrid) F *= 2;
+        Fs[n] = F;
+        ITs[n] = 1;
+        total_blocks += blocks(n);
         order[n] = n;
         ++n;
+    }
+    // Every block stages its token and sums it before any product, so more
+    // blocks than the chip holds at once (two per CU) repeat that prologue in
+    // later rounds. Coarsen the linear with the most blocks (more fragments
+    // per group, then two groups per block) until they fit or none can grow.
+    while (total_blocks > 2 * kD1MaxGrid) {
+        int best = -1;
+        for (int i = 0; i < n; ++i) {
+            const bool grow = nvps[i] * Fs[i] * 2 <= kGroupSteps || ITs[i] == 1;
+            if (grow && (best < 0 || blocks(i) > blocks(best))) best = i;
+        }
+        if (best < 0) break;
+        total_blocks -= blocks(best);
+        if (nvps[best] * Fs[best] * 2 <= kGroupSteps) Fs[best] *= 2;
+        else ITs[best] = 2;
+        total_blocks += blocks(best);
+    }
+    for (int i = 0; i < n; ++i) {
+        D1Item& d = g.it[i];
+        const int F = Fs[i], nvp = nvps[i];
+        d.nblk = int(blocks(i));
+        if (ITs[i] == 1) d.cfg = nvp == 1 ? (F == 1 ? 0 : F == 2 ? 1 : 2) : nvp == 2 ? (F == 1 ? 3 : 4) : 5;
+        else d.cfg = nvp == 1 ? 6 : nvp == 2 ? 7 : 8;     // F = kGroupSteps / nvp, two groups per block
+        cost[i] = int64_t(F) * ITs[i] * d.TQ;
     }
     if (n == 0) return hipSuccess;
     // heaviest blocks first (stable), then the prefix sums of the block counts
