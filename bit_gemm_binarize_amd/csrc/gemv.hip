@@ -1548,7 +1548,14 @@ hipError_t launch_w1a16_decodem_group(const W1a16Item* items, int count, int64_t
     if (!w1a16_decodem_group_supported(items, count, M)) return hipErrorInvalidValue;
     DmGroup g{};
     int order[kGroupMax], n = 0;
-    int64_t cost[kGroupMax];
+    int Fs[kGroupMax];
+    int64_t cost[kGroupMax], frag[kGroupMax], stp[kGroupMax];
+    auto spw = [&](int i, int f) {                           // steps per wave, as the one-linear launcher
+        const int64_t need = (stp[i] + kDmWaves / f - 1) / (kDmWaves / f);
+        return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+    };
+    auto grows = [&](int i) { return 2 * Fs[i] <= kDmWaves && spw(i, 2 * Fs[i]) <= kD1MaxTiles; };
+    int64_t total_blocks = 0;
     for (int i = 0; i < count; ++i) {
         if (items[i].N <= 0) continue;
         const W1a16Item& in = items[i];
@@ -1560,21 +1567,36 @@ hipError_t launch_w1a16_decodem_group(const W1a16Item* items, int count, int64_t
         d.K = in.K;
         d.N = in.N;
         d.TQ = tiles_per_col(in.K);
-        const int64_t steps = (d.TQ + 3) / 4, frags = (in.N + 15) / 16;
-        auto spw = [&](int f) {                              // as the one-linear launcher
-            const int64_t need = (steps + kDmWaves / f - 1) / (kDmWaves / f);
-            return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
-        };
-        int F = 1;
-        while (2 * F <= kDmWaves && spw(2 * F) <= kD1MaxTiles && (frags + F - 1) / F > kD1MaxGrid) F *= 2;
-        const int S = spw(F);
-        if (S > kD1MaxTiles) return hipErrorInvalidValue;  // not reached: supported()
-        d.nblk = int((frags + F - 1) / F);
-        const bool tj = M * d.TQ >= kDmWaves * 64;          // whole tiles per thread, as the one-linear launcher
-        d.cfg = 16 * tj + 4 * (F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3) + (S == 1 ? 0 : S == 2 ? 1 : S == 4 ? 2 : 3);
-        cost[n] = int64_t(F) * d.TQ;
+        stp[n] = (d.TQ + 3) / 4;
+        frag[n] = (in.N + 15) / 16;
+        Fs[n] = 1;                                           // enough blocks for the linear alone to fill the chip
+        while (grows(n) && (frag[n] + Fs[n] - 1) / Fs[n] > kD1MaxGrid) Fs[n] *= 2;
+        total_blocks += (frag[n] + Fs[n] - 1) / Fs[n];
         order[n] = n;
         ++n;
+    }
+    // Every block stages all the tokens before any product and a block fills
+    // a CU's LDS, so a grid beyond one block per CU repeats that staging in
+    // later rounds: widen the groups of the linear with the most blocks until
+    // the grid fits or none can widen.
+    while (total_blocks > kD1MaxGrid) {
+        int best = -1;
+        for (int i = 0; i < n; ++i)
+            if (grows(i) && (best < 0 || (frag[i] + Fs[i] - 1) / Fs[i] > (frag[best] + Fs[best] - 1) / Fs[best]))
+                best = i;
+        if (best < 0) break;
+        total_blocks -= (frag[best] + Fs[best] - 1) / Fs[best];
+        Fs[best] *= 2;
+        total_blocks += (frag[best] + Fs[best] - 1) / Fs[best];
+    }
+    for (int i = 0; i < n; ++i) {
+        DmItem& d = g.it[i];
+        const int F = Fs[i], S = spw(i, F);
+        if (S > kD1MaxTiles) return hipErrorInvalidValue;  // not reached: supported()
+        d.nblk = int((frag[i] + F - 1) / F);
+        const bool tj = M * d.TQ >= kDmWaves * 64;          // whole tiles per thread, as the one-linear launcher
+        d.cfg = 16 * tj + 4 * (F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3) + (S == 1 ? 0 : S == 2 ? 1 : S == 4 ? 2 : 3);
+        cost[i] = int64_t(F) * d.TQ;
     }
     if (n == 0) return hipSuccess;
     for (int a = 1; a < n; ++a)
