@@ -219,8 +219,38 @@ int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, in
         return finish(one == 1 ? bgb::launch_w1a16_decode1_group(in, n, xf, af, ydt, s)
                                : bgb::launch_w1a16_decodem_group(in, n, M, xf, af, ydt, s));
     }
+    // Up to 16 tokens with some items too large for the one-launch form (the
+    // tokens do not fit in LDS whole): the others still go as one group
+    // launch when there are at least two of them, the rest one by one (the
+    // items are independent, so the order does not matter).
+    bool alone[BGB_GROUP_MAX] = {};
+    if (M <= 16) {
+        bgb::W1a16Item fit[BGB_GROUP_MAX];
+        int nf = 0;
+        for (int i = 0; i < count; ++i) {
+            if (!live[i]) continue;
+            const bool ok = M == 1 ? bgb::w1a16_decode1_supported(items[i].K)
+                                   : bgb::w1a16_decodem_supported(M, items[i].K);
+            if (ok)
+                fit[nf++] = bgb::W1a16Item{items[i].x, items[i].P, items[i].alpha, items[i].y, items[i].K,
+                                           items[i].N};
+            else
+                alone[i] = true;
+        }
+        if (nf >= 2) {
+            const int ydt = y_dtype == BGB_F32 ? 0 : (y_dtype == BGB_F16 ? 1 : 2);
+            const int xf = x_dtype == BGB_F16, af = alpha_dtype == BGB_F16;
+            rc = finish(M == 1 ? bgb::launch_w1a16_decode1_group(fit, nf, xf, af, ydt, s)
+                               : bgb::launch_w1a16_decodem_group(fit, nf, M, xf, af, ydt, s));
+            if (rc) return rc;
+        } else {
+            for (int i = 0; i < count; ++i) alone[i] = live[i];
+        }
+    } else {
+        for (int i = 0; i < count; ++i) alone[i] = live[i];
+    }
     for (int i = 0; i < count; ++i) {
-        if (!live[i]) continue;
+        if (!alone[i]) continue;
         const bgb_w1a16_item& it = items[i];
         rc = fbi_run(it.x, x_dtype, M, it.K, it.N, it.P, it.alpha, alpha_dtype, it.y, y_dtype, ws, s);
         if (rc) return rc;

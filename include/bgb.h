@@ -191,8 +191,10 @@ typedef struct {
  * when every item's tokens fit in LDS (about 140 KB for M (K + 136) 16-bit
  * values), and for 17 <= M <= 64 tokens (each item as 64-token x 256-column
  * matrix-core tiles, its K range split into equal parts whose fp32 sums one
- * reduce launch for the whole group adds in part order);
- * otherwise they run one after another in the order given. Sums are accumulated in fp32 in a fixed order,
+ * reduce launch for the whole group adds in part order). Up to 16 tokens,
+ * when some items do not fit those limits, the others (if at least two) run
+ * as one launch and the rest one after another in the order given; beyond
+ * that, all run one after another. Sums are accumulated in fp32 in a fixed order,
  * so results are the same from run to run; the one-launch form may group a
  * linear's K range differently from fbi_linear_w1a16 (a different rounding
  * order of the fp32 sum, not bit-identical to it).

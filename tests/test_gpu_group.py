@@ -123,9 +123,32 @@ def test_group_7b_layer_sampled_columns(bgb_gpu, orc):
         check_w1a16(to_bits(y)[:, cols], ref, "bf16", f"7B group N={y.shape[1]}")
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_group_7b_layer_batches_sampled_columns(bgb_gpu, orc, M):
+    """The 7B layer's fused linears at 1, 4 and 16 tokens as the decode
+    benchmark runs them (at 16 tokens the down projection's tokens do not fit
+    in LDS: the other three run as one launch, down alone): 64 sampled columns
+    of each item against the oracle."""
+    shapes = [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)]
+    say(f"group 7B layer M={M}")
+    lin, refs = [], []
+    for i, (K, N) in enumerate(shapes):
+        W = syn.normal_f32(950 + i, 0, (K, N), std=0.02)
+        xb = _x_bits("bf16", 950 + i + M, M, K)
+        P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI, torch.float16)
+        cols = np.sort(syn.rng_for(950 + i, 3).choice(N, 64, replace=False))
+        a_host = alpha.detach().float().cpu().numpy().astype(np.float32)
+        refs.append((cols, orc.fbi_linear(xb, np.ascontiguousarray(W[:, cols]), a_host[cols], "bf16")))
+        lin.append((dev_bits16(xb, torch.bfloat16), P, alpha, N))
+    ys = bgb_gpu.fbi_linear_w1a16_group(lin, torch.bfloat16)
+    torch.cuda.synchronize()
+    for (cols, ref), y in zip(refs, ys):
+        check_w1a16(to_bits(y)[:, cols], ref, "bf16", f"7B group M={M} N={y.shape[1]}")
+
+
 def test_group_single_token_beyond_fused_size(bgb_gpu, orc):
-    """One item with K beyond the fused single-token size: the whole group
-    runs item by item (the chunked decode for that one)."""
+    """One item with K beyond the fused single-token size: the other two run
+    as one launch, that one alone (the chunked decode)."""
     shapes = [(768, 300), (16416, 40), (4096, 100)]
     say(f"group M=1 sequential shapes={shapes}")
     items = _items(bgb_gpu, shapes, 1, "bf16", "f32", 1000)
@@ -139,8 +162,8 @@ def test_group_few_tokens_every_shape(bgb_gpu, orc, M):
     """A few tokens over shapes that take (fragments per block, steps per wave)
     = (8, 8), (4, 4), (4, 1), (2, 4), (2, 2), (1, 4), (1, 1), with ragged N,
     in one launch for M = 2 and 3 (the 12288-row item staging whole tiles at
-    M = 3); at M = 8 that item's tokens do not fit in LDS, so the group runs
-    item by item."""
+    M = 3); at M = 8 that item's tokens do not fit in LDS, so the other items
+    run as one launch and that one alone."""
     shapes = [(4096, 22016), (4096, 12288), (1024, 8200), (8192, 5000), (4096, 5000), (12288, 100), (96, 65),
               (2048, 300)]
     say(f"group M={M} few-token shapes={shapes}")
