@@ -29,21 +29,29 @@ pack_signs_kernel(const float* __restrict__ W, int64_t K, int64_t N, uint32_t* _
     const int64_t tq = blockIdx.y;
     if (j >= N) return;
     const int64_t T = K / 32;
+    // W > c exactly (BitNet): on order keys, false when either side is NaN;
+    // the centre's key and NaN test are computed once
     const float c = kBitnet ? centre[0] : 0.0f;
+    const uint32_t kc = f32_order_key(c);
+    const bool cnan = f32_is_nan(c);
     uint32_t words[4];
     double s = 0.0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const int64_t t = tq * 4 + w;
         uint32_t word = 0;
-        if (t < T) {
+        if (t < T) {                                   // uniform: t depends on the block only
+            // the word's 32 loads are issued before any of them is used
             const float* col = W + (32 * t) * N + j;
-#pragma unroll 8
+            float v[32];
+#pragma unroll
+            for (int b = 0; b < 32; ++b) v[b] = __builtin_nontemporal_load(col + int64_t(b) * N);
+#pragma unroll
             for (int b = 0; b < 32; ++b) {
-                const float v = __builtin_nontemporal_load(col + int64_t(b) * N);
-                const bool pos = kBitnet ? f32_gt_exact(v, c) : f32_gt_zero(v);
+                const bool pos = kBitnet ? (!f32_is_nan(v[b]) & !cnan & (f32_order_key(v[b]) > kc))
+                                         : f32_gt_zero(v[b]);
                 word |= uint32_t(pos) << b;
-                if (!kBitnet) s += fabs(double(v));
+                if (!kBitnet) s += fabs(double(v[b]));
             }
         }
         words[w] = word;
@@ -69,11 +77,14 @@ pack_ternary_kernel(const float* __restrict__ W, int64_t K, int64_t N, uint32_t*
     for (int w = 0; w < 4; ++w) {
         const int64_t t = tq * 4 + w;
         uint32_t wp = 0, wn = 0;
-        if (t < T) {
+        if (t < T) {                                   // uniform: t depends on the block only
             const float* col = W + (32 * t) * N + j;
-#pragma unroll 8
+            float v[32];                               // the word's 32 loads in flight together
+#pragma unroll
+            for (int b = 0; b < 32; ++b) v[b] = __builtin_nontemporal_load(col + int64_t(b) * N);
+#pragma unroll
             for (int b = 0; b < 32; ++b) {
-                const float r = __builtin_rintf(__builtin_nontemporal_load(col + int64_t(b) * N) / den);
+                const float r = __builtin_rintf(v[b] / den);
                 wp |= uint32_t(r >= 1.0f) << b;
                 wn |= uint32_t(r <= -1.0f) << b;
             }
@@ -92,7 +103,14 @@ fbi_alpha_kernel(const double* __restrict__ colsum, int64_t TQ, int64_t N, int64
     const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (j >= N) return;
     double s = 0.0;
-    for (int64_t tq = 0; tq < TQ; ++tq) s += colsum[tq * N + j];
+    for (int64_t t0 = 0; t0 < TQ; t0 += 8) {       // 8 loads in flight, added in tile order
+        double v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = colsum[(t0 + q < TQ ? t0 + q : TQ - 1) * N + j];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (t0 + q < TQ) s += v[q];
+    }
     const float a = float(s / double(K));
     if (alpha_f16) reinterpret_cast<uint16_t*>(alpha)[j] = f32_to_f16_rne(a);
     else reinterpret_cast<float*>(alpha)[j] = a;
