@@ -20,10 +20,13 @@
 // DMA operations a stage issues.
 //
 // LDS layout of a stage: token row t at t*128 bytes, its eight 16-byte chunks
-// XOR-swizzled by a function of bits 2..3 of t, so that the B-operand reads of
-// a wave (W1A8: 16 token rows x 4 chunks of 16 bytes; W1A16: 16 rows x 4
-// pieces of 8 bytes) fall on distinct banks of gfx950's 128-bank LDS. The DMA writes lane L of an instruction to chunk
-// base+L, so the swizzle is applied by choosing the source chunk per lane.
+// XOR-swizzled by a function of bits 1..3 of t, so that the 16-byte B-operand
+// reads of every 16 consecutive lanes hit 16 distinct 16-byte bank groups of
+// 256 bytes, and those of every 32 lanes 32 distinct groups of 512 bytes (a
+// swizzle on bits 2..3 alone left two-way conflicts within 16 lanes:
+// SQ_LDS_BANK_CONFLICT read half of SQ_LDS_IDX_ACTIVE). The DMA writes lane L
+// of an instruction to chunk base+L, so the swizzle is applied by choosing the
+// source chunk per lane.
 //
 // Sign decoding (A operand, rows = output columns), per MFMA:
 // * W1A16: lane group g takes word g>>1 of the stage and, for MFMA half v,
@@ -72,10 +75,13 @@ BGB_DEV void dma16(const void* src, uint8_t* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
 
-// Chunk swizzles of a stage row (see the header comment); both are
-// involutions on 0..7 and depend only on bits 2..3 of the token row.
-BGB_DEV int swz16(int t) { return 2 * ((t >> 2) & 3); }
-BGB_DEV int swz8(int t) { return ((t >> 2) & 1) | (((t >> 3) & 1) << 2); }
+// Chunk swizzles of a stage row (see the header comment): XOR masks in 0..7
+// from bits 1..3 of the token row. Over the 8 rows of one parity each takes
+// all 8 values (16-lane passes); over the 4 rows of one residue mod 4 each
+// takes one value from each coset of the chunk pair a half-wave reads ({c,
+// c^2} for W1A8, {c, c^1} for W1A16: 32-lane passes).
+BGB_DEV int swz16(int t) { return (2 * ((t >> 2) & 3)) | ((t >> 1) & 1); }
+BGB_DEV int swz8(int t) { return (((t >> 2) & 1) | (((t >> 3) & 1) << 2)) ^ (t & 2); }
 
 // The sign bits a W1A16 lane needs from a 32-row word w, placed for the
 // decode: with sel picking bytes (h, h + 2, h, h + 2) of w (rows 8h..8h+7 and
