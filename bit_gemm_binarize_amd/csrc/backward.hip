@@ -186,6 +186,13 @@ dalpha_sum_kernel(const double* __restrict__ part, int64_t chunks, int64_t N, fl
 // and the one after it is loaded. Tokens past M and features past K or N
 // read as zeros.
 constexpr int kDwChunk = 64, kDwRow = kDwChunk + 8;   // LDS row: 64 tokens + 16 bytes
+// The 8 token slots (16 bytes each) of a row are XOR-swizzled by bits 4..6 of
+// the row: a store instruction writes rows 8 apart across its lanes (one
+// feature of each lane's 8 x 8 block), which the 16-byte padding alone maps
+// onto two 16-byte bank groups per 256 bytes; with the swizzle every 16
+// consecutive lanes hit 16 distinct groups, and the reads (16 consecutive
+// rows, one slot) stay distinct too.
+BGB_DEV int dw_swz(int row) { return (row >> 4) & 7; }
 
 // T: the square output tile (128 or 256), 2 T threads (T / 32 waves); wave w
 // takes 64 j x 64 BI i (BI = T / 128): 4 x 4 BI MFMA fragments.
@@ -228,7 +235,8 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
             o.y = __builtin_amdgcn_perm(v[3][f >> 1], v[2][f >> 1], sel);
             o.z = __builtin_amdgcn_perm(v[5][f >> 1], v[4][f >> 1], sel);
             o.w = __builtin_amdgcn_perm(v[7][f >> 1], v[6][f >> 1], sel);
-            *reinterpret_cast<u32x4_t*>(tile + (8 * fb + f) * kDwRow + 8 * mb) = o;
+            const int row = 8 * fb + f;
+            *reinterpret_cast<u32x4_t*>(tile + row * kDwRow + 8 * (mb ^ dw_swz(row))) = o;
         }
     };
 
@@ -255,11 +263,15 @@ dw_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy, int64
         for (int ks = 0; ks < kDwChunk / 32; ++ks) {
             u32x4_t av[4], bv[4 * BI];
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
-                av[f] = *reinterpret_cast<const u32x4_t*>(gb + (wj + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
+            for (int f = 0; f < 4; ++f) {
+                const int row = wj + 16 * f + r;
+                av[f] = *reinterpret_cast<const u32x4_t*>(gb + row * kDwRow + 8 * ((4 * ks + g) ^ dw_swz(row)));
+            }
 #pragma unroll
-            for (int f = 0; f < 4 * BI; ++f)
-                bv[f] = *reinterpret_cast<const u32x4_t*>(xb + (wi + 16 * f + r) * kDwRow + 32 * ks + 8 * g);
+            for (int f = 0; f < 4 * BI; ++f) {
+                const int row = wi + 16 * f + r;
+                bv[f] = *reinterpret_cast<const u32x4_t*>(xb + row * kDwRow + 8 * ((4 * ks + g) ^ dw_swz(row)));
+            }
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
