@@ -69,21 +69,37 @@ MALL_FLUSH_BYTES = 1 << 30          # read before a timed region: 4x the 256 MB 
 _flush_buf = None
 
 
-def flush_mall(torch):
-    """Stream 1 GiB through the memory-side cache (a read-only reduction), so
-    that nothing a timed region reads is left in the 256 MB MALL or the L2s."""
+def flush_buffer(torch):
+    """The 1 GiB buffer flush_mall reads, allocated on first use."""
     global _flush_buf
     if _flush_buf is None:
         _flush_buf = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-    _flush_buf.sum()
+        torch.cuda.synchronize()
+    return _flush_buf
+
+
+def flush_mall(torch):
+    """Stream 1 GiB through the memory-side cache (a read-only reduction), so
+    that nothing a timed region reads is left in the 256 MB MALL or the L2s."""
+    flush_buffer(torch).sum()
     torch.cuda.synchronize()
 
 
+GRAPH_WARM_S = 0.1                  # untimed replays before a timed one: at least this much GPU work
+
+
 def graph_time(torch, body, steps, warmup, flush=True):
-    """Capture `steps` calls of body(i) into one HIP graph; replay once untimed
-    (warm-up, also `warmup` eager calls before capture), stream 1 GiB through
-    the MALL (flush=True), then replay once timed.
+    """Capture `steps` calls of body(i) into one HIP graph; replay it untimed
+    until at least GRAPH_WARM_S has passed (warm-up, also `warmup` eager calls
+    before capture), stream 1 GiB through the MALL (flush=True), then replay
+    once timed. The clocks climb for some milliseconds after an idle spell: a
+    3 ms window of prefill GEMMs read up to 25% slow right after one idle
+    second, and the same at any length once the GPU had been busy for 50 ms.
+    The flush buffer is allocated before the warm-up, so that no idle spell
+    falls between the warm-up and the timed replay.
     Returns milliseconds for the timed replay."""
+    if flush:
+        flush_buffer(torch)
     for i in range(warmup):
         body(i)
     torch.cuda.synchronize()
@@ -91,8 +107,12 @@ def graph_time(torch, body, steps, warmup, flush=True):
     with torch.cuda.graph(g):
         for i in range(steps):
             body(i)
+    t0 = time.perf_counter()
     g.replay()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < GRAPH_WARM_S:
+        g.replay()
+        torch.cuda.synchronize()
     if flush:
         flush_mall(torch)
     e0 = torch.cuda.Event(enable_timing=True)
