@@ -215,12 +215,18 @@ BGB_DEV void store_out16(void* y, int y_dtype, int64_t o, const float (&v)[4], b
     }
 }
 
-BGB_DEV void store_out8(const GemmArgs& a, int64_t o, int64_t m, const i32x4_t& s, bool full, int64_t jb) {
-    const float scale = (a.beta[0] * a.gamma[m * a.gstride]) / a.qb;
-    const int32_t rs = a.tern ? 0 : a.rowsum[m];
+// The W1A8 epilogue's per-token factors: beta gamma_m / Q_b and the code row
+// sum of token m (0 for ternary weights).
+BGB_DEV void epi8_token(const GemmArgs& a, bool tern, int64_t m, float& scale, int32_t& rs) {
+    scale = (a.beta[0] * a.gamma[m * a.gstride]) / a.qb;
+    rs = tern ? 0 : a.rowsum[m];
+}
+
+BGB_DEV void store_out8(const GemmArgs& a, bool tern, int64_t o, const i32x4_t& s, float scale, int32_t rs,
+                        bool full, int64_t jb) {
     i32x4_t v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = a.tern ? s[i] : 2 * s[i] - rs;   // binary: 2 sum b q - sum q
+    for (int i = 0; i < 4; ++i) v[i] = tern ? s[i] : 2 * s[i] - rs;     // binary: 2 sum b q - sum q
     float* y = static_cast<float*>(a.y);
     if (full) {
         *reinterpret_cast<f32x4_t*>(y + o) =
@@ -446,16 +452,37 @@ BGB_DEV void gemm_tile(const GemmArgs& a, const int tile, const int z) {
 #pragma unroll
             for (int n = 0; n < NN; ++n) acc[f][n] -= accn[f][n];
     }
-    // Epilogue: lane (g, r) holds columns jb..jb+3 of token 16n + r.
+    // Epilogue: lane (g, r) holds columns jb..jb+3 of token 16n + r. Every
+    // load it needs (alpha of the lane's 16 columns, or the NN tokens' scale
+    // and row sum) is issued before its first store: a wait for a load also
+    // waits for every store issued before it, so loads between the stores
+    // would make each group of stores wait for the previous one to land.
+    float al[4][4], sc[NN];
+    int32_t rsum[NN];
+    if (!a.part) {
+        if constexpr (kW1A8) {
+#pragma unroll
+            for (int n = 0; n < NN; ++n) {
+                const int64_t m = m0 + 16 * n + r;
+                epi8_token(a, kTern, m < M ? m : M - 1, sc[n], rsum[n]);   // kTern is a.tern here
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int64_t jb = j0 + 64 * wave + 16 * f + 4 * g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = alpha_at(a.alpha, a.alpha_f16, jb + i < N ? jb + i : N - 1);
+                    al[f][i] = jb + i < N ? v : 0.0f;
+                }
+            }
+        }
+        wait_vmcnt<0>();                        // (the compiler's own waits would sit between the stores)
+    }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
         const int64_t jb = j0 + 64 * wave + 16 * f + 4 * g;
         const bool full = jb + 4 <= N && (N & 3) == 0;
-        float al[4] = {0.f, 0.f, 0.f, 0.f};
-        if (!kW1A8 && !a.part) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = jb + i < N ? alpha_at(a.alpha, a.alpha_f16, jb + i) : 0.0f;
-        }
 #pragma unroll
         for (int n = 0; n < NN; ++n) {
             const int64_t m = m0 + 16 * n + r;
@@ -474,10 +501,10 @@ BGB_DEV void gemm_tile(const GemmArgs& a, const int tile, const int z) {
                     }
                 }
             } else if constexpr (kW1A8) {
-                store_out8(a, o, m, acc[f][n], full, jb);
+                store_out8(a, kTern, o, acc[f][n], sc[n], rsum[n], full, jb);
             } else {
-                const float v[4] = {al[0] * acc[f][n][0], al[1] * acc[f][n][1], al[2] * acc[f][n][2],
-                                    al[3] * acc[f][n][3]};
+                const float v[4] = {al[f][0] * acc[f][n][0], al[f][1] * acc[f][n][1], al[f][2] * acc[f][n][2],
+                                    al[f][3] * acc[f][n][3]};
                 store_out16(a.y, a.y_dtype, o, v, full, jb, N);
             }
         }
@@ -523,6 +550,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs a, in
     const int64_t MN = M * N;
     if constexpr (kW1A8) {
         const int32_t* p = static_cast<const int32_t*>(a.part);
+        float scale;
+        int32_t rs;
+        epi8_token(a, a.tern, m, scale, rs);                // in flight with the first batch
         i32x4_t s = {0, 0, 0, 0};
         if (full) {
             i32x4_t v[8];
@@ -535,7 +565,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs a, in
                 for (int i = 0; i < 4; ++i)
                     if (jb + i < N) s[i] += p[z * MN + o + i];
         }
-        store_out8(a, o, m, s, full, jb);
+        store_out8(a, a.tern, o, s, scale, rs, full, jb);
     } else {
         const float* p = static_cast<const float*>(a.part);
         float al[4];
