@@ -148,6 +148,59 @@ BGB_DEV void w1a8_step(const u32x4_t& w, const i32x4_t* b, i32x4_t* acc) {
     acc[7] = w1a8_mfma<7>(w, b[7], acc[7]);
 }
 
+// Single-token W1A8 product on the fp4 (e2m1) matrix cores, 16 x 16 x 128.
+// A holds signs as fp4 nibbles. MFMA type p (0..3) takes bit 4n + p of each of
+// the tile's four words into nibble n of the matching dword (rows 32d + 4n + p
+// of the tile, d = the word). Type 3 leaves the bit where it is, the sign
+// field of 1.0: a set bit gives +1, a clear one -1. Types 0..2 keep the bit as
+// the only set field bit of the nibble, 0.5, 1.0 or 2.0 times b (b = 1 for
+// +1), so sum_k s q = 2 sum_k b q - sum_k q over those rows. B holds a code q
+// as four base-4 digits of |q|, one per token column 0..3 (nibble codes 0..3
+// are the fp4 values 0, 0.5, 1, 1.5, so column c carries digit / 2) with q's
+// sign in bit 3. Every product and partial sum is a multiple of 1/4 below
+// 2^22, so the fp32 accumulators hold them exactly.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+template <int P>
+BGB_DEV i32x4_t f4_signs(const u32x4_t& w) {
+    if constexpr (P == 3) {   // (~w & 0x88888888) | 0x22222222: +-1.0 per nibble (truth table 0xAE)
+        return i32x4_t{int(__builtin_amdgcn_bitop3_b32(w.x, 0x88888888u, 0x22222222u, 0xAE)),
+                       int(__builtin_amdgcn_bitop3_b32(w.y, 0x88888888u, 0x22222222u, 0xAE)),
+                       int(__builtin_amdgcn_bitop3_b32(w.z, 0x88888888u, 0x22222222u, 0xAE)),
+                       int(__builtin_amdgcn_bitop3_b32(w.w, 0x88888888u, 0x22222222u, 0xAE))};
+    } else {
+        constexpr uint32_t m = 0x11111111u << P;
+        return i32x4_t{int(w.x & m), int(w.y & m), int(w.z & m), int(w.w & m)};
+    }
+}
+BGB_DEV f32x4_t mfma_f4(const i32x4_t& a, const i32x4_t& b, const f32x4_t& c) {
+    const i32x8_t a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};   // fp4 operands use the first four dwords
+    const i32x8_t b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, 127, 0, 127);   // scales 2^0
+}
+// One 512-row step: the four types against the lane's digit operands b[p].
+BGB_DEV void w1a8_f4_step(const u32x4_t& w, const i32x4_t* b, f32x4_t* acc) {
+    acc[0] = mfma_f4(f4_signs<0>(w), b[0], acc[0]);
+    acc[1] = mfma_f4(f4_signs<1>(w), b[1], acc[1]);
+    acc[2] = mfma_f4(f4_signs<2>(w), b[2], acc[2]);
+    acc[3] = mfma_f4(f4_signs<3>(w), b[3], acc[3]);
+}
+// Per lane (digit column r of output rows 4g..4g+3): 2 sum b q over types 0..2
+// plus sum s q over type 3, for digit r, scaled by its weight 4^r; then summed
+// over the quad of digit columns 0..3. Exact (integers below 2^24).
+BGB_DEV i32x4_t w1a8_f4_combine(const f32x4_t* acc, int r) {
+    const f32x4_t z = ((8.0f * acc[0] + 4.0f * acc[1]) + 2.0f * acc[2]) + 2.0f * acc[3];
+    const float wt = r < 4 ? float(1 << (2 * r)) : 0.0f;
+    i32x4_t t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = z[i] * wt;
+        v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+        v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+        t[i] = int(v);
+    }
+    return t;
+}
+
 // sum_k b q from the 8 shift accumulators (each division by 2^s is exact).
 BGB_DEV i32x4_t w1a8_combine(const i32x4_t* acc) {
     i32x4_t t;
@@ -287,7 +340,11 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
     constexpr int KQ = NW / F;
     constexpr int S = w1a8_d1_steps(NV, F);
     static_assert(NW % F == 0 && IT * S * (kTern ? 2 : 1) <= kD1MaxTiles, "single-token W1A8 shape");
-    __shared__ __attribute__((aligned(16))) int8_t qs[kFusedMaxKp + 128];   // codes, then one zero tile
+    // binary weights with two or more code dwords per thread: the fp4 product
+    // (a thread then owns octets of rows instead of pairs, see below)
+    constexpr bool kF4 = !kTern && NV % 2 == 0;
+    // codes (int8: 128 B per 128-row tile; fp4 digits: 256 B), then one zero tile
+    __shared__ __attribute__((aligned(16))) int8_t qs[(kF4 ? 2 : 1) * (kFusedMaxKp + 128)];
     __shared__ i32x4_t red[KQ > 1 ? 2 : 1][KQ > 1 ? NW : 1][64];
     __shared__ double dsum[NW], dsq[NW], dsq2[NW];
     __shared__ uint32_t dmx[NW], dmn[NW];
@@ -298,6 +355,11 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
     const int Kp = int(TQ * 128);
     const int64_t steps = (TQ + 3) / 4;
     const int pairs = int(K / 4);                      // (t, s): rows 32t + s + 8c, c = 0..3
+    // fp4 form: octet o = (t, p) = (o / 4, o % 4) holds rows 32t + p + 4n,
+    // n = 0..7; thread tid owns octets h NT + tid, h < NV / 2, and v[2h + e][c]
+    // holds n = 2c + e
+    const int octets = int(K / 8);
+    auto valid = [&](int i) { return kF4 ? (i >> 1) * NT + tid < octets : i * NT + tid < pairs; };
 
     // 1. the token (an L2 hit after the first block): thread tid owns the
     //    pairs p = i * NT + tid, i.e. the rows of one dword of the decode
@@ -309,8 +371,14 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
     float v[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int p = i * NT + tid;
-        const int64_t k0 = p < pairs ? int64_t(32 * (p >> 3) + (p & 7)) : 0;
+        int64_t k0;
+        if constexpr (kF4) {
+            const int o = (i >> 1) * NT + tid;       // an octet past K loads rows 4e + 8c of word 0
+            k0 = int64_t(o < octets ? 32 * (o >> 2) + (o & 3) : 0) + 4 * (i & 1);
+        } else {
+            const int p = i * NT + tid;
+            k0 = p < pairs ? int64_t(32 * (p >> 3) + (p & 7)) : 0;
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[i][c] = load1(x, k0 + 8 * c);
     }
@@ -354,7 +422,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
     auto pass1 = [&](auto masked) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const bool ok = !decltype(masked)::value || i * NT + tid < pairs;
+            const bool ok = !decltype(masked)::value || valid(i);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const double d = ok ? double(v[i][c]) : 0.0;
@@ -420,7 +488,7 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
             double q2s = 0.0;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                if (i * NT + tid >= pairs) continue;
+                if (!valid(i)) continue;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const double d = double(v[i][c]) - mu;
@@ -485,37 +553,86 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
 #pragma unroll
             for (int c = 0; c < 4; ++c) codes[i][c] = exact_code<rn>(v[i][c], qb, gamma, lim);
     }
+    // sq: the thread's share of sum q (int8 form: every row; fp4 form: the
+    // rows of types 0..2, whose 0/1 products need it)
     int sq = 0;
+    if constexpr (kF4) {
+        // octet (t, p) -> per digit c one dword at [tile t/4][p][c][word t%4]:
+        // nibble n = digit c of |q| for row 32t + p + 4n, sign in bit 3. The
+        // even rows' magnitudes sit in bytes of m0 (n = 0, 2, 4, 6), the odd
+        // rows' in m1, so one shift and mask per half places a digit in
+        // nibbles 2i and 2i + 1.
+        uint32_t* q32 = reinterpret_cast<uint32_t*>(qs);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int p = i * NT + tid;
-        if (p >= pairs) continue;
-        const uint32_t word = uint32_t(uint8_t(codes[i][0])) | uint32_t(uint8_t(codes[i][1])) << 8 |
-                              uint32_t(uint8_t(codes[i][2])) << 16 | uint32_t(uint8_t(codes[i][3])) << 24;
-        sq += (codes[i][0] + codes[i][1]) + (codes[i][2] + codes[i][3]);
-        const int t = p >> 3, sr = p & 7;
-        *reinterpret_cast<uint32_t*>(qs + (t >> 2) * 128 + sr * 16 + (t & 3) * 4) = word;
-        if (xq_opt && blockIdx.x == 0) {
-            const int64_t k0 = 32 * t + sr;
+        for (int h = 0; h < NV / 2; ++h) {
+            const int o = h * NT + tid;
+            if (o >= octets) continue;
+            const int t = o >> 2, p = o & 3;
+            uint32_t m0 = 0, m1 = 0, sg = 0;
+            int s8 = 0;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) xq_opt[k0 + 8 * c] = int8_t(codes[i][c]);
+            for (int c = 0; c < 4; ++c) {
+                const int a = codes[2 * h][c], b = codes[2 * h + 1][c];
+                m0 |= uint32_t(a < 0 ? -a : a) << (8 * c);
+                m1 |= uint32_t(b < 0 ? -b : b) << (8 * c);
+                sg |= uint32_t(a < 0) << (8 * c + 3) | uint32_t(b < 0) << (8 * c + 7);
+                s8 += a + b;
+            }
+            sq += p != 3 ? s8 : 0;
+            uint32_t* dst = q32 + (t >> 2) * 64 + p * 16 + (t & 3);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                dst[4 * c] = __builtin_amdgcn_bitop3_b32(m0 >> (2 * c), 0x03030303u,
+                                                         ((m1 >> (2 * c)) & 0x03030303u) << 4 | sg, 0xEA);
+            if (xq_opt && blockIdx.x == 0) {
+                const int64_t k0 = 32 * t + p;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    xq_opt[k0 + 8 * c] = int8_t(codes[2 * h][c]);
+                    xq_opt[k0 + 8 * c + 4] = int8_t(codes[2 * h + 1][c]);
+                }
+            }
         }
+        // words K/32 .. 4 TQ - 1 (padding rows) and the zero tile
+        const int w0 = int(K >> 5), nz = (4 * int(TQ) - w0) * 16;
+        for (int z = tid; z < nz; z += NT) {
+            const int t = w0 + (z >> 4);
+            q32[(t >> 2) * 64 + (z & 15) * 4 + (t & 3)] = 0u;
+        }
+        if (tid < 64) q32[(kFusedMaxKp / 128) * 64 + tid] = 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int p = i * NT + tid;
+            if (p >= pairs) continue;
+            const uint32_t word = uint32_t(uint8_t(codes[i][0])) | uint32_t(uint8_t(codes[i][1])) << 8 |
+                                  uint32_t(uint8_t(codes[i][2])) << 16 | uint32_t(uint8_t(codes[i][3])) << 24;
+            sq += (codes[i][0] + codes[i][1]) + (codes[i][2] + codes[i][3]);
+            const int t = p >> 3, sr = p & 7;
+            *reinterpret_cast<uint32_t*>(qs + (t >> 2) * 128 + sr * 16 + (t & 3) * 4) = word;
+            if (xq_opt && blockIdx.x == 0) {
+                const int64_t k0 = 32 * t + sr;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xq_opt[k0 + 8 * c] = int8_t(codes[i][c]);
+            }
+        }
+        for (int k = int(K) + tid; k < Kp; k += NT) qs[q_pos(k)] = 0;
+        if (tid < 32) reinterpret_cast<uint32_t*>(qs + kFusedMaxKp)[tid] = 0u;
     }
-    for (int k = int(K) + tid; k < Kp; k += NT) qs[q_pos(k)] = 0;
-    if (tid < 32) reinterpret_cast<uint32_t*>(qs + kFusedMaxKp)[tid] = 0u;
     if (gamma_opt && blockIdx.x == 0 && tid == 0) gamma_opt[0] = gamma;
     sq = wave_sum63_i(sq);
     if (lane == 63) iscr[wave] = sq;
     __syncthreads();
 
-    // 4. per column group: the product (token 0 lives in lanes with r == 0,
-    //    the rest are zero), then the KQ parts' sums through LDS (one barrier
-    //    per group; none when a wave covers all of K) and the epilogue
+    // 4. per column group: the product (int8 form: token 0 in the lanes with
+    //    r == 0; fp4 form: its four digits in the lanes with r < 4), then the
+    //    KQ parts' sums through LDS (one barrier per group; none when a wave
+    //    covers all of K) and the epilogue
     int rowsum = 0;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) rowsum += iscr[wv];
     const float scale = (beta0 * gamma) / qb;
-    // the B operand: lanes r != 0 never load it, and whatever their registers
+    // the B operand: lanes past the token's columns never load it, and whatever their registers
     // hold only reaches token columns that are never read (an empty asm
     // defines the registers without spending instructions on zeros)
     i32x4_t bk[8];
@@ -525,32 +642,54 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = int64_t(blockIdx.x) + int64_t(it) * gridDim.x;
         if (grp >= ngroups) break;
-        i32x4_t acc[8], accn[kTern ? 8 : 1];
+        i32x4_t sum;
+        if constexpr (kF4) {
+            // lanes r < 4 read digit r of the step's codes (16 bytes per
+            // type); the other lanes' columns are never read, so their B
+            // operand may hold anything (any nibble is a finite fp4 value)
+            f32x4_t acc[4];
 #pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
-        if constexpr (kTern) {
+            for (int p = 0; p < 4; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s8 = 0; s8 < 8; ++s8) accn[s8] = i32x4_t{0, 0, 0, 0};
-        }
-        // only lanes r == 0 (token 0) read the codes: the other lanes' token
-        // columns are never read, so their B operand may hold anything; steps
-        // past the column's tiles read the zero code tile, which cancels
-        // their unmasked signs. Reading for 4 lanes instead of 64 saves LDS
-        // return bandwidth.
+            for (int i = 0; i < S; ++i) {
+                const int st = kq + KQ * i, tq = st * 4 + g;
+                const i32x4_t* src = reinterpret_cast<const i32x4_t*>(qs) +
+                                     (st < steps && tq < int(TQ) ? tq : kFusedMaxKp / 128) * 16 + r;
+                if (r < 4) {
 #pragma unroll
-        for (int i = 0; i < S; ++i) {
-            const int st = kq + KQ * i, tq = st * 4 + g;
-            const i32x4_t* src =
-                reinterpret_cast<const i32x4_t*>(qs + (st < steps && tq < int(TQ) ? tq : kFusedMaxKp / 128) * 128);
-            if (r == 0) {
-#pragma unroll
-                for (int s8 = 0; s8 < 8; ++s8) bk[s8] = src[s8];
+                    for (int p = 0; p < 4; ++p) bk[p] = src[4 * p];
+                }
+                w1a8_f4_step(w[it][i], bk, acc);
             }
-            w1a8_step(w[it][i], bk, acc);
-            if constexpr (kTern) w1a8_step(wn[it][i], bk, accn);
+            sum = w1a8_f4_combine(acc, r);
+        } else {
+            i32x4_t acc[8], accn[kTern ? 8 : 1];
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) acc[s8] = i32x4_t{0, 0, 0, 0};
+            if constexpr (kTern) {
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) accn[s8] = i32x4_t{0, 0, 0, 0};
+            }
+            // only lanes r == 0 (token 0) read the codes: the other lanes'
+            // token columns are never read, so their B operand may hold
+            // anything; steps past the column's tiles read the zero code
+            // tile, which cancels their unmasked signs. Reading for 4 lanes
+            // instead of 64 saves LDS return bandwidth.
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const int st = kq + KQ * i, tq = st * 4 + g;
+                const i32x4_t* src = reinterpret_cast<const i32x4_t*>(
+                    qs + (st < steps && tq < int(TQ) ? tq : kFusedMaxKp / 128) * 128);
+                if (r == 0) {
+#pragma unroll
+                    for (int s8 = 0; s8 < 8; ++s8) bk[s8] = src[s8];
+                }
+                w1a8_step(w[it][i], bk, acc);
+                if constexpr (kTern) w1a8_step(wn[it][i], bk, accn);
+            }
+            sum = w1a8_combine(acc);
+            if constexpr (kTern) sum -= w1a8_combine(accn);
         }
-        i32x4_t sum = w1a8_combine(acc);
-        if constexpr (kTern) sum -= w1a8_combine(accn);
         if constexpr (KQ > 1) {
             red[it & 1][wave][lane] = sum;
             __syncthreads();
@@ -565,7 +704,8 @@ bitlinear_decode1_kernel(const XT* __restrict__ x, int64_t K, double rk, int64_t
         for (int i = 0; i < 4; ++i) {
             const int64_t col = j0 + i;
             if (col >= N) continue;
-            const int32_t a = kTern ? sum[i] : 2 * sum[i] - rowsum;   // binary: 2 sum b q - sum q
+            // binary: 2 sum b q - sum q (fp4 form: sum over the rows of types 0..2 only)
+            const int32_t a = kTern ? sum[i] : kF4 ? sum[i] - rowsum : 2 * sum[i] - rowsum;
             y[col] = float(a) * scale;
             if (acc_opt) acc_opt[col] = a;
         }
