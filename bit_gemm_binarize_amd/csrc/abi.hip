@@ -229,7 +229,7 @@ int fbi_linear_w1a16_group(const bgb_w1a16_item* items, int count, int64_t M, in
         int nf = 0;
         for (int i = 0; i < count; ++i) {
             if (!live[i]) continue;
-            const bool ok = M == 1 ? bgb::w1a16_decode1_supported(items[i].K)
+            const bool ok = M == 1 ? bgb::w1a16_decode1_group_item_ok(items[i].K)
                                    : bgb::w1a16_decodem_supported(M, items[i].K);
             if (ok)
                 fit[nf++] = bgb::W1a16Item{items[i].x, items[i].P, items[i].alpha, items[i].y, items[i].K,

@@ -166,6 +166,7 @@ struct W1a16Item {
     void* y;
     int64_t K, N;
 };
+bool w1a16_decode1_group_item_ok(int64_t K);
 bool w1a16_decode1_group_supported(const W1a16Item* items, int count);
 hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f16, int alpha_f16, int y_dtype,
                                       hipStream_t s);

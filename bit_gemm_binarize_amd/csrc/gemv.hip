@@ -938,18 +938,76 @@ BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2,
     return 2.0f * sb - (((X0 + X1) + X2) + X3);
 }
 
-// Single token, activation staging fused: the block permutes x into LDS and
-// computes the four X_T itself, once, then takes up to IT column groups
+// Single token on the fp4 x fp8 matrix cores (16 x 16 x 128, fp8 = e4m3).
+// A holds the signs as fp4 +-1.0: MFMA type p (0..3) takes bit 4n + p of word
+// d of the lane's tile into nibble n of dword d (tile row 32d + 4n + p), moved
+// to the sign field of 1.0 (a set bit gives +1). B holds the token scaled by
+// 2^sc (its largest magnitude then lies in [8, 16)) as five fixed-point limbs
+// in token columns 0..4, each an integer in [-16, 16]: l0 = rint(v), then
+// l_c = rint(16 r_c) with r_1 = v - l0 and r_(c+1) = 16 r_c - l_c (every step
+// exact in fp32), so v = l0 + l1/16 + l2/256 + l3/4096 + l4/65536 up to at
+// most 2^-17 (exact whenever v is a multiple of 2^-16: a bf16 value within
+// 2^-12 of the largest magnitude, and every integer). The matrix cores align
+// a column's 128 products to the largest one and keep about 14 bits below it
+// (measured: fp8 values more than 2^13 below the largest in their column are
+// dropped), so every limb column must hold values of one quantum; integers
+// below 2^5 are, and each column's sums stay exact integers. The lane layout
+// pairs fp4 lane group ga's nibbles 16h + u with fp8 lane group
+// (2 ga + h) mod 4, byte 16 (ga / 2) + u (checked on the box), so fp8 lane
+// group gb reads rows of tiles 4 st + gb / 2 (bytes 0..15) and
+// 4 st + 2 + gb / 2 (bytes 16..31), words 2 (gb % 2) and 2 (gb % 2) + 1.
+// LDS: per 128-row tile and type p, per limb c, the 4 words' 8 rows each as
+// bytes at f8_off(tile, p, c, word) + n; tile TQ is a zero tile. A token with
+// an inf or NaN gives NaN outputs.
+constexpr int kF8Limbs = 5;
+constexpr int kF8TileBytes = 4 * kF8Limbs * 32;
+constexpr int kF8LdsBytes = (kFusedMaxKp / 128 + 1) * kF8TileBytes;    // the largest K and the zero tile
+constexpr int kF8GroupLds = 65536;                                      // the grouped kernel's dynamic LDS cap
+BGB_DEV int f8_off(int tq, int p, int c, int d) { return ((tq * 4 + p) * kF8Limbs + c) * 32 + d * 8; }
+template <int P>
+BGB_DEV i32x4_t f4_pm1(const u32x4_t& w) {      // (~(w << (3 - P)) & 0x88888888) | 0x22222222
+    constexpr int sh = 3 - P;
+    return i32x4_t{int(__builtin_amdgcn_bitop3_b32(w.x << sh, 0x88888888u, 0x22222222u, 0xAE)),
+                   int(__builtin_amdgcn_bitop3_b32(w.y << sh, 0x88888888u, 0x22222222u, 0xAE)),
+                   int(__builtin_amdgcn_bitop3_b32(w.z << sh, 0x88888888u, 0x22222222u, 0xAE)),
+                   int(__builtin_amdgcn_bitop3_b32(w.w << sh, 0x88888888u, 0x22222222u, 0xAE))};
+}
+BGB_DEV f32x4_t mfma_f4f8(const i32x4_t& a, const i32x8_t& b, const f32x4_t& c) {
+    const i32x8_t a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};   // fp4 A uses the first four dwords
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, 0, 127, 0, 127);   // scales 2^0
+}
+// The limbs of 8 scaled values (|v| < 16), stored as 8 bytes each at dst + c * 32.
+BGB_DEV void f8_limbs(float (&v)[8], uint8_t* dst) {
+#pragma unroll
+    for (int c = 0; c < kF8Limbs; ++c) {
+        float t[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            t[n] = __builtin_rintf(v[n]);
+            v[n] = 16.0f * (v[n] - t[n]);
+        }
+        int lo = 0, hi = 0;   // integers up to 16 in magnitude: exact in e4m3
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], lo, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], lo, true);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(t[4], t[5], hi, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(t[6], t[7], hi, true);
+        *reinterpret_cast<uint2*>(dst + c * 32) = uint2{uint32_t(lo), uint32_t(hi)};
+    }
+}
+
+// Single token, activation staging fused: the block scales the token and
+// writes its limbs to LDS, once, then takes up to IT column groups
 // (bid + i * nblk) of F 16-column fragments, as the W1A8 kernel. The body is
 // shared by the one-linear kernel (bid, nblk = the block index and count)
 // and the grouped one (the block's rank and count within its linear). LDS:
-// xs [kFusedMaxKp], xzero [128] (the B operand of steps past the last tile),
-// red [2 NW 64] when KQ > 1 (the K parts' sums), dX [NW 4].
+// xb [(TQ + 1) kF8TileBytes] (the limbs and a zero tile, the B operand of
+// steps past the last tile), red [2 NW 64] when KQ > 1 (the K parts' sums),
+// mx [NW].
 template <bool kF16, int NV, int NW, int F, int IT>
 BGB_DEV void fbi_decode1_body(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ,
                               const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
-                              void* __restrict__ y, int y_dtype, int64_t bid, int64_t nblk, uint16_t* xs,
-                              uint16_t* xzero, f32x4_t* red, double* dX) {
+                              void* __restrict__ y, int y_dtype, int64_t bid, int64_t nblk, uint8_t* xb,
+                              f32x4_t* red, uint32_t* mx) {
     constexpr int NT = NW * 64;
     constexpr int KQ = NW / F;
     constexpr int S = NV * F;          // steps per wave: TQ <= NV NT / 16 tiles = NV NW steps, over KQ waves
@@ -957,19 +1015,21 @@ BGB_DEV void fbi_decode1_body(const uint16_t* __restrict__ x, int64_t K, int64_t
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r = lane & 15, f = wave % F, kq = wave / F;
     const int64_t ngroups = (N + 16 * F - 1) / (16 * F);
-    const int pieces = int(TQ * 16);                   // 16-byte pieces of the padded token
+    const int octets = int(K / 8), poct = int(TQ * 16);   // octets inside K; of the padded rows
     const int64_t steps = (TQ + 3) / 4;
-    const int Ki = int(K);
 
-    // 1. the token, 16 bytes per load (K % 32 == 0: a piece is all inside K or
-    //    all padding); the loads complete before the sign stream starts
-    u32x4_t xv[NV];
+    // 1. the token: octet o = (t, p) = (o / 4, o % 4) holds rows 32t + p + 4n,
+    //    n = 0..7 (K % 32 == 0: an octet is all inside K or all padding, whose
+    //    values are zero); the loads complete before the sign stream starts
+    uint32_t xv[NV][4];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int p = i * NT + tid;
-        const bool ok = 8 * p < Ki;
-        const u32x4_t t = *reinterpret_cast<const u32x4_t*>(x + (ok ? 8 * p : 0));
-        xv[i] = t & u32x4_t(0u - uint32_t(ok));       // a mask (not a select): the load stays unconditional
+        const int o = i * NT + tid;
+        const bool ok = o < octets;
+        const uint16_t* xo = x + (ok ? 32 * (o >> 2) + (o & 3) : 0);
+        const uint32_t keep = 0u - uint32_t(ok);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[i][j] = (uint32_t(xo[8 * j]) | uint32_t(xo[8 * j + 4]) << 16) & keep;
     }
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));     // vmcnt(0): the token is in
     // the epilogue's arguments (on a later cache line of the argument block
@@ -1004,78 +1064,89 @@ BGB_DEV void fbi_decode1_body(const uint16_t* __restrict__ x, int64_t K, int64_t
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. scatter rows 8p..8p+7 into the decode layout (they share t, and
-    //    (k % 16) runs over 8 consecutive values 8 elements apart), sum each
-    //    type k % 4 in fp64
-    if (tid < 16) reinterpret_cast<u32x4_t*>(xzero)[tid] = u32x4_t{0u, 0u, 0u, 0u};
-    double xs4[4] = {0.0, 0.0, 0.0, 0.0};
+    // 2. the largest magnitude (16-bit magnitude patterns order as the
+    //    values; NaN above inf) and the scale 2^sc that puts it in [128, 256)
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = max(m, max(xv[i][j] & 0x7fffu, (xv[i][j] >> 16) & 0x7fffu));
+    m = wave_umax63(m);
+    if (lane == 63) mx[wave] = m;
+    __syncthreads();
+    uint32_t mt = mx[0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) mt = max(mt, mx[wv]);
+    const bool finite = mt < (kF16 ? 0x7c00u : 0x7f80u);
+    const float xmax = kF16 ? f16_to_f32(uint16_t(mt)) : bf16_to_f32(uint16_t(mt));
+    const int sc = finite && mt != 0 ? 4 - __builtin_amdgcn_frexp_expf(xmax) : 0;
+
+    // 3. the limbs into LDS (padding octets store zeros), and the zero tile
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int p = i * NT + tid;
-        if (p >= pieces) continue;
-        const int k = 8 * p, t = k >> 5, bq = k & 31;
-        uint16_t* dst = xs + (t >> 2) * 128 + (bq & 15) * 8 + (t & 3) * 2 + (bq >> 4);
+        const int o = i * NT + tid;
+        if (o >= poct) continue;
+        const int t = o >> 2, p = o & 3;
+        float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint16_t v = uint16_t(e & 1 ? xv[i][e >> 1] >> 16 : xv[i][e >> 1] & 0xffffu);
-            dst[8 * e] = v;
-            xs4[e & 3] += double(kF16 ? f16_to_f32(v) : bf16_to_f32(v));
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t e0 = uint16_t(xv[i][j] & 0xffffu), e1 = uint16_t(xv[i][j] >> 16);
+            v[2 * j] = __builtin_amdgcn_ldexpf(kF16 ? f16_to_f32(e0) : bf16_to_f32(e0), sc);
+            v[2 * j + 1] = __builtin_amdgcn_ldexpf(kF16 ? f16_to_f32(e1) : bf16_to_f32(e1), sc);
         }
+        f8_limbs(v, xb + f8_off(t >> 2, p, 0, t & 3));      // xv[i][j] holds rows n = 2j, 2j + 1
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const double t = wave_sum63(xs4[c]);
-        if (lane == 63) dX[wave * 4 + c] = t;
-    }
+    const int kZeroTile = int(TQ);
+    for (int z = tid; z < kF8TileBytes / 4; z += NT) reinterpret_cast<uint32_t*>(xb + kZeroTile * kF8TileBytes)[z] = 0u;
     __syncthreads();
-    double Xd[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int wv = 0; wv < NW; ++wv)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) Xd[c] += dX[wv * 4 + c];
-    const float X0 = float(Xd[0]), X1 = float(Xd[1]), X2 = float(Xd[2]), X3 = float(Xd[3]);
-    const float corr = ((8.0f * X0 + 4.0f * X1) + 2.0f * X2) + X3;
-    const float xall = ((X0 + X1) + X2) + X3;
-    constexpr int kBx = S > 4 ? 16 : 1;
-    u32x4_t bx[kBx];
-#pragma unroll
-    for (int u = 0; u < kBx; ++u) bx[u] = u32x4_t{0u, 0u, 0u, 0u};
 
-    // 3. per column group: the product (token 0 lives in lanes with r == 0;
-    //    the other lanes' tokens are never read; tiles past the last one read
-    //    zero activations, since a zero sign word decodes to -1 weights), then
-    //    the KQ parts' sums through LDS (none when a wave covers all of K)
+    // 4. per column group: the product (the limbs live in lanes r < 5; the
+    //    other lanes' B registers stay zero, since an undefined fp8 byte may
+    //    be a NaN; tiles past the last one read the zero limb tile, since a
+    //    zero sign word decodes to -1 weights), then the KQ parts' sums
+    //    through LDS (none when a wave covers all of K)
+    i32x8_t bq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bq[q] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int64_t grp = bid + int64_t(it) * nblk;
         if (grp >= ngroups) break;
-        f32x4_t acc[1][4];
-#pragma unroll
-        for (int T = 0; T < 4; ++T) acc[0][T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int i = 0; i < S; ++i) {
             const int64_t st = kq + int64_t(KQ) * i;
-            const int64_t tq = st * 4 + g;
-            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(st < steps && tq < TQ ? xs + tq * 128 : xzero);
-            if constexpr (S > 4) {
-                // many steps per wave: only lanes r == 0 (token 0) read the
-                // activations, into registers whose other lanes may hold
-                // anything (their token columns are never read); saves LDS
-                // return bandwidth (measured 1-9% faster at S = 8, 2% slower
-                // at S = 4)
-                if (r == 0) {
+            const int64_t ta = st * 4 + (g >> 1), tb = ta + 2;
+            const bool oka = st < steps && ta < TQ, okb = st < steps && tb < TQ;
+            const int c = r < kF8Limbs ? r : 0;
+            const uint8_t* pa = xb + f8_off(oka ? int(ta) : kZeroTile, 0, c, 2 * (g & 1));
+            const uint8_t* pb = xb + f8_off(okb ? int(tb) : kZeroTile, 0, c, 2 * (g & 1));
+            if (r < kF8Limbs) {
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) bx[u] = src[u];
+                for (int q = 0; q < 4; ++q) {
+                    const i32x4_t ha = *reinterpret_cast<const i32x4_t*>(pa + kF8Limbs * 32 * q);
+                    const i32x4_t hb = *reinterpret_cast<const i32x4_t*>(pb + kF8Limbs * 32 * q);
+                    bq[q] = i32x8_t{ha.x, ha.y, ha.z, ha.w, hb.x, hb.y, hb.z, hb.w};
                 }
-                auto bsrc = [&](int u, int) -> u32x4_t { return bx[u]; };
-                w1a16_step<kF16, 1>(w[it][i], bsrc, acc);
-            } else {
-                auto bsrc = [&](int u, int) -> u32x4_t { return src[u]; };
-                w1a16_step<kF16, 1>(w[it][i], bsrc, acc);
             }
+            const u32x4_t& wt = w[it][i];
+            acc[0] = mfma_f4f8(f4_pm1<0>(wt), bq[0], acc[0]);
+            acc[1] = mfma_f4f8(f4_pm1<1>(wt), bq[1], acc[1]);
+            acc[0] = mfma_f4f8(f4_pm1<2>(wt), bq[2], acc[0]);
+            acc[1] = mfma_f4f8(f4_pm1<3>(wt), bq[3], acc[1]);
         }
-        // per wave z = 8 acc_0 + 4 acc_1 + 2 acc_2 + 2 acc_3
-        f32x4_t z = ((8.0f * acc[0][0] + 4.0f * acc[0][1]) + 2.0f * acc[0][2]) + 2.0f * acc[0][3];
+        // limb columns 0..4 weighted 16^-c, summed over the two quads of
+        // lanes 0..7 of each row (the total lands in lane r = 0)
+        f32x4_t z = acc[0] + acc[1];
+        const float lw = __builtin_amdgcn_ldexpf(1.0f, -4 * r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = r < kF8Limbs ? z[e] * lw : 0.0f;
+            v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+            v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+            v += dpp_f32<0x104, 0xF>(v);  // row_shl:4 (lane r + 4; zero past the row)
+            z[e] = v;
+        }
         if constexpr (KQ > 1) {
             red[((it & 1) * NW + wave) * 64 + lane] = z;
             __syncthreads();
@@ -1095,7 +1166,8 @@ BGB_DEV void fbi_decode1_body(const uint16_t* __restrict__ x, int64_t K, int64_t
             const float a = !kAlphaAhead ? load_alpha(alpha, alpha_f16, col)
                             : alpha_f16  ? f16_to_f32(uint16_t(aw[i >> 1] >> (16 * (i & 1))))
                                          : __uint_as_float(aw[i]);
-            store_y(y, y_dtype, col, a * (2.0f * (z[i] - corr) - xall));
+            const float s = finite ? __builtin_amdgcn_ldexpf(z[i], -sc) : __builtin_nanf("");
+            store_y(y, y_dtype, col, a * s);
         }
     }
 }
@@ -1105,12 +1177,11 @@ __global__ void __launch_bounds__(NW * 64)
 fbi_decode1_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t TQ, const uint32_t* __restrict__ P,
                    const void* __restrict__ alpha, int alpha_f16, void* __restrict__ y, int y_dtype) {
     constexpr int KQ = NW / F;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
-    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];
+    __shared__ __attribute__((aligned(16))) uint8_t xb[kF8LdsBytes];
     __shared__ f32x4_t red[(KQ > 1 ? 2 * NW : 1) * 64];
-    __shared__ double dX[NW * 4];
-    fbi_decode1_body<kF16, NV, NW, F, IT>(x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, blockIdx.x, gridDim.x, xs,
-                                          xzero, red, dX);
+    __shared__ uint32_t mx[NW];
+    fbi_decode1_body<kF16, NV, NW, F, IT>(x, K, N, TQ, P, alpha, alpha_f16, y, y_dtype, blockIdx.x, gridDim.x, xb,
+                                          red, mx);
 }
 
 bool w1a16_decode1_supported(int64_t K) { return padded_k(K) <= kFusedMaxKp; }
@@ -1224,10 +1295,10 @@ template <bool kF16>
 __global__ void __launch_bounds__(kD1Waves * 64)
 fbi_decode1_group_kernel(const D1Group g) {
     constexpr int NW = kD1Waves;
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kFusedMaxKp];
-    __shared__ __attribute__((aligned(16))) uint16_t xzero[128];
+    extern __shared__ __attribute__((aligned(16))) uint8_t xb_dyn[];   // (largest TQ + 1) tiles of limbs
+    uint8_t* xb = xb_dyn;
     __shared__ f32x4_t red[2 * NW * 64];
-    __shared__ double dX[NW * 4];
+    __shared__ uint32_t mx[NW];
     D1Item it = g.it[0];
 #pragma unroll
     for (int i = 1; i < kGroupMax; ++i)
@@ -1236,7 +1307,7 @@ fbi_decode1_group_kernel(const D1Group g) {
 #define BGB_G1(C, NVV, FV, ITV)                                                                                 \
     case C:                                                                                                  \
         fbi_decode1_body<kF16, NVV, NW, FV, ITV>(it.x, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y,  \
-                                                 g.y_dtype, bid, it.nblk, xs, xzero, red, dX);                \
+                                                 g.y_dtype, bid, it.nblk, xb, red, mx);                       \
         break;
     static_assert(kGroupSteps == 4, "the cases below are the shapes with NV F <= 4");
     switch (it.cfg) {
@@ -1254,10 +1325,16 @@ fbi_decode1_group_kernel(const D1Group g) {
 #undef BGB_G1
 }
 
+// A grouped block holds its linear's limbs in dynamic LDS, at most
+// kF8GroupLds bytes so that two blocks share a CU: K up to 12928.
+bool w1a16_decode1_group_item_ok(int64_t K) {
+    return w1a16_decode1_supported(K) && (tiles_per_col(K) + 1) * kF8TileBytes <= kF8GroupLds;
+}
+
 bool w1a16_decode1_group_supported(const W1a16Item* items, int count) {
     if (count < 0 || count > kGroupMax) return false;
     for (int i = 0; i < count; ++i)
-        if (!w1a16_decode1_supported(items[i].K)) return false;
+        if (!w1a16_decode1_group_item_ok(items[i].K)) return false;
     return true;
 }
 
@@ -1334,9 +1411,12 @@ hipError_t launch_w1a16_decode1_group(const W1a16Item* items, int count, int x_f
     }
     h.count = n;
     h.alpha_f16 = alpha_f16;
+    int64_t tq_max = 0;
+    for (int i = 0; i < n; ++i) tq_max = h.it[i].TQ > tq_max ? h.it[i].TQ : tq_max;
+    const size_t lds = size_t(tq_max + 1) * kF8TileBytes;
     h.y_dtype = y_dtype;
-    if (x_f16) fbi_decode1_group_kernel<true><<<unsigned(total), NT, 0, s>>>(h);
-    else fbi_decode1_group_kernel<false><<<unsigned(total), NT, 0, s>>>(h);
+    if (x_f16) fbi_decode1_group_kernel<true><<<unsigned(total), NT, lds, s>>>(h);
+    else fbi_decode1_group_kernel<false><<<unsigned(total), NT, lds, s>>>(h);
     return hipGetLastError();
 }
 

@@ -134,3 +134,41 @@ def test_fbi_linear_empty_and_deterministic(bgb_gpu):
         torch.cuda.synchronize()
         for t in ys[1:]:
             assert torch.equal(ys[0], t)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 4096), (11008, 700), (768, 768), (96, 65)])
+@pytest.mark.parametrize("x_kind", ["bf16", "f16"])
+def test_single_token_wide_range_bound(bgb_gpu, orc, K, N, x_kind):
+    """One token: the activations' exponents spread over many binades. The
+    single-token kernels carry the token, scaled by a power of two so that its
+    largest magnitude lies in [8, 16), as five limbs of quantum 2^-16, so each
+    activation is off by at most max|x| 2^-20; every limb column sums exactly
+    on the matrix cores, and the final fp32 combine and the alpha product round
+    a few times. So |y_j - ref_j| <= |alpha_j| (K max|x| 2^-20 + sum|x| 2^-20),
+    beside the 2e-3 normwise tolerance."""
+    say(f"single token wide range K={K} N={N} x={x_kind}")
+    W = syn.normal_f32(700 + K, 0, (K, N), std=0.02)
+    spread = 6.0 if x_kind == "bf16" else 2.0          # f16 keeps its values inside its range
+    a = syn.normal_f32(701, 1, (1, K)) * np.exp2(np.round(syn.normal_f32(701, 2, (1, K)) * spread))
+    xb = syn.f32_to_bf16_bits(a.astype(np.float32)) if x_kind == "bf16" else syn.f32_to_f16_bits(a.astype(np.float32))
+    y, ref, a_host = _run(bgb_gpu, orc, W, xb, x_kind, "f32")
+    xv = (syn.bf16_bits_to_f32(xb) if x_kind == "bf16" else syn.f16_bits_to_f32(xb)).astype(np.float64)
+    xm, xs = np.abs(xv).max(), np.abs(xv).sum()
+    bound = np.abs(a_host.astype(np.float64)) * (K * xm + xs) * 2.0 ** -20
+    assert np.all(np.abs(y[0] - ref[0]) <= bound), float(np.max(np.abs(y[0] - ref[0]) / bound))
+    check_w1a16(y, ref, "f32", "wide range")
+
+
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_single_token_non_finite_gives_nan(bgb_gpu, orc, bad):
+    """A token holding an inf or a NaN: every output of the single-token kernels is NaN."""
+    say(f"single token non-finite {bad}")
+    K, N = 1024, 300
+    W = syn.normal_f32(710, 0, (K, N), std=0.02)
+    a = syn.normal_f32(711, 1, (1, K))
+    a[0, 17] = bad
+    xb = syn.f32_to_bf16_bits(a.astype(np.float32))
+    P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI)
+    y = bgb_gpu.fbi_linear_w1a16(dev_bits16(xb, torch.bfloat16), P, alpha, N)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(to_bits(y)))
