@@ -154,7 +154,12 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
  * rounded to nearest even). Products of +-1 and x are exact; sums use fp32
  * accumulation on the matrix cores; alpha is applied once to the fp32 sum.
  * M <= 64 runs the decode kernels (activations staged in LDS), M > 64 the
- * MFMA GEMM.
+ * MFMA GEMM. One token with K <= 16384 runs on the fp8 matrix cores: the token,
+ * scaled by a power of two into [8, 16), as five integer limbs of quantum
+ * 2^-16, whose column sums are exact; each activation is then carried to
+ * within max|x| 2^-20 (exactly for integers and for values within about 2^-12
+ * of the largest magnitude), and a token holding an inf or a NaN gives NaN
+ * outputs.
  * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes. When that is 0
  * (one token with K <= 16384, up to 16 tokens whose activations fit on chip
  * whole, and decode shapes whose K range is not split) ws is neither read nor
@@ -187,7 +192,7 @@ typedef struct {
  * the result of fbi_linear_w1a16(item.x, x_dtype, M, item.K, item.N, item.P,
  * item.alpha, alpha_dtype, item.y, y_dtype, ...). All items run in one
  * launch (each item split into column groups of its own, one per block) for a
- * single token (M = 1) with every K <= 16384, for 2 <= M <= 16 tokens
+ * single token (M = 1) with every K <= 12928, for 2 <= M <= 16 tokens
  * when every item's tokens fit in LDS (about 140 KB for M (K + 136) 16-bit
  * values), and for 17 <= M <= 64 tokens (each item as 64-token x 256-column
  * matrix-core tiles, its K range split into equal parts whose fp32 sums one
