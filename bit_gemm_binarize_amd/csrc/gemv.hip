@@ -947,7 +947,8 @@ BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2,
 // l_c = rint(16 r_c) with r_1 = v - l0 and r_(c+1) = 16 r_c - l_c (every step
 // exact in fp32), so v = l0 + l1/16 + l2/256 + l3/4096 + l4/65536 up to at
 // most 2^-17 (exact whenever v is a multiple of 2^-16: a bf16 value within
-// 2^-12 of the largest magnitude, and every integer). The matrix cores align
+// 2^-12 of the largest magnitude, and every integer while the largest
+// magnitude is below 2^20). The matrix cores align
 // a column's 128 products to the largest one and keep about 14 bits below it
 // (measured: fp8 values more than 2^13 below the largest in their column are
 // dropped), so every limb column must hold values of one quantum; integers

@@ -157,9 +157,9 @@ int binarize_pack(const float* W, int64_t K, int64_t N, int mode, uint32_t* P,
  * MFMA GEMM. One token with K <= 16384 runs on the fp8 matrix cores: the token,
  * scaled by a power of two into [8, 16), as five integer limbs of quantum
  * 2^-16, whose column sums are exact; each activation is then carried to
- * within max|x| 2^-20 (exactly for integers and for values within about 2^-12
- * of the largest magnitude), and a token holding an inf or a NaN gives NaN
- * outputs.
+ * within max|x| 2^-20 (exactly for values within about 2^-12 of the largest
+ * magnitude, and for integers while the largest magnitude is below 2^20), and
+ * a token holding an inf or a NaN gives NaN outputs.
  * ws: bgb_workspace_bytes(BGB_OP_FBI_LINEAR, M, K, N) bytes. When that is 0
  * (one token with K <= 16384, up to 16 tokens whose activations fit on chip
  * whole, and decode shapes whose K range is not split) ws is neither read nor
