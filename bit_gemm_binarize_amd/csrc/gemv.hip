@@ -1448,16 +1448,21 @@ constexpr int kDmMaxTokens = 16;
 constexpr int kDmWaves = 8;
 constexpr int kDmLdsBytes = 140 * 1024;              // staged tokens: [M][Kp + 8] 16-bit values
 constexpr int kDmMaxJobs = 2;                        // 256-byte token tiles per thread
+constexpr int kDmSeqMinTokens = 8;                   // sequential column groups from this many tokens
 
 // The body is shared by the one-linear kernel (bid, nblk = the block index
 // and count) and the grouped one (the block's rank and count within its
 // linear). LDS: xs [kDmLdsBytes / 2], xzero [128] (the B operand of steps
-// past the last tile), red [2 NW 64] when KQ > 1.
-template <bool kF16, bool kTileJobs, int F, int S, int IT>
+// past the last tile), red [2 NW 64] when KQ > 1. kSeq (with IT == 1): a
+// block takes seq column groups one after another (bid + q nblk, q < seq) on
+// one staging of the tokens; group q + 1's sign tiles and scales are
+// requested into a second set of registers while group q runs.
+template <bool kF16, bool kTileJobs, int F, int S, int IT, bool kSeq = false>
 BGB_DEV void fbi_decodem_body(const uint16_t* __restrict__ x, int M, int64_t K, int64_t N, int64_t TQ,
                               const uint32_t* __restrict__ P, const void* __restrict__ alpha, int alpha_f16,
                               void* __restrict__ y, int y_dtype, int64_t bid, int64_t nblk, uint16_t* xs,
-                              uint16_t* xzero, f32x4_t* red) {
+                              uint16_t* xzero, f32x4_t* red, int seq = 1) {
+    static_assert(!kSeq || IT == 1, "sequential column groups take one group at a time");
     constexpr int NW = kDmWaves, NT = NW * 64;
     constexpr int KQ = NW / F;
     static_assert(NW % F == 0 && IT * S <= kD1MaxTiles, "few-token W1A16 shape");
@@ -1561,10 +1566,22 @@ BGB_DEV void fbi_decodem_body(const uint16_t* __restrict__ x, int M, int64_t K, 
     for (int it = 0; it < IT; ++it)
         alpha4_load(alpha, alpha_f16, (bid + int64_t(it) * nblk) * 16 * F + 16 * f + 4 * g, N,
                     araw[it]);
+    const int nseq = kSeq ? seq : 1;
+    u32x4_t wn[kSeq ? S : 1];                           // the next sequential group's tiles
+    uint2 arawn[2] = {};
+    for (int q = 0; q < nseq; ++q) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int64_t grp = bid + int64_t(it) * nblk;
+        const int64_t grp = bid + int64_t(it + q) * nblk;   // q > 0 only with kSeq
         if (grp >= ngroups) break;
+        if constexpr (kSeq) {
+            const int64_t g2 = grp + nblk;
+            if (q + 1 < nseq && g2 < ngroups) {
+                preload<S>(wn, P, kq, KQ, steps, TQ, N, g2 * 16 * F + 16 * f + r, g);
+                alpha4_load(alpha, alpha_f16, g2 * 16 * F + 16 * f + 4 * g, N, arawn);
+            }
+        }
+        const int rb = (it + q) & 1;                      // reduce buffer: alternates between groups
         f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};   // by u parity
 #pragma unroll
         for (int i = 0; i < S; ++i) {
@@ -1586,12 +1603,12 @@ BGB_DEV void fbi_decodem_body(const uint16_t* __restrict__ x, int M, int64_t K, 
         }
         f32x4_t z = acc[0] + acc[1];
         if constexpr (KQ > 1) {
-            red[((it & 1) * NW + wave) * 64 + lane] = z;
+            red[(rb * NW + wave) * 64 + lane] = z;
             __syncthreads();
             if (kq != 0 || r >= M) continue;
             // the parts in a fixed order: kq = 0, 1, ..., KQ - 1
 #pragma unroll
-            for (int q = 1; q < KQ; ++q) z += red[((it & 1) * NW + f + F * q) * 64 + lane];
+            for (int kp = 1; kp < KQ; ++kp) z += red[(rb * NW + f + F * kp) * 64 + lane];
         } else {
             if (r >= M) continue;
         }
@@ -1602,6 +1619,14 @@ BGB_DEV void fbi_decodem_body(const uint16_t* __restrict__ x, int M, int64_t K, 
             if (col >= N) continue;
             store_y(y, y_dtype, int64_t(r) * N + col, alpha4_get(araw[it], alpha_f16, i) * z[i]);
         }
+    }
+    if constexpr (kSeq) {                               // the prefetched group becomes the current one
+        if (q + 1 >= nseq || bid + int64_t(q + 1) * nblk >= ngroups) break;
+#pragma unroll
+        for (int i = 0; i < S; ++i) w[0][i] = wn[i];
+        araw[0][0] = arawn[0];
+        araw[0][1] = arawn[1];
+    }
     }
 }
 
@@ -1719,6 +1744,7 @@ struct DmItem {
     void* y;
     int64_t K, N, TQ;
     int first, nblk, cfg;   // first block, block count, (staging, F, S) case
+    int seq;                // column groups per block, one after another
 };
 struct DmGroup {
     DmItem it[kGroupMax];
@@ -1740,6 +1766,10 @@ fbi_decodem_group_kernel(const DmGroup g) {
     case C:                                                                                                    \
         fbi_decodem_body<kF16, TJ, FV, SV, 1>(it.x, g.M, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16, it.y,   \
                                               g.y_dtype, bid, it.nblk, xs, xzero, red);                        \
+        break;                                                                                                 \
+    case 32 + C:                                                                                               \
+        fbi_decodem_body<kF16, TJ, FV, SV, 1, true>(it.x, g.M, it.K, it.N, it.TQ, it.P, it.alpha, g.alpha_f16,   \
+                                                    it.y, g.y_dtype, bid, it.nblk, xs, xzero, red, it.seq);    \
         break;
     switch (it.cfg) {
         BGB_GM(0, false, 1, 1) BGB_GM(1, false, 1, 2) BGB_GM(2, false, 1, 4) BGB_GM(3, false, 1, 8)
@@ -1810,14 +1840,66 @@ hipError_t launch_w1a16_decodem_group(const W1a16Item* items, int count, int64_t
         Fs[best] *= 2;
         total_blocks += (frag[best] + Fs[best] - 1) / Fs[best];
     }
+    // Still more blocks than CUs (every item at its widest groups): rather
+    // than a second round that stages the tokens again, blocks take several
+    // column groups one after another. The smallest cap C on a block's work
+    // (fragments x 128-row tiles) whose plan fits one block per CU: per item
+    // the fragments per group F (its widest groups or half as wide, so that
+    // a group's barrier and reduction stay few) and seq = C / (F TQ) groups
+    // per block, whichever F gives the fewest blocks. More work per block
+    // means fewer blocks, so C is found by bisection. Only from 8 tokens:
+    // below that the staging is cheap (4 tokens of 4096: 32 KB per block) and
+    // the groups' extra barriers and reductions cost more than a second round
+    // (7B-shaped layer at 4 tokens: 27.7 us with sequential groups against
+    // 23.3 us in two rounds; at 16 tokens 36.9 against 43.9 us).
+    int seqs[kGroupMax];
+    for (int i = 0; i < n; ++i) seqs[i] = 1;
+    if (total_blocks > kD1MaxGrid && M >= kDmSeqMinTokens) {
+        int fc[kGroupMax], sc[kGroupMax];
+        auto fit = [&](int64_t C) {
+            int64_t tot = 0;
+            for (int i = 0; i < n; ++i) {
+                const int64_t tq = g.it[i].TQ;
+                int64_t bestb = -1;
+                fc[i] = Fs[i];
+                sc[i] = 1;
+                for (int F = Fs[i] > 1 ? Fs[i] / 2 : 1; F <= Fs[i]; F *= 2) {
+                    const int64_t sq = C / (F * tq);
+                    if (sq < 1) continue;
+                    const int64_t nb = ((frag[i] + F - 1) / F + sq - 1) / sq;
+                    if (bestb < 0 || nb <= bestb) {
+                        bestb = nb;
+                        fc[i] = F;
+                        sc[i] = int(sq < (int64_t(1) << 20) ? sq : (int64_t(1) << 20));
+                    }
+                }
+                tot += bestb < 0 ? (frag[i] + Fs[i] - 1) / Fs[i] : bestb;
+            }
+            return tot <= kD1MaxGrid;
+        };
+        int64_t lo = 1, hi = 1;
+        for (int i = 0; i < n; ++i) hi += int64_t(Fs[i]) * g.it[i].TQ * ((frag[i] + Fs[i] - 1) / Fs[i]);
+        while (lo < hi) {                                // smallest C that fits (fit(hi) holds: one block per item)
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (fit(mid)) hi = mid;
+            else lo = mid + 1;
+        }
+        fit(lo);
+        for (int i = 0; i < n; ++i) {
+            Fs[i] = fc[i];
+            seqs[i] = sc[i];
+        }
+    }
     for (int i = 0; i < n; ++i) {
         DmItem& d = g.it[i];
         const int F = Fs[i], S = spw(i, F);
         if (S > kD1MaxTiles) return hipErrorInvalidValue;  // not reached: supported()
-        d.nblk = int((frag[i] + F - 1) / F);
+        d.seq = seqs[i];
+        d.nblk = int(((frag[i] + F - 1) / F + seqs[i] - 1) / seqs[i]);
         const bool tj = M * d.TQ >= kDmWaves * 64;          // whole tiles per thread, as the one-linear launcher
-        d.cfg = 16 * tj + 4 * (F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3) + (S == 1 ? 0 : S == 2 ? 1 : S == 4 ? 2 : 3);
-        cost[i] = int64_t(F) * d.TQ;
+        d.cfg = 32 * (seqs[i] > 1) + 16 * tj + 4 * (F == 1 ? 0 : F == 2 ? 1 : F == 4 ? 2 : 3) +
+                (S == 1 ? 0 : S == 2 ? 1 : S == 4 ? 2 : 3);
+        cost[i] = int64_t(F) * seqs[i] * d.TQ;
     }
     if (n == 0) return hipSuccess;
     for (int a = 1; a < n; ++a)

@@ -87,6 +87,22 @@ def test_group_several_tokens_parity(bgb_gpu, orc, M):
     _check_items(orc, items, ys, "bf16", "bf16")
 
 
+@pytest.mark.parametrize("M", [4, 8, 16])
+@pytest.mark.parametrize("int_x", [True, False])
+def test_group_sequential_column_groups(bgb_gpu, orc, M, int_x):
+    """2..16 tokens over more column groups than one block per CU can hold at
+    the widest groups (378 here): from 8 tokens blocks take several column
+    groups one after another on one staging of the tokens, below that the
+    grid runs in two rounds. Every output against the oracle; bit-exact on
+    integer activations."""
+    shapes = [(1024, 24000), (512, 20000), (2048, 4100)]
+    say(f"group sequential column groups M={M} int_x={int_x}")
+    items = _items(bgb_gpu, shapes, M, "bf16", "f32", 1100 + M, int_x=int_x)
+    ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items])
+    torch.cuda.synchronize()
+    _check_items(orc, items, ys, "bf16", "f32", exact=int_x)
+
+
 def test_group_empty_items_and_determinism(bgb_gpu, orc):
     say("group empty items + determinism")
     shapes = [(4096, 300), (1024, 0), (768, 100)]
