@@ -954,7 +954,7 @@ BGB_DEV float w1a16_out(const f32x4_t* tot, int i, float X0, float X1, float X2,
 // dropped), so every limb column must hold values of one quantum; integers
 // below 2^5 are, and each column's sums stay exact integers. The lane layout
 // pairs fp4 lane group ga's nibbles 16h + u with fp8 lane group
-// (2 ga + h) mod 4, byte 16 (ga / 2) + u (checked on the box), so fp8 lane
+// (2 ga + h) mod 4, byte 16 (ga / 2) + u (measured with one-element operands), so fp8 lane
 // group gb reads rows of tiles 4 st + gb / 2 (bytes 0..15) and
 // 4 st + 2 + gb / 2 (bytes 16..31), words 2 (gb % 2) and 2 (gb % 2) + 1.
 // LDS: per 128-row tile and type p, per limb c, the 4 words' 8 rows each as
