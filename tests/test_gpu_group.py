@@ -77,8 +77,8 @@ def test_group_integer_activations_bit_exact(bgb_gpu, orc, x_kind):
 @pytest.mark.parametrize("M", [2, 4, 16, 40, 70])
 def test_group_several_tokens_parity(bgb_gpu, orc, M):
     """More than one token: one launch for 2..16 tokens (pieces or whole tiles
-    staged per item), otherwise the items one after another through the
-    single-linear dispatch (40, 70), sharing the largest item's workspace."""
+    staged per item), the grouped GEMM for 17..64 (40), and beyond 64 tokens
+    the items one after another through the single-linear GEMM (70)."""
     shapes = [(1024, 300), (11008, 200), (96, 65), (2048, 520)]
     say(f"group M={M} shapes={shapes}")
     items = _items(bgb_gpu, shapes, M, "bf16", "f32", 700 + M)
@@ -101,6 +101,43 @@ def test_group_sequential_column_groups(bgb_gpu, orc, M, int_x):
     ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items])
     torch.cuda.synchronize()
     _check_items(orc, items, ys, "bf16", "f32", exact=int_x)
+
+
+@pytest.mark.parametrize("M", [65, 130, 300])
+@pytest.mark.parametrize("int_x", [True, False])
+def test_group_prefill_parity(bgb_gpu, orc, M, int_x):
+    """More than 64 tokens: the items one after another through the
+    single-linear GEMM (a ragged token tile, a K tail, items of different K).
+    Every output against the oracle; bit-exact on integer activations."""
+    shapes = [(1024, 1000), (2048, 520), (352, 300), (4096, 257)]
+    say(f"group prefill M={M} int_x={int_x}")
+    items = _items(bgb_gpu, shapes, M, "bf16", "f32", 1200 + M, int_x=int_x)
+    ys = bgb_gpu.fbi_linear_w1a16_group([(x, P, a, W.shape[1]) for (W, _, x, P, a) in items])
+    torch.cuda.synchronize()
+    _check_items(orc, items, ys, "bf16", "f32", exact=int_x)
+
+
+def test_group_1p3b_layer_prefill_sampled_rows(bgb_gpu, orc):
+    """A 1.3B-shaped layer's four fused linears (qkv 2048 x 6144, o 2048 x
+    2048, gate_up 2048 x 11264, down 5632 x 2048) over 2048 tokens through
+    the group call: 8 sampled token rows of each item against the oracle,
+    bf16 outputs."""
+    shapes = [(2048, 6144), (2048, 2048), (2048, 11264), (5632, 2048)]
+    M = 2048
+    say("group 1.3B layer prefill M=2048")
+    lin, refs = [], []
+    for i, (K, N) in enumerate(shapes):
+        W = syn.normal_f32(1300 + i, 0, (K, N), std=0.02)
+        xb = _x_bits("bf16", 1300 + i, M, K)
+        P, alpha = bgb_gpu.binarize_pack(dev_f32(W), bgb_gpu.MODE_FBI, torch.float16)
+        rows = np.sort(syn.rng_for(1300 + i, 4).choice(M, 8, replace=False))
+        a_host = alpha.detach().float().cpu().numpy().astype(np.float32)
+        refs.append((rows, orc.fbi_linear(np.ascontiguousarray(xb[rows]), W, a_host, "bf16")))
+        lin.append((dev_bits16(xb, torch.bfloat16), P, alpha, N))
+    ys = bgb_gpu.fbi_linear_w1a16_group(lin, torch.bfloat16)
+    torch.cuda.synchronize()
+    for (rows, ref), y in zip(refs, ys):
+        check_w1a16(to_bits(y)[rows], ref, "bf16", f"1.3B prefill group N={y.shape[1]}")
 
 
 def test_group_empty_items_and_determinism(bgb_gpu, orc):
