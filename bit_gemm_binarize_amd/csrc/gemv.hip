@@ -2105,11 +2105,15 @@ constexpr int kDkMaxTokens = 64;
 bool w1a16_decodek_supported(int64_t M, int64_t K) { return M >= 1 && M <= kDkMaxTokens && K > 0; }
 
 // Launch plan. Measured on the chunked kernel: about 3.6 us of fixed cost
-// (launch, first loads, epilogue) plus about 2.4 us per chunk a block stages,
-// at up to one block per CU; a split adds the reduce pass (a launch plus its
-// traffic). Splits are chosen to cut the chunks per block while the grid
-// stays within one block per CU; more fragments per block (each activation
-// read feeding more MFMAs) are preferred at equal cost.
+// (launch, first loads, epilogue) plus about 2.4 us per chunk of 32768 staged
+// elements (32 tokens x 1024 rows; a chunk of 16 tokens x 1024 rows costs
+// half), at up to one block per CU; a split adds the reduce pass (a launch
+// plus its traffic). Splits are chosen to cut the chunks per block while the
+// grid stays within one block per CU; more fragments per block (each
+// activation read feeding more MFMAs) are preferred at equal cost. Chunks are
+// one tile per wave: at 16 tokens, two tiles per wave (2048-row chunks) left
+// the 16-token 11008 x 4096 linear at 3 splits of 2 chunks on 192 blocks,
+// 1.5 us slower than 4 splits of 3 chunks on 256.
 namespace {
 constexpr double kDkFixedUs = 3.6, kDkChunkUs = 2.4, kDkReduceUs = 2.5, kDkReduceBytesPerUs = 4.0e6;
 constexpr int kDkMaxBlocks = 256;
@@ -2117,11 +2121,12 @@ constexpr int kDkMaxBlocks = 256;
 
 DecodekPlan decodek_plan(int64_t M, int64_t K, int64_t N) {
     DecodekPlan p{};
-    p.tf = M <= 16 ? 1 : 2;                  // 16 tokens per block: chunks of 16 tiles (2 per wave); 32: of 8
-    p.tpw = p.tf == 1 ? 2 : 1;
+    p.tf = M <= 16 ? 1 : 2;                  // 16 or 32 tokens per block, chunks of 8 tiles
+    p.tpw = 1;
     const int64_t TQ = tiles_per_col(K);
     const int CT = kDkWaves * p.tpw;
     p.nchunks = int((TQ + CT - 1) / CT);
+    const double chunk_us = kDkChunkUs * double(16 * p.tf * 128 * CT) / double(kDkChunkElems);
     const int64_t frags = (N + 15) / 16;
     const int64_t tblocks = (M + 16 * p.tf - 1) / (16 * p.tf);
     double best = 1e300;
@@ -2133,7 +2138,7 @@ DecodekPlan decodek_plan(int64_t M, int64_t K, int64_t N) {
             if (splits != S) continue;                       // same split count as a smaller S
             const int64_t blocks = cb * tblocks * splits;
             const double rounds = double((blocks + kDkMaxBlocks - 1) / kDkMaxBlocks);
-            double t = kDkFixedUs + rounds * cps * kDkChunkUs;
+            double t = kDkFixedUs + rounds * cps * chunk_us;
             if (splits > 1) t += kDkReduceUs + double(splits + 1) * double(M) * double(N) * 4.0 / kDkReduceBytesPerUs;
             if (blocks < 128 && fb > 1) t += blocks < 64 ? 1.0 : 0.3;   // few CUs streaming the signs
             if (t < best - 1e-9) {
@@ -2188,8 +2193,8 @@ hipError_t launch_w1a16_decodek(const void* x, int x_f16, int64_t M, int64_t K, 
     const uint16_t* xx = static_cast<const uint16_t*>(x);
     const int m = int(M);
     if (p.tf == 1)
-        return x_f16 ? launch_w1a16_decodek_t<true, 1, 2>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s)
-                     : launch_w1a16_decodek_t<false, 1, 2>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s);
+        return x_f16 ? launch_w1a16_decodek_t<true, 1, 1>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s)
+                     : launch_w1a16_decodek_t<false, 1, 1>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s);
     return x_f16 ? launch_w1a16_decodek_t<true, 2, 1>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s)
                  : launch_w1a16_decodek_t<false, 2, 1>(p, xx, m, K, N, P, alpha, alpha_f16, y, y_dtype, part, s);
 }
