@@ -540,10 +540,10 @@ BGB_DEV void add_splits8(V& s, const V (&v)[8], int z0, int splits) {
         if (z0 + q < splits) s += v[q];
 }
 
-template <bool kW1A8>
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs a, int splits) {
+template <bool kW1A8, int kT = 256>
+__global__ void __launch_bounds__(kT) splitk_reduce_kernel(const GemmArgs a, int splits) {
     const int64_t M = a.M, N = a.N, nq = (N + 3) / 4;
-    const int64_t id = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t id = int64_t(blockIdx.x) * kT + threadIdx.x;
     if (id >= M * nq) return;
     const int64_t m = id / nq, jb = 4 * (id % nq), o = m * N + jb;
     const bool full = jb + 4 <= N && (N & 3) == 0;
@@ -879,7 +879,9 @@ hipError_t launch_w1a16_splitk_reduce(const float* part, int splits, int64_t M, 
     a.y_dtype = y_dtype;
     a.part = const_cast<float*>(part);
     const int64_t n = M * ((N + 3) / 4);
-    splitk_reduce_kernel<false><<<unsigned((n + 255) / 256), 256, 0, s>>>(a, splits);
+    // one wave per block: at decode sizes (M x N / 4 threads, 16K at 16 tokens
+    // x 4096 columns) the pass is a single round of loads, spread over 4x the CUs
+    splitk_reduce_kernel<false, 64><<<unsigned((n + 63) / 64), 64, 0, s>>>(a, splits);
     return hipGetLastError();
 }
 
